@@ -106,3 +106,17 @@ def test_huge_splat_covers_every_tile():
     assert pr["tiles_touched"][0] == tx * ty == 15
     keys, ids, ranges = oracle.bin_pairs(pr, cam)
     assert np.array_equal(ranges[:, 0], np.arange(15)) and np.array_equal(ranges[:, 1], np.arange(1, 16))
+
+
+def test_equal_depths_keep_ascending_id():
+    # Many Gaussians at exactly the same depth: equal keys within a tile must keep ascending
+    # Gaussian id (the stable sort of section 5's argsort(depths, stable=True)).
+    wl = synth.WORKLOADS["tiny_1k"]
+    sc = synth.make_scene(wl, n=3000)
+    sc["means"][:, 2] = 4.0
+    cam = synth.make_cameras(wl)[0]
+    pr = oracle.project(sc, cam)
+    keys, ids, _ = oracle.bin_pairs(pr, cam)
+    eq = keys[1:] == keys[:-1]
+    assert eq.sum() > 1000
+    assert np.all(ids[1:][eq] > ids[:-1][eq])

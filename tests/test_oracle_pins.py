@@ -361,3 +361,17 @@ def test_culled_inputs_are_safe():
     for v in raw.values():
         assert np.all(np.isfinite(v)) and np.all(v[:4] == 0)
     assert np.any(raw["means"][4] != 0)
+
+
+def test_stop_comparison_is_less_or_equal():
+    # Section 5's loop stops before adding when T * (1 - alpha) <= 1e-4f (gsplat's comparison;
+    # 3DGS uses <). With alphas (0.99, 0.98, 0.49999905) at one pixel centre, the third product is
+    # exactly 1e-4f in fp32 arithmetic, so the third splat is not added.
+    alphas = np.array([0.99, 0.98, 0.4999990463256836], np.float32)
+    T = np.float32(1.0)
+    for a in alphas:
+        T = np.float32(T * np.float32(np.float32(1.0) - a))
+    assert T == np.float32(1e-4)
+    pr = splats_2d([[0.5, 0.5]] * 3, [[1.0, 0.0, 1.0]] * 3, alphas, [[1, 1, 1]] * 3)
+    out = oracle.render(pr, ident_cam(8, 8, 10.0), pixels=np.array([[0, 0]]), dtype=np.float32)
+    assert out["n_contrib"][0] == 2 and out["fragile"][0]
