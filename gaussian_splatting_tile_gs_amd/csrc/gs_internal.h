@@ -1,0 +1,161 @@
+// Internal declarations shared by the HIP translation units of libgs_hip.so (gfx950 only).
+//
+// The whole library is compiled with -ffp-contract=off: every fused multiply-add below is an
+// explicit fmaf, so each expression rounds exactly as written. That makes the projection's
+// integer results (radii, tile rectangles, tile counts) reproducible bit for bit, and makes the
+// forward and backward raster kernels take identical skip/stop decisions, because they share
+// the same inline evaluation of a splat at a pixel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "gs.h"
+
+namespace gs {
+
+// ---------------------------------------------------------------------------------------------
+// Device-side camera: copied by value into kernel arguments.
+// ---------------------------------------------------------------------------------------------
+struct DevCamera {
+  float V[16];
+  float fx, fy, cx, cy;
+  int32_t W, H;
+  float near_plane;
+  float bg[3];
+  int32_t tiles_x, tiles_y;
+};
+
+inline DevCamera to_dev(const gs_camera& c) {
+  DevCamera d;
+  for (int i = 0; i < 16; ++i) d.V[i] = c.viewmat[i];
+  d.fx = c.fx; d.fy = c.fy; d.cx = c.cx; d.cy = c.cy;
+  d.W = c.width; d.H = c.height;
+  d.near_plane = c.near_plane;
+  d.bg[0] = c.background[0]; d.bg[1] = c.background[1]; d.bg[2] = c.background[2];
+  d.tiles_x = (c.width + GS_TILE_SIZE - 1) / GS_TILE_SIZE;
+  d.tiles_y = (c.height + GS_TILE_SIZE - 1) / GS_TILE_SIZE;
+  return d;
+}
+
+// max/min with the exact semantics of (a < b) ? b : a and (b < a) ? b : a.
+__host__ __device__ __forceinline__ float omax(float a, float b) { return (a < b) ? b : a; }
+__host__ __device__ __forceinline__ float omin(float a, float b) { return (b < a) ? b : a; }
+
+// ---------------------------------------------------------------------------------------------
+// Reproducible fp32 exp and log for the activations.
+// exp: Cody & Waite (1980) additive range reduction x = k ln2 + r, with ln2 split into a short
+// head (exact products k * head) and a tail; e^r from the degree-7 Taylor polynomial by Horner's
+// rule in fused multiply-adds; e^x = 2^k e^r. Input clamped to [-87, 88] (normal results).
+// log: x = m 2^e, m moved into [sqrt(1/2), sqrt(2)); ln m = 2 atanh(s), s = (m - 1)/(m + 1),
+// odd atanh series through s^9; ln x = e ln2 + ln m.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float act_exp(float x) {
+  if (x != x) return x;
+  x = (x < -87.0f) ? -87.0f : x;
+  x = (x > 88.0f) ? 88.0f : x;
+  const float k = rintf(x * 0x1.715476p+0f);
+  const float r = (x - k * 0x1.62e4p-1f) - k * 0x1.7f7d1cp-20f;
+  float p = 0x1.a01a02p-13f;
+  p = fmaf(p, r, 0x1.6c16c2p-10f);
+  p = fmaf(p, r, 0x1.111112p-7f);
+  p = fmaf(p, r, 0x1.555556p-5f);
+  p = fmaf(p, r, 0x1.555556p-3f);
+  p = fmaf(p, r, 0.5f);
+  p = fmaf(p, r, 1.0f);
+  p = fmaf(p, r, 1.0f);
+  return ldexpf(p, (int)k);
+}
+
+__device__ __forceinline__ float act_log(float x) {
+  if (x != x) return x;
+  if (x < 0.0f) return __builtin_nanf("");
+  if (x == 0.0f) return -__builtin_inff();
+  if (x == __builtin_inff()) return x;
+  int e = 0;
+  float m = frexpf(x, &e);
+  if (m < 0x1.6a09e6p-1f) {
+    m = m * 2.0f;
+    e = e - 1;
+  }
+  const float s = (m - 1.0f) / (m + 1.0f);
+  const float s2 = s * s;
+  float q = 0x1.c71c72p-4f;
+  q = fmaf(q, s2, 0x1.24924ap-3f);
+  q = fmaf(q, s2, 0x1.99999ap-3f);
+  q = fmaf(q, s2, 0x1.555556p-2f);
+  const float t = s2 * q;
+  const float two_s = 2.0f * s;
+  const float lnm = fmaf(two_s, t, two_s);
+  const float fe = (float)e;
+  const float r = fmaf(fe, 0x1.7f7d1cp-20f, lnm);
+  return fmaf(fe, 0x1.62e4p-1f, r);
+}
+
+// Tile rectangle [x0, x1) x [y0, y1) of a splat with mean (mx, my) and radii (rx, ry), clamped
+// to the grid; the same expression is used by the projection (to count) and by the emitter.
+struct TileRect {
+  int32_t x0, y0, x1, y1;
+};
+__device__ __forceinline__ TileRect tile_rect(float mx, float my, float rx, float ry, int32_t tiles_x,
+                                              int32_t tiles_y) {
+  float x0 = floorf((mx - rx) / 16.0f), x1 = ceilf((mx + rx) / 16.0f);
+  float y0 = floorf((my - ry) / 16.0f), y1 = ceilf((my + ry) / 16.0f);
+  x0 = omin(omax(x0, 0.0f), (float)tiles_x);
+  x1 = omin(omax(x1, 0.0f), (float)tiles_x);
+  y0 = omin(omax(y0, 0.0f), (float)tiles_y);
+  y1 = omin(omax(y1, 0.0f), (float)tiles_y);
+  return {(int32_t)x0, (int32_t)y0, (int32_t)x1, (int32_t)y1};
+}
+
+// ---------------------------------------------------------------------------------------------
+// One splat evaluated at one pixel centre: the blend's sigma, alpha and its skip decision.
+// The record stores the conic pre-scaled by log2(e) (hA = A/2 log2e, B2 = B log2e, hC = C/2
+// log2e) so that exp(-sigma) is a single exp2. Forward and backward call this same function.
+// ---------------------------------------------------------------------------------------------
+constexpr float kLog2e = 0x1.715476p+0f;
+constexpr float kAlphaMin = 1.0f / 255.0f;
+constexpr float kAlphaMax = 0.99f;
+constexpr float kTransmittanceMin = 1e-4f;
+
+struct SplatEval {
+  float alpha;  // min(0.99, o G), meaningful when !skip
+  float G;      // exp(-sigma)
+  bool skip;    // sigma < 0 or alpha < 1/255
+  bool capped;  // o G >= 0.99 (alpha is the constant cap: no gradient to o or sigma)
+};
+
+__device__ __forceinline__ SplatEval eval_splat(float dx, float dy, float hA, float B2, float hC, float o) {
+  // s2 = log2(e) * sigma = hA dx^2 + hC dy^2 + B2 dx dy
+  const float s2 = fmaf(hA * dx, dx, fmaf(hC * dy, dy, (B2 * dx) * dy));
+  SplatEval e;
+  e.G = exp2f(-s2);
+  const float raw = o * e.G;
+  e.capped = raw >= kAlphaMax;
+  e.alpha = e.capped ? kAlphaMax : raw;
+  e.skip = (s2 < 0.0f) || (e.alpha < kAlphaMin);
+  return e;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Host side: status, last error, kernel timing.
+// ---------------------------------------------------------------------------------------------
+gs_status set_error(gs_status s, const std::string& msg);
+gs_status check_launch(const char* what);
+bool valid_camera(const gs_camera* cam, std::string* why);
+
+// Kernel timing: bracket a launch with events when enabled.
+void timing_begin(const char* name, hipStream_t stream);
+void timing_end(hipStream_t stream);
+
+struct TimedScope {
+  hipStream_t s;
+  TimedScope(const char* name, hipStream_t stream) : s(stream) { timing_begin(name, stream); }
+  ~TimedScope() { timing_end(s); }
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace gs

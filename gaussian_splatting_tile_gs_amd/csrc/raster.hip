@@ -1,0 +1,598 @@
+// Forward blend (k-blend), backward raster (k-rbwd) and backward projection (k-pbwd).
+//
+// Forward ("Gaussian splatting in PyTorch", section 5): per pixel, front to back over its tile's
+// sorted list, alpha = min(0.99, o exp(-sigma)), skip below 1/255 or for sigma < 0, stop before
+// adding once T (1 - alpha) <= 1e-4, finally add T * background.
+// Backward (section 6; the production kernels "write the backward pass by hand, back to front"
+// and recover T_i by dividing by 1 - alpha_j): per pixel back to front from its last
+// contributor, with the weights recomputed rather than stored.
+//
+// MI355X design:
+//  - one 256-thread workgroup (4 wave64) per 16 x 16 tile, one pixel per thread; Gaussians are
+//    staged 256 at a time in LDS as pre-scaled records (every lane then reads the same record:
+//    an LDS broadcast, no bank conflicts);
+//  - a wave leaves the batch loop as soon as all 64 of its pixels are done (wave-uniform test),
+//    the workgroup stops loading batches when all 256 are (__syncthreads_count);
+//  - workgroup -> tile mapping is XCD-aware: consecutive workgroup ids go round-robin to the 8
+//    XCDs, so each XCD is given a contiguous band of tiles and neighbouring tiles, which share
+//    most Gaussians, hit the same L2;
+//  - backward: the 9 per-splat gradient terms of a wave are summed with DPP row shifts and row
+//    broadcasts (7 VALU ops per value, lane 63 holds the sum), accumulated per workgroup in LDS
+//    (ds_add_f32), and flushed once per (tile, splat) with global fp32 atomics.
+// Both raster kernels evaluate a splat with the same inline eval_splat, so the backward takes
+// exactly the forward's skip decisions.
+#include "project_core.h"
+
+namespace gs {
+namespace {
+
+constexpr int kTile = 16;
+constexpr int kRasterThreads = kTile * kTile;  // 256: one pixel per thread
+constexpr int kBatch = kRasterThreads;         // splats staged per batch
+
+// XCD-aware tile index for workgroup b when the grid has 8 * per_xcd workgroups.
+__device__ __forceinline__ int tile_of_block(int b, int per_xcd) { return (b & 7) * per_xcd + (b >> 3); }
+
+// Pre-scaled splat record: (mx, my, hA, hC), (B2, o, r, g), b. hA = A/2 log2e, B2 = B log2e,
+// hC = C/2 log2e, so that log2(e) sigma = hA dx^2 + hC dy^2 + B2 dx dy.
+// An id >= n (impossible for a well-formed sorted list) loads a record that never contributes.
+__device__ __forceinline__ void load_record(uint32_t g, uint32_t n, const float* __restrict__ means2d,
+                                            const float* __restrict__ conics, const float* __restrict__ opac,
+                                            const float* __restrict__ colors, float4& a, float4& b, float& c) {
+  if (g >= n) {
+    a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    b = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    c = 0.0f;
+    return;
+  }
+  const float2 m = *reinterpret_cast<const float2*>(means2d + 2 * g);
+  const float A = conics[3 * g], B = conics[3 * g + 1], C = conics[3 * g + 2];
+  a = make_float4(m.x, m.y, (0.5f * kLog2e) * A, (0.5f * kLog2e) * C);
+  b = make_float4(kLog2e * B, opac[g], colors[3 * g], colors[3 * g + 1]);
+  c = colors[3 * g + 2];
+}
+
+// Sum over the 64 lanes of a wave with DPP; the total lands in lane 63 (other lanes hold partial
+// sums). Row shifts with bound_ctrl read 0 past a row's start, so no row/bank masking is needed
+// for lane 63's result, and every step folds into one v_add_f32_dpp.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float wave_sum_lane63(float v) {
+  float r = v + dpp_f<0x111>(v);  // row_shr:1
+  r = r + dpp_f<0x112>(v);        // row_shr:2
+  r = r + dpp_f<0x113>(v);        // row_shr:3 -> lane i: v[i-3..i] within its row
+  r = r + dpp_f<0x114>(r);        // row_shr:4 -> v[i-7..i]
+  r = r + dpp_f<0x118>(r);        // row_shr:8 -> lane 15 of each row holds the row's sum
+  r = r + dpp_f<0x142>(r);        // row_bcast:15 -> lane 63 holds rows 2 + 3, lane 31 rows 0 + 1
+  r = r + dpp_f<0x143>(r);        // row_bcast:31 -> lane 63 holds the wave
+  return r;
+}
+
+// ---------------------------------------------------------------------------------------------
+// k-blend
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kRasterThreads) void k_blend(
+    uint32_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ ids, const float* __restrict__ means2d,
+    const float* __restrict__ conics, const float* __restrict__ opac, const float* __restrict__ colors,
+    DevCamera cam, int per_xcd, float* __restrict__ image, float* __restrict__ final_T,
+    uint32_t* __restrict__ n_contrib, unsigned long long* __restrict__ eval_count) {
+  __shared__ float4 s_a[kBatch];
+  __shared__ float4 s_b[kBatch];
+  __shared__ float s_c[kBatch];
+
+  const int tile = tile_of_block(blockIdx.x, per_xcd);
+  if (tile >= cam.tiles_x * cam.tiles_y) return;  // whole workgroup: uniform
+  const int tid = threadIdx.x;
+  const int px_i = (tile % cam.tiles_x) * kTile + (tid & (kTile - 1));
+  const int py_i = (tile / cam.tiles_x) * kTile + (tid / kTile);
+  const bool inside = px_i < cam.W && py_i < cam.H;
+  const float px = (float)px_i + 0.5f, py = (float)py_i + 0.5f;
+  const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
+
+  float T = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f;
+  uint32_t last = 0, n_eval = 0;
+  bool done = !inside;
+  for (uint32_t bs = start; bs < end; bs += kBatch) {
+    if (__syncthreads_count(done) == kRasterThreads) break;
+    const uint32_t j = bs + tid;
+    if (j < end) load_record(ids[j], n, means2d, conics, opac, colors, s_a[tid], s_b[tid], s_c[tid]);
+    __syncthreads();
+    const int cnt = (end - bs) < (uint32_t)kBatch ? (int)(end - bs) : kBatch;
+    for (int k = 0; k < cnt; ++k) {
+      if (!__any(!done)) break;
+      if (done) continue;
+      const float4 a = s_a[k];
+      const float4 b = s_b[k];
+      const SplatEval e = eval_splat(a.x - px, a.y - py, a.z, b.x, a.w, b.y);
+      ++n_eval;
+      if (e.skip) continue;
+      const float nT = T * (1.0f - e.alpha);
+      if (nT <= kTransmittanceMin) {
+        done = true;
+        continue;
+      }
+      const float w = e.alpha * T;
+      cr = fmaf(b.z, w, cr);
+      cg = fmaf(b.w, w, cg);
+      cb = fmaf(s_c[k], w, cb);
+      T = nT;
+      last = bs + (uint32_t)k - start + 1u;
+    }
+  }
+  if (inside) {
+    const int p = py_i * cam.W + px_i;
+    image[3 * p + 0] = fmaf(T, cam.bg[0], cr);
+    image[3 * p + 1] = fmaf(T, cam.bg[1], cg);
+    image[3 * p + 2] = fmaf(T, cam.bg[2], cb);
+    final_T[p] = T;
+    n_contrib[p] = last;
+  }
+  if (eval_count) {
+    const float tot = wave_sum_lane63((float)n_eval);
+    if ((tid & 63) == 63) atomicAdd(eval_count, (unsigned long long)(tot + 0.5f));
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// k-rbwd
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kRasterThreads) void k_rbwd(
+    uint32_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ ids, const float* __restrict__ means2d,
+    const float* __restrict__ conics, const float* __restrict__ opac, const float* __restrict__ colors,
+    DevCamera cam, int per_xcd, const float* __restrict__ final_T, const uint32_t* __restrict__ n_contrib,
+    const float* __restrict__ dL_dimage, float* __restrict__ g2d, unsigned long long* __restrict__ eval_count) {
+  __shared__ float4 s_a[kBatch];
+  __shared__ float4 s_b[kBatch];
+  __shared__ float s_c[kBatch];
+  __shared__ uint32_t s_id[kBatch];
+  __shared__ float s_acc[9][kBatch];
+  __shared__ uint32_t s_max;
+
+  const int tile = tile_of_block(blockIdx.x, per_xcd);
+  if (tile >= cam.tiles_x * cam.tiles_y) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int px_i = (tile % cam.tiles_x) * kTile + (tid & (kTile - 1));
+  const int py_i = (tile / cam.tiles_x) * kTile + (tid / kTile);
+  const bool inside = px_i < cam.W && py_i < cam.H;
+  const float px = (float)px_i + 0.5f, py = (float)py_i + 0.5f;
+  const uint32_t start = ranges[2 * tile];
+
+  float T = 1.0f, gr = 0.0f, gg = 0.0f, gb = 0.0f;
+  uint32_t nc = 0;
+  if (inside) {
+    const int p = py_i * cam.W + px_i;
+    T = final_T[p];
+    nc = n_contrib[p];
+    gr = dL_dimage[3 * p];
+    gg = dL_dimage[3 * p + 1];
+    gb = dL_dimage[3 * p + 2];
+  }
+  // g . S with S = (sum over splats behind) + T_final bg, carried as one scalar
+  float gS = T * ((gr * cam.bg[0] + gg * cam.bg[1]) + gb * cam.bg[2]);
+  if (tid == 0) s_max = 0;
+  __syncthreads();
+  if (nc) atomicMax(&s_max, nc);
+  __syncthreads();
+  const uint32_t max_nc = s_max;
+  uint32_t n_eval = 0;
+
+  for (uint32_t bend = max_nc; bend > 0;) {
+    const uint32_t bstart = bend > (uint32_t)kBatch ? bend - kBatch : 0u;
+    const int cnt = (int)(bend - bstart);
+    __syncthreads();
+    if (tid < cnt) {
+      const uint32_t e = bend - 1u - (uint32_t)tid;  // reversed: slot k holds entry bend-1-k
+      const uint32_t g = ids[start + e];
+      s_id[tid] = g;
+      load_record(g, n, means2d, conics, opac, colors, s_a[tid], s_b[tid], s_c[tid]);
+#pragma unroll
+      for (int c = 0; c < 9; ++c) s_acc[c][tid] = 0.0f;
+    }
+    __syncthreads();
+    for (int k = 0; k < cnt; ++k) {
+      const uint32_t e = bend - 1u - (uint32_t)k;
+      const bool active = e < nc;
+      if (!__any(active)) continue;
+      float v[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+      bool contrib = false;
+      if (active) {
+        const float4 a = s_a[k];
+        const float4 b = s_b[k];
+        const float dx = a.x - px, dy = a.y - py;
+        const SplatEval ev = eval_splat(dx, dy, a.z, b.x, a.w, b.y);
+        ++n_eval;
+        if (!ev.skip) {
+          contrib = true;
+          const float one_m = 1.0f - ev.alpha;
+          const float inv = 1.0f / one_m;
+          T = T * inv;  // T_i, the transmittance in front of this splat
+          const float cr = b.z, cg = b.w, cb = s_c[k];
+          const float gc = fmaf(gr, cr, fmaf(gg, cg, gb * cb));
+          const float g_alpha = fmaf(T, gc, -gS * inv);
+          const float wT = ev.alpha * T;
+          gS = fmaf(gc, wT, gS);
+          v[6] = wT * gr;
+          v[7] = wT * gg;
+          v[8] = wT * gb;
+          if (!ev.capped) {
+            v[5] = ev.G * g_alpha;
+            const float gsig = -ev.alpha * g_alpha;  // dL/dsigma
+            // sigma = A/2 dx^2 + C/2 dy^2 + B dx dy; A = 2 hA / log2e etc.
+            v[2] = 0.5f * gsig * dx * dx;
+            v[3] = gsig * dx * dy;
+            v[4] = 0.5f * gsig * dy * dy;
+            const float inv_l2e = 1.0f / kLog2e;
+            v[0] = gsig * (fmaf(2.0f * a.z, dx, b.x * dy) * inv_l2e);
+            v[1] = gsig * (fmaf(2.0f * a.w, dy, b.x * dx) * inv_l2e);
+          }
+        }
+      }
+      if (!__any(contrib)) continue;
+#pragma unroll
+      for (int c = 0; c < 9; ++c) {
+        const float s = wave_sum_lane63(v[c]);
+        if (lane == 63 && s != 0.0f) unsafeAtomicAdd(&s_acc[c][k], s);
+      }
+    }
+    __syncthreads();
+    if (tid < cnt && s_id[tid] < n) {
+      float* dst = g2d + (size_t)s_id[tid] * 9;
+#pragma unroll
+      for (int c = 0; c < 9; ++c) {
+        const float s = s_acc[c][tid];
+        if (s != 0.0f) unsafeAtomicAdd(dst + c, s);
+      }
+    }
+    bend = bstart;
+  }
+  if (eval_count) {
+    const float tot = wave_sum_lane63((float)n_eval);
+    if (lane == 63) atomicAdd(eval_count, (unsigned long long)(tot + 0.5f));
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// k-pbwd: chain rule from the 2D gradients (mean2d, conic, opacity, colour) to the raw
+// parameters (sections 1-4 of the PyTorch lesson, differentiated). One thread per Gaussian.
+// The decisions (culled, J clamps, det clamp) are the forward's: the fp32 projection is replayed
+// bit for bit. The chain itself runs in fp64: it is O(N) work, and in fp32 it loses up to three
+// digits for needle-like splats (inverting a near-singular 2x2) and for SH terms that cancel.
+// Scale and rotation gradients go through Q = J W R (2x3): Sigma' - 0.3 I = sum_j s_j^2 q_j q_j^T,
+// so dL/dl_j = 2 s_j^2 q_j^T G2 q_j, dL/dQ = 2 G2 Q S^2 and dL/dR = (J W)^T dL/dQ.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ void sh_basis_grad_f64(int degree, double x, double y, double z, double* B,
+                                                  double (*dB)[3]) {
+  const double s3 = 1.7320508075688772, s15 = 3.872983346207417, s5 = 2.23606797749979,
+               s15h = 1.9364916731037085, s358 = 2.091650066335189, s105 = 10.246950765959598,
+               s218 = 1.6201851746019651, s7h = 1.3228756555322954, s105h = 5.123475382979799,
+               s5h = 1.118033988749895;
+  for (int k = 0; k < 16; ++k) dB[k][0] = dB[k][1] = dB[k][2] = 0.0;
+  B[0] = 1.0;
+  if (degree < 1) return;
+  B[1] = s3 * y; dB[1][1] = s3;
+  B[2] = s3 * z; dB[2][2] = s3;
+  B[3] = s3 * x; dB[3][0] = s3;
+  if (degree < 2) return;
+  B[4] = s15 * x * y; dB[4][0] = s15 * y; dB[4][1] = s15 * x;
+  B[5] = s15 * y * z; dB[5][1] = s15 * z; dB[5][2] = s15 * y;
+  B[6] = s5h * (3.0 * z * z - 1.0); dB[6][2] = 3.0 * s5 * z;
+  B[7] = s15 * x * z; dB[7][0] = s15 * z; dB[7][2] = s15 * x;
+  B[8] = s15h * (x * x - y * y); dB[8][0] = s15 * x; dB[8][1] = -s15 * y;
+  if (degree < 3) return;
+  B[9] = s358 * y * (3.0 * x * x - y * y);
+  dB[9][0] = 6.0 * s358 * x * y; dB[9][1] = 3.0 * s358 * (x * x - y * y);
+  B[10] = s105 * x * y * z;
+  dB[10][0] = s105 * y * z; dB[10][1] = s105 * x * z; dB[10][2] = s105 * x * y;
+  B[11] = s218 * y * (5.0 * z * z - 1.0);
+  dB[11][1] = s218 * (5.0 * z * z - 1.0); dB[11][2] = 10.0 * s218 * y * z;
+  B[12] = s7h * z * (5.0 * z * z - 3.0);
+  dB[12][2] = s7h * (15.0 * z * z - 3.0);
+  B[13] = s218 * x * (5.0 * z * z - 1.0);
+  dB[13][0] = s218 * (5.0 * z * z - 1.0); dB[13][2] = 10.0 * s218 * x * z;
+  B[14] = s105h * z * (x * x - y * y);
+  dB[14][0] = 2.0 * s105h * x * z; dB[14][1] = -2.0 * s105h * y * z; dB[14][2] = s105h * (x * x - y * y);
+  B[15] = s358 * x * (x * x - 3.0 * y * y);
+  dB[15][0] = 3.0 * s358 * (x * x - y * y); dB[15][1] = -6.0 * s358 * x * y;
+}
+
+template <int DEG>
+__global__ __launch_bounds__(256) void k_pbwd(
+    int32_t n, const float* __restrict__ means, const float* __restrict__ log_scales, const float* __restrict__ quats,
+    const float* __restrict__ logits, const float* __restrict__ sh, DevCamera cam,
+    const uint32_t* __restrict__ tiles_touched, const float* __restrict__ g2d, float* __restrict__ d_means,
+    float* __restrict__ d_log_scales, float* __restrict__ d_quats, float* __restrict__ d_logits,
+    float* __restrict__ d_sh, float* __restrict__ d_means2d) {
+  constexpr int K = (DEG + 1) * (DEG + 1);
+  const int g = blockIdx.x * 256 + threadIdx.x;
+  if (g >= n) return;
+  double gm[3] = {0, 0, 0}, gl[3] = {0, 0, 0}, gq4[4] = {0, 0, 0, 0}, glogit = 0.0;
+  double gsh[K * 3];
+#pragma unroll
+  for (int i = 0; i < K * 3; ++i) gsh[i] = 0.0;
+  double G9[9];
+#pragma unroll
+  for (int c = 0; c < 9; ++c) G9[c] = (double)g2d[(size_t)g * 9 + c];
+
+  const bool drawn = tiles_touched[g] > 0;
+  if (drawn) {
+    const float m0f = means[3 * g], m1f = means[3 * g + 1], m2f = means[3 * g + 2];
+    const float l0f = log_scales[3 * g], l1f = log_scales[3 * g + 1], l2f = log_scales[3 * g + 2];
+    const float4 q4 = *reinterpret_cast<const float4*>(quats + 4 * g);
+    const float logitf = logits[g];
+    float shc[K * 3];
+#pragma unroll
+    for (int i = 0; i < K * 3; ++i) shc[i] = sh[(size_t)g * (K * 3) + i];
+    // the forward's decisions
+    const ProjF32 P32 = project_f32<DEG, false>(m0f, m1f, m2f, l0f, l1f, l2f, q4, logitf, shc, cam);
+
+    // ---- forward intermediates in fp64 ----
+    const double mu[3] = {m0f, m1f, m2f};
+    const double qw = q4.x, qx = q4.y, qy = q4.z, qz = q4.w;
+    const double qn_raw = sqrt(qw * qw + qx * qx + qy * qy + qz * qz);
+    const double qn = qn_raw > 1e-12 ? qn_raw : 1e-12;
+    const double w = qw / qn, x = qx / qn, y = qy / qn, z = qz / qn;
+    const double s[3] = {exp((double)l0f), exp((double)l1f), exp((double)l2f)};
+    const double o = 1.0 / (1.0 + exp(-(double)logitf));
+    double R[9];
+    R[0] = 1.0 - 2.0 * (y * y + z * z);
+    R[1] = 2.0 * (x * y - w * z);
+    R[2] = 2.0 * (x * z + w * y);
+    R[3] = 2.0 * (x * y + w * z);
+    R[4] = 1.0 - 2.0 * (x * x + z * z);
+    R[5] = 2.0 * (y * z - w * x);
+    R[6] = 2.0 * (x * z - w * y);
+    R[7] = 2.0 * (y * z + w * x);
+    R[8] = 1.0 - 2.0 * (x * x + y * y);
+    double W[9], w0[3];
+    for (int r = 0; r < 3; ++r) {
+      for (int c = 0; c < 3; ++c) W[r * 3 + c] = (double)cam.V[r * 4 + c];
+      w0[r] = (double)cam.V[r * 4 + 3];
+    }
+    double t[3];
+    for (int r = 0; r < 3; ++r) t[r] = W[r * 3] * mu[0] + W[r * 3 + 1] * mu[1] + W[r * 3 + 2] * mu[2] + w0[r];
+    const double tx = t[0], ty = t[1], tz = t[2];
+    const double fx = cam.fx, fy = cam.fy, cx = cam.cx, cy = cam.cy;
+    const double tfx = 0.5 * (double)cam.W / fx, tfy = 0.5 * (double)cam.H / fy;
+    const double lxl = -(cx / fx + 0.3 * tfx), lxh = ((double)cam.W - cx) / fx + 0.3 * tfx;
+    const double lyl = -(cy / fy + 0.3 * tfy), lyh = ((double)cam.H - cy) / fy + 0.3 * tfy;
+    const double xz = tx / tz, yz = ty / tz;
+    const double jx = tz * fmin(fmax(xz, lxl), lxh), jy = tz * fmin(fmax(yz, lyl), lyh);
+    const double iz = 1.0 / tz, iz2 = iz * iz;
+    const double J[6] = {fx * iz, 0.0, -fx * jx * iz2, 0.0, fy * iz, -fy * jy * iz2};
+    double JW[6], Q[6];
+    for (int a2 = 0; a2 < 2; ++a2)
+      for (int j = 0; j < 3; ++j) JW[a2 * 3 + j] = J[a2 * 3] * W[j] + J[a2 * 3 + 1] * W[3 + j] + J[a2 * 3 + 2] * W[6 + j];
+    for (int a2 = 0; a2 < 2; ++a2)
+      for (int j = 0; j < 3; ++j) Q[a2 * 3 + j] = JW[a2 * 3] * R[j] + JW[a2 * 3 + 1] * R[3 + j] + JW[a2 * 3 + 2] * R[6 + j];
+    double a = 0.3, b = 0.0, c = 0.3;
+    for (int j = 0; j < 3; ++j) {
+      const double s2 = s[j] * s[j];
+      a += s2 * Q[j] * Q[j];
+      b += s2 * Q[j] * Q[3 + j];
+      c += s2 * Q[3 + j] * Q[3 + j];
+    }
+    // Sigma_c = W Sigma W^T = (W R) S^2 (W R)^T, for J's dependence on t
+    double WR[9], Sc[9];
+    for (int i = 0; i < 3; ++i)
+      for (int j = 0; j < 3; ++j) WR[i * 3 + j] = W[i * 3] * R[j] + W[i * 3 + 1] * R[3 + j] + W[i * 3 + 2] * R[6 + j];
+    for (int i = 0; i < 3; ++i)
+      for (int k = 0; k < 3; ++k)
+        Sc[i * 3 + k] = s[0] * s[0] * WR[i * 3] * WR[k * 3] + s[1] * s[1] * WR[i * 3 + 1] * WR[k * 3 + 1] +
+                        s[2] * s[2] * WR[i * 3 + 2] * WR[k * 3 + 2];
+
+    // ---- conic (A, B, C) = (c, -b, a) / det  ->  dL/d(a, b, c) ----
+    const double gA = G9[2], gB = G9[3], gC = G9[4];
+    double ga, gb, gc;
+    if (!P32.det_clamped) {
+      const double id = 1.0 / (a * c - b * b);
+      const double PA = c * id, PB = -b * id, PC = a * id;
+      ga = -(gA * PA * PA + gB * PA * PB + gC * PB * PB);
+      gc = -(gA * PB * PB + gB * PB * PC + gC * PC * PC);
+      gb = -2.0 * (gA * PA * PB + 0.5 * gB * (PA * PC + PB * PB) + gC * PB * PC);
+    } else {
+      ga = gC * 1e10;
+      gb = -gB * 1e10;
+      gc = gA * 1e10;
+    }
+    const double G2[4] = {ga, 0.5 * gb, 0.5 * gb, gc};
+
+    // ---- scales and rotation through Q ----
+    double gR[9];
+    for (int j = 0; j < 3; ++j) {
+      const double q0 = Q[j], q1 = Q[3 + j];
+      const double u0 = G2[0] * q0 + G2[1] * q1, u1 = G2[2] * q0 + G2[3] * q1;
+      const double s2 = s[j] * s[j];
+      gl[j] = 2.0 * s2 * (q0 * u0 + q1 * u1);
+      const double gQ0 = 2.0 * s2 * u0, gQ1 = 2.0 * s2 * u1;
+      for (int i = 0; i < 3; ++i) gR[i * 3 + j] = JW[i] * gQ0 + JW[3 + i] * gQ1;
+    }
+    gq4[0] = 2.0 * (-z * gR[1] + y * gR[2] + z * gR[3] - x * gR[5] - y * gR[6] + x * gR[7]);
+    gq4[1] = 2.0 * (y * gR[1] + z * gR[2] + y * gR[3] - 2.0 * x * gR[4] - w * gR[5] + z * gR[6] + w * gR[7] -
+                    2.0 * x * gR[8]);
+    gq4[2] = 2.0 * (-2.0 * y * gR[0] + x * gR[1] + w * gR[2] + x * gR[3] + z * gR[5] - w * gR[6] + z * gR[7] -
+                    2.0 * y * gR[8]);
+    gq4[3] = 2.0 * (-2.0 * z * gR[0] - w * gR[1] + x * gR[2] + w * gR[3] - 2.0 * z * gR[4] + y * gR[5] +
+                    x * gR[6] + y * gR[7]);
+    {
+      const double qh[4] = {w, x, y, z};
+      if (qn_raw > 1e-12) {
+        const double dot = w * gq4[0] + x * gq4[1] + y * gq4[2] + z * gq4[3];
+        for (int j = 0; j < 4; ++j) gq4[j] = (gq4[j] - qh[j] * dot) / qn;
+      } else {
+        for (int j = 0; j < 4; ++j) gq4[j] = gq4[j] / qn;
+      }
+    }
+
+    // ---- the camera-space mean: through J (dL/dJ = 2 G2 J Sc) and through mean2d ----
+    double GJ[6];
+    for (int p2 = 0; p2 < 2; ++p2)
+      for (int j = 0; j < 3; ++j) GJ[p2 * 3 + j] = G2[p2 * 2] * J[j] + G2[p2 * 2 + 1] * J[3 + j];
+    double gJ[6];
+    for (int p2 = 0; p2 < 2; ++p2)
+      for (int j = 0; j < 3; ++j)
+        gJ[p2 * 3 + j] = 2.0 * (GJ[p2 * 3] * Sc[j] + GJ[p2 * 3 + 1] * Sc[3 + j] + GJ[p2 * 3 + 2] * Sc[6 + j]);
+    double gt[3] = {0.0, 0.0, 0.0};
+    gt[2] -= (gJ[0] * fx + gJ[4] * fy) * iz2;
+    {
+      const double dxx = P32.clamp_x ? 0.0 : 1.0, dxz = P32.clamp_x ? jx * iz : 0.0;
+      gt[0] += gJ[2] * (-fx * iz2) * dxx;
+      gt[2] += gJ[2] * (2.0 * fx * jx * iz2 * iz - fx * dxz * iz2);
+      const double dyy = P32.clamp_y ? 0.0 : 1.0, dyz = P32.clamp_y ? jy * iz : 0.0;
+      gt[1] += gJ[5] * (-fy * iz2) * dyy;
+      gt[2] += gJ[5] * (2.0 * fy * jy * iz2 * iz - fy * dyz * iz2);
+    }
+    gt[0] += G9[0] * fx * iz;
+    gt[2] -= G9[0] * fx * tx * iz2;
+    gt[1] += G9[1] * fy * iz;
+    gt[2] -= G9[1] * fy * ty * iz2;
+    for (int j = 0; j < 3; ++j) gm[j] = W[j] * gt[0] + W[3 + j] * gt[1] + W[6 + j] * gt[2];
+
+    // ---- log-scales, opacity, colour ----
+    glogit = o * (1.0 - o) * G9[5];
+    if (DEG == 0) {
+      gsh[0] = G9[6]; gsh[1] = G9[7]; gsh[2] = G9[8];
+    } else {
+      double C[3];
+      for (int j = 0; j < 3; ++j) C[j] = -(W[j] * w0[0] + W[3 + j] * w0[1] + W[6 + j] * w0[2]);
+      const double d[3] = {mu[0] - C[0], mu[1] - C[1], mu[2] - C[2]};
+      const double dnr = sqrt(d[0] * d[0] + d[1] * d[1] + d[2] * d[2]);
+      const double dn = dnr > 1e-12 ? dnr : 1e-12;
+      const double u[3] = {d[0] / dn, d[1] / dn, d[2] / dn};
+      double B[16], dB[16][3];
+      sh_basis_grad_f64(DEG, u[0], u[1], u[2], B, dB);
+      double gd[3] = {0.0, 0.0, 0.0};
+#pragma unroll
+      for (int l = 0; l < K; ++l)
+#pragma unroll
+        for (int ch = 0; ch < 3; ++ch) {
+          gsh[l * 3 + ch] = B[l] * G9[6 + ch];
+          if (l > 0) {
+            const double wgt = (double)shc[l * 3 + ch] * G9[6 + ch];
+            for (int j = 0; j < 3; ++j) gd[j] += wgt * dB[l][j];
+          }
+        }
+      const double dot = u[0] * gd[0] + u[1] * gd[1] + u[2] * gd[2];
+      for (int j = 0; j < 3; ++j) gm[j] += (gd[j] - u[j] * dot) / dn;
+    }
+  }
+  for (int j = 0; j < 3; ++j) d_means[3 * g + j] = (float)gm[j];
+  for (int j = 0; j < 3; ++j) d_log_scales[3 * g + j] = (float)gl[j];
+  *reinterpret_cast<float4*>(d_quats + 4 * g) = make_float4((float)gq4[0], (float)gq4[1], (float)gq4[2], (float)gq4[3]);
+  d_logits[g] = (float)glogit;
+#pragma unroll
+  for (int i = 0; i < K * 3; ++i) d_sh[(size_t)g * (K * 3) + i] = (float)gsh[i];
+  if (d_means2d) {
+    d_means2d[2 * g] = drawn ? (float)G9[0] : 0.0f;
+    d_means2d[2 * g + 1] = drawn ? (float)G9[1] : 0.0f;
+  }
+}
+
+__global__ void k_fill_zero(float* __restrict__ p, size_t count) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < count; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0.0f;
+}
+
+}  // namespace
+}  // namespace gs
+
+using namespace gs;
+
+namespace {
+bool proj_ok(const gs_projected* p) {
+  return p && p->d_means2d && p->d_conics && p->d_depths && p->d_opacities && p->d_colors && p->d_radii &&
+         p->d_tiles_touched;
+}
+int per_xcd_for(const gs_camera* cam) {
+  const int ntiles = ((cam->width + 15) / 16) * ((cam->height + 15) / 16);
+  return (ntiles + 7) / 8;
+}
+}  // namespace
+
+extern "C" gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const gs_camera* cam,
+                                      const uint32_t* d_ids, const uint32_t* d_tile_ranges, float* d_image,
+                                      float* d_final_T, uint32_t* d_n_contrib, uint64_t* d_eval_count,
+                                      void* stream) {
+  std::string why;
+  if (n < 0) return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: n < 0");
+  if (!valid_camera(cam, &why)) return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: " + why);
+  if (!d_tile_ranges || !d_image || !d_final_T || !d_n_contrib)
+    return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: NULL output or ranges");
+  if (n > 0 && (!proj_ok(proj) || !d_ids)) return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: NULL input");
+  const int64_t ntiles = (int64_t)((cam->width + 15) / 16) * ((cam->height + 15) / 16);
+  if (ntiles > ((int64_t)1 << 24)) return set_error(GS_ERR_LIMIT, "gs_rasterize_fwd: more than 2^24 tiles");
+  const int per_xcd = per_xcd_for(cam);
+  const DevCamera dc = to_dev(*cam);
+  hipStream_t s = (hipStream_t)stream;
+  {
+    TimedScope ts("blend", s);
+    hipLaunchKernelGGL(k_blend, dim3(8 * per_xcd), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges, d_ids,
+                       n > 0 ? proj->d_means2d : nullptr, n > 0 ? proj->d_conics : nullptr,
+                       n > 0 ? proj->d_opacities : nullptr, n > 0 ? proj->d_colors : nullptr, dc, per_xcd, d_image,
+                       d_final_T, d_n_contrib, (unsigned long long*)d_eval_count);
+  }
+  return check_launch("gs_rasterize_fwd");
+}
+
+extern "C" size_t gs_bwd_workspace_bytes(int32_t n) { return n <= 0 ? 256 : align_up((size_t)n * 9 * 4, 256); }
+
+extern "C" gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float* d_means,
+                                      const float* d_log_scales, const float* d_quats,
+                                      const float* d_opacity_logits, const float* d_sh, const gs_camera* cam,
+                                      const gs_projected* proj, const uint32_t* d_ids,
+                                      const uint32_t* d_tile_ranges, const float* d_final_T,
+                                      const uint32_t* d_n_contrib, const float* d_dL_dimage, void* d_workspace,
+                                      size_t workspace_bytes, float* d_grad_means, float* d_grad_log_scales,
+                                      float* d_grad_quats, float* d_grad_opacity_logits, float* d_grad_sh,
+                                      float* d_grad_means2d, uint64_t* d_eval_count, void* stream) {
+  std::string why;
+  if (n < 0) return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_bwd: n < 0");
+  if (sh_degree < 0 || sh_degree > GS_MAX_SH_DEGREE)
+    return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_bwd: sh_degree not in 0..3");
+  if (!valid_camera(cam, &why)) return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_bwd: " + why);
+  if (n == 0) return GS_OK;
+  if (!d_means || !d_log_scales || !d_quats || !d_opacity_logits || !d_sh || !proj_ok(proj) || !d_ids ||
+      !d_tile_ranges || !d_final_T || !d_n_contrib || !d_dL_dimage || !d_grad_means || !d_grad_log_scales ||
+      !d_grad_quats || !d_grad_opacity_logits || !d_grad_sh)
+    return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_bwd: NULL pointer with n > 0");
+  if (!d_workspace || workspace_bytes < gs_bwd_workspace_bytes(n))
+    return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_bwd: workspace smaller than gs_bwd_workspace_bytes()");
+  if (((reinterpret_cast<uintptr_t>(d_quats) | reinterpret_cast<uintptr_t>(d_grad_quats)) & 15) != 0)
+    return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_bwd: quaternion arrays must be 16-byte aligned");
+  const int64_t ntiles = (int64_t)((cam->width + 15) / 16) * ((cam->height + 15) / 16);
+  if (ntiles > ((int64_t)1 << 24)) return set_error(GS_ERR_LIMIT, "gs_rasterize_bwd: more than 2^24 tiles");
+  const int per_xcd = per_xcd_for(cam);
+  const DevCamera dc = to_dev(*cam);
+  hipStream_t s = (hipStream_t)stream;
+  float* g2d = (float*)d_workspace;
+  {
+    TimedScope ts("bwd_zero", s);
+    const size_t count = (size_t)n * 9;
+    const unsigned blocks = (unsigned)((count + 255) / 256 < 4096 ? (count + 255) / 256 : 4096);
+    hipLaunchKernelGGL(k_fill_zero, dim3(blocks), dim3(256), 0, s, g2d, count);
+  }
+  {
+    TimedScope ts("rbwd", s);
+    hipLaunchKernelGGL(k_rbwd, dim3(8 * per_xcd), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges, d_ids,
+                       proj->d_means2d,
+                       proj->d_conics, proj->d_opacities, proj->d_colors, dc, per_xcd, d_final_T, d_n_contrib,
+                       d_dL_dimage, g2d, (unsigned long long*)d_eval_count);
+  }
+  {
+    TimedScope ts("pbwd", s);
+    const dim3 grid((n + 255) / 256), block(256);
+#define GS_LAUNCH_PBWD(D)                                                                                       \
+  hipLaunchKernelGGL(k_pbwd<D>, grid, block, 0, s, n, d_means, d_log_scales, d_quats, d_opacity_logits, d_sh, dc, \
+                     proj->d_tiles_touched, g2d, d_grad_means, d_grad_log_scales, d_grad_quats,                 \
+                     d_grad_opacity_logits, d_grad_sh, d_grad_means2d)
+    switch (sh_degree) {
+      case 0: GS_LAUNCH_PBWD(0); break;
+      case 1: GS_LAUNCH_PBWD(1); break;
+      case 2: GS_LAUNCH_PBWD(2); break;
+      default: GS_LAUNCH_PBWD(3); break;
+    }
+#undef GS_LAUNCH_PBWD
+  }
+  return check_launch("gs_rasterize_bwd");
+}

@@ -1,0 +1,283 @@
+"""ctypes binding of libgs_hip.so (include/gs.h): argument marshalling only.
+
+Every function here has the name of the C entry point it calls and does nothing but convert
+torch CUDA tensors (device memory) and a torch stream into pointers, call the library and turn a
+non-OK status into an exception. All arithmetic runs in the HIP kernels; there is no fallback:
+if the library is missing, or no GPU is present, calls raise.
+
+``Pipeline`` owns the device buffers of one scene/resolution and chains the entry points for a
+forward+backward iteration (allocation and call order only).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch  # loads the HIP runtime the library binds to (same libamdhip64 soname)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgs_hip.so")
+
+GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_LIMIT, GS_ERR_DEVICE = 0, 1, 2, 3, 4
+
+
+class GsError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{status_name(status)}: {msg}")
+        self.status = status
+
+
+class GsCamera(ctypes.Structure):
+    _fields_ = [("viewmat", ctypes.c_float * 16), ("fx", ctypes.c_float), ("fy", ctypes.c_float),
+                ("cx", ctypes.c_float), ("cy", ctypes.c_float), ("width", ctypes.c_int32),
+                ("height", ctypes.c_int32), ("near_plane", ctypes.c_float), ("background", ctypes.c_float * 3)]
+
+
+class GsProjected(ctypes.Structure):
+    _fields_ = [("d_means2d", ctypes.c_void_p), ("d_conics", ctypes.c_void_p), ("d_depths", ctypes.c_void_p),
+                ("d_opacities", ctypes.c_void_p), ("d_colors", ctypes.c_void_p), ("d_radii", ctypes.c_void_p),
+                ("d_tiles_touched", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load():
+    """Load libgs_hip.so (built by gaussian_splatting_tile_gs_amd/build.py). Raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise GsError(GS_ERR_DEVICE, f"{LIB_PATH} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    cam_p, proj_p = ctypes.POINTER(GsCamera), ctypes.POINTER(GsProjected)
+    sig = {
+        "gs_project": (i32, [i32, i32, P, P, P, P, P, cam_p, proj_p, P]),
+        "gs_bin_workspace_bytes": (sz, [i32, i64, cam_p]),
+        "gs_bin_and_sort": (i32, [i32, proj_p, cam_p, P, sz, i64, P, P, P, ctypes.POINTER(ctypes.c_int64), P]),
+        "gs_rasterize_fwd": (i32, [i32, proj_p, cam_p, P, P, P, P, P, P, P]),
+        "gs_bwd_workspace_bytes": (sz, [i32]),
+        "gs_rasterize_bwd": (i32, [i32, i32, P, P, P, P, P, cam_p, proj_p, P, P, P, P, P, P, sz, P, P, P, P, P, P, P, P]),
+        "gs_loss_l1": (i32, [i32, i32, P, P, P, P, P]),
+        "gs_status_string": (ctypes.c_char_p, [i32]),
+        "gs_last_error": (ctypes.c_char_p, []),
+        "gs_timing_enable": (i32, [i32]),
+        "gs_timing_collect": (i32, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), i32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_name(status: int) -> str:
+    try:
+        return load().gs_status_string(status).decode()
+    except GsError:
+        return f"status {status}"
+
+
+def _check(status: int, allow=()):
+    if status != GS_OK and status not in allow:
+        raise GsError(status, load().gs_last_error().decode())
+    return status
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise GsError(GS_ERR_INVALID_ARG, "expected a contiguous CUDA tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_camera(cam: dict) -> GsCamera:
+    """GsCamera from a camera dict (viewmat [4,4], fx, fy, cx, cy, width, height, near, background)."""
+    c = GsCamera()
+    v = np.asarray(cam["viewmat"], np.float32).reshape(16)
+    for i in range(16):
+        c.viewmat[i] = float(v[i])
+    c.fx, c.fy, c.cx, c.cy = float(cam["fx"]), float(cam["fy"]), float(cam["cx"]), float(cam["cy"])
+    c.width, c.height = int(cam["width"]), int(cam["height"])
+    c.near_plane = float(cam.get("near", 0.01))
+    bg = cam.get("background", (0.0, 0.0, 0.0))
+    for i in range(3):
+        c.background[i] = float(bg[i])
+    return c
+
+
+# ---- the entry points -------------------------------------------------------------------------
+def gs_project(n, sh_degree, means, log_scales, quats, opacity_logits, sh, cam: GsCamera, out: "Projected",
+               stream=None):
+    return _check(load().gs_project(n, sh_degree, _ptr(means), _ptr(log_scales), _ptr(quats), _ptr(opacity_logits),
+                                    _ptr(sh), ctypes.byref(cam), ctypes.byref(out.struct()), _stream(stream)))
+
+
+def gs_bin_workspace_bytes(n, pair_capacity, cam: GsCamera) -> int:
+    return int(load().gs_bin_workspace_bytes(n, pair_capacity, ctypes.byref(cam)))
+
+
+def gs_bin_and_sort(n, proj: "Projected", cam: GsCamera, workspace, pair_capacity, keys, ids, tile_ranges,
+                    stream=None):
+    """Returns (status, P); status is GS_OK or GS_ERR_CAPACITY (then P is the count needed)."""
+    P = ctypes.c_int64(0)
+    st = _check(load().gs_bin_and_sort(n, ctypes.byref(proj.struct()), ctypes.byref(cam), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), pair_capacity, _ptr(keys),
+                                       _ptr(ids), _ptr(tile_ranges), ctypes.byref(P), _stream(stream)),
+                allow=(GS_ERR_CAPACITY,))
+    return st, int(P.value)
+
+
+def gs_rasterize_fwd(n, proj: "Projected", cam: GsCamera, ids, tile_ranges, image, final_T, n_contrib,
+                     eval_count=None, stream=None):
+    return _check(load().gs_rasterize_fwd(n, ctypes.byref(proj.struct()), ctypes.byref(cam), _ptr(ids),
+                                          _ptr(tile_ranges), _ptr(image), _ptr(final_T), _ptr(n_contrib),
+                                          _ptr(eval_count), _stream(stream)))
+
+
+def gs_bwd_workspace_bytes(n) -> int:
+    return int(load().gs_bwd_workspace_bytes(n))
+
+
+def gs_rasterize_bwd(n, sh_degree, means, log_scales, quats, opacity_logits, sh, cam: GsCamera, proj: "Projected",
+                     ids, tile_ranges, final_T, n_contrib, dL_dimage, workspace, grad_means, grad_log_scales,
+                     grad_quats, grad_opacity_logits, grad_sh, grad_means2d=None, eval_count=None, stream=None):
+    return _check(load().gs_rasterize_bwd(
+        n, sh_degree, _ptr(means), _ptr(log_scales), _ptr(quats), _ptr(opacity_logits), _ptr(sh), ctypes.byref(cam),
+        ctypes.byref(proj.struct()), _ptr(ids), _ptr(tile_ranges), _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(grad_means), _ptr(grad_log_scales),
+        _ptr(grad_quats), _ptr(grad_opacity_logits), _ptr(grad_sh), _ptr(grad_means2d), _ptr(eval_count),
+        _stream(stream)))
+
+
+def gs_loss_l1(width, height, image, target, dL_dimage, loss=None, stream=None):
+    return _check(load().gs_loss_l1(width, height, _ptr(image), _ptr(target), _ptr(dL_dimage), _ptr(loss),
+                                    _stream(stream)))
+
+
+def gs_timing_enable(on: bool):
+    return _check(load().gs_timing_enable(1 if on else 0))
+
+
+def gs_timing_collect(max_records=4096):
+    names = (ctypes.c_char_p * max_records)()
+    ms = (ctypes.c_float * max_records)()
+    k = load().gs_timing_collect(names, ms, max_records)
+    return [(names[i].decode(), float(ms[i])) for i in range(k)]
+
+
+# ---- buffers ------------------------------------------------------------------------------------
+@dataclass
+class Projected:
+    means2d: torch.Tensor
+    conics: torch.Tensor
+    depths: torch.Tensor
+    opacities: torch.Tensor
+    colors: torch.Tensor
+    radii: torch.Tensor
+    tiles_touched: torch.Tensor
+
+    @staticmethod
+    def empty(n, device="cuda"):
+        f = dict(device=device, dtype=torch.float32)
+        return Projected(torch.empty(n, 2, **f), torch.empty(n, 3, **f), torch.empty(n, **f), torch.empty(n, **f),
+                         torch.empty(n, 3, **f), torch.empty(n, 2, device=device, dtype=torch.int32),
+                         torch.empty(n, device=device, dtype=torch.int32))
+
+    def struct(self) -> GsProjected:
+        s = GsProjected()
+        for f in ("means2d", "conics", "depths", "opacities", "colors", "radii", "tiles_touched"):
+            setattr(s, "d_" + f, getattr(self, f).data_ptr())
+        self._keep = s
+        return s
+
+
+def scene_to_device(scene: dict, device="cuda"):
+    """Raw parameters of a scene dict as contiguous fp32 CUDA tensors."""
+    out = {}
+    for k in ("means", "log_scales", "quats", "opacity_logits", "sh"):
+        out[k] = torch.as_tensor(np.ascontiguousarray(scene[k], dtype=np.float32)).to(device).contiguous()
+    out["sh_degree"] = int(scene.get("sh_degree", 0))
+    out["n"] = int(out["means"].shape[0])
+    return out
+
+
+class Pipeline:
+    """Device buffers for one scene at one image size, and the entry points in iteration order."""
+
+    def __init__(self, params: dict, width: int, height: int, pair_capacity: int = 1 << 20, device="cuda"):
+        self.p = params
+        self.n = params["n"]
+        self.width, self.height = width, height
+        self.device = device
+        self.tiles = ((width + 15) // 16) * ((height + 15) // 16)
+        self.proj = Projected.empty(self.n, device)
+        self.image = torch.empty(height, width, 3, device=device)
+        self.final_T = torch.empty(height, width, device=device)
+        self.n_contrib = torch.empty(height, width, device=device, dtype=torch.int32)
+        self.dL_dimage = torch.zeros(height, width, 3, device=device)
+        self.ranges = torch.empty(self.tiles, 2, device=device, dtype=torch.int32)
+        self.bwd_ws = torch.empty(gs_bwd_workspace_bytes(self.n), device=device, dtype=torch.uint8)
+        K = (params["sh_degree"] + 1) ** 2
+        f = dict(device=device, dtype=torch.float32)
+        self.grads = {"means": torch.empty(self.n, 3, **f), "log_scales": torch.empty(self.n, 3, **f),
+                      "quats": torch.empty(self.n, 4, **f), "opacity_logits": torch.empty(self.n, **f),
+                      "sh": torch.empty(self.n, K, 3, **f), "means2d": torch.empty(self.n, 2, **f)}
+        self.num_pairs = 0
+        self._alloc_pairs(pair_capacity)
+
+    def _alloc_pairs(self, cap):
+        self.capacity = int(cap)
+        self.keys = torch.empty(max(self.capacity, 1), device=self.device, dtype=torch.int64)
+        self.ids = torch.empty(max(self.capacity, 1), device=self.device, dtype=torch.int32)
+        cam0 = GsCamera()
+        cam0.width, cam0.height = self.width, self.height
+        self.bin_ws = torch.empty(gs_bin_workspace_bytes(self.n, self.capacity, cam0), device=self.device,
+                                  dtype=torch.uint8)
+
+    def project(self, cam: GsCamera, stream=None):
+        p = self.p
+        gs_project(self.n, p["sh_degree"], p["means"], p["log_scales"], p["quats"], p["opacity_logits"], p["sh"],
+                   cam, self.proj, stream)
+
+    def bin(self, cam: GsCamera, stream=None):
+        st, P = gs_bin_and_sort(self.n, self.proj, cam, self.bin_ws, self.capacity, self.keys, self.ids,
+                                self.ranges, stream)
+        if st == GS_ERR_CAPACITY:
+            self._alloc_pairs(int(P * 1.25) + 1024)
+            st, P = gs_bin_and_sort(self.n, self.proj, cam, self.bin_ws, self.capacity, self.keys, self.ids,
+                                    self.ranges, stream)
+        self.num_pairs = P
+        return P
+
+    def forward(self, cam: GsCamera, eval_count=None, stream=None):
+        gs_rasterize_fwd(self.n, self.proj, cam, self.ids, self.ranges, self.image, self.final_T, self.n_contrib,
+                         eval_count, stream)
+
+    def loss_l1(self, target, loss=None, stream=None):
+        gs_loss_l1(self.width, self.height, self.image, target, self.dL_dimage, loss, stream)
+
+    def backward(self, cam: GsCamera, dL_dimage=None, eval_count=None, stream=None):
+        p, g = self.p, self.grads
+        gs_rasterize_bwd(self.n, p["sh_degree"], p["means"], p["log_scales"], p["quats"], p["opacity_logits"],
+                         p["sh"], cam, self.proj, self.ids, self.ranges, self.final_T, self.n_contrib,
+                         self.dL_dimage if dL_dimage is None else dL_dimage, self.bwd_ws, g["means"], g["log_scales"],
+                         g["quats"], g["opacity_logits"], g["sh"], g["means2d"], eval_count, stream)
+
+    def iteration(self, cam: GsCamera, target, stream=None):
+        """One fwd+bwd iteration: project, bin+sort, blend, L1 gradient, backward."""
+        self.project(cam, stream)
+        self.bin(cam, stream)
+        self.forward(cam, stream=stream)
+        self.loss_l1(target, stream=stream)
+        self.backward(cam, stream=stream)

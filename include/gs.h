@@ -1,0 +1,192 @@
+/*
+ * gs.h -- C ABI of the MI355X (gfx950) tile-based 3D Gaussian Splatting rasterizer.
+ *
+ * Method: "Gaussian splatting in PyTorch" (coderigor.dev/lessons/py-gaussian-splatting), whose
+ * sections 1-6 define what is computed: raw parameters and their activations (section 1),
+ * Sigma = R S S^T R^T (section 2), the world->camera transform and EWA projection with the
+ * widened-frustum clamp (section 3), the eps2d dilation, conic and radius (section 4), the
+ * front-to-back blend with early termination (section 5) and the backward (section 6). The tile
+ * pipeline -- project, count, emit, sort, range, blend -- is the one of "SplatRs: The Week the
+ * Gap Closed" (section "Throughput: the tile rasterizer"); the backward walks each tile back to
+ * front and recovers the transmittance by division (section 6 of the PyTorch lesson).
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named d_* are device pointers (HBM of the current HIP device), h_* host pointers.
+ *    Arrays are contiguous, row-major, fp32 unless typed otherwise. The caller allocates and owns
+ *    every buffer; the library never frees or retains a caller pointer after a call returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls enqueue work on
+ *    it and return without waiting, except gs_bin_and_sort, which waits once for the pair count.
+ *  - Every call returns a gs_status; on anything but GS_OK, gs_last_error() describes it and no
+ *    output has been written past what the status documents. No exception crosses the ABI.
+ *  - Calls with disjoint buffers may run concurrently on different streams.
+ *  - Image layout: pixel (i, j) is row i, column j and is sampled at (j + 0.5, i + 0.5);
+ *    images are [height, width, 3]; tiles are 16 x 16 pixels, tile id = ty * tiles_x + tx with
+ *    tiles_x = ceil(width / 16), tiles_y = ceil(height / 16).
+ */
+#ifndef GS_H
+#define GS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GS_TILE_SIZE 16
+#define GS_MAX_SH_DEGREE 3
+
+typedef enum gs_status {
+  GS_OK = 0,
+  GS_ERR_INVALID_ARG = 1, /* bad size, NULL pointer, degree, or a non-finite camera */
+  GS_ERR_CAPACITY = 2,    /* the pair buffers are too small: *h_num_pairs holds the need */
+  GS_ERR_LIMIT = 3,       /* a size beyond what the kernels index (pairs >= 2^31, tiles > 2^24) */
+  GS_ERR_DEVICE = 4       /* a HIP runtime error; gs_last_error() has its text */
+} gs_status;
+
+/* Pinhole camera with OpenCV axes (+x right, +y down, +z forward): section 3 of the PyTorch
+ * lesson takes a world->camera viewmat [4,4] and intrinsics K. Read on the host only. */
+typedef struct gs_camera {
+  float viewmat[16];   /* row-major [R | t; 0 0 0 1], world -> camera */
+  float fx, fy, cx, cy; /* intrinsics in pixels (cx = width/2 centres the image) */
+  int32_t width, height;
+  float near_plane;    /* Gaussians with camera z <= near_plane are culled (0.01 typical) */
+  float background[3]; /* composited with the final transmittance */
+} gs_camera;
+
+/* Projected records, structure of arrays of length n, written by gs_project. A Gaussian is
+ * drawn iff tiles_touched > 0 (then radii > 0). Undefined projections (camera z <= near, or a
+ * non-finite input or derived value) are all zeros; defined but undrawn ones (opacity < 1/255,
+ * or no tile on screen) keep their projected values with radii = (0, 0), tiles_touched = 0. */
+typedef struct gs_projected {
+  float* d_means2d;          /* [n,2] pixel coordinates of the mean (not clamped) */
+  float* d_conics;           /* [n,3] (A, B, C) = inverse of the dilated 2D covariance */
+  float* d_depths;           /* [n]   camera-space z */
+  float* d_opacities;        /* [n]   sigmoid(logit) */
+  float* d_colors;           /* [n,3] sum_lm k_lm B_lm(view direction); degree 0: the RGB */
+  int32_t* d_radii;          /* [n,2] ceil(k sqrt(Sigma'_xx)), ceil(k sqrt(Sigma'_yy)) */
+  uint32_t* d_tiles_touched; /* [n]   tiles of the tile rectangle */
+} gs_projected;
+
+/*
+ * gs_project -- activations, covariance, EWA projection, culling, conic, radius, tile count and
+ * colour for every Gaussian (sections 1-4 of the PyTorch lesson).
+ *   q = quat / max(|quat|, 1e-12) (w, x, y, z); s = exp(log_scale); o = 1 / (1 + exp(-logit));
+ *   Sigma = M M^T, M = R(q) diag(s); t = W mean + w0; Sigma_c = W Sigma W^T;
+ *   J = [[fx/z, 0, -fx x~/z^2], [0, fy/z, -fy y~/z^2]] with x~/z, y~/z clamped to the view
+ *   widened by 0.3 tan(half FoV) per side; Sigma' = J Sigma_c J^T + 0.3 I = [[a, b], [b, c]];
+ *   conic = (c, -b, a) / max(ac - b^2, 1e-10); mean2d = (fx x/z + cx, fy y/z + cy);
+ *   k = min(3.33, sqrt(2 ln(255 o))), radii = ceil(k sqrt(a)), ceil(k sqrt(c)) (opacity-aware
+ *   extent: alpha < 1/255 outside it); tile rectangle [floor((mean2d - r)/16),
+ *   ceil((mean2d + r)/16)) clamped to the grid; colour from real SH of degree sh_degree, scaled
+ *   so that the degree-0 basis is 1, at the unit direction from the camera centre to the mean.
+ *   exp and log are evaluated with a fixed written-out fp32 algorithm (Cody-Waite exp, atanh-
+ *   series log), so radii, rectangles and tile counts are reproducible bit for bit.
+ * Inputs (device, fp32): d_means [n,3], d_log_scales [n,3], d_quats [n,4] (w,x,y,z, any norm),
+ *   d_opacity_logits [n], d_sh [n, (sh_degree+1)^2, 3] coefficient-major.
+ * Output: every array of *out, length n.
+ * Errors: GS_ERR_INVALID_ARG for n < 0, a NULL pointer with n > 0, sh_degree outside 0..3,
+ *   width/height <= 0, fx/fy <= 0 or a non-finite camera field.
+ */
+gs_status gs_project(int32_t n, int32_t sh_degree, const float* d_means, const float* d_log_scales,
+                     const float* d_quats, const float* d_opacity_logits, const float* d_sh,
+                     const gs_camera* cam, const gs_projected* out, void* stream);
+
+/*
+ * gs_bin_and_sort -- count, emit, sort and range ("project, count, emit, sort, range" of the
+ * SplatRs tile rasterizer). For every drawn Gaussian i and every tile (tx, ty) of its rectangle
+ * it forms the key (ty * tiles_x + tx) << 32 | float_bits(depth_i) and the value i, sorts the
+ * pairs by key, keeping equal keys in ascending i (stable), and writes per tile the range
+ * [start, end) of its pairs in the sorted list ((0, 0) for an empty tile).
+ * Implementation: a stable LSD radix sort of the Gaussians by depth, a prefix scan of the tile
+ * counts in depth order, emission of (tile, i) pairs in that order, and a stable LSD radix sort
+ * of the pairs by tile id (Onesweep-style single-pass passes with decoupled look-back).
+ * Inputs: n and proj (from gs_project with the same camera); d_workspace of at least
+ *   gs_bin_workspace_bytes(n, pair_capacity, cam) bytes (device, 256-byte aligned, contents
+ *   need not persist between calls); pair_capacity = length of d_keys and d_ids.
+ * Outputs: d_keys [P] uint64, d_ids [P] uint32, d_tile_ranges [tiles, 2] uint32,
+ *   *h_num_pairs = P (host). d_keys doubles as scratch during the call.
+ * Waits on `stream` once, to read P. If P > pair_capacity it returns GS_ERR_CAPACITY with
+ *   *h_num_pairs = P and writes nothing to d_keys, d_ids or d_tile_ranges.
+ * Errors: GS_ERR_INVALID_ARG (as gs_project, or a workspace below the size needed),
+ *   GS_ERR_LIMIT (P >= 2^31 or more than 2^24 tiles).
+ */
+size_t gs_bin_workspace_bytes(int32_t n, int64_t pair_capacity, const gs_camera* cam);
+gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const gs_camera* cam, void* d_workspace,
+                          size_t workspace_bytes, int64_t pair_capacity, uint64_t* d_keys, uint32_t* d_ids,
+                          uint32_t* d_tile_ranges, int64_t* h_num_pairs, void* stream);
+
+/*
+ * gs_rasterize_fwd -- per-pixel front-to-back alpha blending over the pixel's tile list (section
+ * 5 of the PyTorch lesson): for each pair in the tile's range, in order,
+ *   sigma = 0.5 (A dx^2 + C dy^2) + B dx dy with (dx, dy) = mean2d - pixel centre;
+ *   alpha = min(0.99, o exp(-sigma)); skip if sigma < 0 or alpha < 1/255;
+ *   stop before adding when T (1 - alpha) <= 1e-4; else pixel += colour alpha T, T *= 1 - alpha;
+ * and finally pixel += T background.
+ * Inputs: proj, d_ids and d_tile_ranges from gs_bin_and_sort for the same camera.
+ * Outputs: d_image [h,w,3]; d_final_T [h,w] the transmittance after the last added splat;
+ *   d_n_contrib [h,w] uint32: number of tile-list entries up to and including the last added
+ *   splat (0 if none). d_eval_count: NULL, or a device uint64 to which the number of
+ *   (pixel, entry) evaluations is added (a work counter for measurement).
+ * Deterministic: no atomics on the outputs; each pixel is written once.
+ */
+gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const gs_camera* cam, const uint32_t* d_ids,
+                           const uint32_t* d_tile_ranges, float* d_image, float* d_final_T,
+                           uint32_t* d_n_contrib, uint64_t* d_eval_count, void* stream);
+
+/*
+ * gs_rasterize_bwd -- gradients of a loss L with respect to the raw parameters, given
+ * dL/dimage (section 6 of the PyTorch lesson). Each tile is walked back to front from each
+ * pixel's last contributor; T_i = T_{i+1} / (1 - alpha_i) is recovered by division (the 0.99
+ * cap keeps 1 - alpha >= 0.01) and the blend weights are recomputed, never stored:
+ *   dC/dc_i = alpha_i T_i,  dC/dalpha_i = c_i T_i - S_i / (1 - alpha_i),
+ *   S_i = sum_{j>i} c_j alpha_j T_j + T_final background,
+ * then through alpha = o exp(-sigma) (no gradient where the 0.99 cap is active) to the 2D mean,
+ * conic and opacity, and by the chain rule of gs_project to the raw parameters. Culled
+ * Gaussians get exactly zero; radii, rectangles, keys and the sort carry no gradient.
+ * Inputs: the raw parameters and camera given to gs_project, its proj, the d_ids/d_tile_ranges
+ *   of gs_bin_and_sort, d_final_T/d_n_contrib of gs_rasterize_fwd, d_dL_dimage [h,w,3];
+ *   d_workspace of at least gs_bwd_workspace_bytes(n) bytes (device).
+ * Outputs (overwritten, not accumulated): d_grad_means [n,3], d_grad_log_scales [n,3],
+ *   d_grad_quats [n,4], d_grad_opacity_logits [n], d_grad_sh [n,(sh_degree+1)^2,3], and
+ *   d_grad_means2d [n,2] (may be NULL) = dL/d mean2d. d_eval_count as in gs_rasterize_fwd.
+ * Per-Gaussian sums use fp32 atomics, so results may differ in the last bits run to run.
+ */
+size_t gs_bwd_workspace_bytes(int32_t n);
+gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float* d_means, const float* d_log_scales,
+                           const float* d_quats, const float* d_opacity_logits, const float* d_sh,
+                           const gs_camera* cam, const gs_projected* proj, const uint32_t* d_ids,
+                           const uint32_t* d_tile_ranges, const float* d_final_T, const uint32_t* d_n_contrib,
+                           const float* d_dL_dimage, void* d_workspace, size_t workspace_bytes,
+                           float* d_grad_means, float* d_grad_log_scales, float* d_grad_quats,
+                           float* d_grad_opacity_logits, float* d_grad_sh, float* d_grad_means2d,
+                           uint64_t* d_eval_count, void* stream);
+
+/*
+ * gs_loss_l1 -- the L1 photometric term of the training loss (section 7 of the PyTorch lesson:
+ * (1 - lambda) L1 + lambda (1 - SSIM)): L = mean |image - target| over h*w*3 values, so
+ * dL/dimage = sign(image - target) / (3 h w) with sign(0) = 0.
+ * Inputs: d_image, d_target [h,w,3]. Outputs: d_dL_dimage [h,w,3]; d_loss (device float[1],
+ * may be NULL) receives L.
+ */
+gs_status gs_loss_l1(int32_t width, int32_t height, const float* d_image, const float* d_target,
+                     float* d_dL_dimage, float* d_loss, void* stream);
+
+/* Human-readable name of a status, and a thread-local description of the last non-OK return. */
+const char* gs_status_string(gs_status s);
+const char* gs_last_error(void);
+
+/*
+ * Kernel timing for measurement. While enabled, every kernel the library launches is bracketed
+ * by HIP events on its stream. gs_timing_collect waits for those events and returns up to `max`
+ * (name, milliseconds) records in launch order, then forgets them; it returns the number of
+ * records written. Not thread-safe; intended for a single measuring thread.
+ */
+gs_status gs_timing_enable(int32_t on);
+int32_t gs_timing_collect(const char** names, float* ms, int32_t max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GS_H */

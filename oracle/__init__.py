@@ -32,8 +32,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-# Fragility band for fp32 decisions (units of relative rounding): 8 ulp of fp32.
-BAND_F32 = 2.0 ** -20
+# Unit roundoff of the fp32 implementation compared against (sets the fragility bands).
+BAND_F32 = 2.0 ** -24
 
 
 def load():
@@ -244,7 +244,8 @@ def render_backward(proj, cam, dL_dimage, pixels=None, dtype=np.float32, band_ep
 
     dL_dimage: [H,W,3] (pixels=None) or [M,3] matching ``pixels``.
     Returns (g2d [N,9] float64, aref [N,9] float64): per Gaussian d/d(mu'x, mu'y, A, B, C,
-    opacity, r, g, b) and the sum of absolute per-pixel contributions of each component.
+    opacity, r, g, b) and the rounding scale of each (sum over pixels of the magnitudes of the
+    terms each contribution is computed from).
     """
     lib = load()
     if band_eps is None:

@@ -394,13 +394,18 @@ struct Contributor {
 struct Trace {
   std::vector<Contributor> contrib;
   bool fragile = false;
+  double errT = 0.0;  // bound on the relative rounding of the final transmittance (band units)
   int64_t n_eval = 0;
   int64_t escapes = 0;
 };
 
 // Walks `order` (un-culled Gaussians, stable ascending depth) at pixel centre (px, py).
-// fragile is set when any decision lies within a rounding band of its threshold; the band is
-// band_eps times a bound on the accumulated relative rounding of the quantity compared.
+// fragile is set when a decision lies within the rounding band of its threshold. band_eps is the
+// unit roundoff of the implementation being compared (2^-24 for fp32); the band of each compared
+// quantity is a bound on its accumulated relative rounding, with a safety factor of 8:
+//   sigma: 8 eps times the sum of the magnitudes of its terms,
+//   alpha: that (relative, through exp) plus 8 eps,
+//   T * (1 - alpha): the running bound on T plus alpha / (1 - alpha) times alpha's bound.
 template <class T>
 void trace_pixel(T px, T py, const std::vector<int>& order, const std::vector<Splat2D<T>>& S,
                  const int32_t* rects, int tile_x, int tile_y, double band_eps, Trace& tr) {
@@ -408,6 +413,7 @@ void trace_pixel(T px, T py, const std::vector<int>& order, const std::vector<Sp
   tr.fragile = false;
   tr.n_eval = 0;
   tr.escapes = 0;
+  tr.errT = 0.0;
   T Tr = (T)1;
   double errT = 0.0;  // bound on the relative rounding carried by Tr, in units of band_eps
   const T thr_a = (T)1 / (T)255;
@@ -425,8 +431,8 @@ void trace_pixel(T px, T py, const std::vector<int>& order, const std::vector<Sp
     // rounding bound on sigma (relative to the magnitudes summed) and on alpha
     double sig_mag = 0.5 * (std::fabs((double)s.A) * dx * dx + std::fabs((double)s.C) * dy * dy) +
                      std::fabs((double)s.B * dx * dy);
-    double e_sig = band_eps * (4.0 * sig_mag + 1e-30);
-    double e_alpha = e_sig + 4.0 * band_eps;  // relative
+    double e_sig = 8.0 * band_eps * sig_mag;   // absolute, on sigma
+    double e_alpha = e_sig + 8.0 * band_eps;   // relative, on alpha
     if (std::fabs((double)sigma) <= e_sig) tr.fragile = true;
     if (std::fabs((double)alpha - (double)thr_a) <= e_alpha * (double)thr_a) tr.fragile = true;
     if (std::fabs((double)raw - 0.99) <= e_alpha * 0.99) tr.fragile = true;
@@ -440,11 +446,12 @@ void trace_pixel(T px, T py, const std::vector<int>& order, const std::vector<Sp
     // contributes unless it would drive T to or below 1e-4
     T next_T = Tr * ((T)1 - alpha);
     double errN = errT + e_alpha * (double)alpha / (1.0 - (double)alpha) + 2.0 * band_eps;
-    if (std::fabs((double)next_T - 1e-4) <= 4.0 * errN * 1e-4) tr.fragile = true;
+    if (std::fabs((double)next_T - 1e-4) <= errN * 1e-4) tr.fragile = true;
     if (next_T <= (T)1e-4) break;
     tr.contrib.push_back({g, raw >= (T)0.99});
     Tr = next_T;
     errT = errN;
+    tr.errT = errT;
   }
 }
 
@@ -556,7 +563,10 @@ int render_impl(int n, const T* means2d, const T* conics, const T* opac, const T
 //   a = o exp(-sigma) when below the cap (else constant 0.99): da/do = exp(-sigma), da/dsigma = -a,
 //   sigma = 0.5 (A dx^2 + C dy^2) + B dx dy with dx = mu'_x - px.
 // Output per Gaussian (9): d mu'_x, d mu'_y, dA, dB, dC, d opacity, d colour (3), accumulated in
-// double; aref holds the sum of absolute per-pixel contributions of each (for tolerance floors).
+// double. aref is the rounding scale of each sum, for tolerance floors: per pixel, the absolute
+// values of the terms each contribution is computed from (|c| T + |S| / (1 - a) for dC/da, which
+// cancels when a splat's colour matches what lies behind it), times max(1, e_T / 1e-5) with e_T
+// the pixel's bound on the relative rounding of its transmittance, summed over pixels.
 template <class T>
 int render_bwd_impl(int n, const T* means2d, const T* conics, const T* opac, const T* colors,
                     const T* depths, const uint32_t* tiles, const int32_t* rects, int W, int H,
@@ -587,30 +597,47 @@ int render_bwd_impl(int n, const T* means2d, const T* conics, const T* opac, con
       trace_pixel<T>(px, py, order, S, rects, col / 16, row / 16, band_eps, tr);
       double Tf;
       pixel_values<T>(tr, S, (double)px, (double)py, al, Ti, Gi, Tf);
+      // T_i is recovered from rounded (1 - alpha) factors: where the bound on its relative rounding
+      // exceeds 1e-5, the floor of this pixel's terms grows with it
+      const double tscale = std::max(1.0, tr.errT / 1e-5);
       double Sacc[3] = {Tf * (double)bg[0], Tf * (double)bg[1], Tf * (double)bg[2]};
+      double Sabs[3] = {Tf * std::fabs((double)bg[0]), Tf * std::fabs((double)bg[1]), Tf * std::fabs((double)bg[2])};
       for (int i = (int)tr.contrib.size() - 1; i >= 0; --i) {
         const int g = tr.contrib[i].g;
         const Splat2D<T>& s = S[g];
         double c[3] = {(double)s.col[0], (double)s.col[1], (double)s.col[2]};
-        double gal = 0.0;
-        for (int ch = 0; ch < 3; ++ch) gal += gp[ch] * (c[ch] * Ti[i] - Sacc[ch] / (1.0 - al[i]));
-        double contrib[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
-        for (int ch = 0; ch < 3; ++ch) contrib[6 + ch] = al[i] * Ti[i] * gp[ch];
+        double gal = 0.0, gal_mag = 0.0;
+        for (int ch = 0; ch < 3; ++ch) {
+          gal += gp[ch] * (c[ch] * Ti[i] - Sacc[ch] / (1.0 - al[i]));
+          gal_mag += std::fabs(gp[ch]) * (std::fabs(c[ch]) * Ti[i] + Sabs[ch] / (1.0 - al[i]));
+        }
+        double contrib[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0}, mag[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+        for (int ch = 0; ch < 3; ++ch) {
+          contrib[6 + ch] = al[i] * Ti[i] * gp[ch];
+          mag[6 + ch] = std::fabs(contrib[6 + ch]);
+        }
         if (!tr.contrib[i].capped) {
           double dx = (double)s.mx - (double)px, dy = (double)s.my - (double)py;
           contrib[5] = Gi[i] * gal;
           double gsig = -al[i] * gal;
-          contrib[2] = gsig * 0.5 * dx * dx;
-          contrib[3] = gsig * dx * dy;
-          contrib[4] = gsig * 0.5 * dy * dy;
-          contrib[0] = gsig * ((double)s.A * dx + (double)s.B * dy);
-          contrib[1] = gsig * ((double)s.B * dx + (double)s.C * dy);
+          double dsig[5] = {(double)s.A * dx + (double)s.B * dy, (double)s.B * dx + (double)s.C * dy,
+                            0.5 * dx * dx, dx * dy, 0.5 * dy * dy};
+          for (int k = 0; k < 5; ++k) contrib[k] = gsig * dsig[k];
+          // magnitudes: dC/dalpha summed from its terms' absolute values; d sigma/d mean2d too
+          mag[5] = Gi[i] * gal_mag;
+          double dsig_mag[5] = {std::fabs((double)s.A * dx) + std::fabs((double)s.B * dy),
+                                std::fabs((double)s.B * dx) + std::fabs((double)s.C * dy), std::fabs(dsig[2]),
+                                std::fabs(dsig[3]), std::fabs(dsig[4])};
+          for (int k = 0; k < 5; ++k) mag[k] = al[i] * gal_mag * dsig_mag[k];
         }
         for (int k = 0; k < 9; ++k) {
           G[(size_t)g * 9 + k] += contrib[k];
-          Aa[(size_t)g * 9 + k] += std::fabs(contrib[k]);
+          Aa[(size_t)g * 9 + k] += mag[k] * tscale;
         }
-        for (int ch = 0; ch < 3; ++ch) Sacc[ch] += c[ch] * al[i] * Ti[i];
+        for (int ch = 0; ch < 3; ++ch) {
+          Sacc[ch] += c[ch] * al[i] * Ti[i];
+          Sabs[ch] += std::fabs(c[ch]) * al[i] * Ti[i];
+        }
       }
     }
   }

@@ -1,0 +1,55 @@
+"""The C-ABI library loads and exports every entry point include/gs.h declares (CPU only: no
+compute call is made), and the host-only size helpers behave."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gs.h")
+LIB = os.path.join(ROOT, "gaussian_splatting_tile_gs_amd", "libgs_hip.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gs_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from gaussian_splatting_tile_gs_amd import build
+
+        build.build()
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("gs_project", "gs_bin_and_sort", "gs_rasterize_fwd", "gs_rasterize_bwd"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_host_only_helpers(lib):
+    lib.gs_status_string.restype = ctypes.c_char_p
+    lib.gs_status_string.argtypes = [ctypes.c_int]
+    assert lib.gs_status_string(2) == b"GS_ERR_CAPACITY"
+    lib.gs_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.gs_bwd_workspace_bytes.argtypes = [ctypes.c_int32]
+    assert lib.gs_bwd_workspace_bytes(1000) >= 1000 * 9 * 4
+    from gaussian_splatting_tile_gs_amd import gs
+
+    cam = gs.GsCamera()
+    cam.width, cam.height = 1280, 720
+    lib.gs_bin_workspace_bytes.restype = ctypes.c_size_t
+    lib.gs_bin_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(gs.GsCamera)]
+    small = lib.gs_bin_workspace_bytes(1000, 10000, ctypes.byref(cam))
+    big = lib.gs_bin_workspace_bytes(1000, 1000000, ctypes.byref(cam))
+    assert 0 < small < big

@@ -1,0 +1,267 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on seeded synthetic inputs.
+
+Bar: projected integers (radii, tile counts) and the floats written in the oracle's op order are
+bit-exact; pair counts, sorted keys/ids and tile ranges are bit-exact; pixels within 1e-4 per
+channel off the oracle's fragile set (decisions within a rounding band of a threshold); raw
+gradients within 1e-3 relative plus 1e-5 of the oracle's sum of absolute contributions.
+Small cases are compared whole; the full workload sizes compare projection and binning whole and
+pixels/gradients on a seeded pixel sample (a loss that is non-zero only on the sample, so the
+oracle's gradients are exact).
+"""
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+from gaussian_splatting_tile_gs_amd import synth
+from _gpu_util import (assert_projection_bit_exact, compare_forward, compare_grads, log, proj_from_numpy,
+                       proj_to_numpy, run_gpu_bin, run_gpu_project)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+
+    assert torch.cuda.is_available(), "the GPU tests need a GPU"
+    from gaussian_splatting_tile_gs_amd import gs
+
+    gs.load()
+    return gs, torch
+
+
+def _full_pixels(cam):
+    H, W = cam["height"], cam["width"]
+    r, c = np.mgrid[0:H, 0:W]
+    return np.stack([r.ravel(), c.ravel()], -1).astype(np.int32)
+
+
+def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7, label=""):
+    """Project, bin, forward (and backward) on the GPU; compare every stage with the oracle."""
+    gs, torch = env
+    t0 = time.time()
+    log(f"[{label}] n={scene['means'].shape[0]} {cam_dict['width']}x{cam_dict['height']} deg={scene['sh_degree']}")
+    params, cam, proj = run_gpu_project(gs, torch, scene, cam_dict)
+    o_proj = oracle.project(scene, cam_dict, np.float32)
+    nvis = assert_projection_bit_exact(proj_to_numpy(proj), o_proj)
+    # binning end to end (GPU projection) and stage-isolated (the oracle's projection uploaded)
+    o_keys, o_ids, o_ranges = oracle.bin_pairs(o_proj, cam_dict)
+    P_exp = int(o_keys.size)
+    st, P, keys, ids, ranges = run_gpu_bin(gs, torch, params["n"], proj, cam, P_exp + 17)
+    assert st == gs.GS_OK and P == P_exp
+    keys_np = keys.cpu().numpy()[:P].view(np.uint64)
+    ids_np = ids.cpu().numpy()[:P].view(np.uint32)
+    ranges_np = ranges.cpu().numpy().view(np.uint32)
+    assert np.array_equal(keys_np, o_keys), "sorted keys differ"
+    assert np.array_equal(ids_np, o_ids), "sorted ids differ"
+    assert np.array_equal(ranges_np, o_ranges), "tile ranges differ"
+    iso = proj_from_numpy(gs, torch, o_proj)
+    st2, P2, keys2, ids2, ranges2 = run_gpu_bin(gs, torch, params["n"], iso, cam, P_exp)
+    assert st2 == gs.GS_OK and P2 == P_exp
+    assert np.array_equal(keys2.cpu().numpy()[:P].view(np.uint64), o_keys)
+    assert np.array_equal(ranges2.cpu().numpy().view(np.uint32), o_ranges)
+    log(f"[{label}] visible={nvis} pairs={P} projection+binning bit-exact ({time.time() - t0:.1f}s)")
+
+    # forward
+    H, W = cam_dict["height"], cam_dict["width"]
+    img = torch.empty(H, W, 3, device="cuda")
+    fT = torch.empty(H, W, device="cuda")
+    nc = torch.empty(H, W, device="cuda", dtype=torch.int32)
+    evals = torch.zeros(1, device="cuda", dtype=torch.int64)
+    gs.gs_rasterize_fwd(params["n"], proj, cam, ids, ranges, img, fT, nc, evals)
+    torch.cuda.synchronize()
+    pix = _full_pixels(cam_dict) if pixels is None else pixels
+    o_fwd = oracle.render(o_proj, cam_dict, pixels=pix)
+    assert o_fwd["escapes"] == 0
+    dmax, nfrag = compare_forward(img.cpu().numpy(), fT.cpu().numpy(), nc.cpu().numpy(), ids_np, ranges_np, o_fwd,
+                                  pix, W)
+    assert nfrag <= max(2, len(pix) // 50), f"{nfrag} fragile pixels"
+    log(f"[{label}] forward: {len(pix)} px, max |diff| {dmax:.2e}, fragile {nfrag}, evals {int(evals.item())} "
+        f"({time.time() - t0:.1f}s)")
+    if not backward:
+        return
+    # backward: seeded dL/dimage on the compared pixels (zero elsewhere and on fragile pixels)
+    g = synth.random_image_grad(H, W, seed=grad_seed)
+    gsel = g[pix[:, 0], pix[:, 1]].astype(np.float64)
+    gsel[o_fwd["fragile"]] = 0.0
+    dimg = np.zeros((H, W, 3), np.float32)
+    dimg[pix[:, 0], pix[:, 1]] = gsel
+    pipe_grads = {k: torch.empty_like(v) for k, v in
+                  (("means", params["means"]), ("log_scales", params["log_scales"]), ("quats", params["quats"]),
+                   ("opacity_logits", params["opacity_logits"]), ("sh", params["sh"]))}
+    g2d_out = torch.empty(params["n"], 2, device="cuda")
+    ws = torch.empty(gs.gs_bwd_workspace_bytes(params["n"]), device="cuda", dtype=torch.uint8)
+    gs.gs_rasterize_bwd(params["n"], params["sh_degree"], params["means"], params["log_scales"], params["quats"],
+                        params["opacity_logits"], params["sh"], cam, proj, ids, ranges, fT, nc,
+                        torch.from_numpy(dimg).cuda(), ws, pipe_grads["means"], pipe_grads["log_scales"],
+                        pipe_grads["quats"], pipe_grads["opacity_logits"], pipe_grads["sh"], g2d_out)
+    torch.cuda.synchronize()
+    g2d, aref2d = oracle.render_backward(o_proj, cam_dict, gsel, pixels=pix)
+    raw = oracle.project_backward(scene, cam_dict, g2d, aref2d)
+    gpu = {k: v.cpu().numpy() for k, v in pipe_grads.items()}
+    worst = compare_grads(gpu, raw, scene["sh_degree"], label)
+    m2 = g2d_out.cpu().numpy().astype(np.float64)
+    tol = 1e-3 * np.abs(g2d[:, :2]) + 1e-5 * aref2d[:, :2] + 1e-12
+    assert np.all(np.abs(m2 - g2d[:, :2]) <= tol), "dL/dmean2d differs"
+    culled = o_proj["tiles_touched"] == 0
+    assert all(np.all(gpu[k][culled] == 0) for k in gpu), "culled Gaussians must get exactly zero"
+    log(f"[{label}] backward: worst error/tolerance {worst:.3f} ({time.time() - t0:.1f}s)")
+
+
+# ---- small cases, compared whole --------------------------------------------------------------
+def test_tiny_workload_full_frame(env):
+    wl = synth.WORKLOADS["tiny_1k"]
+    _pipeline_case(env, synth.make_scene(wl), synth.make_cameras(wl)[0], label="tiny_1k")
+
+
+def test_ragged_sh3_small(env):
+    # 37 x 23: a ragged tail in both directions (3 x 2 tiles), degree-3 colour, a few culled ones
+    sc = synth.random_scene(300, seed=21, width=37, height=23, focal=30.0, sh_degree=3, logit_std=2.0)
+    sc["means"][:5, 2] = -1.0
+    cam = synth.make_camera(np.eye(4), 37, 23, 30.0, background=(0.2, 0.4, 0.6))
+    _pipeline_case(env, sc, cam, label="ragged_sh3")
+
+
+@pytest.mark.parametrize("deg", [1, 2])
+def test_sh_degrees_small(env, deg):
+    sc = synth.random_scene(400, seed=30 + deg, width=64, height=48, focal=50.0, sh_degree=deg)
+    V = synth.look_at((0.4, -0.3, -0.5), target=(0.0, 0.0, 3.0), up=(0.0, -1.0, 0.0))
+    _pipeline_case(env, sc, synth.make_camera(V, 64, 48, 50.0), label=f"sh{deg}")
+
+
+# ---- full workload sizes: whole projection/binning, sampled pixels ------------------------------
+@pytest.mark.parametrize("name,cam_index,backward", [
+    ("distill_30k", 0, True), ("distill_30k", 17, True), ("mid_150k_sh3", 0, True),
+    ("teacher_742k", 0, False), ("stress_400k_sh3", 0, True)])
+def test_workload_sampled(env, name, cam_index, backward):
+    wl = synth.WORKLOADS[name]
+    scene = synth.make_scene(wl)
+    cam = synth.make_cameras(wl)[cam_index]
+    pix = synth.sample_pixels(cam["width"], cam["height"], 4096, seed=cam_index + 1)
+    _pipeline_case(env, scene, cam, pixels=pix, backward=backward, label=f"{name}#{cam_index}")
+
+
+# ---- edge cases ---------------------------------------------------------------------------------
+def test_empty_and_all_culled(env):
+    gs, torch = env
+    cam_d = synth.make_camera(np.eye(4), 40, 24, 30.0, background=(0.3, 0.2, 0.1))
+    cam = gs.make_camera(cam_d)
+    for n in (0, 5):
+        sc = synth.random_scene(max(n, 1), seed=3, width=40, height=24, focal=30.0)
+        if n == 0:
+            sc = {k: (v[:0] if isinstance(v, np.ndarray) else v) for k, v in sc.items()}
+        else:
+            sc["means"][:, 2] = -2.0  # all behind the camera
+        params = gs.scene_to_device(sc)
+        pipe = gs.Pipeline(params, 40, 24, pair_capacity=16)
+        pipe.project(cam)
+        assert pipe.bin(cam) == 0
+        pipe.forward(cam)
+        torch.cuda.synchronize()
+        img = pipe.image.cpu().numpy()
+        assert np.allclose(img, np.array([0.3, 0.2, 0.1], np.float32)) and np.all(pipe.final_T.cpu().numpy() == 1)
+        assert np.all(pipe.ranges.cpu().numpy() == 0)
+        if n:
+            pipe.dL_dimage.fill_(1.0)
+            pipe.backward(cam)
+            torch.cuda.synchronize()
+            assert all(np.all(v.cpu().numpy() == 0) for v in pipe.grads.values())
+
+
+def test_capacity_error_writes_nothing(env):
+    gs, torch = env
+    wl = synth.WORKLOADS["tiny_1k"]
+    cam_d = synth.make_cameras(wl)[0]
+    params, cam, proj = run_gpu_project(gs, torch, synth.make_scene(wl), cam_d)
+    need = int(proj.tiles_touched.sum().item())
+    cap = need - 1
+    keys = torch.full((cap,), -7, device="cuda", dtype=torch.int64)
+    ids = torch.full((cap,), -7, device="cuda", dtype=torch.int32)
+    ranges = torch.full((64, 2), -7, device="cuda", dtype=torch.int32)
+    ws = torch.empty(gs.gs_bin_workspace_bytes(params["n"], cap, cam), device="cuda", dtype=torch.uint8)
+    st, P = gs.gs_bin_and_sort(params["n"], proj, cam, ws, cap, keys, ids, ranges)
+    torch.cuda.synchronize()
+    assert st == gs.GS_ERR_CAPACITY and P == need
+    assert torch.all(keys == -7) and torch.all(ids == -7) and torch.all(ranges == -7)
+
+
+def test_invalid_arguments(env):
+    gs, torch = env
+    cam_d = synth.make_camera(np.eye(4), 32, 32, 40.0)
+    params = gs.scene_to_device(synth.random_scene(10, seed=1))
+    proj = gs.Projected.empty(10)
+    cam = gs.make_camera(cam_d)
+    with pytest.raises(gs.GsError) as e:
+        gs.gs_project(10, 4, params["means"], params["log_scales"], params["quats"], params["opacity_logits"],
+                      params["sh"], cam, proj)
+    assert e.value.status == gs.GS_ERR_INVALID_ARG
+    bad = gs.make_camera(dict(cam_d, width=0))
+    with pytest.raises(gs.GsError):
+        gs.gs_project(10, 0, params["means"], params["log_scales"], params["quats"], params["opacity_logits"],
+                      params["sh"], bad, proj)
+    nan_cam = gs.make_camera(dict(cam_d, fx=float("nan")))
+    with pytest.raises(gs.GsError):
+        gs.gs_project(10, 0, params["means"], params["log_scales"], params["quats"], params["opacity_logits"],
+                      params["sh"], nan_cam, proj)
+    with pytest.raises(gs.GsError):
+        gs.gs_project(-1, 0, params["means"], params["log_scales"], params["quats"], params["opacity_logits"],
+                      params["sh"], cam, proj)
+    # too small a workspace
+    keys = torch.empty(100, device="cuda", dtype=torch.int64)
+    ids = torch.empty(100, device="cuda", dtype=torch.int32)
+    ranges = torch.empty(4, 2, device="cuda", dtype=torch.int32)
+    ws = torch.empty(16, device="cuda", dtype=torch.uint8)
+    with pytest.raises(gs.GsError):
+        gs.gs_bin_and_sort(10, proj, cam, ws, 100, keys, ids, ranges)
+
+
+def test_huge_splat_and_tile_edges(env):
+    # one splat covering every tile of a ragged grid, plus splats centred exactly on tile edges
+    sc = {"means": np.array([[0.0, 0.0, 2.0], [0.0, 0.0, 3.0], [16.0 / 40 * 3, 0.0, 3.0], [0.0, -16.0 / 40 * 3, 3.0]]),
+          "log_scales": np.array([[1.0] * 3, [-2.5] * 3, [-2.5] * 3, [-2.5] * 3]),
+          "quats": np.tile([1.0, 0, 0, 0], (4, 1)), "opacity_logits": np.array([-1.0, 3.0, 3.0, 3.0]),
+          "sh": np.random.default_rng(1).uniform(0, 1, (4, 1, 3)), "sh_degree": 0}
+    cam = synth.make_camera(np.eye(4), 70, 40, 40.0)
+    _pipeline_case(env, sc, cam, label="huge+edges")
+
+
+def test_opacity_extremes(env):
+    sc = synth.random_scene(200, seed=8, width=48, height=48, focal=50.0)
+    sc["opacity_logits"][:40] = 30.0
+    sc["opacity_logits"][40:60] = -30.0
+    _pipeline_case(env, sc, synth.make_camera(np.eye(4), 48, 48, 50.0, background=(1.0, 1.0, 1.0)), label="opacity")
+
+
+def test_forward_and_sort_deterministic(env):
+    gs, torch = env
+    wl = synth.WORKLOADS["distill_30k"]
+    params = gs.scene_to_device(synth.make_scene(wl))
+    cam = gs.make_camera(synth.make_cameras(wl)[5])
+    pipe = gs.Pipeline(params, wl.width, wl.height, pair_capacity=1 << 18)
+    outs = []
+    for _ in range(2):
+        pipe.project(cam)
+        pipe.bin(cam)
+        pipe.forward(cam)
+        torch.cuda.synchronize()
+        outs.append((pipe.keys[:pipe.num_pairs].clone(), pipe.ids[:pipe.num_pairs].clone(), pipe.image.clone(),
+                     pipe.n_contrib.clone()))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+
+
+def test_loss_l1(env):
+    gs, torch = env
+    rng = np.random.default_rng(2)
+    img = rng.uniform(0, 1, (37, 23, 3)).astype(np.float32)
+    tgt = rng.uniform(0, 1, (37, 23, 3)).astype(np.float32)
+    tgt[0, 0] = img[0, 0]  # sign(0) = 0
+    dimg = torch.empty(37, 23, 3, device="cuda")
+    loss = torch.empty(1, device="cuda")
+    gs.gs_loss_l1(23, 37, torch.from_numpy(img).cuda(), torch.from_numpy(tgt).cuda(), dimg, loss)
+    torch.cuda.synchronize()
+    want = np.sign(img.astype(np.float64) - tgt) / img.size
+    assert np.allclose(dimg.cpu().numpy(), want, rtol=1e-6, atol=0)
+    assert loss.item() == pytest.approx(np.abs(img.astype(np.float64) - tgt).mean(), rel=1e-5)

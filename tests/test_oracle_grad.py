@@ -38,7 +38,7 @@ def _stable_scene(sh_degree, W=32, H=32, f=40.0):
         sc = _scene(seed, sh_degree, W=W, H=H, f=f)
         pr = oracle.project(sc, cam, np.float64)
         # decisions within ~1e-4 relative of a threshold are refused (band_eps scales the bound)
-        out = oracle.render(pr, cam, dtype=np.float64, band_eps=2e-5)
+        out = oracle.render(pr, cam, dtype=np.float64, band_eps=5e-6)
         if not out["fragile"].any() and (pr["tiles_touched"] > 0).sum() >= 8:
             return sc, cam, pr
     raise RuntimeError("no stable scene found")
