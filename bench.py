@@ -1,0 +1,260 @@
+"""Throughput of one fwd+bwd iteration of the tile rasterizer on one MI355X.
+
+A step is one pass of the whole hot path for one camera: gs_project -> gs_bin_and_sort ->
+gs_rasterize_fwd -> gs_loss_l1 (L1 gradient against the camera's target image) ->
+gs_rasterize_bwd. Steps cycle through the workload's cameras; all inputs (Gaussians, cameras,
+target images) are resident in HBM before the timed region. The default workload is the
+30,000-Gaussian distillation student at 1280x720 over 60 ring cameras, with target images
+rendered once (by the forward path) from a seeded 300,000-Gaussian teacher.
+
+Prints one JSON line: the iterations/s metric, Mpix/s and sorted pairs/s, per-kernel times from
+HIP events recorded by the library on the stream it launches on (a second pass over the same
+steps, right after the timed one), the roofline of the dominant kernel and the CPU oracle timed
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X figures used for rooflines (public specs): HBM3E 8 TB/s; 256 CUs x 4 SIMD x 16 lanes at
+# 2.4 GHz issue 39.3e12 non-packed fp32 VALU lane-operations per second (157.3 TFLOP/s counts
+# packed FMAs as 4 flops per lane-cycle).
+HBM_PEAK_GBS = 8000.0
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+# VALU instructions executed per (pixel, splat) evaluation on the kernels' main path, counted in
+# the gfx950 ISA of the built library ("Rooflines").
+VALU_PER_EVAL = {"blend": 25.0, "rbwd": 48.0}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=600)
+    ap.add_argument("--warmup", type=int, default=60)
+    ap.add_argument("--workload", default="distill_30k")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_bytes(name, stats):
+    """Algorithmic HBM bytes of one launch of a binning kernel."""
+    P, N = stats["pairs"], stats["n"]
+    return {
+        "depth_prep": 16.0 * N,
+        "depth_sort_pass": 16.0 * N,
+        "scan": 12.0 * N,
+        "emit": 8.0 * P + 24.0 * stats["visible"],
+        "pair_sort_pass": 16.0 * P + 4.0 * P / stats["pair_passes"],
+        "ranges": 8.0 * P,
+        "project": stats["project_bytes"],
+        "loss_l1": 12.0 * stats["pixels"] * 3,
+    }.get(name)
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current source of that kernel; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel)
+    except ValueError:
+        return None
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "gaussian_splatting_tile_gs_amd", "csrc", rec["source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["sha256"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def cpu_baseline(wl, scene, cam, target_np, seconds):
+    """The oracle on the host cores: projection of all N, dense render + backward of a seeded
+    pixel sample (sparse L1 loss on it), chain rule to raw parameters; scaled to a full frame."""
+    import oracle
+    from gaussian_splatting_tile_gs_amd import synth
+
+    W, H = cam["width"], cam["height"]
+    npix = 1024
+    while True:
+        pix = synth.sample_pixels(W, H, npix, seed=1)
+        t0 = time.perf_counter()
+        proj = oracle.project(scene, cam)
+        t1 = time.perf_counter()
+        fwd = oracle.render(proj, cam, pixels=pix)
+        diff = fwd["image"] - target_np[pix[:, 0], pix[:, 1]]
+        dimg = np.sign(diff) / (3.0 * W * H)
+        t2 = time.perf_counter()
+        g2d, _ = oracle.render_backward(proj, cam, dimg, pixels=pix)
+        t3 = time.perf_counter()
+        oracle.project_backward(scene, cam, g2d)
+        t4 = time.perf_counter()
+        total = t4 - t0
+        if total >= 0.5 * seconds or npix >= W * H:
+            break
+        npix = min(W * H, int(npix * max(2.0, 0.7 * seconds / max(total, 1e-3))))
+    per_pixel = (t3 - t1) / npix
+    frame = (t1 - t0) + (t4 - t3) + per_pixel * W * H
+    return {"value": 1.0 / frame, "unit": "iterations/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"camera 0 of {wl.name}: projection of all {scene['means'].shape[0]} Gaussians, dense "
+                      f"render + backward on {npix} seeded pixels of {W * H} (sparse L1 loss), chain rule; "
+                      f"per-pixel time scaled to the full frame (measured {total:.1f} s)",
+            "measured_seconds": round(total, 3), "frame_seconds_extrapolated": round(frame, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU: bench.py --gpus N with N > 1 is not supported"}))
+        sys.exit(2)
+    import torch
+
+    from gaussian_splatting_tile_gs_amd import gs, synth
+
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    scene = synth.make_scene(wl)
+    cams_d = synth.make_cameras(wl)
+    cams = [gs.make_camera(c) for c in cams_d]
+    W, H = wl.width, wl.height
+    params = gs.scene_to_device(scene)
+
+    # targets: the teacher rendered by the forward path, once, resident in HBM
+    teacher = synth.make_teacher(wl)
+    tparams = gs.scene_to_device(teacher)
+    tpipe = gs.Pipeline(tparams, W, H, pair_capacity=1 << 20)
+    targets = torch.empty(len(cams), H, W, 3, device="cuda")
+    for i, cam in enumerate(cams):
+        tpipe.project(cam)
+        tpipe.bin(cam)
+        tpipe.forward(cam)
+        targets[i].copy_(tpipe.image)
+    del tpipe, tparams
+    torch.cuda.synchronize()
+
+    pipe = gs.Pipeline(params, W, H, pair_capacity=1 << 16)
+    pairs = []
+    for cam in cams:  # size the pair buffers for every camera
+        pipe.project(cam)
+        pairs.append(pipe.bin(cam))
+    need = max(pairs)
+    if pipe.capacity < need:
+        pipe._alloc_pairs(int(need * 1.1) + 1024)
+    ncam = len(cams)
+
+    def step(i):
+        c = i % ncam
+        if wl.backward:
+            pipe.iteration(cams[c], targets[c])
+        else:
+            pipe.project(cams[c])
+            pipe.bin(cams[c])
+            pipe.forward(cams[c])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    its = args.steps / elapsed
+    steps_pairs = sum(pairs[(args.warmup + i) % ncam] for i in range(args.steps))
+
+    result = {
+        "metric": "fwd+bwd iterations/sec and Mpix/s at 30k Gaussians 1280x720; sorted pairs/sec",
+        "value": its, "unit": "iterations/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": 1e3 * elapsed / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "mpix_per_s": its * W * H / 1e6, "sorted_pairs_per_s": steps_pairs / elapsed,
+        "config": {"workload": wl.name, "gaussians": wl.n, "width": W, "height": H, "cameras": ncam,
+                   "sh_degree": wl.sh_degree, "teacher_gaussians": int(teacher["means"].shape[0]),
+                   "mean_pairs_per_camera": float(np.mean(pairs)), "parallelism": "single GPU"},
+    }
+
+    if not args.no_kernel_timing:
+        # per-kernel HIP events (recorded by the library on the stream it launches on) over a
+        # second pass of the same steps; then an untimed pass with the evaluation counters on
+        nprof = min(args.steps, 4 * ncam)
+        gs.gs_timing_enable(True)
+        for i in range(nprof):
+            step(args.warmup + i)
+        torch.cuda.synchronize()
+        recs = gs.gs_timing_collect(1 << 16)
+        gs.gs_timing_enable(False)
+        evals_f = torch.zeros(1, device="cuda", dtype=torch.int64)
+        evals_b = torch.zeros(1, device="cuda", dtype=torch.int64)
+        for i in range(nprof):
+            c = (args.warmup + i) % ncam
+            pipe.project(cams[c])
+            pipe.bin(cams[c])
+            pipe.forward(cams[c], eval_count=evals_f)
+            if wl.backward:
+                pipe.loss_l1(targets[c])
+                pipe.backward(cams[c], eval_count=evals_b)
+        torch.cuda.synchronize()
+        per = {}
+        for name, ms in recs:
+            d = per.setdefault(name, [0.0, 0])
+            d[0] += ms
+            d[1] += 1
+        visible = int((pipe.proj.tiles_touched > 0).sum().item())
+        K = (wl.sh_degree + 1) ** 2
+        stats = {"pairs": float(np.mean(pairs)), "n": wl.n, "visible": visible, "pixels": W * H,
+                 "pair_passes": max(1, per.get("pair_sort_pass", [0, 1])[1] // max(1, per.get("emit", [0, 1])[1])),
+                 "project_bytes": wl.n * (4 * (3 + 3 + 4 + 1 + 3 * K) + 52)}
+        kernels = {}
+        for name, (tot, cnt) in sorted(per.items(), key=lambda kv: -kv[1][0]):
+            kernels[name] = {"launches": cnt, "avg_us": 1e3 * tot / cnt, "share": tot / sum(v[0] for v in per.values())}
+        result["kernels"] = kernels
+        dom = max(per.items(), key=lambda kv: kv[1][0])[0]
+        tot, cnt = per[dom]
+        avg_s = tot / cnt / 1e3
+        if dom in VALU_PER_EVAL:
+            evals = (evals_f if dom == "blend" else evals_b).item() / cnt
+            ops = evals * VALU_PER_EVAL[dom]
+            achieved = ops / avg_s / 1e12
+            roof = {"bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TOPS, "unit": "TOP/s",
+                    "frac": achieved / VALU_PEAK_TOPS, "traffic": traffic_for(dom), "kernel": dom,
+                    "evals_per_launch": evals, "valu_per_eval": VALU_PER_EVAL[dom], "avg_us": avg_s * 1e6}
+        else:
+            b = kernel_bytes(dom, stats) or 0.0
+            achieved = b / avg_s / 1e9
+            roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(dom), "kernel": dom,
+                    "bytes_per_launch": b, "avg_us": avg_s * 1e6}
+        result["roofline"] = roof
+        bin_names = ("depth_prep", "depth_sort_pass", "scan", "emit", "pair_sort_pass", "ranges")
+        bin_s = sum(per[k][0] for k in bin_names if k in per) / 1e3 / nprof
+        bin_b = sum((kernel_bytes(k, stats) or 0.0) * per[k][1] for k in bin_names if k in per) / nprof
+        result["bin_sort"] = {"kernel_us_per_step": bin_s * 1e6, "bytes_per_step": bin_b,
+                              "gbs": bin_b / bin_s / 1e9 if bin_s > 0 else None,
+                              "frac_hbm": (bin_b / bin_s / 1e9) / HBM_PEAK_GBS if bin_s > 0 else None}
+        result["evals_per_step"] = {"fwd": evals_f.item() / nprof, "bwd": evals_b.item() / nprof}
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, scene, cams_d[0], targets[0].cpu().numpy().astype(np.float64),
+                                              args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

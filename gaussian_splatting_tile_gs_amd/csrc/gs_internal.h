@@ -131,7 +131,7 @@ __device__ __forceinline__ SplatEval eval_splat(float dx, float dy, float hA, fl
   // s2 = log2(e) * sigma = hA dx^2 + hC dy^2 + B2 dx dy
   const float s2 = fmaf(hA * dx, dx, fmaf(hC * dy, dy, (B2 * dx) * dy));
   SplatEval e;
-  e.G = exp2f(-s2);
+  e.G = __builtin_amdgcn_exp2f(-s2);  // v_exp_f32; results below 2^-126 flush to 0 (alpha < 1/255)
   const float raw = o * e.G;
   e.capped = raw >= kAlphaMax;
   e.alpha = e.capped ? kAlphaMax : raw;

@@ -8,14 +8,17 @@
 // contributor, with the weights recomputed rather than stored.
 //
 // MI355X design:
-//  - one 256-thread workgroup (4 wave64) per 16 x 16 tile, one pixel per thread; Gaussians are
-//    staged 256 at a time in LDS as pre-scaled records (every lane then reads the same record:
-//    an LDS broadcast, no bank conflicts);
-//  - a wave leaves the batch loop as soon as all 64 of its pixels are done (wave-uniform test),
-//    the workgroup stops loading batches when all 256 are (__syncthreads_count);
-//  - workgroup -> tile mapping is XCD-aware: consecutive workgroup ids go round-robin to the 8
-//    XCDs, so each XCD is given a contiguous band of tiles and neighbouring tiles, which share
-//    most Gaussians, hit the same L2;
+//  - one 256-thread workgroup (4 wave64) per 16 x 16 tile, one pixel per thread, wave q owning
+//    the 8 x 8 quadrant q; Gaussians are staged 256 at a time in LDS as pre-scaled records (every
+//    lane then reads the same record: an LDS broadcast, no bank conflicts);
+//  - the loaders mark which quadrants each staged splat's pixel box reaches (64-lane ballots into
+//    four 256-bit masks); a wave walks only its mask's set bits, with a wave-uniform scalar loop,
+//    and a predicated (branch-free) body;
+//  - a wave leaves the batch as soon as all 64 of its pixels are done (wave-uniform test), the
+//    workgroup stops loading batches when all 256 are (__syncthreads_count);
+//  - workgroup b is tile b: consecutive tiles go round-robin to the 8 XCDs, which spreads the
+//    dense regions of a frame over all of them (the splat records of a frame are a few MB and
+//    stay cache-resident);
 //  - backward: the 9 per-splat gradient terms of a wave are summed with DPP row shifts and row
 //    broadcasts (7 VALU ops per value, lane 63 holds the sum), accumulated per workgroup in LDS
 //    (ds_add_f32), and flushed once per (tile, splat) with global fp32 atomics.
@@ -30,26 +33,36 @@ constexpr int kTile = 16;
 constexpr int kRasterThreads = kTile * kTile;  // 256: one pixel per thread
 constexpr int kBatch = kRasterThreads;         // splats staged per batch
 
-// XCD-aware tile index for workgroup b when the grid has 8 * per_xcd workgroups.
-__device__ __forceinline__ int tile_of_block(int b, int per_xcd) { return (b & 7) * per_xcd + (b >> 3); }
-
-// Pre-scaled splat record: (mx, my, hA, hC), (B2, o, r, g), b. hA = A/2 log2e, B2 = B log2e,
-// hC = C/2 log2e, so that log2(e) sigma = hA dx^2 + hC dy^2 + B2 dx dy.
+// Staged splat record: (mx, my, hA, hC), (B2, o, r, g), b. hA = A/2 log2e, B2 = B log2e,
+// hC = C/2 log2e, so that log2(e) sigma = hA dx^2 + hC dy^2 + B2 dx dy. Also returns the 4-bit
+// set of 8x8 quadrants of the tile that the splat's pixel box (radii + 1 px) reaches: outside
+// that box alpha < 1/255 at every pixel centre, so a quadrant it misses skips the splat anyway.
 // An id >= n (impossible for a well-formed sorted list) loads a record that never contributes.
-__device__ __forceinline__ void load_record(uint32_t g, uint32_t n, const float* __restrict__ means2d,
-                                            const float* __restrict__ conics, const float* __restrict__ opac,
-                                            const float* __restrict__ colors, float4& a, float4& b, float& c) {
+__device__ __forceinline__ uint32_t load_record(uint32_t g, uint32_t n, const float* __restrict__ means2d,
+                                                const float* __restrict__ conics, const float* __restrict__ opac,
+                                                const float* __restrict__ colors, const int32_t* __restrict__ radii,
+                                                float tx0, float ty0, float4& a, float4& b, float& c) {
   if (g >= n) {
     a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     b = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     c = 0.0f;
-    return;
+    return 0u;
   }
   const float2 m = *reinterpret_cast<const float2*>(means2d + 2 * g);
+  const int2 r = *reinterpret_cast<const int2*>(radii + 2 * g);
   const float A = conics[3 * g], B = conics[3 * g + 1], C = conics[3 * g + 2];
   a = make_float4(m.x, m.y, (0.5f * kLog2e) * A, (0.5f * kLog2e) * C);
   b = make_float4(kLog2e * B, opac[g], colors[3 * g], colors[3 * g + 1]);
   c = colors[3 * g + 2];
+  const float rx = (float)r.x + 1.0f, ry = (float)r.y + 1.0f;
+  uint32_t qm = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float x_lo = tx0 + (float)((q & 1) * 8) + 0.5f, y_lo = ty0 + (float)((q >> 1) * 8) + 0.5f;
+    const bool hit = (m.x + rx >= x_lo) && (m.x - rx <= x_lo + 7.0f) && (m.y + ry >= y_lo) && (m.y - ry <= y_lo + 7.0f);
+    qm |= hit ? (1u << q) : 0u;
+  }
+  return qm;
 }
 
 // Sum over the 64 lanes of a wave with DPP; the total lands in lane 63 (other lanes hold partial
@@ -70,23 +83,72 @@ __device__ __forceinline__ float wave_sum_lane63(float v) {
   return r;
 }
 
+// Adds the workgroup's evaluation count to *eval_count: one atomic per workgroup.
+__device__ __forceinline__ void count_evals(uint32_t n_eval, unsigned long long* eval_count) {
+  __shared__ uint32_t s_cnt;
+  if (threadIdx.x == 0) s_cnt = 0;
+  __syncthreads();
+  const float tot = wave_sum_lane63((float)n_eval);
+  if ((threadIdx.x & 63) == 63 && tot > 0.0f) atomicAdd(&s_cnt, (uint32_t)(tot + 0.5f));
+  __syncthreads();
+  if (threadIdx.x == 0 && s_cnt) atomicAdd(eval_count, (unsigned long long)s_cnt);
+}
+
+// A wave-uniform 64-bit value read from LDS, moved to scalar registers.
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Per batch, the loaders publish one 64-bit ballot per (quadrant, loading wave): bit j of
+// s_qm[q][w] says that staged splat 64 w + j reaches quadrant q. Wave q then walks its set bits.
+__device__ __forceinline__ void publish_quadrant_masks(uint32_t qm, bool valid, uint64_t (*s_qm)[4]) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint64_t b = __ballot(valid && ((qm >> q) & 1u));
+    if (lane == 0) s_qm[q][wave] = b;
+  }
+}
+
+// One front-to-back blend step of a pixel (section 5's loop body, predicated).
+__device__ __forceinline__ void blend_step(const SplatEval& e, bool act, float cr_, float cg_, float cb_, uint32_t idx,
+                                           float& T, float& cr, float& cg, float& cb, uint32_t& last, bool& done) {
+  const bool ok = act && !done && !e.skip;
+  const float nT = T * (1.0f - e.alpha);
+  const bool stop = ok && nT <= kTransmittanceMin;
+  const bool add = ok && !stop;
+  const float wgt = add ? e.alpha * T : 0.0f;
+  cr = fmaf(cr_, wgt, cr);
+  cg = fmaf(cg_, wgt, cg);
+  cb = fmaf(cb_, wgt, cb);
+  T = add ? nT : T;
+  last = add ? idx : last;
+  done = done || stop;
+}
+
 // ---------------------------------------------------------------------------------------------
-// k-blend
+// k-blend: one 256-thread workgroup per 16x16 tile; wave q owns the 8x8 quadrant q and walks its
+// splats two per iteration (their alphas are independent; the T updates are sequential).
 // ---------------------------------------------------------------------------------------------
+template <bool COUNT>
 __global__ __launch_bounds__(kRasterThreads) void k_blend(
     uint32_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ ids, const float* __restrict__ means2d,
     const float* __restrict__ conics, const float* __restrict__ opac, const float* __restrict__ colors,
-    DevCamera cam, int per_xcd, float* __restrict__ image, float* __restrict__ final_T,
+    const int32_t* __restrict__ radii, DevCamera cam, float* __restrict__ image, float* __restrict__ final_T,
     uint32_t* __restrict__ n_contrib, unsigned long long* __restrict__ eval_count) {
   __shared__ float4 s_a[kBatch];
   __shared__ float4 s_b[kBatch];
   __shared__ float s_c[kBatch];
+  __shared__ uint64_t s_qm[4][4];
 
-  const int tile = tile_of_block(blockIdx.x, per_xcd);
-  if (tile >= cam.tiles_x * cam.tiles_y) return;  // whole workgroup: uniform
-  const int tid = threadIdx.x;
-  const int px_i = (tile % cam.tiles_x) * kTile + (tid & (kTile - 1));
-  const int py_i = (tile / cam.tiles_x) * kTile + (tid / kTile);
+  const int tile = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tx = tile % cam.tiles_x, ty = tile / cam.tiles_x;
+  const float tx0 = (float)(tx * kTile), ty0 = (float)(ty * kTile);
+  const int px_i = tx * kTile + (wave & 1) * 8 + (lane & 7);
+  const int py_i = ty * kTile + (wave >> 1) * 8 + (lane >> 3);
   const bool inside = px_i < cam.W && py_i < cam.H;
   const float px = (float)px_i + 0.5f, py = (float)py_i + 0.5f;
   const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
@@ -97,28 +159,30 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
   for (uint32_t bs = start; bs < end; bs += kBatch) {
     if (__syncthreads_count(done) == kRasterThreads) break;
     const uint32_t j = bs + tid;
-    if (j < end) load_record(ids[j], n, means2d, conics, opac, colors, s_a[tid], s_b[tid], s_c[tid]);
+    uint32_t qm = 0;
+    if (j < end) qm = load_record(ids[j], n, means2d, conics, opac, colors, radii, tx0, ty0, s_a[tid], s_b[tid], s_c[tid]);
+    publish_quadrant_masks(qm, j < end, s_qm);
     __syncthreads();
-    const int cnt = (end - bs) < (uint32_t)kBatch ? (int)(end - bs) : kBatch;
-    for (int k = 0; k < cnt; ++k) {
-      if (!__any(!done)) break;
-      if (done) continue;
-      const float4 a = s_a[k];
-      const float4 b = s_b[k];
-      const SplatEval e = eval_splat(a.x - px, a.y - py, a.z, b.x, a.w, b.y);
-      ++n_eval;
-      if (e.skip) continue;
-      const float nT = T * (1.0f - e.alpha);
-      if (nT <= kTransmittanceMin) {
-        done = true;
-        continue;
+    const uint32_t base_idx = bs - start + 1u;
+    for (int w = 0; w < 4; ++w) {
+      uint64_t m = uniform64(s_qm[wave][w]);
+      while (m) {
+        if (!__any(!done)) break;
+        const int bit0 = __builtin_ctzll(m);
+        m &= m - 1;
+        const bool has1 = m != 0;
+        const int bit1 = has1 ? __builtin_ctzll(m) : bit0;
+        m &= has1 ? m - 1 : m;
+        const int k0 = w * 64 + bit0, k1 = w * 64 + bit1;
+        const float4 a0 = s_a[k0], b0 = s_b[k0];
+        const float4 a1 = s_a[k1], b1 = s_b[k1];
+        const float c0 = s_c[k0], c1 = s_c[k1];
+        const SplatEval e0 = eval_splat(a0.x - px, a0.y - py, a0.z, b0.x, a0.w, b0.y);
+        const SplatEval e1 = eval_splat(a1.x - px, a1.y - py, a1.z, b1.x, a1.w, b1.y);
+        if (COUNT) n_eval += (done ? 0u : 1u) + ((done || !has1) ? 0u : 1u);
+        blend_step(e0, true, b0.z, b0.w, c0, base_idx + (uint32_t)k0, T, cr, cg, cb, last, done);
+        blend_step(e1, has1, b1.z, b1.w, c1, base_idx + (uint32_t)k1, T, cr, cg, cb, last, done);
       }
-      const float w = e.alpha * T;
-      cr = fmaf(b.z, w, cr);
-      cg = fmaf(b.w, w, cg);
-      cb = fmaf(s_c[k], w, cb);
-      T = nT;
-      last = bs + (uint32_t)k - start + 1u;
     }
   }
   if (inside) {
@@ -129,32 +193,97 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
     final_T[p] = T;
     n_contrib[p] = last;
   }
-  if (eval_count) {
-    const float tot = wave_sum_lane63((float)n_eval);
-    if ((tid & 63) == 63) atomicAdd(eval_count, (unsigned long long)(tot + 0.5f));
+  if (COUNT) count_evals(n_eval, eval_count);
+}
+
+// Adds the nine per-lane gradient terms v[0..8] of one splat, summed over the wave, into
+// acc[0..8] (LDS). Reduce-scatter within each 8-lane group: three DPP exchanges (pairs l^7, l^3,
+// l^1) halve the values a lane holds each time, leaving lane l with term (l & 7) summed over its
+// group; a row rotation by 8 adds the other half of the 16-lane row. One LDS atomic from lanes
+// 0-7 of each row then adds eight terms at once (four rows per address). Term 8 is summed along
+// each row separately. 27 VALU per splat instead of 63 for nine full wave reductions.
+template <int CTRL>
+__device__ __forceinline__ float dppx(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ void reduce9_to_lds(const float* v, float* acc, int lane) {
+  const bool b2 = (lane & 4) != 0, b1 = (lane & 2) != 0, b0 = (lane & 1) != 0;
+  float u[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float send = b2 ? v[j] : v[j + 4];
+    const float keep = b2 ? v[j + 4] : v[j];
+    u[j] = keep + dppx<0x141>(send);  // row_half_mirror: lane l <-> l ^ 7
   }
+  float w[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float send = b1 ? u[j] : u[j + 2];
+    const float keep = b1 ? u[j + 2] : u[j];
+    w[j] = keep + dppx<0x1B>(send);  // quad_perm [3,2,1,0]: l <-> l ^ 3
+  }
+  float x = (b0 ? w[1] : w[0]) + dppx<0xB1>(b0 ? w[0] : w[1]);  // quad_perm [1,0,3,2]: l <-> l ^ 1
+  x = x + dppx<0x128>(x);                                          // row_ror:8
+  float y = v[8] + dppx<0x111>(v[8]);
+  y = y + dppx<0x112>(v[8]);
+  y = y + dppx<0x113>(v[8]);
+  y = y + dppx<0x114>(y);
+  y = y + dppx<0x118>(y);  // lane 15 of each row holds the row's sum of term 8
+  if ((lane & 15) < 8) unsafeAtomicAdd(acc + (lane & 7), x);
+  if ((lane & 15) == 15) unsafeAtomicAdd(acc + 8, y);
+}
+
+// Per-lane gradient terms of one splat for one pixel, back to front: consumes T (the
+// transmittance behind the splat) and gS = g . S, returns them updated to the front of it.
+__device__ __forceinline__ void splat_grad(bool contrib, const SplatEval& ev, float dx, float dy, const float4& a,
+                                           const float4& b, float cb, float gr, float gg, float gb, float& T,
+                                           float& gS, float* v) {
+  const float inv = 1.0f / (1.0f - ev.alpha);
+  const float Ti = contrib ? T * inv : T;  // T_i, the transmittance in front of this splat
+  const float gc = fmaf(gr, b.z, fmaf(gg, b.w, gb * cb));
+  const float g_alpha = fmaf(Ti, gc, -gS * inv);  // dL/dalpha = g . (c T_i - S / (1 - alpha))
+  const float wT = contrib ? ev.alpha * Ti : 0.0f;
+  gS = fmaf(gc, wT, gS);
+  T = Ti;
+  const float gsig = (contrib && !ev.capped) ? -ev.alpha * g_alpha : 0.0f;  // dL/dsigma
+  constexpr float inv_l2e = 1.0f / kLog2e;
+  v[0] = gsig * (fmaf(2.0f * a.z, dx, b.x * dy) * inv_l2e);  // dsigma/dmx = A dx + B dy
+  v[1] = gsig * (fmaf(2.0f * a.w, dy, b.x * dx) * inv_l2e);  // dsigma/dmy = B dx + C dy
+  v[2] = (0.5f * gsig) * (dx * dx);
+  v[3] = gsig * (dx * dy);
+  v[4] = (0.5f * gsig) * (dy * dy);
+  v[5] = (contrib && !ev.capped) ? ev.G * g_alpha : 0.0f;
+  v[6] = wT * gr;
+  v[7] = wT * gg;
+  v[8] = wT * gb;
 }
 
 // ---------------------------------------------------------------------------------------------
-// k-rbwd
+// k-rbwd: same tiling; each wave walks its quadrant's splats back to front from the last
+// contributor of its pixels, recovering T_i = T_{i+1} / (1 - alpha_i), two splats per
+// iteration (their alphas are independent; only the T / g.S updates are sequential).
 // ---------------------------------------------------------------------------------------------
+template <bool COUNT>
 __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
     uint32_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ ids, const float* __restrict__ means2d,
     const float* __restrict__ conics, const float* __restrict__ opac, const float* __restrict__ colors,
-    DevCamera cam, int per_xcd, const float* __restrict__ final_T, const uint32_t* __restrict__ n_contrib,
-    const float* __restrict__ dL_dimage, float* __restrict__ g2d, unsigned long long* __restrict__ eval_count) {
+    const int32_t* __restrict__ radii, DevCamera cam, const float* __restrict__ final_T,
+    const uint32_t* __restrict__ n_contrib, const float* __restrict__ dL_dimage, float* __restrict__ g2d,
+    unsigned long long* __restrict__ eval_count) {
   __shared__ float4 s_a[kBatch];
   __shared__ float4 s_b[kBatch];
   __shared__ float s_c[kBatch];
   __shared__ uint32_t s_id[kBatch];
-  __shared__ float s_acc[9][kBatch];
+  __shared__ float s_acc[kBatch * 9];
+  __shared__ uint64_t s_qm[4][4];
   __shared__ uint32_t s_max;
 
-  const int tile = tile_of_block(blockIdx.x, per_xcd);
-  if (tile >= cam.tiles_x * cam.tiles_y) return;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int px_i = (tile % cam.tiles_x) * kTile + (tid & (kTile - 1));
-  const int py_i = (tile / cam.tiles_x) * kTile + (tid / kTile);
+  const int tile = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tx = tile % cam.tiles_x, ty = tile / cam.tiles_x;
+  const float tx0 = (float)(tx * kTile), ty0 = (float)(ty * kTile);
+  const int px_i = tx * kTile + (wave & 1) * 8 + (lane & 7);
+  const int py_i = ty * kTile + (wave >> 1) * 8 + (lane >> 3);
   const bool inside = px_i < cam.W && py_i < cam.H;
   const float px = (float)px_i + 0.5f, py = (float)py_i + 0.5f;
   const uint32_t start = ranges[2 * tile];
@@ -169,7 +298,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
     gg = dL_dimage[3 * p + 1];
     gb = dL_dimage[3 * p + 2];
   }
-  // g . S with S = (sum over splats behind) + T_final bg, carried as one scalar
+  // g . S with S = (what lies behind, composited) + T_final bg, carried as one scalar
   float gS = T * ((gr * cam.bg[0] + gg * cam.bg[1]) + gb * cam.bg[2]);
   if (tid == 0) s_max = 0;
   __syncthreads();
@@ -182,58 +311,40 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
     const uint32_t bstart = bend > (uint32_t)kBatch ? bend - kBatch : 0u;
     const int cnt = (int)(bend - bstart);
     __syncthreads();
+    uint32_t qm = 0;
     if (tid < cnt) {
-      const uint32_t e = bend - 1u - (uint32_t)tid;  // reversed: slot k holds entry bend-1-k
-      const uint32_t g = ids[start + e];
+      const uint32_t g = ids[start + bstart + (uint32_t)tid];
       s_id[tid] = g;
-      load_record(g, n, means2d, conics, opac, colors, s_a[tid], s_b[tid], s_c[tid]);
-#pragma unroll
-      for (int c = 0; c < 9; ++c) s_acc[c][tid] = 0.0f;
+      qm = load_record(g, n, means2d, conics, opac, colors, radii, tx0, ty0, s_a[tid], s_b[tid], s_c[tid]);
     }
+    for (int i = tid; i < cnt * 9; i += kRasterThreads) s_acc[i] = 0.0f;
+    publish_quadrant_masks(qm, tid < cnt, s_qm);
     __syncthreads();
-    for (int k = 0; k < cnt; ++k) {
-      const uint32_t e = bend - 1u - (uint32_t)k;
-      const bool active = e < nc;
-      if (!__any(active)) continue;
-      float v[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
-      bool contrib = false;
-      if (active) {
-        const float4 a = s_a[k];
-        const float4 b = s_b[k];
-        const float dx = a.x - px, dy = a.y - py;
-        const SplatEval ev = eval_splat(dx, dy, a.z, b.x, a.w, b.y);
-        ++n_eval;
-        if (!ev.skip) {
-          contrib = true;
-          const float one_m = 1.0f - ev.alpha;
-          const float inv = 1.0f / one_m;
-          T = T * inv;  // T_i, the transmittance in front of this splat
-          const float cr = b.z, cg = b.w, cb = s_c[k];
-          const float gc = fmaf(gr, cr, fmaf(gg, cg, gb * cb));
-          const float g_alpha = fmaf(T, gc, -gS * inv);
-          const float wT = ev.alpha * T;
-          gS = fmaf(gc, wT, gS);
-          v[6] = wT * gr;
-          v[7] = wT * gg;
-          v[8] = wT * gb;
-          if (!ev.capped) {
-            v[5] = ev.G * g_alpha;
-            const float gsig = -ev.alpha * g_alpha;  // dL/dsigma
-            // sigma = A/2 dx^2 + C/2 dy^2 + B dx dy; A = 2 hA / log2e etc.
-            v[2] = 0.5f * gsig * dx * dx;
-            v[3] = gsig * dx * dy;
-            v[4] = 0.5f * gsig * dy * dy;
-            const float inv_l2e = 1.0f / kLog2e;
-            v[0] = gsig * (fmaf(2.0f * a.z, dx, b.x * dy) * inv_l2e);
-            v[1] = gsig * (fmaf(2.0f * a.w, dy, b.x * dx) * inv_l2e);
-          }
-        }
-      }
-      if (!__any(contrib)) continue;
-#pragma unroll
-      for (int c = 0; c < 9; ++c) {
-        const float s = wave_sum_lane63(v[c]);
-        if (lane == 63 && s != 0.0f) unsafeAtomicAdd(&s_acc[c][k], s);
+    for (int w = 3; w >= 0; --w) {
+      uint64_t m = uniform64(s_qm[wave][w]);  // walked from the highest set bit down
+      while (m) {
+        const int bit0 = 63 - __builtin_clzll(m);
+        m &= ~(1ull << bit0);
+        const bool has1 = m != 0;
+        const int bit1 = has1 ? 63 - __builtin_clzll(m) : bit0;
+        if (has1) m &= ~(1ull << bit1);
+        const int k0 = w * 64 + bit0, k1 = w * 64 + bit1;
+        const bool act0 = bstart + (uint32_t)k0 < nc;
+        const bool act1 = has1 && (bstart + (uint32_t)k1 < nc);
+        if (!__any(act0 || act1)) continue;
+        const float4 a0 = s_a[k0], b0 = s_b[k0];
+        const float4 a1 = s_a[k1], b1 = s_b[k1];
+        const float cb0 = s_c[k0], cb1 = s_c[k1];
+        const float dx0 = a0.x - px, dy0 = a0.y - py, dx1 = a1.x - px, dy1 = a1.y - py;
+        const SplatEval e0 = eval_splat(dx0, dy0, a0.z, b0.x, a0.w, b0.y);
+        const SplatEval e1 = eval_splat(dx1, dy1, a1.z, b1.x, a1.w, b1.y);
+        if (COUNT) n_eval += (act0 ? 1u : 0u) + (act1 ? 1u : 0u);
+        const bool c0 = act0 && !e0.skip, c1 = act1 && !e1.skip;
+        float v0[9], v1[9];
+        splat_grad(c0, e0, dx0, dy0, a0, b0, cb0, gr, gg, gb, T, gS, v0);
+        splat_grad(c1, e1, dx1, dy1, a1, b1, cb1, gr, gg, gb, T, gS, v1);
+        if (__any(c0)) reduce9_to_lds(v0, s_acc + k0 * 9, lane);
+        if (__any(c1)) reduce9_to_lds(v1, s_acc + k1 * 9, lane);
       }
     }
     __syncthreads();
@@ -241,16 +352,13 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
       float* dst = g2d + (size_t)s_id[tid] * 9;
 #pragma unroll
       for (int c = 0; c < 9; ++c) {
-        const float s = s_acc[c][tid];
-        if (s != 0.0f) unsafeAtomicAdd(dst + c, s);
+        const float s9 = s_acc[tid * 9 + c];
+        if (s9 != 0.0f) unsafeAtomicAdd(dst + c, s9);
       }
     }
     bend = bstart;
   }
-  if (eval_count) {
-    const float tot = wave_sum_lane63((float)n_eval);
-    if (lane == 63) atomicAdd(eval_count, (unsigned long long)(tot + 0.5f));
-  }
+  if (COUNT) count_evals(n_eval, eval_count);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -504,10 +612,6 @@ bool proj_ok(const gs_projected* p) {
   return p && p->d_means2d && p->d_conics && p->d_depths && p->d_opacities && p->d_colors && p->d_radii &&
          p->d_tiles_touched;
 }
-int per_xcd_for(const gs_camera* cam) {
-  const int ntiles = ((cam->width + 15) / 16) * ((cam->height + 15) / 16);
-  return (ntiles + 7) / 8;
-}
 }  // namespace
 
 extern "C" gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const gs_camera* cam,
@@ -522,15 +626,16 @@ extern "C" gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const
   if (n > 0 && (!proj_ok(proj) || !d_ids)) return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: NULL input");
   const int64_t ntiles = (int64_t)((cam->width + 15) / 16) * ((cam->height + 15) / 16);
   if (ntiles > ((int64_t)1 << 24)) return set_error(GS_ERR_LIMIT, "gs_rasterize_fwd: more than 2^24 tiles");
-  const int per_xcd = per_xcd_for(cam);
   const DevCamera dc = to_dev(*cam);
   hipStream_t s = (hipStream_t)stream;
   {
     TimedScope ts("blend", s);
-    hipLaunchKernelGGL(k_blend, dim3(8 * per_xcd), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges, d_ids,
+    auto kern = d_eval_count ? k_blend<true> : k_blend<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges, d_ids,
                        n > 0 ? proj->d_means2d : nullptr, n > 0 ? proj->d_conics : nullptr,
-                       n > 0 ? proj->d_opacities : nullptr, n > 0 ? proj->d_colors : nullptr, dc, per_xcd, d_image,
-                       d_final_T, d_n_contrib, (unsigned long long*)d_eval_count);
+                       n > 0 ? proj->d_opacities : nullptr, n > 0 ? proj->d_colors : nullptr,
+                       n > 0 ? proj->d_radii : nullptr, dc, d_image, d_final_T, d_n_contrib,
+                       (unsigned long long*)d_eval_count);
   }
   return check_launch("gs_rasterize_fwd");
 }
@@ -562,7 +667,6 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float*
     return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_bwd: quaternion arrays must be 16-byte aligned");
   const int64_t ntiles = (int64_t)((cam->width + 15) / 16) * ((cam->height + 15) / 16);
   if (ntiles > ((int64_t)1 << 24)) return set_error(GS_ERR_LIMIT, "gs_rasterize_bwd: more than 2^24 tiles");
-  const int per_xcd = per_xcd_for(cam);
   const DevCamera dc = to_dev(*cam);
   hipStream_t s = (hipStream_t)stream;
   float* g2d = (float*)d_workspace;
@@ -574,10 +678,10 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float*
   }
   {
     TimedScope ts("rbwd", s);
-    hipLaunchKernelGGL(k_rbwd, dim3(8 * per_xcd), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges, d_ids,
-                       proj->d_means2d,
-                       proj->d_conics, proj->d_opacities, proj->d_colors, dc, per_xcd, d_final_T, d_n_contrib,
-                       d_dL_dimage, g2d, (unsigned long long*)d_eval_count);
+    auto kern = d_eval_count ? k_rbwd<true> : k_rbwd<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges, d_ids,
+                       proj->d_means2d, proj->d_conics, proj->d_opacities, proj->d_colors, proj->d_radii, dc,
+                       d_final_T, d_n_contrib, d_dL_dimage, g2d, (unsigned long long*)d_eval_count);
   }
   {
     TimedScope ts("pbwd", s);
