@@ -53,10 +53,9 @@ def kernel_bytes(name, stats):
     """Algorithmic HBM bytes of one launch of a binning kernel."""
     P, N = stats["pairs"], stats["n"]
     return {
-        "depth_prep": 16.0 * N,
+        "bin_prep": 16.0 * N,
         "depth_sort_pass": 16.0 * N,
-        "scan": 12.0 * N,
-        "emit": 8.0 * P + 24.0 * stats["visible"],
+        "scan_emit": 8.0 * N + 8.0 * P + 16.0 * stats["visible"],
         "pair_sort_pass": 16.0 * P + 4.0 * P / stats["pair_passes"],
         "ranges": 8.0 * P,
         "project": stats["project_bytes"],
@@ -152,17 +151,17 @@ def main():
         pipe.project(cam)
         pairs.append(pipe.bin(cam))
     need = max(pairs)
-    if pipe.capacity < need:
-        pipe._alloc_pairs(int(need * 1.1) + 1024)
+    pipe.reserve_pairs(int(need * 1.1) + 1024)
     ncam = len(cams)
 
     def step(i):
+        # no host wait anywhere in a step: the pair buffers already hold every camera's pairs
         c = i % ncam
         if wl.backward:
-            pipe.iteration(cams[c], targets[c])
+            pipe.iteration(cams[c], targets[c], wait=False)
         else:
             pipe.project(cams[c])
-            pipe.bin(cams[c])
+            pipe.bin(cams[c], wait=False)
             pipe.forward(cams[c])
 
     for i in range(args.warmup):
@@ -175,6 +174,8 @@ def main():
     t1 = time.perf_counter()
     elapsed = t1 - t0
     its = args.steps / elapsed
+    last = (args.warmup + args.steps - 1) % ncam
+    assert int(pipe.num_pairs_dev.item()) == pairs[last] <= pipe.capacity, "pair count changed between runs"
     steps_pairs = sum(pairs[(args.warmup + i) % ncam] for i in range(args.steps))
 
     result = {
@@ -203,7 +204,7 @@ def main():
         for i in range(nprof):
             c = (args.warmup + i) % ncam
             pipe.project(cams[c])
-            pipe.bin(cams[c])
+            pipe.bin(cams[c], wait=False)
             pipe.forward(cams[c], eval_count=evals_f)
             if wl.backward:
                 pipe.loss_l1(targets[c])
@@ -217,7 +218,7 @@ def main():
         visible = int((pipe.proj.tiles_touched > 0).sum().item())
         K = (wl.sh_degree + 1) ** 2
         stats = {"pairs": float(np.mean(pairs)), "n": wl.n, "visible": visible, "pixels": W * H,
-                 "pair_passes": max(1, per.get("pair_sort_pass", [0, 1])[1] // max(1, per.get("emit", [0, 1])[1])),
+                 "pair_passes": max(1, per.get("pair_sort_pass", [0, 1])[1] // max(1, per.get("scan_emit", [0, 1])[1])),
                  "project_bytes": wl.n * (4 * (3 + 3 + 4 + 1 + 3 * K) + 52)}
         kernels = {}
         for name, (tot, cnt) in sorted(per.items(), key=lambda kv: -kv[1][0]):
@@ -240,7 +241,7 @@ def main():
                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(dom), "kernel": dom,
                     "bytes_per_launch": b, "avg_us": avg_s * 1e6}
         result["roofline"] = roof
-        bin_names = ("depth_prep", "depth_sort_pass", "scan", "emit", "pair_sort_pass", "ranges")
+        bin_names = ("bin_prep", "hist_reduce", "depth_sort_pass", "scan_emit", "pair_sort_pass", "ranges")
         bin_s = sum(per[k][0] for k in bin_names if k in per) / 1e3 / nprof
         bin_b = sum((kernel_bytes(k, stats) or 0.0) * per[k][1] for k in bin_names if k in per) / nprof
         result["bin_sort"] = {"kernel_us_per_step": bin_s * 1e6, "bytes_per_step": bin_b,

@@ -57,7 +57,7 @@ def load():
     sig = {
         "gs_project": (i32, [i32, i32, P, P, P, P, P, cam_p, proj_p, P]),
         "gs_bin_workspace_bytes": (sz, [i32, i64, cam_p]),
-        "gs_bin_and_sort": (i32, [i32, proj_p, cam_p, P, sz, i64, P, P, P, ctypes.POINTER(ctypes.c_int64), P]),
+        "gs_bin_and_sort": (i32, [i32, proj_p, cam_p, P, sz, i64, P, P, P, P, ctypes.POINTER(ctypes.c_int64), P]),
         "gs_rasterize_fwd": (i32, [i32, proj_p, cam_p, P, P, P, P, P, P, P]),
         "gs_bwd_workspace_bytes": (sz, [i32]),
         "gs_rasterize_bwd": (i32, [i32, i32, P, P, P, P, P, cam_p, proj_p, P, P, P, P, P, P, sz, P, P, P, P, P, P, P, P]),
@@ -128,14 +128,17 @@ def gs_bin_workspace_bytes(n, pair_capacity, cam: GsCamera) -> int:
 
 
 def gs_bin_and_sort(n, proj: "Projected", cam: GsCamera, workspace, pair_capacity, keys, ids, tile_ranges,
-                    stream=None):
-    """Returns (status, P); status is GS_OK or GS_ERR_CAPACITY (then P is the count needed)."""
+                    num_pairs_dev=None, stream=None, wait=True):
+    """With wait=True returns (status, P): status is GS_OK or GS_ERR_CAPACITY (P = the count
+    needed). With wait=False nothing waits and it returns (GS_OK, None); P goes to num_pairs_dev
+    (a one-element int64 CUDA tensor) when given."""
     P = ctypes.c_int64(0)
     st = _check(load().gs_bin_and_sort(n, ctypes.byref(proj.struct()), ctypes.byref(cam), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), pair_capacity, _ptr(keys),
-                                       _ptr(ids), _ptr(tile_ranges), ctypes.byref(P), _stream(stream)),
+                                       _ptr(ids), _ptr(tile_ranges), _ptr(num_pairs_dev),
+                                       ctypes.byref(P) if wait else None, _stream(stream)),
                 allow=(GS_ERR_CAPACITY,))
-    return st, int(P.value)
+    return st, (int(P.value) if wait else None)
 
 
 def gs_rasterize_fwd(n, proj: "Projected", cam: GsCamera, ids, tile_ranges, image, final_T, n_contrib,
@@ -234,6 +237,7 @@ class Pipeline:
                       "quats": torch.empty(self.n, 4, **f), "opacity_logits": torch.empty(self.n, **f),
                       "sh": torch.empty(self.n, K, 3, **f), "means2d": torch.empty(self.n, 2, **f)}
         self.num_pairs = 0
+        self.num_pairs_dev = torch.zeros(1, device=device, dtype=torch.int64)
         self._alloc_pairs(pair_capacity)
 
     def _alloc_pairs(self, cap):
@@ -250,15 +254,28 @@ class Pipeline:
         gs_project(self.n, p["sh_degree"], p["means"], p["log_scales"], p["quats"], p["opacity_logits"], p["sh"],
                    cam, self.proj, stream)
 
-    def bin(self, cam: GsCamera, stream=None):
+    def bin(self, cam: GsCamera, stream=None, wait=True):
+        """Bin and sort. wait=True reads P on the host and regrows the pair buffers when they
+        overflow; wait=False only enqueues (P lands in self.num_pairs_dev; an overflow leaves every
+        tile empty and shows as self.num_pairs_dev > self.capacity)."""
+        if not wait:
+            gs_bin_and_sort(self.n, self.proj, cam, self.bin_ws, self.capacity, self.keys, self.ids, self.ranges,
+                            self.num_pairs_dev, stream, wait=False)
+            self.num_pairs = None
+            return None
         st, P = gs_bin_and_sort(self.n, self.proj, cam, self.bin_ws, self.capacity, self.keys, self.ids,
-                                self.ranges, stream)
+                                self.ranges, self.num_pairs_dev, stream)
         if st == GS_ERR_CAPACITY:
             self._alloc_pairs(int(P * 1.25) + 1024)
             st, P = gs_bin_and_sort(self.n, self.proj, cam, self.bin_ws, self.capacity, self.keys, self.ids,
-                                    self.ranges, stream)
+                                    self.ranges, self.num_pairs_dev, stream)
         self.num_pairs = P
         return P
+
+    def reserve_pairs(self, cap):
+        """Grow the pair buffers to at least cap pairs (for runs that do not wait on bin)."""
+        if cap > self.capacity:
+            self._alloc_pairs(int(cap))
 
     def forward(self, cam: GsCamera, eval_count=None, stream=None):
         gs_rasterize_fwd(self.n, self.proj, cam, self.ids, self.ranges, self.image, self.final_T, self.n_contrib,
@@ -274,10 +291,11 @@ class Pipeline:
                          self.dL_dimage if dL_dimage is None else dL_dimage, self.bwd_ws, g["means"], g["log_scales"],
                          g["quats"], g["opacity_logits"], g["sh"], g["means2d"], eval_count, stream)
 
-    def iteration(self, cam: GsCamera, target, stream=None):
-        """One fwd+bwd iteration: project, bin+sort, blend, L1 gradient, backward."""
+    def iteration(self, cam: GsCamera, target, stream=None, wait=True):
+        """One fwd+bwd iteration: project, bin+sort, blend, L1 gradient, backward. wait=False runs
+        it without any host wait (the pair buffers must already be large enough)."""
         self.project(cam, stream)
-        self.bin(cam, stream)
+        self.bin(cam, stream, wait=wait)
         self.forward(cam, stream=stream)
         self.loss_l1(target, stream=stream)
         self.backward(cam, stream=stream)

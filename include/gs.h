@@ -15,7 +15,8 @@
  *    Arrays are contiguous, row-major, fp32 unless typed otherwise. The caller allocates and owns
  *    every buffer; the library never frees or retains a caller pointer after a call returns.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls enqueue work on
- *    it and return without waiting, except gs_bin_and_sort, which waits once for the pair count.
+ *    it and return without waiting, except gs_bin_and_sort when asked for the pair count on the
+ *    host (h_num_pairs != NULL), which waits once for it.
  *  - Every call returns a gs_status; on anything but GS_OK, gs_last_error() describes it and no
  *    output has been written past what the status documents. No exception crosses the ABI.
  *  - Calls with disjoint buffers may run concurrently on different streams.
@@ -40,7 +41,7 @@ typedef enum gs_status {
   GS_OK = 0,
   GS_ERR_INVALID_ARG = 1, /* bad size, NULL pointer, degree, or a non-finite camera */
   GS_ERR_CAPACITY = 2,    /* the pair buffers are too small: *h_num_pairs holds the need */
-  GS_ERR_LIMIT = 3,       /* a size beyond what the kernels index (pairs >= 2^31, tiles > 2^24) */
+  GS_ERR_LIMIT = 3,       /* a size beyond what the kernels index (n or capacity >= 2^30, tiles > 2^24) */
   GS_ERR_DEVICE = 4       /* a HIP runtime error; gs_last_error() has its text */
 } gs_status;
 
@@ -103,18 +104,26 @@ gs_status gs_project(int32_t n, int32_t sh_degree, const float* d_means, const f
  * of the pairs by tile id (Onesweep-style single-pass passes with decoupled look-back).
  * Inputs: n and proj (from gs_project with the same camera); d_workspace of at least
  *   gs_bin_workspace_bytes(n, pair_capacity, cam) bytes (device, 256-byte aligned, contents
- *   need not persist between calls); pair_capacity = length of d_keys and d_ids.
- * Outputs: d_keys [P] uint64, d_ids [P] uint32, d_tile_ranges [tiles, 2] uint32,
- *   *h_num_pairs = P (host). d_keys doubles as scratch during the call.
- * Waits on `stream` once, to read P. If P > pair_capacity it returns GS_ERR_CAPACITY with
- *   *h_num_pairs = P and writes nothing to d_keys, d_ids or d_tile_ranges.
- * Errors: GS_ERR_INVALID_ARG (as gs_project, or a workspace below the size needed),
- *   GS_ERR_LIMIT (P >= 2^31 or more than 2^24 tiles).
+ *   arbitrary on entry and need not persist between calls); pair_capacity = length of d_keys
+ *   and d_ids.
+ * Outputs: d_keys [P] uint64, d_ids [P] uint32, d_tile_ranges [tiles, 2] uint32; P itself goes
+ *   to *d_num_pairs (device int64, optional, written on `stream`) and to *h_num_pairs (host,
+ *   optional). d_keys doubles as scratch during the call.
+ * Waiting: with h_num_pairs == NULL nothing waits: the call only enqueues kernels, sized by the
+ *   capacity, that stop at the device-side count. With h_num_pairs != NULL it waits once on
+ *   `stream` to read P and returns GS_ERR_CAPACITY when P > pair_capacity.
+ * Capacity overflow (P > pair_capacity): every tile range is (0, 0), so a later blend draws the
+ *   background only; the first pair_capacity entries of d_keys/d_ids hold unspecified values and
+ *   nothing past them is written; P is still reported in full. Callers that do not wait check
+ *   *d_num_pairs <= pair_capacity later.
+ * Errors: GS_ERR_INVALID_ARG (as gs_project, or a workspace below the size needed, or a
+ *   misaligned d_workspace / d_keys / d_num_pairs), GS_ERR_LIMIT (n or pair_capacity >= 2^30,
+ *   or more than 2^24 tiles).
  */
 size_t gs_bin_workspace_bytes(int32_t n, int64_t pair_capacity, const gs_camera* cam);
 gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const gs_camera* cam, void* d_workspace,
                           size_t workspace_bytes, int64_t pair_capacity, uint64_t* d_keys, uint32_t* d_ids,
-                          uint32_t* d_tile_ranges, int64_t* h_num_pairs, void* stream);
+                          uint32_t* d_tile_ranges, int64_t* d_num_pairs, int64_t* h_num_pairs, void* stream);
 
 /*
  * gs_rasterize_fwd -- per-pixel front-to-back alpha blending over the pixel's tile list (section

@@ -170,21 +170,51 @@ def test_empty_and_all_culled(env):
             assert all(np.all(v.cpu().numpy() == 0) for v in pipe.grads.values())
 
 
-def test_capacity_error_writes_nothing(env):
+def test_capacity_overflow_contract(env):
+    # P > capacity: GS_ERR_CAPACITY with P in full (host and device), every range empty, nothing
+    # written past the capacity; the same without the host wait; capacity 0 with n > 0
     gs, torch = env
     wl = synth.WORKLOADS["tiny_1k"]
     cam_d = synth.make_cameras(wl)[0]
     params, cam, proj = run_gpu_project(gs, torch, synth.make_scene(wl), cam_d)
     need = int(proj.tiles_touched.sum().item())
-    cap = need - 1
-    keys = torch.full((cap,), -7, device="cuda", dtype=torch.int64)
-    ids = torch.full((cap,), -7, device="cuda", dtype=torch.int32)
-    ranges = torch.full((64, 2), -7, device="cuda", dtype=torch.int32)
-    ws = torch.empty(gs.gs_bin_workspace_bytes(params["n"], cap, cam), device="cuda", dtype=torch.uint8)
-    st, P = gs.gs_bin_and_sort(params["n"], proj, cam, ws, cap, keys, ids, ranges)
+    tiles = ((cam.width + 15) // 16) * ((cam.height + 15) // 16)
+    for cap in (need - 1, need // 3, 0):
+        for wait in (True, False):
+            print(f"capacity {cap} of {need}, wait={wait}", flush=True)
+            keys = torch.full((cap + 64,), -7, device="cuda", dtype=torch.int64)
+            ids = torch.full((cap + 64,), -7, device="cuda", dtype=torch.int32)
+            ranges = torch.full((tiles, 2), -7, device="cuda", dtype=torch.int32)
+            pdev = torch.full((1,), -7, device="cuda", dtype=torch.int64)
+            ws = torch.empty(gs.gs_bin_workspace_bytes(params["n"], cap, cam), device="cuda", dtype=torch.uint8)
+            ws.fill_(0xAB)  # the workspace's contents on entry are arbitrary
+            st, P = gs.gs_bin_and_sort(params["n"], proj, cam, ws, cap, keys, ids, ranges, pdev, wait=wait)
+            torch.cuda.synchronize()
+            if wait:
+                assert st == gs.GS_ERR_CAPACITY and P == need
+            else:
+                assert st == gs.GS_OK and P is None
+            assert int(pdev.item()) == need
+            assert torch.all(ranges == 0)
+            assert torch.all(keys[cap:] == -7) and torch.all(ids[cap:] == -7)
+
+
+def test_async_bin_matches_waiting_bin(env):
+    gs, torch = env
+    wl = synth.WORKLOADS["distill_30k"]
+    params = gs.scene_to_device(synth.make_scene(wl))
+    cam = gs.make_camera(synth.make_cameras(wl)[9])
+    pipe = gs.Pipeline(params, wl.width, wl.height, pair_capacity=1 << 10)
+    pipe.project(cam)
+    P = pipe.bin(cam)  # regrows from 1024 pairs
+    keys, ids, ranges = pipe.keys[:P].clone(), pipe.ids[:P].clone(), pipe.ranges.clone()
+    pipe.keys.fill_(-1)
+    pipe.ranges.fill_(-1)
+    pipe.bin_ws.fill_(0x5A)
+    pipe.bin(cam, wait=False)
     torch.cuda.synchronize()
-    assert st == gs.GS_ERR_CAPACITY and P == need
-    assert torch.all(keys == -7) and torch.all(ids == -7) and torch.all(ranges == -7)
+    assert int(pipe.num_pairs_dev.item()) == P
+    assert torch.equal(pipe.keys[:P], keys) and torch.equal(pipe.ids[:P], ids) and torch.equal(pipe.ranges, ranges)
 
 
 def test_invalid_arguments(env):
