@@ -3,6 +3,8 @@
 Every translation unit is compiled with:
   -ffp-contract=off              expressions round exactly as written (explicit fmaf only)
   -target-feature -packed-fp32-ops  no packed-FP32 VALU instructions
+  -amdgpu-atomic-optimizer-strategy=None  atomics stay as written (the kernels reduce over the
+                                 wave themselves before the one lane that adds)
 and the objects are linked into one shared library next to this file.
 """
 from __future__ import annotations
@@ -25,6 +27,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

@@ -19,9 +19,10 @@
 //  - workgroup b is tile b: consecutive tiles go round-robin to the 8 XCDs, which spreads the
 //    dense regions of a frame over all of them (the splat records of a frame are a few MB and
 //    stay cache-resident);
-//  - backward: the 9 per-splat gradient terms of a wave are summed with DPP row shifts and row
-//    broadcasts (7 VALU ops per value, lane 63 holds the sum), accumulated per workgroup in LDS
-//    (ds_add_f32), and flushed once per (tile, splat) with global fp32 atomics.
+//  - backward: nine per-lane terms per splat (linear pieces of its 2D gradient) are summed over
+//    the wave by a reduce-scatter of permlane swaps and DPP exchanges (25 VALU ops in all),
+//    accumulated per workgroup in LDS (ds_add_f32), turned into the 2D gradient and flushed once
+//    per (tile, splat) with global fp32 atomics.
 // Both raster kernels evaluate a splat with the same inline eval_splat, so the backward takes
 // exactly the forward's skip decisions.
 #include "project_core.h"
@@ -80,6 +81,22 @@ __device__ __forceinline__ float wave_sum_lane63(float v) {
   r = r + dpp_f<0x118>(r);        // row_shr:8 -> lane 15 of each row holds the row's sum
   r = r + dpp_f<0x142>(r);        // row_bcast:15 -> lane 63 holds rows 2 + 3, lane 31 rows 0 + 1
   r = r + dpp_f<0x143>(r);        // row_bcast:31 -> lane 63 holds the wave
+  return r;
+}
+
+// Maximum over the 64 lanes of a wave, into lane 63 (same DPP pattern; 0 is the identity).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, true);
+}
+__device__ __forceinline__ uint32_t wave_max_lane63(uint32_t v) {
+  uint32_t r = max(v, dpp_u<0x111>(v));
+  r = max(r, dpp_u<0x112>(v));
+  r = max(r, dpp_u<0x113>(v));
+  r = max(r, dpp_u<0x114>(r));
+  r = max(r, dpp_u<0x118>(r));
+  r = max(r, dpp_u<0x142>(r));
+  r = max(r, dpp_u<0x143>(r));
   return r;
 }
 
@@ -172,7 +189,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
         m &= m - 1;
         const bool has1 = m != 0;
         const int bit1 = has1 ? __builtin_ctzll(m) : bit0;
-        m &= has1 ? m - 1 : m;
+        m &= m - 1;  // no-op when !has1 (m is already 0)
         const int k0 = w * 64 + bit0, k1 = w * 64 + bit1;
         const float4 a0 = s_a[k0], b0 = s_b[k0];
         const float4 a1 = s_a[k1], b1 = s_b[k1];
@@ -196,63 +213,72 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
   if (COUNT) count_evals(n_eval, eval_count);
 }
 
-// Adds the nine per-lane gradient terms v[0..8] of one splat, summed over the wave, into
-// acc[0..8] (LDS). Reduce-scatter within each 8-lane group: three DPP exchanges (pairs l^7, l^3,
-// l^1) halve the values a lane holds each time, leaving lane l with term (l & 7) summed over its
-// group; a row rotation by 8 adds the other half of the 16-lane row. One LDS atomic from lanes
-// 0-7 of each row then adds eight terms at once (four rows per address). Term 8 is summed along
-// each row separately. 27 VALU per splat instead of 63 for nine full wave reductions.
+// gfx950 lane exchanges: v_permlane32_swap trades lanes 32-63 of its first operand for lanes 0-31
+// of its second (a' = [a.lo, b.lo], b' = [a.hi, b.hi]); v_permlane16_swap trades the odd 16-lane
+// rows of the first for the even rows of the second (a' = [a.r0, b.r0, a.r2, b.r2],
+// b' = [a.r1, b.r1, a.r3, b.r3]).
+__device__ __forceinline__ float swap32_sum(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const uint32_t x = r[0], y = r[1];
+  return __uint_as_float(x) + __uint_as_float(y);
+}
+__device__ __forceinline__ float swap16_sum(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const uint32_t x = r[0], y = r[1];
+  return __uint_as_float(x) + __uint_as_float(y);
+}
 template <int CTRL>
 __device__ __forceinline__ float dppx(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
 }
+
+// Adds the nine per-lane terms v[0..8] of one splat, summed over the wave, into acc[0..8] (LDS).
+// Terms 0-7 go through a reduce-scatter: a permlane32 swap + add leaves term j in the low half
+// and term j + 4 in the high half of one register (summed over lanes l, l ^ 32); a permlane16
+// swap + add leaves terms j, j + 2, j + 4, j + 6 in rows 0-3 (summed over the four rows); a
+// row_ror:8 exchange splits each row between two terms; three DPP adds finish each 8-lane group,
+// so lane 8t holds term t: 18 VALU ops for eight terms, and the eight LDS atomics hit distinct
+// addresses. Term 8 is summed with row shifts and row broadcasts into lane 63.
 __device__ __forceinline__ void reduce9_to_lds(const float* v, float* acc, int lane) {
-  const bool b2 = (lane & 4) != 0, b1 = (lane & 2) != 0, b0 = (lane & 1) != 0;
   float u[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float send = b2 ? v[j] : v[j + 4];
-    const float keep = b2 ? v[j + 4] : v[j];
-    u[j] = keep + dppx<0x141>(send);  // row_half_mirror: lane l <-> l ^ 7
-  }
-  float w[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float send = b1 ? u[j] : u[j + 2];
-    const float keep = b1 ? u[j + 2] : u[j];
-    w[j] = keep + dppx<0x1B>(send);  // quad_perm [3,2,1,0]: l <-> l ^ 3
-  }
-  float x = (b0 ? w[1] : w[0]) + dppx<0xB1>(b0 ? w[0] : w[1]);  // quad_perm [1,0,3,2]: l <-> l ^ 1
-  x = x + dppx<0x128>(x);                                          // row_ror:8
-  float y = v[8] + dppx<0x111>(v[8]);
-  y = y + dppx<0x112>(v[8]);
-  y = y + dppx<0x113>(v[8]);
-  y = y + dppx<0x114>(y);
-  y = y + dppx<0x118>(y);  // lane 15 of each row holds the row's sum of term 8
-  if ((lane & 15) < 8) unsafeAtomicAdd(acc + (lane & 7), x);
-  if ((lane & 15) == 15) unsafeAtomicAdd(acc + 8, y);
+  for (int j = 0; j < 4; ++j) u[j] = swap32_sum(v[j], v[j + 4]);
+  const float w0 = swap16_sum(u[0], u[2]);  // rows: terms 0, 2, 4, 6
+  const float w1 = swap16_sum(u[1], u[3]);  // rows: terms 1, 3, 5, 7
+  const bool hi = (lane & 8) != 0;
+  float x = (hi ? w1 : w0) + dppx<0x128>(hi ? w0 : w1);  // row_ror:8: lanes l <-> l ^ 8
+  x = x + dppx<0x141>(x);                                // row_half_mirror: l <-> 7 - l
+  x = x + dppx<0x4E>(x);                                 // quad_perm [2,3,0,1]: l <-> l ^ 2
+  x = x + dppx<0xB1>(x);                                 // quad_perm [1,0,3,2]: l <-> l ^ 1
+  const float y = wave_sum_lane63(v[8]);
+  if ((lane & 7) == 0) unsafeAtomicAdd(acc + (lane >> 3), x);
+  if (lane == 63) unsafeAtomicAdd(acc + 8, y);
 }
 
 // Per-lane gradient terms of one splat for one pixel, back to front: consumes T (the
 // transmittance behind the splat) and gS = g . S, returns them updated to the front of it.
-__device__ __forceinline__ void splat_grad(bool contrib, const SplatEval& ev, float dx, float dy, const float4& a,
-                                           const float4& b, float cb, float gr, float gg, float gb, float& T,
-                                           float& gS, float* v) {
-  const float inv = 1.0f / (1.0f - ev.alpha);
+// The nine terms are linear pieces of the splat's 2D gradient, finished once per workgroup:
+//   v0 = s dx, v1 = s dy, v2 = s dx^2, v3 = s dx dy, v4 = s dy^2 (s = dL/dsigma), v5 = s,
+//   v6..8 = alpha T_i g_rgb; then dL/dmean = (A P0 + B P1, B P0 + C P1), dL/dA = P2 / 2,
+//   dL/dB = P3, dL/dC = P4 / 2, dL/do = -P5 / o (d alpha/do = G = alpha / o, d alpha/dsigma =
+//   -alpha below the cap), dL/drgb = P6..8 (P = the sums over pixels).
+__device__ __forceinline__ void splat_grad(bool contrib, const SplatEval& ev, float dx, float dy, float cr, float cg,
+                                           float cb, float gr, float gg, float gb, float& T, float& gS, float* v) {
+  const float inv = __builtin_amdgcn_rcpf(1.0f - ev.alpha);
   const float Ti = contrib ? T * inv : T;  // T_i, the transmittance in front of this splat
-  const float gc = fmaf(gr, b.z, fmaf(gg, b.w, gb * cb));
+  const float gc = fmaf(gr, cr, fmaf(gg, cg, gb * cb));
   const float g_alpha = fmaf(Ti, gc, -gS * inv);  // dL/dalpha = g . (c T_i - S / (1 - alpha))
   const float wT = contrib ? ev.alpha * Ti : 0.0f;
   gS = fmaf(gc, wT, gS);
   T = Ti;
-  const float gsig = (contrib && !ev.capped) ? -ev.alpha * g_alpha : 0.0f;  // dL/dsigma
-  constexpr float inv_l2e = 1.0f / kLog2e;
-  v[0] = gsig * (fmaf(2.0f * a.z, dx, b.x * dy) * inv_l2e);  // dsigma/dmx = A dx + B dy
-  v[1] = gsig * (fmaf(2.0f * a.w, dy, b.x * dx) * inv_l2e);  // dsigma/dmy = B dx + C dy
-  v[2] = (0.5f * gsig) * (dx * dx);
-  v[3] = gsig * (dx * dy);
-  v[4] = (0.5f * gsig) * (dy * dy);
-  v[5] = (contrib && !ev.capped) ? ev.G * g_alpha : 0.0f;
+  const float s = (contrib && !ev.capped) ? -ev.alpha * g_alpha : 0.0f;  // dL/dsigma
+  const float p = s * dx, q = s * dy;
+  v[0] = p;
+  v[1] = q;
+  v[2] = p * dx;
+  v[3] = p * dy;
+  v[4] = q * dy;
+  v[5] = s;
   v[6] = wT * gr;
   v[7] = wT * gg;
   v[8] = wT * gb;
@@ -302,7 +328,8 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
   float gS = T * ((gr * cam.bg[0] + gg * cam.bg[1]) + gb * cam.bg[2]);
   if (tid == 0) s_max = 0;
   __syncthreads();
-  if (nc) atomicMax(&s_max, nc);
+  const uint32_t wmax = wave_max_lane63(nc);
+  if (lane == 63 && wmax) atomicMax(&s_max, wmax);
   __syncthreads();
   const uint32_t max_nc = s_max;
   uint32_t n_eval = 0;
@@ -324,11 +351,12 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
       uint64_t m = uniform64(s_qm[wave][w]);  // walked from the highest set bit down
       while (m) {
         const int bit0 = 63 - __builtin_clzll(m);
-        m &= ~(1ull << bit0);
+        m ^= 1ull << bit0;
         const bool has1 = m != 0;
         const int bit1 = has1 ? 63 - __builtin_clzll(m) : bit0;
-        if (has1) m &= ~(1ull << bit1);
-        const int k0 = w * 64 + bit0, k1 = w * 64 + bit1;
+        m &= ~(1ull << bit1);  // no-op when !has1 (m is already 0)
+        const int k0 = __builtin_amdgcn_readfirstlane(w * 64 + bit0);
+        const int k1 = __builtin_amdgcn_readfirstlane(w * 64 + bit1);
         const bool act0 = bstart + (uint32_t)k0 < nc;
         const bool act1 = has1 && (bstart + (uint32_t)k1 < nc);
         if (!__any(act0 || act1)) continue;
@@ -341,20 +369,32 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
         if (COUNT) n_eval += (act0 ? 1u : 0u) + (act1 ? 1u : 0u);
         const bool c0 = act0 && !e0.skip, c1 = act1 && !e1.skip;
         float v0[9], v1[9];
-        splat_grad(c0, e0, dx0, dy0, a0, b0, cb0, gr, gg, gb, T, gS, v0);
-        splat_grad(c1, e1, dx1, dy1, a1, b1, cb1, gr, gg, gb, T, gS, v1);
+        splat_grad(c0, e0, dx0, dy0, b0.z, b0.w, cb0, gr, gg, gb, T, gS, v0);
+        splat_grad(c1, e1, dx1, dy1, b1.z, b1.w, cb1, gr, gg, gb, T, gS, v1);
         if (__any(c0)) reduce9_to_lds(v0, s_acc + k0 * 9, lane);
         if (__any(c1)) reduce9_to_lds(v1, s_acc + k1 * 9, lane);
       }
     }
     __syncthreads();
+    // finish the 2D gradient of each staged splat from its nine sums and add it to g2d
     if (tid < cnt && s_id[tid] < n) {
-      float* dst = g2d + (size_t)s_id[tid] * 9;
+      const uint32_t g = s_id[tid];
+      const float* P = s_acc + tid * 9;
+      const float A = conics[3 * g], B = conics[3 * g + 1], C = conics[3 * g + 2], o = opac[g];
+      float gv[9];
+      gv[0] = fmaf(A, P[0], B * P[1]);
+      gv[1] = fmaf(B, P[0], C * P[1]);
+      gv[2] = 0.5f * P[2];
+      gv[3] = P[3];
+      gv[4] = 0.5f * P[4];
+      gv[5] = -P[5] / o;
+      gv[6] = P[6];
+      gv[7] = P[7];
+      gv[8] = P[8];
+      float* dst = g2d + (size_t)g * 9;
 #pragma unroll
-      for (int c = 0; c < 9; ++c) {
-        const float s9 = s_acc[tid * 9 + c];
-        if (s9 != 0.0f) unsafeAtomicAdd(dst + c, s9);
-      }
+      for (int c = 0; c < 9; ++c)
+        if (gv[c] != 0.0f) unsafeAtomicAdd(dst + c, gv[c]);
     }
     bend = bstart;
   }
