@@ -32,9 +32,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 
-# VALU instructions executed per (pixel, splat) evaluation on the kernels' main path, counted in
-# the gfx950 ISA of the built library ("Rooflines").
-VALU_PER_EVAL = {"blend": 25.0, "rbwd": 48.0}
+# VALU instructions per (pixel, splat) evaluation on the kernels' main path, counted in the
+# gfx950 ISA of the built library: the blend loop body issues 60 VALU ops per two splats, the
+# backward loop body 147 per two splats (evaluation, gradient terms and wave reduction).
+VALU_PER_EVAL = {"blend": 30.0, "rbwd": 73.5}
 
 
 def parse():
@@ -46,6 +47,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before the timed steps, copy a buffer of this many MiB 5 times (a plain copy "
+                         "kernel of known size, to scale HBM byte counters)")
     return ap.parse_args()
 
 
@@ -81,38 +85,57 @@ def traffic_for(kernel):
     return rec["bytes_per_launch"]
 
 
-def cpu_baseline(wl, scene, cam, target_np, seconds):
-    """The oracle on the host cores: projection of all N, dense render + backward of a seeded
-    pixel sample (sparse L1 loss on it), chain rule to raw parameters; scaled to a full frame."""
+def cpu_baseline(wl, scene, cams_d, target_of, seconds):
+    """The oracle on the host cores: projection of all N, dense render + backward (sparse L1 loss on
+    the rendered pixels), chain rule to raw parameters. The pixel sample of camera 0 grows until it
+    takes about half the time budget; once it is the whole frame, further cameras' full frames are
+    added until about 0.7 of the budget is spent. A partial frame is scaled to the full frame."""
     import oracle
     from gaussian_splatting_tile_gs_amd import synth
 
-    W, H = cam["width"], cam["height"]
-    npix = 1024
-    while True:
+    W, H = wl.width, wl.height
+
+    def one(ci, npix):
+        cam = cams_d[ci]
         pix = synth.sample_pixels(W, H, npix, seed=1)
+        tgt = target_of(ci)
         t0 = time.perf_counter()
         proj = oracle.project(scene, cam)
         t1 = time.perf_counter()
         fwd = oracle.render(proj, cam, pixels=pix)
-        diff = fwd["image"] - target_np[pix[:, 0], pix[:, 1]]
-        dimg = np.sign(diff) / (3.0 * W * H)
-        t2 = time.perf_counter()
+        dimg = np.sign(fwd["image"] - tgt[pix[:, 0], pix[:, 1]]) / (3.0 * W * H)
         g2d, _ = oracle.render_backward(proj, cam, dimg, pixels=pix)
         t3 = time.perf_counter()
         oracle.project_backward(scene, cam, g2d)
         t4 = time.perf_counter()
-        total = t4 - t0
+        return t4 - t0, (t1 - t0) + (t4 - t3) + (t3 - t1) / npix * W * H
+
+    npix = 1024
+    while True:
+        total, frame = one(0, npix)
         if total >= 0.5 * seconds or npix >= W * H:
             break
         npix = min(W * H, int(npix * max(2.0, 0.7 * seconds / max(total, 1e-3))))
-    per_pixel = (t3 - t1) / npix
-    frame = (t1 - t0) + (t4 - t3) + per_pixel * W * H
-    return {"value": 1.0 / frame, "unit": "iterations/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"camera 0 of {wl.name}: projection of all {scene['means'].shape[0]} Gaussians, dense "
-                      f"render + backward on {npix} seeded pixels of {W * H} (sparse L1 loss), chain rule; "
-                      f"per-pixel time scaled to the full frame (measured {total:.1f} s)",
-            "measured_seconds": round(total, 3), "frame_seconds_extrapolated": round(frame, 3)}
+    frames, measured = [frame], total
+    if npix >= W * H:
+        while measured < 0.7 * seconds and len(frames) < len(cams_d):
+            total, frame = one(len(frames), W * H)
+            frames.append(frame)
+            measured += total
+        sample = (f"full frames of cameras 0-{len(frames) - 1} of {wl.name}: projection of all "
+                  f"{scene['means'].shape[0]} Gaussians, dense render + backward of all {W * H} pixels "
+                  f"(L1 loss), chain rule (measured {measured:.1f} s)")
+    else:
+        sample = (f"camera 0 of {wl.name}: projection of all {scene['means'].shape[0]} Gaussians, dense "
+                  f"render + backward on {npix} seeded pixels of {W * H} (sparse L1 loss), chain rule; "
+                  f"per-pixel time scaled to the full frame (measured {measured:.1f} s)")
+    frame_s = sum(frames) / len(frames)
+    return {"value": 1.0 / frame_s, "unit": "iterations/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": sample, "measured_seconds": round(measured, 3), "frame_seconds": round(frame_s, 3)}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def main():
@@ -144,6 +167,7 @@ def main():
         targets[i].copy_(tpipe.image)
     del tpipe, tparams
     torch.cuda.synchronize()
+    log(f"{wl.name}: {len(cams)} target images rendered from the {teacher['means'].shape[0]}-Gaussian teacher")
 
     pipe = gs.Pipeline(params, W, H, pair_capacity=1 << 16)
     pairs = []
@@ -164,6 +188,14 @@ def main():
             pipe.bin(cams[c], wait=False)
             pipe.forward(cams[c])
 
+    if args.copy_calibration_mib:
+        src = torch.ones(args.copy_calibration_mib << 18, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -174,6 +206,7 @@ def main():
     t1 = time.perf_counter()
     elapsed = t1 - t0
     its = args.steps / elapsed
+    log(f"timed {args.steps} steps: {1e3 * elapsed / args.steps:.4f} ms/step")
     last = (args.warmup + args.steps - 1) % ncam
     assert int(pipe.num_pairs_dev.item()) == pairs[last] <= pipe.capacity, "pair count changed between runs"
     steps_pairs = sum(pairs[(args.warmup + i) % ncam] for i in range(args.steps))
@@ -250,7 +283,9 @@ def main():
         result["evals_per_step"] = {"fwd": evals_f.item() / nprof, "bwd": evals_b.item() / nprof}
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, scene, cams_d[0], targets[0].cpu().numpy().astype(np.float64),
+        log("timing the CPU oracle on a pixel sample")
+        result["cpu_baseline"] = cpu_baseline(wl, scene, cams_d,
+                                              lambda i: targets[i].cpu().numpy().astype(np.float64),
                                               args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
