@@ -10,7 +10,8 @@
 //   1. k_bin_prep     depth keys (culled -> 0xFFFFFFFF), per-workgroup digit histograms of the
 //                     four depth passes, and the zeroing of every counter, look-back word and
 //                     tile range the later kernels rely on (no memset nodes, no host wait)
-//   2. k_hist_reduce  the per-workgroup depth histograms summed
+//   2. k_hist_reduce  the per-workgroup depth histograms summed (beyond 32 workgroups; below
+//                     that each depth pass sums them itself)
 //   3. 4 x k_onesweep stable LSD radix sort of the N Gaussians by depth bits
 //   4. k_scan_emit    single-pass prefix scan of the tile counts in depth order; each workgroup
 //                     then writes its Gaussians' (tile id, i) pairs with all 256 lanes sharing
@@ -30,7 +31,8 @@
 // offsets by decoupled look-back over earlier tiles. Tiles take their index from an atomic
 // ticket, so a tile only ever waits on tiles that have already started (no forward-progress
 // assumption between workgroups). Ranking is stable: within a wave, equal digits are matched
-// with eight 64-lane ballots; waves own contiguous 1024-key segments in index order.
+// with eight 64-lane ballots; the 16 waves of a workgroup own contiguous 256-key segments in
+// index order (four keys per lane keep each wave's ranking chain short).
 //
 // Bytes per pair (algorithmic): emit writes 8; each pair pass reads 8 and writes 8 (the last
 // writes 12 and gathers 4); ranges read 8. With 2 pair passes that is 8 + 16 + 24 + 8 = 56 B/pair,
@@ -42,9 +44,9 @@
 namespace gs {
 namespace {
 
-constexpr int kSortThreads = 256;
+constexpr int kSortThreads = 1024;  // 16 waves: short per-wave ranking chains
 constexpr int kSortWaves = kSortThreads / 64;
-constexpr int kSortItems = 16;
+constexpr int kSortItems = 4;
 constexpr int kSortTile = kSortThreads * kSortItems;  // 4096 keys per workgroup
 constexpr int kScanTile = 256;                        // Gaussians per scan/emit workgroup
 constexpr int kRadix = 256;
@@ -86,16 +88,17 @@ __device__ __forceinline__ T wave_incl_scan(T v, int lane) {
   return v;
 }
 
-// Exclusive scan of one value per thread over a 256-thread workgroup; *total gets the sum.
+// Exclusive scan over the values of the first 256 threads of the workgroup (the others pass 0);
+// *total gets the sum. Every thread of the workgroup calls it (it holds two barriers).
 template <typename T>
 __device__ __forceinline__ T block_excl_scan256(T v, T* s_wsum, T* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const T inc = wave_incl_scan<T>(v, lane);
-  if (lane == 63) s_wsum[wave] = inc;
+  if (wave < 4 && lane == 63) s_wsum[wave] = inc;
   __syncthreads();
   T before = 0, sum = 0;
 #pragma unroll
-  for (int w = 0; w < kSortWaves; ++w) {
+  for (int w = 0; w < 4; ++w) {
     const T x = s_wsum[w];
     before += (w < wave) ? x : T(0);
     sum += x;
@@ -106,22 +109,31 @@ __device__ __forceinline__ T block_excl_scan256(T v, T* s_wsum, T* total) {
 }
 
 // Decoupled look-back: the inclusive prefix of the tiles before `vb` in one column of look-back
-// words. Every earlier tile has taken its ticket before this one, so each wait ends.
-template <typename T, T kFlagMask, T kPre, T kVal>
+// words. W predecessor words are read at once (independent loads, one round trip) and consumed
+// nearest first until an inclusive prefix is found; a word not yet published stops the
+// consumption and the window is read again from there. Every earlier tile has taken its ticket
+// before this one, so every wait ends; tile 0 always publishes an inclusive prefix.
+template <int W, typename T, T kFlagMask, T kPre, T kVal>
 __device__ __forceinline__ T look_back(const T* status, uint32_t vb, int stride) {
   T excl = 0;
   int64_t j = (int64_t)vb - 1;
-  while (j >= 0) {
-    const T st = ld_dev(status + (size_t)j * stride);
-    if ((st & kFlagMask) == 0) {
-      __builtin_amdgcn_s_sleep(1);
-      continue;
+  while (true) {
+    T st[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      const int64_t p = j - i;
+      st[i] = p >= 0 ? ld_dev(status + (size_t)p * stride) : kPre;  // below tile 0: never consumed
     }
-    excl += st & kVal;
-    if ((st & kFlagMask) == kPre) break;
-    --j;
+    int i = 0;
+    for (; i < W; ++i) {
+      const T f = st[i] & kFlagMask;
+      if (f == 0) break;
+      excl += st[i] & kVal;
+      if (f == kPre) return excl;
+    }
+    j -= i;
+    if (i < W) __builtin_amdgcn_s_sleep(1);
   }
-  return excl;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -139,24 +151,35 @@ __global__ __launch_bounds__(kSortThreads) void k_bin_prep(int32_t n, const floa
   for (size_t i = blockIdx.x * (size_t)kSortThreads + tid; i < zero_a_words; i += gsz) zero_a[i] = 0u;
   for (size_t i = blockIdx.x * (size_t)kSortThreads + tid; i < zero_b_words; i += gsz) zero_b[i] = 0u;
   if (blockIdx.x >= nbN) return;  // workgroup-uniform
+  if (tid < kRadix) {
 #pragma unroll
-  for (int p = 0; p < 4; ++p) s_hist[p][tid] = 0;
+    for (int p = 0; p < 4; ++p) s_hist[p][tid] = 0;
+  }
   __syncthreads();
   const int base = blockIdx.x * kSortTile;
-#pragma unroll 4
+  uint32_t k[kSortItems];
+#pragma unroll
+  for (int i = 0; i < kSortItems; ++i) {  // all loads in flight before any is used
+    const int idx = base + i * kSortThreads + tid;
+    const uint32_t t = idx < n ? tiles[idx] : 0u;
+    const float z = idx < n ? depths[idx] : 0.0f;
+    k[i] = t > 0 ? __float_as_uint(z) : 0xFFFFFFFFu;
+  }
+#pragma unroll
   for (int i = 0; i < kSortItems; ++i) {
     const int idx = base + i * kSortThreads + tid;
     if (idx < n) {
-      const uint32_t k = tiles[idx] > 0 ? __float_as_uint(depths[idx]) : 0xFFFFFFFFu;
-      keys[idx] = k;
+      keys[idx] = k[i];
       vals[idx] = (uint32_t)idx;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) atomicAdd(&s_hist[p][(k >> (8 * p)) & 0xFF], 1u);
+      for (int p = 0; p < 4; ++p) atomicAdd(&s_hist[p][(k[i] >> (8 * p)) & 0xFF], 1u);
     }
   }
   __syncthreads();
+  if (tid < kRadix) {
 #pragma unroll
-  for (int p = 0; p < 4; ++p) dhist[((size_t)blockIdx.x * 4 + p) * kRadix + tid] = s_hist[p][tid];
+    for (int p = 0; p < 4; ++p) dhist[((size_t)blockIdx.x * 4 + p) * kRadix + tid] = s_hist[p][tid];
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -164,6 +187,7 @@ __global__ __launch_bounds__(kSortThreads) void k_bin_prep(int32_t n, const floa
 // (ctrl->hist_depth was zeroed by k_bin_prep)
 // ---------------------------------------------------------------------------------------------
 constexpr int kReduceRows = 64;
+constexpr int kDirectHistRows = 32;
 __global__ __launch_bounds__(kRadix) void k_hist_reduce(const uint32_t* __restrict__ dhist, uint32_t nbN, Ctrl* ctrl) {
   const int p = blockIdx.x, d = threadIdx.x;
   const uint32_t r0 = blockIdx.y * kReduceRows;
@@ -175,28 +199,28 @@ __global__ __launch_bounds__(kRadix) void k_hist_reduce(const uint32_t* __restri
 
 // ---------------------------------------------------------------------------------------------
 // 3/5. one stable LSD radix pass over `bits` (<= 8) bits at `shift` (Onesweep-style)
-// The element count is *n_dev when given (pairs: grid sized by the capacity), else n_host.
+// The element count is *n_dev when given (pairs: grid sized by the capacity), else n_host. The
+// pass's digit histogram is the sum of `hist_parts` rows of 256 counts, `hist_stride` apart.
 // ---------------------------------------------------------------------------------------------
 template <bool FINAL>
 __global__ __launch_bounds__(kSortThreads) void k_onesweep(
     const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, uint32_t* __restrict__ keys_out,
     uint32_t* __restrict__ vals_out, uint64_t* __restrict__ out_keys64, const uint32_t* __restrict__ depth_bits,
     uint32_t n_host, const uint64_t* __restrict__ n_dev, int shift, int bits, const uint32_t* __restrict__ hist,
-    uint32_t* __restrict__ status, uint32_t* __restrict__ ticket) {
+    int hist_parts, int hist_stride, uint32_t* __restrict__ status, uint32_t* __restrict__ ticket) {
   __shared__ uint32_t s_keys[kSortTile];
   __shared__ uint32_t s_vals[kSortTile];
-  __shared__ uint32_t s_wcnt[kSortWaves][kRadix];
+  __shared__ uint32_t s_wcnt[kSortWaves][kRadix];  // per wave and digit: count, then wave offset
   __shared__ uint32_t s_dpre[kRadix];
   __shared__ uint32_t s_goff[kRadix];
-  __shared__ uint32_t s_wsum[kSortWaves];
+  __shared__ uint32_t s_wsum[4];
   __shared__ uint32_t s_vb;
 
   const uint32_t n = n_dev ? (uint32_t)*n_dev : n_host;
   if ((uint64_t)blockIdx.x * kSortTile >= n) return;  // workgroup-uniform: idle workgroups take no ticket
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) s_vb = atomicAdd(ticket, 1u);
-#pragma unroll
-  for (int w = 0; w < kSortWaves; ++w) s_wcnt[w][tid] = 0;
+  for (int i = tid; i < kSortWaves * kRadix; i += kSortThreads) (&s_wcnt[0][0])[i] = 0;
   __syncthreads();
   // exactly ceil(n / 4096) workgroups take tickets, so every ticket has base < n
   const uint32_t vb = s_vb;
@@ -205,7 +229,7 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
   const uint32_t mask = (1u << bits) - 1u;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-  // ---- load (wave-striped: wave w owns [base + 1024 w, base + 1024 (w + 1))) and rank ----
+  // ---- load (wave-striped: wave w owns [base + 256 w, base + 256 (w + 1))) and rank ----
   uint32_t k[kSortItems], v[kSortItems], rank[kSortItems];
 #pragma unroll
   for (int i = 0; i < kSortItems; ++i) {
@@ -214,6 +238,9 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
     k[i] = valid ? keys_in[idx] : 0u;
     v[i] = valid ? vals_in[idx] : 0u;
   }
+  uint32_t h = 0;  // the pass's histogram, read while the keys arrive
+  if (tid < kRadix)
+    for (int r = 0; r < hist_parts; ++r) h += hist[(size_t)r * hist_stride + tid];
 #pragma unroll
   for (int i = 0; i < kSortItems; ++i) {
     const uint32_t idx = base + (uint32_t)(wave * 64 * kSortItems + i * 64 + lane);
@@ -234,25 +261,31 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
   }
   __syncthreads();
 
-  // ---- per digit: wave offsets, tile total, publish, look back ----
-  const uint32_t c0 = s_wcnt[0][tid], c1 = s_wcnt[1][tid], c2 = s_wcnt[2][tid], c3 = s_wcnt[3][tid];
-  const uint32_t tot = c0 + c1 + c2 + c3;
-  uint32_t* my_status = status + (size_t)vb * kRadix + tid;
-  st_dev(my_status, (vb == 0 ? kFlagPre : kFlagAgg) | tot);
-  uint32_t dummy;
-  const uint32_t bucket_excl = block_excl_scan256<uint32_t>(hist[tid], s_wsum, &dummy);
-  const uint32_t dpre = block_excl_scan256<uint32_t>(tot, s_wsum, &dummy);
-  s_wcnt[0][tid] = 0;
-  s_wcnt[1][tid] = c0;
-  s_wcnt[2][tid] = c0 + c1;
-  s_wcnt[3][tid] = c0 + c1 + c2;
-  s_dpre[tid] = dpre;
-  uint32_t excl = 0;
-  if (vb > 0) {
-    excl = look_back<uint32_t, ~kValMask, kFlagPre, kValMask>(status + tid, vb, kRadix);
-    st_dev(my_status, kFlagPre | (excl + tot));
+  // ---- per digit (threads 0-255): wave offsets, tile total, publish, look back ----
+  uint32_t tot = 0;
+  if (tid < kRadix) {
+    uint32_t c[kSortWaves];
+#pragma unroll
+    for (int w = 0; w < kSortWaves; ++w) c[w] = s_wcnt[w][tid];
+#pragma unroll
+    for (int w = 0; w < kSortWaves; ++w) {
+      s_wcnt[w][tid] = tot;
+      tot += c[w];
+    }
+    st_dev(status + (size_t)vb * kRadix + tid, (vb == 0 ? kFlagPre : kFlagAgg) | tot);
   }
-  s_goff[tid] = bucket_excl + excl - dpre;
+  uint32_t dummy;
+  const uint32_t bucket_excl = block_excl_scan256<uint32_t>(h, s_wsum, &dummy);
+  const uint32_t dpre = block_excl_scan256<uint32_t>(tot, s_wsum, &dummy);
+  if (tid < kRadix) {
+    s_dpre[tid] = dpre;
+    uint32_t excl = 0;
+    if (vb > 0) {
+      excl = look_back<8, uint32_t, ~kValMask, kFlagPre, kValMask>(status + tid, vb, kRadix);
+      st_dev(status + (size_t)vb * kRadix + tid, kFlagPre | (excl + tot));
+    }
+    s_goff[tid] = bucket_excl + excl - dpre;
+  }
   __syncthreads();
 
   // ---- scatter to LDS in local sorted order, then out with consecutive threads ----
@@ -268,7 +301,10 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
   }
   __syncthreads();
   const uint32_t count = (n - base < (uint32_t)kSortTile) ? (n - base) : (uint32_t)kSortTile;
-  for (uint32_t j = tid; j < count; j += kSortThreads) {
+#pragma unroll
+  for (int i = 0; i < kSortItems; ++i) {
+    const uint32_t j = (uint32_t)(i * kSortThreads + tid);
+    if (j >= count) break;
     const uint32_t key = s_keys[j], val = s_vals[j];
     const uint32_t gp = s_goff[(key >> shift) & mask] + j;
     if (gp >= n) continue;  // cannot happen when the histogram matches the keys; never write past n
@@ -291,7 +327,7 @@ __global__ __launch_bounds__(kScanTile) void k_scan_emit(
     const float* __restrict__ means2d, const int32_t* __restrict__ radii, int32_t tiles_x, int32_t tiles_y,
     uint32_t* __restrict__ pkeys, uint32_t* __restrict__ pvals, uint64_t capacity, int npass,
     uint64_t* __restrict__ status, Ctrl* ctrl, int64_t* __restrict__ user_num_pairs) {
-  __shared__ uint64_t s_wsum[kSortWaves];
+  __shared__ uint64_t s_wsum[4];
   __shared__ uint32_t s_incl[kScanTile];  // workgroup-inclusive pair counts, saturated at 2^31
   __shared__ uint32_t s_g[kScanTile];
   __shared__ int32_t s_x0[kScanTile], s_y0[kScanTile], s_w[kScanTile];
@@ -330,7 +366,7 @@ __global__ __launch_bounds__(kScanTile) void k_scan_emit(
     st_dev(status + vb, (vb == 0 ? kFlagPre64 : kFlagAgg64) | tot);
     uint64_t excl = 0;
     if (vb > 0) {
-      excl = look_back<uint64_t, ~kValMask64, kFlagPre64, kValMask64>(status, vb, 1);
+      excl = look_back<16, uint64_t, ~kValMask64, kFlagPre64, kValMask64>(status, vb, 1);
       st_dev(status + vb, kFlagPre64 | (excl + tot));
     }
     s_excl = excl;
@@ -490,18 +526,21 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
                        dkA, dvA, dhist, L.nbN, (uint32_t*)(ws + L.ctrl), zero_words, d_tile_ranges,
                        (size_t)(2 * ntiles));
   }
-  {
+  // up to kDirectHistRows workgroups, each depth pass sums the per-workgroup histograms itself
+  const bool direct_hist = L.nbN <= (uint32_t)kDirectHistRows;
+  if (!direct_hist) {
     TimedScope ts("hist_reduce", s);
     hipLaunchKernelGGL(k_hist_reduce, dim3(4, (L.nbN + kReduceRows - 1) / kReduceRows), dim3(kRadix), 0, s, dhist,
                        L.nbN, ctrl);
   }
   for (int p = 0; p < 4; ++p) {
     const bool even = (p % 2) == 0;
+    const uint32_t* hist = direct_hist ? dhist + p * kRadix : ctrl->hist_depth[p];
     TimedScope ts("depth_sort_pass", s);
     hipLaunchKernelGGL(k_onesweep<false>, dim3(L.nbN), dim3(kSortThreads), 0, s, even ? dkA : dkB, even ? dvA : dvB,
                        even ? dkB : dkA, even ? dvB : dvA, (uint64_t*)nullptr, (const uint32_t*)nullptr,
-                       (uint32_t)n, (const uint64_t*)nullptr, 8 * p, 8, ctrl->hist_depth[p],
-                       dstatus + (size_t)p * L.nbN * kRadix, &ctrl->tickets[p]);
+                       (uint32_t)n, (const uint64_t*)nullptr, 8 * p, 8, hist, direct_hist ? (int)L.nbN : 1,
+                       4 * kRadix, dstatus + (size_t)p * L.nbN * kRadix, &ctrl->tickets[p]);
   }
   // ping-pong of the pair sort: A = d_keys viewed as two u32 arrays of pair_capacity, B = workspace
   uint32_t* kA = (uint32_t*)d_keys;
@@ -527,11 +566,11 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
       if (last) {
         hipLaunchKernelGGL(k_onesweep<true>, dim3(L.nbCap), dim3(kSortThreads), 0, s, ki, vi, (uint32_t*)nullptr,
                            d_ids, d_keys, (const uint32_t*)proj->d_depths, 0u, &ctrl->eff_pairs, shift, bits,
-                           ctrl->hist_pair[p], pstatus + (size_t)p * L.nbCap * kRadix, &ctrl->tickets[4 + p]);
+                           ctrl->hist_pair[p], 1, 0, pstatus + (size_t)p * L.nbCap * kRadix, &ctrl->tickets[4 + p]);
       } else {
         hipLaunchKernelGGL(k_onesweep<false>, dim3(L.nbCap), dim3(kSortThreads), 0, s, ki, vi, ko, vo,
                            (uint64_t*)nullptr, (const uint32_t*)nullptr, 0u, &ctrl->eff_pairs, shift, bits,
-                           ctrl->hist_pair[p], pstatus + (size_t)p * L.nbCap * kRadix, &ctrl->tickets[4 + p]);
+                           ctrl->hist_pair[p], 1, 0, pstatus + (size_t)p * L.nbCap * kRadix, &ctrl->tickets[4 + p]);
       }
       in_A = !in_A;
     }
