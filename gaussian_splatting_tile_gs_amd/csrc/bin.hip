@@ -7,19 +7,27 @@
 //
 // How (MI355X design, not the pages'): a full 64-bit key sort would take 6 radix passes over the
 // pairs. Here the depth part is settled once per Gaussian instead of once per pair:
-//   1. k_bin_prep     depth keys (culled -> 0xFFFFFFFF), per-workgroup digit histograms of the
-//                     four depth passes, and the zeroing of every counter, look-back word and
+//   1. k_bin_prep     depth keys (culled -> 0xFFFFFFFF), packed (count, first tile, width)
+//                     rectangles, per-workgroup digit histograms of the four depth passes, and
+//                     the zeroing of every counter, look-back word and
 //                     tile range the later kernels rely on (no memset nodes, no host wait)
 //   2. k_hist_reduce  the per-workgroup depth histograms summed (beyond 32 workgroups; below
 //                     that each depth pass sums them itself)
-//   3. 4 x k_onesweep stable LSD radix sort of the N Gaussians by depth bits
-//   4. k_scan_emit    single-pass prefix scan of the tile counts in depth order; each workgroup
-//                     then writes its Gaussians' (tile id, i) pairs with all 256 lanes sharing
-//                     the work (coalesced, balanced however uneven the counts), accumulates the
-//                     tile-digit histograms, and the last workgroup publishes P
-//   5. ceil(bits/8) x k_onesweep  stable LSD radix sort of the pairs by tile id only; the last
+//   3. 4 x k_onesweep stable LSD radix sort of the N Gaussians by depth bits; extra workgroups of
+//                     the first two passes count the pairs of every tile (they do not depend on
+//                     the depth order) and turn the counts into the tile ranges and the
+//                     tile-digit histograms of the pair sort
+//   4. k_scan         single-pass prefix scan of the tile counts in depth order (4096 Gaussians
+//                     per workgroup, wave-wide look-back): per Gaussian in depth order its first
+//                     pair position, rectangle and id; per chunk of 4096 pair positions the
+//                     Gaussian it starts in; the last workgroup publishes P
+//   5. k_emit         one workgroup per chunk of 4096 pair positions writes those (tile id, i)
+//                     pairs, however the pairs spread over Gaussians (the nearest splats, first
+//                     in depth order, cover thousands of tiles): the owner of each position is a
+//                     max-scan of the markers that staged Gaussians leave at their first
+//                     position
+//   6. ceil(bits/8) x k_onesweep  stable LSD radix sort of the pairs by tile id only; the last
 //                     pass writes the 64-bit key (tile << 32 | depth bits of i) and the id
-//   6. k_ranges       per-tile [start, end)
 // Emitting in (depth, id) order and sorting stably by tile gives exactly the (tile, depth, id)
 // order of the stable 64-bit key sort, with 1-2 passes over the pairs instead of 6. P never has
 // to reach the host: the pair kernels are sized by the capacity and their workgroups stop at the
@@ -35,8 +43,8 @@
 // index order (four keys per lane keep each wave's ranking chain short).
 //
 // Bytes per pair (algorithmic): emit writes 8; each pair pass reads 8 and writes 8 (the last
-// writes 12 and gathers 4); ranges read 8. With 2 pair passes that is 8 + 16 + 24 + 8 = 56 B/pair,
-// plus ~40 B per Gaussian for the depth sort and scan.
+// writes 12 and gathers 4). With 2 pair passes that is 8 + 16 + 24 = 48 B/pair, plus about
+// 150 B per Gaussian for the depth sort, the rectangles and the scan.
 #include <algorithm>
 
 #include "gs_internal.h"
@@ -48,7 +56,13 @@ constexpr int kSortThreads = 1024;  // 16 waves: short per-wave ranking chains
 constexpr int kSortWaves = kSortThreads / 64;
 constexpr int kSortItems = 4;
 constexpr int kSortTile = kSortThreads * kSortItems;  // 4096 keys per workgroup
-constexpr int kScanTile = 256;                        // Gaussians per scan/emit workgroup
+constexpr int kEmitThreads = 1024;
+constexpr int kEmitWaves = kEmitThreads / 64;
+constexpr int kScanItems = 4;
+constexpr int kScanTile = kEmitThreads * kScanItems;  // 4096 Gaussians per scan workgroup
+constexpr int kEmitPer = 4;
+constexpr int kEmitChunk = kEmitThreads * kEmitPer;   // pair positions per emit workgroup
+constexpr int kEmitWindow = 2048;                     // Gaussians staged per emission round
 constexpr int kRadix = 256;
 // Radix-pass look-back words are 32 bits: [31:30] flag (0 not ready, 1 tile aggregate,
 // 2 inclusive prefix), [29:0] count, so sorted sequences are limited to below 2^30 elements.
@@ -63,7 +77,7 @@ constexpr uint64_t kValMask64 = (1ull << 62) - 1;
 struct Ctrl {
   uint64_t num_pairs;    // P
   uint64_t eff_pairs;    // P if it fits the capacity, else 0: what the pair kernels process
-  uint32_t tickets[16];  // [0..3] depth passes, [4..6] pair passes, [7] scan
+  uint32_t tickets[16];  // [0..3] depth passes, [4..6] pair passes, [7] scan, [8] scan workgroups done
   uint32_t hist_depth[4][kRadix];
   uint32_t hist_pair[3][kRadix];
 };
@@ -108,6 +122,26 @@ __device__ __forceinline__ T block_excl_scan256(T v, T* s_wsum, T* total) {
   return before + inc - v;
 }
 
+// Exclusive sum over one value per thread of a 1024-thread workgroup; *total gets the sum. Two
+// barriers; every thread calls it.
+template <typename T>
+__device__ __forceinline__ T block_excl_scan1024(T v, T* s_wsum, T* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const T inc = wave_incl_scan<T>(v, lane);
+  if (lane == 63) s_wsum[wave] = inc;
+  __syncthreads();
+  T before = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < kSortWaves; ++w) {
+    const T x = s_wsum[w];
+    before += (w < wave) ? x : T(0);
+    sum += x;
+  }
+  __syncthreads();
+  *total = sum;
+  return before + inc - v;
+}
+
 // Decoupled look-back: the inclusive prefix of the tiles before `vb` in one column of look-back
 // words. W predecessor words are read at once (independent loads, one round trip) and consumed
 // nearest first until an inclusive prefix is found; a word not yet published stops the
@@ -141,6 +175,9 @@ __device__ __forceinline__ T look_back(const T* status, uint32_t vb, int stride)
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kSortThreads) void k_bin_prep(int32_t n, const float* __restrict__ depths,
                                                            const uint32_t* __restrict__ tiles,
+                                                           const float* __restrict__ means2d,
+                                                           const int32_t* __restrict__ radii, int32_t tiles_x,
+                                                           int32_t tiles_y, uint4* __restrict__ rec,
                                                            uint32_t* __restrict__ keys, uint32_t* __restrict__ vals,
                                                            uint32_t* __restrict__ dhist, uint32_t nbN,
                                                            uint32_t* __restrict__ zero_a, size_t zero_a_words,
@@ -157,13 +194,17 @@ __global__ __launch_bounds__(kSortThreads) void k_bin_prep(int32_t n, const floa
   }
   __syncthreads();
   const int base = blockIdx.x * kSortTile;
-  uint32_t k[kSortItems];
+  uint32_t k[kSortItems], t[kSortItems];
+  float2 m[kSortItems];
+  int2 r[kSortItems];
 #pragma unroll
   for (int i = 0; i < kSortItems; ++i) {  // all loads in flight before any is used
     const int idx = base + i * kSortThreads + tid;
-    const uint32_t t = idx < n ? tiles[idx] : 0u;
+    t[i] = idx < n ? tiles[idx] : 0u;
     const float z = idx < n ? depths[idx] : 0.0f;
-    k[i] = t > 0 ? __float_as_uint(z) : 0xFFFFFFFFu;
+    m[i] = idx < n ? *reinterpret_cast<const float2*>(means2d + 2 * idx) : make_float2(0.0f, 0.0f);
+    r[i] = idx < n ? *reinterpret_cast<const int2*>(radii + 2 * idx) : make_int2(0, 0);
+    k[i] = t[i] > 0 ? __float_as_uint(z) : 0xFFFFFFFFu;
   }
 #pragma unroll
   for (int i = 0; i < kSortItems; ++i) {
@@ -171,6 +212,13 @@ __global__ __launch_bounds__(kSortThreads) void k_bin_prep(int32_t n, const floa
     if (idx < n) {
       keys[idx] = k[i];
       vals[idx] = (uint32_t)idx;
+      uint32_t tb = 0, w = 1;
+      if (t[i] > 0) {
+        const TileRect rc = tile_rect(m[i].x, m[i].y, (float)r[i].x, (float)r[i].y, tiles_x, tiles_y);
+        tb = (uint32_t)(rc.y0 * tiles_x + rc.x0);
+        w = (uint32_t)(rc.x1 - rc.x0);
+      }
+      rec[idx] = make_uint4(t[i], tb, w, 0u);
 #pragma unroll
       for (int p = 0; p < 4; ++p) atomicAdd(&s_hist[p][(k[i] >> (8 * p)) & 0xFF], 1u);
     }
@@ -198,24 +246,165 @@ __global__ __launch_bounds__(kRadix) void k_hist_reduce(const uint32_t* __restri
 }
 
 // ---------------------------------------------------------------------------------------------
-// 3/5. one stable LSD radix pass over `bits` (<= 8) bits at `shift` (Onesweep-style)
+// Pairs per tile, tile ranges and the tile-digit histograms of the pair sort. The count of pairs
+// per tile does not depend on the depth order, so extra workgroups of the first two depth passes
+// compute it while those passes sort: row y of a rectangle puts one pair on each tile of the run
+// [a, a + w) of tile ids, i.e. +1 at a and -1 at a + w of a difference array over the tiles
+// (pass 0); one workgroup then prefix-sums it into per-tile counts, ranges and histograms
+// (pass 1). The total of the counts is P, so that workgroup also knows whether P fits the
+// capacity (else every range stays (0, 0)).
+// ---------------------------------------------------------------------------------------------
+struct TileCountArgs {
+  const uint4* rec;     // (count, first tile, width, -) per Gaussian, id order (k_bin_prep)
+  int32_t n;
+  int32_t tiles_x;
+  uint32_t ntiles;
+  uint32_t* tdiff;      // ntiles + 1 words, zeroed by k_bin_prep
+  uint32_t* ranges;     // [ntiles, 2], zeroed by k_bin_prep
+  uint64_t capacity;
+  int npass;
+  uint32_t* hist_pair;  // [npass][256]
+};
+constexpr int kRowGaussians = 2048;  // Gaussians per row workgroup (two per lane)
+
+// Row workgroup rb: Gaussians [2048 rb, 2048 (rb + 1)) of the id order, two per lane. A lane
+// walks the rows of its own Gaussian when there are at most kOwnRows of them; the taller ones
+// are walked by the whole wave, one Gaussian at a time (its rectangle read with readlane), so a
+// screen-filling splat does not hold up its wave. The difference array is staged in LDS (`lds`,
+// `lds_words` long) when it fits.
+constexpr uint32_t kOwnRows = 8;
+__device__ void tile_rows(const TileCountArgs& a, uint32_t rb, uint32_t* lds, uint32_t lds_words) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool staged = a.ntiles + 1 <= lds_words;
+  if (staged) {
+    for (uint32_t t = tid; t <= a.ntiles; t += kSortThreads) lds[t] = 0;
+    __syncthreads();
+  }
+  uint32_t* diff = staged ? lds : a.tdiff;
+  const uint32_t tx = (uint32_t)a.tiles_x;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int64_t j = (int64_t)rb * kRowGaussians + wave * 128 + k * 64 + lane;
+    const uint4 r = j < a.n ? a.rec[j] : make_uint4(0u, 0u, 1u, 0u);
+    const uint32_t h = r.x / r.z;
+    if (h <= kOwnRows) {
+      for (uint32_t y = 0; y < h; ++y) {
+        atomicAdd(&diff[r.y + y * tx], 1u);
+        atomicSub(&diff[r.y + y * tx + r.z], 1u);
+      }
+    }
+    uint64_t tall = __ballot(h > kOwnRows);
+    while (tall) {
+      const int src = __builtin_ctzll(tall);
+      tall &= tall - 1;
+      const uint32_t hh = __builtin_amdgcn_readlane(h, src);
+      const uint32_t tb = __builtin_amdgcn_readlane(r.y, src), w = __builtin_amdgcn_readlane(r.z, src);
+      for (uint32_t y = lane; y < hh; y += 64) {
+        atomicAdd(&diff[tb + y * tx], 1u);
+        atomicSub(&diff[tb + y * tx + w], 1u);
+      }
+    }
+  }
+  if (staged) {
+    __syncthreads();
+    for (uint32_t t = tid; t <= a.ntiles; t += kSortThreads) {
+      const uint32_t v = lds[t];
+      if (v) atomicAdd(&a.tdiff[t], v);
+    }
+  }
+}
+
+// One workgroup: per-tile counts = prefix sums of the difference array, in chunks of 8192 tiles
+// staged in `lds`; a first sweep finds P, a second writes ranges and histograms.
+__device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t* s_wsum, uint32_t (*s_hist)[kRadix]) {
+  const int tid = threadIdx.x;
+  constexpr uint32_t kChunk = kSortThreads * 8;
+  if (tid < kRadix)
+    for (int k = 0; k < a.npass; ++k) s_hist[k][tid] = 0;
+  uint64_t P = 0;
+  for (int sweep = 0; sweep < 2; ++sweep) {
+    const bool write = sweep == 1 && P <= a.capacity;
+    if (sweep == 1 && !write) break;
+    uint32_t carry_d = 0, carry_c = 0;
+    for (uint32_t cb = 0; cb < a.ntiles; cb += kChunk) {
+      uint32_t v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t t = cb + (uint32_t)(q * kSortThreads + tid);
+        v[q] = t < a.ntiles ? ld_dev(&a.tdiff[t]) : 0u;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) lds[q * kSortThreads + tid] = v[q];
+      __syncthreads();
+      uint32_t d[8], dsum = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        d[q] = lds[tid * 8 + q];
+        dsum += d[q];
+      }
+      uint32_t dtot;
+      const uint32_t dpre = carry_d + block_excl_scan1024<uint32_t>(dsum, s_wsum, &dtot);
+      uint32_t cnt[8], csum = 0, run = dpre;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        run += d[q];
+        cnt[q] = cb + (uint32_t)(tid * 8 + q) < a.ntiles ? run : 0u;  // no tiles past the grid
+        csum += cnt[q];
+      }
+      uint32_t ctot;
+      uint32_t start = carry_c + block_excl_scan1024<uint32_t>(csum, s_wsum, &ctot);
+      if (write) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t t = cb + (uint32_t)(tid * 8 + q);
+          if (t < a.ntiles && cnt[q]) {
+            a.ranges[2 * t] = start;
+            a.ranges[2 * t + 1] = start + cnt[q];
+            for (int k = 0; k < a.npass; ++k) atomicAdd(&s_hist[k][(t >> (8 * k)) & 255u], cnt[q]);
+          }
+          start += cnt[q];
+        }
+      }
+      carry_d += dtot;
+      carry_c += ctot;
+      __syncthreads();  // the chunk's LDS is reused
+    }
+    P = carry_c;
+  }
+  __syncthreads();
+  if (tid < kRadix)
+    for (int k = 0; k < a.npass; ++k) a.hist_pair[k * kRadix + tid] = s_hist[k][tid];
+}
+
+// ---------------------------------------------------------------------------------------------
+// 3/6. one stable LSD radix pass over `bits` (<= 8) bits at `shift` (Onesweep-style)
 // The element count is *n_dev when given (pairs: grid sized by the capacity), else n_host. The
 // pass's digit histogram is the sum of `hist_parts` rows of 256 counts, `hist_stride` apart.
 // ---------------------------------------------------------------------------------------------
-template <bool FINAL>
+// EXTRA: 0 none; 1 the last `n_extra` workgroups are tile-row workgroups; 2 the last one is the
+// tile-count finalizer (see above).
+template <bool FINAL, int EXTRA>
 __global__ __launch_bounds__(kSortThreads) void k_onesweep(
     const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, uint32_t* __restrict__ keys_out,
     uint32_t* __restrict__ vals_out, uint64_t* __restrict__ out_keys64, const uint32_t* __restrict__ depth_bits,
     uint32_t n_host, const uint64_t* __restrict__ n_dev, int shift, int bits, const uint32_t* __restrict__ hist,
-    int hist_parts, int hist_stride, uint32_t* __restrict__ status, uint32_t* __restrict__ ticket) {
-  __shared__ uint32_t s_keys[kSortTile];
-  __shared__ uint32_t s_vals[kSortTile];
-  __shared__ uint32_t s_wcnt[kSortWaves][kRadix];  // per wave and digit: count, then wave offset
+    int hist_parts, int hist_stride, uint32_t* __restrict__ status, uint32_t* __restrict__ ticket,
+    uint32_t n_extra, TileCountArgs targs) {
+  constexpr uint32_t kLdsWords = 2 * kSortTile + kSortWaves * kRadix;
+  __shared__ uint32_t s_mem[kLdsWords];
+  uint32_t* s_keys = s_mem;
+  uint32_t* s_vals = s_mem + kSortTile;
+  uint32_t (*s_wcnt)[kRadix] = reinterpret_cast<uint32_t (*)[kRadix]>(s_mem + 2 * kSortTile);  // count, then offset
   __shared__ uint32_t s_dpre[kRadix];
   __shared__ uint32_t s_goff[kRadix];
-  __shared__ uint32_t s_wsum[4];
+  __shared__ uint32_t s_wsum[kSortWaves];
   __shared__ uint32_t s_vb;
 
+  if (EXTRA != 0 && blockIdx.x >= gridDim.x - n_extra) {  // workgroup-uniform
+    if (EXTRA == 1) tile_rows(targs, blockIdx.x - (gridDim.x - n_extra), s_mem, kLdsWords);
+    if (EXTRA == 2) tile_finalize(targs, s_mem, s_wsum, s_wcnt);
+    return;
+  }
   const uint32_t n = n_dev ? (uint32_t)*n_dev : n_host;
   if ((uint64_t)blockIdx.x * kSortTile >= n) return;  // workgroup-uniform: idle workgroups take no ticket
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -319,102 +508,192 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
 }
 
 // ---------------------------------------------------------------------------------------------
-// 4. exclusive scan of tiles_touched in depth order (single pass, decoupled look-back) and
-// emission of each workgroup's (tile id, Gaussian id) pairs, all 256 lanes sharing the pairs
+// 4. exclusive scan of tiles_touched in depth order (single pass, decoupled look-back)
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kScanTile) void k_scan_emit(
-    int32_t n, const uint32_t* __restrict__ sorted_ids, const uint32_t* __restrict__ tiles,
-    const float* __restrict__ means2d, const int32_t* __restrict__ radii, int32_t tiles_x, int32_t tiles_y,
-    uint32_t* __restrict__ pkeys, uint32_t* __restrict__ pvals, uint64_t capacity, int npass,
-    uint64_t* __restrict__ status, Ctrl* ctrl, int64_t* __restrict__ user_num_pairs) {
-  __shared__ uint64_t s_wsum[4];
-  __shared__ uint32_t s_incl[kScanTile];  // workgroup-inclusive pair counts, saturated at 2^31
-  __shared__ uint32_t s_g[kScanTile];
-  __shared__ int32_t s_x0[kScanTile], s_y0[kScanTile], s_w[kScanTile];
-  __shared__ uint32_t s_hist[3][kRadix];
+// Scan over one value per thread of a 1024-thread workgroup with an associative OP: returns the
+// exclusive prefix (identity for thread 0); *total gets the reduction. Two barriers.
+template <typename T, typename OP>
+__device__ __forceinline__ T block_scan1024(T v, T identity, T* s_wsum, T* total, OP op) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  T inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const T t = __shfl_up(inc, off, 64);
+    if (lane >= off) inc = op(inc, t);
+  }
+  if (lane == 63) s_wsum[wave] = inc;
+  __syncthreads();
+  T before = identity, all = identity;
+#pragma unroll
+  for (int w = 0; w < kEmitWaves; ++w) {
+    const T x = s_wsum[w];
+    if (w < wave) before = op(before, x);
+    all = op(all, x);
+  }
+  __syncthreads();
+  *total = all;
+  const T ex = __shfl_up(inc, 1, 64);
+  return op(before, lane == 0 ? identity : ex);
+}
+
+// Workgroup vb scans Gaussians [4096 vb, 4096 (vb + 1)) of the depth order (four consecutive per
+// thread). It writes, in depth order, the record (first pair position, first tile, rect width,
+// Gaussian id) of each, and for every pair chunk (kEmitChunk positions) that starts inside one of
+// its Gaussians' runs, that Gaussian's depth index into chunk_first. The last workgroup
+// publishes P.
+__global__ __launch_bounds__(kEmitThreads) void k_scan(int32_t n, const uint32_t* __restrict__ sorted_ids,
+                                                       const uint4* __restrict__ rec, uint4* __restrict__ drec,
+                                                       uint32_t* __restrict__ chunk_first, uint64_t capacity,
+                                                       uint64_t* __restrict__ status, Ctrl* ctrl,
+                                                       int64_t* __restrict__ user_num_pairs) {
+  __shared__ uint64_t s_wsum[kEmitWaves];
   __shared__ uint32_t s_vb;
   __shared__ uint64_t s_excl;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) s_vb = atomicAdd(&ctrl->tickets[7], 1u);
-  for (int p = 0; p < npass; ++p) s_hist[p][tid] = 0;
   __syncthreads();
   const uint32_t vb = s_vb;
-  const int idx = (int)vb * kScanTile + tid;
-  uint32_t g = 0, c = 0;
-  if (idx < n) {
-    g = sorted_ids[idx];
-    c = tiles[g];
-  }
-  int32_t x0 = 0, y0 = 0, w = 1;
-  if (c > 0) {
-    const float2 m = *reinterpret_cast<const float2*>(means2d + 2 * g);
-    const int2 r = *reinterpret_cast<const int2*>(radii + 2 * g);
-    const TileRect rc = tile_rect(m.x, m.y, (float)r.x, (float)r.y, tiles_x, tiles_y);
-    x0 = rc.x0;
-    y0 = rc.y0;
-    w = rc.x1 - rc.x0;
-  }
-  s_g[tid] = g;
-  s_x0[tid] = x0;
-  s_y0[tid] = y0;
-  s_w[tid] = w;
-  uint64_t tot;
-  const uint64_t texcl = block_excl_scan256<uint64_t>((uint64_t)c, s_wsum, &tot);
-  const uint64_t tincl = texcl + c;
-  s_incl[tid] = tincl < 0x80000000ull ? (uint32_t)tincl : 0x80000000u;
-  if (tid == 0) {
-    st_dev(status + vb, (vb == 0 ? kFlagPre64 : kFlagAgg64) | tot);
-    uint64_t excl = 0;
-    if (vb > 0) {
-      excl = look_back<16, uint64_t, ~kValMask64, kFlagPre64, kValMask64>(status, vb, 1);
-      st_dev(status + vb, kFlagPre64 | (excl + tot));
-    }
-    s_excl = excl;
-    if ((uint64_t)(vb + 1) * kScanTile >= (uint64_t)n) {  // the last workgroup knows P
-      const uint64_t P = excl + tot;
-      ctrl->num_pairs = P;
-      ctrl->eff_pairs = P <= capacity ? P : 0u;
-      if (user_num_pairs) *user_num_pairs = (int64_t)P;
-    }
-  }
-  __syncthreads();
-  const uint64_t excl = s_excl;
-  // pairs [excl, excl + tot) belong to this workgroup; those at or past the capacity are dropped
-  // (then P > capacity and no later kernel reads any pair)
-  const uint32_t emit = excl >= capacity ? 0u : (uint32_t)std::min<uint64_t>(tot, capacity - excl);
-  for (uint32_t j = tid; j < emit; j += kScanTile) {
-    // owner: the first Gaussian whose inclusive count exceeds j (j < 2^30, below saturation)
-    uint32_t lo = 0;
+  uint4 r[kScanItems];
+  uint32_t g[kScanItems];
+  uint64_t sum = 0;
 #pragma unroll
-    for (uint32_t step = kScanTile / 2; step > 0; step >>= 1)
-      if (s_incl[lo + step - 1] <= j) lo += step;
-    const uint32_t local = j - (lo ? s_incl[lo - 1] : 0u);
-    const uint32_t ww = (uint32_t)s_w[lo];
-    const uint32_t row = local / ww, col = local - row * ww;
-    const uint32_t t = (uint32_t)(s_y0[lo] + (int32_t)row) * (uint32_t)tiles_x + (uint32_t)s_x0[lo] + col;
-    pkeys[excl + j] = t;
-    pvals[excl + j] = s_g[lo];
-    for (int p = 0; p < npass; ++p) atomicAdd(&s_hist[p][(t >> (8 * p)) & 0xFF], 1u);
+  for (int i = 0; i < kScanItems; ++i) {
+    const int j = (int)vb * kScanTile + tid * kScanItems + i;
+    g[i] = j < n ? sorted_ids[j] : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < kScanItems; ++i) r[i] = rec[g[i]];  // g = 0 past n: a valid index, unused
+#pragma unroll
+  for (int i = 0; i < kScanItems; ++i) {
+    const int j = (int)vb * kScanTile + tid * kScanItems + i;
+    if (j >= n) r[i] = make_uint4(0u, 0u, 1u, 0u);
+    sum += r[i].x;
+  }
+  uint64_t tot;
+  const uint64_t texcl = block_scan1024<uint64_t>(sum, 0ull, s_wsum, &tot,
+                                                   [](uint64_t a, uint64_t b) { return a + b; });
+  // ---- publish, look back (wave 0: 64 predecessors per round), publish the prefix ----
+  if (wave == 0) {
+    if (lane == 0) st_dev(status + vb, (vb == 0 ? kFlagPre64 : kFlagAgg64) | tot);
+    uint64_t excl = 0;
+    int64_t j = (int64_t)vb - 1;
+    while (j >= 0) {
+      const int64_t p = j - lane;
+      const uint64_t st = p >= 0 ? ld_dev(status + p) : kFlagPre64;  // below tile 0: never consumed
+      const uint64_t fl = st & ~kValMask64;
+      const uint64_t notready = __ballot(fl == 0), pre = __ballot(fl == kFlagPre64);
+      const int first_nr = notready ? __builtin_ctzll(notready) : 64;
+      const int first_pre = pre ? __builtin_ctzll(pre) : 64;
+      const int take = first_pre < first_nr ? first_pre + 1 : first_nr;  // words consumed this round
+      uint64_t v = lane < take ? (st & kValMask64) : 0ull;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+      excl += v;
+      if (first_pre < first_nr) break;
+      j -= take;
+      if (take == 0) __builtin_amdgcn_s_sleep(1);
+    }
+    if (lane == 0) {
+      if (vb > 0) st_dev(status + vb, kFlagPre64 | (excl + tot));
+      s_excl = excl;
+      if ((uint64_t)(vb + 1) * kScanTile >= (uint64_t)n) {  // the last workgroup knows P
+        const uint64_t P = excl + tot;
+        ctrl->num_pairs = P;
+        ctrl->eff_pairs = P <= capacity ? P : 0u;
+        if (user_num_pairs) *user_num_pairs = (int64_t)P;
+      }
+    }
   }
   __syncthreads();
-  for (int p = 0; p < npass; ++p) {
-    const uint32_t h = s_hist[p][tid];
-    if (h) atomicAdd(&ctrl->hist_pair[p][tid], h);
+  uint64_t o = s_excl + texcl;
+#pragma unroll
+  for (int i = 0; i < kScanItems; ++i) {
+    const int j = (int)vb * kScanTile + tid * kScanItems + i;
+    if (j < n) {
+      drec[j] = make_uint4(o < 0xFFFFFFFFull ? (uint32_t)o : 0xFFFFFFFFu, r[i].y, r[i].z, g[i]);
+      const uint64_t end = o + r[i].x;
+      for (uint64_t c = (o + kEmitChunk - 1) / kEmitChunk * kEmitChunk; c < end && c < capacity; c += kEmitChunk)
+        chunk_first[c / kEmitChunk] = (uint32_t)j;
+    }
+    o += r[i].x;
   }
 }
 
 // ---------------------------------------------------------------------------------------------
-// 6. per-tile ranges from the sorted 64-bit keys (the ranges were zeroed by k_bin_prep)
+// 5. emission: workgroup k writes pair positions [kEmitChunk k, kEmitChunk (k + 1)), whatever
+// Gaussians they belong to, so the work is the same for every workgroup
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_ranges(const uint64_t* __restrict__ n_dev, const uint64_t* __restrict__ keys,
-                                                uint32_t ntiles, uint32_t* __restrict__ ranges) {
+__global__ __launch_bounds__(kEmitThreads) void k_emit(const uint64_t* __restrict__ n_dev, int32_t n,
+                                                       const uint4* __restrict__ drec,
+                                                       const uint32_t* __restrict__ chunk_first, int32_t tiles_x,
+                                                       uint32_t* __restrict__ pkeys, uint32_t* __restrict__ pvals) {
+  __shared__ uint32_t s_wsum[kEmitWaves];
+  __shared__ uint32_t s_off[kEmitWindow];
+  __shared__ uint32_t s_tb[kEmitWindow];
+  __shared__ uint32_t s_w[kEmitWindow];
+  __shared__ uint32_t s_g[kEmitWindow];
+  __shared__ uint32_t s_owner[kEmitChunk];
   const uint64_t P = *n_dev;
-  const uint64_t i = blockIdx.x * 256ull + threadIdx.x;
-  if (i >= P) return;
-  const uint32_t t = (uint32_t)(keys[i] >> 32);
-  if (t >= ntiles) return;
-  if (i == 0 || (uint32_t)(keys[i - 1] >> 32) != t) ranges[2 * t] = (uint32_t)i;
-  if (i == P - 1 || (uint32_t)(keys[i + 1] >> 32) != t) ranges[2 * t + 1] = (uint32_t)(i + 1);
+  const uint64_t cs = (uint64_t)blockIdx.x * kEmitChunk;
+  if (cs >= P) return;  // workgroup-uniform
+  const int tid = threadIdx.x;
+  const uint32_t ce = (uint32_t)std::min<uint64_t>(P - cs, kEmitChunk);
+  uint32_t jw = chunk_first[blockIdx.x];  // the Gaussian (depth index) that holds position cs
+  uint32_t done = 0;
+  while (done < ce) {  // workgroup-uniform; each window covers at least kEmitWindow - 1 positions
+    for (int q = tid; q < kEmitChunk; q += kEmitThreads) s_owner[q] = 0u;
+    __syncthreads();
+    // window of kEmitWindow Gaussians from jw; each marks its first position in [done, ce)
+    const uint64_t lo = cs + done, hi = cs + ce;
+#pragma unroll
+    for (int i = 0; i < kEmitWindow / kEmitThreads; ++i) {
+      const uint32_t li = (uint32_t)(i * kEmitThreads + tid);
+      const uint64_t j = (uint64_t)jw + li;
+      const uint4 d = j < (uint64_t)n ? drec[j] : make_uint4(0xFFFFFFFFu, 0u, 1u, 0u);
+      s_off[li] = d.x;
+      s_tb[li] = d.y;
+      s_w[li] = d.z;
+      s_g[li] = d.w;
+      if (d.x >= lo && d.x < hi) atomicMax(&s_owner[d.x - lo], li);
+    }
+    __syncthreads();
+    // positions below the last window Gaussian's start are covered by this window
+    const uint32_t last_off = s_off[kEmitWindow - 1];
+    const uint64_t cover = (uint64_t)jw + kEmitWindow - 1 < (uint64_t)n && (uint64_t)last_off < hi
+                               ? (uint64_t)last_off : hi;
+    const uint32_t lim = (uint32_t)(cover - cs);
+    // inclusive max-scan of the markers: owner of each position
+    uint32_t v[kEmitPer];
+    uint32_t run = 0;
+#pragma unroll
+    for (int q = 0; q < kEmitPer; ++q) {
+      v[q] = max(run, s_owner[tid * kEmitPer + q]);
+      run = v[q];
+    }
+    uint32_t mx;
+    const uint32_t before = block_scan1024<uint32_t>(run, 0u, s_wsum, &mx,
+                                                      [](uint32_t a, uint32_t b) { return max(a, b); });
+#pragma unroll
+    for (int q = 0; q < kEmitPer; ++q) s_owner[tid * kEmitPer + q] = max(before, v[q]);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kEmitPer; ++q) {
+      const uint32_t p = done + (uint32_t)(q * kEmitThreads + tid);
+      if (p < lim) {
+        const uint32_t li = s_owner[p - done];
+        const uint32_t local = (uint32_t)(cs + p - s_off[li]);
+        const uint32_t ww = s_w[li];
+        const uint32_t row = local / ww, col = local - row * ww;
+        const uint32_t t = s_tb[li] + row * (uint32_t)tiles_x + col;
+        pkeys[cs + p] = t;
+        pvals[cs + p] = s_g[li];
+      }
+    }
+    __syncthreads();
+    // the next window starts at the Gaussian holding position lim (the window's last one)
+    if (lim < ce) jw += kEmitWindow - 1;
+    done = lim;
+  }
 }
 
 __global__ void k_fill_u32(uint32_t* __restrict__ p, size_t count, uint32_t v) {
@@ -427,9 +706,9 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, size_t count, uint32_t v) {
 // k_bin_prep; the rest is written before it is read
 // ---------------------------------------------------------------------------------------------
 struct BinLayout {
-  size_t ctrl, scan_status, dstatus, pstatus, zero_end;
-  size_t dhist, dkA, dvA, dkB, dvB, pkB, pvB, total;
-  uint32_t nbN, nbS, nbCap;
+  size_t ctrl, scan_status, dstatus, pstatus, tdiff, zero_end;
+  size_t dhist, dkA, dvA, dkB, dvB, rec, drec, chunk_first, pkB, pvB, total;
+  uint32_t nbN, nbS, nbCap, nbEmit;
   int tile_bits, npass;
 };
 
@@ -444,6 +723,7 @@ BinLayout bin_layout(int32_t n, int64_t cap, const gs_camera* cam) {
   L.nbN = (uint32_t)((n + kSortTile - 1) / kSortTile);
   L.nbS = (uint32_t)((n + kScanTile - 1) / kScanTile);
   L.nbCap = (uint32_t)((cap + kSortTile - 1) / kSortTile);
+  L.nbEmit = (uint32_t)((cap + kEmitChunk - 1) / kEmitChunk);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -454,12 +734,16 @@ BinLayout bin_layout(int32_t n, int64_t cap, const gs_camera* cam) {
   L.scan_status = take((size_t)L.nbS * 8);
   L.dstatus = take((size_t)4 * L.nbN * kRadix * 4);
   L.pstatus = take((size_t)L.npass * L.nbCap * kRadix * 4);
+  L.tdiff = take(((size_t)ntiles + 1) * 4);
   L.zero_end = off;
   L.dhist = take((size_t)L.nbN * 4 * kRadix * 4);
   L.dkA = take((size_t)n * 4);
   L.dvA = take((size_t)n * 4);
   L.dkB = take((size_t)n * 4);
   L.dvB = take((size_t)n * 4);
+  L.rec = take((size_t)n * 16);
+  L.drec = take((size_t)n * 16);
+  L.chunk_first = take((size_t)L.nbEmit * 4);
   L.pkB = take((size_t)cap * 4);
   L.pvB = take((size_t)cap * 4);
   L.total = off;
@@ -516,6 +800,7 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
   uint32_t* dstatus = (uint32_t*)(ws + L.dstatus);
   uint32_t* pstatus = (uint32_t*)(ws + L.pstatus);
   const size_t zero_words = (L.zero_end - L.ctrl) / 4;
+  const int32_t tiles_x = (cam->width + 15) / 16, tiles_y = (cam->height + 15) / 16;
   {
     // enough workgroups for the depth keys, and for zeroing about 32 words per thread
     const size_t zwords = zero_words + (size_t)(2 * ntiles);
@@ -523,8 +808,8 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
     const unsigned blocks = (unsigned)std::max<size_t>(L.nbN, std::min<size_t>(zblocks, 2048));
     TimedScope ts("bin_prep", s);
     hipLaunchKernelGGL(k_bin_prep, dim3(blocks), dim3(kSortThreads), 0, s, n, proj->d_depths, proj->d_tiles_touched,
-                       dkA, dvA, dhist, L.nbN, (uint32_t*)(ws + L.ctrl), zero_words, d_tile_ranges,
-                       (size_t)(2 * ntiles));
+                       proj->d_means2d, proj->d_radii, tiles_x, tiles_y, (uint4*)(ws + L.rec), dkA, dvA, dhist,
+                       L.nbN, (uint32_t*)(ws + L.ctrl), zero_words, d_tile_ranges, (size_t)(2 * ntiles));
   }
   // up to kDirectHistRows workgroups, each depth pass sums the per-workgroup histograms itself
   const bool direct_hist = L.nbN <= (uint32_t)kDirectHistRows;
@@ -533,26 +818,45 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
     hipLaunchKernelGGL(k_hist_reduce, dim3(4, (L.nbN + kReduceRows - 1) / kReduceRows), dim3(kRadix), 0, s, dhist,
                        L.nbN, ctrl);
   }
+  // pass 0 carries the tile-row workgroups, pass 1 the tile-count finalizer
+  TileCountArgs targs;
+  targs.rec = (const uint4*)(ws + L.rec);
+  targs.n = n;
+  targs.tiles_x = tiles_x;
+  targs.ntiles = (uint32_t)ntiles;
+  targs.tdiff = (uint32_t*)(ws + L.tdiff);
+  targs.ranges = d_tile_ranges;
+  targs.capacity = (uint64_t)pair_capacity;
+  targs.npass = L.npass;
+  targs.hist_pair = &ctrl->hist_pair[0][0];
+  const uint32_t n_rows = (uint32_t)((n + kRowGaussians - 1) / kRowGaussians);
   for (int p = 0; p < 4; ++p) {
     const bool even = (p % 2) == 0;
     const uint32_t* hist = direct_hist ? dhist + p * kRadix : ctrl->hist_depth[p];
+    const uint32_t n_extra = p == 0 ? n_rows : (p == 1 ? 1u : 0u);
+    auto kern = p == 0 ? k_onesweep<false, 1> : (p == 1 ? k_onesweep<false, 2> : k_onesweep<false, 0>);
     TimedScope ts("depth_sort_pass", s);
-    hipLaunchKernelGGL(k_onesweep<false>, dim3(L.nbN), dim3(kSortThreads), 0, s, even ? dkA : dkB, even ? dvA : dvB,
+    hipLaunchKernelGGL(kern, dim3(L.nbN + n_extra), dim3(kSortThreads), 0, s, even ? dkA : dkB, even ? dvA : dvB,
                        even ? dkB : dkA, even ? dvB : dvA, (uint64_t*)nullptr, (const uint32_t*)nullptr,
                        (uint32_t)n, (const uint64_t*)nullptr, 8 * p, 8, hist, direct_hist ? (int)L.nbN : 1,
-                       4 * kRadix, dstatus + (size_t)p * L.nbN * kRadix, &ctrl->tickets[p]);
+                       4 * kRadix, dstatus + (size_t)p * L.nbN * kRadix, &ctrl->tickets[p], n_extra, targs);
   }
   // ping-pong of the pair sort: A = d_keys viewed as two u32 arrays of pair_capacity, B = workspace
   uint32_t* kA = (uint32_t*)d_keys;
   uint32_t* vA = kA ? kA + pair_capacity : nullptr;
   uint32_t *kB = (uint32_t*)(ws + L.pkB), *vB = (uint32_t*)(ws + L.pvB);
   const bool emit_to_A = (L.npass % 2) == 0;
-  const int32_t tiles_x = (cam->width + 15) / 16, tiles_y = (cam->height + 15) / 16;
   {
-    TimedScope ts("scan_emit", s);
-    hipLaunchKernelGGL(k_scan_emit, dim3(L.nbS), dim3(kScanTile), 0, s, n, dvA, proj->d_tiles_touched,
-                       proj->d_means2d, proj->d_radii, tiles_x, tiles_y, emit_to_A ? kA : kB, emit_to_A ? vA : vB,
-                       (uint64_t)pair_capacity, L.npass, scan_status, ctrl, d_num_pairs);
+    TimedScope ts("scan", s);
+    hipLaunchKernelGGL(k_scan, dim3(L.nbS), dim3(kEmitThreads), 0, s, n, dvA, (const uint4*)(ws + L.rec),
+                       (uint4*)(ws + L.drec), (uint32_t*)(ws + L.chunk_first), (uint64_t)pair_capacity, scan_status,
+                       ctrl, d_num_pairs);
+  }
+  if (L.nbEmit > 0) {
+    TimedScope ts("emit", s);
+    hipLaunchKernelGGL(k_emit, dim3(L.nbEmit), dim3(kEmitThreads), 0, s, &ctrl->eff_pairs, n,
+                       (const uint4*)(ws + L.drec), (const uint32_t*)(ws + L.chunk_first), tiles_x,
+                       emit_to_A ? kA : kB, emit_to_A ? vA : vB);
   }
   if (L.nbCap > 0) {
     bool in_A = emit_to_A;
@@ -564,19 +868,18 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
       uint32_t *ko = in_A ? kB : kA, *vo = in_A ? vB : vA;
       TimedScope ts("pair_sort_pass", s);
       if (last) {
-        hipLaunchKernelGGL(k_onesweep<true>, dim3(L.nbCap), dim3(kSortThreads), 0, s, ki, vi, (uint32_t*)nullptr,
+        hipLaunchKernelGGL((k_onesweep<true, 0>), dim3(L.nbCap), dim3(kSortThreads), 0, s, ki, vi, (uint32_t*)nullptr,
                            d_ids, d_keys, (const uint32_t*)proj->d_depths, 0u, &ctrl->eff_pairs, shift, bits,
-                           ctrl->hist_pair[p], 1, 0, pstatus + (size_t)p * L.nbCap * kRadix, &ctrl->tickets[4 + p]);
+                           ctrl->hist_pair[p], 1, 0, pstatus + (size_t)p * L.nbCap * kRadix, &ctrl->tickets[4 + p],
+                           0u, targs);
       } else {
-        hipLaunchKernelGGL(k_onesweep<false>, dim3(L.nbCap), dim3(kSortThreads), 0, s, ki, vi, ko, vo,
+        hipLaunchKernelGGL((k_onesweep<false, 0>), dim3(L.nbCap), dim3(kSortThreads), 0, s, ki, vi, ko, vo,
                            (uint64_t*)nullptr, (const uint32_t*)nullptr, 0u, &ctrl->eff_pairs, shift, bits,
-                           ctrl->hist_pair[p], 1, 0, pstatus + (size_t)p * L.nbCap * kRadix, &ctrl->tickets[4 + p]);
+                           ctrl->hist_pair[p], 1, 0, pstatus + (size_t)p * L.nbCap * kRadix, &ctrl->tickets[4 + p],
+                           0u, targs);
       }
       in_A = !in_A;
     }
-    TimedScope ts("ranges", s);
-    hipLaunchKernelGGL(k_ranges, dim3((unsigned)((pair_capacity + 255) / 256)), dim3(256), 0, s, &ctrl->eff_pairs,
-                       d_keys, (uint32_t)ntiles, d_tile_ranges);
   }
   const gs_status st = check_launch("gs_bin_and_sort");
   if (st != GS_OK || !h_num_pairs) return st;

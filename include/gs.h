@@ -176,7 +176,8 @@ gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float* d_means, c
  * (1 - lambda) L1 + lambda (1 - SSIM)): L = mean |image - target| over h*w*3 values, so
  * dL/dimage = sign(image - target) / (3 h w) with sign(0) = 0.
  * Inputs: d_image, d_target [h,w,3]. Outputs: d_dL_dimage [h,w,3]; d_loss (device float[1],
- * may be NULL) receives L.
+ * may be NULL) receives L. Arrays must be 4-byte aligned (16-byte aligned ones take a float4
+ * path). Errors: GS_ERR_INVALID_ARG for a size <= 0, a NULL array or a misaligned one.
  */
 gs_status gs_loss_l1(int32_t width, int32_t height, const float* d_image, const float* d_target,
                      float* d_dL_dimage, float* d_loss, void* stream);

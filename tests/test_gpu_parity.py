@@ -295,3 +295,11 @@ def test_loss_l1(env):
     want = np.sign(img.astype(np.float64) - tgt) / img.size
     assert np.allclose(dimg.cpu().numpy(), want, rtol=1e-6, atol=0)
     assert loss.item() == pytest.approx(np.abs(img.astype(np.float64) - tgt).mean(), rel=1e-5)
+    # arrays that are 4- but not 16-byte aligned (a target image inside a batch of odd-sized ones)
+    big_i = torch.from_numpy(np.concatenate([[0.0], img.ravel()]).astype(np.float32)).cuda()
+    big_t = torch.from_numpy(np.concatenate([[0.0], tgt.ravel()]).astype(np.float32)).cuda()
+    big_g = torch.zeros(img.size + 1, device="cuda")
+    gs.gs_loss_l1(23, 37, big_i[1:], big_t[1:], big_g[1:], loss)
+    torch.cuda.synchronize()
+    assert np.allclose(big_g[1:].cpu().numpy(), want.ravel(), rtol=1e-6, atol=0) and big_g[0].item() == 0.0
+    assert loss.item() == pytest.approx(np.abs(img.astype(np.float64) - tgt).mean(), rel=1e-5)
