@@ -382,19 +382,22 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t* s
 // pass's digit histogram is the sum of `hist_parts` rows of 256 counts, `hist_stride` apart.
 // ---------------------------------------------------------------------------------------------
 // EXTRA: 0 none; 1 the last `n_extra` workgroups are tile-row workgroups; 2 the last one is the
-// tile-count finalizer (see above).
-template <bool FINAL, int EXTRA>
+// tile-count finalizer (see above). ITEMS keys per lane: a workgroup sorts 1024 ITEMS keys
+// (4 keeps the ranking chains short for small inputs; 8 halves the workgroups, and so the
+// look-back traffic, for large ones).
+template <bool FINAL, int EXTRA, int ITEMS>
 __global__ __launch_bounds__(kSortThreads) void k_onesweep(
     const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, uint32_t* __restrict__ keys_out,
     uint32_t* __restrict__ vals_out, uint64_t* __restrict__ out_keys64, const uint32_t* __restrict__ depth_bits,
     uint32_t n_host, const uint64_t* __restrict__ n_dev, int shift, int bits, const uint32_t* __restrict__ hist,
     int hist_parts, int hist_stride, uint32_t* __restrict__ status, uint32_t* __restrict__ ticket,
     uint32_t n_extra, TileCountArgs targs) {
-  constexpr uint32_t kLdsWords = 2 * kSortTile + kSortWaves * kRadix;
+  constexpr int TILE = kSortThreads * ITEMS;
+  constexpr uint32_t kLdsWords = 2 * TILE + kSortWaves * kRadix;
   __shared__ uint32_t s_mem[kLdsWords];
   uint32_t* s_keys = s_mem;
-  uint32_t* s_vals = s_mem + kSortTile;
-  uint32_t (*s_wcnt)[kRadix] = reinterpret_cast<uint32_t (*)[kRadix]>(s_mem + 2 * kSortTile);  // count, then offset
+  uint32_t* s_vals = s_mem + TILE;
+  uint32_t (*s_wcnt)[kRadix] = reinterpret_cast<uint32_t (*)[kRadix]>(s_mem + 2 * TILE);  // count, then offset
   __shared__ uint32_t s_dpre[kRadix];
   __shared__ uint32_t s_goff[kRadix];
   __shared__ uint32_t s_wsum[kSortWaves];
@@ -406,23 +409,23 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
     return;
   }
   const uint32_t n = n_dev ? (uint32_t)*n_dev : n_host;
-  if ((uint64_t)blockIdx.x * kSortTile >= n) return;  // workgroup-uniform: idle workgroups take no ticket
+  if ((uint64_t)blockIdx.x * TILE >= n) return;  // workgroup-uniform: idle workgroups take no ticket
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) s_vb = atomicAdd(ticket, 1u);
   for (int i = tid; i < kSortWaves * kRadix; i += kSortThreads) (&s_wcnt[0][0])[i] = 0;
   __syncthreads();
   // exactly ceil(n / 4096) workgroups take tickets, so every ticket has base < n
   const uint32_t vb = s_vb;
-  const uint32_t base = vb * (uint32_t)kSortTile;
+  const uint32_t base = vb * (uint32_t)TILE;
   if (base >= n) return;  // unreachable with a zeroed ticket; guards a stale one
   const uint32_t mask = (1u << bits) - 1u;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
   // ---- load (wave-striped: wave w owns [base + 256 w, base + 256 (w + 1))) and rank ----
-  uint32_t k[kSortItems], v[kSortItems], rank[kSortItems];
+  uint32_t k[ITEMS], v[ITEMS], rank[ITEMS];
 #pragma unroll
-  for (int i = 0; i < kSortItems; ++i) {
-    const uint32_t idx = base + (uint32_t)(wave * 64 * kSortItems + i * 64 + lane);
+  for (int i = 0; i < ITEMS; ++i) {
+    const uint32_t idx = base + (uint32_t)(wave * 64 * ITEMS + i * 64 + lane);
     const bool valid = idx < n;
     k[i] = valid ? keys_in[idx] : 0u;
     v[i] = valid ? vals_in[idx] : 0u;
@@ -431,8 +434,8 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
   if (tid < kRadix)
     for (int r = 0; r < hist_parts; ++r) h += hist[(size_t)r * hist_stride + tid];
 #pragma unroll
-  for (int i = 0; i < kSortItems; ++i) {
-    const uint32_t idx = base + (uint32_t)(wave * 64 * kSortItems + i * 64 + lane);
+  for (int i = 0; i < ITEMS; ++i) {
+    const uint32_t idx = base + (uint32_t)(wave * 64 * ITEMS + i * 64 + lane);
     const bool valid = idx < n;
     const uint32_t d = (k[i] >> shift) & mask;
     uint64_t m = __ballot(valid);
@@ -479,8 +482,8 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
 
   // ---- scatter to LDS in local sorted order, then out with consecutive threads ----
 #pragma unroll
-  for (int i = 0; i < kSortItems; ++i) {
-    const uint32_t idx = base + (uint32_t)(wave * 64 * kSortItems + i * 64 + lane);
+  for (int i = 0; i < ITEMS; ++i) {
+    const uint32_t idx = base + (uint32_t)(wave * 64 * ITEMS + i * 64 + lane);
     if (idx < n) {
       const uint32_t d = (k[i] >> shift) & mask;
       const uint32_t lp = s_dpre[d] + s_wcnt[wave][d] + rank[i];
@@ -489,9 +492,9 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
     }
   }
   __syncthreads();
-  const uint32_t count = (n - base < (uint32_t)kSortTile) ? (n - base) : (uint32_t)kSortTile;
+  const uint32_t count = (n - base < (uint32_t)TILE) ? (n - base) : (uint32_t)TILE;
 #pragma unroll
-  for (int i = 0; i < kSortItems; ++i) {
+  for (int i = 0; i < ITEMS; ++i) {
     const uint32_t j = (uint32_t)(i * kSortThreads + tid);
     if (j >= count) break;
     const uint32_t key = s_keys[j], val = s_vals[j];
@@ -834,7 +837,7 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
     const bool even = (p % 2) == 0;
     const uint32_t* hist = direct_hist ? dhist + p * kRadix : ctrl->hist_depth[p];
     const uint32_t n_extra = p == 0 ? n_rows : (p == 1 ? 1u : 0u);
-    auto kern = p == 0 ? k_onesweep<false, 1> : (p == 1 ? k_onesweep<false, 2> : k_onesweep<false, 0>);
+    auto kern = p == 0 ? k_onesweep<false, 1, 4> : (p == 1 ? k_onesweep<false, 2, 4> : k_onesweep<false, 0, 4>);
     TimedScope ts("depth_sort_pass", s);
     hipLaunchKernelGGL(kern, dim3(L.nbN + n_extra), dim3(kSortThreads), 0, s, even ? dkA : dkB, even ? dvA : dvB,
                        even ? dkB : dkA, even ? dvB : dvA, (uint64_t*)nullptr, (const uint32_t*)nullptr,
@@ -859,6 +862,9 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
                        emit_to_A ? kA : kB, emit_to_A ? vA : vB);
   }
   if (L.nbCap > 0) {
+    // 8 keys per lane (8192 per workgroup) for large pair buffers
+    const bool wide = pair_capacity > ((int64_t)1 << 19);
+    const unsigned grid = wide ? (L.nbCap + 1) / 2 : L.nbCap;
     bool in_A = emit_to_A;
     for (int p = 0; p < L.npass; ++p) {
       const int shift = 8 * p;
@@ -866,18 +872,14 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
       const bool last = p == L.npass - 1;
       uint32_t *ki = in_A ? kA : kB, *vi = in_A ? vA : vB;
       uint32_t *ko = in_A ? kB : kA, *vo = in_A ? vB : vA;
+      auto kern = last ? (wide ? k_onesweep<true, 0, 8> : k_onesweep<true, 0, 4>)
+                       : (wide ? k_onesweep<false, 0, 8> : k_onesweep<false, 0, 4>);
       TimedScope ts("pair_sort_pass", s);
-      if (last) {
-        hipLaunchKernelGGL((k_onesweep<true, 0>), dim3(L.nbCap), dim3(kSortThreads), 0, s, ki, vi, (uint32_t*)nullptr,
-                           d_ids, d_keys, (const uint32_t*)proj->d_depths, 0u, &ctrl->eff_pairs, shift, bits,
-                           ctrl->hist_pair[p], 1, 0, pstatus + (size_t)p * L.nbCap * kRadix, &ctrl->tickets[4 + p],
-                           0u, targs);
-      } else {
-        hipLaunchKernelGGL((k_onesweep<false, 0>), dim3(L.nbCap), dim3(kSortThreads), 0, s, ki, vi, ko, vo,
-                           (uint64_t*)nullptr, (const uint32_t*)nullptr, 0u, &ctrl->eff_pairs, shift, bits,
-                           ctrl->hist_pair[p], 1, 0, pstatus + (size_t)p * L.nbCap * kRadix, &ctrl->tickets[4 + p],
-                           0u, targs);
-      }
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(kSortThreads), 0, s, ki, vi, last ? (uint32_t*)nullptr : ko,
+                         last ? d_ids : vo, last ? d_keys : (uint64_t*)nullptr,
+                         last ? (const uint32_t*)proj->d_depths : (const uint32_t*)nullptr, 0u, &ctrl->eff_pairs,
+                         shift, bits, ctrl->hist_pair[p], 1, 0, pstatus + (size_t)p * L.nbCap * kRadix,
+                         &ctrl->tickets[4 + p], 0u, targs);
       in_A = !in_A;
     }
   }
