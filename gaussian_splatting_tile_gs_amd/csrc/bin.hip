@@ -261,6 +261,7 @@ struct TileCountArgs {
   uint32_t ntiles;
   uint32_t* tdiff;      // ntiles + 1 words, zeroed by k_bin_prep
   uint32_t* ranges;     // [ntiles, 2], zeroed by k_bin_prep
+  uint32_t* order;      // [ntiles] processing order of the tiles (optional)
   uint64_t capacity;
   int npass;
   uint32_t* hist_pair;  // [npass][256]
@@ -315,16 +316,25 @@ __device__ void tile_rows(const TileCountArgs& a, uint32_t rb, uint32_t* lds, ui
 }
 
 // One workgroup: per-tile counts = prefix sums of the difference array, in chunks of 8192 tiles
-// staged in `lds`; a first sweep finds P, a second writes ranges and histograms.
+// staged in `lds`. A first sweep finds P and how many tiles fall in each count class
+// (bit length of the count); a second writes the ranges and histograms (when P fits) and the
+// processing order: tiles by count class, the heaviest class first, empty tiles last, so that
+// the long raster workgroups start first.
+__device__ __forceinline__ uint32_t count_class(uint32_t c) { return c ? 32u - (uint32_t)__clz(c) : 0u; }
+
 __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t* s_wsum, uint32_t (*s_hist)[kRadix]) {
   const int tid = threadIdx.x;
   constexpr uint32_t kChunk = kSortThreads * 8;
+  uint32_t* s_cls = s_hist[3];       // tiles per count class (33)
+  uint32_t* s_cur = s_hist[3] + 64;  // next order slot per class
   if (tid < kRadix)
     for (int k = 0; k < a.npass; ++k) s_hist[k][tid] = 0;
+  if (tid < 64) s_cls[tid] = 0;
+  __syncthreads();
   uint64_t P = 0;
   for (int sweep = 0; sweep < 2; ++sweep) {
     const bool write = sweep == 1 && P <= a.capacity;
-    if (sweep == 1 && !write) break;
+    if (sweep == 1 && !write && !a.order) break;
     uint32_t carry_d = 0, carry_c = 0;
     for (uint32_t cb = 0; cb < a.ntiles; cb += kChunk) {
       uint32_t v[8];
@@ -353,26 +363,41 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t* s
       }
       uint32_t ctot;
       uint32_t start = carry_c + block_excl_scan1024<uint32_t>(csum, s_wsum, &ctot);
-      if (write) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint32_t t = cb + (uint32_t)(tid * 8 + q);
-          if (t < a.ntiles && cnt[q]) {
-            a.ranges[2 * t] = start;
-            a.ranges[2 * t + 1] = start + cnt[q];
-            for (int k = 0; k < a.npass; ++k) atomicAdd(&s_hist[k][(t >> (8 * k)) & 255u], cnt[q]);
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t t = cb + (uint32_t)(tid * 8 + q);
+        if (t < a.ntiles) {
+          if (sweep == 0) {
+            atomicAdd(&s_cls[count_class(cnt[q])], 1u);
+          } else {
+            if (write && cnt[q]) {
+              a.ranges[2 * t] = start;
+              a.ranges[2 * t + 1] = start + cnt[q];
+              for (int k = 0; k < a.npass; ++k) atomicAdd(&s_hist[k][(t >> (8 * k)) & 255u], cnt[q]);
+            }
+            if (a.order) a.order[atomicAdd(&s_cur[count_class(cnt[q])], 1u)] = t;
           }
-          start += cnt[q];
         }
+        start += cnt[q];
       }
       carry_d += dtot;
       carry_c += ctot;
       __syncthreads();  // the chunk's LDS is reused
     }
-    P = carry_c;
+    if (sweep == 0) {
+      P = carry_c;
+      if (tid == 0) {
+        uint32_t slot = 0;
+        for (int c = 32; c >= 0; --c) {
+          s_cur[c] = slot;
+          slot += s_cls[c];
+        }
+      }
+      __syncthreads();
+    }
   }
   __syncthreads();
-  if (tid < kRadix)
+  if (tid < kRadix && P <= a.capacity)
     for (int k = 0; k < a.npass; ++k) a.hist_pair[k * kRadix + tid] = s_hist[k][tid];
 }
 
@@ -699,6 +724,10 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit(const uint64_t* __restric
   }
 }
 
+__global__ void k_iota_u32(uint32_t* __restrict__ p, uint32_t count) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < count; i += gridDim.x * blockDim.x) p[i] = i;
+}
+
 __global__ void k_fill_u32(uint32_t* __restrict__ p, size_t count, uint32_t v) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < count; i += (size_t)gridDim.x * blockDim.x)
     p[i] = v;
@@ -765,8 +794,8 @@ extern "C" size_t gs_bin_workspace_bytes(int32_t n, int64_t pair_capacity, const
 
 extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const gs_camera* cam, void* d_workspace,
                                      size_t workspace_bytes, int64_t pair_capacity, uint64_t* d_keys,
-                                     uint32_t* d_ids, uint32_t* d_tile_ranges, int64_t* d_num_pairs,
-                                     int64_t* h_num_pairs, void* stream) {
+                                     uint32_t* d_ids, uint32_t* d_tile_ranges, uint32_t* d_tile_order,
+                                     int64_t* d_num_pairs, int64_t* h_num_pairs, void* stream) {
   std::string why;
   if (n < 0) return set_error(GS_ERR_INVALID_ARG, "gs_bin_and_sort: n < 0");
   if (!valid_camera(cam, &why)) return set_error(GS_ERR_INVALID_ARG, "gs_bin_and_sort: " + why);
@@ -793,6 +822,9 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
     hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((2 * ntiles + 255) / 256)), dim3(256), 0, s, d_tile_ranges,
                        (size_t)(2 * ntiles), 0u);
     if (d_num_pairs) hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, s, (uint32_t*)d_num_pairs, (size_t)2, 0u);
+    if (d_tile_order)
+      hipLaunchKernelGGL(k_iota_u32, dim3((unsigned)((ntiles + 255) / 256)), dim3(256), 0, s, d_tile_order,
+                         (uint32_t)ntiles);
     return check_launch("gs_bin_and_sort");
   }
   char* ws = (char*)d_workspace;
@@ -829,6 +861,7 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
   targs.ntiles = (uint32_t)ntiles;
   targs.tdiff = (uint32_t*)(ws + L.tdiff);
   targs.ranges = d_tile_ranges;
+  targs.order = d_tile_order;
   targs.capacity = (uint64_t)pair_capacity;
   targs.npass = L.npass;
   targs.hist_pair = &ctrl->hist_pair[0][0];

@@ -16,9 +16,8 @@
 //    and a predicated (branch-free) body;
 //  - a wave leaves the batch as soon as all 64 of its pixels are done (wave-uniform test), the
 //    workgroup stops loading batches when all 256 are (__syncthreads_count);
-//  - workgroup b is tile b: consecutive tiles go round-robin to the 8 XCDs, which spreads the
-//    dense regions of a frame over all of them (the splat records of a frame are a few MB and
-//    stay cache-resident);
+//  - workgroup b takes tile order[b] when a processing order is given (heaviest tiles first, so
+//    the longest workgroups start first and do not end the kernel alone), else tile b;
 //  - backward: nine per-lane terms per splat (linear pieces of its 2D gradient) are summed over
 //    the wave by a reduce-scatter of permlane swaps and DPP exchanges (25 VALU ops in all),
 //    accumulated per workgroup in LDS (ds_add_f32), turned into the 2D gradient and flushed once
@@ -151,7 +150,8 @@ __device__ __forceinline__ void blend_step(const SplatEval& e, bool act, float c
 // ---------------------------------------------------------------------------------------------
 template <bool COUNT>
 __global__ __launch_bounds__(kRasterThreads) void k_blend(
-    uint32_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ ids, const float* __restrict__ means2d,
+    uint32_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ tile_order,
+    const uint32_t* __restrict__ ids, const float* __restrict__ means2d,
     const float* __restrict__ conics, const float* __restrict__ opac, const float* __restrict__ colors,
     const int32_t* __restrict__ radii, DevCamera cam, float* __restrict__ image, float* __restrict__ final_T,
     uint32_t* __restrict__ n_contrib, unsigned long long* __restrict__ eval_count) {
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
   __shared__ float s_c[kBatch];
   __shared__ uint64_t s_qm[4][4];
 
-  const int tile = blockIdx.x;
+  const int tile = tile_order ? (int)tile_order[blockIdx.x] : (int)blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int tx = tile % cam.tiles_x, ty = tile / cam.tiles_x;
   const float tx0 = (float)(tx * kTile), ty0 = (float)(ty * kTile);
@@ -291,7 +291,8 @@ __device__ __forceinline__ void splat_grad(bool contrib, const SplatEval& ev, fl
 // ---------------------------------------------------------------------------------------------
 template <bool COUNT>
 __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
-    uint32_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ ids, const float* __restrict__ means2d,
+    uint32_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ tile_order,
+    const uint32_t* __restrict__ ids, const float* __restrict__ means2d,
     const float* __restrict__ conics, const float* __restrict__ opac, const float* __restrict__ colors,
     const int32_t* __restrict__ radii, DevCamera cam, const float* __restrict__ final_T,
     const uint32_t* __restrict__ n_contrib, const float* __restrict__ dL_dimage, float* __restrict__ g2d,
@@ -304,7 +305,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
   __shared__ uint64_t s_qm[4][4];
   __shared__ uint32_t s_max;
 
-  const int tile = blockIdx.x;
+  const int tile = tile_order ? (int)tile_order[blockIdx.x] : (int)blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int tx = tile % cam.tiles_x, ty = tile / cam.tiles_x;
   const float tx0 = (float)(tx * kTile), ty0 = (float)(ty * kTile);
@@ -655,7 +656,8 @@ bool proj_ok(const gs_projected* p) {
 }  // namespace
 
 extern "C" gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const gs_camera* cam,
-                                      const uint32_t* d_ids, const uint32_t* d_tile_ranges, float* d_image,
+                                      const uint32_t* d_ids, const uint32_t* d_tile_ranges,
+                                      const uint32_t* d_tile_order, float* d_image,
                                       float* d_final_T, uint32_t* d_n_contrib, uint64_t* d_eval_count,
                                       void* stream) {
   std::string why;
@@ -671,8 +673,8 @@ extern "C" gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const
   {
     TimedScope ts("blend", s);
     auto kern = d_eval_count ? k_blend<true> : k_blend<false>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges, d_ids,
-                       n > 0 ? proj->d_means2d : nullptr, n > 0 ? proj->d_conics : nullptr,
+    hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges,
+                       d_tile_order, d_ids, n > 0 ? proj->d_means2d : nullptr, n > 0 ? proj->d_conics : nullptr,
                        n > 0 ? proj->d_opacities : nullptr, n > 0 ? proj->d_colors : nullptr,
                        n > 0 ? proj->d_radii : nullptr, dc, d_image, d_final_T, d_n_contrib,
                        (unsigned long long*)d_eval_count);
@@ -686,7 +688,8 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float*
                                       const float* d_log_scales, const float* d_quats,
                                       const float* d_opacity_logits, const float* d_sh, const gs_camera* cam,
                                       const gs_projected* proj, const uint32_t* d_ids,
-                                      const uint32_t* d_tile_ranges, const float* d_final_T,
+                                      const uint32_t* d_tile_ranges, const uint32_t* d_tile_order,
+                                      const float* d_final_T,
                                       const uint32_t* d_n_contrib, const float* d_dL_dimage, void* d_workspace,
                                       size_t workspace_bytes, float* d_grad_means, float* d_grad_log_scales,
                                       float* d_grad_quats, float* d_grad_opacity_logits, float* d_grad_sh,
@@ -719,8 +722,8 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float*
   {
     TimedScope ts("rbwd", s);
     auto kern = d_eval_count ? k_rbwd<true> : k_rbwd<false>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges, d_ids,
-                       proj->d_means2d, proj->d_conics, proj->d_opacities, proj->d_colors, proj->d_radii, dc,
+    hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges,
+                       d_tile_order, d_ids, proj->d_means2d, proj->d_conics, proj->d_opacities, proj->d_colors, proj->d_radii, dc,
                        d_final_T, d_n_contrib, d_dL_dimage, g2d, (unsigned long long*)d_eval_count);
   }
   {

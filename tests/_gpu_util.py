@@ -71,10 +71,21 @@ def run_gpu_bin(gs, torch, params_n, proj, cam, capacity):
     ids = torch.empty(max(capacity, 1), device="cuda", dtype=torch.int32)
     tiles = ((cam.width + 15) // 16) * ((cam.height + 15) // 16)
     ranges = torch.empty(tiles, 2, device="cuda", dtype=torch.int32)
+    order = torch.full((tiles,), -1, device="cuda", dtype=torch.int32)
     ws = torch.empty(gs.gs_bin_workspace_bytes(params_n, capacity, cam), device="cuda", dtype=torch.uint8)
-    st, P = gs.gs_bin_and_sort(params_n, proj, cam, ws, capacity, keys, ids, ranges)
+    st, P = gs.gs_bin_and_sort(params_n, proj, cam, ws, capacity, keys, ids, ranges, tile_order=order)
     torch.cuda.synchronize()
-    return st, P, keys, ids, ranges
+    return st, P, keys, ids, ranges, order
+
+
+def assert_tile_order(order_np, ranges_np):
+    """The processing order is a permutation of the tiles by non-increasing bit length of the
+    pair count (empty tiles last)."""
+    n = ranges_np.shape[0]
+    assert np.array_equal(np.sort(order_np.astype(np.int64)), np.arange(n)), "tile order is not a permutation"
+    cnt = (ranges_np[:, 1].astype(np.int64) - ranges_np[:, 0])[order_np]
+    cls = np.where(cnt > 0, np.floor(np.log2(np.maximum(cnt, 1))).astype(np.int64) + 1, 0)
+    assert np.all(np.diff(cls) <= 0), "tile order is not heaviest class first"
 
 
 def pixel_last_ids(nc, ids_np, ranges_np, pixels, width):

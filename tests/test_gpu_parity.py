@@ -15,8 +15,8 @@ import pytest
 
 import oracle
 from gaussian_splatting_tile_gs_amd import synth
-from _gpu_util import (assert_projection_bit_exact, compare_forward, compare_grads, log, proj_from_numpy,
-                       proj_to_numpy, run_gpu_bin, run_gpu_project)
+from _gpu_util import (assert_projection_bit_exact, assert_tile_order, compare_forward, compare_grads, log,
+                       proj_from_numpy, proj_to_numpy, run_gpu_bin, run_gpu_project)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,7 +49,7 @@ def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7
     # binning end to end (GPU projection) and stage-isolated (the oracle's projection uploaded)
     o_keys, o_ids, o_ranges = oracle.bin_pairs(o_proj, cam_dict)
     P_exp = int(o_keys.size)
-    st, P, keys, ids, ranges = run_gpu_bin(gs, torch, params["n"], proj, cam, P_exp + 17)
+    st, P, keys, ids, ranges, order = run_gpu_bin(gs, torch, params["n"], proj, cam, P_exp + 17)
     assert st == gs.GS_OK and P == P_exp
     keys_np = keys.cpu().numpy()[:P].view(np.uint64)
     ids_np = ids.cpu().numpy()[:P].view(np.uint32)
@@ -57,8 +57,9 @@ def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7
     assert np.array_equal(keys_np, o_keys), "sorted keys differ"
     assert np.array_equal(ids_np, o_ids), "sorted ids differ"
     assert np.array_equal(ranges_np, o_ranges), "tile ranges differ"
+    assert_tile_order(order.cpu().numpy(), ranges_np)
     iso = proj_from_numpy(gs, torch, o_proj)
-    st2, P2, keys2, ids2, ranges2 = run_gpu_bin(gs, torch, params["n"], iso, cam, P_exp)
+    st2, P2, keys2, ids2, ranges2, _ = run_gpu_bin(gs, torch, params["n"], iso, cam, P_exp)
     assert st2 == gs.GS_OK and P2 == P_exp
     assert np.array_equal(keys2.cpu().numpy()[:P].view(np.uint64), o_keys)
     assert np.array_equal(ranges2.cpu().numpy().view(np.uint32), o_ranges)
@@ -70,7 +71,7 @@ def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7
     fT = torch.empty(H, W, device="cuda")
     nc = torch.empty(H, W, device="cuda", dtype=torch.int32)
     evals = torch.zeros(1, device="cuda", dtype=torch.int64)
-    gs.gs_rasterize_fwd(params["n"], proj, cam, ids, ranges, img, fT, nc, evals)
+    gs.gs_rasterize_fwd(params["n"], proj, cam, ids, ranges, img, fT, nc, evals, tile_order=order)
     torch.cuda.synchronize()
     pix = _full_pixels(cam_dict) if pixels is None else pixels
     o_fwd = oracle.render(o_proj, cam_dict, pixels=pix)
@@ -96,7 +97,8 @@ def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7
     gs.gs_rasterize_bwd(params["n"], params["sh_degree"], params["means"], params["log_scales"], params["quats"],
                         params["opacity_logits"], params["sh"], cam, proj, ids, ranges, fT, nc,
                         torch.from_numpy(dimg).cuda(), ws, pipe_grads["means"], pipe_grads["log_scales"],
-                        pipe_grads["quats"], pipe_grads["opacity_logits"], pipe_grads["sh"], g2d_out)
+                        pipe_grads["quats"], pipe_grads["opacity_logits"], pipe_grads["sh"], g2d_out,
+                        tile_order=order)
     torch.cuda.synchronize()
     g2d, aref2d = oracle.render_backward(o_proj, cam_dict, gsel, pixels=pix)
     raw = oracle.project_backward(scene, cam_dict, g2d, aref2d)
@@ -186,9 +188,11 @@ def test_capacity_overflow_contract(env):
             ids = torch.full((cap + 64,), -7, device="cuda", dtype=torch.int32)
             ranges = torch.full((tiles, 2), -7, device="cuda", dtype=torch.int32)
             pdev = torch.full((1,), -7, device="cuda", dtype=torch.int64)
+            order = torch.full((tiles,), -1, device="cuda", dtype=torch.int32)
             ws = torch.empty(gs.gs_bin_workspace_bytes(params["n"], cap, cam), device="cuda", dtype=torch.uint8)
             ws.fill_(0xAB)  # the workspace's contents on entry are arbitrary
-            st, P = gs.gs_bin_and_sort(params["n"], proj, cam, ws, cap, keys, ids, ranges, pdev, wait=wait)
+            st, P = gs.gs_bin_and_sort(params["n"], proj, cam, ws, cap, keys, ids, ranges, pdev, wait=wait,
+                                       tile_order=order)
             torch.cuda.synchronize()
             if wait:
                 assert st == gs.GS_ERR_CAPACITY and P == need
@@ -196,6 +200,7 @@ def test_capacity_overflow_contract(env):
                 assert st == gs.GS_OK and P is None
             assert int(pdev.item()) == need
             assert torch.all(ranges == 0)
+            assert np.array_equal(np.sort(order.cpu().numpy()), np.arange(tiles))
             assert torch.all(keys[cap:] == -7) and torch.all(ids[cap:] == -7)
 
 
@@ -271,7 +276,8 @@ def test_forward_and_sort_deterministic(env):
     cam = gs.make_camera(synth.make_cameras(wl)[5])
     pipe = gs.Pipeline(params, wl.width, wl.height, pair_capacity=1 << 18)
     outs = []
-    for _ in range(2):
+    for use_order in (True, False):  # the tile order changes scheduling only
+        pipe.use_order = use_order
         pipe.project(cam)
         pipe.bin(cam)
         pipe.forward(cam)
