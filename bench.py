@@ -67,9 +67,9 @@ def kernel_bytes(name, stats):
     }.get(name)
 
 
-def traffic_for(kernel):
+def traffic_for(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
-    current source of that kernel; else None."""
+    current source of that kernel and on this workload; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -77,7 +77,7 @@ def traffic_for(kernel):
         rec = json.load(open(path)).get(kernel)
     except ValueError:
         return None
-    if not rec:
+    if not rec or rec.get("workload") != workload:
         return None
     src = os.path.join(ROOT, "gaussian_splatting_tile_gs_amd", "csrc", rec["source"])
     if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["sha256"]:
@@ -265,13 +265,13 @@ def main():
             ops = evals * VALU_PER_EVAL[dom]
             achieved = ops / avg_s / 1e12
             roof = {"bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TOPS, "unit": "TOP/s",
-                    "frac": achieved / VALU_PEAK_TOPS, "traffic": traffic_for(dom), "kernel": dom,
+                    "frac": achieved / VALU_PEAK_TOPS, "traffic": traffic_for(dom, wl.name), "kernel": dom,
                     "evals_per_launch": evals, "valu_per_eval": VALU_PER_EVAL[dom], "avg_us": avg_s * 1e6}
         else:
             b = kernel_bytes(dom, stats) or 0.0
             achieved = b / avg_s / 1e9
             roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(dom), "kernel": dom,
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(dom, wl.name), "kernel": dom,
                     "bytes_per_launch": b, "avg_us": avg_s * 1e6}
         result["roofline"] = roof
         bin_names = ("bin_prep", "hist_reduce", "depth_sort_pass", "scan", "emit", "pair_sort_pass")
