@@ -163,7 +163,7 @@ def main():
     for i, cam in enumerate(cams):
         tpipe.project(cam)
         tpipe.bin(cam)
-        tpipe.forward(cam)
+        tpipe.forward(cam, checkpoints=False)
         targets[i].copy_(tpipe.image)
     del tpipe, tparams
     torch.cuda.synchronize()
@@ -186,7 +186,7 @@ def main():
         else:
             pipe.project(cams[c])
             pipe.bin(cams[c], wait=False)
-            pipe.forward(cams[c])
+            pipe.forward(cams[c], checkpoints=False)  # a render: no backward follows
 
     if args.copy_calibration_mib:
         src = torch.ones(args.copy_calibration_mib << 18, device="cuda")
@@ -238,7 +238,7 @@ def main():
             c = (args.warmup + i) % ncam
             pipe.project(cams[c])
             pipe.bin(cams[c], wait=False)
-            pipe.forward(cams[c], eval_count=evals_f)
+            pipe.forward(cams[c], eval_count=evals_f, checkpoints=None if wl.backward else False)
             if wl.backward:
                 pipe.loss_l1(targets[c])
                 pipe.backward(cams[c], eval_count=evals_b)

@@ -261,7 +261,7 @@ struct TileCountArgs {
   uint32_t ntiles;
   uint32_t* tdiff;      // ntiles + 1 words, zeroed by k_bin_prep
   uint32_t* ranges;     // [ntiles, 2], zeroed by k_bin_prep
-  uint32_t* order;      // [ntiles] processing order of the tiles (optional)
+  uint32_t* plan;       // raster plan (optional; layout in gs_internal.h)
   uint64_t capacity;
   int npass;
   uint32_t* hist_pair;  // [npass][256]
@@ -316,10 +316,11 @@ __device__ void tile_rows(const TileCountArgs& a, uint32_t rb, uint32_t* lds, ui
 }
 
 // One workgroup: per-tile counts = prefix sums of the difference array, in chunks of 8192 tiles
-// staged in `lds`. A first sweep finds P and how many tiles fall in each count class
-// (bit length of the count); a second writes the ranges and histograms (when P fits) and the
-// processing order: tiles by count class, the heaviest class first, empty tiles last, so that
-// the long raster workgroups start first.
+// staged in `lds`. A first sweep finds P and how many tiles fall in each count class (bit
+// length of the count). A second writes the ranges and histograms (when P fits) and the raster
+// plan: the processing order (the heaviest class first, empty tiles last, so that the long
+// raster workgroups start first), the chunk length L (the smallest power of two >= 256 with
+// P <= kPlanMaxChunks L), and per tile its checkpoint slot base and (tile, chunk) work items.
 __device__ __forceinline__ uint32_t count_class(uint32_t c) { return c ? 32u - (uint32_t)__clz(c) : 0u; }
 
 __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t* s_wsum, uint32_t (*s_hist)[kRadix]) {
@@ -332,9 +333,10 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t* s
   if (tid < 64) s_cls[tid] = 0;
   __syncthreads();
   uint64_t P = 0;
+  uint32_t L = kPlanMinChunk;
   for (int sweep = 0; sweep < 2; ++sweep) {
     const bool write = sweep == 1 && P <= a.capacity;
-    if (sweep == 1 && !write && !a.order) break;
+    if (sweep == 1 && !write && !a.plan) break;
     uint32_t carry_d = 0, carry_c = 0;
     for (uint32_t cb = 0; cb < a.ntiles; cb += kChunk) {
       uint32_t v[8];
@@ -363,22 +365,42 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t* s
       }
       uint32_t ctot;
       uint32_t start = carry_c + block_excl_scan1024<uint32_t>(csum, s_wsum, &ctot);
+      if (sweep == 0) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const uint32_t t = cb + (uint32_t)(tid * 8 + q);
-        if (t < a.ntiles) {
-          if (sweep == 0) {
-            atomicAdd(&s_cls[count_class(cnt[q])], 1u);
-          } else {
-            if (write && cnt[q]) {
-              a.ranges[2 * t] = start;
-              a.ranges[2 * t + 1] = start + cnt[q];
-              for (int k = 0; k < a.npass; ++k) atomicAdd(&s_hist[k][(t >> (8 * k)) & 255u], cnt[q]);
+        for (int q = 0; q < 8; ++q)
+          if (cb + (uint32_t)(tid * 8 + q) < a.ntiles) atomicAdd(&s_cls[count_class(cnt[q])], 1u);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t t = cb + (uint32_t)(tid * 8 + q);
+          if (t < a.ntiles && write && cnt[q]) {
+            a.ranges[2 * t] = start;
+            a.ranges[2 * t + 1] = start + cnt[q];
+            for (int k = 0; k < a.npass; ++k) atomicAdd(&s_hist[k][(t >> (8 * k)) & 255u], cnt[q]);
+          }
+          start += cnt[q];
+          if (a.plan) {
+            // order slot: lanes with the same count class share one LDS atomic
+            const bool valid = t < a.ntiles;
+            const uint32_t cls = count_class(write ? cnt[q] : 0u);
+            uint64_t m = __ballot(valid);
+#pragma unroll
+            for (int b = 0; b < 6; ++b) {
+              const bool bit = (cls >> b) & 1u;
+              const uint64_t bb = __ballot(bit);
+              m &= bit ? bb : ~bb;
             }
-            if (a.order) a.order[atomicAdd(&s_cur[count_class(cnt[q])], 1u)] = t;
+            const int lane = tid & 63;
+            const int leader = __builtin_ctzll(m | (1ull << 63));
+            uint32_t base = 0;
+            if (valid && lane == leader) base = atomicAdd(&s_cur[cls], (uint32_t)__popcll(m));
+            base = __shfl(base, leader, 64);
+            if (valid) {
+              const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+              a.plan[kPlanOrder + base + (uint32_t)__popcll(m & lt)] = t;
+            }
           }
         }
-        start += cnt[q];
       }
       carry_d += dtot;
       carry_c += ctot;
@@ -386,11 +408,13 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t* s
     }
     if (sweep == 0) {
       P = carry_c;
+      while ((uint64_t)L * kPlanMaxChunks < P) L <<= 1;
       if (tid == 0) {
+        // on overflow every tile is empty for the raster calls: all in class 0
         uint32_t slot = 0;
         for (int c = 32; c >= 0; --c) {
           s_cur[c] = slot;
-          slot += s_cls[c];
+          slot += P <= a.capacity ? s_cls[c] : (c == 0 ? a.ntiles : 0u);
         }
       }
       __syncthreads();
@@ -399,6 +423,46 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t* s
   __syncthreads();
   if (tid < kRadix && P <= a.capacity)
     for (int k = 0; k < a.npass; ++k) a.hist_pair[k * kRadix + tid] = s_hist[k][tid];
+  if (!a.plan) return;
+  // work items and checkpoint slots, in processing order (the order and ranges written above by
+  // this workgroup are visible to it after the barrier)
+  const bool fits = P <= a.capacity;
+  uint32_t carry_i = 0, carry_k = 0;
+  for (uint32_t ob = 0; ob < a.ntiles; ob += kChunk) {
+    uint32_t t[8], nch[8], isum = 0, ksum = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t i = ob + (uint32_t)(tid * 8 + q);
+      t[q] = i < a.ntiles ? a.plan[kPlanOrder + i] : 0u;
+      const uint32_t c = (i < a.ntiles && fits) ? a.ranges[2 * t[q] + 1] - a.ranges[2 * t[q]] : 0u;
+      nch[q] = (c + L - 1) / L;
+      isum += nch[q];
+      ksum += nch[q] >= 2 ? nch[q] : 0u;
+    }
+    uint32_t itot, ktot;
+    uint32_t ibase = carry_i + block_excl_scan1024<uint32_t>(isum, s_wsum, &itot);
+    uint32_t kbase = carry_k + block_excl_scan1024<uint32_t>(ksum, s_wsum, &ktot);
+    uint32_t* it = a.plan + kPlanOrder + 2 * a.ntiles;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (ob + (uint32_t)(tid * 8 + q) < a.ntiles) {
+        a.plan[kPlanOrder + a.ntiles + t[q]] = kbase;
+        for (uint32_t c = 0; c < nch[q]; ++c) {
+          it[2 * (ibase + c)] = t[q];
+          it[2 * (ibase + c) + 1] = c;
+        }
+      }
+      ibase += nch[q];
+      kbase += nch[q] >= 2 ? nch[q] : 0u;
+    }
+    carry_i += itot;
+    carry_k += ktot;
+  }
+  if (tid == 0) {
+    a.plan[kPlanChunk] = L;
+    a.plan[kPlanItems] = carry_i;
+    a.plan[kPlanCheckpoints] = carry_k;
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -724,8 +788,18 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit(const uint64_t* __restric
   }
 }
 
-__global__ void k_iota_u32(uint32_t* __restrict__ p, uint32_t count) {
-  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < count; i += gridDim.x * blockDim.x) p[i] = i;
+// The raster plan of a frame without pairs: natural tile order, no work items or checkpoints.
+__global__ void k_empty_plan(uint32_t* __restrict__ plan, uint32_t ntiles) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0) {
+    plan[kPlanChunk] = kPlanMinChunk;
+    plan[kPlanItems] = 0;
+    plan[kPlanCheckpoints] = 0;
+  }
+  if (i < ntiles) {
+    plan[kPlanOrder + i] = i;
+    plan[kPlanOrder + ntiles + i] = 0;
+  }
 }
 
 __global__ void k_fill_u32(uint32_t* __restrict__ p, size_t count, uint32_t v) {
@@ -787,6 +861,12 @@ BinLayout bin_layout(int32_t n, int64_t cap, const gs_camera* cam) {
 
 using namespace gs;
 
+extern "C" size_t gs_raster_plan_words(const gs_camera* cam) {
+  if (!cam || cam->width <= 0 || cam->height <= 0) return 0;
+  const size_t ntiles = (size_t)((cam->width + 15) / 16) * ((cam->height + 15) / 16);
+  return plan_words(ntiles);
+}
+
 extern "C" size_t gs_bin_workspace_bytes(int32_t n, int64_t pair_capacity, const gs_camera* cam) {
   if (n < 0 || pair_capacity < 0 || !cam || cam->width <= 0 || cam->height <= 0) return 0;
   return bin_layout(n, pair_capacity, cam).total;
@@ -794,7 +874,7 @@ extern "C" size_t gs_bin_workspace_bytes(int32_t n, int64_t pair_capacity, const
 
 extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const gs_camera* cam, void* d_workspace,
                                      size_t workspace_bytes, int64_t pair_capacity, uint64_t* d_keys,
-                                     uint32_t* d_ids, uint32_t* d_tile_ranges, uint32_t* d_tile_order,
+                                     uint32_t* d_ids, uint32_t* d_tile_ranges, uint32_t* d_raster_plan,
                                      int64_t* d_num_pairs, int64_t* h_num_pairs, void* stream) {
   std::string why;
   if (n < 0) return set_error(GS_ERR_INVALID_ARG, "gs_bin_and_sort: n < 0");
@@ -822,8 +902,8 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
     hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((2 * ntiles + 255) / 256)), dim3(256), 0, s, d_tile_ranges,
                        (size_t)(2 * ntiles), 0u);
     if (d_num_pairs) hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, s, (uint32_t*)d_num_pairs, (size_t)2, 0u);
-    if (d_tile_order)
-      hipLaunchKernelGGL(k_iota_u32, dim3((unsigned)((ntiles + 255) / 256)), dim3(256), 0, s, d_tile_order,
+    if (d_raster_plan)
+      hipLaunchKernelGGL(k_empty_plan, dim3((unsigned)((ntiles + 255) / 256)), dim3(256), 0, s, d_raster_plan,
                          (uint32_t)ntiles);
     return check_launch("gs_bin_and_sort");
   }
@@ -861,7 +941,7 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
   targs.ntiles = (uint32_t)ntiles;
   targs.tdiff = (uint32_t*)(ws + L.tdiff);
   targs.ranges = d_tile_ranges;
-  targs.order = d_tile_order;
+  targs.plan = d_raster_plan;
   targs.capacity = (uint64_t)pair_capacity;
   targs.npass = L.npass;
   targs.hist_pair = &ctrl->hist_pair[0][0];

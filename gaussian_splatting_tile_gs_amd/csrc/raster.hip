@@ -32,6 +32,7 @@ namespace {
 constexpr int kTile = 16;
 constexpr int kRasterThreads = kTile * kTile;  // 256: one pixel per thread
 constexpr int kBatch = kRasterThreads;         // splats staged per batch
+static_assert(kPlanMinChunk % kBatch == 0, "chunk boundaries must fall on batch starts");
 
 // Staged splat record: (mx, my, hA, hC), (B2, o, r, g), b. hA = A/2 log2e, B2 = B log2e,
 // hC = C/2 log2e, so that log2(e) sigma = hA dx^2 + hC dy^2 + B2 dx dy. Also returns the 4-bit
@@ -147,11 +148,15 @@ __device__ __forceinline__ void blend_step(const SplatEval& e, bool act, float c
 // ---------------------------------------------------------------------------------------------
 // k-blend: one 256-thread workgroup per 16x16 tile; wave q owns the 8x8 quadrant q and walks its
 // splats two per iteration (their alphas are independent; the T updates are sequential).
+// With a raster plan, workgroup b takes tile order[b]; with a checkpoint buffer too, a tile
+// longer than the plan's chunk length L accumulates its colour per chunk of L list entries and
+// stores, for every chunk j, each pixel's transmittance after the chunk and the colour the chunk
+// added (slot j). The backward then splits the tile into chunks that run in parallel.
 // ---------------------------------------------------------------------------------------------
-template <bool COUNT>
+template <bool COUNT, bool CKPT>
 __global__ __launch_bounds__(kRasterThreads) void k_blend(
-    uint32_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ tile_order,
-    const uint32_t* __restrict__ ids, const float* __restrict__ means2d,
+    uint32_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ plan, uint32_t ntiles,
+    float4* __restrict__ ckpt, const uint32_t* __restrict__ ids, const float* __restrict__ means2d,
     const float* __restrict__ conics, const float* __restrict__ opac, const float* __restrict__ colors,
     const int32_t* __restrict__ radii, DevCamera cam, float* __restrict__ image, float* __restrict__ final_T,
     uint32_t* __restrict__ n_contrib, unsigned long long* __restrict__ eval_count) {
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
   __shared__ float s_c[kBatch];
   __shared__ uint64_t s_qm[4][4];
 
-  const int tile = tile_order ? (int)tile_order[blockIdx.x] : (int)blockIdx.x;
+  const int tile = plan ? (int)plan[kPlanOrder + blockIdx.x] : (int)blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int tx = tile % cam.tiles_x, ty = tile / cam.tiles_x;
   const float tx0 = (float)(tx * kTile), ty0 = (float)(ty * kTile);
@@ -170,17 +175,35 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
   const float px = (float)px_i + 0.5f, py = (float)py_i + 0.5f;
   const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
 
-  float T = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f;
+  // (cr, cg, cb): the colour added so far; with checkpoints, by the current chunk only, and
+  // (pr, pg, pb) by the chunks before it
+  float T = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f, pr = 0.0f, pg = 0.0f, pb = 0.0f;
   uint32_t last = 0, n_eval = 0;
   bool done = !inside;
+  // chunk boundaries are multiples of L >= kBatch, so they fall on batch starts
+  const uint32_t len = end - start;
+  const uint32_t L = CKPT ? plan[kPlanChunk] : 0u;
+  uint32_t next_b = (CKPT && len > L) ? L : 0xFFFFFFFFu;
+  float4* ck = (CKPT && len > L) ? ckpt + (size_t)plan[kPlanOrder + ntiles + tile] * kRasterThreads + tid : nullptr;
+  auto store_ckpt = [&]() {
+    *ck = make_float4(T, cr, cg, cb);
+    ck += kRasterThreads;
+    pr += cr;
+    pg += cg;
+    pb += cb;
+    cr = cg = cb = 0.0f;
+    next_b += L;
+    if (next_b >= len) next_b = 0xFFFFFFFFu;
+  };
   for (uint32_t bs = start; bs < end; bs += kBatch) {
     if (__syncthreads_count(done) == kRasterThreads) break;
+    if (CKPT && bs - start >= next_b) store_ckpt();  // workgroup-uniform
     const uint32_t j = bs + tid;
     uint32_t qm = 0;
     if (j < end) qm = load_record(ids[j], n, means2d, conics, opac, colors, radii, tx0, ty0, s_a[tid], s_b[tid], s_c[tid]);
     publish_quadrant_masks(qm, j < end, s_qm);
     __syncthreads();
-    const uint32_t base_idx = bs - start + 1u;
+    const uint32_t list1 = bs - start + 1u;  // 1-based list index of staged splat 0
     for (int w = 0; w < 4; ++w) {
       uint64_t m = uniform64(s_qm[wave][w]);
       while (m) {
@@ -189,7 +212,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
         m &= m - 1;
         const bool has1 = m != 0;
         const int bit1 = has1 ? __builtin_ctzll(m) : bit0;
-        m &= m - 1;  // no-op when !has1 (m is already 0)
+        if (has1) m &= m - 1;
         const int k0 = w * 64 + bit0, k1 = w * 64 + bit1;
         const float4 a0 = s_a[k0], b0 = s_b[k0];
         const float4 a1 = s_a[k1], b1 = s_b[k1];
@@ -197,10 +220,17 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
         const SplatEval e0 = eval_splat(a0.x - px, a0.y - py, a0.z, b0.x, a0.w, b0.y);
         const SplatEval e1 = eval_splat(a1.x - px, a1.y - py, a1.z, b1.x, a1.w, b1.y);
         if (COUNT) n_eval += (done ? 0u : 1u) + ((done || !has1) ? 0u : 1u);
-        blend_step(e0, true, b0.z, b0.w, c0, base_idx + (uint32_t)k0, T, cr, cg, cb, last, done);
-        blend_step(e1, has1, b1.z, b1.w, c1, base_idx + (uint32_t)k1, T, cr, cg, cb, last, done);
+        blend_step(e0, true, b0.z, b0.w, c0, list1 + (uint32_t)k0, T, cr, cg, cb, last, done);
+        blend_step(e1, has1, b1.z, b1.w, c1, list1 + (uint32_t)k1, T, cr, cg, cb, last, done);
       }
     }
+  }
+  if (CKPT) {
+    while (next_b != 0xFFFFFFFFu) store_ckpt();  // boundaries past the last walked batch
+    if (ck) *ck = make_float4(T, cr, cg, cb);    // the last chunk's slot
+    cr += pr;
+    cg += pg;
+    cb += pb;
   }
   if (inside) {
     const int p = py_i * cam.W + px_i;
@@ -288,15 +318,19 @@ __device__ __forceinline__ void splat_grad(bool contrib, const SplatEval& ev, fl
 // k-rbwd: same tiling; each wave walks its quadrant's splats back to front from the last
 // contributor of its pixels, recovering T_i = T_{i+1} / (1 - alpha_i), two splats per
 // iteration (their alphas are independent; only the T / g.S updates are sequential).
+// With a raster plan and the forward's checkpoints, workgroup b takes work item b: one chunk
+// [c L, (c + 1) L) of a tile's list. An inner chunk starts from the transmittance stored after
+// it and from S = T_final background + the colour that every later chunk added (summed back to
+// front, like the sums of the whole-tile walk: a sum of the terms, never a difference).
 // ---------------------------------------------------------------------------------------------
 template <bool COUNT>
 __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
-    uint32_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ tile_order,
-    const uint32_t* __restrict__ ids, const float* __restrict__ means2d,
-    const float* __restrict__ conics, const float* __restrict__ opac, const float* __restrict__ colors,
-    const int32_t* __restrict__ radii, DevCamera cam, const float* __restrict__ final_T,
-    const uint32_t* __restrict__ n_contrib, const float* __restrict__ dL_dimage, float* __restrict__ g2d,
-    unsigned long long* __restrict__ eval_count) {
+    uint32_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ plan, uint32_t ntiles,
+    const float4* __restrict__ ckpt, const uint32_t* __restrict__ ids,
+    const float* __restrict__ means2d, const float* __restrict__ conics, const float* __restrict__ opac,
+    const float* __restrict__ colors, const int32_t* __restrict__ radii, DevCamera cam,
+    const float* __restrict__ final_T, const uint32_t* __restrict__ n_contrib, const float* __restrict__ dL_dimage,
+    float* __restrict__ g2d, unsigned long long* __restrict__ eval_count) {
   __shared__ float4 s_a[kBatch];
   __shared__ float4 s_b[kBatch];
   __shared__ float s_c[kBatch];
@@ -305,7 +339,28 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
   __shared__ uint64_t s_qm[4][4];
   __shared__ uint32_t s_max;
 
-  const int tile = tile_order ? (int)tile_order[blockIdx.x] : (int)blockIdx.x;
+  // the work: a whole tile (no checkpoints) or one chunk of a tile's list
+  int tile;
+  uint32_t lo = 0, hi = 0xFFFFFFFFu, chunk = 0, nch = 0;
+  bool from_ckpt = false;
+  size_t slot0 = 0;
+  if (plan && ckpt) {
+    if (blockIdx.x >= plan[kPlanItems]) return;  // workgroup-uniform
+    const uint32_t* item = plan + kPlanOrder + 2 * ntiles + 2 * blockIdx.x;
+    tile = (int)item[0];
+    chunk = item[1];
+    const uint32_t L = plan[kPlanChunk];
+    const uint32_t len = ranges[2 * tile + 1] - ranges[2 * tile];
+    nch = (len + L - 1) / L;
+    lo = chunk * L;
+    hi = lo + L;
+    if (hi < len) {
+      from_ckpt = true;
+      slot0 = (size_t)plan[kPlanOrder + ntiles + tile] * kRasterThreads;
+    }
+  } else {
+    tile = plan ? (int)plan[kPlanOrder + blockIdx.x] : (int)blockIdx.x;
+  }
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int tx = tile % cam.tiles_x, ty = tile / cam.tiles_x;
   const float tx0 = (float)(tx * kTile), ty0 = (float)(ty * kTile);
@@ -315,28 +370,42 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
   const float px = (float)px_i + 0.5f, py = (float)py_i + 0.5f;
   const uint32_t start = ranges[2 * tile];
 
-  float T = 1.0f, gr = 0.0f, gg = 0.0f, gb = 0.0f;
+  float T = 1.0f, gr = 0.0f, gg = 0.0f, gb = 0.0f, gS = 0.0f;
   uint32_t nc = 0;
   if (inside) {
     const int p = py_i * cam.W + px_i;
-    T = final_T[p];
     nc = n_contrib[p];
     gr = dL_dimage[3 * p];
     gg = dL_dimage[3 * p + 1];
     gb = dL_dimage[3 * p + 2];
+    if (from_ckpt) {
+      // S after the chunk = T_final background + the colour of chunks nch - 1 .. chunk + 1
+      const float Tf = final_T[p];
+      float sr = Tf * cam.bg[0], sg = Tf * cam.bg[1], sb = Tf * cam.bg[2];
+      for (uint32_t k = nch - 1; k > chunk; --k) {
+        const float4 st = ckpt[slot0 + (size_t)k * kRasterThreads + tid];
+        sr += st.y;
+        sg += st.z;
+        sb += st.w;
+      }
+      T = ckpt[slot0 + (size_t)chunk * kRasterThreads + tid].x;
+      gS = (gr * sr + gg * sg) + gb * sb;
+    } else {
+      // g . S with S = T_final background
+      T = final_T[p];
+      gS = T * ((gr * cam.bg[0] + gg * cam.bg[1]) + gb * cam.bg[2]);
+    }
   }
-  // g . S with S = (what lies behind, composited) + T_final bg, carried as one scalar
-  float gS = T * ((gr * cam.bg[0] + gg * cam.bg[1]) + gb * cam.bg[2]);
   if (tid == 0) s_max = 0;
   __syncthreads();
   const uint32_t wmax = wave_max_lane63(nc);
   if (lane == 63 && wmax) atomicMax(&s_max, wmax);
   __syncthreads();
-  const uint32_t max_nc = s_max;
+  const uint32_t max_nc = s_max < hi ? s_max : hi;
   uint32_t n_eval = 0;
 
-  for (uint32_t bend = max_nc; bend > 0;) {
-    const uint32_t bstart = bend > (uint32_t)kBatch ? bend - kBatch : 0u;
+  for (uint32_t bend = max_nc; bend > lo;) {
+    const uint32_t bstart = bend > lo + (uint32_t)kBatch ? bend - kBatch : lo;
     const int cnt = (int)(bend - bstart);
     __syncthreads();
     uint32_t qm = 0;
@@ -655,9 +724,13 @@ bool proj_ok(const gs_projected* p) {
 }
 }  // namespace
 
+extern "C" size_t gs_raster_workspace_bytes(void) {
+  return (size_t)kPlanMaxSlots * kRasterThreads * sizeof(float4);
+}
+
 extern "C" gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const gs_camera* cam,
                                       const uint32_t* d_ids, const uint32_t* d_tile_ranges,
-                                      const uint32_t* d_tile_order, float* d_image,
+                                      const uint32_t* d_raster_plan, void* d_raster_ws, float* d_image,
                                       float* d_final_T, uint32_t* d_n_contrib, uint64_t* d_eval_count,
                                       void* stream) {
   std::string why;
@@ -672,9 +745,12 @@ extern "C" gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const
   hipStream_t s = (hipStream_t)stream;
   {
     TimedScope ts("blend", s);
-    auto kern = d_eval_count ? k_blend<true> : k_blend<false>;
+    const bool ck = d_raster_plan && d_raster_ws;
+    auto kern = d_eval_count ? (ck ? k_blend<true, true> : k_blend<true, false>)
+                             : (ck ? k_blend<false, true> : k_blend<false, false>);
     hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges,
-                       d_tile_order, d_ids, n > 0 ? proj->d_means2d : nullptr, n > 0 ? proj->d_conics : nullptr,
+                       d_raster_plan, (uint32_t)ntiles, d_raster_plan ? (float4*)d_raster_ws : nullptr, d_ids,
+                       n > 0 ? proj->d_means2d : nullptr, n > 0 ? proj->d_conics : nullptr,
                        n > 0 ? proj->d_opacities : nullptr, n > 0 ? proj->d_colors : nullptr,
                        n > 0 ? proj->d_radii : nullptr, dc, d_image, d_final_T, d_n_contrib,
                        (unsigned long long*)d_eval_count);
@@ -688,8 +764,8 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float*
                                       const float* d_log_scales, const float* d_quats,
                                       const float* d_opacity_logits, const float* d_sh, const gs_camera* cam,
                                       const gs_projected* proj, const uint32_t* d_ids,
-                                      const uint32_t* d_tile_ranges, const uint32_t* d_tile_order,
-                                      const float* d_final_T,
+                                      const uint32_t* d_tile_ranges, const uint32_t* d_raster_plan,
+                                      const void* d_raster_ws, const float* d_final_T,
                                       const uint32_t* d_n_contrib, const float* d_dL_dimage, void* d_workspace,
                                       size_t workspace_bytes, float* d_grad_means, float* d_grad_log_scales,
                                       float* d_grad_quats, float* d_grad_opacity_logits, float* d_grad_sh,
@@ -722,8 +798,12 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float*
   {
     TimedScope ts("rbwd", s);
     auto kern = d_eval_count ? k_rbwd<true> : k_rbwd<false>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges,
-                       d_tile_order, d_ids, proj->d_means2d, proj->d_conics, proj->d_opacities, proj->d_colors, proj->d_radii, dc,
+    // with checkpoints: one workgroup per work item of the plan (at most tiles + checkpoints)
+    const bool chunked = d_raster_plan && d_raster_ws;
+    const unsigned grid = (unsigned)(chunked ? ntiles + kPlanMaxChunks : ntiles);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges, d_raster_plan,
+                       (uint32_t)ntiles, chunked ? (const float4*)d_raster_ws : nullptr, d_ids,
+                       proj->d_means2d, proj->d_conics, proj->d_opacities, proj->d_colors, proj->d_radii, dc,
                        d_final_T, d_n_contrib, d_dL_dimage, g2d, (unsigned long long*)d_eval_count);
   }
   {

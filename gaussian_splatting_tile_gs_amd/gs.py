@@ -57,11 +57,13 @@ def load():
     sig = {
         "gs_project": (i32, [i32, i32, P, P, P, P, P, cam_p, proj_p, P]),
         "gs_bin_workspace_bytes": (sz, [i32, i64, cam_p]),
+        "gs_raster_plan_words": (sz, [cam_p]),
+        "gs_raster_workspace_bytes": (sz, []),
         "gs_bin_and_sort": (i32, [i32, proj_p, cam_p, P, sz, i64, P, P, P, P, P, ctypes.POINTER(ctypes.c_int64), P]),
-        "gs_rasterize_fwd": (i32, [i32, proj_p, cam_p, P, P, P, P, P, P, P, P]),
+        "gs_rasterize_fwd": (i32, [i32, proj_p, cam_p, P, P, P, P, P, P, P, P, P]),
         "gs_bwd_workspace_bytes": (sz, [i32]),
-        "gs_rasterize_bwd": (i32, [i32, i32, P, P, P, P, P, cam_p, proj_p, P, P, P, P, P, P, P, sz, P, P, P, P, P, P, P,
-                                   P]),
+        "gs_rasterize_bwd": (i32, [i32, i32, P, P, P, P, P, cam_p, proj_p, P, P, P, P, P, P, P, P, sz, P, P, P, P, P,
+                                   P, P, P]),
         "gs_loss_l1": (i32, [i32, i32, P, P, P, P, P]),
         "gs_status_string": (ctypes.c_char_p, [i32]),
         "gs_last_error": (ctypes.c_char_p, []),
@@ -128,25 +130,33 @@ def gs_bin_workspace_bytes(n, pair_capacity, cam: GsCamera) -> int:
     return int(load().gs_bin_workspace_bytes(n, pair_capacity, ctypes.byref(cam)))
 
 
+def gs_raster_plan_words(cam: GsCamera) -> int:
+    return int(load().gs_raster_plan_words(ctypes.byref(cam)))
+
+
+def gs_raster_workspace_bytes() -> int:
+    return int(load().gs_raster_workspace_bytes())
+
+
 def gs_bin_and_sort(n, proj: "Projected", cam: GsCamera, workspace, pair_capacity, keys, ids, tile_ranges,
-                    num_pairs_dev=None, stream=None, wait=True, tile_order=None):
+                    num_pairs_dev=None, stream=None, wait=True, plan=None):
     """With wait=True returns (status, P): status is GS_OK or GS_ERR_CAPACITY (P = the count
     needed). With wait=False nothing waits and it returns (GS_OK, None); P goes to num_pairs_dev
     (a one-element int64 CUDA tensor) when given."""
     P = ctypes.c_int64(0)
     st = _check(load().gs_bin_and_sort(n, ctypes.byref(proj.struct()), ctypes.byref(cam), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), pair_capacity, _ptr(keys),
-                                       _ptr(ids), _ptr(tile_ranges), _ptr(tile_order), _ptr(num_pairs_dev),
+                                       _ptr(ids), _ptr(tile_ranges), _ptr(plan), _ptr(num_pairs_dev),
                                        ctypes.byref(P) if wait else None, _stream(stream)),
                 allow=(GS_ERR_CAPACITY,))
     return st, (int(P.value) if wait else None)
 
 
 def gs_rasterize_fwd(n, proj: "Projected", cam: GsCamera, ids, tile_ranges, image, final_T, n_contrib,
-                     eval_count=None, stream=None, tile_order=None):
+                     eval_count=None, stream=None, plan=None, raster_ws=None):
     return _check(load().gs_rasterize_fwd(n, ctypes.byref(proj.struct()), ctypes.byref(cam), _ptr(ids),
-                                          _ptr(tile_ranges), _ptr(tile_order), _ptr(image), _ptr(final_T),
-                                          _ptr(n_contrib), _ptr(eval_count), _stream(stream)))
+                                          _ptr(tile_ranges), _ptr(plan), _ptr(raster_ws), _ptr(image),
+                                          _ptr(final_T), _ptr(n_contrib), _ptr(eval_count), _stream(stream)))
 
 
 def gs_bwd_workspace_bytes(n) -> int:
@@ -156,11 +166,11 @@ def gs_bwd_workspace_bytes(n) -> int:
 def gs_rasterize_bwd(n, sh_degree, means, log_scales, quats, opacity_logits, sh, cam: GsCamera, proj: "Projected",
                      ids, tile_ranges, final_T, n_contrib, dL_dimage, workspace, grad_means, grad_log_scales,
                      grad_quats, grad_opacity_logits, grad_sh, grad_means2d=None, eval_count=None, stream=None,
-                     tile_order=None):
+                     plan=None, raster_ws=None):
     return _check(load().gs_rasterize_bwd(
         n, sh_degree, _ptr(means), _ptr(log_scales), _ptr(quats), _ptr(opacity_logits), _ptr(sh), ctypes.byref(cam),
-        ctypes.byref(proj.struct()), _ptr(ids), _ptr(tile_ranges), _ptr(tile_order), _ptr(final_T), _ptr(n_contrib),
-        _ptr(dL_dimage),
+        ctypes.byref(proj.struct()), _ptr(ids), _ptr(tile_ranges), _ptr(plan), _ptr(raster_ws), _ptr(final_T),
+        _ptr(n_contrib), _ptr(dL_dimage),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(grad_means), _ptr(grad_log_scales),
         _ptr(grad_quats), _ptr(grad_opacity_logits), _ptr(grad_sh), _ptr(grad_means2d), _ptr(eval_count),
         _stream(stream)))
@@ -233,7 +243,10 @@ class Pipeline:
         self.n_contrib = torch.empty(height, width, device=device, dtype=torch.int32)
         self.dL_dimage = torch.zeros(height, width, 3, device=device)
         self.ranges = torch.empty(self.tiles, 2, device=device, dtype=torch.int32)
-        self.order = torch.empty(self.tiles, device=device, dtype=torch.int32)
+        cam0 = GsCamera()
+        cam0.width, cam0.height = width, height
+        self.plan = torch.empty(gs_raster_plan_words(cam0), device=device, dtype=torch.int32)
+        self.raster_ws = torch.empty(gs_raster_workspace_bytes(), device=device, dtype=torch.uint8)
         self.bwd_ws = torch.empty(gs_bwd_workspace_bytes(self.n), device=device, dtype=torch.uint8)
         K = (params["sh_degree"] + 1) ** 2
         f = dict(device=device, dtype=torch.float32)
@@ -242,7 +255,7 @@ class Pipeline:
                       "sh": torch.empty(self.n, K, 3, **f), "means2d": torch.empty(self.n, 2, **f)}
         self.num_pairs = 0
         self.num_pairs_dev = torch.zeros(1, device=device, dtype=torch.int64)
-        self.use_order = True  # raster calls take the tiles heaviest first
+        self.schedule = "chunks"  # "chunks": plan + checkpoints; "order": plan only; "tiles": neither
         self._alloc_pairs(pair_capacity)
 
     def _alloc_pairs(self, cap):
@@ -265,15 +278,15 @@ class Pipeline:
         tile empty and shows as self.num_pairs_dev > self.capacity)."""
         if not wait:
             gs_bin_and_sort(self.n, self.proj, cam, self.bin_ws, self.capacity, self.keys, self.ids, self.ranges,
-                            self.num_pairs_dev, stream, wait=False, tile_order=self.order)
+                            self.num_pairs_dev, stream, wait=False, plan=self.plan)
             self.num_pairs = None
             return None
         st, P = gs_bin_and_sort(self.n, self.proj, cam, self.bin_ws, self.capacity, self.keys, self.ids,
-                                self.ranges, self.num_pairs_dev, stream, tile_order=self.order)
+                                self.ranges, self.num_pairs_dev, stream, plan=self.plan)
         if st == GS_ERR_CAPACITY:
             self._alloc_pairs(int(P * 1.25) + 1024)
             st, P = gs_bin_and_sort(self.n, self.proj, cam, self.bin_ws, self.capacity, self.keys, self.ids,
-                                    self.ranges, self.num_pairs_dev, stream, tile_order=self.order)
+                                    self.ranges, self.num_pairs_dev, stream, plan=self.plan)
         self.num_pairs = P
         return P
 
@@ -282,9 +295,14 @@ class Pipeline:
         if cap > self.capacity:
             self._alloc_pairs(int(cap))
 
-    def forward(self, cam: GsCamera, eval_count=None, stream=None):
+    def forward(self, cam: GsCamera, eval_count=None, stream=None, checkpoints=None):
+        """Blend. checkpoints (default: the "chunks" schedule) stores the per-chunk state that lets
+        the backward split long tiles; a render that no backward follows can leave it out."""
+        ck = self.schedule == "chunks" if checkpoints is None else bool(checkpoints)
+        self._ckpt_written = ck
         gs_rasterize_fwd(self.n, self.proj, cam, self.ids, self.ranges, self.image, self.final_T, self.n_contrib,
-                         eval_count, stream, tile_order=self.order if self.use_order else None)
+                         eval_count, stream, plan=self.plan if self.schedule != "tiles" else None,
+                         raster_ws=self.raster_ws if ck else None)
 
     def loss_l1(self, target, loss=None, stream=None):
         gs_loss_l1(self.width, self.height, self.image, target, self.dL_dimage, loss, stream)
@@ -295,7 +313,8 @@ class Pipeline:
                          p["sh"], cam, self.proj, self.ids, self.ranges, self.final_T, self.n_contrib,
                          self.dL_dimage if dL_dimage is None else dL_dimage, self.bwd_ws, g["means"], g["log_scales"],
                          g["quats"], g["opacity_logits"], g["sh"], g["means2d"], eval_count, stream,
-                         tile_order=self.order if self.use_order else None)
+                         plan=self.plan if self.schedule != "tiles" else None,
+                         raster_ws=self.raster_ws if getattr(self, "_ckpt_written", False) else None)
 
     def iteration(self, cam: GsCamera, target, stream=None, wait=True):
         """One fwd+bwd iteration: project, bin+sort, blend, L1 gradient, backward. wait=False runs

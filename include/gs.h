@@ -106,12 +106,13 @@ gs_status gs_project(int32_t n, int32_t sh_degree, const float* d_means, const f
  *   gs_bin_workspace_bytes(n, pair_capacity, cam) bytes (device, 256-byte aligned, contents
  *   arbitrary on entry and need not persist between calls); pair_capacity = length of d_keys
  *   and d_ids.
- * Outputs: d_keys [P] uint64, d_ids [P] uint32, d_tile_ranges [tiles, 2] uint32; d_tile_order
- *   [tiles] uint32 (optional): every tile id once, tiles with more pairs first (by the bit
- *   length of their pair count, empty tiles last), an order in which the raster calls may take
- *   the tiles so that the longest ones start first; P itself goes to *d_num_pairs (device int64,
- *   optional, written on `stream`) and to *h_num_pairs (host, optional). d_keys doubles as
- *   scratch during the call.
+ * Outputs: d_keys [P] uint64, d_ids [P] uint32, d_tile_ranges [tiles, 2] uint32;
+ *   d_raster_plan (optional, gs_raster_plan_words(cam) uint32): how the raster calls schedule the
+ *   frame -- the tiles in an order with the ones holding more pairs first (by the bit length of
+ *   the count, empty tiles last), a chunk length L (a power of two >= 256 with P <= 2048 L), and
+ *   the (tile, chunk of L list entries) work items of the backward; P itself goes to
+ *   *d_num_pairs (device int64, optional, written on `stream`) and to *h_num_pairs (host,
+ *   optional). d_keys doubles as scratch during the call.
  * Waiting: with h_num_pairs == NULL nothing waits: the call only enqueues kernels, sized by the
  *   capacity, that stop at the device-side count. With h_num_pairs != NULL it waits once on
  *   `stream` to read P and returns GS_ERR_CAPACITY when P > pair_capacity.
@@ -124,9 +125,10 @@ gs_status gs_project(int32_t n, int32_t sh_degree, const float* d_means, const f
  *   or more than 2^24 tiles).
  */
 size_t gs_bin_workspace_bytes(int32_t n, int64_t pair_capacity, const gs_camera* cam);
+size_t gs_raster_plan_words(const gs_camera* cam);
 gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const gs_camera* cam, void* d_workspace,
                           size_t workspace_bytes, int64_t pair_capacity, uint64_t* d_keys, uint32_t* d_ids,
-                          uint32_t* d_tile_ranges, uint32_t* d_tile_order, int64_t* d_num_pairs,
+                          uint32_t* d_tile_ranges, uint32_t* d_raster_plan, int64_t* d_num_pairs,
                           int64_t* h_num_pairs, void* stream);
 
 /*
@@ -136,18 +138,24 @@ gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const gs_camera* 
  *   alpha = min(0.99, o exp(-sigma)); skip if sigma < 0 or alpha < 1/255;
  *   stop before adding when T (1 - alpha) <= 1e-4; else pixel += colour alpha T, T *= 1 - alpha;
  * and finally pixel += T background.
- * Inputs: proj, d_ids and d_tile_ranges from gs_bin_and_sort for the same camera; d_tile_order
- *   (optional, NULL = tile id order): the order in which the tiles are taken, a permutation of
- *   the tile ids such as gs_bin_and_sort's (it changes only the scheduling, not the results).
+ * Inputs: proj, d_ids and d_tile_ranges from gs_bin_and_sort for the same camera;
+ *   d_raster_plan (optional, NULL = tiles in id order) from that gs_bin_and_sort call: the tiles
+ *   are taken in its order (scheduling only, the results do not change); d_raster_ws (optional,
+ *   gs_raster_workspace_bytes() bytes, device, used only with a plan): the forward stores there,
+ *   for tiles longer than the plan's chunk length L, per chunk of L list entries and per pixel
+ *   the transmittance after the chunk and the colour the chunk added, which lets
+ *   gs_rasterize_bwd split such tiles (the image is then summed chunk by chunk).
  * Outputs: d_image [h,w,3]; d_final_T [h,w] the transmittance after the last added splat;
  *   d_n_contrib [h,w] uint32: number of tile-list entries up to and including the last added
  *   splat (0 if none). d_eval_count: NULL, or a device uint64 to which the number of
  *   (pixel, entry) evaluations is added (a work counter for measurement).
  * Deterministic: no atomics on the outputs; each pixel is written once.
  */
+size_t gs_raster_workspace_bytes(void);
 gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const gs_camera* cam, const uint32_t* d_ids,
-                           const uint32_t* d_tile_ranges, const uint32_t* d_tile_order, float* d_image,
-                           float* d_final_T, uint32_t* d_n_contrib, uint64_t* d_eval_count, void* stream);
+                           const uint32_t* d_tile_ranges, const uint32_t* d_raster_plan, void* d_raster_ws,
+                           float* d_image, float* d_final_T, uint32_t* d_n_contrib, uint64_t* d_eval_count,
+                           void* stream);
 
 /*
  * gs_rasterize_bwd -- gradients of a loss L with respect to the raw parameters, given
@@ -160,8 +168,12 @@ gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const gs_camera*
  * conic and opacity, and by the chain rule of gs_project to the raw parameters. Culled
  * Gaussians get exactly zero; radii, rectangles, keys and the sort carry no gradient.
  * Inputs: the raw parameters and camera given to gs_project, its proj, the d_ids/d_tile_ranges
- *   (and optional d_tile_order, as in gs_rasterize_fwd) of gs_bin_and_sort, d_final_T/d_n_contrib
- *   of gs_rasterize_fwd, d_dL_dimage [h,w,3];
+ *   of gs_bin_and_sort, d_final_T/d_n_contrib of gs_rasterize_fwd, d_dL_dimage [h,w,3];
+ *   d_raster_plan and d_raster_ws (optional): with both -- the plan and workspace the forward was
+ *   given -- each work item of the plan (one chunk of L list entries of a tile) runs as its own
+ *   workgroup, an inner chunk starting from the forward's checkpoints (the transmittance after
+ *   the chunk, and S = T_final background + the colour each later chunk added); with a plan
+ *   only, the tiles are taken in its order; without, in id order;
  *   d_workspace of at least gs_bwd_workspace_bytes(n) bytes (device).
  * Outputs (overwritten, not accumulated): d_grad_means [n,3], d_grad_log_scales [n,3],
  *   d_grad_quats [n,4], d_grad_opacity_logits [n], d_grad_sh [n,(sh_degree+1)^2,3], and
@@ -172,8 +184,8 @@ size_t gs_bwd_workspace_bytes(int32_t n);
 gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float* d_means, const float* d_log_scales,
                            const float* d_quats, const float* d_opacity_logits, const float* d_sh,
                            const gs_camera* cam, const gs_projected* proj, const uint32_t* d_ids,
-                           const uint32_t* d_tile_ranges, const uint32_t* d_tile_order, const float* d_final_T,
-                           const uint32_t* d_n_contrib,
+                           const uint32_t* d_tile_ranges, const uint32_t* d_raster_plan, const void* d_raster_ws,
+                           const float* d_final_T, const uint32_t* d_n_contrib,
                            const float* d_dL_dimage, void* d_workspace, size_t workspace_bytes,
                            float* d_grad_means, float* d_grad_log_scales, float* d_grad_quats,
                            float* d_grad_opacity_logits, float* d_grad_sh, float* d_grad_means2d,

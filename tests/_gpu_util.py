@@ -71,21 +71,40 @@ def run_gpu_bin(gs, torch, params_n, proj, cam, capacity):
     ids = torch.empty(max(capacity, 1), device="cuda", dtype=torch.int32)
     tiles = ((cam.width + 15) // 16) * ((cam.height + 15) // 16)
     ranges = torch.empty(tiles, 2, device="cuda", dtype=torch.int32)
-    order = torch.full((tiles,), -1, device="cuda", dtype=torch.int32)
+    plan = torch.full((gs.gs_raster_plan_words(cam),), -1, device="cuda", dtype=torch.int32)
     ws = torch.empty(gs.gs_bin_workspace_bytes(params_n, capacity, cam), device="cuda", dtype=torch.uint8)
-    st, P = gs.gs_bin_and_sort(params_n, proj, cam, ws, capacity, keys, ids, ranges, tile_order=order)
+    st, P = gs.gs_bin_and_sort(params_n, proj, cam, ws, capacity, keys, ids, ranges, plan=plan)
     torch.cuda.synchronize()
-    return st, P, keys, ids, ranges, order
+    return st, P, keys, ids, ranges, plan
 
 
-def assert_tile_order(order_np, ranges_np):
-    """The processing order is a permutation of the tiles by non-increasing bit length of the
-    pair count (empty tiles last)."""
+def assert_raster_plan(plan_np, ranges_np, P):
+    """The raster plan: tiles ordered by non-increasing bit length of their pair count (empty
+    ones last), a chunk length L = the smallest power of two >= 256 with P <= 2048 L, per tile
+    ceil(count / L) work items (tile, 0..) and, with two or more chunks, as many checkpoint
+    slots; items and slots follow the processing order."""
+    plan = plan_np.view(np.uint32).astype(np.int64)
     n = ranges_np.shape[0]
-    assert np.array_equal(np.sort(order_np.astype(np.int64)), np.arange(n)), "tile order is not a permutation"
-    cnt = (ranges_np[:, 1].astype(np.int64) - ranges_np[:, 0])[order_np]
-    cls = np.where(cnt > 0, np.floor(np.log2(np.maximum(cnt, 1))).astype(np.int64) + 1, 0)
+    L, n_items, n_ck = plan[0], plan[1], plan[2]
+    order = plan[4:4 + n]
+    assert np.array_equal(np.sort(order), np.arange(n)), "tile order is not a permutation"
+    cnt = ranges_np[:, 1].astype(np.int64) - ranges_np[:, 0]
+    cls = np.where(cnt[order] > 0, np.floor(np.log2(np.maximum(cnt[order], 1))).astype(np.int64) + 1, 0)
     assert np.all(np.diff(cls) <= 0), "tile order is not heaviest class first"
+    want_L = 256
+    while want_L * 2048 < P:
+        want_L *= 2
+    assert L == want_L, (L, want_L)
+    nch = (cnt + L - 1) // L
+    slots = np.where(nch >= 2, nch, 0)
+    assert n_items == nch.sum() and n_ck == slots.sum()
+    # slots and work items follow the processing order
+    base = np.zeros(n, np.int64)
+    base[order] = np.concatenate([[0], np.cumsum(slots[order])[:-1]])
+    assert np.array_equal(plan[4 + n:4 + 2 * n], base)
+    items = plan[4 + 2 * n:4 + 2 * n + 2 * n_items].reshape(-1, 2)
+    want = np.array([(t, c) for t in order for c in range(nch[t])], np.int64).reshape(-1, 2)
+    assert np.array_equal(items, want), "work items differ"
 
 
 def pixel_last_ids(nc, ids_np, ranges_np, pixels, width):

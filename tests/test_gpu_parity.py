@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 from gaussian_splatting_tile_gs_amd import synth
-from _gpu_util import (assert_projection_bit_exact, assert_tile_order, compare_forward, compare_grads, log,
+from _gpu_util import (assert_projection_bit_exact, assert_raster_plan, compare_forward, compare_grads, log,
                        proj_from_numpy, proj_to_numpy, run_gpu_bin, run_gpu_project)
 
 pytestmark = pytest.mark.gpu
@@ -49,7 +49,7 @@ def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7
     # binning end to end (GPU projection) and stage-isolated (the oracle's projection uploaded)
     o_keys, o_ids, o_ranges = oracle.bin_pairs(o_proj, cam_dict)
     P_exp = int(o_keys.size)
-    st, P, keys, ids, ranges, order = run_gpu_bin(gs, torch, params["n"], proj, cam, P_exp + 17)
+    st, P, keys, ids, ranges, plan = run_gpu_bin(gs, torch, params["n"], proj, cam, P_exp + 17)
     assert st == gs.GS_OK and P == P_exp
     keys_np = keys.cpu().numpy()[:P].view(np.uint64)
     ids_np = ids.cpu().numpy()[:P].view(np.uint32)
@@ -57,7 +57,7 @@ def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7
     assert np.array_equal(keys_np, o_keys), "sorted keys differ"
     assert np.array_equal(ids_np, o_ids), "sorted ids differ"
     assert np.array_equal(ranges_np, o_ranges), "tile ranges differ"
-    assert_tile_order(order.cpu().numpy(), ranges_np)
+    assert_raster_plan(plan.cpu().numpy(), ranges_np, P)
     iso = proj_from_numpy(gs, torch, o_proj)
     st2, P2, keys2, ids2, ranges2, _ = run_gpu_bin(gs, torch, params["n"], iso, cam, P_exp)
     assert st2 == gs.GS_OK and P2 == P_exp
@@ -71,7 +71,8 @@ def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7
     fT = torch.empty(H, W, device="cuda")
     nc = torch.empty(H, W, device="cuda", dtype=torch.int32)
     evals = torch.zeros(1, device="cuda", dtype=torch.int64)
-    gs.gs_rasterize_fwd(params["n"], proj, cam, ids, ranges, img, fT, nc, evals, tile_order=order)
+    rws = torch.empty(gs.gs_raster_workspace_bytes(), device="cuda", dtype=torch.uint8)
+    gs.gs_rasterize_fwd(params["n"], proj, cam, ids, ranges, img, fT, nc, evals, plan=plan, raster_ws=rws)
     torch.cuda.synchronize()
     pix = _full_pixels(cam_dict) if pixels is None else pixels
     o_fwd = oracle.render(o_proj, cam_dict, pixels=pix)
@@ -98,7 +99,7 @@ def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7
                         params["opacity_logits"], params["sh"], cam, proj, ids, ranges, fT, nc,
                         torch.from_numpy(dimg).cuda(), ws, pipe_grads["means"], pipe_grads["log_scales"],
                         pipe_grads["quats"], pipe_grads["opacity_logits"], pipe_grads["sh"], g2d_out,
-                        tile_order=order)
+                        plan=plan, raster_ws=rws)
     torch.cuda.synchronize()
     g2d, aref2d = oracle.render_backward(o_proj, cam_dict, gsel, pixels=pix)
     raw = oracle.project_backward(scene, cam_dict, g2d, aref2d)
@@ -188,11 +189,11 @@ def test_capacity_overflow_contract(env):
             ids = torch.full((cap + 64,), -7, device="cuda", dtype=torch.int32)
             ranges = torch.full((tiles, 2), -7, device="cuda", dtype=torch.int32)
             pdev = torch.full((1,), -7, device="cuda", dtype=torch.int64)
-            order = torch.full((tiles,), -1, device="cuda", dtype=torch.int32)
+            plan = torch.full((gs.gs_raster_plan_words(cam),), -1, device="cuda", dtype=torch.int32)
             ws = torch.empty(gs.gs_bin_workspace_bytes(params["n"], cap, cam), device="cuda", dtype=torch.uint8)
             ws.fill_(0xAB)  # the workspace's contents on entry are arbitrary
             st, P = gs.gs_bin_and_sort(params["n"], proj, cam, ws, cap, keys, ids, ranges, pdev, wait=wait,
-                                       tile_order=order)
+                                       plan=plan)
             torch.cuda.synchronize()
             if wait:
                 assert st == gs.GS_ERR_CAPACITY and P == need
@@ -200,7 +201,8 @@ def test_capacity_overflow_contract(env):
                 assert st == gs.GS_OK and P is None
             assert int(pdev.item()) == need
             assert torch.all(ranges == 0)
-            assert np.array_equal(np.sort(order.cpu().numpy()), np.arange(tiles))
+            pl = plan.cpu().numpy().view(np.uint32)
+            assert np.array_equal(np.sort(pl[4:4 + tiles]), np.arange(tiles)) and pl[1] == 0 and pl[2] == 0
             assert torch.all(keys[cap:] == -7) and torch.all(ids[cap:] == -7)
 
 
@@ -270,14 +272,16 @@ def test_opacity_extremes(env):
 
 
 def test_forward_and_sort_deterministic(env):
+    # the same schedule twice: bit-identical; chunked (per-chunk colour sums) vs whole tiles: the
+    # same sort and contributor counts, images equal up to the order of the colour additions
     gs, torch = env
     wl = synth.WORKLOADS["distill_30k"]
     params = gs.scene_to_device(synth.make_scene(wl))
     cam = gs.make_camera(synth.make_cameras(wl)[5])
     pipe = gs.Pipeline(params, wl.width, wl.height, pair_capacity=1 << 18)
     outs = []
-    for use_order in (True, False):  # the tile order changes scheduling only
-        pipe.use_order = use_order
+    for schedule in ("chunks", "chunks", "tiles"):
+        pipe.schedule = schedule
         pipe.project(cam)
         pipe.bin(cam)
         pipe.forward(cam)
@@ -286,6 +290,11 @@ def test_forward_and_sort_deterministic(env):
                      pipe.n_contrib.clone()))
     for a, b in zip(outs[0], outs[1]):
         assert torch.equal(a, b)
+    for i, (a, b) in enumerate(zip(outs[0], outs[2])):
+        if i == 2:
+            assert torch.allclose(a, b, rtol=0, atol=1e-6)
+        else:
+            assert torch.equal(a, b)
 
 
 def test_loss_l1(env):
