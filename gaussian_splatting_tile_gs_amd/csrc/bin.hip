@@ -315,153 +315,241 @@ __device__ void tile_rows(const TileCountArgs& a, uint32_t rb, uint32_t* lds, ui
   }
 }
 
-// One workgroup: per-tile counts = prefix sums of the difference array, in chunks of 8192 tiles
-// staged in `lds`. A first sweep finds P and how many tiles fall in each count class (bit
-// length of the count). A second writes the ranges and histograms (when P fits) and the raster
-// plan: the processing order (the heaviest class first, empty tiles last, so that the long
-// raster workgroups start first), the chunk length L (the smallest power of two >= 256 with
-// P <= kPlanMaxChunks L), and per tile its checkpoint slot base and (tile, chunk) work items.
+// One workgroup, in steps of 10240 tiles held in LDS (one step up to 10240 tiles): thread tid
+// takes tiles 1024 q + tid, so each row of 1024 tiles is loaded and stored contiguously. The
+// difference array is scanned into per-tile counts and the counts into range starts, in place.
+// A first sweep finds P (64 bits) and how many tiles fall in each count class (bit length of the
+// count). A second writes the ranges and the pair-sort histograms (when P fits), the processing
+// order (heaviest class first, empty tiles last, so that the long raster workgroups start
+// first), and for each tile of two or more chunks of L its checkpoint slots and extra work items
+// (chunks 1 ..). With one step the second sweep finds the starts still in LDS.
+// The code is loops over rows rather than unrolled: it runs once per frame, on one compute unit,
+// where straight-line code would wait on instruction fetch.
+// Histogram digits above the lowest are constant over aligned runs of 256^k tiles: a run's count
+// is the difference of the range starts at its ends, added with two LDS atomics per run.
 __device__ __forceinline__ uint32_t count_class(uint32_t c) { return c ? 32u - (uint32_t)__clz(c) : 0u; }
 
-__device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t* s_wsum, uint32_t (*s_hist)[kRadix]) {
-  const int tid = threadIdx.x;
-  constexpr uint32_t kChunk = kSortThreads * 8;
-  uint32_t* s_cls = s_hist[3];       // tiles per count class (33)
-  uint32_t* s_cur = s_hist[3] + 64;  // next order slot per class
+// Lanes with the same class share one LDS atomic on ctr[cls]; returns a valid lane's slot.
+// Every lane of the wave calls it.
+__device__ __forceinline__ uint32_t wave_class_slot(bool valid, uint32_t cls, uint32_t* ctr, int lane) {
+  uint64_t m = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 6; ++b) {
+    const bool bit = (cls >> b) & 1u;
+    const uint64_t bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  const int leader = __builtin_ctzll(m | (1ull << 63));
+  uint32_t base = 0;
+  if (valid && lane == leader) base = atomicAdd(&ctr[cls], (uint32_t)__popcll(m));
+  base = __shfl(base, leader, 64);
+  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  return base + (uint32_t)__popcll(m & lt);
+}
+
+// DPP lane shifts within rows of 16 lanes (row_shr) and row broadcasts (row_bcast); lanes whose
+// source lies outside the row read 0, lanes of rows outside ROWMASK are left as they are.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWMASK, 0xf, true);
+}
+// Inclusive sum within each row of 16 lanes.
+__device__ __forceinline__ uint32_t row16_incl_scan(uint32_t v) {
+  v += dpp_u32<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_u32<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_u32<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_u32<0x118, 0xf>(v);  // row_shr:8
+  return v;
+}
+// Inclusive sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
+  v = row16_incl_scan(v);
+  v += dpp_u32<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_u32<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+constexpr int kFinRows = 10;
+constexpr uint32_t kFinStep = kSortThreads * kFinRows;
+constexpr uint32_t kFinAuxWords = 8 * kRadix;  // histograms, classes, scan partials
+
+// Exclusive scan, in place, of `rows` rows of 1024 values in LDS (s[1024 q + tid] in thread
+// tid), offset by carry; returns the sum (mod 2^32). Every thread calls it; it ends with a
+// barrier, after which any thread may read any element.
+__device__ uint32_t lds_rows_scan(uint32_t* s, int rows, uint32_t carry, uint32_t* s_wt, uint32_t* s_rt) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll 1
+  for (int q = 0; q < rows; ++q) {
+    uint32_t* p = s + q * kSortThreads + tid;
+    const uint32_t v = *p;
+    const uint32_t inc = wave_incl_scan_dpp(v);
+    *p = inc - v;
+    if (lane == 63) s_wt[q * kSortWaves + wave] = inc;
+  }
+  __syncthreads();
+  if (tid < rows * kSortWaves) {  // a 16-lane row per row of tiles: the scan over its waves
+    const uint32_t v = s_wt[tid];
+    const uint32_t inc = row16_incl_scan(v);
+    s_wt[tid] = inc - v;
+    if ((tid & (kSortWaves - 1)) == kSortWaves - 1) s_rt[tid / kSortWaves] = inc;
+  }
+  __syncthreads();
+  uint32_t before = carry;
+#pragma unroll 1
+  for (int q = 0; q < rows; ++q) {
+    s[q * kSortThreads + tid] += before + s_wt[q * kSortWaves + wave];
+    before += s_rt[q];
+  }
+  __syncthreads();
+  return before - carry;
+}
+
+__device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t lds_words) {
+  __shared__ unsigned long long s_p64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  uint32_t* aux = lds + (lds_words - kFinAuxWords);
+  uint32_t(*s_hist)[kRadix] = reinterpret_cast<uint32_t(*)[kRadix]>(aux);  // rows 0-2: histograms
+  uint32_t* s_cls = aux + 3 * kRadix;  // tiles per count class (33)
+  uint32_t* s_cur = s_cls + 64;        // next order slot per class
+  uint32_t* s_misc = s_cls + 128;      // [0] extra work items, [1] checkpoint slots
+  uint32_t* s_wt = aux + 4 * kRadix;   // kFinRows x 16 scan partials
+  uint32_t* s_rt = aux + 5 * kRadix;   // kFinRows row sums
+  uint32_t* s = lds;                   // the step's tiles
+  const bool one_step = a.ntiles <= kFinStep;
   if (tid < kRadix)
     for (int k = 0; k < a.npass; ++k) s_hist[k][tid] = 0;
-  if (tid < 64) s_cls[tid] = 0;
+  if (tid < 130) s_cls[tid] = 0;  // classes, cursors, misc
+  if (tid == 0) s_p64 = 0;
   __syncthreads();
   uint64_t P = 0;
-  uint32_t L = kPlanMinChunk;
+  uint32_t P32 = 0, L = kPlanMinChunk;
+  bool fits = false;
+#pragma unroll 1
   for (int sweep = 0; sweep < 2; ++sweep) {
-    const bool write = sweep == 1 && P <= a.capacity;
-    if (sweep == 1 && !write && !a.plan) break;
+    if (sweep == 1 && !fits && !a.plan) break;
     uint32_t carry_d = 0, carry_c = 0;
-    for (uint32_t cb = 0; cb < a.ntiles; cb += kChunk) {
-      uint32_t v[8];
+#pragma unroll 1
+    for (uint32_t cb = 0; cb < a.ntiles; cb += kFinStep) {
+      const uint32_t m = a.ntiles - cb < kFinStep ? a.ntiles - cb : kFinStep;  // tiles in the step
+      const int rows = (int)((m + kSortThreads - 1) / kSortThreads);
+      uint32_t step_end = P32;  // the start after the step's last tile
+      if (sweep == 0 || !one_step) {
+        __syncthreads();  // the previous step's reads of s (neighbours included) are done
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const uint32_t t = cb + (uint32_t)(q * kSortThreads + tid);
-        v[q] = t < a.ntiles ? ld_dev(&a.tdiff[t]) : 0u;
-      }
+        for (int q = 0; q < kFinRows; ++q) {
+          const uint32_t i = (uint32_t)(q * kSortThreads + tid);
+          if (q < rows) s[i] = i < m ? a.tdiff[cb + i] : 0u;
+        }
+        // counts: the inclusive prefix of the differences = the next tile's exclusive one
+        const uint32_t dtot = lds_rows_scan(s, rows, carry_d, s_wt, s_rt);
+        carry_d += dtot;
+        uint32_t c[kFinRows];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) lds[q * kSortThreads + tid] = v[q];
-      __syncthreads();
-      uint32_t d[8], dsum = 0;
+        for (int q = 0; q < kFinRows; ++q) {
+          const uint32_t i = (uint32_t)(q * kSortThreads + tid);
+          c[q] = (q < rows && i < m) ? (i + 1 < m ? s[i + 1] : carry_d) : 0u;
+        }
+        __syncthreads();
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        d[q] = lds[tid * 8 + q];
-        dsum += d[q];
-      }
-      uint32_t dtot;
-      const uint32_t dpre = carry_d + block_excl_scan1024<uint32_t>(dsum, s_wsum, &dtot);
-      uint32_t cnt[8], csum = 0, run = dpre;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        run += d[q];
-        cnt[q] = cb + (uint32_t)(tid * 8 + q) < a.ntiles ? run : 0u;  // no tiles past the grid
-        csum += cnt[q];
-      }
-      uint32_t ctot;
-      uint32_t start = carry_c + block_excl_scan1024<uint32_t>(csum, s_wsum, &ctot);
-      if (sweep == 0) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (cb + (uint32_t)(tid * 8 + q) < a.ntiles) atomicAdd(&s_cls[count_class(cnt[q])], 1u);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint32_t t = cb + (uint32_t)(tid * 8 + q);
-          if (t < a.ntiles && write && cnt[q]) {
-            a.ranges[2 * t] = start;
-            a.ranges[2 * t + 1] = start + cnt[q];
-            for (int k = 0; k < a.npass; ++k) atomicAdd(&s_hist[k][(t >> (8 * k)) & 255u], cnt[q]);
+        for (int q = 0; q < kFinRows; ++q)
+          if (q < rows) s[q * kSortThreads + tid] = c[q];
+        if (sweep == 0) {
+          uint64_t c64 = 0;
+#pragma unroll 1
+          for (int q = 0; q < rows; ++q) {
+            const uint32_t i = (uint32_t)(q * kSortThreads + tid);
+            const uint32_t cq = s[i];  // this thread's own entry (0 past the step)
+            c64 += cq;
+            wave_class_slot(i < m, count_class(cq), s_cls, lane);
           }
-          start += cnt[q];
-          if (a.plan) {
-            // order slot: lanes with the same count class share one LDS atomic
-            const bool valid = t < a.ntiles;
-            const uint32_t cls = count_class(write ? cnt[q] : 0u);
-            uint64_t m = __ballot(valid);
-#pragma unroll
-            for (int b = 0; b < 6; ++b) {
-              const bool bit = (cls >> b) & 1u;
-              const uint64_t bb = __ballot(bit);
-              m &= bit ? bb : ~bb;
-            }
-            const int lane = tid & 63;
-            const int leader = __builtin_ctzll(m | (1ull << 63));
-            uint32_t base = 0;
-            if (valid && lane == leader) base = atomicAdd(&s_cur[cls], (uint32_t)__popcll(m));
-            base = __shfl(base, leader, 64);
-            if (valid) {
-              const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
-              a.plan[kPlanOrder + base + (uint32_t)__popcll(m & lt)] = t;
+          c64 = wave_sum_u64(c64);
+          if (lane == 0) atomicAdd(&s_p64, (unsigned long long)c64);
+        }
+        // range starts (mod 2^32: used only when P fits, < 2^30)
+        carry_c += lds_rows_scan(s, rows, carry_c, s_wt, s_rt);
+        step_end = carry_c;
+      }
+      if (sweep == 0) continue;
+      uint32_t* extra = a.plan + kPlanOrder + 2 * a.ntiles;
+#pragma unroll 1
+      for (int q = 0; q < rows; ++q) {
+        const uint32_t i = (uint32_t)(q * kSortThreads + tid), t = cb + i;
+        const bool valid = i < m;
+        const uint32_t st = valid ? s[i] : 0u;
+        const uint32_t c = (valid && fits) ? (i + 1 < m ? s[i + 1] : step_end) - st : 0u;
+        if (c) {
+          a.ranges[2 * t] = st;
+          a.ranges[2 * t + 1] = st + c;
+          atomicAdd(&s_hist[0][t & 255u], c);
+        }
+        if (valid && fits) {
+          // a run of 256^k tiles starting at t: its digit-k count starts at -start(t) and the
+          // previous run's gets start(t)
+          for (int k = 1; k < a.npass; ++k) {
+            if ((t & ((1u << (8 * k)) - 1u)) == 0u) {
+              atomicSub(&s_hist[k][(t >> (8 * k)) & 255u], st);
+              if (t) atomicAdd(&s_hist[k][((t - 1u) >> (8 * k)) & 255u], st);
             }
           }
         }
+        if (!a.plan) continue;
+        const uint32_t slot = wave_class_slot(valid, count_class(c), s_cur, lane);
+        if (valid) a.plan[kPlanOrder + slot] = t;
+        // a tile of two or more chunks: its checkpoint slots and extra work items
+        const uint32_t nch = (c + L - 1u) / L;
+        const bool multi = valid && nch >= 2u;
+        uint32_t xb = 0;
+        if (multi) {
+          a.plan[kPlanOrder + a.ntiles + t] = atomicAdd(&s_misc[1], nch);
+          xb = atomicAdd(&s_misc[0], nch - 1u);
+        }
+        uint64_t mm = __ballot(multi);
+        while (mm) {  // the wave writes each such tile's items together
+          const int src = __builtin_ctzll(mm);
+          mm &= mm - 1;
+          const uint32_t n1 = (uint32_t)__builtin_amdgcn_readlane((int)nch, src) - 1u;
+          const uint32_t x0 = (uint32_t)__builtin_amdgcn_readlane((int)xb, src);
+          const uint32_t tt = (uint32_t)__builtin_amdgcn_readlane((int)t, src);
+          for (uint32_t j = (uint32_t)lane; j < n1; j += 64) {
+            extra[2 * (x0 + j)] = tt;
+            extra[2 * (x0 + j) + 1] = j + 1u;
+          }
+        }
       }
-      carry_d += dtot;
-      carry_c += ctot;
-      __syncthreads();  // the chunk's LDS is reused
     }
     if (sweep == 0) {
-      P = carry_c;
-      while ((uint64_t)L * kPlanMaxChunks < P) L <<= 1;
+      __syncthreads();  // every wave's class counts and count sums are in
+      P = s_p64;
+      P32 = carry_c;
+      fits = P <= a.capacity;
+      if (fits)
+        while ((uint64_t)L * kPlanMaxChunks < P) L <<= 1;
       if (tid == 0) {
         // on overflow every tile is empty for the raster calls: all in class 0
         uint32_t slot = 0;
         for (int c = 32; c >= 0; --c) {
           s_cur[c] = slot;
-          slot += P <= a.capacity ? s_cls[c] : (c == 0 ? a.ntiles : 0u);
+          slot += fits ? s_cls[c] : (c == 0 ? a.ntiles : 0u);
         }
       }
       __syncthreads();
     }
   }
+  if (tid == 0 && fits)  // the last run ends at P
+    for (int k = 1; k < a.npass; ++k) atomicAdd(&s_hist[k][((a.ntiles - 1u) >> (8 * k)) & 255u], (uint32_t)P);
   __syncthreads();
-  if (tid < kRadix && P <= a.capacity)
+  if (tid < kRadix && fits)
     for (int k = 0; k < a.npass; ++k) a.hist_pair[k * kRadix + tid] = s_hist[k][tid];
-  if (!a.plan) return;
-  // work items and checkpoint slots, in processing order (the order and ranges written above by
-  // this workgroup are visible to it after the barrier)
-  const bool fits = P <= a.capacity;
-  uint32_t carry_i = 0, carry_k = 0;
-  for (uint32_t ob = 0; ob < a.ntiles; ob += kChunk) {
-    uint32_t t[8], nch[8], isum = 0, ksum = 0;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint32_t i = ob + (uint32_t)(tid * 8 + q);
-      t[q] = i < a.ntiles ? a.plan[kPlanOrder + i] : 0u;
-      const uint32_t c = (i < a.ntiles && fits) ? a.ranges[2 * t[q] + 1] - a.ranges[2 * t[q]] : 0u;
-      nch[q] = (c + L - 1) / L;
-      isum += nch[q];
-      ksum += nch[q] >= 2 ? nch[q] : 0u;
-    }
-    uint32_t itot, ktot;
-    uint32_t ibase = carry_i + block_excl_scan1024<uint32_t>(isum, s_wsum, &itot);
-    uint32_t kbase = carry_k + block_excl_scan1024<uint32_t>(ksum, s_wsum, &ktot);
-    uint32_t* it = a.plan + kPlanOrder + 2 * a.ntiles;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      if (ob + (uint32_t)(tid * 8 + q) < a.ntiles) {
-        a.plan[kPlanOrder + a.ntiles + t[q]] = kbase;
-        for (uint32_t c = 0; c < nch[q]; ++c) {
-          it[2 * (ibase + c)] = t[q];
-          it[2 * (ibase + c) + 1] = c;
-        }
-      }
-      ibase += nch[q];
-      kbase += nch[q] >= 2 ? nch[q] : 0u;
-    }
-    carry_i += itot;
-    carry_k += ktot;
-  }
-  if (tid == 0) {
+  if (a.plan && tid == 0) {
     a.plan[kPlanChunk] = L;
-    a.plan[kPlanItems] = carry_i;
-    a.plan[kPlanCheckpoints] = carry_k;
+    a.plan[kPlanExtra] = s_misc[0];
+    a.plan[kPlanCheckpoints] = s_misc[1];
   }
 }
 
@@ -494,7 +582,7 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
 
   if (EXTRA != 0 && blockIdx.x >= gridDim.x - n_extra) {  // workgroup-uniform
     if (EXTRA == 1) tile_rows(targs, blockIdx.x - (gridDim.x - n_extra), s_mem, kLdsWords);
-    if (EXTRA == 2) tile_finalize(targs, s_mem, s_wsum, s_wcnt);
+    if (EXTRA == 2) tile_finalize(targs, s_mem, kLdsWords);
     return;
   }
   const uint32_t n = n_dev ? (uint32_t)*n_dev : n_host;
@@ -788,12 +876,12 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit(const uint64_t* __restric
   }
 }
 
-// The raster plan of a frame without pairs: natural tile order, no work items or checkpoints.
+// The raster plan of a frame without pairs: natural tile order, no extra work items or checkpoints.
 __global__ void k_empty_plan(uint32_t* __restrict__ plan, uint32_t ntiles) {
   const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i == 0) {
     plan[kPlanChunk] = kPlanMinChunk;
-    plan[kPlanItems] = 0;
+    plan[kPlanExtra] = 0;
     plan[kPlanCheckpoints] = 0;
   }
   if (i < ntiles) {

@@ -141,19 +141,20 @@ __device__ __forceinline__ SplatEval eval_splat(float dx, float dy, float hA, fl
 
 // ---------------------------------------------------------------------------------------------
 // Raster plan (written by gs_bin_and_sort, read by the raster calls), u32 words:
-//   [0] chunk length L, [1] work items, [2] checkpoint slots, [3] unused,
+//   [0] chunk length L, [1] X = extra work items, [2] checkpoint slots, [3] unused,
 //   [4, 4 + T)          tile processing order (T = number of tiles),
-//   [4 + T, 4 + 2T)     per tile, the index of its first checkpoint slot,
-//   [4 + 2T, ...)       work items (tile, chunk), at most T + kPlanMaxChunks of them.
+//   [4 + T, 4 + 2T)     per tile with two or more chunks, the index of its first checkpoint slot,
+//   [4 + 2T, 4 + 2T + 2X)  the extra work items (tile, chunk >= 1).
 // A tile with c pairs has k = ceil(c / L) chunks of L list entries; when k >= 2 it has k slots,
 // slot j holding, per pixel, the transmittance after chunk j and the colour that chunk j added.
-// L >= P / kPlanMaxChunks keeps the slots at most 2 kPlanMaxChunks.
+// The backward's work items are the X extra ones, then (order[i], chunk 0) for every tile.
+// L >= P / kPlanMaxChunks keeps X below kPlanMaxChunks and the slots below 2 kPlanMaxChunks.
 // ---------------------------------------------------------------------------------------------
-constexpr uint32_t kPlanChunk = 0, kPlanItems = 1, kPlanCheckpoints = 2, kPlanOrder = 4;
+constexpr uint32_t kPlanChunk = 0, kPlanExtra = 1, kPlanCheckpoints = 2, kPlanOrder = 4;
 constexpr uint32_t kPlanMinChunk = 256;  // one raster batch: chunk boundaries are batch starts
 constexpr uint32_t kPlanMaxChunks = 2048;
 constexpr uint32_t kPlanMaxSlots = 2 * kPlanMaxChunks;
-inline size_t plan_words(size_t ntiles) { return kPlanOrder + 2 * ntiles + 2 * (ntiles + kPlanMaxChunks); }
+inline size_t plan_words(size_t ntiles) { return kPlanOrder + 2 * ntiles + 2 * kPlanMaxChunks; }
 
 // ---------------------------------------------------------------------------------------------
 // Host side: status, last error, kernel timing.

@@ -345,10 +345,16 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
   bool from_ckpt = false;
   size_t slot0 = 0;
   if (plan && ckpt) {
-    if (blockIdx.x >= plan[kPlanItems]) return;  // workgroup-uniform
-    const uint32_t* item = plan + kPlanOrder + 2 * ntiles + 2 * blockIdx.x;
-    tile = (int)item[0];
-    chunk = item[1];
+    // work items: the extra ones (chunks >= 1 of long tiles), then chunk 0 of every tile in order
+    const uint32_t nx = plan[kPlanExtra];
+    if (blockIdx.x < nx) {
+      const uint32_t* item = plan + kPlanOrder + 2 * ntiles + 2 * blockIdx.x;
+      tile = (int)item[0];
+      chunk = item[1];
+    } else {
+      if (blockIdx.x - nx >= ntiles) return;  // workgroup-uniform
+      tile = (int)plan[kPlanOrder + blockIdx.x - nx];
+    }
     const uint32_t L = plan[kPlanChunk];
     const uint32_t len = ranges[2 * tile + 1] - ranges[2 * tile];
     nch = (len + L - 1) / L;
@@ -798,7 +804,8 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float*
   {
     TimedScope ts("rbwd", s);
     auto kern = d_eval_count ? k_rbwd<true> : k_rbwd<false>;
-    // with checkpoints: one workgroup per work item of the plan (at most tiles + checkpoints)
+    // with checkpoints: one workgroup per work item of the plan (the extra ones, fewer than
+    // kPlanMaxChunks, then one per tile)
     const bool chunked = d_raster_plan && d_raster_ws;
     const unsigned grid = (unsigned)(chunked ? ntiles + kPlanMaxChunks : ntiles);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges, d_raster_plan,

@@ -109,8 +109,9 @@ gs_status gs_project(int32_t n, int32_t sh_degree, const float* d_means, const f
  * Outputs: d_keys [P] uint64, d_ids [P] uint32, d_tile_ranges [tiles, 2] uint32;
  *   d_raster_plan (optional, gs_raster_plan_words(cam) uint32): how the raster calls schedule the
  *   frame -- the tiles in an order with the ones holding more pairs first (by the bit length of
- *   the count, empty tiles last), a chunk length L (a power of two >= 256 with P <= 2048 L), and
- *   the (tile, chunk of L list entries) work items of the backward; P itself goes to
+ *   the count, empty tiles last), a chunk length L (a power of two >= 256 with P <= 2048 L),
+ *   and for every tile of two or more chunks of L list entries its checkpoint slots and the
+ *   backward's extra work items (its chunks after the first); P itself goes to
  *   *d_num_pairs (device int64, optional, written on `stream`) and to *h_num_pairs (host,
  *   optional). d_keys doubles as scratch during the call.
  * Waiting: with h_num_pairs == NULL nothing waits: the call only enqueues kernels, sized by the

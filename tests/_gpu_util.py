@@ -80,12 +80,12 @@ def run_gpu_bin(gs, torch, params_n, proj, cam, capacity):
 
 def assert_raster_plan(plan_np, ranges_np, P):
     """The raster plan: tiles ordered by non-increasing bit length of their pair count (empty
-    ones last), a chunk length L = the smallest power of two >= 256 with P <= 2048 L, per tile
-    ceil(count / L) work items (tile, 0..) and, with two or more chunks, as many checkpoint
-    slots; items and slots follow the processing order."""
+    ones last), a chunk length L = the smallest power of two >= 256 with P <= 2048 L, and for
+    every tile of k = ceil(count / L) >= 2 chunks k checkpoint slots (disjoint intervals that
+    tile [0, slots)) and the extra work items (tile, 1 .. k - 1), in any order."""
     plan = plan_np.view(np.uint32).astype(np.int64)
     n = ranges_np.shape[0]
-    L, n_items, n_ck = plan[0], plan[1], plan[2]
+    L, n_extra, n_ck = plan[0], plan[1], plan[2]
     order = plan[4:4 + n]
     assert np.array_equal(np.sort(order), np.arange(n)), "tile order is not a permutation"
     cnt = ranges_np[:, 1].astype(np.int64) - ranges_np[:, 0]
@@ -96,15 +96,18 @@ def assert_raster_plan(plan_np, ranges_np, P):
         want_L *= 2
     assert L == want_L, (L, want_L)
     nch = (cnt + L - 1) // L
-    slots = np.where(nch >= 2, nch, 0)
-    assert n_items == nch.sum() and n_ck == slots.sum()
-    # slots and work items follow the processing order
-    base = np.zeros(n, np.int64)
-    base[order] = np.concatenate([[0], np.cumsum(slots[order])[:-1]])
-    assert np.array_equal(plan[4 + n:4 + 2 * n], base)
-    items = plan[4 + 2 * n:4 + 2 * n + 2 * n_items].reshape(-1, 2)
-    want = np.array([(t, c) for t in order for c in range(nch[t])], np.int64).reshape(-1, 2)
-    assert np.array_equal(items, want), "work items differ"
+    multi = np.nonzero(nch >= 2)[0]
+    assert n_extra == (nch[multi] - 1).sum() and n_ck == nch[multi].sum()
+    assert n_extra < 2048
+    base = plan[4 + n + multi]
+    span = np.zeros(n_ck, np.int64)
+    for t, b0 in zip(multi, base):
+        assert 0 <= b0 and b0 + nch[t] <= n_ck
+        span[b0:b0 + nch[t]] += 1
+    assert np.all(span == 1), "checkpoint slots overlap"
+    items = plan[4 + 2 * n:4 + 2 * n + 2 * n_extra].reshape(-1, 2)
+    want = sorted((t, c) for t in multi for c in range(1, nch[t]))
+    assert sorted(map(tuple, items.tolist())) == want, "extra work items differ"
 
 
 def pixel_last_ids(nc, ids_np, ranges_np, pixels, width):

@@ -264,6 +264,16 @@ def test_huge_splat_and_tile_edges(env):
     _pipeline_case(env, sc, cam, label="huge+edges")
 
 
+@pytest.mark.parametrize("width,height", [(3000, 1100), (4200, 4200)])
+def test_many_tiles(env, width, height):
+    # 12,972 tiles: more than one step of the tile-count finalizer holds; 69,169 tiles: three
+    # pair-sort passes (17 tile-id bits), histograms of digits 1 and 2 from run boundaries
+    sc = synth.random_scene(3000, seed=width, width=width, height=height, focal=width / 2.0)
+    cam = synth.make_camera(np.eye(4), width, height, width / 2.0)
+    pix = synth.sample_pixels(width, height, 4096, seed=5)
+    _pipeline_case(env, sc, cam, pixels=pix, label=f"tiles {width}x{height}")
+
+
 def test_opacity_extremes(env):
     sc = synth.random_scene(200, seed=8, width=48, height=48, focal=50.0)
     sc["opacity_logits"][:40] = 30.0
