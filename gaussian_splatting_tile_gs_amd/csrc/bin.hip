@@ -264,6 +264,8 @@ struct TileCountArgs {
   uint32_t* plan;       // raster plan (optional; layout in gs_internal.h)
   uint64_t capacity;
   int npass;
+  int pshift[3];        // the pair passes' digit shifts and widths (tile id bits split evenly)
+  int pbits[3];
   uint32_t* hist_pair;  // [npass][256]
 };
 constexpr int kRowGaussians = 2048;  // Gaussians per row workgroup (two per lane)
@@ -325,8 +327,8 @@ __device__ void tile_rows(const TileCountArgs& a, uint32_t rb, uint32_t* lds, ui
 // (chunks 1 ..). With one step the second sweep finds the starts still in LDS.
 // The code is loops over rows rather than unrolled: it runs once per frame, on one compute unit,
 // where straight-line code would wait on instruction fetch.
-// Histogram digits above the lowest are constant over aligned runs of 256^k tiles: a run's count
-// is the difference of the range starts at its ends, added with two LDS atomics per run.
+// Histogram digits above the lowest (shift s > 0) are constant over aligned runs of 2^s tiles: a
+// run's count is the difference of the range starts at its ends, added with two LDS atomics.
 __device__ __forceinline__ uint32_t count_class(uint32_t c) { return c ? 32u - (uint32_t)__clz(c) : 0u; }
 
 // Lanes with the same class share one LDS atomic on ctr[cls]; returns a valid lane's slot.
@@ -486,15 +488,16 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
         if (c) {
           a.ranges[2 * t] = st;
           a.ranges[2 * t + 1] = st + c;
-          atomicAdd(&s_hist[0][t & 255u], c);
+          atomicAdd(&s_hist[0][t & ((1u << a.pbits[0]) - 1u)], c);
         }
         if (valid && fits) {
-          // a run of 256^k tiles starting at t: its digit-k count starts at -start(t) and the
-          // previous run's gets start(t)
+          // a run of 2^shift_k tiles starting at t: its digit-k count starts at -start(t) and
+          // the previous run's gets start(t)
           for (int k = 1; k < a.npass; ++k) {
-            if ((t & ((1u << (8 * k)) - 1u)) == 0u) {
-              atomicSub(&s_hist[k][(t >> (8 * k)) & 255u], st);
-              if (t) atomicAdd(&s_hist[k][((t - 1u) >> (8 * k)) & 255u], st);
+            const uint32_t dm = (1u << a.pbits[k]) - 1u;
+            if ((t & ((1u << a.pshift[k]) - 1u)) == 0u) {
+              atomicSub(&s_hist[k][(t >> a.pshift[k]) & dm], st);
+              if (t) atomicAdd(&s_hist[k][((t - 1u) >> a.pshift[k]) & dm], st);
             }
           }
         }
@@ -542,7 +545,8 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
     }
   }
   if (tid == 0 && fits)  // the last run ends at P
-    for (int k = 1; k < a.npass; ++k) atomicAdd(&s_hist[k][((a.ntiles - 1u) >> (8 * k)) & 255u], (uint32_t)P);
+    for (int k = 1; k < a.npass; ++k)
+      atomicAdd(&s_hist[k][((a.ntiles - 1u) >> a.pshift[k]) & ((1u << a.pbits[k]) - 1u)], (uint32_t)P);
   __syncthreads();
   if (tid < kRadix && fits)
     for (int k = 0; k < a.npass; ++k) a.hist_pair[k * kRadix + tid] = s_hist[k][tid];
@@ -562,19 +566,25 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
 // tile-count finalizer (see above). ITEMS keys per lane: a workgroup sorts 1024 ITEMS keys
 // (4 keeps the ranking chains short for small inputs; 8 halves the workgroups, and so the
 // look-back traffic, for large ones).
+// Eight waves per SIMD (two 1024-thread workgroups per compute unit) need at most 64 VGPRs and
+// about 80 SGPRs; the scalar registers are the tighter limit, so the target is spelled out.
 template <bool FINAL, int EXTRA, int ITEMS>
-__global__ __launch_bounds__(kSortThreads) void k_onesweep(
+__global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_onesweep(
     const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, uint32_t* __restrict__ keys_out,
     uint32_t* __restrict__ vals_out, uint64_t* __restrict__ out_keys64, const uint32_t* __restrict__ depth_bits,
     uint32_t n_host, const uint64_t* __restrict__ n_dev, int shift, int bits, const uint32_t* __restrict__ hist,
     int hist_parts, int hist_stride, uint32_t* __restrict__ status, uint32_t* __restrict__ ticket,
     uint32_t n_extra, TileCountArgs targs) {
   constexpr int TILE = kSortThreads * ITEMS;
-  constexpr uint32_t kLdsWords = 2 * TILE + kSortWaves * kRadix;
+  // the per-wave digit counts share LDS with the staged keys (they are dead by then), so a
+  // workgroup of 8 keys per lane takes 64 KB and two fit on a compute unit; the extra
+  // workgroups of the depth passes get 48 KB
+  constexpr uint32_t kLdsWords = (EXTRA != 0 && 2 * TILE < 12288) ? 12288u : 2u * TILE;
+  static_assert(kSortWaves * kRadix <= 2 * TILE, "digit counts must fit in the key staging");
   __shared__ uint32_t s_mem[kLdsWords];
   uint32_t* s_keys = s_mem;
   uint32_t* s_vals = s_mem + TILE;
-  uint32_t (*s_wcnt)[kRadix] = reinterpret_cast<uint32_t (*)[kRadix]>(s_mem + 2 * TILE);  // count, then offset
+  uint32_t (*s_wcnt)[kRadix] = reinterpret_cast<uint32_t (*)[kRadix]>(s_mem);  // count, then offset
   __shared__ uint32_t s_dpre[kRadix];
   __shared__ uint32_t s_goff[kRadix];
   __shared__ uint32_t s_wsum[kSortWaves];
@@ -625,48 +635,57 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
     uint32_t pre = 0;
     if (valid) pre = s_wcnt[wave][d];
     rank[i] = pre + r;
+    // keep the rank in one register from here on (left to itself the compiler keeps the
+    // 64-bit match mask alive until the scatter, and the extra registers halve occupancy)
+    asm volatile("" : "+v"(rank[i]));
     if (valid && r == 0) s_wcnt[wave][d] = pre + (uint32_t)__popcll(m);
     __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
 
-  // ---- per digit (threads 0-255): wave offsets, tile total, publish, look back ----
+  // ---- per digit (threads below 2^bits): wave offsets, tile total, publish the aggregate ----
+  const int radix = 1 << bits;
   uint32_t tot = 0;
-  if (tid < kRadix) {
-    uint32_t c[kSortWaves];
-#pragma unroll
-    for (int w = 0; w < kSortWaves; ++w) c[w] = s_wcnt[w][tid];
-#pragma unroll
+  if (tid < radix) {
+    // four waves' counts at a time: the keys, values and ranks are still live
+#pragma unroll 4
     for (int w = 0; w < kSortWaves; ++w) {
+      const uint32_t c = s_wcnt[w][tid];
       s_wcnt[w][tid] = tot;
-      tot += c[w];
+      tot += c;
     }
     st_dev(status + (size_t)vb * kRadix + tid, (vb == 0 ? kFlagPre : kFlagAgg) | tot);
   }
   uint32_t dummy;
   const uint32_t bucket_excl = block_excl_scan256<uint32_t>(h, s_wsum, &dummy);
   const uint32_t dpre = block_excl_scan256<uint32_t>(tot, s_wsum, &dummy);
-  if (tid < kRadix) {
-    s_dpre[tid] = dpre;
+  if (tid < kRadix) s_dpre[tid] = dpre;  // 0 past the pass's digits
+  __syncthreads();
+
+  // ---- scatter to LDS in local sorted order (it needs no look-back, and frees the registers
+  // of the keys before the look-back's loads are in flight) ----
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const uint32_t d = (k[i] >> shift) & mask;
+    rank[i] += s_dpre[d] + s_wcnt[wave][d];  // the local position
+  }
+  __syncthreads();  // the digit counts are dead: their LDS takes keys
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const uint32_t idx = base + (uint32_t)(wave * 64 * ITEMS + i * 64 + lane);
+    if (idx < n) {
+      s_keys[rank[i]] = k[i];
+      s_vals[rank[i]] = v[i];
+    }
+  }
+  // ---- look back for the digits' global offsets, then out with consecutive threads ----
+  if (tid < radix) {
     uint32_t excl = 0;
     if (vb > 0) {
       excl = look_back<8, uint32_t, ~kValMask, kFlagPre, kValMask>(status + tid, vb, kRadix);
       st_dev(status + (size_t)vb * kRadix + tid, kFlagPre | (excl + tot));
     }
     s_goff[tid] = bucket_excl + excl - dpre;
-  }
-  __syncthreads();
-
-  // ---- scatter to LDS in local sorted order, then out with consecutive threads ----
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const uint32_t idx = base + (uint32_t)(wave * 64 * ITEMS + i * 64 + lane);
-    if (idx < n) {
-      const uint32_t d = (k[i] >> shift) & mask;
-      const uint32_t lp = s_dpre[d] + s_wcnt[wave][d] + rank[i];
-      s_keys[lp] = k[i];
-      s_vals[lp] = v[i];
-    }
   }
   __syncthreads();
   const uint32_t count = (n - base < (uint32_t)TILE) ? (n - base) : (uint32_t)TILE;
@@ -903,7 +922,7 @@ struct BinLayout {
   size_t ctrl, scan_status, dstatus, pstatus, tdiff, zero_end;
   size_t dhist, dkA, dvA, dkB, dvB, rec, drec, chunk_first, pkB, pvB, total;
   uint32_t nbN, nbS, nbCap, nbEmit;
-  int tile_bits, npass;
+  int tile_bits, npass, pshift[3], pbits[3];
 };
 
 BinLayout bin_layout(int32_t n, int64_t cap, const gs_camera* cam) {
@@ -914,6 +933,13 @@ BinLayout bin_layout(int32_t n, int64_t cap, const gs_camera* cam) {
   while (((int64_t)1 << tb) < ntiles) ++tb;
   L.tile_bits = tb;
   L.npass = (tb + 7) / 8;
+  // the tile-id bits split evenly over the passes (14 = 7 + 7, not 8 + 6): fewer digits per pass
+  // mean fewer look-back columns
+  for (int p = 0, sh = 0; p < L.npass; ++p) {
+    L.pbits[p] = tb / L.npass + (p < tb % L.npass ? 1 : 0);
+    L.pshift[p] = sh;
+    sh += L.pbits[p];
+  }
   L.nbN = (uint32_t)((n + kSortTile - 1) / kSortTile);
   L.nbS = (uint32_t)((n + kScanTile - 1) / kScanTile);
   L.nbCap = (uint32_t)((cap + kSortTile - 1) / kSortTile);
@@ -1032,6 +1058,10 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
   targs.plan = d_raster_plan;
   targs.capacity = (uint64_t)pair_capacity;
   targs.npass = L.npass;
+  for (int p = 0; p < 3; ++p) {
+    targs.pshift[p] = p < L.npass ? L.pshift[p] : 0;
+    targs.pbits[p] = p < L.npass ? L.pbits[p] : 0;
+  }
   targs.hist_pair = &ctrl->hist_pair[0][0];
   const uint32_t n_rows = (uint32_t)((n + kRowGaussians - 1) / kRowGaussians);
   for (int p = 0; p < 4; ++p) {
@@ -1068,8 +1098,7 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
     const unsigned grid = wide ? (L.nbCap + 1) / 2 : L.nbCap;
     bool in_A = emit_to_A;
     for (int p = 0; p < L.npass; ++p) {
-      const int shift = 8 * p;
-      const int bits = (L.tile_bits - shift) < 8 ? (L.tile_bits - shift) : 8;
+      const int shift = L.pshift[p], bits = L.pbits[p];
       const bool last = p == L.npass - 1;
       uint32_t *ki = in_A ? kA : kB, *vi = in_A ? vA : vB;
       uint32_t *ko = in_A ? kB : kA, *vo = in_A ? vB : vA;
