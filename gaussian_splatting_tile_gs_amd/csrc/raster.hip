@@ -375,6 +375,31 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
   const bool inside = px_i < cam.W && py_i < cam.H;
   const float px = (float)px_i + 0.5f, py = (float)py_i + 0.5f;
   const uint32_t start = ranges[2 * tile];
+  const uint32_t len = ranges[2 * tile + 1] - start;
+  const uint32_t chunk_end = hi < len ? hi : len;
+
+  // Stage splats [bstart, bstart + cnt) of the list: ids, evaluation records and quadrant masks in
+  // LDS, the sums zeroed; the staging thread keeps its splat's raw conic and opacity for the finish.
+  float rA = 0.0f, rB = 0.0f, rC = 0.0f, ro = 1.0f;
+  auto stage = [&](uint32_t bstart, int cnt) {
+    uint32_t qm = 0;
+    if (tid < cnt) {
+      const uint32_t g = ids[start + bstart + (uint32_t)tid];
+      s_id[tid] = g;
+      qm = load_record(g, n, means2d, conics, opac, colors, radii, tx0, ty0, s_a[tid], s_b[tid], s_c[tid]);
+      if (g < n) {
+        rA = conics[3 * g];
+        rB = conics[3 * g + 1];
+        rC = conics[3 * g + 2];
+        ro = opac[g];
+      }
+    }
+    for (int i = tid; i < cnt * 9; i += kRasterThreads) s_acc[i] = 0.0f;
+    publish_quadrant_masks(qm, tid < cnt, s_qm);
+  };
+  // a chunk of at most one batch is staged at once: its loads overlap the pixels' loads below
+  const bool single = chunk_end <= lo + (uint32_t)kBatch;
+  if (single && chunk_end > lo) stage(lo, (int)(chunk_end - lo));
 
   float T = 1.0f, gr = 0.0f, gg = 0.0f, gb = 0.0f, gS = 0.0f;
   uint32_t nc = 0;
@@ -410,18 +435,14 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
   const uint32_t max_nc = s_max < hi ? s_max : hi;
   uint32_t n_eval = 0;
 
-  for (uint32_t bend = max_nc; bend > lo;) {
+  // a staged single batch covers [lo, chunk_end), which holds [lo, max_nc)
+  for (uint32_t bend = single ? chunk_end : max_nc; bend > lo;) {
     const uint32_t bstart = bend > lo + (uint32_t)kBatch ? bend - kBatch : lo;
     const int cnt = (int)(bend - bstart);
-    __syncthreads();
-    uint32_t qm = 0;
-    if (tid < cnt) {
-      const uint32_t g = ids[start + bstart + (uint32_t)tid];
-      s_id[tid] = g;
-      qm = load_record(g, n, means2d, conics, opac, colors, radii, tx0, ty0, s_a[tid], s_b[tid], s_c[tid]);
+    if (!single) {
+      __syncthreads();
+      stage(bstart, cnt);
     }
-    for (int i = tid; i < cnt * 9; i += kRasterThreads) s_acc[i] = 0.0f;
-    publish_quadrant_masks(qm, tid < cnt, s_qm);
     __syncthreads();
     for (int w = 3; w >= 0; --w) {
       uint64_t m = uniform64(s_qm[wave][w]);  // walked from the highest set bit down
@@ -456,7 +477,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
     if (tid < cnt && s_id[tid] < n) {
       const uint32_t g = s_id[tid];
       const float* P = s_acc + tid * 9;
-      const float A = conics[3 * g], B = conics[3 * g + 1], C = conics[3 * g + 2], o = opac[g];
+      const float A = rA, B = rB, C = rC, o = ro;
       float gv[9];
       gv[0] = fmaf(A, P[0], B * P[1]);
       gv[1] = fmaf(B, P[0], C * P[1]);
