@@ -128,13 +128,13 @@ struct SplatEval {
 };
 
 __device__ __forceinline__ SplatEval eval_splat(float dx, float dy, float hA, float B2, float hC, float o) {
-  // s2 = log2(e) * sigma = hA dx^2 + hC dy^2 + B2 dx dy
-  const float s2 = fmaf(hA * dx, dx, fmaf(hC * dy, dy, (B2 * dx) * dy));
+  // s2 = log2(e) * sigma = dx (hA dx + B2 dy) + hC dy^2: five VALU operations
+  const float s2 = fmaf(fmaf(hA, dx, B2 * dy), dx, (hC * dy) * dy);
   SplatEval e;
   e.G = __builtin_amdgcn_exp2f(-s2);  // v_exp_f32; results below 2^-126 flush to 0 (alpha < 1/255)
-  const float raw = o * e.G;
+  const float raw = o * e.G;          // never NaN: o in [0, 1], G in [0, inf)
   e.capped = raw >= kAlphaMax;
-  e.alpha = e.capped ? kAlphaMax : raw;
+  e.alpha = fminf(raw, kAlphaMax);
   e.skip = (s2 < 0.0f) || (e.alpha < kAlphaMin);
   return e;
 }

@@ -134,13 +134,17 @@ __device__ __forceinline__ void blend_step(const SplatEval& e, bool act, float c
                                            float& T, float& cr, float& cg, float& cb, uint32_t& last, bool& done) {
   const bool ok = act && !done && !e.skip;
   const float nT = T * (1.0f - e.alpha);
-  const bool stop = ok && nT <= kTransmittanceMin;
-  const bool add = ok && !stop;
-  const float wgt = add ? e.alpha * T : 0.0f;
+  // nT >= 0, so comparing its bits as integers orders it like the float, and, unlike a float
+  // compare (NaN), the negation is free: one compare serves both outcomes
+  const bool low = __float_as_uint(nT) <= __float_as_uint(kTransmittanceMin);
+  const bool stop = ok && low;
+  const bool add = ok && !low;
+  const float Tn = add ? nT : T;
+  const float wgt = T - Tn;  // alpha T when added (to rounding), exactly 0 otherwise
   cr = fmaf(cr_, wgt, cr);
   cg = fmaf(cg_, wgt, cg);
   cb = fmaf(cb_, wgt, cb);
-  T = add ? nT : T;
+  T = Tn;
   last = add ? idx : last;
   done = done || stop;
 }
@@ -298,6 +302,7 @@ __device__ __forceinline__ void splat_grad(bool contrib, const SplatEval& ev, fl
   const float Ti = contrib ? T * inv : T;  // T_i, the transmittance in front of this splat
   const float gc = fmaf(gr, cr, fmaf(gg, cg, gb * cb));
   const float g_alpha = fmaf(Ti, gc, -gS * inv);  // dL/dalpha = g . (c T_i - S / (1 - alpha))
+  // alpha T_i as a product: Ti - T would save one operation but cancels for alpha near 1/255
   const float wT = contrib ? ev.alpha * Ti : 0.0f;
   gS = fmaf(gc, wT, gS);
   T = Ti;
