@@ -33,9 +33,9 @@ HBM_PEAK_GBS = 8000.0
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 
 # VALU instructions per (pixel, splat) evaluation on the kernels' main path, counted in the
-# gfx950 ISA of the built library: the blend loop body issues 60 VALU ops per two splats, the
-# backward loop body 147 per two splats (evaluation, gradient terms and wave reduction).
-VALU_PER_EVAL = {"blend": 30.0, "rbwd": 73.5}
+# gfx950 ISA of the built library: the blend loop body issues 54 VALU ops per two splats, the
+# backward loop body 143 per two splats (evaluation, gradient terms and wave reduction).
+VALU_PER_EVAL = {"blend": 27.0, "rbwd": 71.5}
 
 
 def parse():
