@@ -60,8 +60,12 @@ def kernel_bytes(name, stats):
         "bin_prep": 48.0 * N,
         "depth_sort_pass": 16.0 * N,
         "scan": 40.0 * N,
-        "emit": 8.0 * P + 16.0 * stats["visible"],
-        "pair_sort_pass": 16.0 * P + 4.0 * P / stats["pair_passes"],
+        # the emission fused with the first pair pass: depth-ordered records in, pairs out
+        # (the final pass when it is the only one: 64-bit keys, ids and the depth gather)
+        "emit_sort": 16.0 * stats["visible"] + (16.0 if stats["pair_passes"] == 0 else 8.0) * P,
+        # the other pair passes: 8 B in and 8 B out per pair; the final one writes 12 B and
+        # gathers 4 B of depth
+        "pair_sort_pass": (16.0 * P + 8.0 * P / max(1, stats["pair_passes"])) if stats["pair_passes"] else 0.0,
         "project": stats["project_bytes"],
         "loss_l1": 12.0 * stats["pixels"] * 3,
     }.get(name)
@@ -251,7 +255,7 @@ def main():
         visible = int((pipe.proj.tiles_touched > 0).sum().item())
         K = (wl.sh_degree + 1) ** 2
         stats = {"pairs": float(np.mean(pairs)), "n": wl.n, "visible": visible, "pixels": W * H,
-                 "pair_passes": max(1, per.get("pair_sort_pass", [0, 1])[1] // max(1, per.get("scan", [0, 1])[1])),
+                 "pair_passes": per.get("pair_sort_pass", [0, 0])[1] // max(1, per.get("scan", [0, 1])[1]),
                  "project_bytes": wl.n * (4 * (3 + 3 + 4 + 1 + 3 * K) + 52)}
         kernels = {}
         for name, (tot, cnt) in sorted(per.items(), key=lambda kv: -kv[1][0]):
@@ -274,7 +278,7 @@ def main():
                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(dom, wl.name), "kernel": dom,
                     "bytes_per_launch": b, "avg_us": avg_s * 1e6}
         result["roofline"] = roof
-        bin_names = ("bin_prep", "hist_reduce", "depth_sort_pass", "scan", "emit", "pair_sort_pass")
+        bin_names = ("bin_prep", "hist_reduce", "depth_sort_pass", "scan", "emit_sort", "pair_sort_pass")
         bin_s = sum(per[k][0] for k in bin_names if k in per) / 1e3 / nprof
         bin_b = sum((kernel_bytes(k, stats) or 0.0) * per[k][1] for k in bin_names if k in per) / nprof
         result["bin_sort"] = {"kernel_us_per_step": bin_s * 1e6, "bytes_per_step": bin_b,

@@ -21,13 +21,14 @@
 //                     per workgroup, wave-wide look-back): per Gaussian in depth order its first
 //                     pair position, rectangle and id; per chunk of 4096 pair positions the
 //                     Gaussian it starts in; the last workgroup publishes P
-//   5. k_emit         one workgroup per chunk of 4096 pair positions writes those (tile id, i)
-//                     pairs, however the pairs spread over Gaussians (the nearest splats, first
-//                     in depth order, cover thousands of tiles): the owner of each position is a
-//                     max-scan of the markers that staged Gaussians leave at their first
-//                     position
-//   6. ceil(bits/8) x k_onesweep  stable LSD radix sort of the pairs by tile id only; the last
-//                     pass writes the 64-bit key (tile << 32 | depth bits of i) and the id
+//   5. k_emit_sort    one workgroup per chunk of 4096 pair positions emits those (tile id, i)
+//                     pairs into LDS, however the pairs spread over Gaussians (the nearest
+//                     splats, first in depth order, cover thousands of tiles): the owner of each
+//                     position is a max-scan of the markers that staged Gaussians leave at their
+//                     first position; then it runs the first radix pass of the pairs on them
+//   6. ceil(bits/8) - 1 x k_onesweep  the remaining stable LSD radix passes of the pairs by tile
+//                     id (the tile-id bits split evenly over the passes); the last pass writes the
+//                     64-bit key (tile << 32 | depth bits of i) and the id
 // Emitting in (depth, id) order and sorting stably by tile gives exactly the (tile, depth, id)
 // order of the stable 64-bit key sort, with 1-2 passes over the pairs instead of 6. P never has
 // to reach the host: the pair kernels are sized by the capacity and their workgroups stop at the
@@ -62,7 +63,6 @@ constexpr int kScanItems = 4;
 constexpr int kScanTile = kEmitThreads * kScanItems;  // 4096 Gaussians per scan workgroup
 constexpr int kEmitPer = 4;
 constexpr int kEmitChunk = kEmitThreads * kEmitPer;   // pair positions per emit workgroup
-constexpr int kEmitWindow = 2048;                     // Gaussians staged per emission round
 constexpr int kRadix = 256;
 // Radix-pass look-back words are 32 bits: [31:30] flag (0 not ready, 1 tile aggregate,
 // 2 inclusive prefix), [29:0] count, so sorted sequences are limited to below 2^30 elements.
@@ -568,58 +568,28 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
 // look-back traffic, for large ones).
 // Eight waves per SIMD (two 1024-thread workgroups per compute unit) need at most 64 VGPRs and
 // about 80 SGPRs; the scalar registers are the tighter limit, so the target is spelled out.
-template <bool FINAL, int EXTRA, int ITEMS>
-__global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_onesweep(
-    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, uint32_t* __restrict__ keys_out,
-    uint32_t* __restrict__ vals_out, uint64_t* __restrict__ out_keys64, const uint32_t* __restrict__ depth_bits,
-    uint32_t n_host, const uint64_t* __restrict__ n_dev, int shift, int bits, const uint32_t* __restrict__ hist,
-    int hist_parts, int hist_stride, uint32_t* __restrict__ status, uint32_t* __restrict__ ticket,
-    uint32_t n_extra, TileCountArgs targs) {
+// The part of a radix pass after the load, for one tile of 1024 ITEMS keys starting at `base`
+// (ticket vb): item i of lane l of wave w is element base + 64 ITEMS w + 64 i + l (valid below n).
+// Ranks the keys with wave ballots (stable), publishes the tile's digit counts, stages the keys
+// in LDS in local sorted order, resolves the digits' global offsets by decoupled look-back and
+// writes the keys out with consecutive threads. s_mem (2 TILE words) must hold zeroed per-wave
+// digit counts in its first 16 x 256 words; h is this thread's digit count of the pass (threads
+// below 256). Every thread calls it.
+template <bool FINAL, int ITEMS>
+__device__ __forceinline__ void radix_tile(uint32_t (&k)[ITEMS], uint32_t (&v)[ITEMS], uint32_t n, uint32_t base,
+                                           uint32_t vb, int shift, int bits, uint32_t h, uint32_t* s_mem,
+                                           uint32_t* s_dpre, uint32_t* s_goff, uint32_t* s_wsum,
+                                           uint32_t* __restrict__ status, uint32_t* __restrict__ keys_out,
+                                           uint32_t* __restrict__ vals_out, uint64_t* __restrict__ out_keys64,
+                                           const uint32_t* __restrict__ depth_bits) {
   constexpr int TILE = kSortThreads * ITEMS;
-  // the per-wave digit counts share LDS with the staged keys (they are dead by then), so a
-  // workgroup of 8 keys per lane takes 64 KB and two fit on a compute unit; the extra
-  // workgroups of the depth passes get 48 KB
-  constexpr uint32_t kLdsWords = (EXTRA != 0 && 2 * TILE < 12288) ? 12288u : 2u * TILE;
-  static_assert(kSortWaves * kRadix <= 2 * TILE, "digit counts must fit in the key staging");
-  __shared__ uint32_t s_mem[kLdsWords];
   uint32_t* s_keys = s_mem;
   uint32_t* s_vals = s_mem + TILE;
   uint32_t (*s_wcnt)[kRadix] = reinterpret_cast<uint32_t (*)[kRadix]>(s_mem);  // count, then offset
-  __shared__ uint32_t s_dpre[kRadix];
-  __shared__ uint32_t s_goff[kRadix];
-  __shared__ uint32_t s_wsum[kSortWaves];
-  __shared__ uint32_t s_vb;
-
-  if (EXTRA != 0 && blockIdx.x >= gridDim.x - n_extra) {  // workgroup-uniform
-    if (EXTRA == 1) tile_rows(targs, blockIdx.x - (gridDim.x - n_extra), s_mem, kLdsWords);
-    if (EXTRA == 2) tile_finalize(targs, s_mem, kLdsWords);
-    return;
-  }
-  const uint32_t n = n_dev ? (uint32_t)*n_dev : n_host;
-  if ((uint64_t)blockIdx.x * TILE >= n) return;  // workgroup-uniform: idle workgroups take no ticket
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) s_vb = atomicAdd(ticket, 1u);
-  for (int i = tid; i < kSortWaves * kRadix; i += kSortThreads) (&s_wcnt[0][0])[i] = 0;
-  __syncthreads();
-  // exactly ceil(n / 4096) workgroups take tickets, so every ticket has base < n
-  const uint32_t vb = s_vb;
-  const uint32_t base = vb * (uint32_t)TILE;
-  if (base >= n) return;  // unreachable with a zeroed ticket; guards a stale one
   const uint32_t mask = (1u << bits) - 1u;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-
-  // ---- load (wave-striped: wave w owns [base + 256 w, base + 256 (w + 1))) and rank ----
-  uint32_t k[ITEMS], v[ITEMS], rank[ITEMS];
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const uint32_t idx = base + (uint32_t)(wave * 64 * ITEMS + i * 64 + lane);
-    const bool valid = idx < n;
-    k[i] = valid ? keys_in[idx] : 0u;
-    v[i] = valid ? vals_in[idx] : 0u;
-  }
-  uint32_t h = 0;  // the pass's histogram, read while the keys arrive
-  if (tid < kRadix)
-    for (int r = 0; r < hist_parts; ++r) h += hist[(size_t)r * hist_stride + tid];
+  uint32_t rank[ITEMS];
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     const uint32_t idx = base + (uint32_t)(wave * 64 * ITEMS + i * 64 + lane);
@@ -704,6 +674,57 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(8)
       vals_out[gp] = val;
     }
   }
+}
+
+template <bool FINAL, int EXTRA, int ITEMS>
+__global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_onesweep(
+    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, uint32_t* __restrict__ keys_out,
+    uint32_t* __restrict__ vals_out, uint64_t* __restrict__ out_keys64, const uint32_t* __restrict__ depth_bits,
+    uint32_t n_host, const uint64_t* __restrict__ n_dev, int shift, int bits, const uint32_t* __restrict__ hist,
+    int hist_parts, int hist_stride, uint32_t* __restrict__ status, uint32_t* __restrict__ ticket,
+    uint32_t n_extra, TileCountArgs targs) {
+  constexpr int TILE = kSortThreads * ITEMS;
+  // the per-wave digit counts share LDS with the staged keys (they are dead by then), so a
+  // workgroup of 8 keys per lane takes 64 KB and two fit on a compute unit; the extra
+  // workgroups of the depth passes get 48 KB
+  constexpr uint32_t kLdsWords = (EXTRA != 0 && 2 * TILE < 12288) ? 12288u : 2u * TILE;
+  static_assert(kSortWaves * kRadix <= 2 * TILE, "digit counts must fit in the key staging");
+  __shared__ uint32_t s_mem[kLdsWords];
+  uint32_t (*s_wcnt)[kRadix] = reinterpret_cast<uint32_t (*)[kRadix]>(s_mem);  // count, then offset
+  __shared__ uint32_t s_dpre[kRadix];
+  __shared__ uint32_t s_goff[kRadix];
+  __shared__ uint32_t s_wsum[kSortWaves];
+  __shared__ uint32_t s_vb;
+
+  if (EXTRA != 0 && blockIdx.x >= gridDim.x - n_extra) {  // workgroup-uniform
+    if (EXTRA == 1) tile_rows(targs, blockIdx.x - (gridDim.x - n_extra), s_mem, kLdsWords);
+    if (EXTRA == 2) tile_finalize(targs, s_mem, kLdsWords);
+    return;
+  }
+  const uint32_t n = n_dev ? (uint32_t)*n_dev : n_host;
+  if ((uint64_t)blockIdx.x * TILE >= n) return;  // workgroup-uniform: idle workgroups take no ticket
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) s_vb = atomicAdd(ticket, 1u);
+  for (int i = tid; i < kSortWaves * kRadix; i += kSortThreads) (&s_wcnt[0][0])[i] = 0;
+  __syncthreads();
+  // exactly ceil(n / 4096) workgroups take tickets, so every ticket has base < n
+  const uint32_t vb = s_vb;
+  const uint32_t base = vb * (uint32_t)TILE;
+  if (base >= n) return;  // unreachable with a zeroed ticket; guards a stale one
+  // ---- load (wave-striped: wave w owns [base + 256 w, base + 256 (w + 1))) ----
+  uint32_t k[ITEMS], v[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const uint32_t idx = base + (uint32_t)(wave * 64 * ITEMS + i * 64 + lane);
+    const bool valid = idx < n;
+    k[i] = valid ? keys_in[idx] : 0u;
+    v[i] = valid ? vals_in[idx] : 0u;
+  }
+  uint32_t h = 0;  // the pass's histogram, read while the keys arrive
+  if (tid < kRadix)
+    for (int r = 0; r < hist_parts; ++r) h += hist[(size_t)r * hist_stride + tid];
+  radix_tile<FINAL, ITEMS>(k, v, n, base, vb, shift, bits, h, s_mem, s_dpre, s_goff, s_wsum, status, keys_out,
+                           vals_out, out_keys64, depth_bits);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -819,80 +840,113 @@ __global__ __launch_bounds__(kEmitThreads) void k_scan(int32_t n, const uint32_t
 }
 
 // ---------------------------------------------------------------------------------------------
-// 5. emission: workgroup k writes pair positions [kEmitChunk k, kEmitChunk (k + 1)), whatever
-// Gaussians they belong to, so the work is the same for every workgroup
+// 5+6. emission fused with the first pair pass: the workgroup with ticket c emits pair positions
+// [4096 c, 4096 (c + 1)) into LDS, each position's owner found by a max-scan over the staged
+// Gaussians' first positions, then sorts them by the pass's digit and scatters them to the
+// pass's output. The pass's digit histogram comes from the tile-count finalizer, so the pairs
+// need not round-trip through memory before their first pass.
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kEmitThreads) void k_emit(const uint64_t* __restrict__ n_dev, int32_t n,
-                                                       const uint4* __restrict__ drec,
-                                                       const uint32_t* __restrict__ chunk_first, int32_t tiles_x,
-                                                       uint32_t* __restrict__ pkeys, uint32_t* __restrict__ pvals) {
-  __shared__ uint32_t s_wsum[kEmitWaves];
-  __shared__ uint32_t s_off[kEmitWindow];
-  __shared__ uint32_t s_tb[kEmitWindow];
-  __shared__ uint32_t s_w[kEmitWindow];
-  __shared__ uint32_t s_g[kEmitWindow];
-  __shared__ uint32_t s_owner[kEmitChunk];
+constexpr int kFuseWindow = 1024;  // Gaussians staged per emission round (one per thread)
+template <bool FINAL>
+__global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_emit_sort(
+    const uint64_t* __restrict__ n_dev, int32_t n, const uint4* __restrict__ drec,
+    const uint32_t* __restrict__ chunk_first, int32_t tiles_x, int shift, int bits,
+    const uint32_t* __restrict__ hist, uint32_t* __restrict__ status, uint32_t* __restrict__ ticket,
+    uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint64_t* __restrict__ out_keys64,
+    const uint32_t* __restrict__ depth_bits) {
+  constexpr int ITEMS = 4, TILE = kSortThreads * ITEMS;
+  static_assert(TILE == kEmitChunk && kEmitThreads == kSortThreads, "one emission chunk per sort tile");
+  static_assert(kFuseWindow == kSortThreads, "one staged Gaussian per thread");
+  __shared__ uint32_t s_mem[2 * TILE];  // the emitted pairs (keys, values), then the sort's staging
+  __shared__ uint32_t s_owner[TILE];
+  __shared__ uint32_t s_off[kFuseWindow];
+  __shared__ uint32_t s_tb[kFuseWindow];
+  __shared__ uint32_t s_w[kFuseWindow];
+  __shared__ uint32_t s_g[kFuseWindow];
+  __shared__ uint32_t s_dpre[kRadix];
+  __shared__ uint32_t s_goff[kRadix];
+  __shared__ uint32_t s_wsum[kSortWaves];
+  __shared__ uint32_t s_vb;
   const uint64_t P = *n_dev;
-  const uint64_t cs = (uint64_t)blockIdx.x * kEmitChunk;
-  if (cs >= P) return;  // workgroup-uniform
-  const int tid = threadIdx.x;
-  const uint32_t ce = (uint32_t)std::min<uint64_t>(P - cs, kEmitChunk);
-  uint32_t jw = chunk_first[blockIdx.x];  // the Gaussian (depth index) that holds position cs
+  if ((uint64_t)blockIdx.x * TILE >= P) return;  // workgroup-uniform: idle workgroups take no ticket
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) s_vb = atomicAdd(ticket, 1u);
+  __syncthreads();
+  const uint32_t vb = s_vb;
+  const uint64_t cs = (uint64_t)vb * TILE;
+  if (cs >= P) return;  // unreachable with a zeroed ticket; guards a stale one
+  const uint32_t ce = (uint32_t)(P - cs < (uint64_t)TILE ? P - cs : (uint64_t)TILE);
+  uint32_t* s_pk = s_mem;
+  uint32_t* s_pv = s_mem + TILE;
+
+  // ---- emission of positions [cs, cs + ce) into s_pk / s_pv ----
+  uint32_t jw = chunk_first[vb];  // the Gaussian (depth index) that holds position cs
   uint32_t done = 0;
-  while (done < ce) {  // workgroup-uniform; each window covers at least kEmitWindow - 1 positions
-    for (int q = tid; q < kEmitChunk; q += kEmitThreads) s_owner[q] = 0u;
+  while (done < ce) {  // workgroup-uniform; each window covers at least kFuseWindow - 1 positions
+    for (int q = tid; q < TILE; q += kSortThreads) s_owner[q] = 0u;
     __syncthreads();
-    // window of kEmitWindow Gaussians from jw; each marks its first position in [done, ce)
     const uint64_t lo = cs + done, hi = cs + ce;
-#pragma unroll
-    for (int i = 0; i < kEmitWindow / kEmitThreads; ++i) {
-      const uint32_t li = (uint32_t)(i * kEmitThreads + tid);
-      const uint64_t j = (uint64_t)jw + li;
+    {
+      const uint64_t j = (uint64_t)jw + (uint32_t)tid;
       const uint4 d = j < (uint64_t)n ? drec[j] : make_uint4(0xFFFFFFFFu, 0u, 1u, 0u);
-      s_off[li] = d.x;
-      s_tb[li] = d.y;
-      s_w[li] = d.z;
-      s_g[li] = d.w;
-      if (d.x >= lo && d.x < hi) atomicMax(&s_owner[d.x - lo], li);
+      s_off[tid] = d.x;
+      s_tb[tid] = d.y;
+      s_w[tid] = d.z;
+      s_g[tid] = d.w;
+      if (d.x >= lo && d.x < hi) atomicMax(&s_owner[d.x - lo], (uint32_t)tid);
     }
     __syncthreads();
     // positions below the last window Gaussian's start are covered by this window
-    const uint32_t last_off = s_off[kEmitWindow - 1];
-    const uint64_t cover = (uint64_t)jw + kEmitWindow - 1 < (uint64_t)n && (uint64_t)last_off < hi
+    const uint32_t last_off = s_off[kFuseWindow - 1];
+    const uint64_t cover = (uint64_t)jw + kFuseWindow - 1 < (uint64_t)n && (uint64_t)last_off < hi
                                ? (uint64_t)last_off : hi;
     const uint32_t lim = (uint32_t)(cover - cs);
     // inclusive max-scan of the markers: owner of each position
-    uint32_t v[kEmitPer];
+    uint32_t o[kEmitPer];
     uint32_t run = 0;
 #pragma unroll
     for (int q = 0; q < kEmitPer; ++q) {
-      v[q] = max(run, s_owner[tid * kEmitPer + q]);
-      run = v[q];
+      o[q] = max(run, s_owner[tid * kEmitPer + q]);
+      run = o[q];
     }
     uint32_t mx;
     const uint32_t before = block_scan1024<uint32_t>(run, 0u, s_wsum, &mx,
-                                                      [](uint32_t a, uint32_t b) { return max(a, b); });
+                                                      [](uint32_t x, uint32_t y) { return max(x, y); });
 #pragma unroll
-    for (int q = 0; q < kEmitPer; ++q) s_owner[tid * kEmitPer + q] = max(before, v[q]);
+    for (int q = 0; q < kEmitPer; ++q) s_owner[tid * kEmitPer + q] = max(before, o[q]);
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < kEmitPer; ++q) {
-      const uint32_t p = done + (uint32_t)(q * kEmitThreads + tid);
+      const uint32_t p = done + (uint32_t)(q * kSortThreads + tid);
       if (p < lim) {
         const uint32_t li = s_owner[p - done];
         const uint32_t local = (uint32_t)(cs + p - s_off[li]);
         const uint32_t ww = s_w[li];
         const uint32_t row = local / ww, col = local - row * ww;
-        const uint32_t t = s_tb[li] + row * (uint32_t)tiles_x + col;
-        pkeys[cs + p] = t;
-        pvals[cs + p] = s_g[li];
+        s_pk[p] = s_tb[li] + row * (uint32_t)tiles_x + col;
+        s_pv[p] = s_g[li];
       }
     }
     __syncthreads();
     // the next window starts at the Gaussian holding position lim (the window's last one)
-    if (lim < ce) jw += kEmitWindow - 1;
+    if (lim < ce) jw += kFuseWindow - 1;
     done = lim;
   }
+
+  // ---- the first pass over the tile's pairs ----
+  uint32_t k[ITEMS], v[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const uint32_t idx = (uint32_t)(wave * 64 * ITEMS + i * 64 + lane);
+    k[i] = idx < ce ? s_pk[idx] : 0u;
+    v[i] = idx < ce ? s_pv[idx] : 0u;
+  }
+  __syncthreads();  // s_mem now takes the per-wave digit counts
+  for (int i = tid; i < kSortWaves * kRadix; i += kSortThreads) s_mem[i] = 0u;
+  const uint32_t h = tid < kRadix ? hist[tid] : 0u;
+  __syncthreads();
+  radix_tile<FINAL, ITEMS>(k, v, (uint32_t)P, (uint32_t)cs, vb, shift, bits, h, s_mem, s_dpre, s_goff, s_wsum,
+                           status, keys_out, vals_out, out_keys64, depth_bits);
 }
 
 // The raster plan of a frame without pairs: natural tile order, no extra work items or checkpoints.
@@ -1075,31 +1129,40 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
                        (uint32_t)n, (const uint64_t*)nullptr, 8 * p, 8, hist, direct_hist ? (int)L.nbN : 1,
                        4 * kRadix, dstatus + (size_t)p * L.nbN * kRadix, &ctrl->tickets[p], n_extra, targs);
   }
-  // ping-pong of the pair sort: A = d_keys viewed as two u32 arrays of pair_capacity, B = workspace
+  // ping-pong of the pair sort: A = d_keys viewed as two u32 arrays of pair_capacity, B = workspace.
+  // The last pass writes the 64-bit keys over A, so it reads B: pass p writes B when
+  // npass - 2 - p is even, A otherwise.
   uint32_t* kA = (uint32_t*)d_keys;
   uint32_t* vA = kA ? kA + pair_capacity : nullptr;
   uint32_t *kB = (uint32_t*)(ws + L.pkB), *vB = (uint32_t*)(ws + L.pvB);
-  const bool emit_to_A = (L.npass % 2) == 0;
   {
     TimedScope ts("scan", s);
     hipLaunchKernelGGL(k_scan, dim3(L.nbS), dim3(kEmitThreads), 0, s, n, dvA, (const uint4*)(ws + L.rec),
                        (uint4*)(ws + L.drec), (uint32_t*)(ws + L.chunk_first), (uint64_t)pair_capacity, scan_status,
                        ctrl, d_num_pairs);
   }
-  if (L.nbEmit > 0) {
-    TimedScope ts("emit", s);
-    hipLaunchKernelGGL(k_emit, dim3(L.nbEmit), dim3(kEmitThreads), 0, s, &ctrl->eff_pairs, n,
-                       (const uint4*)(ws + L.drec), (const uint32_t*)(ws + L.chunk_first), tiles_x,
-                       emit_to_A ? kA : kB, emit_to_A ? vA : vB);
-  }
   if (L.nbCap > 0) {
+    auto out_A = [&](int p) { return ((L.npass - 2 - p) % 2) != 0; };
+    {
+      // emission and the first pass, one workgroup per 4096 pair positions
+      TimedScope ts("emit_sort", s);
+      const bool last = L.npass == 1;
+      auto kern = last ? k_emit_sort<true> : k_emit_sort<false>;
+      const bool oa = out_A(0);
+      hipLaunchKernelGGL(kern, dim3(L.nbCap), dim3(kSortThreads), 0, s, &ctrl->eff_pairs, n,
+                         (const uint4*)(ws + L.drec), (const uint32_t*)(ws + L.chunk_first), tiles_x, L.pshift[0],
+                         L.pbits[0], ctrl->hist_pair[0], pstatus, &ctrl->tickets[4],
+                         last ? (uint32_t*)nullptr : (oa ? kA : kB), last ? d_ids : (oa ? vA : vB),
+                         last ? d_keys : (uint64_t*)nullptr,
+                         last ? (const uint32_t*)proj->d_depths : (const uint32_t*)nullptr);
+    }
     // 8 keys per lane (8192 per workgroup) for large pair buffers
     const bool wide = pair_capacity > ((int64_t)1 << 19);
     const unsigned grid = wide ? (L.nbCap + 1) / 2 : L.nbCap;
-    bool in_A = emit_to_A;
-    for (int p = 0; p < L.npass; ++p) {
+    for (int p = 1; p < L.npass; ++p) {
       const int shift = L.pshift[p], bits = L.pbits[p];
       const bool last = p == L.npass - 1;
+      const bool in_A = out_A(p - 1);
       uint32_t *ki = in_A ? kA : kB, *vi = in_A ? vA : vB;
       uint32_t *ko = in_A ? kB : kA, *vo = in_A ? vB : vA;
       auto kern = last ? (wide ? k_onesweep<true, 0, 8> : k_onesweep<true, 0, 4>)
@@ -1110,7 +1173,6 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
                          last ? (const uint32_t*)proj->d_depths : (const uint32_t*)nullptr, 0u, &ctrl->eff_pairs,
                          shift, bits, ctrl->hist_pair[p], 1, 0, pstatus + (size_t)p * L.nbCap * kRadix,
                          &ctrl->tickets[4 + p], 0u, targs);
-      in_A = !in_A;
     }
   }
   const gs_status st = check_launch("gs_bin_and_sort");
