@@ -281,9 +281,15 @@ def main():
         bin_names = ("bin_prep", "hist_reduce", "depth_sort_pass", "scan", "emit_sort", "pair_sort_pass")
         bin_s = sum(per[k][0] for k in bin_names if k in per) / 1e3 / nprof
         bin_b = sum((kernel_bytes(k, stats) or 0.0) * per[k][1] for k in bin_names if k in per) / nprof
+        # the same time against the bytes a stable 64-bit (tile | depth) key sort with a separate
+        # count/emit/range would move (172 B per pair + 32 B per Gaussian): what a design that
+        # sorts the full keys would have to stream to finish in this time
+        ref_b = 172.0 * stats["pairs"] + 32.0 * wl.n
         result["bin_sort"] = {"kernel_us_per_step": bin_s * 1e6, "bytes_per_step": bin_b,
                               "gbs": bin_b / bin_s / 1e9 if bin_s > 0 else None,
-                              "frac_hbm": (bin_b / bin_s / 1e9) / HBM_PEAK_GBS if bin_s > 0 else None}
+                              "frac_hbm": (bin_b / bin_s / 1e9) / HBM_PEAK_GBS if bin_s > 0 else None,
+                              "key_sort_bytes_per_step": ref_b,
+                              "key_sort_equiv_frac_hbm": (ref_b / bin_s / 1e9) / HBM_PEAK_GBS if bin_s > 0 else None}
         result["evals_per_step"] = {"fwd": evals_f.item() / nprof, "bwd": evals_b.item() / nprof}
 
     if not args.no_cpu_baseline:

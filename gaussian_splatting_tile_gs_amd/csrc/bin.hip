@@ -234,14 +234,15 @@ __global__ __launch_bounds__(kSortThreads) void k_bin_prep(int32_t n, const floa
 // 2. sum of the per-workgroup depth histograms: blockIdx.x = pass, blockIdx.y = chunk of rows
 // (ctrl->hist_depth was zeroed by k_bin_prep)
 // ---------------------------------------------------------------------------------------------
-constexpr int kReduceRows = 64;
-constexpr int kDirectHistRows = 32;
+constexpr int kReduceRows = 8;       // rows per workgroup: independent loads, many workgroups
+constexpr int kDirectHistRows = 32;  // up to here each depth pass sums the rows itself
 __global__ __launch_bounds__(kRadix) void k_hist_reduce(const uint32_t* __restrict__ dhist, uint32_t nbN, Ctrl* ctrl) {
   const int p = blockIdx.x, d = threadIdx.x;
   const uint32_t r0 = blockIdx.y * kReduceRows;
-  const uint32_t r1 = (r0 + kReduceRows < nbN) ? r0 + kReduceRows : nbN;
   uint32_t s = 0;
-  for (uint32_t r = r0; r < r1; ++r) s += dhist[((size_t)r * 4 + p) * kRadix + d];
+#pragma unroll
+  for (int i = 0; i < kReduceRows; ++i)
+    if (r0 + i < nbN) s += dhist[((size_t)(r0 + i) * 4 + p) * kRadix + d];
   if (s) atomicAdd(&ctrl->hist_depth[p][d], s);
 }
 
@@ -720,9 +721,22 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(8)
     k[i] = valid ? keys_in[idx] : 0u;
     v[i] = valid ? vals_in[idx] : 0u;
   }
-  uint32_t h = 0;  // the pass's histogram, read while the keys arrive
-  if (tid < kRadix)
-    for (int r = 0; r < hist_parts; ++r) h += hist[(size_t)r * hist_stride + tid];
+  // the pass's histogram, read while the keys arrive: the sum of hist_parts rows, four threads per
+  // digit each taking every fourth row, combined in the (not yet used) value staging of s_mem
+  uint32_t h = 0;
+  if (hist_parts == 1) {
+    if (tid < kRadix) h = hist[tid];
+  } else {
+    uint32_t part = 0;
+    for (int r = tid >> 8; r < hist_parts; r += kSortThreads / kRadix) part += hist[(size_t)r * hist_stride + (tid & (kRadix - 1))];
+    uint32_t* s_part = s_mem + TILE;
+    s_part[tid] = part;
+    __syncthreads();
+    if (tid < kRadix) {
+#pragma unroll
+      for (int q = 0; q < kSortThreads / kRadix; ++q) h += s_part[q * kRadix + tid];
+    }
+  }
   radix_tile<FINAL, ITEMS>(k, v, n, base, vb, shift, bits, h, s_mem, s_dpre, s_goff, s_wsum, status, keys_out,
                            vals_out, out_keys64, depth_bits);
 }
@@ -1094,7 +1108,9 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
                        proj->d_means2d, proj->d_radii, tiles_x, tiles_y, (uint4*)(ws + L.rec), dkA, dvA, dhist,
                        L.nbN, (uint32_t*)(ws + L.ctrl), zero_words, d_tile_ranges, (size_t)(2 * ntiles));
   }
-  // up to kDirectHistRows workgroups, each depth pass sums the per-workgroup histograms itself
+  // up to kDirectHistRows prep workgroups, each depth pass sums the per-workgroup histograms itself
+  // (one launch fewer); beyond, every pass workgroup would re-read too many rows, and
+  // k_hist_reduce sums them once
   const bool direct_hist = L.nbN <= (uint32_t)kDirectHistRows;
   if (!direct_hist) {
     TimedScope ts("hist_reduce", s);
