@@ -2,7 +2,7 @@
 
 A step is one pass of the whole hot path for one camera: gs_project -> gs_bin_and_sort ->
 gs_rasterize_fwd -> gs_loss_l1 (L1 gradient against the camera's target image) ->
-gs_rasterize_bwd. Steps cycle through the workload's cameras; all inputs (Gaussians, cameras,
+gs_rasterize_bwd (with --optimizer, then gs_adam_step). Steps cycle through the workload's cameras; all inputs (Gaussians, cameras,
 target images) are resident in HBM before the timed region. The default workload is the
 30,000-Gaussian distillation student at 1280x720 over 60 ring cameras, with target images
 rendered once (by the forward path) from a seeded 300,000-Gaussian teacher.
@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--optimizer", action="store_true",
+                    help="a training step: each step also takes an Adam step on the raw parameters")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the timed steps, copy a buffer of this many MiB 5 times (a plain copy "
                          "kernel of known size, to scale HBM byte counters)")
@@ -138,6 +140,28 @@ def cpu_baseline(wl, scene, cams_d, target_of, seconds):
             "sample": sample, "measured_seconds": round(measured, 3), "frame_seconds": round(frame_s, 3)}
 
 
+def adam_roofline(gs, torch, params, grads, wl, launches=50):
+    """The Adam kernel on copies of the parameters: 16 B read (p, g, m, v) and 12 B written
+    (p, m, v) per value, against its average launch time from the library's HIP events."""
+    p = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in params.items()}
+    F = gs.gs_adam_state_floats(wl.n, wl.sh_degree)
+    m = torch.zeros(F, device="cuda")
+    v = torch.zeros(F, device="cuda")
+    cfg = gs.adam_config()
+    gs.gs_adam_step(wl.n, wl.sh_degree, 1, cfg, p, grads, m, v)
+    torch.cuda.synchronize()
+    gs.gs_timing_enable(True)
+    for t in range(launches):
+        gs.gs_adam_step(wl.n, wl.sh_degree, t + 2, cfg, p, grads, m, v)
+    torch.cuda.synchronize()
+    recs = [ms for name, ms in gs.gs_timing_collect(1 << 12) if name == "adam"]
+    gs.gs_timing_enable(False)
+    avg_s = sum(recs) / len(recs) / 1e3
+    b = 28.0 * wl.n * (11 + 3 * (wl.sh_degree + 1) ** 2)  # the values, not the state's padding
+    return {"kernel": "adam", "bound": "hbm", "bytes_per_launch": b, "avg_us": avg_s * 1e6,
+            "achieved": b / avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": b / avg_s / 1e9 / HBM_PEAK_GBS}
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -179,14 +203,18 @@ def main():
         pipe.project(cam)
         pairs.append(pipe.bin(cam))
     need = max(pairs)
-    pipe.reserve_pairs(int(need * 1.1) + 1024)
+    # with the optimizer the scene drifts, so leave more room
+    pipe.reserve_pairs(int(need * (1.5 if args.optimizer else 1.1)) + 1024)
     ncam = len(cams)
+    adam_cfg = gs.adam_config()
 
     def step(i):
         # no host wait anywhere in a step: the pair buffers already hold every camera's pairs
         c = i % ncam
         if wl.backward:
             pipe.iteration(cams[c], targets[c], wait=False)
+            if args.optimizer:
+                pipe.adam_step(adam_cfg)
         else:
             pipe.project(cams[c])
             pipe.bin(cams[c], wait=False)
@@ -212,11 +240,18 @@ def main():
     its = args.steps / elapsed
     log(f"timed {args.steps} steps: {1e3 * elapsed / args.steps:.4f} ms/step")
     last = (args.warmup + args.steps - 1) % ncam
-    assert int(pipe.num_pairs_dev.item()) == pairs[last] <= pipe.capacity, "pair count changed between runs"
-    steps_pairs = sum(pairs[(args.warmup + i) % ncam] for i in range(args.steps))
+    if args.optimizer:
+        # the scene moved: every camera's pairs must still fit the buffers the steps ran with
+        P_last = int(pipe.num_pairs_dev.item())
+        assert P_last <= pipe.capacity, "pair buffers overflowed"
+        steps_pairs = args.steps * P_last
+    else:
+        assert int(pipe.num_pairs_dev.item()) == pairs[last] <= pipe.capacity, "pair count changed between runs"
+        steps_pairs = sum(pairs[(args.warmup + i) % ncam] for i in range(args.steps))
 
     result = {
-        "metric": "fwd+bwd iterations/sec and Mpix/s at 30k Gaussians 1280x720; sorted pairs/sec",
+        "metric": "fwd+bwd iterations/sec and Mpix/s at 30k Gaussians 1280x720; sorted pairs/sec"
+                  + (" (training steps: fwd+bwd+Adam)" if args.optimizer else ""),
         "value": its, "unit": "iterations/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": 1e3 * elapsed / args.steps, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
@@ -291,6 +326,7 @@ def main():
                               "key_sort_bytes_per_step": ref_b,
                               "key_sort_equiv_frac_hbm": (ref_b / bin_s / 1e9) / HBM_PEAK_GBS if bin_s > 0 else None}
         result["evals_per_step"] = {"fwd": evals_f.item() / nprof, "bwd": evals_b.item() / nprof}
+        result["optimizer"] = adam_roofline(gs, torch, params, pipe.grads, wl)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a pixel sample")

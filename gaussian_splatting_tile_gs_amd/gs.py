@@ -41,6 +41,11 @@ class GsProjected(ctypes.Structure):
                 ("d_tiles_touched", ctypes.c_void_p)]
 
 
+class GsAdamConfig(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_float) for k in ("lr_means", "lr_log_scales", "lr_quats", "lr_opacity", "lr_sh_dc",
+                                               "lr_sh_rest", "beta1", "beta2", "eps", "size_penalty")]
+
+
 _lib = None
 
 
@@ -65,6 +70,8 @@ def load():
         "gs_rasterize_bwd": (i32, [i32, i32, P, P, P, P, P, cam_p, proj_p, P, P, P, P, P, P, P, P, sz, P, P, P, P, P,
                                    P, P, P]),
         "gs_loss_l1": (i32, [i32, i32, P, P, P, P, P]),
+        "gs_adam_state_floats": (sz, [i32, i32]),
+        "gs_adam_step": (i32, [i32, i32, i32, ctypes.POINTER(GsAdamConfig)] + [P] * 12 + [P]),
         "gs_status_string": (ctypes.c_char_p, [i32]),
         "gs_last_error": (ctypes.c_char_p, []),
         "gs_timing_enable": (i32, [i32]),
@@ -193,6 +200,25 @@ def gs_timing_collect(max_records=4096):
 
 
 # ---- buffers ------------------------------------------------------------------------------------
+def adam_config(lr_means=1.6e-4, lr_log_scales=5e-3, lr_quats=1e-3, lr_opacity=2.5e-2, lr_sh_dc=2.5e-3,
+                lr_sh_rest=2.5e-3 / 20.0, beta1=0.9, beta2=0.999, eps=1e-15, size_penalty=0.0) -> GsAdamConfig:
+    """Adam settings; the defaults are 3DGS's per-parameter rates (means: times the scene extent)."""
+    return GsAdamConfig(lr_means, lr_log_scales, lr_quats, lr_opacity, lr_sh_dc, lr_sh_rest, beta1, beta2, eps,
+                        size_penalty)
+
+
+def gs_adam_state_floats(n, sh_degree) -> int:
+    return int(load().gs_adam_state_floats(n, sh_degree))
+
+
+def gs_adam_step(n, sh_degree, step, cfg: GsAdamConfig, params: dict, grads: dict, m, v, stream=None):
+    """One Adam step on params (updated in place) from grads; m, v: the moment buffers."""
+    _check(load().gs_adam_step(n, sh_degree, step, ctypes.byref(cfg),
+                               *[_ptr(params[k]) for k in ("means", "log_scales", "quats", "opacity_logits", "sh")],
+                               *[_ptr(grads[k]) for k in ("means", "log_scales", "quats", "opacity_logits", "sh")],
+                               _ptr(m), _ptr(v), _stream(stream)))
+
+
 @dataclass
 class Projected:
     means2d: torch.Tensor
@@ -324,3 +350,15 @@ class Pipeline:
         self.forward(cam, stream=stream)
         self.loss_l1(target, stream=stream)
         self.backward(cam, stream=stream)
+
+    def adam_step(self, cfg: GsAdamConfig, stream=None):
+        """Adam on the raw parameters (in place) from the last backward's gradients. The moment
+        buffers are allocated (zeroed) at the first call and carried between calls."""
+        if getattr(self, "_adam_m", None) is None:
+            f = gs_adam_state_floats(self.n, self.p["sh_degree"])
+            self._adam_m = torch.zeros(max(f, 1), device=self.device)
+            self._adam_v = torch.zeros(max(f, 1), device=self.device)
+            self._adam_t = 0
+        self._adam_t += 1
+        gs_adam_step(self.n, self.p["sh_degree"], self._adam_t, cfg, self.p, self.grads, self._adam_m, self._adam_v,
+                     stream)

@@ -203,6 +203,40 @@ gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float* d_means, c
 gs_status gs_loss_l1(int32_t width, int32_t height, const float* d_image, const float* d_target,
                      float* d_dL_dimage, float* d_loss, void* stream);
 
+/*
+ * gs_adam_step -- one optimizer step on the raw parameters: Adam (Kingma and Ba 2015, in the form
+ * torch.optim.Adam uses, which the fitting loop of section 7 of the PyTorch lesson calls) with a
+ * learning rate per group (the lesson lists per-parameter rates for 3DGS training), plus the
+ * splat-size penalty of the distillation write-up ("The backward pass I deleted": a loss term on
+ * splat size; its form there is unstated and read here as size_penalty * mean over Gaussians of
+ * sum_j exp(l_j), which adds size_penalty * exp(l_j) / n to dL/dl_j before the update).
+ * Per value: m <- b1 m + (1 - b1) g, v <- b2 v + (1 - b2) g^2,
+ *            p <- p - lr / (1 - b1^step) * m / (sqrt(v) / sqrt(1 - b2^step) + eps).
+ * Inputs: n, sh_degree and the raw parameter arrays as in gs_project (updated in place), the
+ *   gradients of gs_rasterize_bwd (same layouts), step >= 1 (the count of steps so far, this one
+ *   included), cfg (host). SH band 0 (the first 3 values of each Gaussian's [K,3] block) takes
+ *   lr_sh_dc, the other bands lr_sh_rest.
+ * State: d_m, d_v (device, gs_adam_state_floats(n, sh_degree) floats each, zero before step 1,
+ *   owned by the caller and carried between steps), laid out as means [n,3], log_scales [n,3],
+ *   quats [n,4], opacity_logits [n], sh [n,K,3] in that order, each group starting at a float
+ *   offset that is a multiple of 64 (the previous groups' sizes, each rounded up to 64 floats).
+ *   Groups whose arrays are 16-byte aligned and hold a multiple of 4 values take a float4 path.
+ * Errors: GS_ERR_INVALID_ARG (n < 0, sh_degree outside 0..3, step < 1, a NULL pointer with
+ *   n > 0, a negative or non-finite rate or penalty, a beta outside [0, 1), eps <= 0),
+ *   GS_ERR_LIMIT (3 K n >= 2^31).
+ */
+typedef struct {
+  float lr_means, lr_log_scales, lr_quats, lr_opacity, lr_sh_dc, lr_sh_rest;
+  float beta1, beta2, eps;
+  float size_penalty;
+} gs_adam_config;
+size_t gs_adam_state_floats(int32_t n, int32_t sh_degree);
+gs_status gs_adam_step(int32_t n, int32_t sh_degree, int32_t step, const gs_adam_config* cfg, float* d_means,
+                       float* d_log_scales, float* d_quats, float* d_opacity_logits, float* d_sh,
+                       const float* d_grad_means, const float* d_grad_log_scales, const float* d_grad_quats,
+                       const float* d_grad_opacity_logits, const float* d_grad_sh, float* d_m, float* d_v,
+                       void* stream);
+
 /* Human-readable name of a status, and a thread-local description of the last non-OK return. */
 const char* gs_status_string(gs_status s);
 const char* gs_last_error(void);

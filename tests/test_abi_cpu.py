@@ -53,3 +53,10 @@ def test_host_only_helpers(lib):
     small = lib.gs_bin_workspace_bytes(1000, 10000, ctypes.byref(cam))
     big = lib.gs_bin_workspace_bytes(1000, 1000000, ctypes.byref(cam))
     assert 0 < small < big
+    lib.gs_adam_state_floats.restype = ctypes.c_size_t
+    lib.gs_adam_state_floats.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    # groups of 3n, 3n, 4n, n and 3Kn values, each rounded up to 64 floats
+    for n, deg in ((1000, 0), (1001, 3), (1, 1)):
+        sizes = [3 * n, 3 * n, 4 * n, n, 3 * (deg + 1) ** 2 * n]
+        assert lib.gs_adam_state_floats(n, deg) == sum(-(-c // 64) * 64 for c in sizes)
+    assert lib.gs_adam_state_floats(0, 0) == 0 and lib.gs_adam_state_floats(10, 4) == 0
