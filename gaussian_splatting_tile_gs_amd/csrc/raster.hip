@@ -11,8 +11,8 @@
 //  - one 256-thread workgroup (4 wave64) per 16 x 16 tile, one pixel per thread, wave q owning
 //    the 8 x 8 quadrant q; Gaussians are staged 256 at a time in LDS as pre-scaled records (every
 //    lane then reads the same record: an LDS broadcast, no bank conflicts);
-//  - the loaders mark which quadrants each staged splat's pixel box reaches (64-lane ballots into
-//    four 256-bit masks); a wave walks only its mask's set bits, with a wave-uniform scalar loop,
+//  - the loaders mark which quadrants each staged splat's ellipse reaches at alpha >= 1/255
+//    (64-lane ballots into four 256-bit masks); a wave walks only its mask's set bits, with a wave-uniform scalar loop,
 //    and a predicated (branch-free) body;
 //  - a wave leaves the batch as soon as all 64 of its pixels are done (wave-uniform test), the
 //    workgroup stops loading batches when all 256 are (__syncthreads_count);
@@ -36,8 +36,9 @@ static_assert(kPlanMinChunk % kBatch == 0, "chunk boundaries must fall on batch 
 
 // Staged splat record: (mx, my, hA, hC), (B2, o, r, g), b. hA = A/2 log2e, B2 = B log2e,
 // hC = C/2 log2e, so that log2(e) sigma = hA dx^2 + hC dy^2 + B2 dx dy. Also returns the 4-bit
-// set of 8x8 quadrants of the tile that the splat's pixel box (radii + 1 px) reaches: outside
-// that box alpha < 1/255 at every pixel centre, so a quadrant it misses skips the splat anyway.
+// set of 8x8 quadrants of the tile where the splat can reach alpha >= 1/255 at some pixel
+// centre: the quadrant must meet the splat's pixel box (radii + 1 px) and its ellipse at that
+// level; a quadrant outside either skips the splat at every pixel anyway.
 // An id >= n (impossible for a well-formed sorted list) loads a record that never contributes.
 __device__ __forceinline__ uint32_t load_record(uint32_t g, uint32_t n, const float* __restrict__ means2d,
                                                 const float* __restrict__ conics, const float* __restrict__ opac,
@@ -56,11 +57,32 @@ __device__ __forceinline__ uint32_t load_record(uint32_t g, uint32_t n, const fl
   b = make_float4(kLog2e * B, opac[g], colors[3 * g], colors[3 * g + 1]);
   c = colors[3 * g + 2];
   const float rx = (float)r.x + 1.0f, ry = (float)r.y + 1.0f;
+  // Exact test of the splat's ellipse against each quadrant: the minimum over the quadrant's box
+  // of pixel centres of s2 = log2(e) sigma (a positive definite quadratic in the offset, so the
+  // minimum is 0 inside the box and otherwise lies on an edge, where it is a 1D quadratic) must
+  // not exceed log2(255 o), else alpha < 1/255 at every pixel centre of the quadrant. The slack
+  // (0.02 + 4e-6 times the size of the quadratic's terms over the tile) is far above the fp32
+  // rounding of both this bound and the evaluation's s2, so no contributing splat is dropped.
+  const float qa = a.z, qb = b.x, qc = a.w;  // hA, B2, hC
+  const float ia = 0.5f / qa, ic = 0.5f / qc;
+  const float ex0 = tx0 + 0.5f - m.x, ey0 = ty0 + 0.5f - m.y;  // offsets of the tile's first centre
+  const float X = fmaxf(fabsf(ex0), fabsf(ex0 + 15.0f)), Y = fmaxf(fabsf(ey0), fabsf(ey0 + 15.0f));
+  const float terms = fmaf(qa * X, X, fmaf(fabsf(qb) * X, Y, (qc * Y) * Y));
+  const float lim = __log2f(255.0f * b.y) + fmaf(4e-6f, terms, 0.02f);
+  auto q2 = [&](float x, float y) { return fmaf(fmaf(qa, x, qb * y), x, (qc * y) * y); };
   uint32_t qm = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const float x_lo = tx0 + (float)((q & 1) * 8) + 0.5f, y_lo = ty0 + (float)((q >> 1) * 8) + 0.5f;
-    const bool hit = (m.x + rx >= x_lo) && (m.x - rx <= x_lo + 7.0f) && (m.y + ry >= y_lo) && (m.y - ry <= y_lo + 7.0f);
+    const bool box = (m.x + rx >= x_lo) && (m.x - rx <= x_lo + 7.0f) && (m.y + ry >= y_lo) && (m.y - ry <= y_lo + 7.0f);
+    const float x0 = x_lo - m.x, x1 = x0 + 7.0f, y0 = y_lo - m.y, y1 = y0 + 7.0f;
+    // on the edge x = e the minimiser is y = -B2 e / (2 hC), clamped; likewise on y = e
+    const float s_l = q2(x0, fminf(fmaxf(-qb * x0 * ic, y0), y1));
+    const float s_r = q2(x1, fminf(fmaxf(-qb * x1 * ic, y0), y1));
+    const float s_t = q2(fminf(fmaxf(-qb * y0 * ia, x0), x1), y0);
+    const float s_b = q2(fminf(fmaxf(-qb * y1 * ia, x0), x1), y1);
+    const bool in = x0 <= 0.0f && x1 >= 0.0f && y0 <= 0.0f && y1 >= 0.0f;
+    const bool hit = box && (in || fminf(fminf(s_l, s_r), fminf(s_t, s_b)) <= lim);
     qm |= hit ? (1u << q) : 0u;
   }
   return qm;
