@@ -358,6 +358,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
     const float* __restrict__ colors, const int32_t* __restrict__ radii, DevCamera cam,
     const float* __restrict__ final_T, const uint32_t* __restrict__ n_contrib, const float* __restrict__ dL_dimage,
     float* __restrict__ g2d, unsigned long long* __restrict__ eval_count) {
+  // g2d is [9, n]: component c of splat g at c * n + g
   __shared__ float4 s_a[kBatch];
   __shared__ float4 s_b[kBatch];
   __shared__ float s_c[kBatch];
@@ -515,10 +516,10 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
       gv[6] = P[6];
       gv[7] = P[7];
       gv[8] = P[8];
-      float* dst = g2d + (size_t)g * 9;
+      // one plane per component: the nine atomics of a lane go to nine different cache lines
 #pragma unroll
       for (int c = 0; c < 9; ++c)
-        if (gv[c] != 0.0f) unsafeAtomicAdd(dst + c, gv[c]);
+        if (gv[c] != 0.0f) unsafeAtomicAdd(g2d + (size_t)c * n + g, gv[c]);
     }
     bend = bstart;
   }
@@ -585,7 +586,7 @@ __global__ __launch_bounds__(256) void k_pbwd(
   for (int i = 0; i < K * 3; ++i) gsh[i] = 0.0;
   double G9[9];
 #pragma unroll
-  for (int c = 0; c < 9; ++c) G9[c] = (double)g2d[(size_t)g * 9 + c];
+  for (int c = 0; c < 9; ++c) G9[c] = (double)g2d[(size_t)c * n + g];  // [9, n]
 
   const bool drawn = tiles_touched[g] > 0;
   if (drawn) {
