@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="the bitwise-reproducible backward (gs_rasterize_bwd_deterministic)")
     ap.add_argument("--optimizer", action="store_true",
                     help="a training step: each step also takes an Adam step on the raw parameters")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -198,6 +200,7 @@ def main():
     log(f"{wl.name}: {len(cams)} target images rendered from the {teacher['means'].shape[0]}-Gaussian teacher")
 
     pipe = gs.Pipeline(params, W, H, pair_capacity=1 << 16)
+    pipe.deterministic = args.deterministic
     pairs = []
     for cam in cams:  # size the pair buffers for every camera
         pipe.project(cam)
@@ -251,7 +254,8 @@ def main():
 
     result = {
         "metric": "fwd+bwd iterations/sec and Mpix/s at 30k Gaussians 1280x720; sorted pairs/sec"
-                  + (" (training steps: fwd+bwd+Adam)" if args.optimizer else ""),
+                  + (" (training steps: fwd+bwd+Adam)" if args.optimizer else "")
+                  + (" (deterministic backward)" if args.deterministic else ""),
         "value": its, "unit": "iterations/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": 1e3 * elapsed / args.steps, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp32", "data": "synthetic",

@@ -24,6 +24,8 @@
 //    per (tile, splat) with global fp32 atomics.
 // Both raster kernels evaluate a splat with the same inline eval_splat, so the backward takes
 // exactly the forward's skip decisions.
+#include <type_traits>
+
 #include "project_core.h"
 
 namespace gs {
@@ -295,6 +297,7 @@ __device__ __forceinline__ float dppx(float x) {
 // row_ror:8 exchange splits each row between two terms; three DPP adds finish each 8-lane group,
 // so lane 8t holds term t: 18 VALU ops for eight terms, and the eight LDS atomics hit distinct
 // addresses. Term 8 is summed with row shifts and row broadcasts into lane 63.
+template <bool STORE>
 __device__ __forceinline__ void reduce9_to_lds(const float* v, float* acc, int lane) {
   float u[4];
 #pragma unroll
@@ -307,8 +310,25 @@ __device__ __forceinline__ void reduce9_to_lds(const float* v, float* acc, int l
   x = x + dppx<0x4E>(x);                                 // quad_perm [2,3,0,1]: l <-> l ^ 2
   x = x + dppx<0xB1>(x);                                 // quad_perm [1,0,3,2]: l <-> l ^ 1
   const float y = wave_sum_lane63(v[8]);
-  if ((lane & 7) == 0) unsafeAtomicAdd(acc + (lane >> 3), x);
-  if (lane == 63) unsafeAtomicAdd(acc + 8, y);
+  if (STORE) {  // the wave's own slot: plain stores
+    if ((lane & 7) == 0) acc[lane >> 3] = x;
+    if (lane == 63) acc[8] = y;
+  } else {
+    if ((lane & 7) == 0) unsafeAtomicAdd(acc + (lane >> 3), x);
+    if (lane == 63) unsafeAtomicAdd(acc + 8, y);
+  }
+}
+
+// Slot of the pair (Gaussian g, tile (tx, ty)) in the per-pair gradient records: the pairs of a
+// Gaussian are contiguous from base[g] (the exclusive prefix sum of tiles_touched in id order),
+// in row-major order over its tile rectangle (the rectangle of the projection and the emitter).
+__device__ __forceinline__ uint32_t pair_slot(uint32_t g, const float* __restrict__ means2d,
+                                              const int32_t* __restrict__ radii, const uint32_t* __restrict__ base,
+                                              int tx, int ty, int32_t tiles_x, int32_t tiles_y) {
+  const float2 m = *reinterpret_cast<const float2*>(means2d + 2 * g);
+  const int2 r = *reinterpret_cast<const int2*>(radii + 2 * g);
+  const TileRect rc = tile_rect(m.x, m.y, (float)r.x, (float)r.y, tiles_x, tiles_y);
+  return base[g] + (uint32_t)((ty - rc.y0) * (rc.x1 - rc.x0) + (tx - rc.x0));
 }
 
 // Per-lane gradient terms of one splat for one pixel, back to front: consumes T (the
@@ -349,16 +369,27 @@ __device__ __forceinline__ void splat_grad(bool contrib, const SplatEval& ev, fl
 // [c L, (c + 1) L) of a tile's list. An inner chunk starts from the transmittance stored after
 // it and from S = T_final background + the colour that every later chunk added (summed back to
 // front, like the sums of the whole-tile walk: a sum of the terms, never a difference).
+// Where the 2D gradient of a (tile, splat) pair goes (MODE):
+//   kBwdAtomic  added to g2d [9, n] with global fp32 atomics;
+//   kBwdRecords written to its own slot of rec [rec_cap, 9] (pair_slot), summed per Gaussian later;
+//   kBwdDeterministic  as kBwdRecords, and the four waves' sums of a splat are kept apart in LDS
+//               (per 64-splat group, with a barrier after each group) and added in wave order,
+//               so every floating-point sum has a fixed order: bitwise-reproducible gradients.
+// With records, the slots of the pairs a chunk does not stage (behind every pixel's last
+// contributor) keep the zeros the records were cleared to before the launch.
 // ---------------------------------------------------------------------------------------------
-template <bool COUNT>
+constexpr int kBwdAtomic = 0, kBwdRecords = 1, kBwdDeterministic = 2;
+template <bool COUNT, int MODE>
 __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
     uint32_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ plan, uint32_t ntiles,
     const float4* __restrict__ ckpt, const uint32_t* __restrict__ ids,
     const float* __restrict__ means2d, const float* __restrict__ conics, const float* __restrict__ opac,
     const float* __restrict__ colors, const int32_t* __restrict__ radii, DevCamera cam,
     const float* __restrict__ final_T, const uint32_t* __restrict__ n_contrib, const float* __restrict__ dL_dimage,
-    float* __restrict__ g2d, unsigned long long* __restrict__ eval_count) {
-  // g2d is [9, n]: component c of splat g at c * n + g
+    float* __restrict__ g2d, const uint32_t* __restrict__ pair_base, float* __restrict__ rec, uint32_t rec_cap,
+    unsigned long long* __restrict__ eval_count) {
+  // g2d is [9, n]: component c of splat g at c * n + g; rec is [rec_cap, 9] (a pair's 36 B together)
+  constexpr bool REC = MODE != kBwdAtomic, DET = MODE == kBwdDeterministic;
   __shared__ float4 s_a[kBatch];
   __shared__ float4 s_b[kBatch];
   __shared__ float s_c[kBatch];
@@ -409,6 +440,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
   // Stage splats [bstart, bstart + cnt) of the list: ids, evaluation records and quadrant masks in
   // LDS, the sums zeroed; the staging thread keeps its splat's raw conic and opacity for the finish.
   float rA = 0.0f, rB = 0.0f, rC = 0.0f, ro = 1.0f;
+  uint32_t rslot = 0;
   auto stage = [&](uint32_t bstart, int cnt) {
     uint32_t qm = 0;
     if (tid < cnt) {
@@ -420,10 +452,38 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
         rB = conics[3 * g + 1];
         rC = conics[3 * g + 2];
         ro = opac[g];
+        if (REC) rslot = pair_slot(g, means2d, radii, pair_base, tx, ty, cam.tiles_x, cam.tiles_y);
       }
     }
-    for (int i = tid; i < cnt * 9; i += kRasterThreads) s_acc[i] = 0.0f;
+    if (!DET)
+      for (int i = tid; i < cnt * 9; i += kRasterThreads) s_acc[i] = 0.0f;
     publish_quadrant_masks(qm, tid < cnt, s_qm);
+  };
+  // the 2D gradient of staged splat tid from its nine sums P, to g2d or its record slot
+  auto finish = [&](const float* P) {
+    const uint32_t g = s_id[tid];
+    const float A = rA, B = rB, C = rC, o = ro;
+    float gv[9];
+    gv[0] = fmaf(A, P[0], B * P[1]);
+    gv[1] = fmaf(B, P[0], C * P[1]);
+    gv[2] = 0.5f * P[2];
+    gv[3] = P[3];
+    gv[4] = 0.5f * P[4];
+    gv[5] = -P[5] / o;
+    gv[6] = P[6];
+    gv[7] = P[7];
+    gv[8] = P[8];
+    if (REC) {
+      if (rslot < rec_cap) {
+#pragma unroll
+        for (int c = 0; c < 9; ++c) rec[(size_t)rslot * 9 + c] = gv[c];
+      }
+    } else {
+      // one plane per component: the nine atomics of a lane go to nine different cache lines
+#pragma unroll
+      for (int c = 0; c < 9; ++c)
+        if (gv[c] != 0.0f) unsafeAtomicAdd(g2d + (size_t)c * n + g, gv[c]);
+    }
   };
   // a chunk of at most one batch is staged at once: its loads overlap the pixels' loads below
   const bool single = chunk_end <= lo + (uint32_t)kBatch;
@@ -473,6 +533,12 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
     }
     __syncthreads();
     for (int w = 3; w >= 0; --w) {
+      // DET: this wave's sums of group w's 64 splats, zeroed first (row `lane` per lane)
+      float* part = s_acc + (size_t)wave * 64 * 9;
+      if (DET) {
+#pragma unroll
+        for (int c = 0; c < 9; ++c) part[lane * 9 + c] = 0.0f;
+      }
       uint64_t m = uniform64(s_qm[wave][w]);  // walked from the highest set bit down
       while (m) {
         const int bit0 = 63 - __builtin_clzll(m);
@@ -496,31 +562,35 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
         float v0[9], v1[9];
         splat_grad(c0, e0, dx0, dy0, b0.z, b0.w, cb0, gr, gg, gb, T, gS, v0);
         splat_grad(c1, e1, dx1, dy1, b1.z, b1.w, cb1, gr, gg, gb, T, gS, v1);
-        if (__any(c0)) reduce9_to_lds(v0, s_acc + k0 * 9, lane);
-        if (__any(c1)) reduce9_to_lds(v1, s_acc + k1 * 9, lane);
+        if (DET) {
+          if (__any(c0)) reduce9_to_lds<true>(v0, part + (k0 - w * 64) * 9, lane);
+          if (__any(c1)) reduce9_to_lds<true>(v1, part + (k1 - w * 64) * 9, lane);
+        } else {
+          if (__any(c0)) reduce9_to_lds<false>(v0, s_acc + k0 * 9, lane);
+          if (__any(c1)) reduce9_to_lds<false>(v1, s_acc + k1 * 9, lane);
+        }
+      }
+      if (DET) {
+        // group w is staged by wave w: its threads add the four waves' sums in wave order
+        __syncthreads();
+        if (wave == w && tid < cnt && s_id[tid] < n) {
+          float P[9];
+#pragma unroll
+          for (int c = 0; c < 9; ++c) {
+            float acc = s_acc[(0 * 64 + lane) * 9 + c];
+            acc += s_acc[(1 * 64 + lane) * 9 + c];
+            acc += s_acc[(2 * 64 + lane) * 9 + c];
+            acc += s_acc[(3 * 64 + lane) * 9 + c];
+            P[c] = acc;
+          }
+          finish(P);
+        }
+        __syncthreads();
       }
     }
     __syncthreads();
-    // finish the 2D gradient of each staged splat from its nine sums and add it to g2d
-    if (tid < cnt && s_id[tid] < n) {
-      const uint32_t g = s_id[tid];
-      const float* P = s_acc + tid * 9;
-      const float A = rA, B = rB, C = rC, o = ro;
-      float gv[9];
-      gv[0] = fmaf(A, P[0], B * P[1]);
-      gv[1] = fmaf(B, P[0], C * P[1]);
-      gv[2] = 0.5f * P[2];
-      gv[3] = P[3];
-      gv[4] = 0.5f * P[4];
-      gv[5] = -P[5] / o;
-      gv[6] = P[6];
-      gv[7] = P[7];
-      gv[8] = P[8];
-      // one plane per component: the nine atomics of a lane go to nine different cache lines
-#pragma unroll
-      for (int c = 0; c < 9; ++c)
-        if (gv[c] != 0.0f) unsafeAtomicAdd(g2d + (size_t)c * n + g, gv[c]);
-    }
+    // finish the 2D gradient of each staged splat from its nine sums
+    if (!DET && tid < cnt && s_id[tid] < n) finish(s_acc + tid * 9);
     bend = bstart;
   }
   if (COUNT) count_evals(n_eval, eval_count);
@@ -767,6 +837,115 @@ __global__ void k_fill_zero(float* __restrict__ p, size_t count) {
     p[i] = 0.0f;
 }
 
+// Clears the records of the P = *total pairs (none when P exceeds the capacity: nothing is then
+// read), four floats per store.
+__global__ void k_clear_records(float4* __restrict__ rec, const unsigned long long* __restrict__ total,
+                                uint32_t rec_cap) {
+  const unsigned long long P = *total;
+  if (P > rec_cap) return;
+  const size_t count = ((size_t)P * 9 + 3) / 4;  // the record array is 256-byte aligned and padded
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < count; i += (size_t)gridDim.x * blockDim.x)
+    rec[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Per-pair records: base[g] = sum of tiles_touched over ids < g (exclusive prefix in id order),
+// total = the sum over all ids (= P). Two launches, reduce then scan, over blocks of 4096 ids;
+// integer sums, so the result does not depend on the order of the additions.
+// ---------------------------------------------------------------------------------------------
+constexpr int kBaseThreads = 1024, kBaseItems = 4, kBaseTile = kBaseThreads * kBaseItems;
+
+__device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v, unsigned long long* s_w) {
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s_w[wave] = v;
+  __syncthreads();
+  unsigned long long t = 0;
+  for (int w = 0; w < kBaseThreads / 64; ++w) t += s_w[w];
+  return t;
+}
+
+__global__ __launch_bounds__(kBaseThreads) void k_base_sums(int32_t n, const uint32_t* __restrict__ tiles_touched,
+                                                            unsigned long long* __restrict__ bsum) {
+  __shared__ unsigned long long s_w[kBaseThreads / 64];
+  unsigned long long v = 0;
+#pragma unroll
+  for (int i = 0; i < kBaseItems; ++i) {
+    const int64_t idx = (int64_t)blockIdx.x * kBaseTile + i * kBaseThreads + threadIdx.x;
+    if (idx < n) v += tiles_touched[idx];
+  }
+  const unsigned long long t = block_sum_u64(v, s_w);
+  if (threadIdx.x == 0) bsum[blockIdx.x] = t;
+}
+
+__global__ __launch_bounds__(kBaseThreads) void k_base_scan(int32_t n, const uint32_t* __restrict__ tiles_touched,
+                                                            const unsigned long long* __restrict__ bsum,
+                                                            uint32_t* __restrict__ base,
+                                                            unsigned long long* __restrict__ total) {
+  __shared__ unsigned long long s_w[kBaseThreads / 64];
+  __shared__ unsigned long long s_x[kBaseThreads / 64];
+  // the totals of the blocks before this one
+  unsigned long long pre = 0;
+  for (uint32_t b = threadIdx.x; b < blockIdx.x; b += kBaseThreads) pre += bsum[b];
+  pre = block_sum_u64(pre, s_w);
+  // exclusive scan of this block's 4096 counts, four consecutive ids per thread
+  const int64_t i0 = (int64_t)blockIdx.x * kBaseTile + (int64_t)threadIdx.x * kBaseItems;
+  uint32_t c[kBaseItems];
+  unsigned long long own = 0;
+#pragma unroll
+  for (int i = 0; i < kBaseItems; ++i) {
+    c[i] = i0 + i < n ? tiles_touched[i0 + i] : 0u;
+    own += c[i];
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  unsigned long long inc = own;
+  for (int d = 1; d < 64; d <<= 1) {
+    const unsigned long long up = __shfl_up(inc, d);
+    if (lane >= d) inc += up;
+  }
+  if (lane == 63) s_x[wave] = inc;
+  __syncthreads();
+  unsigned long long wpre = 0;
+  for (int w = 0; w < wave; ++w) wpre += s_x[w];
+  unsigned long long run = pre + wpre + inc - own;
+#pragma unroll
+  for (int i = 0; i < kBaseItems; ++i) {
+    if (i0 + i < n) base[i0 + i] = (uint32_t)run;
+    run += c[i];
+  }
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == kBaseThreads - 1) *total = run;
+}
+
+// dL/d(2D parameters) of every Gaussian from its records, one wave per Gaussian: lane l adds the
+// records l, l + 64, ... in order, then a fixed DPP tree adds the lanes (a fixed order). When
+// the pairs did not fit the records (total > rec_cap; the pair sort then left every tile range
+// empty) every gradient is zero.
+__global__ __launch_bounds__(256) void k_seg_reduce(int32_t n, const uint32_t* __restrict__ tiles_touched,
+                                                    const uint32_t* __restrict__ base,
+                                                    const unsigned long long* __restrict__ total,
+                                                    const float* __restrict__ rec, uint32_t rec_cap,
+                                                    float* __restrict__ g2d) {
+  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (g >= n) return;  // wave-uniform
+  const uint32_t cnt = *total <= (unsigned long long)rec_cap ? tiles_touched[g] : 0u;
+  const uint32_t b = base[g];
+  float acc[9];
+#pragma unroll
+  for (int c = 0; c < 9; ++c) acc[c] = 0.0f;
+  for (uint32_t j = lane; j < cnt; j += 64) {
+#pragma unroll
+    for (int c = 0; c < 9; ++c) acc[c] += rec[((size_t)b + j) * 9 + c];
+  }
+#pragma unroll
+  for (int c = 0; c < 9; ++c) acc[c] = wave_sum_lane63(acc[c]);
+  if (lane == 63) {
+#pragma unroll
+    for (int c = 0; c < 9; ++c) g2d[(size_t)c * n + g] = acc[c];
+  }
+}
+
 }  // namespace
 }  // namespace gs
 
@@ -813,46 +992,88 @@ extern "C" gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const
   return check_launch("gs_rasterize_fwd");
 }
 
-extern "C" size_t gs_bwd_workspace_bytes(int32_t n) { return n <= 0 ? 256 : align_up((size_t)n * 9 * 4, 256); }
+namespace {
+// Workspace of the record modes: g2d [9, n] | base [n] u32 | total u64 | block sums u64 | rec [cap, 9]
+struct BwdRecLayout {
+  size_t g2d, base, total, bsum, rec, bytes;
+};
+BwdRecLayout bwd_rec_layout(int32_t n, int64_t cap) {
+  BwdRecLayout L{};
+  const size_t nb = ((size_t)n + kBaseTile - 1) / kBaseTile;
+  L.g2d = 0;
+  L.base = align_up(L.g2d + (size_t)n * 9 * 4, 256);
+  L.total = align_up(L.base + (size_t)n * 4, 256);
+  L.bsum = align_up(L.total + 8, 256);
+  L.rec = align_up(L.bsum + nb * 8, 256);
+  L.bytes = align_up(L.rec + (size_t)cap * 9 * 4 + 16, 256);  // + one float4 of clearing slack
+  return L;
+}
 
-extern "C" gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float* d_means,
-                                      const float* d_log_scales, const float* d_quats,
-                                      const float* d_opacity_logits, const float* d_sh, const gs_camera* cam,
-                                      const gs_projected* proj, const uint32_t* d_ids,
-                                      const uint32_t* d_tile_ranges, const uint32_t* d_raster_plan,
-                                      const void* d_raster_ws, const float* d_final_T,
-                                      const uint32_t* d_n_contrib, const float* d_dL_dimage, void* d_workspace,
-                                      size_t workspace_bytes, float* d_grad_means, float* d_grad_log_scales,
-                                      float* d_grad_quats, float* d_grad_opacity_logits, float* d_grad_sh,
-                                      float* d_grad_means2d, uint64_t* d_eval_count, void* stream) {
+gs_status rasterize_bwd(const char* name, int mode, int32_t n, int32_t sh_degree, const float* d_means,
+                        const float* d_log_scales, const float* d_quats, const float* d_opacity_logits,
+                        const float* d_sh, const gs_camera* cam, const gs_projected* proj, const uint32_t* d_ids,
+                        const uint32_t* d_tile_ranges, const uint32_t* d_raster_plan, const void* d_raster_ws,
+                        const float* d_final_T, const uint32_t* d_n_contrib, const float* d_dL_dimage,
+                        int64_t pair_capacity, void* d_workspace, size_t workspace_bytes, float* d_grad_means,
+                        float* d_grad_log_scales, float* d_grad_quats, float* d_grad_opacity_logits,
+                        float* d_grad_sh, float* d_grad_means2d, uint64_t* d_eval_count, void* stream) {
+  const std::string nm = name;
   std::string why;
-  if (n < 0) return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_bwd: n < 0");
-  if (sh_degree < 0 || sh_degree > GS_MAX_SH_DEGREE)
-    return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_bwd: sh_degree not in 0..3");
-  if (!valid_camera(cam, &why)) return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_bwd: " + why);
+  if (n < 0) return set_error(GS_ERR_INVALID_ARG, nm + ": n < 0");
+  if (sh_degree < 0 || sh_degree > GS_MAX_SH_DEGREE) return set_error(GS_ERR_INVALID_ARG, nm + ": sh_degree not in 0..3");
+  if (!valid_camera(cam, &why)) return set_error(GS_ERR_INVALID_ARG, nm + ": " + why);
+  if (mode != kBwdAtomic && (pair_capacity < 0 || pair_capacity >= ((int64_t)1 << 30)))
+    return set_error(pair_capacity < 0 ? GS_ERR_INVALID_ARG : GS_ERR_LIMIT, nm + ": pair_capacity not in [0, 2^30)");
   if (n == 0) return GS_OK;
   if (!d_means || !d_log_scales || !d_quats || !d_opacity_logits || !d_sh || !proj_ok(proj) || !d_ids ||
       !d_tile_ranges || !d_final_T || !d_n_contrib || !d_dL_dimage || !d_grad_means || !d_grad_log_scales ||
       !d_grad_quats || !d_grad_opacity_logits || !d_grad_sh)
-    return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_bwd: NULL pointer with n > 0");
-  if (!d_workspace || workspace_bytes < gs_bwd_workspace_bytes(n))
-    return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_bwd: workspace smaller than gs_bwd_workspace_bytes()");
+    return set_error(GS_ERR_INVALID_ARG, nm + ": NULL pointer with n > 0");
+  const BwdRecLayout RL = bwd_rec_layout(n, pair_capacity);
+  const size_t need = mode == kBwdAtomic ? gs_bwd_workspace_bytes(n) : RL.bytes;
+  if (!d_workspace || workspace_bytes < need)
+    return set_error(GS_ERR_INVALID_ARG, nm + ": workspace smaller than its size function");
+  if (mode != kBwdAtomic && (reinterpret_cast<uintptr_t>(d_workspace) & 255) != 0)
+    return set_error(GS_ERR_INVALID_ARG, nm + ": workspace must be 256-byte aligned");
   if (((reinterpret_cast<uintptr_t>(d_quats) | reinterpret_cast<uintptr_t>(d_grad_quats)) & 15) != 0)
-    return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_bwd: quaternion arrays must be 16-byte aligned");
+    return set_error(GS_ERR_INVALID_ARG, nm + ": quaternion arrays must be 16-byte aligned");
   const int64_t ntiles = (int64_t)((cam->width + 15) / 16) * ((cam->height + 15) / 16);
-  if (ntiles > ((int64_t)1 << 24)) return set_error(GS_ERR_LIMIT, "gs_rasterize_bwd: more than 2^24 tiles");
+  if (ntiles > ((int64_t)1 << 24)) return set_error(GS_ERR_LIMIT, nm + ": more than 2^24 tiles");
   const DevCamera dc = to_dev(*cam);
   hipStream_t s = (hipStream_t)stream;
-  float* g2d = (float*)d_workspace;
-  {
+  char* ws = (char*)d_workspace;
+  float* g2d = (float*)(ws + RL.g2d);
+  uint32_t* base = nullptr;
+  unsigned long long* total = nullptr;
+  float* rec = nullptr;
+  if (mode == kBwdAtomic) {
     TimedScope ts("bwd_zero", s);
     const size_t count = (size_t)n * 9;
     const unsigned blocks = (unsigned)((count + 255) / 256 < 4096 ? (count + 255) / 256 : 4096);
     hipLaunchKernelGGL(k_fill_zero, dim3(blocks), dim3(256), 0, s, g2d, count);
+  } else {
+    TimedScope ts("bwd_base", s);
+    base = (uint32_t*)(ws + RL.base);
+    total = (unsigned long long*)(ws + RL.total);
+    rec = (float*)(ws + RL.rec);
+    unsigned long long* bsum = (unsigned long long*)(ws + RL.bsum);
+    const unsigned nb = (unsigned)(((size_t)n + kBaseTile - 1) / kBaseTile);
+    hipLaunchKernelGGL(k_base_sums, dim3(nb), dim3(kBaseThreads), 0, s, n, proj->d_tiles_touched, bsum);
+    hipLaunchKernelGGL(k_base_scan, dim3(nb), dim3(kBaseThreads), 0, s, n, proj->d_tiles_touched, bsum, base, total);
+    // every record starts at zero: the pairs no pixel reaches are never staged
+    const size_t count4 = ((size_t)pair_capacity * 9 + 3) / 4;
+    const unsigned blocks = (unsigned)((count4 + 255) / 256 < 8192 ? (count4 + 255) / 256 : 8192);
+    if (count4)
+      hipLaunchKernelGGL(k_clear_records, dim3(blocks), dim3(256), 0, s, (float4*)rec, total, (uint32_t)pair_capacity);
   }
   {
     TimedScope ts("rbwd", s);
-    auto kern = d_eval_count ? k_rbwd<true> : k_rbwd<false>;
+    auto pick = [&](auto count_tag) {
+      constexpr bool C = decltype(count_tag)::value;
+      return mode == kBwdAtomic ? k_rbwd<C, kBwdAtomic> : mode == kBwdRecords ? k_rbwd<C, kBwdRecords>
+                                                                              : k_rbwd<C, kBwdDeterministic>;
+    };
+    auto kern = d_eval_count ? pick(std::true_type{}) : pick(std::false_type{});
     // with checkpoints: one workgroup per work item of the plan (the extra ones, fewer than
     // kPlanMaxChunks, then one per tile)
     const bool chunked = d_raster_plan && d_raster_ws;
@@ -860,7 +1081,13 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float*
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges, d_raster_plan,
                        (uint32_t)ntiles, chunked ? (const float4*)d_raster_ws : nullptr, d_ids,
                        proj->d_means2d, proj->d_conics, proj->d_opacities, proj->d_colors, proj->d_radii, dc,
-                       d_final_T, d_n_contrib, d_dL_dimage, g2d, (unsigned long long*)d_eval_count);
+                       d_final_T, d_n_contrib, d_dL_dimage, g2d, base, rec, (uint32_t)pair_capacity,
+                       (unsigned long long*)d_eval_count);
+  }
+  if (mode != kBwdAtomic) {
+    TimedScope ts("bwd_reduce", s);
+    hipLaunchKernelGGL(k_seg_reduce, dim3((unsigned)(((size_t)n + 3) / 4)), dim3(256), 0, s, n,
+                       proj->d_tiles_touched, base, total, rec, (uint32_t)pair_capacity, g2d);
   }
   {
     TimedScope ts("pbwd", s);
@@ -877,5 +1104,44 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float*
     }
 #undef GS_LAUNCH_PBWD
   }
-  return check_launch("gs_rasterize_bwd");
+  return check_launch(name);
 }
+}  // namespace
+
+extern "C" size_t gs_bwd_workspace_bytes(int32_t n) { return n <= 0 ? 256 : align_up((size_t)n * 9 * 4, 256); }
+
+extern "C" size_t gs_bwd_det_workspace_bytes(int32_t n, int64_t pair_capacity) {
+  if (n < 0 || pair_capacity < 0 || pair_capacity >= ((int64_t)1 << 30)) return 0;
+  return bwd_rec_layout(n, pair_capacity).bytes;
+}
+
+extern "C" gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float* d_means,
+                                      const float* d_log_scales, const float* d_quats,
+                                      const float* d_opacity_logits, const float* d_sh, const gs_camera* cam,
+                                      const gs_projected* proj, const uint32_t* d_ids,
+                                      const uint32_t* d_tile_ranges, const uint32_t* d_raster_plan,
+                                      const void* d_raster_ws, const float* d_final_T,
+                                      const uint32_t* d_n_contrib, const float* d_dL_dimage, void* d_workspace,
+                                      size_t workspace_bytes, float* d_grad_means, float* d_grad_log_scales,
+                                      float* d_grad_quats, float* d_grad_opacity_logits, float* d_grad_sh,
+                                      float* d_grad_means2d, uint64_t* d_eval_count, void* stream) {
+  return rasterize_bwd("gs_rasterize_bwd", kBwdAtomic, n, sh_degree, d_means, d_log_scales, d_quats,
+                       d_opacity_logits, d_sh, cam, proj, d_ids, d_tile_ranges, d_raster_plan, d_raster_ws, d_final_T,
+                       d_n_contrib, d_dL_dimage, 0, d_workspace, workspace_bytes, d_grad_means, d_grad_log_scales,
+                       d_grad_quats, d_grad_opacity_logits, d_grad_sh, d_grad_means2d, d_eval_count, stream);
+}
+
+extern "C" gs_status gs_rasterize_bwd_deterministic(
+    int32_t n, int32_t sh_degree, const float* d_means, const float* d_log_scales, const float* d_quats,
+    const float* d_opacity_logits, const float* d_sh, const gs_camera* cam, const gs_projected* proj,
+    const uint32_t* d_ids, const uint32_t* d_tile_ranges, const uint32_t* d_raster_plan, const void* d_raster_ws,
+    const float* d_final_T, const uint32_t* d_n_contrib, const float* d_dL_dimage, int64_t pair_capacity,
+    void* d_workspace, size_t workspace_bytes, float* d_grad_means, float* d_grad_log_scales, float* d_grad_quats,
+    float* d_grad_opacity_logits, float* d_grad_sh, float* d_grad_means2d, uint64_t* d_eval_count, void* stream) {
+  return rasterize_bwd("gs_rasterize_bwd_deterministic", kBwdDeterministic, n, sh_degree, d_means, d_log_scales,
+                       d_quats, d_opacity_logits, d_sh, cam, proj, d_ids, d_tile_ranges, d_raster_plan, d_raster_ws,
+                       d_final_T, d_n_contrib, d_dL_dimage, pair_capacity, d_workspace, workspace_bytes, d_grad_means,
+                       d_grad_log_scales, d_grad_quats, d_grad_opacity_logits, d_grad_sh, d_grad_means2d,
+                       d_eval_count, stream);
+}
+

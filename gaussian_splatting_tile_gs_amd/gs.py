@@ -67,6 +67,9 @@ def load():
         "gs_bin_and_sort": (i32, [i32, proj_p, cam_p, P, sz, i64, P, P, P, P, P, ctypes.POINTER(ctypes.c_int64), P]),
         "gs_rasterize_fwd": (i32, [i32, proj_p, cam_p, P, P, P, P, P, P, P, P, P]),
         "gs_bwd_workspace_bytes": (sz, [i32]),
+        "gs_bwd_det_workspace_bytes": (sz, [i32, i64]),
+        "gs_rasterize_bwd_deterministic": (i32, [i32, i32, P, P, P, P, P, cam_p, proj_p, P, P, P, P, P, P, P, i64,
+                                                 P, sz, P, P, P, P, P, P, P, P]),
         "gs_rasterize_bwd": (i32, [i32, i32, P, P, P, P, P, cam_p, proj_p, P, P, P, P, P, P, P, P, sz, P, P, P, P, P,
                                    P, P, P]),
         "gs_loss_l1": (i32, [i32, i32, P, P, P, P, P]),
@@ -170,10 +173,23 @@ def gs_bwd_workspace_bytes(n) -> int:
     return int(load().gs_bwd_workspace_bytes(n))
 
 
+def gs_bwd_det_workspace_bytes(n, pair_capacity) -> int:
+    return int(load().gs_bwd_det_workspace_bytes(n, pair_capacity))
+
+
 def gs_rasterize_bwd(n, sh_degree, means, log_scales, quats, opacity_logits, sh, cam: GsCamera, proj: "Projected",
                      ids, tile_ranges, final_T, n_contrib, dL_dimage, workspace, grad_means, grad_log_scales,
                      grad_quats, grad_opacity_logits, grad_sh, grad_means2d=None, eval_count=None, stream=None,
-                     plan=None, raster_ws=None):
+                     plan=None, raster_ws=None, pair_capacity=None):
+    """pair_capacity=None: gs_rasterize_bwd (fp32 atomics); else gs_rasterize_bwd_deterministic."""
+    if pair_capacity is not None:
+        return _check(load().gs_rasterize_bwd_deterministic(
+            n, sh_degree, _ptr(means), _ptr(log_scales), _ptr(quats), _ptr(opacity_logits), _ptr(sh),
+            ctypes.byref(cam), ctypes.byref(proj.struct()), _ptr(ids), _ptr(tile_ranges), _ptr(plan),
+            _ptr(raster_ws), _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage), int(pair_capacity),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(grad_means), _ptr(grad_log_scales),
+            _ptr(grad_quats), _ptr(grad_opacity_logits), _ptr(grad_sh), _ptr(grad_means2d), _ptr(eval_count),
+            _stream(stream)))
     return _check(load().gs_rasterize_bwd(
         n, sh_degree, _ptr(means), _ptr(log_scales), _ptr(quats), _ptr(opacity_logits), _ptr(sh), ctypes.byref(cam),
         ctypes.byref(proj.struct()), _ptr(ids), _ptr(tile_ranges), _ptr(plan), _ptr(raster_ws), _ptr(final_T),
@@ -282,6 +298,7 @@ class Pipeline:
         self.num_pairs = 0
         self.num_pairs_dev = torch.zeros(1, device=device, dtype=torch.int64)
         self.schedule = "chunks"  # "chunks": plan + checkpoints; "order": plan only; "tiles": neither
+        self.deterministic = False  # True: the bitwise-reproducible backward
         self._alloc_pairs(pair_capacity)
 
     def _alloc_pairs(self, cap):
@@ -334,13 +351,23 @@ class Pipeline:
         gs_loss_l1(self.width, self.height, self.image, target, self.dL_dimage, loss, stream)
 
     def backward(self, cam: GsCamera, dL_dimage=None, eval_count=None, stream=None):
+        """self.deterministic selects gs_rasterize_bwd_deterministic (records sized by the pair
+        capacity) over gs_rasterize_bwd (fp32 atomics)."""
         p, g = self.p, self.grads
+        det = getattr(self, "deterministic", False)
+        ws = self.bwd_ws
+        if det:
+            need = gs_bwd_det_workspace_bytes(self.n, self.capacity)
+            if getattr(self, "_det_ws", None) is None or self._det_ws.numel() < need:
+                self._det_ws = torch.empty(need, device=self.device, dtype=torch.uint8)
+            ws = self._det_ws
         gs_rasterize_bwd(self.n, p["sh_degree"], p["means"], p["log_scales"], p["quats"], p["opacity_logits"],
                          p["sh"], cam, self.proj, self.ids, self.ranges, self.final_T, self.n_contrib,
-                         self.dL_dimage if dL_dimage is None else dL_dimage, self.bwd_ws, g["means"], g["log_scales"],
+                         self.dL_dimage if dL_dimage is None else dL_dimage, ws, g["means"], g["log_scales"],
                          g["quats"], g["opacity_logits"], g["sh"], g["means2d"], eval_count, stream,
                          plan=self.plan if self.schedule != "tiles" else None,
-                         raster_ws=self.raster_ws if getattr(self, "_ckpt_written", False) else None)
+                         raster_ws=self.raster_ws if getattr(self, "_ckpt_written", False) else None,
+                         pair_capacity=self.capacity if det else None)
 
     def iteration(self, cam: GsCamera, target, stream=None, wait=True):
         """One fwd+bwd iteration: project, bin+sort, blend, L1 gradient, backward. wait=False runs

@@ -193,6 +193,33 @@ gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float* d_means, c
                            uint64_t* d_eval_count, void* stream);
 
 /*
+ * gs_rasterize_bwd_deterministic -- gs_rasterize_bwd with bitwise-reproducible gradients: the
+ * same inputs give the same bits on every run. No floating-point atomics: the 2D gradient of
+ * each (tile, Gaussian) pair is written to its own slot -- a Gaussian's pairs are contiguous
+ * from the prefix sum of tiles_touched in id order, row-major over its tile rectangle -- and the
+ * slots of a Gaussian are added in a fixed order (one wave per Gaussian, strided lanes, then a
+ * fixed lane tree); inside a tile the four waves' sums of a splat are added in wave order.
+ * Arguments as gs_rasterize_bwd, plus pair_capacity: at least the P of gs_bin_and_sort (the
+ *   capacity given to it will do); d_workspace (256-byte aligned) of at least
+ *   gs_bwd_det_workspace_bytes(n, pair_capacity) bytes. If P > pair_capacity every gradient is 0
+ *   (as after a binning overflow). Results agree with gs_rasterize_bwd to rounding.
+ * Errors: those of gs_rasterize_bwd, GS_ERR_INVALID_ARG for pair_capacity < 0 or a misaligned
+ *   workspace, GS_ERR_LIMIT for pair_capacity >= 2^30.
+ */
+size_t gs_bwd_det_workspace_bytes(int32_t n, int64_t pair_capacity);
+gs_status gs_rasterize_bwd_deterministic(int32_t n, int32_t sh_degree, const float* d_means,
+                                         const float* d_log_scales, const float* d_quats,
+                                         const float* d_opacity_logits, const float* d_sh, const gs_camera* cam,
+                                         const gs_projected* proj, const uint32_t* d_ids,
+                                         const uint32_t* d_tile_ranges, const uint32_t* d_raster_plan,
+                                         const void* d_raster_ws, const float* d_final_T,
+                                         const uint32_t* d_n_contrib, const float* d_dL_dimage,
+                                         int64_t pair_capacity, void* d_workspace, size_t workspace_bytes,
+                                         float* d_grad_means, float* d_grad_log_scales, float* d_grad_quats,
+                                         float* d_grad_opacity_logits, float* d_grad_sh, float* d_grad_means2d,
+                                         uint64_t* d_eval_count, void* stream);
+
+/*
  * gs_loss_l1 -- the L1 photometric term of the training loss (section 7 of the PyTorch lesson:
  * (1 - lambda) L1 + lambda (1 - SSIM)): L = mean |image - target| over h*w*3 values, so
  * dL/dimage = sign(image - target) / (3 h w) with sign(0) = 0.

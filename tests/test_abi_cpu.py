@@ -60,3 +60,9 @@ def test_host_only_helpers(lib):
         sizes = [3 * n, 3 * n, 4 * n, n, 3 * (deg + 1) ** 2 * n]
         assert lib.gs_adam_state_floats(n, deg) == sum(-(-c // 64) * 64 for c in sizes)
     assert lib.gs_adam_state_floats(0, 0) == 0 and lib.gs_adam_state_floats(10, 4) == 0
+    lib.gs_bwd_det_workspace_bytes.restype = ctypes.c_size_t
+    lib.gs_bwd_det_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int64]
+    # 36 B per pair record on top of the per-Gaussian arrays; invalid capacities give 0
+    a, b = lib.gs_bwd_det_workspace_bytes(1000, 10000), lib.gs_bwd_det_workspace_bytes(1000, 20000)
+    assert b - a == 36 * 10000 and a >= 1000 * 40 + 36 * 10000
+    assert lib.gs_bwd_det_workspace_bytes(1000, -1) == 0 and lib.gs_bwd_det_workspace_bytes(1000, 1 << 30) == 0

@@ -38,8 +38,11 @@ def _full_pixels(cam):
     return np.stack([r.ravel(), c.ravel()], -1).astype(np.int32)
 
 
-def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7, label=""):
-    """Project, bin, forward (and backward) on the GPU; compare every stage with the oracle."""
+def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7, label="", bwd="atomic"):
+    """Project, bin, forward (and backward) on the GPU; compare every stage with the oracle.
+    bwd: "atomic" (gs_rasterize_bwd), "det" (gs_rasterize_bwd_deterministic, run twice over a
+    scrambled workspace: the two results must be equal bit for bit), "det_tiles" (the same
+    without the raster plan and checkpoints)."""
     gs, torch = env
     t0 = time.time()
     log(f"[{label}] n={scene['means'].shape[0]} {cam_dict['width']}x{cam_dict['height']} deg={scene['sh_degree']}")
@@ -94,13 +97,30 @@ def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7
                   (("means", params["means"]), ("log_scales", params["log_scales"]), ("quats", params["quats"]),
                    ("opacity_logits", params["opacity_logits"]), ("sh", params["sh"]))}
     g2d_out = torch.empty(params["n"], 2, device="cuda")
-    ws = torch.empty(gs.gs_bwd_workspace_bytes(params["n"]), device="cuda", dtype=torch.uint8)
-    gs.gs_rasterize_bwd(params["n"], params["sh_degree"], params["means"], params["log_scales"], params["quats"],
-                        params["opacity_logits"], params["sh"], cam, proj, ids, ranges, fT, nc,
-                        torch.from_numpy(dimg).cuda(), ws, pipe_grads["means"], pipe_grads["log_scales"],
-                        pipe_grads["quats"], pipe_grads["opacity_logits"], pipe_grads["sh"], g2d_out,
-                        plan=plan, raster_ws=rws)
-    torch.cuda.synchronize()
+    det = bwd != "atomic"
+    cap = P_exp + 17  # the capacity the pairs were binned with
+    ws = torch.empty(gs.gs_bwd_det_workspace_bytes(params["n"], cap) if det else gs.gs_bwd_workspace_bytes(params["n"]),
+                     device="cuda", dtype=torch.uint8)
+    dimg_d = torch.from_numpy(dimg).cuda()
+    use_plan = bwd != "det_tiles"
+
+    def run_bwd():
+        gs.gs_rasterize_bwd(params["n"], params["sh_degree"], params["means"], params["log_scales"],
+                            params["quats"], params["opacity_logits"], params["sh"], cam, proj, ids, ranges, fT, nc,
+                            dimg_d, ws, pipe_grads["means"], pipe_grads["log_scales"], pipe_grads["quats"],
+                            pipe_grads["opacity_logits"], pipe_grads["sh"], g2d_out,
+                            plan=plan if use_plan else None, raster_ws=rws if use_plan else None,
+                            pair_capacity=cap if det else None)
+        torch.cuda.synchronize()
+
+    run_bwd()
+    if det:
+        first = {k: v.clone() for k, v in pipe_grads.items()}
+        first["means2d"] = g2d_out.clone()
+        ws.random_(0, 256)  # the records of every pair must be rewritten
+        run_bwd()
+        same = all(torch.equal(first[k], v) for k, v in pipe_grads.items()) and torch.equal(first["means2d"], g2d_out)
+        assert same, "the deterministic backward gave different bits on a second run"
     g2d, aref2d = oracle.render_backward(o_proj, cam_dict, gsel, pixels=pix)
     raw = oracle.project_backward(scene, cam_dict, g2d, aref2d)
     gpu = {k: v.cpu().numpy() for k, v in pipe_grads.items()}
@@ -110,7 +130,7 @@ def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7
     assert np.all(np.abs(m2 - g2d[:, :2]) <= tol), "dL/dmean2d differs"
     culled = o_proj["tiles_touched"] == 0
     assert all(np.all(gpu[k][culled] == 0) for k in gpu), "culled Gaussians must get exactly zero"
-    log(f"[{label}] backward: worst error/tolerance {worst:.3f} ({time.time() - t0:.1f}s)")
+    log(f"[{label}] backward ({bwd}): worst error/tolerance {worst:.3f} ({time.time() - t0:.1f}s)")
 
 
 # ---- small cases, compared whole --------------------------------------------------------------
@@ -144,6 +164,58 @@ def test_workload_sampled(env, name, cam_index, backward):
     cam = synth.make_cameras(wl)[cam_index]
     pix = synth.sample_pixels(cam["width"], cam["height"], 4096, seed=cam_index + 1)
     _pipeline_case(env, scene, cam, pixels=pix, backward=backward, label=f"{name}#{cam_index}")
+
+
+# ---- deterministic backward: oracle parity and bitwise reproducibility ---------------------------
+@pytest.mark.parametrize("case,bwd", [("tiny", "det"), ("tiny", "det_tiles"), ("ragged", "det"),
+                                      ("distill_30k", "det"), ("mid_150k_sh3", "det"), ("stress_400k_sh3", "det")])
+def test_deterministic_backward(env, case, bwd):
+    if case == "tiny":
+        wl = synth.WORKLOADS["tiny_1k"]
+        _pipeline_case(env, synth.make_scene(wl), synth.make_cameras(wl)[0], label="tiny_1k", bwd=bwd)
+    elif case == "ragged":
+        sc = synth.random_scene(300, seed=21, width=37, height=23, focal=30.0, sh_degree=3, logit_std=2.0)
+        cam = synth.make_camera(np.eye(4), 37, 23, 30.0, background=(0.2, 0.4, 0.6))
+        _pipeline_case(env, sc, cam, label="ragged_sh3", bwd=bwd)
+    else:
+        wl = synth.WORKLOADS[case]
+        cam = synth.make_cameras(wl)[0]
+        pix = synth.sample_pixels(cam["width"], cam["height"], 4096, seed=1)
+        _pipeline_case(env, synth.make_scene(wl), cam, pixels=pix, label=f"{case}#0", bwd=bwd)
+
+
+def test_deterministic_backward_capacity_and_arguments(env):
+    """Pairs beyond the record capacity: every gradient is zero (as after a binning overflow);
+    bad capacities and a misaligned workspace are rejected before any launch."""
+    gs, torch = env
+    wl = synth.WORKLOADS["tiny_1k"]
+    params = gs.scene_to_device(synth.make_scene(wl))
+    cam = gs.make_camera(synth.make_cameras(wl)[0])
+    pipe = gs.Pipeline(params, wl.width, wl.height, pair_capacity=1 << 16)
+    pipe.project(cam)
+    P = pipe.bin(cam)
+    pipe.forward(cam)
+    pipe.dL_dimage.copy_(torch.from_numpy(synth.random_image_grad(wl.height, wl.width, seed=3)))
+    pipe.deterministic = True
+    pipe.backward(cam)
+    torch.cuda.synchronize()
+    assert float(pipe.grads["means"].abs().sum()) > 0.0
+    g = pipe.grads
+    ws = torch.empty(gs.gs_bwd_det_workspace_bytes(params["n"], P - 1), device="cuda", dtype=torch.uint8)
+    args = lambda cap, w: (params["n"], 0, params["means"], params["log_scales"], params["quats"],
+                           params["opacity_logits"], params["sh"], cam, pipe.proj, pipe.ids, pipe.ranges, pipe.final_T,
+                           pipe.n_contrib, pipe.dL_dimage, w, g["means"], g["log_scales"], g["quats"],
+                           g["opacity_logits"], g["sh"], g["means2d"])
+    gs.gs_rasterize_bwd(*args(P - 1, ws), plan=pipe.plan, raster_ws=pipe.raster_ws, pair_capacity=P - 1)
+    torch.cuda.synchronize()
+    assert all(float(v.abs().sum()) == 0.0 for v in g.values())
+    for bad in (-1, 1 << 30):
+        with pytest.raises(gs.GsError):
+            gs.gs_rasterize_bwd(*args(bad, ws), pair_capacity=bad)
+    big = torch.empty(ws.numel() + 256, device="cuda", dtype=torch.uint8)
+    with pytest.raises(gs.GsError):
+        gs.gs_rasterize_bwd(*args(P - 1, big[4:]), pair_capacity=P - 1)
+    assert gs.gs_bwd_det_workspace_bytes(params["n"], -1) == 0
 
 
 # ---- edge cases ---------------------------------------------------------------------------------
