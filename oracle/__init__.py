@@ -87,11 +87,17 @@ def _suffix(dtype):
     return "f32" if np.dtype(dtype) == np.float32 else "f64"
 
 
+RADIUS_MODES = {"gsplat": 0, "3dgs": 1}
+
+
 def camera_array(cam, dtype=np.float32):
-    """Pack a camera dict into the oracle's 24-number layout."""
+    """Pack a camera dict into the oracle's 26-number layout. Options (section 4 of the PyTorch
+    lesson): cam["radius_mode"] "gsplat" (default, the opacity-aware per-axis extent) or "3dgs"
+    (ceil(3 sqrt(lambda_max)) on both axes); cam["antialiased"] (default False)."""
     v = np.asarray(cam["viewmat"], dtype=np.float64).reshape(16)
     bg = np.asarray(cam.get("background", (0.0, 0.0, 0.0)), dtype=np.float64)
-    arr = np.concatenate([v, [cam["fx"], cam["fy"], cam["cx"], cam["cy"], cam.get("near", 0.01)], bg])
+    opts = [RADIUS_MODES[cam.get("radius_mode", "gsplat")], 1.0 if cam.get("antialiased", False) else 0.0]
+    arr = np.concatenate([v, [cam["fx"], cam["fy"], cam["cx"], cam["cy"], cam.get("near", 0.01)], bg, opts])
     return _c(arr, dtype)
 
 
@@ -197,7 +203,9 @@ def _render_inputs(proj, dtype):
 
 
 def render(proj, cam, pixels=None, dtype=np.float32, band_eps=None):
-    """Dense render: every pixel walks every un-culled Gaussian in stable depth order.
+    """Per-pixel render: every pixel walks, in one stable global depth order, the un-culled
+    Gaussians whose tile rectangle holds its tile (the tiled renderer's lists; with the default
+    opacity-aware radius that is every Gaussian that can reach it, i.e. the dense render).
 
     pixels: None (whole image, row-major) or int array [M,2] of (row, col).
     Returns dict image [M,3] f64, final_T [M] f64, last_id [M] int32 (-1: none),

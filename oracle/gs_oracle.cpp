@@ -10,8 +10,10 @@
 //   * world -> camera, EWA Jacobian with the widened-frustum clamp, eps2d dilation (section 3),
 //   * conic, opacity-aware per-axis radius and the tile rectangle (section 4),
 //   * the per-pixel front-to-back blend with the 1/255 skip, the 0.99 cap and the T <= 1e-4
-//     stop-before-add (section 5), done the dense way: every pixel walks every un-culled Gaussian
-//     in one stable global depth order (section 5's argsort(depths, stable=True)),
+//     stop-before-add (section 5), per pixel: every pixel walks the un-culled Gaussians whose
+//     tile rectangle holds its tile (the tiled renderer's lists; with the default opacity-aware
+//     radius that is every Gaussian that can reach the pixel, i.e. the dense render) in one
+//     stable global depth order (section 5's argsort(depths, stable=True)),
 //   * the analytic backward of all of the above (section 6 names the chain; the formulas are
 //     derived from the forward definitions and checked against central finite differences).
 // Binning is brute force: enumerate each Gaussian's tile rectangle, std::stable_sort the
@@ -117,15 +119,22 @@ template <class T> bool finite(T x) { return std::isfinite(x); }
 
 // ---------------------------------------------------------------------------------------------
 // Camera: row-major world->camera viewmat [4,4] with OpenCV axes (+x right, +y down, +z
-// forward) and pinhole intrinsics (the PyTorch lesson, section 3). Packed as 24 numbers:
-// viewmat[16], fx, fy, cx, cy, near, bg[3]; width and height are passed separately.
+// forward) and pinhole intrinsics (the PyTorch lesson, section 3). Packed as 26 numbers:
+// viewmat[16], fx, fy, cx, cy, near, bg[3], radius_mode, antialiased; width and height are
+// passed separately. The two options are the variants section 4 of the lesson lists:
+// radius_mode 0 = gsplat's opacity-aware per-axis extent, 1 = the original 3DGS radius
+// ceil(3 sqrt(lambda_max)) for both axes; antialiased 1 = opacity times the compensation
+// sqrt(det Sigma2d / det(Sigma2d + 0.3 I)) (gsplat's "antialiased" mode, Mip-Splatting's 2D
+// filter), read with Sigma2d the covariance before the eps2d dilation.
 // ---------------------------------------------------------------------------------------------
+constexpr int kNumCam = 26;
 template <class T> struct Cam {
   T V[16];
   T fx, fy, cx, cy, near_plane;
   T bg[3];
   int W, H;
   int tiles_x, tiles_y;
+  int radius_mode, antialiased;
 };
 
 template <class T> Cam<T> make_cam(const T* p, int W, int H) {
@@ -133,6 +142,8 @@ template <class T> Cam<T> make_cam(const T* p, int W, int H) {
   for (int i = 0; i < 16; ++i) c.V[i] = p[i];
   c.fx = p[16]; c.fy = p[17]; c.cx = p[18]; c.cy = p[19]; c.near_plane = p[20];
   c.bg[0] = p[21]; c.bg[1] = p[22]; c.bg[2] = p[23];
+  c.radius_mode = (int)p[24];
+  c.antialiased = (int)p[25];
   c.W = W; c.H = H;
   c.tiles_x = (W + 15) / 16;
   c.tiles_y = (H + 15) / 16;
@@ -216,6 +227,9 @@ template <class T> struct Proj {
   bool clamp_x, clamp_y;
   T J[6];            // rows (J00 J01 J02), (J10 J11 J12)
   T a, b, c;         // dilated 2D covariance
+  T a0, c0, det0;    // the diagonal and determinant before the dilation
+  T comp;            // antialiased compensation sqrt(det0 / det) (1 when off)
+  T o_eff;           // the opacity the blend uses: o comp
   T det_raw, det;
   T conic[3];
   T m2d[2];
@@ -316,6 +330,13 @@ void project_one(const T* mean, const T* log_scale, const T* quat, T logit, cons
   P.c = C2[3] + (T)0.3;
   P.det_raw = P.a * P.c - P.b * P.b;
   P.det = std::max(P.det_raw, (T)1e-10);
+  P.a0 = C2[0];
+  P.c0 = C2[3];
+  P.det0 = C2[0] * C2[3] - C2[1] * C2[1];
+  // Antialiased: o times sqrt(det Sigma2d / det Sigma'), which keeps the splat's integral
+  // o 2 pi sqrt(det) equal to that of the undilated Gaussian (section 4's last variant).
+  P.comp = cam.antialiased ? std::sqrt(std::max(P.det0, (T)0) / P.det) : (T)1;
+  P.o_eff = cam.antialiased ? P.o * P.comp : P.o;
   P.conic[0] = P.c / P.det;
   P.conic[1] = -P.b / P.det;
   P.conic[2] = P.a / P.det;
@@ -354,15 +375,20 @@ void project_one(const T* mean, const T* log_scale, const T* quat, T logit, cons
   P.radius_3dgs = (int)std::min(std::ceil((T)3 * std::sqrt(lam)), sat3);
 
   // Radius: per-axis extent of the k-sigma ellipse, k = min(3.33, sqrt(2 ln(255 o))): the
-  // distance at which o exp(-m^2/2) falls below 1/255. Gaussians with o < 1/255 never reach it.
-  if (P.o < (T)1 / (T)255) return;
-  T kk = (T)2 * Act<T>::log((T)255 * P.o);
+  // distance at which o exp(-m^2/2) falls below 1/255 (o the opacity the blend uses).
+  // Gaussians with o < 1/255 never reach it. With radius_mode 1 both radii are the 3DGS one.
+  if (P.o_eff < (T)1 / (T)255) return;
+  T kk = (T)2 * Act<T>::log((T)255 * P.o_eff);
   if (!(kk > (T)0)) kk = (T)0;
   P.k = std::sqrt(kk);
   if (P.k > (T)3.33) P.k = (T)3.33;
   const T sat = (T)16777216;  // 2^24: radii are saturated here (far beyond any tile grid)
-  P.rx = std::min(std::ceil(P.k * std::sqrt(P.a)), sat);
-  P.ry = std::min(std::ceil(P.k * std::sqrt(P.c)), sat);
+  if (cam.radius_mode == 1) {
+    P.rx = P.ry = (T)P.radius_3dgs;
+  } else {
+    P.rx = std::min(std::ceil(P.k * std::sqrt(P.a)), sat);
+    P.ry = std::min(std::ceil(P.k * std::sqrt(P.c)), sat);
+  }
 
   // Tile rectangle [floor((mu - r)/16), ceil((mu + r)/16)) clamped to the grid.
   T x0 = std::floor((P.m2d[0] - P.rx) / (T)16), x1 = std::ceil((P.m2d[0] + P.rx) / (T)16);
@@ -433,16 +459,19 @@ void trace_pixel(T px, T py, const std::vector<int>& order, const std::vector<Sp
                      std::fabs((double)s.B * dx * dy);
     double e_sig = 8.0 * band_eps * sig_mag;   // absolute, on sigma
     double e_alpha = e_sig + 8.0 * band_eps;   // relative, on alpha
+    // The tiled renderer's lists: a pixel sees only the Gaussians whose tile rectangle holds its
+    // tile. One outside that would pass the skip test is counted as an escape (a difference from
+    // the dense render; none with the opacity-aware radius) and then ignored.
+    bool inside = tile_x >= rects[g * 4 + 0] && tile_x < rects[g * 4 + 2] &&
+                  tile_y >= rects[g * 4 + 1] && tile_y < rects[g * 4 + 3];
+    if (!inside) {
+      if (!(sigma < (T)0 || alpha < thr_a)) ++tr.escapes;
+      continue;
+    }
     if (std::fabs((double)sigma) <= e_sig) tr.fragile = true;
     if (std::fabs((double)alpha - (double)thr_a) <= e_alpha * (double)thr_a) tr.fragile = true;
     if (std::fabs((double)raw - 0.99) <= e_alpha * 0.99) tr.fragile = true;
     if (sigma < (T)0 || alpha < thr_a) continue;
-    // Past the skip test this Gaussian takes part in the pixel's decisions (it is added, or it
-    // stops the pixel), so a tiled renderer must have it in the pixel's tile list: count it as
-    // an escape when the pixel's tile lies outside the Gaussian's tile rectangle.
-    bool inside = tile_x >= rects[g * 4 + 0] && tile_x < rects[g * 4 + 2] &&
-                  tile_y >= rects[g * 4 + 1] && tile_y < rects[g * 4 + 3];
-    if (!inside) ++tr.escapes;
     // contributes unless it would drive T to or below 1e-4
     T next_T = Tr * ((T)1 - alpha);
     double errN = errT + e_alpha * (double)alpha / (1.0 - (double)alpha) + 2.0 * band_eps;
@@ -676,6 +705,14 @@ void project_bwd_one(const double* mean, const double* log_scale, const double* 
     gb = gA * (2.0 * b * c / d2) + gB * (-1.0 / det - 2.0 * b * b / d2) + gC * (2.0 * a * b / d2);
     gc = gA * (1.0 / det - a * c / d2) + gB * (a * b / d2) + gC * (-a * a / d2);
   }
+  if (cam.antialiased && P.comp > 0.0) {
+    // o_eff = o comp, comp = sqrt(det0 / det): d comp = comp / 2 (d det0 / det0 - d det / det),
+    // det0 = a0 c0 - b^2 and det = a c - b^2 with a = a0 + 0.3, c = c0 + 0.3 (da = da0)
+    const double h = 0.5 * g9[5] * P.o * P.comp, det0 = P.det0;
+    ga += h * (P.c0 / det0 - c / det);
+    gc += h * (P.a0 / det0 - a / det);
+    gb += h * (-2.0 * b / det0 + 2.0 * b / det);
+  }
   // Sigma' = J Sc J^T + 0.3 I with entries (a, b; b, c): symmetric gradient G2.
   double G2[4] = {ga, 0.5 * gb, 0.5 * gb, gc};
   const double* J = P.J;
@@ -761,8 +798,8 @@ void project_bwd_one(const double* mean, const double* log_scale, const double* 
   } else {
     for (int j = 0; j < 4; ++j) d_quat[j] = gq[j] / P.qn;
   }
-  // o = sigmoid(logit)
-  *d_logit = P.o * (1.0 - P.o) * g9[5];
+  // o = sigmoid(logit); the blend's opacity is o comp
+  *d_logit = P.o * (1.0 - P.o) * P.comp * g9[5];
   // colour
   if (sh_degree == 0) {
     for (int ch = 0; ch < 3; ++ch) d_sh[ch] = g9[6 + ch];
@@ -804,7 +841,7 @@ int project_impl(int n, int sh_degree, const T* means, const T* log_scales, cons
     means2d[2 * g + 1] = P.m2d[1];
     for (int j = 0; j < 3; ++j) conics[3 * g + j] = P.conic[j];
     depths[g] = P.depth;
-    opac[g] = P.o;
+    opac[g] = P.o_eff;
     for (int j = 0; j < 3; ++j) colors[3 * g + j] = P.color[j];
     if (cov2d) {
       cov2d[3 * g] = P.a;
@@ -835,8 +872,8 @@ int project_bwd_impl(int n, int sh_degree, const T* means, const T* log_scales, 
                      double* d_logits, double* d_sh, double* aref_raw) {
   if (sh_degree < 0 || sh_degree > 3) return 1;
   Cam<T> cam = make_cam<T>(camp, W, H);
-  double cp[24];
-  for (int i = 0; i < 24; ++i) cp[i] = (double)camp[i];
+  double cp[kNumCam];
+  for (int i = 0; i < kNumCam; ++i) cp[i] = (double)camp[i];
   Cam<double> camd = make_cam<double>(cp, W, H);
   const int K = (sh_degree + 1) * (sh_degree + 1);
   const int nraw = 3 + 3 + 4 + 1 + K * 3;
