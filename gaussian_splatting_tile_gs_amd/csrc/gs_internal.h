@@ -26,6 +26,7 @@ struct DevCamera {
   float near_plane;
   float bg[3];
   int32_t tiles_x, tiles_y;
+  int32_t radius_mode, antialiased;  // the section-4 variants (0, 0: the default)
 };
 
 inline DevCamera to_dev(const gs_camera& c) {
@@ -37,6 +38,8 @@ inline DevCamera to_dev(const gs_camera& c) {
   d.bg[0] = c.background[0]; d.bg[1] = c.background[1]; d.bg[2] = c.background[2];
   d.tiles_x = (c.width + GS_TILE_SIZE - 1) / GS_TILE_SIZE;
   d.tiles_y = (c.height + GS_TILE_SIZE - 1) / GS_TILE_SIZE;
+  d.radius_mode = c.radius_mode;
+  d.antialiased = c.antialiased;
   return d;
 }
 

@@ -3,8 +3,11 @@
 // clamp). Definitions: "Gaussian splatting in PyTorch", sections 1 (activations), 2
 // (Sigma = R S S^T R^T), 3 (world->camera, EWA Jacobian with the clamp widened by 0.3
 // tan(half-FoV)) and 4 (eps2d dilation, conic, gsplat's per-axis radius with the opacity-aware
-// extent min(3.33, sqrt(2 ln(255 o)))). Every expression is evaluated in fp32 in a fixed order
-// with no contraction, so radii, rectangles and tile counts are reproducible bit for bit.
+// extent min(3.33, sqrt(2 ln(255 o))), and the section's two variants as camera options: the
+// 3DGS radius ceil(3 sqrt(lambda_max)) on both axes, and the antialiased opacity o times
+// sqrt(det Sigma2d / det Sigma') with Sigma2d the covariance before the dilation, on which the
+// cull and the extent then act). Every expression is evaluated in fp32 in a fixed order with no
+// contraction, so radii, rectangles and tile counts are reproducible bit for bit.
 #pragma once
 
 #include "gs_internal.h"
@@ -46,7 +49,8 @@ struct ProjF32 {
   bool defined;  // passed the near plane and every finiteness test
   bool drawn;    // defined, o >= 1/255 and at least one tile on screen
   bool clamp_x, clamp_y, det_clamped;
-  float m2d[2], con[3], depth, o, col[3];
+  float m2d[2], con[3], depth, o, col[3];  // o: the opacity the blend uses (o_act comp)
+  float o_act, comp;                        // sigmoid(logit) and the antialiased factor (1 if off)
   int32_t rad[2];
   uint32_t tiles;
 };
@@ -60,7 +64,8 @@ __device__ __forceinline__ ProjF32 project_f32(float m0, float m1, float m2, flo
   P.defined = P.drawn = P.clamp_x = P.clamp_y = P.det_clamped = false;
   P.m2d[0] = P.m2d[1] = 0.0f;
   P.con[0] = P.con[1] = P.con[2] = 0.0f;
-  P.depth = P.o = 0.0f;
+  P.depth = P.o = P.o_act = 0.0f;
+  P.comp = 1.0f;
   P.col[0] = P.col[1] = P.col[2] = 0.0f;
   P.rad[0] = P.rad[1] = 0;
   P.tiles = 0;
@@ -145,6 +150,11 @@ __device__ __forceinline__ ProjF32 project_f32(float m0, float m1, float m2, flo
   P.det_clamped = det_raw < 1e-10f;
   const float det = omax(det_raw, 1e-10f);
   const float con0 = c / det, con1 = -b / det, con2 = a / det;
+  // antialiased: o sqrt(det Sigma2d / det Sigma'), which keeps o 2 pi sqrt(det) of the undilated
+  // Gaussian
+  const float det0 = c00 * c11 - c01 * c01;
+  const float comp = cam.antialiased ? sqrtf(omax(det0, 0.0f) / det) : 1.0f;
+  const float o_eff = cam.antialiased ? o * comp : o;
   const float mx = fx * tx / tz + cx, my = fy * ty / tz + cy;
   if (!(fin(a) && fin(b) && fin(c) && fin(con0) && fin(con1) && fin(con2) && fin(mx) && fin(my))) return P;
 
@@ -172,17 +182,26 @@ __device__ __forceinline__ ProjF32 project_f32(float m0, float m1, float m2, flo
   P.m2d[0] = mx; P.m2d[1] = my;
   P.con[0] = con0; P.con[1] = con1; P.con[2] = con2;
   P.depth = tz;
-  P.o = o;
+  P.o = o_eff;
+  P.o_act = o;
+  P.comp = comp;
   P.defined = true;
 
-  // radius: opacity-aware per-axis extent; nothing drawn below 1/255
-  if (o < 1.0f / 255.0f) return P;
-  float kk = 2.0f * act_log(255.0f * o);
-  if (!(kk > 0.0f)) kk = 0.0f;
-  float k = sqrtf(kk);
-  if (k > 3.33f) k = 3.33f;
-  const float rx = omin(ceilf(k * sqrtf(a)), 16777216.0f);
-  const float ry = omin(ceilf(k * sqrtf(c)), 16777216.0f);
+  // radius: opacity-aware per-axis extent (or the 3DGS radius); nothing drawn below 1/255
+  if (o_eff < 1.0f / 255.0f) return P;
+  float rx, ry;
+  if (cam.radius_mode == 1) {
+    const float mid = 0.5f * (a + c);
+    const float lam = mid + sqrtf(omax(mid * mid - det, 0.1f));
+    rx = ry = omin(ceilf(3.0f * sqrtf(lam)), 16777216.0f);
+  } else {
+    float kk = 2.0f * act_log(255.0f * o_eff);
+    if (!(kk > 0.0f)) kk = 0.0f;
+    float k = sqrtf(kk);
+    if (k > 3.33f) k = 3.33f;
+    rx = omin(ceilf(k * sqrtf(a)), 16777216.0f);
+    ry = omin(ceilf(k * sqrtf(c)), 16777216.0f);
+  }
   const TileRect rc = tile_rect(mx, my, rx, ry, cam.tiles_x, cam.tiles_y);
   if (!(rc.x1 > rc.x0 && rc.y1 > rc.y0)) return P;
   P.rad[0] = (int32_t)rx;

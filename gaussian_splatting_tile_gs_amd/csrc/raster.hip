@@ -39,8 +39,8 @@ static_assert(kPlanMinChunk % kBatch == 0, "chunk boundaries must fall on batch 
 // Staged splat record: (mx, my, hA, hC), (B2, o, r, g), b. hA = A/2 log2e, B2 = B log2e,
 // hC = C/2 log2e, so that log2(e) sigma = hA dx^2 + hC dy^2 + B2 dx dy. Also returns the 4-bit
 // set of 8x8 quadrants of the tile where the splat can reach alpha >= 1/255 at some pixel
-// centre: the quadrant must meet the splat's pixel box (radii + 1 px) and its ellipse at that
-// level; a quadrant outside either skips the splat at every pixel anyway.
+// centre (its ellipse at that level meets the quadrant); elsewhere it skips at every pixel.
+// The test uses the splat alone, not its radii, so it holds for every radius rule.
 // An id >= n (impossible for a well-formed sorted list) loads a record that never contributes.
 __device__ __forceinline__ uint32_t load_record(uint32_t g, uint32_t n, const float* __restrict__ means2d,
                                                 const float* __restrict__ conics, const float* __restrict__ opac,
@@ -53,12 +53,10 @@ __device__ __forceinline__ uint32_t load_record(uint32_t g, uint32_t n, const fl
     return 0u;
   }
   const float2 m = *reinterpret_cast<const float2*>(means2d + 2 * g);
-  const int2 r = *reinterpret_cast<const int2*>(radii + 2 * g);
   const float A = conics[3 * g], B = conics[3 * g + 1], C = conics[3 * g + 2];
   a = make_float4(m.x, m.y, (0.5f * kLog2e) * A, (0.5f * kLog2e) * C);
   b = make_float4(kLog2e * B, opac[g], colors[3 * g], colors[3 * g + 1]);
   c = colors[3 * g + 2];
-  const float rx = (float)r.x + 1.0f, ry = (float)r.y + 1.0f;
   // Exact test of the splat's ellipse against each quadrant: the minimum over the quadrant's box
   // of pixel centres of s2 = log2(e) sigma (a positive definite quadratic in the offset, so the
   // minimum is 0 inside the box and otherwise lies on an edge, where it is a 1D quadratic) must
@@ -76,7 +74,6 @@ __device__ __forceinline__ uint32_t load_record(uint32_t g, uint32_t n, const fl
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const float x_lo = tx0 + (float)((q & 1) * 8) + 0.5f, y_lo = ty0 + (float)((q >> 1) * 8) + 0.5f;
-    const bool box = (m.x + rx >= x_lo) && (m.x - rx <= x_lo + 7.0f) && (m.y + ry >= y_lo) && (m.y - ry <= y_lo + 7.0f);
     const float x0 = x_lo - m.x, x1 = x0 + 7.0f, y0 = y_lo - m.y, y1 = y0 + 7.0f;
     // on the edge x = e the minimiser is y = -B2 e / (2 hC), clamped; likewise on y = e
     const float s_l = q2(x0, fminf(fmaxf(-qb * x0 * ic, y0), y1));
@@ -84,7 +81,7 @@ __device__ __forceinline__ uint32_t load_record(uint32_t g, uint32_t n, const fl
     const float s_t = q2(fminf(fmaxf(-qb * y0 * ia, x0), x1), y0);
     const float s_b = q2(fminf(fmaxf(-qb * y1 * ia, x0), x1), y1);
     const bool in = x0 <= 0.0f && x1 >= 0.0f && y0 <= 0.0f && y1 >= 0.0f;
-    const bool hit = box && (in || fminf(fminf(s_l, s_r), fminf(s_t, s_b)) <= lim);
+    const bool hit = in || fminf(fminf(s_l, s_r), fminf(s_t, s_b)) <= lim;
     qm |= hit ? (1u << q) : 0u;
   }
   return qm;
@@ -709,13 +706,14 @@ __global__ __launch_bounds__(256) void k_pbwd(
       for (int j = 0; j < 3; ++j) JW[a2 * 3 + j] = J[a2 * 3] * W[j] + J[a2 * 3 + 1] * W[3 + j] + J[a2 * 3 + 2] * W[6 + j];
     for (int a2 = 0; a2 < 2; ++a2)
       for (int j = 0; j < 3; ++j) Q[a2 * 3 + j] = JW[a2 * 3] * R[j] + JW[a2 * 3 + 1] * R[3 + j] + JW[a2 * 3 + 2] * R[6 + j];
-    double a = 0.3, b = 0.0, c = 0.3;
+    double a0 = 0.0, b = 0.0, c0 = 0.0;  // Sigma2d before the dilation
     for (int j = 0; j < 3; ++j) {
       const double s2 = s[j] * s[j];
-      a += s2 * Q[j] * Q[j];
+      a0 += s2 * Q[j] * Q[j];
       b += s2 * Q[j] * Q[3 + j];
-      c += s2 * Q[3 + j] * Q[3 + j];
+      c0 += s2 * Q[3 + j] * Q[3 + j];
     }
+    const double a = a0 + 0.3, c = c0 + 0.3;
     // Sigma_c = W Sigma W^T = (W R) S^2 (W R)^T, for J's dependence on t
     double WR[9], Sc[9];
     for (int i = 0; i < 3; ++i)
@@ -738,6 +736,19 @@ __global__ __launch_bounds__(256) void k_pbwd(
       ga = gC * 1e10;
       gb = -gB * 1e10;
       gc = gA * 1e10;
+    }
+    // ---- antialiased opacity o comp, comp = sqrt(det0 / det): d comp = comp / 2 (d det0 / det0 -
+    // d det / det), det0 = a0 c0 - b^2, det = a c - b^2, da = da0, dc = dc0 ----
+    double comp = 1.0;
+    if (cam.antialiased) {
+      const double det0 = a0 * c0 - b * b, det1 = a * c - b * b;
+      comp = det0 > 0.0 ? sqrt(det0 / det1) : 0.0;
+      if (comp > 0.0) {
+        const double h = 0.5 * G9[5] * o * comp;
+        ga += h * (c0 / det0 - c / det1);
+        gc += h * (a0 / det0 - a / det1);
+        gb += h * (2.0 * b / det1 - 2.0 * b / det0);
+      }
     }
     const double G2[4] = {ga, 0.5 * gb, 0.5 * gb, gc};
 
@@ -793,7 +804,7 @@ __global__ __launch_bounds__(256) void k_pbwd(
     for (int j = 0; j < 3; ++j) gm[j] = W[j] * gt[0] + W[3 + j] * gt[1] + W[6 + j] * gt[2];
 
     // ---- log-scales, opacity, colour ----
-    glogit = o * (1.0 - o) * G9[5];
+    glogit = o * (1.0 - o) * comp * G9[5];
     if (DEG == 0) {
       gsh[0] = G9[6]; gsh[1] = G9[7]; gsh[2] = G9[8];
     } else {

@@ -32,7 +32,11 @@ class GsError(RuntimeError):
 class GsCamera(ctypes.Structure):
     _fields_ = [("viewmat", ctypes.c_float * 16), ("fx", ctypes.c_float), ("fy", ctypes.c_float),
                 ("cx", ctypes.c_float), ("cy", ctypes.c_float), ("width", ctypes.c_int32),
-                ("height", ctypes.c_int32), ("near_plane", ctypes.c_float), ("background", ctypes.c_float * 3)]
+                ("height", ctypes.c_int32), ("near_plane", ctypes.c_float), ("background", ctypes.c_float * 3),
+                ("radius_mode", ctypes.c_int32), ("antialiased", ctypes.c_int32)]
+
+
+RADIUS_MODES = {"gsplat": 0, "3dgs": 1}
 
 
 class GsProjected(ctypes.Structure):
@@ -115,7 +119,8 @@ def _stream(stream):
 
 
 def make_camera(cam: dict) -> GsCamera:
-    """GsCamera from a camera dict (viewmat [4,4], fx, fy, cx, cy, width, height, near, background)."""
+    """GsCamera from a camera dict (viewmat [4,4], fx, fy, cx, cy, width, height, near, background;
+    optional radius_mode "gsplat" (default) or "3dgs", antialiased (default False))."""
     c = GsCamera()
     v = np.asarray(cam["viewmat"], np.float32).reshape(16)
     for i in range(16):
@@ -126,6 +131,8 @@ def make_camera(cam: dict) -> GsCamera:
     bg = cam.get("background", (0.0, 0.0, 0.0))
     for i in range(3):
         c.background[i] = float(bg[i])
+    c.radius_mode = RADIUS_MODES[cam.get("radius_mode", "gsplat")]
+    c.antialiased = 1 if cam.get("antialiased", False) else 0
     return c
 
 

@@ -53,6 +53,16 @@ typedef struct gs_camera {
   int32_t width, height;
   float near_plane;    /* Gaussians with camera z <= near_plane are culled (0.01 typical) */
   float background[3]; /* composited with the final transmittance */
+  /* Variants of section 4 of the PyTorch lesson (0 = the default; set them to 0 otherwise):
+   * radius_mode 0: gsplat's opacity-aware per-axis extent; 1: the original 3DGS radius
+   *   ceil(3 sqrt(lambda_max)) (root argument floored at 0.1) on both axes. A splat then draws
+   *   only in the tiles of its rectangle, even where its alpha would still reach 1/255.
+   * antialiased 1: the blend's opacity is o sqrt(det Sigma2d / det(Sigma2d + 0.3 I)), Sigma2d
+   *   the projected covariance before the dilation (gsplat's "antialiased" mode, Mip-Splatting's
+   *   2D filter); the cull and the extent use that opacity, and the backward differentiates it.
+   * The same options must be given to every call of one iteration. */
+  int32_t radius_mode;
+  int32_t antialiased;
 } gs_camera;
 
 /* Projected records, structure of arrays of length n, written by gs_project. A Gaussian is

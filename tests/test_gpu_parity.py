@@ -79,7 +79,8 @@ def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7
     torch.cuda.synchronize()
     pix = _full_pixels(cam_dict) if pixels is None else pixels
     o_fwd = oracle.render(o_proj, cam_dict, pixels=pix)
-    assert o_fwd["escapes"] == 0
+    if cam_dict.get("radius_mode", "gsplat") == "gsplat":
+        assert o_fwd["escapes"] == 0  # the opacity-aware rectangle holds every reached pixel
     dmax, nfrag = compare_forward(img.cpu().numpy(), fT.cpu().numpy(), nc.cpu().numpy(), ids_np, ranges_np, o_fwd,
                                   pix, W)
     assert nfrag <= max(2, len(pix) // 50), f"{nfrag} fragile pixels"
@@ -218,6 +219,26 @@ def test_deterministic_backward_capacity_and_arguments(env):
     assert gs.gs_bwd_det_workspace_bytes(params["n"], -1) == 0
 
 
+# ---- tile-count variants (camera options) ---------------------------------------------------------
+@pytest.mark.parametrize("case,opts,bwd", [
+    ("tiny", {"antialiased": True}, "atomic"), ("tiny", {"radius_mode": "3dgs"}, "atomic"),
+    ("ragged", {"antialiased": True, "radius_mode": "3dgs"}, "atomic"), ("tiny", {"antialiased": True}, "det"),
+    ("distill_30k", {"antialiased": True}, "atomic"), ("mid_150k_sh3", {"radius_mode": "3dgs"}, "atomic")])
+def test_variants(env, case, opts, bwd):
+    if case == "tiny":
+        wl = synth.WORKLOADS["tiny_1k"]
+        scene, cam, pix = synth.make_scene(wl), dict(synth.make_cameras(wl)[0]), None
+    elif case == "ragged":
+        scene = synth.random_scene(300, seed=21, width=37, height=23, focal=30.0, sh_degree=3, logit_std=2.0)
+        cam, pix = synth.make_camera(np.eye(4), 37, 23, 30.0, background=(0.2, 0.4, 0.6)), None
+    else:
+        wl = synth.WORKLOADS[case]
+        scene, cam = synth.make_scene(wl), dict(synth.make_cameras(wl)[0])
+        pix = synth.sample_pixels(cam["width"], cam["height"], 4096, seed=1)
+    cam.update(opts)
+    _pipeline_case(env, scene, cam, pixels=pix, label=f"{case} {opts}", bwd=bwd)
+
+
 # ---- edge cases ---------------------------------------------------------------------------------
 def test_empty_and_all_culled(env):
     gs, torch = env
@@ -317,6 +338,12 @@ def test_invalid_arguments(env):
     with pytest.raises(gs.GsError):
         gs.gs_project(-1, 0, params["means"], params["log_scales"], params["quats"], params["opacity_logits"],
                       params["sh"], cam, proj)
+    for field in ("radius_mode", "antialiased"):
+        opt = gs.make_camera(cam_d)
+        setattr(opt, field, 2)
+        with pytest.raises(gs.GsError):
+            gs.gs_project(10, 0, params["means"], params["log_scales"], params["quats"],
+                          params["opacity_logits"], params["sh"], opt, proj)
     # too small a workspace
     keys = torch.empty(100, device="cuda", dtype=torch.int64)
     ids = torch.empty(100, device="cuda", dtype=torch.int32)
