@@ -1,7 +1,8 @@
 """Throughput of one fwd+bwd iteration of the tile rasterizer on one MI355X.
 
 A step is one pass of the whole hot path for one camera: gs_project -> gs_bin_and_sort ->
-gs_rasterize_fwd -> gs_loss_l1 (L1 gradient against the camera's target image) ->
+gs_rasterize_fwd -> gs_loss_l1 (L1 gradient against the camera's target image; gs_loss_l1_ssim
+with 0.8 L1 + 0.2 (1 - SSIM) on the workloads whose loss that is) ->
 gs_rasterize_bwd (with --optimizer, then gs_adam_step). Steps cycle through the workload's cameras; all inputs (Gaussians, cameras,
 target images) are resident in HBM before the timed region. The default workload is the
 30,000-Gaussian distillation student at 1280x720 over 60 ring cameras, with target images
@@ -72,6 +73,8 @@ def kernel_bytes(name, stats):
         "pair_sort_pass": (16.0 * P + 8.0 * P / max(1, stats["pair_passes"])) if stats["pair_passes"] else 0.0,
         "project": stats["project_bytes"],
         "loss_l1": 12.0 * stats["pixels"] * 3,
+        # two passes: 24 B in, 36 B of partials out; 36 B of partials and 24 B in, 12 B out
+        "loss_ssim": (24.0 + 36.0 + 36.0 + 24.0 + 12.0) * stats["pixels"],
     }.get(name)
 
 
@@ -201,6 +204,8 @@ def main():
 
     pipe = gs.Pipeline(params, W, H, pair_capacity=1 << 16)
     pipe.deterministic = args.deterministic
+    # the workload's loss: L1, or 0.8 L1 + 0.2 (1 - SSIM) (gs_loss_l1_ssim)
+    pipe.ssim_lambda = 0.2 if wl.loss == "l1_dssim" else 0.0
     pairs = []
     for cam in cams:  # size the pair buffers for every camera
         pipe.project(cam)
@@ -261,6 +266,7 @@ def main():
         "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
         "mpix_per_s": its * W * H / 1e6, "sorted_pairs_per_s": steps_pairs / elapsed,
         "config": {"workload": wl.name, "gaussians": wl.n, "width": W, "height": H, "cameras": ncam,
+                   "loss": "0.8 L1 + 0.2 (1 - SSIM)" if pipe.ssim_lambda > 0 else "L1",
                    "sh_degree": wl.sh_degree, "teacher_gaussians": int(teacher["means"].shape[0]),
                    "mean_pairs_per_camera": float(np.mean(pairs)), "parallelism": "single GPU"},
     }

@@ -77,6 +77,8 @@ def load():
         "gs_rasterize_bwd": (i32, [i32, i32, P, P, P, P, P, cam_p, proj_p, P, P, P, P, P, P, P, P, sz, P, P, P, P, P,
                                    P, P, P]),
         "gs_loss_l1": (i32, [i32, i32, P, P, P, P, P]),
+        "gs_loss_ssim_workspace_bytes": (sz, [i32, i32]),
+        "gs_loss_l1_ssim": (i32, [i32, i32, P, P, ctypes.c_float, P, sz, P, P, P]),
         "gs_adam_state_floats": (sz, [i32, i32]),
         "gs_adam_step": (i32, [i32, i32, i32, ctypes.POINTER(GsAdamConfig)] + [P] * 12 + [P]),
         "gs_status_string": (ctypes.c_char_p, [i32]),
@@ -211,6 +213,16 @@ def gs_loss_l1(width, height, image, target, dL_dimage, loss=None, stream=None):
                                     _stream(stream)))
 
 
+def gs_loss_ssim_workspace_bytes(width, height) -> int:
+    return int(load().gs_loss_ssim_workspace_bytes(width, height))
+
+
+def gs_loss_l1_ssim(width, height, image, target, lam, workspace, dL_dimage, loss=None, stream=None):
+    return _check(load().gs_loss_l1_ssim(width, height, _ptr(image), _ptr(target), float(lam), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _ptr(dL_dimage), _ptr(loss),
+                                         _stream(stream)))
+
+
 def gs_timing_enable(on: bool):
     return _check(load().gs_timing_enable(1 if on else 0))
 
@@ -306,6 +318,7 @@ class Pipeline:
         self.num_pairs_dev = torch.zeros(1, device=device, dtype=torch.int64)
         self.schedule = "chunks"  # "chunks": plan + checkpoints; "order": plan only; "tiles": neither
         self.deterministic = False  # True: the bitwise-reproducible backward
+        self.ssim_lambda = 0.0  # > 0: the loss is (1 - lambda) L1 + lambda (1 - SSIM)
         self._alloc_pairs(pair_capacity)
 
     def _alloc_pairs(self, cap):
@@ -355,7 +368,17 @@ class Pipeline:
                          raster_ws=self.raster_ws if ck else None)
 
     def loss_l1(self, target, loss=None, stream=None):
-        gs_loss_l1(self.width, self.height, self.image, target, self.dL_dimage, loss, stream)
+        """The training loss's gradient into self.dL_dimage: L1, or with self.ssim_lambda > 0
+        (1 - lambda) L1 + lambda (1 - SSIM)."""
+        lam = getattr(self, "ssim_lambda", 0.0)
+        if lam > 0.0:
+            if getattr(self, "_ssim_ws", None) is None:
+                self._ssim_ws = torch.empty(gs_loss_ssim_workspace_bytes(self.width, self.height), device=self.device,
+                                            dtype=torch.uint8)
+            gs_loss_l1_ssim(self.width, self.height, self.image, target, lam, self._ssim_ws, self.dL_dimage, loss,
+                            stream)
+        else:
+            gs_loss_l1(self.width, self.height, self.image, target, self.dL_dimage, loss, stream)
 
     def backward(self, cam: GsCamera, dL_dimage=None, eval_count=None, stream=None):
         """self.deterministic selects gs_rasterize_bwd_deterministic (records sized by the pair

@@ -241,6 +241,26 @@ gs_status gs_loss_l1(int32_t width, int32_t height, const float* d_image, const 
                      float* d_dL_dimage, float* d_loss, void* stream);
 
 /*
+ * gs_loss_l1_ssim -- the full training loss of section 7 of the PyTorch lesson,
+ * L = (1 - lambda) L1 + lambda (1 - SSIM) (lambda = 0.2 there), and dL/dimage. SSIM is that of
+ * Wang, Bovik, Sheikh and Simoncelli (2004), which the lesson names without fixing a window: per
+ * channel, local means and (co)variances under an 11 x 11 Gaussian window of standard deviation
+ * 1.5 (normalised to sum 1) over the image padded with zeros, C1 = 0.01^2, C2 = 0.03^2,
+ * S = (2 mu_x mu_y + C1)(2 s_xy + C2) / ((mu_x^2 + mu_y^2 + C1)(s_xx + s_yy + C2)), and SSIM the
+ * mean of S over the h*w*3 values; L1 = mean |image - target| with sign(0) = 0 in its gradient.
+ * Inputs: d_image, d_target [h,w,3]; lambda in [0, 1]; d_workspace (device, 256-byte aligned) of
+ * at least gs_loss_ssim_workspace_bytes(width, height) bytes, contents arbitrary on entry.
+ * Outputs: d_dL_dimage [h,w,3]; d_loss (device float[1], may be NULL) receives L, its sums added
+ * in a fixed order (the same bits every run).
+ * Errors: GS_ERR_INVALID_ARG for a size <= 0, a NULL pointer, lambda outside [0, 1], a small or
+ * misaligned workspace; GS_ERR_LIMIT for 9 h w >= 2^31.
+ */
+size_t gs_loss_ssim_workspace_bytes(int32_t width, int32_t height);
+gs_status gs_loss_l1_ssim(int32_t width, int32_t height, const float* d_image, const float* d_target, float lambda,
+                          void* d_workspace, size_t workspace_bytes, float* d_dL_dimage, float* d_loss,
+                          void* stream);
+
+/*
  * gs_adam_step -- one optimizer step on the raw parameters: Adam (Kingma and Ba 2015, in the form
  * torch.optim.Adam uses, which the fitting loop of section 7 of the PyTorch lesson calls) with a
  * learning rate per group (the lesson lists per-parameter rates for 3DGS training), plus the

@@ -66,3 +66,8 @@ def test_host_only_helpers(lib):
     a, b = lib.gs_bwd_det_workspace_bytes(1000, 10000), lib.gs_bwd_det_workspace_bytes(1000, 20000)
     assert abs((b - a) - 36 * 10000) < 256 and a >= 1000 * 40 + 36 * 10000
     assert lib.gs_bwd_det_workspace_bytes(1000, -1) == 0 and lib.gs_bwd_det_workspace_bytes(1000, 1 << 30) == 0
+    lib.gs_loss_ssim_workspace_bytes.restype = ctypes.c_size_t
+    lib.gs_loss_ssim_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    # nine partial planes of h*w floats plus a float2 per 16x16 tile, each part 256-byte aligned
+    assert lib.gs_loss_ssim_workspace_bytes(980, 545) >= 980 * 545 * 36 + 62 * 35 * 8
+    assert lib.gs_loss_ssim_workspace_bytes(0, 10) == 0

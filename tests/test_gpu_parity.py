@@ -427,3 +427,39 @@ def test_loss_l1(env):
     torch.cuda.synchronize()
     assert np.allclose(big_g[1:].cpu().numpy(), want.ravel(), rtol=1e-6, atol=0) and big_g[0].item() == 0.0
     assert loss.item() == pytest.approx(np.abs(img.astype(np.float64) - tgt).mean(), rel=1e-5)
+
+
+@pytest.mark.parametrize("W,H,lam", [(37, 23, 0.2), (128, 128, 0.2), (980, 545, 0.2), (64, 48, 1.0), (64, 48, 0.0)])
+def test_loss_l1_ssim(env, W, H, lam):
+    """gs_loss_l1_ssim against the loss oracle (float64): the loss value and dL/dimage. The
+    statistics run in fp32 (window sums of 121 terms, variances as e_xx - mu^2, hardware
+    reciprocals), hence a tolerance of 1e-4 of each element plus 1e-4 of the largest SSIM-part
+    magnitude."""
+    from oracle import loss as oloss
+    gs, torch = env
+    rng = np.random.default_rng(W * 7 + H)
+    x = rng.uniform(0, 1, (H, W, 3)).astype(np.float32)
+    # a target that shares structure with the image (smooth blend plus noise), so S spans a range
+    y = np.clip(0.6 * x + 0.4 * np.roll(x, 3, axis=1) + rng.normal(0, 0.05, x.shape), 0, 1).astype(np.float32)
+    y[: H // 4] = x[: H // 4]  # a band of equal values: sign(0) = 0 and S = 1 there
+    xd, yd = torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda()
+    ws = torch.empty(gs.gs_loss_ssim_workspace_bytes(W, H), device="cuda", dtype=torch.uint8)
+    grad = torch.empty_like(xd)
+    loss = torch.empty(1, device="cuda")
+    gs.gs_loss_l1_ssim(W, H, xd, yd, lam, ws, grad, loss)
+    torch.cuda.synchronize()
+    val_ref, g_ref = oloss.loss_l1_ssim(x.astype(np.float64), y.astype(np.float64), lam)
+    g = grad.cpu().numpy().astype(np.float64)
+    ssim_part = g_ref - (1 - lam) * np.sign(x.astype(np.float64) - y.astype(np.float64)) / x.size
+    tol = 1e-4 * np.abs(g_ref) + 1e-4 * np.abs(ssim_part).max() + 1e-12
+    err = np.abs(g - g_ref)
+    log(f"[loss_ssim {W}x{H} lam={lam}] loss {loss.item():.7f} vs {val_ref:.7f}; grad max err/tol "
+        f"{(err / tol).max():.3f}")
+    assert np.all(err <= tol)
+    assert abs(loss.item() - val_ref) <= 1e-5 * abs(val_ref) + 1e-6
+    # the loss value is summed in a fixed order: the same bits again
+    first = loss.clone()
+    ws.random_(0, 256)
+    gs.gs_loss_l1_ssim(W, H, xd, yd, lam, ws, grad, loss)
+    torch.cuda.synchronize()
+    assert torch.equal(first, loss)
