@@ -8,6 +8,12 @@ target images) are resident in HBM before the timed region. The default workload
 30,000-Gaussian distillation student at 1280x720 over 60 ring cameras, with target images
 rendered once (by the forward path) from a seeded 300,000-Gaussian teacher.
 
+Camera iterations are independent (the Gaussians are only read), so by default four run at once,
+each on its own HIP stream with its own buffers: at this size every kernel of one iteration is
+short and latency-bound, and the concurrent iterations fill the GPU. The same steps run again one
+at a time afterwards ("single_stream" in the output). --optimizer runs one stream (every Adam step
+changes what the next iteration reads).
+
 Prints one JSON line: the iterations/s metric, Mpix/s and sorted pairs/s, per-kernel times from
 HIP events recorded by the library on the stream it launches on (a second pass over the same
 steps, right after the timed one), the roofline of the dominant kernel and the CPU oracle timed
@@ -48,6 +54,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--streams", type=int, default=4,
+                    help="camera iterations in flight at once, each on its own HIP stream with its own buffers "
+                         "(1 with --optimizer, whose updates every iteration must see)")
     ap.add_argument("--deterministic", action="store_true",
                     help="the bitwise-reproducible backward (gs_rasterize_bwd_deterministic)")
     ap.add_argument("--optimizer", action="store_true",
@@ -202,31 +211,54 @@ def main():
     torch.cuda.synchronize()
     log(f"{wl.name}: {len(cams)} target images rendered from the {teacher['means'].shape[0]}-Gaussian teacher")
 
-    pipe = gs.Pipeline(params, W, H, pair_capacity=1 << 16)
-    pipe.deterministic = args.deterministic
-    # the workload's loss: L1, or 0.8 L1 + 0.2 (1 - SSIM) (gs_loss_l1_ssim)
-    pipe.ssim_lambda = 0.2 if wl.loss == "l1_dssim" else 0.0
+    nstreams = 1 if args.optimizer else max(1, args.streams)
+
+    def make_pipe():
+        p = gs.Pipeline(params, W, H, pair_capacity=1 << 16)
+        p.deterministic = args.deterministic
+        # the workload's loss: L1, or 0.8 L1 + 0.2 (1 - SSIM) (gs_loss_l1_ssim)
+        p.ssim_lambda = 0.2 if wl.loss == "l1_dssim" else 0.0
+        return p
+
+    pipe = make_pipe()
     pairs = []
     for cam in cams:  # size the pair buffers for every camera
         pipe.project(cam)
         pairs.append(pipe.bin(cam))
     need = max(pairs)
     # with the optimizer the scene drifts, so leave more room
-    pipe.reserve_pairs(int(need * (1.5 if args.optimizer else 1.1)) + 1024)
+    cap = int(need * (1.5 if args.optimizer else 1.1)) + 1024
+    pipe.reserve_pairs(cap)
+    # concurrent camera iterations: their own buffers (pairs, images, workspaces, gradients) and
+    # streams (default priority); the Gaussians are shared read-only
+    pipes = [pipe] + [make_pipe() for _ in range(nstreams - 1)]
+    for p in pipes[1:]:
+        p.reserve_pairs(cap)
+    streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(nstreams - 1)]
     ncam = len(cams)
     adam_cfg = gs.adam_config()
 
-    def step(i):
+    def step(i, k=0):
         # no host wait anywhere in a step: the pair buffers already hold every camera's pairs
         c = i % ncam
-        if wl.backward:
-            pipe.iteration(cams[c], targets[c], wait=False)
-            if args.optimizer:
-                pipe.adam_step(adam_cfg)
-        else:
-            pipe.project(cams[c])
-            pipe.bin(cams[c], wait=False)
-            pipe.forward(cams[c], checkpoints=False)  # a render: no backward follows
+        p, st = pipes[k], streams[k]
+        with torch.cuda.stream(st):
+            if wl.backward:
+                p.iteration(cams[c], targets[c], stream=st, wait=False)
+                if args.optimizer:
+                    p.adam_step(adam_cfg, stream=st)
+            else:
+                p.project(cams[c], stream=st)
+                p.bin(cams[c], stream=st, wait=False)
+                p.forward(cams[c], stream=st, checkpoints=False)  # a render: no backward follows
+
+    def timed(nsteps, first, k_streams):
+        torch.cuda.synchronize()
+        ta = time.perf_counter()
+        for i in range(nsteps):
+            step(first + i, i % k_streams)
+        torch.cuda.synchronize()
+        return time.perf_counter() - ta
 
     if args.copy_calibration_mib:
         src = torch.ones(args.copy_calibration_mib << 18, device="cuda")
@@ -237,25 +269,28 @@ def main():
         del src, dst
 
     for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
+        step(i, i % nstreams)
+    elapsed = timed(args.steps, args.warmup, nstreams)
     its = args.steps / elapsed
-    log(f"timed {args.steps} steps: {1e3 * elapsed / args.steps:.4f} ms/step")
-    last = (args.warmup + args.steps - 1) % ncam
+    log(f"timed {args.steps} steps on {nstreams} stream(s): {1e3 * elapsed / args.steps:.4f} ms/step")
     if args.optimizer:
         # the scene moved: every camera's pairs must still fit the buffers the steps ran with
         P_last = int(pipe.num_pairs_dev.item())
         assert P_last <= pipe.capacity, "pair buffers overflowed"
         steps_pairs = args.steps * P_last
     else:
-        assert int(pipe.num_pairs_dev.item()) == pairs[last] <= pipe.capacity, "pair count changed between runs"
+        for k, p in enumerate(pipes):
+            ks = [i for i in range(args.steps) if i % nstreams == k]
+            if ks:
+                last = (args.warmup + ks[-1]) % ncam
+                assert int(p.num_pairs_dev.item()) == pairs[last] <= p.capacity, "pair count changed between runs"
         steps_pairs = sum(pairs[(args.warmup + i) % ncam] for i in range(args.steps))
+    # the same steps one at a time (one stream): the latency-bound rate of a single camera
+    single = None
+    if nstreams > 1:
+        e1 = timed(args.steps, args.warmup, 1)
+        single = {"value": args.steps / e1, "ms_per_step": 1e3 * e1 / args.steps}
+        log(f"one stream: {1e3 * e1 / args.steps:.4f} ms/step")
 
     result = {
         "metric": "fwd+bwd iterations/sec and Mpix/s at 30k Gaussians 1280x720; sorted pairs/sec"
@@ -267,10 +302,12 @@ def main():
         "mpix_per_s": its * W * H / 1e6, "sorted_pairs_per_s": steps_pairs / elapsed,
         "config": {"workload": wl.name, "gaussians": wl.n, "width": W, "height": H, "cameras": ncam,
                    "loss": "0.8 L1 + 0.2 (1 - SSIM)" if pipe.ssim_lambda > 0 else "L1",
+                   "concurrent_cameras": nstreams,
                    "sh_degree": wl.sh_degree, "teacher_gaussians": int(teacher["means"].shape[0]),
                    "mean_pairs_per_camera": float(np.mean(pairs)), "parallelism": "single GPU"},
     }
 
+    result["single_stream"] = single
     if not args.no_kernel_timing:
         # per-kernel HIP events (recorded by the library on the stream it launches on) over a
         # second pass of the same steps; then an untimed pass with the evaluation counters on
