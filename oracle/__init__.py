@@ -208,7 +208,8 @@ def render(proj, cam, pixels=None, dtype=np.float32, band_eps=None):
     opacity-aware radius that is every Gaussian that can reach it, i.e. the dense render).
 
     pixels: None (whole image, row-major) or int array [M,2] of (row, col).
-    Returns dict image [M,3] f64, final_T [M] f64, last_id [M] int32 (-1: none),
+    Returns dict image [M,3] f64, depth [M] f64 (the depth channel: camera z blended with the same
+    weights, background depth 0), final_T [M] f64, last_id [M] int32 (-1: none),
     n_contrib [M] int32 (global count), fragile [M] bool, escapes (int), n_near (int).
     For pixels=None the arrays are reshaped to [H,W,...].
     """
@@ -226,6 +227,7 @@ def render(proj, cam, pixels=None, dtype=np.float32, band_eps=None):
         pix = _c(pixels, np.int32).reshape(-1, 2)
         M = pix.shape[0]
     image = np.empty((M, 3))
+    depth = np.empty(M)
     final_T = np.empty(M)
     last_id = np.empty(M, np.int32)
     n_contrib = np.empty(M, np.int32)
@@ -234,26 +236,27 @@ def render(proj, cam, pixels=None, dtype=np.float32, band_eps=None):
     nev = ctypes.c_int64(0)
     fn = getattr(lib, "orc_render_" + _suffix(dtype))
     fn(n, *[_p(a) for a in ins], W, H, _p(bg), M, _p(pix), float(band_eps), _p(image), _p(final_T),
-       _p(last_id), _p(n_contrib), _p(fragile), ctypes.byref(esc), ctypes.byref(nev))
-    out = {"image": image, "final_T": final_T, "last_id": last_id, "n_contrib": n_contrib,
+       _p(last_id), _p(n_contrib), _p(fragile), ctypes.byref(esc), ctypes.byref(nev), _p(depth))
+    out = {"image": image, "depth": depth, "final_T": final_T, "last_id": last_id, "n_contrib": n_contrib,
            "fragile": fragile.astype(bool), "escapes": int(esc.value), "n_near": int(nev.value)}
     if pixels is None:
         out["image"] = image.reshape(H, W, 3)
-        for k in ("final_T", "last_id", "n_contrib", "fragile"):
+        for k in ("depth", "final_T", "last_id", "n_contrib", "fragile"):
             out[k] = out[k].reshape(H, W)
     return out
 
 
-GRAD2D_NAMES = ("mean2d_x", "mean2d_y", "conic_A", "conic_B", "conic_C", "opacity", "r", "g", "b")
+GRAD2D_NAMES = ("mean2d_x", "mean2d_y", "conic_A", "conic_B", "conic_C", "opacity", "r", "g", "b", "depth")
 
 
-def render_backward(proj, cam, dL_dimage, pixels=None, dtype=np.float32, band_eps=None):
-    """Analytic backward of the dense render.
+def render_backward(proj, cam, dL_dimage, pixels=None, dtype=np.float32, band_eps=None, dL_ddepth=None):
+    """Analytic backward of the per-pixel render.
 
-    dL_dimage: [H,W,3] (pixels=None) or [M,3] matching ``pixels``.
-    Returns (g2d [N,9] float64, aref [N,9] float64): per Gaussian d/d(mu'x, mu'y, A, B, C,
-    opacity, r, g, b) and the rounding scale of each (sum over pixels of the magnitudes of the
-    terms each contribution is computed from).
+    dL_dimage: [H,W,3] (pixels=None) or [M,3] matching ``pixels``; dL_ddepth (optional): [H,W] or
+    [M], the gradient on the depth channel.
+    Returns (g2d [N,10] float64, aref [N,10] float64): per Gaussian d/d(mu'x, mu'y, A, B, C,
+    opacity, r, g, b, depth) and the rounding scale of each (sum over pixels of the magnitudes of
+    the terms each contribution is computed from).
     """
     lib = load()
     if band_eps is None:
@@ -269,11 +272,20 @@ def render_backward(proj, cam, dL_dimage, pixels=None, dtype=np.float32, band_ep
         pix = _c(pixels, np.int32).reshape(-1, 2)
         M = pix.shape[0]
     g = _c(dL_dimage, np.float64).reshape(M, 3)
-    g2d = np.empty((n, 9))
-    aref = np.empty((n, 9))
+    gd = _c(dL_ddepth, np.float64).reshape(M) if dL_ddepth is not None else None
+    g2d = np.empty((n, 10))
+    aref = np.empty((n, 10))
     fn = getattr(lib, "orc_render_bwd_" + _suffix(dtype))
-    fn(n, *[_p(a) for a in ins], W, H, _p(bg), M, _p(pix), float(band_eps), _p(g), _p(g2d), _p(aref))
+    fn(n, *[_p(a) for a in ins], W, H, _p(bg), M, _p(pix), float(band_eps), _p(g), _p(gd), _p(g2d), _p(aref))
     return g2d, aref
+
+
+def _pad10(a, n):
+    """[N,9] (no depth channel) or [N,10] 2D gradients as [N,10]."""
+    a = _c(a, np.float64).reshape(n, -1)
+    if a.shape[1] == 9:
+        a = np.concatenate([a, np.zeros((n, 1))], 1)
+    return np.ascontiguousarray(a)
 
 
 def project_backward(scene, cam, g2d, aref2d=None, dtype=np.float32):
@@ -295,8 +307,8 @@ def project_backward(scene, cam, g2d, aref2d=None, dtype=np.float32):
     sh = _c(scene["sh"], dtype).reshape(n, K, 3)
     camp = camera_array(cam, dtype)
     W, H = int(cam["width"]), int(cam["height"])
-    g = _c(g2d, np.float64).reshape(n, 9)
-    ar = _c(aref2d, np.float64).reshape(n, 9) if aref2d is not None else None
+    g = _pad10(g2d, n)
+    ar = _pad10(aref2d, n) if aref2d is not None else None
     out = {"means": np.empty((n, 3)), "log_scales": np.empty((n, 3)), "quats": np.empty((n, 4)),
            "opacity_logits": np.empty(n), "sh": np.empty((n, K, 3))}
     aref_raw = np.empty((n, 11 + 3 * K)) if ar is not None else None
@@ -319,10 +331,10 @@ def split_raw(flat, sh_degree):
             "opacity_logits": flat[:, 10], "sh": flat[:, 11:].reshape(n, K, 3)}
 
 
-def forward_backward(scene, cam, dL_dimage, pixels=None, dtype=np.float32):
+def forward_backward(scene, cam, dL_dimage, pixels=None, dtype=np.float32, dL_ddepth=None):
     """Convenience: project, render, backward to raw parameters (with tolerance floors)."""
     proj = project(scene, cam, dtype)
     fwd = render(proj, cam, pixels, dtype)
-    g2d, aref = render_backward(proj, cam, dL_dimage, pixels, dtype)
+    g2d, aref = render_backward(proj, cam, dL_dimage, pixels, dtype, dL_ddepth=dL_ddepth)
     raw = project_backward(scene, cam, g2d, aref, dtype)
     return proj, fwd, g2d, aref, raw

@@ -409,6 +409,7 @@ void project_one(const T* mean, const T* log_scale, const T* quat, T logit, cons
 // ---------------------------------------------------------------------------------------------
 template <class T> struct Splat2D {
   T mx, my, A, B, C, o, col[3];
+  T z;           // camera depth: the value the depth channel blends
   T skip_above;  // ln(255 o) + 1e-3: sigma above this implies alpha < 1/255 (exact shortcut)
 };
 
@@ -492,7 +493,7 @@ void build_splats(int n, const T* means2d, const T* conics, const T* opac, const
   order.clear();
   for (int g = 0; g < n; ++g) {
     S[g] = {means2d[2 * g], means2d[2 * g + 1], conics[3 * g], conics[3 * g + 1], conics[3 * g + 2],
-            opac[g], {colors[3 * g], colors[3 * g + 1], colors[3 * g + 2]}, (T)0};
+            opac[g], {colors[3 * g], colors[3 * g + 1], colors[3 * g + 2]}, depths[g], (T)0};
     S[g].skip_above = opac[g] > (T)0 ? (T)(std::log(255.0 * (double)opac[g]) + 1e-3) : (T)0;
     if (tiles[g] > 0) order.push_back(g);
   }
@@ -551,7 +552,7 @@ int render_impl(int n, const T* means2d, const T* conics, const T* opac, const T
                 const T* depths, const uint32_t* tiles, const int32_t* rects, int W, int H,
                 const T* bg, int64_t npix, const int32_t* pix, double band_eps, double* image,
                 double* final_T, int32_t* last_id, int32_t* n_contrib, uint8_t* fragile,
-                int64_t* escapes, int64_t* n_eval) {
+                int64_t* escapes, int64_t* n_eval, double* depth_img) {
   std::vector<Splat2D<T>> S;
   std::vector<int> order;
   build_splats<T>(n, means2d, conics, opac, colors, depths, tiles, S, order);
@@ -573,6 +574,12 @@ int render_impl(int n, const T* means2d, const T* conics, const T* opac, const T
       for (size_t i = 0; i < tr.contrib.size(); ++i)
         for (int ch = 0; ch < 3; ++ch) acc[ch] += (double)S[tr.contrib[i].g].col[ch] * al[i] * Ti[i];
       for (int ch = 0; ch < 3; ++ch) image[3 * p + ch] = acc[ch] + Tf * (double)bg[ch];
+      if (depth_img) {
+        // the depth channel: camera z blended with the same weights, background depth 0
+        double d = 0.0;
+        for (size_t i = 0; i < tr.contrib.size(); ++i) d += (double)S[tr.contrib[i].g].z * al[i] * Ti[i];
+        depth_img[p] = d;
+      }
       final_T[p] = Tf;
       last_id[p] = tr.contrib.empty() ? -1 : tr.contrib.back().g;
       n_contrib[p] = (int32_t)tr.contrib.size();
@@ -591,8 +598,10 @@ int render_impl(int n, const T* means2d, const T* conics, const T* opac, const T
 //   dC/dc_i = a_i T_i,  dC/da_i = c_i T_i - S_i / (1 - a_i),  S_i = sum_{j>i} c_j a_j T_j + T_final bg,
 //   a = o exp(-sigma) when below the cap (else constant 0.99): da/do = exp(-sigma), da/dsigma = -a,
 //   sigma = 0.5 (A dx^2 + C dy^2) + B dx dy with dx = mu'_x - px.
-// Output per Gaussian (9): d mu'_x, d mu'_y, dA, dB, dC, d opacity, d colour (3), accumulated in
-// double. aref is the rounding scale of each sum, for tolerance floors: per pixel, the absolute
+// With a depth channel (dL_ddepth, may be NULL) its value z_i joins the colours: D = sum_i z_i a_i T_i
+// (background depth 0), so dD/dz_i = a_i T_i and dD/da_i = z_i T_i - S^D_i / (1 - a_i).
+// Output per Gaussian (10): d mu'_x, d mu'_y, dA, dB, dC, d opacity, d colour (3), d depth,
+// accumulated in double. aref is the rounding scale of each sum, for tolerance floors: per pixel, the absolute
 // values of the terms each contribution is computed from (|c| T + |S| / (1 - a) for dC/da, which
 // cancels when a splat's colour matches what lies behind it), times max(1, e_T / 1e-5) with e_T
 // the pixel's bound on the relative rounding of its transmittance, summed over pixels.
@@ -600,7 +609,7 @@ template <class T>
 int render_bwd_impl(int n, const T* means2d, const T* conics, const T* opac, const T* colors,
                     const T* depths, const uint32_t* tiles, const int32_t* rects, int W, int H,
                     const T* bg, int64_t npix, const int32_t* pix, double band_eps,
-                    const double* dL_dimg, double* g2d, double* aref) {
+                    const double* dL_dimg, const double* dL_ddepth, double* g2d, double* aref) {
   std::vector<Splat2D<T>> S;
   std::vector<int> order;
   build_splats<T>(n, means2d, conics, opac, colors, depths, tiles, S, order);
@@ -610,8 +619,8 @@ int render_bwd_impl(int n, const T* means2d, const T* conics, const T* opac, con
 #pragma omp parallel
   {
     const int tid = thread_id();
-    accg[tid].assign((size_t)n * 9, 0.0);
-    acca[tid].assign((size_t)n * 9, 0.0);
+    accg[tid].assign((size_t)n * 10, 0.0);
+    acca[tid].assign((size_t)n * 10, 0.0);
     double* G = accg[tid].data();
     double* Aa = acca[tid].data();
     Trace tr;
@@ -619,7 +628,8 @@ int render_bwd_impl(int n, const T* means2d, const T* conics, const T* opac, con
 #pragma omp for schedule(dynamic, 16)
     for (int64_t p = 0; p < npix; ++p) {
       const double* gp = dL_dimg + 3 * p;
-      if (gp[0] == 0.0 && gp[1] == 0.0 && gp[2] == 0.0) continue;
+      const double gd = dL_ddepth ? dL_ddepth[p] : 0.0;
+      if (gp[0] == 0.0 && gp[1] == 0.0 && gp[2] == 0.0 && gd == 0.0) continue;
       int row, col;
       pixel_of(pix, W, p, row, col);
       T px = (T)col + (T)0.5, py = (T)row + (T)0.5;
@@ -631,6 +641,7 @@ int render_bwd_impl(int n, const T* means2d, const T* conics, const T* opac, con
       const double tscale = std::max(1.0, tr.errT / 1e-5);
       double Sacc[3] = {Tf * (double)bg[0], Tf * (double)bg[1], Tf * (double)bg[2]};
       double Sabs[3] = {Tf * std::fabs((double)bg[0]), Tf * std::fabs((double)bg[1]), Tf * std::fabs((double)bg[2])};
+      double SD = 0.0, SDabs = 0.0;  // the depth channel's S (background depth 0)
       for (int i = (int)tr.contrib.size() - 1; i >= 0; --i) {
         const int g = tr.contrib[i].g;
         const Splat2D<T>& s = S[g];
@@ -640,11 +651,16 @@ int render_bwd_impl(int n, const T* means2d, const T* conics, const T* opac, con
           gal += gp[ch] * (c[ch] * Ti[i] - Sacc[ch] / (1.0 - al[i]));
           gal_mag += std::fabs(gp[ch]) * (std::fabs(c[ch]) * Ti[i] + Sabs[ch] / (1.0 - al[i]));
         }
-        double contrib[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0}, mag[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+        const double z = (double)s.z;
+        gal += gd * (z * Ti[i] - SD / (1.0 - al[i]));
+        gal_mag += std::fabs(gd) * (std::fabs(z) * Ti[i] + SDabs / (1.0 - al[i]));
+        double contrib[10] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0}, mag[10] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
         for (int ch = 0; ch < 3; ++ch) {
           contrib[6 + ch] = al[i] * Ti[i] * gp[ch];
           mag[6 + ch] = std::fabs(contrib[6 + ch]);
         }
+        contrib[9] = al[i] * Ti[i] * gd;
+        mag[9] = std::fabs(contrib[9]);
         if (!tr.contrib[i].capped) {
           double dx = (double)s.mx - (double)px, dy = (double)s.my - (double)py;
           contrib[5] = Gi[i] * gal;
@@ -659,18 +675,20 @@ int render_bwd_impl(int n, const T* means2d, const T* conics, const T* opac, con
                                 std::fabs(dsig[3]), std::fabs(dsig[4])};
           for (int k = 0; k < 5; ++k) mag[k] = al[i] * gal_mag * dsig_mag[k];
         }
-        for (int k = 0; k < 9; ++k) {
-          G[(size_t)g * 9 + k] += contrib[k];
-          Aa[(size_t)g * 9 + k] += mag[k] * tscale;
+        for (int k = 0; k < 10; ++k) {
+          G[(size_t)g * 10 + k] += contrib[k];
+          Aa[(size_t)g * 10 + k] += mag[k] * tscale;
         }
         for (int ch = 0; ch < 3; ++ch) {
           Sacc[ch] += c[ch] * al[i] * Ti[i];
           Sabs[ch] += std::fabs(c[ch]) * al[i] * Ti[i];
         }
+        SD += z * al[i] * Ti[i];
+        SDabs += std::fabs(z) * al[i] * Ti[i];
       }
     }
   }
-  for (size_t i = 0; i < (size_t)n * 9; ++i) {
+  for (size_t i = 0; i < (size_t)n * 10; ++i) {
     double sg = 0, sa = 0;
     for (int t = 0; t < nt; ++t) {
       sg += accg[t][i];
@@ -683,7 +701,8 @@ int render_bwd_impl(int n, const T* means2d, const T* conics, const T* opac, con
 }
 
 // Backward of the projection for one Gaussian, in double, given the decisions (cull, clamps,
-// det clamp, near) of the T-precision forward. g9 = (d mu'_x, d mu'_y, dA, dB, dC, d o, d rgb).
+// det clamp, near) of the T-precision forward. g9 = (d mu'_x, d mu'_y, dA, dB, dC, d o, d rgb,
+// d depth): 10 values, the depth being camera z = t_z.
 void project_bwd_one(const double* mean, const double* log_scale, const double* quat, double logit,
                      const double* sh, int sh_degree, const Cam<double>& cam, bool clamp_x,
                      bool clamp_y, bool det_clamped, const double* g9, double* d_mean,
@@ -754,6 +773,8 @@ void project_bwd_one(const double* mean, const double* log_scale, const double* 
   gt[2] += -g9[0] * fx * tx / (tz * tz);
   gt[1] += g9[1] * fy / tz;
   gt[2] += -g9[1] * fy * ty / (tz * tz);
+  // the depth channel's value is t_z
+  gt[2] += g9[9];
   // t = W mu + w0  ->  dL/dmu = W^T dL/dt;  Sc = W Sig W^T  ->  dL/dSig = W^T dL/dSc W
   const double* V = cam.V;
   for (int j = 0; j < 3; ++j) d_mean[j] = V[0 * 4 + j] * gt[0] + V[1 * 4 + j] * gt[1] + V[2 * 4 + j] * gt[2];
@@ -903,19 +924,19 @@ int project_bwd_impl(int n, int sh_degree, const T* means, const T* log_scales, 
     for (int j = 0; j < K * 3; ++j) shd[j] = (double)sh[(size_t)g * K * 3 + j];
     const bool det_clamped = !(P.det_raw >= (T)1e-10);
     project_bwd_one(mean, ls, q, lg, shd.data(), sh_degree, camd, P.clamp_x, P.clamp_y, det_clamped,
-                    g2d + 9 * (size_t)g, dm, dl, dq, d_logits + g, dsh);
+                    g2d + 10 * (size_t)g, dm, dl, dq, d_logits + g, dsh);
     if (aref_raw && aref2d) {
       // floor for the raw gradients: |Jacobian| applied to the 2D absolute sums
       double* ar = aref_raw + (size_t)g * nraw;
       std::vector<double> tmp(nraw);
-      for (int k = 0; k < 9; ++k) {
-        double e[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+      for (int k = 0; k < 10; ++k) {
+        double e[10] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
         e[k] = 1.0;
         double tl;
         project_bwd_one(mean, ls, q, lg, shd.data(), sh_degree, camd, P.clamp_x, P.clamp_y, det_clamped, e,
                         tmp.data(), tmp.data() + 3, tmp.data() + 6, &tl, tmp.data() + 11);
         tmp[10] = tl;
-        for (int j = 0; j < nraw; ++j) ar[j] += std::fabs(tmp[j]) * aref2d[9 * (size_t)g + k];
+        for (int j = 0; j < nraw; ++j) ar[j] += std::fabs(tmp[j]) * aref2d[10 * (size_t)g + k];
       }
     }
   }
@@ -1013,32 +1034,32 @@ int orc_render_f32(int n, const float* means2d, const float* conics, const float
                    const float* depths, const uint32_t* tiles, const int32_t* rects, int W, int H,
                    const float* bg, int64_t npix, const int32_t* pix, double band_eps, double* image,
                    double* final_T, int32_t* last_id, int32_t* n_contrib, uint8_t* fragile, int64_t* escapes,
-                   int64_t* n_eval) {
+                   int64_t* n_eval, double* depth_img) {
   return render_impl<float>(n, means2d, conics, opac, colors, depths, tiles, rects, W, H, bg, npix, pix,
-                            band_eps, image, final_T, last_id, n_contrib, fragile, escapes, n_eval);
+                            band_eps, image, final_T, last_id, n_contrib, fragile, escapes, n_eval, depth_img);
 }
 int orc_render_f64(int n, const double* means2d, const double* conics, const double* opac,
                    const double* colors, const double* depths, const uint32_t* tiles, const int32_t* rects,
                    int W, int H, const double* bg, int64_t npix, const int32_t* pix, double band_eps,
                    double* image, double* final_T, int32_t* last_id, int32_t* n_contrib, uint8_t* fragile,
-                   int64_t* escapes, int64_t* n_eval) {
+                   int64_t* escapes, int64_t* n_eval, double* depth_img) {
   return render_impl<double>(n, means2d, conics, opac, colors, depths, tiles, rects, W, H, bg, npix, pix,
-                             band_eps, image, final_T, last_id, n_contrib, fragile, escapes, n_eval);
+                             band_eps, image, final_T, last_id, n_contrib, fragile, escapes, n_eval, depth_img);
 }
 
 int orc_render_bwd_f32(int n, const float* means2d, const float* conics, const float* opac, const float* colors,
                        const float* depths, const uint32_t* tiles, const int32_t* rects, int W, int H,
                        const float* bg, int64_t npix, const int32_t* pix, double band_eps,
-                       const double* dL_dimg, double* g2d, double* aref) {
+                       const double* dL_dimg, const double* dL_ddepth, double* g2d, double* aref) {
   return render_bwd_impl<float>(n, means2d, conics, opac, colors, depths, tiles, rects, W, H, bg, npix, pix,
-                                band_eps, dL_dimg, g2d, aref);
+                                band_eps, dL_dimg, dL_ddepth, g2d, aref);
 }
 int orc_render_bwd_f64(int n, const double* means2d, const double* conics, const double* opac,
                        const double* colors, const double* depths, const uint32_t* tiles, const int32_t* rects,
                        int W, int H, const double* bg, int64_t npix, const int32_t* pix, double band_eps,
-                       const double* dL_dimg, double* g2d, double* aref) {
+                       const double* dL_dimg, const double* dL_ddepth, double* g2d, double* aref) {
   return render_bwd_impl<double>(n, means2d, conics, opac, colors, depths, tiles, rects, W, H, bg, npix, pix,
-                                 band_eps, dL_dimg, g2d, aref);
+                                 band_eps, dL_dimg, dL_ddepth, g2d, aref);
 }
 
 int orc_project_bwd_f32(int n, int sh_degree, const float* means, const float* log_scales, const float* quats,
