@@ -150,9 +150,12 @@ __device__ __forceinline__ void publish_quadrant_masks(uint32_t qm, bool valid, 
   }
 }
 
-// One front-to-back blend step of a pixel (section 5's loop body, predicated).
-__device__ __forceinline__ void blend_step(const SplatEval& e, bool act, float cr_, float cg_, float cb_, uint32_t idx,
-                                           float& T, float& cr, float& cg, float& cb, uint32_t& last, bool& done) {
+// One front-to-back blend step of a pixel (section 5's loop body, predicated). DEPTH: the depth
+// channel (the splat's camera z) goes through the same weight.
+template <bool DEPTH>
+__device__ __forceinline__ void blend_step(const SplatEval& e, bool act, float cr_, float cg_, float cb_, float z_,
+                                           uint32_t idx, float& T, float& cr, float& cg, float& cb, float& cd,
+                                           uint32_t& last, bool& done) {
   const bool ok = act && !done && !e.skip;
   const float nT = T * (1.0f - e.alpha);
   // nT >= 0, so comparing its bits as integers orders it like the float, and, unlike a float
@@ -165,6 +168,7 @@ __device__ __forceinline__ void blend_step(const SplatEval& e, bool act, float c
   cr = fmaf(cr_, wgt, cr);
   cg = fmaf(cg_, wgt, cg);
   cb = fmaf(cb_, wgt, cb);
+  if (DEPTH) cd = fmaf(z_, wgt, cd);
   T = Tn;
   last = add ? idx : last;
   done = done || stop;
@@ -177,17 +181,21 @@ __device__ __forceinline__ void blend_step(const SplatEval& e, bool act, float c
 // longer than the plan's chunk length L accumulates its colour per chunk of L list entries and
 // stores, for every chunk j, each pixel's transmittance after the chunk and the colour the chunk
 // added (slot j). The backward then splits the tile into chunks that run in parallel.
+// DEPTH: also the depth channel, D = sum z_i alpha_i T_i (background depth 0; the chunks' depth
+// contributions go to ckpt_d, one float per pixel and slot).
 // ---------------------------------------------------------------------------------------------
-template <bool COUNT, bool CKPT>
+template <bool COUNT, bool CKPT, bool DEPTH>
 __global__ __launch_bounds__(kRasterThreads) void k_blend(
     uint32_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ plan, uint32_t ntiles,
-    float4* __restrict__ ckpt, const uint32_t* __restrict__ ids, const float* __restrict__ means2d,
-    const float* __restrict__ conics, const float* __restrict__ opac, const float* __restrict__ colors,
-    const int32_t* __restrict__ radii, DevCamera cam, float* __restrict__ image, float* __restrict__ final_T,
+    float4* __restrict__ ckpt, float* __restrict__ ckpt_d, const uint32_t* __restrict__ ids,
+    const float* __restrict__ means2d, const float* __restrict__ conics, const float* __restrict__ opac,
+    const float* __restrict__ colors, const float* __restrict__ depths, const int32_t* __restrict__ radii,
+    DevCamera cam, float* __restrict__ image, float* __restrict__ depth_out, float* __restrict__ final_T,
     uint32_t* __restrict__ n_contrib, unsigned long long* __restrict__ eval_count) {
   __shared__ float4 s_a[kBatch];
   __shared__ float4 s_b[kBatch];
   __shared__ float s_c[kBatch];
+  __shared__ float s_z[DEPTH ? kBatch : 1];
   __shared__ uint64_t s_qm[4][4];
 
   const int tile = plan ? (int)plan[kPlanOrder + blockIdx.x] : (int)blockIdx.x;
@@ -202,14 +210,16 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
 
   // (cr, cg, cb): the colour added so far; with checkpoints, by the current chunk only, and
   // (pr, pg, pb) by the chunks before it
-  float T = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f, pr = 0.0f, pg = 0.0f, pb = 0.0f;
+  float T = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f, pr = 0.0f, pg = 0.0f, pb = 0.0f, cd = 0.0f, pd = 0.0f;
   uint32_t last = 0, n_eval = 0;
   bool done = !inside;
   // chunk boundaries are multiples of L >= kBatch, so they fall on batch starts
   const uint32_t len = end - start;
   const uint32_t L = CKPT ? plan[kPlanChunk] : 0u;
   uint32_t next_b = (CKPT && len > L) ? L : 0xFFFFFFFFu;
-  float4* ck = (CKPT && len > L) ? ckpt + (size_t)plan[kPlanOrder + ntiles + tile] * kRasterThreads + tid : nullptr;
+  const size_t slot_px = (CKPT && len > L) ? (size_t)plan[kPlanOrder + ntiles + tile] * kRasterThreads + tid : 0;
+  float4* ck = (CKPT && len > L) ? ckpt + slot_px : nullptr;
+  float* ckd = (DEPTH && CKPT && len > L) ? ckpt_d + slot_px : nullptr;
   auto store_ckpt = [&]() {
     *ck = make_float4(T, cr, cg, cb);
     ck += kRasterThreads;
@@ -217,6 +227,12 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
     pg += cg;
     pb += cb;
     cr = cg = cb = 0.0f;
+    if (DEPTH) {
+      *ckd = cd;
+      ckd += kRasterThreads;
+      pd += cd;
+      cd = 0.0f;
+    }
     next_b += L;
     if (next_b >= len) next_b = 0xFFFFFFFFu;
   };
@@ -225,7 +241,11 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
     if (CKPT && bs - start >= next_b) store_ckpt();  // workgroup-uniform
     const uint32_t j = bs + tid;
     uint32_t qm = 0;
-    if (j < end) qm = load_record(ids[j], n, means2d, conics, opac, colors, radii, tx0, ty0, s_a[tid], s_b[tid], s_c[tid]);
+    if (j < end) {
+      const uint32_t g = ids[j];
+      qm = load_record(g, n, means2d, conics, opac, colors, radii, tx0, ty0, s_a[tid], s_b[tid], s_c[tid]);
+      if (DEPTH) s_z[tid] = g < n ? depths[g] : 0.0f;
+    }
     publish_quadrant_masks(qm, j < end, s_qm);
     __syncthreads();
     const uint32_t list1 = bs - start + 1u;  // 1-based list index of staged splat 0
@@ -242,20 +262,23 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
         const float4 a0 = s_a[k0], b0 = s_b[k0];
         const float4 a1 = s_a[k1], b1 = s_b[k1];
         const float c0 = s_c[k0], c1 = s_c[k1];
+        const float z0 = DEPTH ? s_z[k0] : 0.0f, z1 = DEPTH ? s_z[k1] : 0.0f;
         const SplatEval e0 = eval_splat(a0.x - px, a0.y - py, a0.z, b0.x, a0.w, b0.y);
         const SplatEval e1 = eval_splat(a1.x - px, a1.y - py, a1.z, b1.x, a1.w, b1.y);
         if (COUNT) n_eval += (done ? 0u : 1u) + ((done || !has1) ? 0u : 1u);
-        blend_step(e0, true, b0.z, b0.w, c0, list1 + (uint32_t)k0, T, cr, cg, cb, last, done);
-        blend_step(e1, has1, b1.z, b1.w, c1, list1 + (uint32_t)k1, T, cr, cg, cb, last, done);
+        blend_step<DEPTH>(e0, true, b0.z, b0.w, c0, z0, list1 + (uint32_t)k0, T, cr, cg, cb, cd, last, done);
+        blend_step<DEPTH>(e1, has1, b1.z, b1.w, c1, z1, list1 + (uint32_t)k1, T, cr, cg, cb, cd, last, done);
       }
     }
   }
   if (CKPT) {
     while (next_b != 0xFFFFFFFFu) store_ckpt();  // boundaries past the last walked batch
     if (ck) *ck = make_float4(T, cr, cg, cb);    // the last chunk's slot
+    if (DEPTH && ckd) *ckd = cd;
     cr += pr;
     cg += pg;
     cb += pb;
+    cd += pd;
   }
   if (inside) {
     const int p = py_i * cam.W + px_i;
@@ -264,6 +287,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
     image[3 * p + 2] = fmaf(T, cam.bg[2], cb);
     final_T[p] = T;
     n_contrib[p] = last;
+    if (DEPTH) depth_out[p] = cd;  // background depth 0
   }
   if (COUNT) count_evals(n_eval, eval_count);
 }
@@ -335,11 +359,15 @@ __device__ __forceinline__ uint32_t pair_slot(uint32_t g, const float* __restric
 //   v6..8 = alpha T_i g_rgb; then dL/dmean = (A P0 + B P1, B P0 + C P1), dL/dA = P2 / 2,
 //   dL/dB = P3, dL/dC = P4 / 2, dL/do = -P5 / o (d alpha/do = G = alpha / o, d alpha/dsigma =
 //   -alpha below the cap), dL/drgb = P6..8 (P = the sums over pixels).
+// DEPTH: the depth channel is a fourth colour (value z, gradient gd): it joins g . c and g . S,
+// and a tenth term v9 = alpha T_i gd gives dL/dz = P9.
+template <bool DEPTH>
 __device__ __forceinline__ void splat_grad(bool contrib, const SplatEval& ev, float dx, float dy, float cr, float cg,
-                                           float cb, float gr, float gg, float gb, float& T, float& gS, float* v) {
+                                           float cb, float z, float gr, float gg, float gb, float gd, float& T,
+                                           float& gS, float* v) {
   const float inv = __builtin_amdgcn_rcpf(1.0f - ev.alpha);
   const float Ti = contrib ? T * inv : T;  // T_i, the transmittance in front of this splat
-  const float gc = fmaf(gr, cr, fmaf(gg, cg, gb * cb));
+  const float gc = DEPTH ? fmaf(gd, z, fmaf(gr, cr, fmaf(gg, cg, gb * cb))) : fmaf(gr, cr, fmaf(gg, cg, gb * cb));
   const float g_alpha = fmaf(Ti, gc, -gS * inv);  // dL/dalpha = g . (c T_i - S / (1 - alpha))
   // alpha T_i as a product: Ti - T would save one operation but cancels for alpha near 1/255
   const float wT = contrib ? ev.alpha * Ti : 0.0f;
@@ -356,6 +384,22 @@ __device__ __forceinline__ void splat_grad(bool contrib, const SplatEval& ev, fl
   v[6] = wT * gr;
   v[7] = wT * gg;
   v[8] = wT * gb;
+  if (DEPTH) v[9] = wT * gd;
+}
+
+// The per-splat sums of reduce9_to_lds, plus (DEPTH) the tenth term summed into acc[9].
+template <bool STORE, bool DEPTH>
+__device__ __forceinline__ void reduce_terms(const float* v, float* acc, int lane) {
+  reduce9_to_lds<STORE>(v, acc, lane);
+  if (DEPTH) {
+    const float y = wave_sum_lane63(v[9]);
+    if (lane == 63) {
+      if (STORE)
+        acc[9] = y;
+      else
+        unsafeAtomicAdd(acc + 9, y);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -376,22 +420,28 @@ __device__ __forceinline__ void splat_grad(bool contrib, const SplatEval& ev, fl
 // contributor) keep the zeros the records were cleared to before the launch.
 // ---------------------------------------------------------------------------------------------
 constexpr int kBwdAtomic = 0, kBwdRecords = 1, kBwdDeterministic = 2;
-template <bool COUNT, int MODE>
+constexpr int kG2d = 10;  // components of a 2D gradient: mean2d (2), conic (3), opacity, rgb (3), depth
+// DEPTH: the backward of the depth channel too (dL/ddepth given; tenth component dL/dz).
+template <bool COUNT, int MODE, bool DEPTH>
 __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
     uint32_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ plan, uint32_t ntiles,
-    const float4* __restrict__ ckpt, const uint32_t* __restrict__ ids,
+    const float4* __restrict__ ckpt, const float* __restrict__ ckpt_d, const uint32_t* __restrict__ ids,
     const float* __restrict__ means2d, const float* __restrict__ conics, const float* __restrict__ opac,
-    const float* __restrict__ colors, const int32_t* __restrict__ radii, DevCamera cam,
-    const float* __restrict__ final_T, const uint32_t* __restrict__ n_contrib, const float* __restrict__ dL_dimage,
-    float* __restrict__ g2d, const uint32_t* __restrict__ pair_base, float* __restrict__ rec, uint32_t rec_cap,
+    const float* __restrict__ colors, const float* __restrict__ depths, const int32_t* __restrict__ radii,
+    DevCamera cam, const float* __restrict__ final_T, const uint32_t* __restrict__ n_contrib,
+    const float* __restrict__ dL_dimage, const float* __restrict__ dL_ddepth, float* __restrict__ g2d,
+    const uint32_t* __restrict__ pair_base, float* __restrict__ rec, uint32_t rec_cap,
     unsigned long long* __restrict__ eval_count) {
-  // g2d is [9, n]: component c of splat g at c * n + g; rec is [rec_cap, 9] (a pair's 36 B together)
+  // g2d is [10, n]: component c of splat g at c * n + g; rec is [rec_cap, 10] (a pair's 40 B
+  // together); without DEPTH the tenth component is not written (it stays 0)
   constexpr bool REC = MODE != kBwdAtomic, DET = MODE == kBwdDeterministic;
+  constexpr int NT = DEPTH ? 10 : 9;  // terms summed per splat
   __shared__ float4 s_a[kBatch];
   __shared__ float4 s_b[kBatch];
   __shared__ float s_c[kBatch];
+  __shared__ float s_z[DEPTH ? kBatch : 1];
   __shared__ uint32_t s_id[kBatch];
-  __shared__ float s_acc[kBatch * 9];
+  __shared__ float s_acc[kBatch * NT];
   __shared__ uint64_t s_qm[4][4];
   __shared__ uint32_t s_max;
 
@@ -444,6 +494,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
       const uint32_t g = ids[start + bstart + (uint32_t)tid];
       s_id[tid] = g;
       qm = load_record(g, n, means2d, conics, opac, colors, radii, tx0, ty0, s_a[tid], s_b[tid], s_c[tid]);
+      if (DEPTH) s_z[tid] = g < n ? depths[g] : 0.0f;
       if (g < n) {
         rA = conics[3 * g];
         rB = conics[3 * g + 1];
@@ -453,14 +504,14 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
       }
     }
     if (!DET)
-      for (int i = tid; i < cnt * 9; i += kRasterThreads) s_acc[i] = 0.0f;
+      for (int i = tid; i < cnt * NT; i += kRasterThreads) s_acc[i] = 0.0f;
     publish_quadrant_masks(qm, tid < cnt, s_qm);
   };
-  // the 2D gradient of staged splat tid from its nine sums P, to g2d or its record slot
+  // the 2D gradient of staged splat tid from its sums P, to g2d or its record slot
   auto finish = [&](const float* P) {
     const uint32_t g = s_id[tid];
     const float A = rA, B = rB, C = rC, o = ro;
-    float gv[9];
+    float gv[kG2d];
     gv[0] = fmaf(A, P[0], B * P[1]);
     gv[1] = fmaf(B, P[0], C * P[1]);
     gv[2] = 0.5f * P[2];
@@ -470,15 +521,16 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
     gv[6] = P[6];
     gv[7] = P[7];
     gv[8] = P[8];
+    gv[9] = DEPTH ? P[9] : 0.0f;
     if (REC) {
       if (rslot < rec_cap) {
 #pragma unroll
-        for (int c = 0; c < 9; ++c) rec[(size_t)rslot * 9 + c] = gv[c];
+        for (int c = 0; c < NT; ++c) rec[(size_t)rslot * kG2d + c] = gv[c];
       }
     } else {
-      // one plane per component: the nine atomics of a lane go to nine different cache lines
+      // one plane per component: the atomics of a lane go to different cache lines
 #pragma unroll
-      for (int c = 0; c < 9; ++c)
+      for (int c = 0; c < NT; ++c)
         if (gv[c] != 0.0f) unsafeAtomicAdd(g2d + (size_t)c * n + g, gv[c]);
     }
   };
@@ -486,7 +538,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
   const bool single = chunk_end <= lo + (uint32_t)kBatch;
   if (single && chunk_end > lo) stage(lo, (int)(chunk_end - lo));
 
-  float T = 1.0f, gr = 0.0f, gg = 0.0f, gb = 0.0f, gS = 0.0f;
+  float T = 1.0f, gr = 0.0f, gg = 0.0f, gb = 0.0f, gd = 0.0f, gS = 0.0f;
   uint32_t nc = 0;
   if (inside) {
     const int p = py_i * cam.W + px_i;
@@ -494,18 +546,22 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
     gr = dL_dimage[3 * p];
     gg = dL_dimage[3 * p + 1];
     gb = dL_dimage[3 * p + 2];
+    if (DEPTH) gd = dL_ddepth[p];
     if (from_ckpt) {
       // S after the chunk = T_final background + the colour of chunks nch - 1 .. chunk + 1
+      // (the depth channel: the later chunks' depth, background depth 0)
       const float Tf = final_T[p];
-      float sr = Tf * cam.bg[0], sg = Tf * cam.bg[1], sb = Tf * cam.bg[2];
+      float sr = Tf * cam.bg[0], sg = Tf * cam.bg[1], sb = Tf * cam.bg[2], sd = 0.0f;
       for (uint32_t k = nch - 1; k > chunk; --k) {
         const float4 st = ckpt[slot0 + (size_t)k * kRasterThreads + tid];
         sr += st.y;
         sg += st.z;
         sb += st.w;
+        if (DEPTH) sd += ckpt_d[slot0 + (size_t)k * kRasterThreads + tid];
       }
       T = ckpt[slot0 + (size_t)chunk * kRasterThreads + tid].x;
       gS = (gr * sr + gg * sg) + gb * sb;
+      if (DEPTH) gS = fmaf(gd, sd, gS);
     } else {
       // g . S with S = T_final background
       T = final_T[p];
@@ -531,10 +587,10 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
     __syncthreads();
     for (int w = 3; w >= 0; --w) {
       // DET: this wave's sums of group w's 64 splats, zeroed first (row `lane` per lane)
-      float* part = s_acc + (size_t)wave * 64 * 9;
+      float* part = s_acc + (size_t)wave * 64 * NT;
       if (DET) {
 #pragma unroll
-        for (int c = 0; c < 9; ++c) part[lane * 9 + c] = 0.0f;
+        for (int c = 0; c < NT; ++c) part[lane * NT + c] = 0.0f;
       }
       uint64_t m = uniform64(s_qm[wave][w]);  // walked from the highest set bit down
       while (m) {
@@ -551,33 +607,34 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
         const float4 a0 = s_a[k0], b0 = s_b[k0];
         const float4 a1 = s_a[k1], b1 = s_b[k1];
         const float cb0 = s_c[k0], cb1 = s_c[k1];
+        const float z0 = DEPTH ? s_z[k0] : 0.0f, z1 = DEPTH ? s_z[k1] : 0.0f;
         const float dx0 = a0.x - px, dy0 = a0.y - py, dx1 = a1.x - px, dy1 = a1.y - py;
         const SplatEval e0 = eval_splat(dx0, dy0, a0.z, b0.x, a0.w, b0.y);
         const SplatEval e1 = eval_splat(dx1, dy1, a1.z, b1.x, a1.w, b1.y);
         if (COUNT) n_eval += (act0 ? 1u : 0u) + (act1 ? 1u : 0u);
         const bool c0 = act0 && !e0.skip, c1 = act1 && !e1.skip;
-        float v0[9], v1[9];
-        splat_grad(c0, e0, dx0, dy0, b0.z, b0.w, cb0, gr, gg, gb, T, gS, v0);
-        splat_grad(c1, e1, dx1, dy1, b1.z, b1.w, cb1, gr, gg, gb, T, gS, v1);
+        float v0[NT], v1[NT];
+        splat_grad<DEPTH>(c0, e0, dx0, dy0, b0.z, b0.w, cb0, z0, gr, gg, gb, gd, T, gS, v0);
+        splat_grad<DEPTH>(c1, e1, dx1, dy1, b1.z, b1.w, cb1, z1, gr, gg, gb, gd, T, gS, v1);
         if (DET) {
-          if (__any(c0)) reduce9_to_lds<true>(v0, part + (k0 - w * 64) * 9, lane);
-          if (__any(c1)) reduce9_to_lds<true>(v1, part + (k1 - w * 64) * 9, lane);
+          if (__any(c0)) reduce_terms<true, DEPTH>(v0, part + (k0 - w * 64) * NT, lane);
+          if (__any(c1)) reduce_terms<true, DEPTH>(v1, part + (k1 - w * 64) * NT, lane);
         } else {
-          if (__any(c0)) reduce9_to_lds<false>(v0, s_acc + k0 * 9, lane);
-          if (__any(c1)) reduce9_to_lds<false>(v1, s_acc + k1 * 9, lane);
+          if (__any(c0)) reduce_terms<false, DEPTH>(v0, s_acc + k0 * NT, lane);
+          if (__any(c1)) reduce_terms<false, DEPTH>(v1, s_acc + k1 * NT, lane);
         }
       }
       if (DET) {
         // group w is staged by wave w: its threads add the four waves' sums in wave order
         __syncthreads();
         if (wave == w && tid < cnt && s_id[tid] < n) {
-          float P[9];
+          float P[NT];
 #pragma unroll
-          for (int c = 0; c < 9; ++c) {
-            float acc = s_acc[(0 * 64 + lane) * 9 + c];
-            acc += s_acc[(1 * 64 + lane) * 9 + c];
-            acc += s_acc[(2 * 64 + lane) * 9 + c];
-            acc += s_acc[(3 * 64 + lane) * 9 + c];
+          for (int c = 0; c < NT; ++c) {
+            float acc = s_acc[(0 * 64 + lane) * NT + c];
+            acc += s_acc[(1 * 64 + lane) * NT + c];
+            acc += s_acc[(2 * 64 + lane) * NT + c];
+            acc += s_acc[(3 * 64 + lane) * NT + c];
             P[c] = acc;
           }
           finish(P);
@@ -587,7 +644,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
     }
     __syncthreads();
     // finish the 2D gradient of each staged splat from its nine sums
-    if (!DET && tid < cnt && s_id[tid] < n) finish(s_acc + tid * 9);
+    if (!DET && tid < cnt && s_id[tid] < n) finish(s_acc + tid * NT);
     bend = bstart;
   }
   if (COUNT) count_evals(n_eval, eval_count);
@@ -651,9 +708,9 @@ __global__ __launch_bounds__(256) void k_pbwd(
   double gsh[K * 3];
 #pragma unroll
   for (int i = 0; i < K * 3; ++i) gsh[i] = 0.0;
-  double G9[9];
+  double G9[kG2d];  // the 2D gradient; G9[9] is dL/d(camera z) of the depth channel
 #pragma unroll
-  for (int c = 0; c < 9; ++c) G9[c] = (double)g2d[(size_t)c * n + g];  // [9, n]
+  for (int c = 0; c < kG2d; ++c) G9[c] = (double)g2d[(size_t)c * n + g];  // [10, n]
 
   const bool drawn = tiles_touched[g] > 0;
   if (drawn) {
@@ -801,6 +858,7 @@ __global__ __launch_bounds__(256) void k_pbwd(
     gt[2] -= G9[0] * fx * tx * iz2;
     gt[1] += G9[1] * fy * iz;
     gt[2] -= G9[1] * fy * ty * iz2;
+    gt[2] += G9[9];  // the depth channel's value is t_z
     for (int j = 0; j < 3; ++j) gm[j] = W[j] * gt[0] + W[3 + j] * gt[1] + W[6 + j] * gt[2];
 
     // ---- log-scales, opacity, colour ----
@@ -854,7 +912,7 @@ __global__ void k_clear_records(float4* __restrict__ rec, const unsigned long lo
                                 uint32_t rec_cap) {
   const unsigned long long P = *total;
   if (P > rec_cap) return;
-  const size_t count = ((size_t)P * 9 + 3) / 4;  // the record array is 256-byte aligned and padded
+  const size_t count = ((size_t)P * kG2d + 3) / 4;  // the record array is 256-byte aligned and padded
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < count; i += (size_t)gridDim.x * blockDim.x)
     rec[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 }
@@ -942,18 +1000,18 @@ __global__ __launch_bounds__(256) void k_seg_reduce(int32_t n, const uint32_t* _
   if (g >= n) return;  // wave-uniform
   const uint32_t cnt = *total <= (unsigned long long)rec_cap ? tiles_touched[g] : 0u;
   const uint32_t b = base[g];
-  float acc[9];
+  float acc[kG2d];
 #pragma unroll
-  for (int c = 0; c < 9; ++c) acc[c] = 0.0f;
+  for (int c = 0; c < kG2d; ++c) acc[c] = 0.0f;
   for (uint32_t j = lane; j < cnt; j += 64) {
 #pragma unroll
-    for (int c = 0; c < 9; ++c) acc[c] += rec[((size_t)b + j) * 9 + c];
+    for (int c = 0; c < kG2d; ++c) acc[c] += rec[((size_t)b + j) * kG2d + c];
   }
 #pragma unroll
-  for (int c = 0; c < 9; ++c) acc[c] = wave_sum_lane63(acc[c]);
+  for (int c = 0; c < kG2d; ++c) acc[c] = wave_sum_lane63(acc[c]);
   if (lane == 63) {
 #pragma unroll
-    for (int c = 0; c < 9; ++c) g2d[(size_t)c * n + g] = acc[c];
+    for (int c = 0; c < kG2d; ++c) g2d[(size_t)c * n + g] = acc[c];
   }
 }
 
@@ -970,14 +1028,15 @@ bool proj_ok(const gs_projected* p) {
 }  // namespace
 
 extern "C" size_t gs_raster_workspace_bytes(void) {
-  return (size_t)kPlanMaxSlots * kRasterThreads * sizeof(float4);
+  // per slot and pixel: (T, r, g, b) and the depth channel's contribution
+  return (size_t)kPlanMaxSlots * kRasterThreads * (sizeof(float4) + sizeof(float));
 }
 
 extern "C" gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const gs_camera* cam,
                                       const uint32_t* d_ids, const uint32_t* d_tile_ranges,
                                       const uint32_t* d_raster_plan, void* d_raster_ws, float* d_image,
-                                      float* d_final_T, uint32_t* d_n_contrib, uint64_t* d_eval_count,
-                                      void* stream) {
+                                      float* d_depth, float* d_final_T, uint32_t* d_n_contrib,
+                                      uint64_t* d_eval_count, void* stream) {
   std::string why;
   if (n < 0) return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: n < 0");
   if (!valid_camera(cam, &why)) return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: " + why);
@@ -991,20 +1050,30 @@ extern "C" gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const
   {
     TimedScope ts("blend", s);
     const bool ck = d_raster_plan && d_raster_ws;
-    auto kern = d_eval_count ? (ck ? k_blend<true, true> : k_blend<true, false>)
-                             : (ck ? k_blend<false, true> : k_blend<false, false>);
+    const bool dep = d_depth != nullptr;
+    auto pick = [&](auto c_, auto k_, auto d_) {
+      return k_blend<decltype(c_)::value, decltype(k_)::value, decltype(d_)::value>;
+    };
+    using T1 = std::true_type;
+    using F0 = std::false_type;
+    auto kern = d_eval_count ? (ck ? (dep ? pick(T1{}, T1{}, T1{}) : pick(T1{}, T1{}, F0{}))
+                                   : (dep ? pick(T1{}, F0{}, T1{}) : pick(T1{}, F0{}, F0{})))
+                             : (ck ? (dep ? pick(F0{}, T1{}, T1{}) : pick(F0{}, T1{}, F0{}))
+                                   : (dep ? pick(F0{}, F0{}, T1{}) : pick(F0{}, F0{}, F0{})));
+    float4* ws4 = d_raster_plan ? (float4*)d_raster_ws : nullptr;
+    float* wsd = ws4 ? (float*)(ws4 + (size_t)kPlanMaxSlots * kRasterThreads) : nullptr;
     hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges,
-                       d_raster_plan, (uint32_t)ntiles, d_raster_plan ? (float4*)d_raster_ws : nullptr, d_ids,
-                       n > 0 ? proj->d_means2d : nullptr, n > 0 ? proj->d_conics : nullptr,
-                       n > 0 ? proj->d_opacities : nullptr, n > 0 ? proj->d_colors : nullptr,
-                       n > 0 ? proj->d_radii : nullptr, dc, d_image, d_final_T, d_n_contrib,
+                       d_raster_plan, (uint32_t)ntiles, ws4, wsd, d_ids, n > 0 ? proj->d_means2d : nullptr,
+                       n > 0 ? proj->d_conics : nullptr, n > 0 ? proj->d_opacities : nullptr,
+                       n > 0 ? proj->d_colors : nullptr, n > 0 ? proj->d_depths : nullptr,
+                       n > 0 ? proj->d_radii : nullptr, dc, d_image, d_depth, d_final_T, d_n_contrib,
                        (unsigned long long*)d_eval_count);
   }
   return check_launch("gs_rasterize_fwd");
 }
 
 namespace {
-// Workspace of the record modes: g2d [9, n] | base [n] u32 | total u64 | block sums u64 | rec [cap, 9]
+// Workspace of the record modes: g2d [10, n] | base [n] u32 | total u64 | block sums u64 | rec [cap, 10]
 struct BwdRecLayout {
   size_t g2d, base, total, bsum, rec, bytes;
 };
@@ -1012,11 +1081,11 @@ BwdRecLayout bwd_rec_layout(int32_t n, int64_t cap) {
   BwdRecLayout L{};
   const size_t nb = ((size_t)n + kBaseTile - 1) / kBaseTile;
   L.g2d = 0;
-  L.base = align_up(L.g2d + (size_t)n * 9 * 4, 256);
+  L.base = align_up(L.g2d + (size_t)n * kG2d * 4, 256);
   L.total = align_up(L.base + (size_t)n * 4, 256);
   L.bsum = align_up(L.total + 8, 256);
   L.rec = align_up(L.bsum + nb * 8, 256);
-  L.bytes = align_up(L.rec + (size_t)cap * 9 * 4 + 16, 256);  // + one float4 of clearing slack
+  L.bytes = align_up(L.rec + (size_t)cap * kG2d * 4 + 16, 256);  // + one float4 of clearing slack
   return L;
 }
 
@@ -1025,7 +1094,8 @@ gs_status rasterize_bwd(const char* name, int mode, int32_t n, int32_t sh_degree
                         const float* d_sh, const gs_camera* cam, const gs_projected* proj, const uint32_t* d_ids,
                         const uint32_t* d_tile_ranges, const uint32_t* d_raster_plan, const void* d_raster_ws,
                         const float* d_final_T, const uint32_t* d_n_contrib, const float* d_dL_dimage,
-                        int64_t pair_capacity, void* d_workspace, size_t workspace_bytes, float* d_grad_means,
+                        const float* d_dL_ddepth, int64_t pair_capacity, void* d_workspace, size_t workspace_bytes,
+                        float* d_grad_means,
                         float* d_grad_log_scales, float* d_grad_quats, float* d_grad_opacity_logits,
                         float* d_grad_sh, float* d_grad_means2d, uint64_t* d_eval_count, void* stream) {
   const std::string nm = name;
@@ -1059,7 +1129,7 @@ gs_status rasterize_bwd(const char* name, int mode, int32_t n, int32_t sh_degree
   float* rec = nullptr;
   if (mode == kBwdAtomic) {
     TimedScope ts("bwd_zero", s);
-    const size_t count = (size_t)n * 9;
+    const size_t count = (size_t)n * kG2d;
     const unsigned blocks = (unsigned)((count + 255) / 256 < 4096 ? (count + 255) / 256 : 4096);
     hipLaunchKernelGGL(k_fill_zero, dim3(blocks), dim3(256), 0, s, g2d, count);
   } else {
@@ -1072,28 +1142,31 @@ gs_status rasterize_bwd(const char* name, int mode, int32_t n, int32_t sh_degree
     hipLaunchKernelGGL(k_base_sums, dim3(nb), dim3(kBaseThreads), 0, s, n, proj->d_tiles_touched, bsum);
     hipLaunchKernelGGL(k_base_scan, dim3(nb), dim3(kBaseThreads), 0, s, n, proj->d_tiles_touched, bsum, base, total);
     // every record starts at zero: the pairs no pixel reaches are never staged
-    const size_t count4 = ((size_t)pair_capacity * 9 + 3) / 4;
+    const size_t count4 = ((size_t)pair_capacity * kG2d + 3) / 4;
     const unsigned blocks = (unsigned)((count4 + 255) / 256 < 8192 ? (count4 + 255) / 256 : 8192);
     if (count4)
       hipLaunchKernelGGL(k_clear_records, dim3(blocks), dim3(256), 0, s, (float4*)rec, total, (uint32_t)pair_capacity);
   }
   {
     TimedScope ts("rbwd", s);
-    auto pick = [&](auto count_tag) {
-      constexpr bool C = decltype(count_tag)::value;
-      return mode == kBwdAtomic ? k_rbwd<C, kBwdAtomic> : mode == kBwdRecords ? k_rbwd<C, kBwdRecords>
-                                                                              : k_rbwd<C, kBwdDeterministic>;
+    auto pick = [&](auto count_tag, auto depth_tag) {
+      constexpr bool C = decltype(count_tag)::value, D = decltype(depth_tag)::value;
+      return mode == kBwdAtomic ? k_rbwd<C, kBwdAtomic, D>
+                                : mode == kBwdRecords ? k_rbwd<C, kBwdRecords, D> : k_rbwd<C, kBwdDeterministic, D>;
     };
-    auto kern = d_eval_count ? pick(std::true_type{}) : pick(std::false_type{});
+    const bool dep = d_dL_ddepth != nullptr;
+    auto kern = d_eval_count ? (dep ? pick(std::true_type{}, std::true_type{}) : pick(std::true_type{}, std::false_type{}))
+                             : (dep ? pick(std::false_type{}, std::true_type{}) : pick(std::false_type{}, std::false_type{}));
     // with checkpoints: one workgroup per work item of the plan (the extra ones, fewer than
     // kPlanMaxChunks, then one per tile)
     const bool chunked = d_raster_plan && d_raster_ws;
     const unsigned grid = (unsigned)(chunked ? ntiles + kPlanMaxChunks : ntiles);
+    const float4* ws4 = chunked ? (const float4*)d_raster_ws : nullptr;
+    const float* wsd = ws4 ? (const float*)(ws4 + (size_t)kPlanMaxSlots * kRasterThreads) : nullptr;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges, d_raster_plan,
-                       (uint32_t)ntiles, chunked ? (const float4*)d_raster_ws : nullptr, d_ids,
-                       proj->d_means2d, proj->d_conics, proj->d_opacities, proj->d_colors, proj->d_radii, dc,
-                       d_final_T, d_n_contrib, d_dL_dimage, g2d, base, rec, (uint32_t)pair_capacity,
-                       (unsigned long long*)d_eval_count);
+                       (uint32_t)ntiles, ws4, wsd, d_ids, proj->d_means2d, proj->d_conics, proj->d_opacities,
+                       proj->d_colors, proj->d_depths, proj->d_radii, dc, d_final_T, d_n_contrib, d_dL_dimage,
+                       d_dL_ddepth, g2d, base, rec, (uint32_t)pair_capacity, (unsigned long long*)d_eval_count);
   }
   if (mode != kBwdAtomic) {
     TimedScope ts("bwd_reduce", s);
@@ -1119,7 +1192,9 @@ gs_status rasterize_bwd(const char* name, int mode, int32_t n, int32_t sh_degree
 }
 }  // namespace
 
-extern "C" size_t gs_bwd_workspace_bytes(int32_t n) { return n <= 0 ? 256 : align_up((size_t)n * 9 * 4, 256); }
+extern "C" size_t gs_bwd_workspace_bytes(int32_t n) {
+  return n <= 0 ? 256 : align_up((size_t)n * kG2d * 4, 256);
+}
 
 extern "C" size_t gs_bwd_det_workspace_bytes(int32_t n, int64_t pair_capacity) {
   if (n < 0 || pair_capacity < 0 || pair_capacity >= ((int64_t)1 << 30)) return 0;
@@ -1132,27 +1207,30 @@ extern "C" gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float*
                                       const gs_projected* proj, const uint32_t* d_ids,
                                       const uint32_t* d_tile_ranges, const uint32_t* d_raster_plan,
                                       const void* d_raster_ws, const float* d_final_T,
-                                      const uint32_t* d_n_contrib, const float* d_dL_dimage, void* d_workspace,
-                                      size_t workspace_bytes, float* d_grad_means, float* d_grad_log_scales,
-                                      float* d_grad_quats, float* d_grad_opacity_logits, float* d_grad_sh,
-                                      float* d_grad_means2d, uint64_t* d_eval_count, void* stream) {
+                                      const uint32_t* d_n_contrib, const float* d_dL_dimage,
+                                      const float* d_dL_ddepth, void* d_workspace, size_t workspace_bytes,
+                                      float* d_grad_means, float* d_grad_log_scales, float* d_grad_quats,
+                                      float* d_grad_opacity_logits, float* d_grad_sh, float* d_grad_means2d,
+                                      uint64_t* d_eval_count, void* stream) {
   return rasterize_bwd("gs_rasterize_bwd", kBwdAtomic, n, sh_degree, d_means, d_log_scales, d_quats,
                        d_opacity_logits, d_sh, cam, proj, d_ids, d_tile_ranges, d_raster_plan, d_raster_ws, d_final_T,
-                       d_n_contrib, d_dL_dimage, 0, d_workspace, workspace_bytes, d_grad_means, d_grad_log_scales,
-                       d_grad_quats, d_grad_opacity_logits, d_grad_sh, d_grad_means2d, d_eval_count, stream);
+                       d_n_contrib, d_dL_dimage, d_dL_ddepth, 0, d_workspace, workspace_bytes, d_grad_means,
+                       d_grad_log_scales, d_grad_quats, d_grad_opacity_logits, d_grad_sh, d_grad_means2d,
+                       d_eval_count, stream);
 }
 
 extern "C" gs_status gs_rasterize_bwd_deterministic(
     int32_t n, int32_t sh_degree, const float* d_means, const float* d_log_scales, const float* d_quats,
     const float* d_opacity_logits, const float* d_sh, const gs_camera* cam, const gs_projected* proj,
     const uint32_t* d_ids, const uint32_t* d_tile_ranges, const uint32_t* d_raster_plan, const void* d_raster_ws,
-    const float* d_final_T, const uint32_t* d_n_contrib, const float* d_dL_dimage, int64_t pair_capacity,
-    void* d_workspace, size_t workspace_bytes, float* d_grad_means, float* d_grad_log_scales, float* d_grad_quats,
-    float* d_grad_opacity_logits, float* d_grad_sh, float* d_grad_means2d, uint64_t* d_eval_count, void* stream) {
+    const float* d_final_T, const uint32_t* d_n_contrib, const float* d_dL_dimage, const float* d_dL_ddepth,
+    int64_t pair_capacity, void* d_workspace, size_t workspace_bytes, float* d_grad_means, float* d_grad_log_scales,
+    float* d_grad_quats, float* d_grad_opacity_logits, float* d_grad_sh, float* d_grad_means2d,
+    uint64_t* d_eval_count, void* stream) {
   return rasterize_bwd("gs_rasterize_bwd_deterministic", kBwdDeterministic, n, sh_degree, d_means, d_log_scales,
                        d_quats, d_opacity_logits, d_sh, cam, proj, d_ids, d_tile_ranges, d_raster_plan, d_raster_ws,
-                       d_final_T, d_n_contrib, d_dL_dimage, pair_capacity, d_workspace, workspace_bytes, d_grad_means,
-                       d_grad_log_scales, d_grad_quats, d_grad_opacity_logits, d_grad_sh, d_grad_means2d,
-                       d_eval_count, stream);
+                       d_final_T, d_n_contrib, d_dL_dimage, d_dL_ddepth, pair_capacity, d_workspace, workspace_bytes,
+                       d_grad_means, d_grad_log_scales, d_grad_quats, d_grad_opacity_logits, d_grad_sh,
+                       d_grad_means2d, d_eval_count, stream);
 }
 

@@ -69,13 +69,13 @@ def load():
         "gs_raster_plan_words": (sz, [cam_p]),
         "gs_raster_workspace_bytes": (sz, []),
         "gs_bin_and_sort": (i32, [i32, proj_p, cam_p, P, sz, i64, P, P, P, P, P, ctypes.POINTER(ctypes.c_int64), P]),
-        "gs_rasterize_fwd": (i32, [i32, proj_p, cam_p, P, P, P, P, P, P, P, P, P]),
+        "gs_rasterize_fwd": (i32, [i32, proj_p, cam_p, P, P, P, P, P, P, P, P, P, P]),
         "gs_bwd_workspace_bytes": (sz, [i32]),
         "gs_bwd_det_workspace_bytes": (sz, [i32, i64]),
-        "gs_rasterize_bwd_deterministic": (i32, [i32, i32, P, P, P, P, P, cam_p, proj_p, P, P, P, P, P, P, P, i64,
-                                                 P, sz, P, P, P, P, P, P, P, P]),
-        "gs_rasterize_bwd": (i32, [i32, i32, P, P, P, P, P, cam_p, proj_p, P, P, P, P, P, P, P, P, sz, P, P, P, P, P,
-                                   P, P, P]),
+        "gs_rasterize_bwd_deterministic": (i32, [i32, i32, P, P, P, P, P, cam_p, proj_p, P, P, P, P, P, P, P, P,
+                                                 i64, P, sz, P, P, P, P, P, P, P, P]),
+        "gs_rasterize_bwd": (i32, [i32, i32, P, P, P, P, P, cam_p, proj_p, P, P, P, P, P, P, P, P, P, sz, P, P, P, P,
+                                   P, P, P, P]),
         "gs_loss_l1": (i32, [i32, i32, P, P, P, P, P]),
         "gs_loss_ssim_workspace_bytes": (sz, [i32, i32]),
         "gs_loss_l1_ssim": (i32, [i32, i32, P, P, ctypes.c_float, P, sz, P, P, P]),
@@ -172,9 +172,10 @@ def gs_bin_and_sort(n, proj: "Projected", cam: GsCamera, workspace, pair_capacit
 
 
 def gs_rasterize_fwd(n, proj: "Projected", cam: GsCamera, ids, tile_ranges, image, final_T, n_contrib,
-                     eval_count=None, stream=None, plan=None, raster_ws=None):
+                     eval_count=None, stream=None, plan=None, raster_ws=None, depth=None):
+    """depth: optional [h,w] output of the depth channel."""
     return _check(load().gs_rasterize_fwd(n, ctypes.byref(proj.struct()), ctypes.byref(cam), _ptr(ids),
-                                          _ptr(tile_ranges), _ptr(plan), _ptr(raster_ws), _ptr(image),
+                                          _ptr(tile_ranges), _ptr(plan), _ptr(raster_ws), _ptr(image), _ptr(depth),
                                           _ptr(final_T), _ptr(n_contrib), _ptr(eval_count), _stream(stream)))
 
 
@@ -189,20 +190,21 @@ def gs_bwd_det_workspace_bytes(n, pair_capacity) -> int:
 def gs_rasterize_bwd(n, sh_degree, means, log_scales, quats, opacity_logits, sh, cam: GsCamera, proj: "Projected",
                      ids, tile_ranges, final_T, n_contrib, dL_dimage, workspace, grad_means, grad_log_scales,
                      grad_quats, grad_opacity_logits, grad_sh, grad_means2d=None, eval_count=None, stream=None,
-                     plan=None, raster_ws=None, pair_capacity=None):
-    """pair_capacity=None: gs_rasterize_bwd (fp32 atomics); else gs_rasterize_bwd_deterministic."""
+                     plan=None, raster_ws=None, pair_capacity=None, dL_ddepth=None):
+    """pair_capacity=None: gs_rasterize_bwd (fp32 atomics); else gs_rasterize_bwd_deterministic.
+    dL_ddepth: optional [h,w] gradient on the depth channel."""
     if pair_capacity is not None:
         return _check(load().gs_rasterize_bwd_deterministic(
             n, sh_degree, _ptr(means), _ptr(log_scales), _ptr(quats), _ptr(opacity_logits), _ptr(sh),
             ctypes.byref(cam), ctypes.byref(proj.struct()), _ptr(ids), _ptr(tile_ranges), _ptr(plan),
-            _ptr(raster_ws), _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage), int(pair_capacity),
+            _ptr(raster_ws), _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage), _ptr(dL_ddepth), int(pair_capacity),
             _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(grad_means), _ptr(grad_log_scales),
             _ptr(grad_quats), _ptr(grad_opacity_logits), _ptr(grad_sh), _ptr(grad_means2d), _ptr(eval_count),
             _stream(stream)))
     return _check(load().gs_rasterize_bwd(
         n, sh_degree, _ptr(means), _ptr(log_scales), _ptr(quats), _ptr(opacity_logits), _ptr(sh), ctypes.byref(cam),
         ctypes.byref(proj.struct()), _ptr(ids), _ptr(tile_ranges), _ptr(plan), _ptr(raster_ws), _ptr(final_T),
-        _ptr(n_contrib), _ptr(dL_dimage),
+        _ptr(n_contrib), _ptr(dL_dimage), _ptr(dL_ddepth),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(grad_means), _ptr(grad_log_scales),
         _ptr(grad_quats), _ptr(grad_opacity_logits), _ptr(grad_sh), _ptr(grad_means2d), _ptr(eval_count),
         _stream(stream)))
@@ -358,14 +360,14 @@ class Pipeline:
         if cap > self.capacity:
             self._alloc_pairs(int(cap))
 
-    def forward(self, cam: GsCamera, eval_count=None, stream=None, checkpoints=None):
+    def forward(self, cam: GsCamera, eval_count=None, stream=None, checkpoints=None, depth=None):
         """Blend. checkpoints (default: the "chunks" schedule) stores the per-chunk state that lets
         the backward split long tiles; a render that no backward follows can leave it out."""
         ck = self.schedule == "chunks" if checkpoints is None else bool(checkpoints)
         self._ckpt_written = ck
         gs_rasterize_fwd(self.n, self.proj, cam, self.ids, self.ranges, self.image, self.final_T, self.n_contrib,
                          eval_count, stream, plan=self.plan if self.schedule != "tiles" else None,
-                         raster_ws=self.raster_ws if ck else None)
+                         raster_ws=self.raster_ws if ck else None, depth=depth)
 
     def loss_l1(self, target, loss=None, stream=None):
         """The training loss's gradient into self.dL_dimage: L1, or with self.ssim_lambda > 0
@@ -380,7 +382,7 @@ class Pipeline:
         else:
             gs_loss_l1(self.width, self.height, self.image, target, self.dL_dimage, loss, stream)
 
-    def backward(self, cam: GsCamera, dL_dimage=None, eval_count=None, stream=None):
+    def backward(self, cam: GsCamera, dL_dimage=None, eval_count=None, stream=None, dL_ddepth=None):
         """self.deterministic selects gs_rasterize_bwd_deterministic (records sized by the pair
         capacity) over gs_rasterize_bwd (fp32 atomics)."""
         p, g = self.p, self.grads
@@ -397,7 +399,7 @@ class Pipeline:
                          g["quats"], g["opacity_logits"], g["sh"], g["means2d"], eval_count, stream,
                          plan=self.plan if self.schedule != "tiles" else None,
                          raster_ws=self.raster_ws if getattr(self, "_ckpt_written", False) else None,
-                         pair_capacity=self.capacity if det else None)
+                         pair_capacity=self.capacity if det else None, dL_ddepth=dL_ddepth)
 
     def iteration(self, cam: GsCamera, target, stream=None, wait=True):
         """One fwd+bwd iteration: project, bin+sort, blend, L1 gradient, backward. wait=False runs

@@ -156,7 +156,11 @@ gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const gs_camera* 
  *   for tiles longer than the plan's chunk length L, per chunk of L list entries and per pixel
  *   the transmittance after the chunk and the colour the chunk added, which lets
  *   gs_rasterize_bwd split such tiles (the image is then summed chunk by chunk).
- * Outputs: d_image [h,w,3]; d_final_T [h,w] the transmittance after the last added splat;
+ * Outputs: d_image [h,w,3]; d_depth [h,w] (optional, NULL = not rendered): the depth channel,
+ *   the splats' camera z through the same weights, D = sum z_i alpha_i T_i with background depth
+ *   0 (section 5: any channel, depth included, blends with the same weights; with a workspace
+ *   its per-chunk parts are stored too, for a backward with d_dL_ddepth);
+ *   d_final_T [h,w] the transmittance after the last added splat;
  *   d_n_contrib [h,w] uint32: number of tile-list entries up to and including the last added
  *   splat (0 if none). d_eval_count: NULL, or a device uint64 to which the number of
  *   (pixel, entry) evaluations is added (a work counter for measurement).
@@ -165,8 +169,8 @@ gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const gs_camera* 
 size_t gs_raster_workspace_bytes(void);
 gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const gs_camera* cam, const uint32_t* d_ids,
                            const uint32_t* d_tile_ranges, const uint32_t* d_raster_plan, void* d_raster_ws,
-                           float* d_image, float* d_final_T, uint32_t* d_n_contrib, uint64_t* d_eval_count,
-                           void* stream);
+                           float* d_image, float* d_depth, float* d_final_T, uint32_t* d_n_contrib,
+                           uint64_t* d_eval_count, void* stream);
 
 /*
  * gs_rasterize_bwd -- gradients of a loss L with respect to the raw parameters, given
@@ -185,6 +189,10 @@ gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const gs_camera*
  *   workgroup, an inner chunk starting from the forward's checkpoints (the transmittance after
  *   the chunk, and S = T_final background + the colour each later chunk added); with a plan
  *   only, the tiles are taken in its order; without, in id order;
+ *   d_dL_ddepth [h,w] (optional, NULL = none): the gradient on the depth channel of
+ *   gs_rasterize_fwd, which then joins the colour channels (dD/dz_i = alpha_i T_i and a depth
+ *   term in dD/dalpha_i) and reaches the means through the camera z; with d_raster_ws the
+ *   forward must have rendered d_depth into that workspace;
  *   d_workspace of at least gs_bwd_workspace_bytes(n) bytes (device).
  * Outputs (overwritten, not accumulated): d_grad_means [n,3], d_grad_log_scales [n,3],
  *   d_grad_quats [n,4], d_grad_opacity_logits [n], d_grad_sh [n,(sh_degree+1)^2,3], and
@@ -196,8 +204,8 @@ gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float* d_means, c
                            const float* d_quats, const float* d_opacity_logits, const float* d_sh,
                            const gs_camera* cam, const gs_projected* proj, const uint32_t* d_ids,
                            const uint32_t* d_tile_ranges, const uint32_t* d_raster_plan, const void* d_raster_ws,
-                           const float* d_final_T, const uint32_t* d_n_contrib,
-                           const float* d_dL_dimage, void* d_workspace, size_t workspace_bytes,
+                           const float* d_final_T, const uint32_t* d_n_contrib, const float* d_dL_dimage,
+                           const float* d_dL_ddepth, void* d_workspace, size_t workspace_bytes,
                            float* d_grad_means, float* d_grad_log_scales, float* d_grad_quats,
                            float* d_grad_opacity_logits, float* d_grad_sh, float* d_grad_means2d,
                            uint64_t* d_eval_count, void* stream);
@@ -210,7 +218,7 @@ gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float* d_means, c
  * slots of a Gaussian are added in a fixed order (one wave per Gaussian, strided lanes, then a
  * fixed lane tree); inside a tile the four waves' sums of a splat are added in wave order.
  * Arguments as gs_rasterize_bwd, plus pair_capacity: at least the P of gs_bin_and_sort (the
- *   capacity given to it will do); d_workspace (256-byte aligned) of at least
+ *   capacity given to it will do); d_dL_ddepth as in gs_rasterize_bwd; d_workspace (256-byte aligned) of at least
  *   gs_bwd_det_workspace_bytes(n, pair_capacity) bytes. If P > pair_capacity every gradient is 0
  *   (as after a binning overflow). Results agree with gs_rasterize_bwd to rounding.
  * Errors: those of gs_rasterize_bwd, GS_ERR_INVALID_ARG for pair_capacity < 0 or a misaligned
@@ -224,7 +232,8 @@ gs_status gs_rasterize_bwd_deterministic(int32_t n, int32_t sh_degree, const flo
                                          const uint32_t* d_tile_ranges, const uint32_t* d_raster_plan,
                                          const void* d_raster_ws, const float* d_final_T,
                                          const uint32_t* d_n_contrib, const float* d_dL_dimage,
-                                         int64_t pair_capacity, void* d_workspace, size_t workspace_bytes,
+                                         const float* d_dL_ddepth, int64_t pair_capacity, void* d_workspace,
+                                         size_t workspace_bytes,
                                          float* d_grad_means, float* d_grad_log_scales, float* d_grad_quats,
                                          float* d_grad_opacity_logits, float* d_grad_sh, float* d_grad_means2d,
                                          uint64_t* d_eval_count, void* stream);

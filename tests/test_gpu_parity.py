@@ -38,11 +38,13 @@ def _full_pixels(cam):
     return np.stack([r.ravel(), c.ravel()], -1).astype(np.int32)
 
 
-def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7, label="", bwd="atomic"):
+def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7, label="", bwd="atomic",
+                   depth=False):
     """Project, bin, forward (and backward) on the GPU; compare every stage with the oracle.
     bwd: "atomic" (gs_rasterize_bwd), "det" (gs_rasterize_bwd_deterministic, run twice over a
     scrambled workspace: the two results must be equal bit for bit), "det_tiles" (the same
-    without the raster plan and checkpoints)."""
+    without the raster plan and checkpoints). depth: render the depth channel too (compared within
+    1e-4 of the largest depth) and give the backward a seeded gradient on it."""
     gs, torch = env
     t0 = time.time()
     log(f"[{label}] n={scene['means'].shape[0]} {cam_dict['width']}x{cam_dict['height']} deg={scene['sh_degree']}")
@@ -75,7 +77,8 @@ def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7
     nc = torch.empty(H, W, device="cuda", dtype=torch.int32)
     evals = torch.zeros(1, device="cuda", dtype=torch.int64)
     rws = torch.empty(gs.gs_raster_workspace_bytes(), device="cuda", dtype=torch.uint8)
-    gs.gs_rasterize_fwd(params["n"], proj, cam, ids, ranges, img, fT, nc, evals, plan=plan, raster_ws=rws)
+    dep = torch.empty(H, W, device="cuda") if depth else None
+    gs.gs_rasterize_fwd(params["n"], proj, cam, ids, ranges, img, fT, nc, evals, plan=plan, raster_ws=rws, depth=dep)
     torch.cuda.synchronize()
     pix = _full_pixels(cam_dict) if pixels is None else pixels
     o_fwd = oracle.render(o_proj, cam_dict, pixels=pix)
@@ -84,6 +87,12 @@ def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7
     dmax, nfrag = compare_forward(img.cpu().numpy(), fT.cpu().numpy(), nc.cpu().numpy(), ids_np, ranges_np, o_fwd,
                                   pix, W)
     assert nfrag <= max(2, len(pix) // 50), f"{nfrag} fragile pixels"
+    if depth:
+        dg = dep.cpu().numpy().astype(np.float64)[pix[:, 0], pix[:, 1]]
+        dref = o_fwd["depth"].reshape(-1)
+        ok = ~o_fwd["fragile"].reshape(-1)
+        dtol = 1e-4 * max(1.0, float(np.abs(dref).max()))
+        assert np.all(np.abs(dg - dref)[ok] <= dtol), f"depth channel differs by {np.abs(dg - dref)[ok].max():.3e}"
     log(f"[{label}] forward: {len(pix)} px, max |diff| {dmax:.2e}, fragile {nfrag}, evals {int(evals.item())} "
         f"({time.time() - t0:.1f}s)")
     if not backward:
@@ -103,6 +112,14 @@ def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7
     ws = torch.empty(gs.gs_bwd_det_workspace_bytes(params["n"], cap) if det else gs.gs_bwd_workspace_bytes(params["n"]),
                      device="cuda", dtype=torch.uint8)
     dimg_d = torch.from_numpy(dimg).cuda()
+    gdsel = None
+    gdep_d = None
+    if depth:
+        gdsel = synth.random_image_grad(H, W, seed=grad_seed + 1)[..., 0][pix[:, 0], pix[:, 1]].astype(np.float64)
+        gdsel[o_fwd["fragile"].reshape(-1)] = 0.0
+        gdep = np.zeros((H, W), np.float32)
+        gdep[pix[:, 0], pix[:, 1]] = gdsel
+        gdep_d = torch.from_numpy(gdep).cuda()
     use_plan = bwd != "det_tiles"
 
     def run_bwd():
@@ -111,7 +128,7 @@ def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7
                             dimg_d, ws, pipe_grads["means"], pipe_grads["log_scales"], pipe_grads["quats"],
                             pipe_grads["opacity_logits"], pipe_grads["sh"], g2d_out,
                             plan=plan if use_plan else None, raster_ws=rws if use_plan else None,
-                            pair_capacity=cap if det else None)
+                            pair_capacity=cap if det else None, dL_ddepth=gdep_d)
         torch.cuda.synchronize()
 
     run_bwd()
@@ -122,7 +139,7 @@ def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7
         run_bwd()
         same = all(torch.equal(first[k], v) for k, v in pipe_grads.items()) and torch.equal(first["means2d"], g2d_out)
         assert same, "the deterministic backward gave different bits on a second run"
-    g2d, aref2d = oracle.render_backward(o_proj, cam_dict, gsel, pixels=pix)
+    g2d, aref2d = oracle.render_backward(o_proj, cam_dict, gsel, pixels=pix, dL_ddepth=gdsel)
     raw = oracle.project_backward(scene, cam_dict, g2d, aref2d)
     gpu = {k: v.cpu().numpy() for k, v in pipe_grads.items()}
     worst = compare_grads(gpu, raw, scene["sh_degree"], label)
@@ -217,6 +234,23 @@ def test_deterministic_backward_capacity_and_arguments(env):
     with pytest.raises(gs.GsError):
         gs.gs_rasterize_bwd(*args(P - 1, big[4:]), pair_capacity=P - 1)
     assert gs.gs_bwd_det_workspace_bytes(params["n"], -1) == 0
+
+
+# ---- depth channel --------------------------------------------------------------------------------
+@pytest.mark.parametrize("case,bwd", [("tiny", "atomic"), ("ragged", "det"), ("distill_30k", "atomic"),
+                                      ("mid_150k_sh3", "det"), ("tiny", "det_tiles")])
+def test_depth_channel(env, case, bwd):
+    if case == "tiny":
+        wl = synth.WORKLOADS["tiny_1k"]
+        scene, cam, pix = synth.make_scene(wl), synth.make_cameras(wl)[0], None
+    elif case == "ragged":
+        scene = synth.random_scene(300, seed=21, width=37, height=23, focal=30.0, sh_degree=3, logit_std=2.0)
+        cam, pix = synth.make_camera(np.eye(4), 37, 23, 30.0, background=(0.2, 0.4, 0.6)), None
+    else:
+        wl = synth.WORKLOADS[case]
+        scene, cam = synth.make_scene(wl), synth.make_cameras(wl)[0]
+        pix = synth.sample_pixels(cam["width"], cam["height"], 4096, seed=1)
+    _pipeline_case(env, scene, cam, pixels=pix, label=f"{case} depth", bwd=bwd, depth=True)
 
 
 # ---- tile-count variants (camera options) ---------------------------------------------------------
