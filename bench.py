@@ -57,8 +57,11 @@ def parse():
     ap.add_argument("--streams", type=int, default=4,
                     help="camera iterations in flight at once, each on its own HIP stream with its own buffers "
                          "(1 with --optimizer, whose updates every iteration must see)")
-    ap.add_argument("--deterministic", action="store_true",
-                    help="the bitwise-reproducible backward (gs_rasterize_bwd_deterministic)")
+    ap.add_argument("--backward", choices=("auto", "atomic", "deterministic"), default="auto",
+                    help="gs_rasterize_bwd (fp32 atomics) or gs_rasterize_bwd_deterministic (per-pair records, "
+                         "bitwise reproducible); auto: the deterministic one up to 4M pairs per camera, where "
+                         "concurrent iterations run it faster (no contended global atomics), else the atomic one")
+    ap.add_argument("--deterministic", action="store_true", help="same as --backward deterministic")
     ap.add_argument("--optimizer", action="store_true",
                     help="a training step: each step also takes an Adam step on the raw parameters")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -215,7 +218,6 @@ def main():
 
     def make_pipe():
         p = gs.Pipeline(params, W, H, pair_capacity=1 << 16)
-        p.deterministic = args.deterministic
         # the workload's loss: L1, or 0.8 L1 + 0.2 (1 - SSIM) (gs_loss_l1_ssim)
         p.ssim_lambda = 0.2 if wl.loss == "l1_dssim" else 0.0
         return p
@@ -231,7 +233,13 @@ def main():
     pipe.reserve_pairs(cap)
     # concurrent camera iterations: their own buffers (pairs, images, workspaces, gradients) and
     # streams (default priority); the Gaussians are shared read-only
+    backward = "deterministic" if args.deterministic else args.backward
+    if backward == "auto":
+        backward = "deterministic" if need <= 4_000_000 else "atomic"
+    pipe.deterministic = backward == "deterministic"
     pipes = [pipe] + [make_pipe() for _ in range(nstreams - 1)]
+    for p in pipes:
+        p.deterministic = pipe.deterministic
     for p in pipes[1:]:
         p.reserve_pairs(cap)
     streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(nstreams - 1)]
@@ -294,15 +302,14 @@ def main():
 
     result = {
         "metric": "fwd+bwd iterations/sec and Mpix/s at 30k Gaussians 1280x720; sorted pairs/sec"
-                  + (" (training steps: fwd+bwd+Adam)" if args.optimizer else "")
-                  + (" (deterministic backward)" if args.deterministic else ""),
+                  + (" (training steps: fwd+bwd+Adam)" if args.optimizer else ""),
         "value": its, "unit": "iterations/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": 1e3 * elapsed / args.steps, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
         "mpix_per_s": its * W * H / 1e6, "sorted_pairs_per_s": steps_pairs / elapsed,
         "config": {"workload": wl.name, "gaussians": wl.n, "width": W, "height": H, "cameras": ncam,
                    "loss": "0.8 L1 + 0.2 (1 - SSIM)" if pipe.ssim_lambda > 0 else "L1",
-                   "concurrent_cameras": nstreams,
+                   "concurrent_cameras": nstreams, "backward": backward,
                    "sh_degree": wl.sh_degree, "teacher_gaussians": int(teacher["means"].shape[0]),
                    "mean_pairs_per_camera": float(np.mean(pairs)), "parallelism": "single GPU"},
     }
