@@ -58,13 +58,13 @@ def load():
     for name in ("orc_project_f32", "orc_project_f64"):
         getattr(lib, name).argtypes = [i32, i32] + [P] * 6 + [i32, i32] + [P] * 10
         getattr(lib, name).restype = ctypes.c_int
-    lib.orc_bin.argtypes = [i32, P, P, P, i32, i32, i64, P, P, P]
+    lib.orc_bin.argtypes = [i32] + [P] * 6 + [i32, i32, i32, i64, P, P, P]
     lib.orc_bin.restype = i64
     for name in ("orc_render_f32", "orc_render_f64"):
-        getattr(lib, name).argtypes = [i32] + [P] * 7 + [i32, i32, P, i64, P, f64] + [P] * 7
+        getattr(lib, name).argtypes = [i32] + [P] * 7 + [i32, i32, i32, P, i64, P, f64] + [P] * 7
         getattr(lib, name).restype = ctypes.c_int
     for name in ("orc_render_bwd_f32", "orc_render_bwd_f64"):
-        getattr(lib, name).argtypes = [i32] + [P] * 7 + [i32, i32, P, i64, P, f64, P, P, P]
+        getattr(lib, name).argtypes = [i32] + [P] * 7 + [i32, i32, i32, P, i64, P, f64, P, P, P]
         getattr(lib, name).restype = ctypes.c_int
     for name in ("orc_project_bwd_f32", "orc_project_bwd_f64"):
         getattr(lib, name).argtypes = [i32, i32] + [P] * 6 + [i32, i32] + [P] * 8
@@ -91,14 +91,21 @@ RADIUS_MODES = {"gsplat": 0, "3dgs": 1}
 
 
 def camera_array(cam, dtype=np.float32):
-    """Pack a camera dict into the oracle's 26-number layout. Options (section 4 of the PyTorch
+    """Pack a camera dict into the oracle's 27-number layout. Options (section 4 of the PyTorch
     lesson): cam["radius_mode"] "gsplat" (default, the opacity-aware per-axis extent) or "3dgs"
-    (ceil(3 sqrt(lambda_max)) on both axes); cam["antialiased"] (default False)."""
+    (ceil(3 sqrt(lambda_max)) on both axes); cam["antialiased"] (default False);
+    cam["tight_tiles"] (default False: every tile of the rectangle; True: only the tiles whose
+    pixel centres the splat's ellipse reaches)."""
     v = np.asarray(cam["viewmat"], dtype=np.float64).reshape(16)
     bg = np.asarray(cam.get("background", (0.0, 0.0, 0.0)), dtype=np.float64)
-    opts = [RADIUS_MODES[cam.get("radius_mode", "gsplat")], 1.0 if cam.get("antialiased", False) else 0.0]
+    opts = [RADIUS_MODES[cam.get("radius_mode", "gsplat")], 1.0 if cam.get("antialiased", False) else 0.0,
+            1.0 if cam.get("tight_tiles", False) else 0.0]
     arr = np.concatenate([v, [cam["fx"], cam["fy"], cam["cx"], cam["cy"], cam.get("near", 0.01)], bg, opts])
     return _c(arr, dtype)
+
+
+def _tight(cam):
+    return 1 if cam.get("tight_tiles", False) else 0
 
 
 def tiles_of(cam):
@@ -192,7 +199,11 @@ def bin_pairs(proj, cam):
     keys = np.empty(P, np.uint64)
     ids = np.empty(P, np.uint32)
     ranges = np.empty((tx * ty, 2), np.uint32)
-    got = lib.orc_bin(n, _p(tiles), _p(rects), _p(depths), tx, ty, P, _p(keys), _p(ids), _p(ranges))
+    m2 = _c(proj["means2d"], np.float32)
+    con = _c(proj["conics"], np.float32)
+    op = _c(proj["opacities"], np.float32)
+    got = lib.orc_bin(n, _p(tiles), _p(rects), _p(depths), _p(m2), _p(con), _p(op), _tight(cam), tx, ty, P,
+                      _p(keys), _p(ids), _p(ranges))
     assert got == P
     return keys, ids, ranges
 
@@ -204,8 +215,9 @@ def _render_inputs(proj, dtype):
 
 def render(proj, cam, pixels=None, dtype=np.float32, band_eps=None):
     """Per-pixel render: every pixel walks, in one stable global depth order, the un-culled
-    Gaussians whose tile rectangle holds its tile (the tiled renderer's lists; with the default
-    opacity-aware radius that is every Gaussian that can reach it, i.e. the dense render).
+    Gaussians whose tile list holds its tile (the tiled renderer's lists: the tile rectangle, or
+    with cam["tight_tiles"] the tiles of it the ellipse reaches; with the default opacity-aware
+    radius that is every Gaussian that can reach the pixel, i.e. the dense render).
 
     pixels: None (whole image, row-major) or int array [M,2] of (row, col).
     Returns dict image [M,3] f64, depth [M] f64 (the depth channel: camera z blended with the same
@@ -235,7 +247,7 @@ def render(proj, cam, pixels=None, dtype=np.float32, band_eps=None):
     esc = ctypes.c_int64(0)
     nev = ctypes.c_int64(0)
     fn = getattr(lib, "orc_render_" + _suffix(dtype))
-    fn(n, *[_p(a) for a in ins], W, H, _p(bg), M, _p(pix), float(band_eps), _p(image), _p(final_T),
+    fn(n, *[_p(a) for a in ins], _tight(cam), W, H, _p(bg), M, _p(pix), float(band_eps), _p(image), _p(final_T),
        _p(last_id), _p(n_contrib), _p(fragile), ctypes.byref(esc), ctypes.byref(nev), _p(depth))
     out = {"image": image, "depth": depth, "final_T": final_T, "last_id": last_id, "n_contrib": n_contrib,
            "fragile": fragile.astype(bool), "escapes": int(esc.value), "n_near": int(nev.value)}
@@ -276,7 +288,8 @@ def render_backward(proj, cam, dL_dimage, pixels=None, dtype=np.float32, band_ep
     g2d = np.empty((n, 10))
     aref = np.empty((n, 10))
     fn = getattr(lib, "orc_render_bwd_" + _suffix(dtype))
-    fn(n, *[_p(a) for a in ins], W, H, _p(bg), M, _p(pix), float(band_eps), _p(g), _p(gd), _p(g2d), _p(aref))
+    fn(n, *[_p(a) for a in ins], _tight(cam), W, H, _p(bg), M, _p(pix), float(band_eps), _p(g), _p(gd), _p(g2d),
+       _p(aref))
     return g2d, aref
 
 

@@ -119,22 +119,24 @@ template <class T> bool finite(T x) { return std::isfinite(x); }
 
 // ---------------------------------------------------------------------------------------------
 // Camera: row-major world->camera viewmat [4,4] with OpenCV axes (+x right, +y down, +z
-// forward) and pinhole intrinsics (the PyTorch lesson, section 3). Packed as 26 numbers:
-// viewmat[16], fx, fy, cx, cy, near, bg[3], radius_mode, antialiased; width and height are
-// passed separately. The two options are the variants section 4 of the lesson lists:
+// forward) and pinhole intrinsics (the PyTorch lesson, section 3). Packed as 27 numbers:
+// viewmat[16], fx, fy, cx, cy, near, bg[3], radius_mode, antialiased, tight_tiles; width and
+// height are passed separately. The first two options are the variants section 4 of the lesson lists:
 // radius_mode 0 = gsplat's opacity-aware per-axis extent, 1 = the original 3DGS radius
 // ceil(3 sqrt(lambda_max)) for both axes; antialiased 1 = opacity times the compensation
 // sqrt(det Sigma2d / det(Sigma2d + 0.3 I)) (gsplat's "antialiased" mode, Mip-Splatting's 2D
-// filter), read with Sigma2d the covariance before the eps2d dilation.
+// filter), read with Sigma2d the covariance before the eps2d dilation. tight_tiles 1 lists a
+// Gaussian only in the tiles of its rectangle that its ellipse reaches (tight_span below): the
+// tighter bound the lesson's section 4 says means fewer sort keys and less blending.
 // ---------------------------------------------------------------------------------------------
-constexpr int kNumCam = 26;
+constexpr int kNumCam = 27;
 template <class T> struct Cam {
   T V[16];
   T fx, fy, cx, cy, near_plane;
   T bg[3];
   int W, H;
   int tiles_x, tiles_y;
-  int radius_mode, antialiased;
+  int radius_mode, antialiased, tight_tiles;
 };
 
 template <class T> Cam<T> make_cam(const T* p, int W, int H) {
@@ -144,6 +146,7 @@ template <class T> Cam<T> make_cam(const T* p, int W, int H) {
   c.bg[0] = p[21]; c.bg[1] = p[22]; c.bg[2] = p[23];
   c.radius_mode = (int)p[24];
   c.antialiased = (int)p[25];
+  c.tight_tiles = (int)p[26];
   c.W = W; c.H = H;
   c.tiles_x = (W + 15) / 16;
   c.tiles_y = (H + 15) / 16;
@@ -242,6 +245,68 @@ template <class T> struct Proj {
   T color[3];
   int radius_3dgs;
 };
+
+// ---------------------------------------------------------------------------------------------
+// Tight tile rows. A pixel centre q sees alpha >= 1/255 only where sigma(q - mu') <= ln(255 o),
+// and never beyond sigma = k^2 / 2 with k = min(3.33, sqrt(2 ln(255 o))) (section 4's extent:
+// past 3.33 sigma even o = 1 is below 1/255). Tile (tx, ty) of the rectangle is kept when the
+// ellipse sigma <= s2 meets the box of its pixel centres [16 tx + 0.5, 16 tx + 15.5] x
+// [16 ty + 0.5, 16 ty + 15.5]. s2 widens k^2 / 2 by 0.002 + s (0.002 + q / 65536) with
+// q = A C / (A C - B^2) >= 1, the ratio that bounds the size of sigma's terms on the ellipse
+// (4 s q), so that fp32 rounding of sigma or of the row bounds cannot drop a reached pixel.
+// Per row (v = y - mu'_y over the row's centre rows clipped to |v| <= sqrt(2 s2 A / D)) the
+// ellipse spans u = x - mu'_x in [L, R]; R is largest at v = -B t and L smallest at v = B t,
+// t = sqrt(2 s2 / (C D)) (clamped into the row), with u = (-B v +- sqrt(2 s2 A - D v^2)) / A.
+// The row keeps tiles [xs, xe) = [ceil((mu'_x + L - 15.5) / 16), floor((mu'_x + R - 0.5) / 16) + 1)
+// inside the rectangle. Degenerate or extreme shapes (D <= 0, q >= 1e6, 2 s2 / D >= 1e30) keep
+// the whole rectangle. Decisions in T (fp32 for parity), one op at a time.
+// span gets 2 ints per rectangle row (xs, xe), xe == xs for an empty row. Returns the count.
+// ---------------------------------------------------------------------------------------------
+template <class T>
+uint32_t tight_span(T mx, T my, T A, T B, T C, T o, const int32_t* rect, std::vector<int32_t>& span) {
+  const int x0 = rect[0], y0 = rect[1], x1 = rect[2], y1 = rect[3];
+  span.assign((size_t)2 * (size_t)std::max(y1 - y0, 0), 0);
+  uint32_t cnt = 0;
+  T kk = (T)2 * Act<T>::log((T)255 * o);
+  if (!(kk > (T)0)) kk = (T)0;
+  T k = std::sqrt(kk);
+  if (k > (T)3.33) k = (T)3.33;
+  const T s = (T)0.5 * k * k;
+  const T D = A * C - B * B;
+  const T q = (A * C) / D;
+  bool full = !(A > (T)0) || !(C > (T)0) || !(D > (T)0) || !(q < (T)1e6);
+  T s2 = (T)0, E = (T)0;
+  if (!full) {
+    s2 = s + ((T)0.002 + s * ((T)0.002 + q * ((T)1 / (T)65536)));
+    E = (T)2 * s2 / D;
+    full = !(E < (T)1e30);
+  }
+  for (int ty = y0; ty < y1; ++ty) {
+    T xs = (T)x0, xe = (T)x1;
+    if (!full) {
+      const T ry = std::sqrt(E * A), t = std::sqrt(E / C);
+      const T ylo = (T)(16 * ty) + (T)0.5 - my, yhi = (T)(16 * ty) + (T)15.5 - my;
+      const T lo = std::max(ylo, -ry), hi = std::min(yhi, ry);
+      if (lo > hi) {
+        xs = xe = (T)x0;
+      } else {
+        const T vr = std::min(std::max(-(B * t), lo), hi);
+        const T vl = std::min(std::max(B * t, lo), hi);
+        const T R = (-(B * vr) + std::sqrt(std::max((T)2 * s2 * A - D * vr * vr, (T)0))) / A;
+        const T L = (-(B * vl) - std::sqrt(std::max((T)2 * s2 * A - D * vl * vl, (T)0))) / A;
+        xs = std::ceil((mx + L - (T)15.5) / (T)16);
+        xe = std::floor((mx + R - (T)0.5) / (T)16) + (T)1;
+        xs = std::min(std::max(xs, (T)x0), (T)x1);
+        xe = std::min(std::max(xe, (T)x0), (T)x1);
+        if (xe < xs) xe = xs;
+      }
+    }
+    span[2 * (ty - y0)] = (int32_t)xs;
+    span[2 * (ty - y0) + 1] = (int32_t)xe;
+    cnt += (uint32_t)((int32_t)xe - (int32_t)xs);
+  }
+  return cnt;
+}
 
 template <class T>
 void project_one(const T* mean, const T* log_scale, const T* quat, T logit, const T* sh,
@@ -400,6 +465,11 @@ void project_one(const T* mean, const T* log_scale, const T* quat, T logit, cons
   P.rect[0] = (int)x0; P.rect[1] = (int)y0; P.rect[2] = (int)x1; P.rect[3] = (int)y1;
   if (!(P.rect[2] > P.rect[0] && P.rect[3] > P.rect[1])) return;  // nothing on screen
   P.tiles = (uint32_t)((P.rect[2] - P.rect[0]) * (P.rect[3] - P.rect[1]));
+  if (cam.tight_tiles) {
+    std::vector<int32_t> span;
+    P.tiles = tight_span<T>(P.m2d[0], P.m2d[1], P.conic[0], P.conic[1], P.conic[2], P.o_eff, P.rect, span);
+    if (P.tiles == 0) return;  // the ellipse reaches no pixel centre
+  }
 
   P.culled = false;
 }
@@ -411,6 +481,7 @@ template <class T> struct Splat2D {
   T mx, my, A, B, C, o, col[3];
   T z;           // camera depth: the value the depth channel blends
   T skip_above;  // ln(255 o) + 1e-3: sigma above this implies alpha < 1/255 (exact shortcut)
+  std::vector<int32_t> span;  // tight tile rows (xs, xe) per rectangle row; empty: whole rectangle
 };
 
 struct Contributor {
@@ -465,6 +536,10 @@ void trace_pixel(T px, T py, const std::vector<int>& order, const std::vector<Sp
     // the dense render; none with the opacity-aware radius) and then ignored.
     bool inside = tile_x >= rects[g * 4 + 0] && tile_x < rects[g * 4 + 2] &&
                   tile_y >= rects[g * 4 + 1] && tile_y < rects[g * 4 + 3];
+    if (inside && !s.span.empty()) {
+      const int r = tile_y - rects[g * 4 + 1];
+      inside = tile_x >= s.span[2 * r] && tile_x < s.span[2 * r + 1];
+    }
     if (!inside) {
       if (!(sigma < (T)0 || alpha < thr_a)) ++tr.escapes;
       continue;
@@ -487,15 +562,17 @@ void trace_pixel(T px, T py, const std::vector<int>& order, const std::vector<Sp
 
 template <class T>
 void build_splats(int n, const T* means2d, const T* conics, const T* opac, const T* colors,
-                  const T* depths, const uint32_t* tiles, std::vector<Splat2D<T>>& S,
-                  std::vector<int>& order) {
+                  const T* depths, const uint32_t* tiles, const int32_t* rects, int tight,
+                  std::vector<Splat2D<T>>& S, std::vector<int>& order) {
   S.resize(n);
   order.clear();
   for (int g = 0; g < n; ++g) {
     S[g] = {means2d[2 * g], means2d[2 * g + 1], conics[3 * g], conics[3 * g + 1], conics[3 * g + 2],
-            opac[g], {colors[3 * g], colors[3 * g + 1], colors[3 * g + 2]}, depths[g], (T)0};
+            opac[g], {colors[3 * g], colors[3 * g + 1], colors[3 * g + 2]}, depths[g], (T)0, {}};
     S[g].skip_above = opac[g] > (T)0 ? (T)(std::log(255.0 * (double)opac[g]) + 1e-3) : (T)0;
     if (tiles[g] > 0) order.push_back(g);
+    if (tight && tiles[g] > 0)
+      tight_span<T>(S[g].mx, S[g].my, S[g].A, S[g].B, S[g].C, S[g].o, rects + 4 * g, S[g].span);
   }
   // one global, stable ascending-depth order (ties keep ascending Gaussian id)
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return depths[a] < depths[b]; });
@@ -549,13 +626,13 @@ void pixel_values(const Trace& tr, const std::vector<Splat2D<T>>& S, double px, 
 
 template <class T>
 int render_impl(int n, const T* means2d, const T* conics, const T* opac, const T* colors,
-                const T* depths, const uint32_t* tiles, const int32_t* rects, int W, int H,
+                const T* depths, const uint32_t* tiles, const int32_t* rects, int tight, int W, int H,
                 const T* bg, int64_t npix, const int32_t* pix, double band_eps, double* image,
                 double* final_T, int32_t* last_id, int32_t* n_contrib, uint8_t* fragile,
                 int64_t* escapes, int64_t* n_eval, double* depth_img) {
   std::vector<Splat2D<T>> S;
   std::vector<int> order;
-  build_splats<T>(n, means2d, conics, opac, colors, depths, tiles, S, order);
+  build_splats<T>(n, means2d, conics, opac, colors, depths, tiles, rects, tight, S, order);
   if (!pix) npix = (int64_t)W * H;
   int64_t esc = 0, nev = 0;
 #pragma omp parallel reduction(+ : esc, nev)
@@ -607,12 +684,12 @@ int render_impl(int n, const T* means2d, const T* conics, const T* opac, const T
 // the pixel's bound on the relative rounding of its transmittance, summed over pixels.
 template <class T>
 int render_bwd_impl(int n, const T* means2d, const T* conics, const T* opac, const T* colors,
-                    const T* depths, const uint32_t* tiles, const int32_t* rects, int W, int H,
+                    const T* depths, const uint32_t* tiles, const int32_t* rects, int tight, int W, int H,
                     const T* bg, int64_t npix, const int32_t* pix, double band_eps,
                     const double* dL_dimg, const double* dL_ddepth, double* g2d, double* aref) {
   std::vector<Splat2D<T>> S;
   std::vector<int> order;
-  build_splats<T>(n, means2d, conics, opac, colors, depths, tiles, S, order);
+  build_splats<T>(n, means2d, conics, opac, colors, depths, tiles, rects, tight, S, order);
   if (!pix) npix = (int64_t)W * H;
   const int nt = nthreads();
   std::vector<std::vector<double>> accg(nt), acca(nt);
@@ -994,10 +1071,12 @@ int orc_project_f64(int n, int sh_degree, const double* means, const double* log
 
 // -- binning: brute-force enumeration, std::stable_sort on the 64-bit key, linear range scan -------
 // keys[p] = (ty * tiles_x + tx) << 32 | float_bits(depth); ids[p] = Gaussian id; Gaussians are
-// enumerated in id order and each rectangle row-major, so stability leaves equal keys in id order.
+// enumerated in id order and each rectangle row-major (with tight 1 only the tiles tight_span
+// keeps), so stability leaves equal keys in id order.
 // ranges[t] = [start, end) into the sorted list; empty tiles are (0, 0). Returns the pair count.
-int64_t orc_bin(int n, const uint32_t* tiles, const int32_t* rects, const float* depths, int tiles_x,
-                int tiles_y, int64_t capacity, uint64_t* keys, uint32_t* ids, uint32_t* ranges) {
+int64_t orc_bin(int n, const uint32_t* tiles, const int32_t* rects, const float* depths, const float* means2d,
+                const float* conics, const float* opac, int tight, int tiles_x, int tiles_y, int64_t capacity,
+                uint64_t* keys, uint32_t* ids, uint32_t* ranges) {
   int64_t P = 0;
   for (int g = 0; g < n; ++g) P += tiles[g];
   if (P > capacity) return P;
@@ -1007,8 +1086,14 @@ int64_t orc_bin(int n, const uint32_t* tiles, const int32_t* rects, const float*
     if (tiles[g] == 0) continue;
     uint32_t dbits;
     std::memcpy(&dbits, &depths[g], 4);
+    std::vector<int32_t> span;
+    if (tight)
+      tight_span<float>(means2d[2 * g], means2d[2 * g + 1], conics[3 * g], conics[3 * g + 1], conics[3 * g + 2],
+                        opac[g], rects + 4 * g, span);
     for (int ty = rects[4 * g + 1]; ty < rects[4 * g + 3]; ++ty)
       for (int tx = rects[4 * g + 0]; tx < rects[4 * g + 2]; ++tx) {
+        if (tight && !(tx >= span[2 * (ty - rects[4 * g + 1])] && tx < span[2 * (ty - rects[4 * g + 1]) + 1]))
+          continue;
         uint64_t tile = (uint64_t)ty * (uint64_t)tiles_x + (uint64_t)tx;
         pairs.push_back({(tile << 32) | (uint64_t)dbits, (uint32_t)g});
       }
@@ -1031,34 +1116,34 @@ int64_t orc_bin(int n, const uint32_t* tiles, const int32_t* rects, const float*
 
 // -- dense render ----------------------------------------------------------------------------------
 int orc_render_f32(int n, const float* means2d, const float* conics, const float* opac, const float* colors,
-                   const float* depths, const uint32_t* tiles, const int32_t* rects, int W, int H,
+                   const float* depths, const uint32_t* tiles, const int32_t* rects, int tight, int W, int H,
                    const float* bg, int64_t npix, const int32_t* pix, double band_eps, double* image,
                    double* final_T, int32_t* last_id, int32_t* n_contrib, uint8_t* fragile, int64_t* escapes,
                    int64_t* n_eval, double* depth_img) {
-  return render_impl<float>(n, means2d, conics, opac, colors, depths, tiles, rects, W, H, bg, npix, pix,
+  return render_impl<float>(n, means2d, conics, opac, colors, depths, tiles, rects, tight, W, H, bg, npix, pix,
                             band_eps, image, final_T, last_id, n_contrib, fragile, escapes, n_eval, depth_img);
 }
 int orc_render_f64(int n, const double* means2d, const double* conics, const double* opac,
                    const double* colors, const double* depths, const uint32_t* tiles, const int32_t* rects,
-                   int W, int H, const double* bg, int64_t npix, const int32_t* pix, double band_eps,
+                   int tight, int W, int H, const double* bg, int64_t npix, const int32_t* pix, double band_eps,
                    double* image, double* final_T, int32_t* last_id, int32_t* n_contrib, uint8_t* fragile,
                    int64_t* escapes, int64_t* n_eval, double* depth_img) {
-  return render_impl<double>(n, means2d, conics, opac, colors, depths, tiles, rects, W, H, bg, npix, pix,
+  return render_impl<double>(n, means2d, conics, opac, colors, depths, tiles, rects, tight, W, H, bg, npix, pix,
                              band_eps, image, final_T, last_id, n_contrib, fragile, escapes, n_eval, depth_img);
 }
 
 int orc_render_bwd_f32(int n, const float* means2d, const float* conics, const float* opac, const float* colors,
-                       const float* depths, const uint32_t* tiles, const int32_t* rects, int W, int H,
-                       const float* bg, int64_t npix, const int32_t* pix, double band_eps,
+                       const float* depths, const uint32_t* tiles, const int32_t* rects, int tight, int W,
+                       int H, const float* bg, int64_t npix, const int32_t* pix, double band_eps,
                        const double* dL_dimg, const double* dL_ddepth, double* g2d, double* aref) {
-  return render_bwd_impl<float>(n, means2d, conics, opac, colors, depths, tiles, rects, W, H, bg, npix, pix,
+  return render_bwd_impl<float>(n, means2d, conics, opac, colors, depths, tiles, rects, tight, W, H, bg, npix, pix,
                                 band_eps, dL_dimg, dL_ddepth, g2d, aref);
 }
 int orc_render_bwd_f64(int n, const double* means2d, const double* conics, const double* opac,
                        const double* colors, const double* depths, const uint32_t* tiles, const int32_t* rects,
-                       int W, int H, const double* bg, int64_t npix, const int32_t* pix, double band_eps,
+                       int tight, int W, int H, const double* bg, int64_t npix, const int32_t* pix, double band_eps,
                        const double* dL_dimg, const double* dL_ddepth, double* g2d, double* aref) {
-  return render_bwd_impl<double>(n, means2d, conics, opac, colors, depths, tiles, rects, W, H, bg, npix, pix,
+  return render_bwd_impl<double>(n, means2d, conics, opac, colors, depths, tiles, rects, tight, W, H, bg, npix, pix,
                                  band_eps, dL_dimg, dL_ddepth, g2d, aref);
 }
 

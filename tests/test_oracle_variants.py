@@ -186,3 +186,118 @@ def test_variant_gradients_finite_differences(opts):
             minus[name][idx] -= h
             fd = (loss(plus) - loss(minus)) / (2 * h)
             assert abs(fd - an[idx]) <= 1e-6 + 1e-5 * abs(an[idx]), (name, idx, fd, an[idx])
+
+
+# ---- tight tile lists (cam["tight_tiles"]) ------------------------------------------------------
+
+def _needles(n, seed, W, H, f):
+    """A scene with elongated, rotated splats (one log-scale up to 3 above the others)."""
+    sc = synth.random_scene(n, seed, width=W, height=H, focal=f, log_scales=(-4.5, -2.5))
+    rng = np.random.default_rng(seed + 1000)
+    sc["log_scales"][:, 0] += rng.uniform(0.0, 3.0, n)
+    return sc
+
+
+def _box_min_sigma(mx, my, A, B, C, bx0, bx1, by0, by1):
+    """min over the box [bx0, bx1] x [by0, by1] of sigma = 0.5 (A u^2 + C v^2) + B u v with
+    (u, v) = (x - mx, y - my), in float64: 0 when the mean is inside, otherwise the least of the
+    four edges, each a 1D convex quadratic minimised on its interval."""
+    if bx0 <= mx <= bx1 and by0 <= my <= by1:
+        return 0.0
+    best = np.inf
+    for x in (bx0, bx1):  # vertical edges: sigma(v) = 0.5 C v^2 + B u v + 0.5 A u^2
+        u = x - mx
+        v = min(max(-B * u / C, by0 - my), by1 - my)
+        best = min(best, 0.5 * (A * u * u + C * v * v) + B * u * v)
+    for y in (by0, by1):
+        v = y - my
+        u = min(max(-B * v / A, bx0 - mx), bx1 - mx)
+        best = min(best, 0.5 * (A * u * u + C * v * v) + B * u * v)
+    return best
+
+
+@pytest.mark.parametrize("seed,opts", [(11, {}), (12, {"antialiased": True}), (13, {"radius_mode": "3dgs"})])
+def test_tight_tiles_are_the_box_test(seed, opts):
+    """Each listed tile, and each tile of the rectangle left out, against an independent float64
+    decision: the least sigma over the tile's pixel-centre box compared with
+    s2 = s + 0.002 + s (0.002 + q / 65536), s = k^2 / 2, q = A C / (A C - B^2)."""
+    W, H, f = 96, 80, 70.0
+    n = 150
+    sc = _needles(n, seed, W, H, f)
+    cam = _cam(W, H, f, tight_tiles=True, **opts)
+    pt = oracle.project(sc, cam)
+    pr = oracle.project(sc, _cam(W, H, f, **opts))
+    keys, ids, _ = oracle.bin_pairs(pt, cam)
+    tx_n = (W + 15) // 16
+    listed = {(int(g), int(k >> 32)) for k, g in zip(keys, ids)}
+    assert len(listed) == len(keys) == int(pt["tiles_touched"].sum())
+    checked = near = dropped = 0
+    for g in range(n):
+        if pr["tiles_touched"][g] == 0:
+            assert pt["tiles_touched"][g] == 0
+            continue
+        mx, my = (float(v) for v in pt["means2d"][g])
+        A, B, C = (float(v) for v in pt["conics"][g])
+        o = float(pt["opacities"][g])
+        k = min(3.33, math.sqrt(max(2.0 * math.log(255.0 * o), 0.0)))
+        s = 0.5 * k * k
+        q = A * C / (A * C - B * B)
+        s2 = s + 0.002 + s * (0.002 + q / 65536.0)
+        x0, y0, x1, y1 = pr["rects"][g]
+        for ty in range(y0, y1):
+            for tx in range(x0, x1):
+                m = _box_min_sigma(mx, my, A, B, C, 16 * tx + 0.5, 16 * tx + 15.5, 16 * ty + 0.5, 16 * ty + 15.5)
+                if abs(m - s2) <= 1e-4 * (1.0 + s2):
+                    near += 1
+                    continue  # within fp32 rounding of the threshold: either answer is right
+                assert ((g, ty * tx_n + tx) in listed) == (m <= s2), (g, tx, ty, m, s2)
+                checked += 1
+                dropped += m > s2
+        # nothing outside the rectangle
+        assert all(x0 <= t % tx_n < x1 and y0 <= t // tx_n < y1 for gg, t in listed if gg == g)
+    assert checked > 300 and dropped > 30 and near < checked // 50
+    # fewer pairs than the rectangles, the same rendered image, no pixel left unreached
+    assert pt["tiles_touched"].sum() < pr["tiles_touched"].sum()
+
+
+@pytest.mark.parametrize("seed", [21, 22, 23])
+def test_tight_tiles_lose_no_pixel(seed):
+    """Every pixel a splat reaches (alpha >= 1/255 at its centre) lies in one of its listed
+    tiles: the render counts none outside ("escapes"), and equals the rectangle lists' render
+    bit for bit (the tiles dropped held only pixels the splat does not reach)."""
+    W, H, f = 80, 64, 60.0
+    sc = _needles(80, seed, W, H, f)
+    cam_r = _cam(W, H, f)
+    cam_t = _cam(W, H, f, tight_tiles=True)
+    a = oracle.render(oracle.project(sc, cam_r), cam_r)
+    pt = oracle.project(sc, cam_t)
+    b = oracle.render(pt, cam_t)
+    assert a["escapes"] == 0 and b["escapes"] == 0
+    assert np.array_equal(a["image"], b["image"]) and np.array_equal(a["n_contrib"], b["n_contrib"])
+
+
+def test_tight_tiles_closed_form():
+    """A round splat of radius-3.33-sigma extent rho centred in a tile: it keeps exactly the
+    tiles whose pixel-centre box lies within distance sqrt(2 s2) sigma of its mean."""
+    f, z, W = 100.0, 4.0, 128
+    cam = _cam(W, W, f, tight_tiles=True)
+    sc = _one([0.0, 0.0, z], 0.35, 8.0)
+    # mean at pixel (56, 56), the middle of tile (3, 3); sigma^2 = (f 0.25 / z)^2 + 0.3
+    sc["means"][0, :2] = (56.0 - cam["cx"]) * z / f
+    pr = oracle.project(sc, cam, np.float64)
+    v = (f * 0.35 / z) ** 2 + 0.3
+    s = 0.5 * 3.33 ** 2
+    s2 = s + 0.002 + s * (0.002 + 1.0 / 65536.0)
+    reach = math.sqrt(2.0 * s2 * v)
+    keys, _, _ = oracle.bin_pairs(oracle.project(sc, cam), cam)
+    got = sorted(int(k >> 32) for k in keys)
+    exp = []
+    for ty in range(8):
+        for tx in range(8):
+            dx = max(16 * tx + 0.5 - 56.0, 0.0, 56.0 - (16 * tx + 15.5))
+            dy = max(16 * ty + 0.5 - 56.0, 0.0, 56.0 - (16 * ty + 15.5))
+            if dx * dx + dy * dy <= reach * reach:
+                exp.append(ty * 8 + tx)
+    x0, y0, x1, y1 = pr["rects"][0]
+    assert len(exp) < (x1 - x0) * (y1 - y0)  # the rectangle's corners are dropped
+    assert got == exp
