@@ -69,8 +69,9 @@ bool valid_camera(const gs_camera* cam, std::string* why) {
     *why = "fx/fy must be > 0";
     return false;
   }
-  if ((cam->radius_mode != 0 && cam->radius_mode != 1) || (cam->antialiased != 0 && cam->antialiased != 1)) {
-    *why = "radius_mode and antialiased must be 0 or 1";
+  if ((cam->radius_mode != 0 && cam->radius_mode != 1) || (cam->antialiased != 0 && cam->antialiased != 1) ||
+      (cam->tight_tiles != 0 && cam->tight_tiles != 1)) {
+    *why = "radius_mode, antialiased and tight_tiles must be 0 or 1";
     return false;
   }
   return true;

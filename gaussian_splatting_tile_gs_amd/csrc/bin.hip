@@ -7,8 +7,8 @@
 //
 // How (MI355X design, not the pages'): a full 64-bit key sort would take 6 radix passes over the
 // pairs. Here the depth part is settled once per Gaussian instead of once per pair:
-//   1. k_bin_prep     depth keys (culled -> 0xFFFFFFFF), packed (count, first tile, width)
-//                     rectangles, per-workgroup digit histograms of the four depth passes, and
+//   1. k_bin_prep     depth keys (culled -> 0xFFFFFFFF), packed (count, first tile, width,
+//                     height) rectangles, per-workgroup digit histograms of the four depth passes, and
 //                     the zeroing of every counter, look-back word and
 //                     tile range the later kernels rely on (no memset nodes, no host wait)
 //   2. k_hist_reduce  the per-workgroup depth histograms summed (beyond 32 workgroups; below
@@ -212,13 +212,14 @@ __global__ __launch_bounds__(kSortThreads) void k_bin_prep(int32_t n, const floa
     if (idx < n) {
       keys[idx] = k[i];
       vals[idx] = (uint32_t)idx;
-      uint32_t tb = 0, w = 1;
+      uint32_t tb = 0, w = 1, h = 0;
       if (t[i] > 0) {
         const TileRect rc = tile_rect(m[i].x, m[i].y, (float)r[i].x, (float)r[i].y, tiles_x, tiles_y);
         tb = (uint32_t)(rc.y0 * tiles_x + rc.x0);
         w = (uint32_t)(rc.x1 - rc.x0);
+        h = (uint32_t)(rc.y1 - rc.y0);
       }
-      rec[idx] = make_uint4(t[i], tb, w, 0u);
+      rec[idx] = make_uint4(t[i], tb, w, h);
 #pragma unroll
       for (int p = 0; p < 4; ++p) atomicAdd(&s_hist[p][(k[i] >> (8 * p)) & 0xFF], 1u);
     }
@@ -250,13 +251,18 @@ __global__ __launch_bounds__(kRadix) void k_hist_reduce(const uint32_t* __restri
 // Pairs per tile, tile ranges and the tile-digit histograms of the pair sort. The count of pairs
 // per tile does not depend on the depth order, so extra workgroups of the first two depth passes
 // compute it while those passes sort: row y of a rectangle puts one pair on each tile of the run
-// [a, a + w) of tile ids, i.e. +1 at a and -1 at a + w of a difference array over the tiles
+// [a, a + w) of tile ids (with tight tiles the row's run [xs, xe) of tight_row), i.e. +1 at a
+// and -1 at a + w of a difference array over the tiles
 // (pass 0); one workgroup then prefix-sums it into per-tile counts, ranges and histograms
 // (pass 1). The total of the counts is P, so that workgroup also knows whether P fits the
 // capacity (else every range stays (0, 0)).
 // ---------------------------------------------------------------------------------------------
 struct TileCountArgs {
-  const uint4* rec;     // (count, first tile, width, -) per Gaussian, id order (k_bin_prep)
+  const uint4* rec;     // (count, first tile, width, height) per Gaussian, id order (k_bin_prep)
+  const float* means2d; // with tight: the ellipse of each Gaussian (tight_shape)
+  const float* conics;
+  const float* opac;
+  int32_t tight;        // camera option tight_tiles: rows hold the tight runs, not the whole width
   int32_t n;
   int32_t tiles_x;
   uint32_t ntiles;
@@ -277,6 +283,11 @@ constexpr int kRowGaussians = 2048;  // Gaussians per row workgroup (two per lan
 // screen-filling splat does not hold up its wave. The difference array is staged in LDS (`lds`,
 // `lds_words` long) when it fits.
 constexpr uint32_t kOwnRows = 8;
+__device__ __forceinline__ TightShape tight_of(const TileCountArgs& a, uint32_t g) {
+  const float2 m = *reinterpret_cast<const float2*>(a.means2d + 2 * (size_t)g);
+  const float* c = a.conics + 3 * (size_t)g;
+  return tight_shape(m.x, m.y, c[0], c[1], c[2], a.opac[g]);
+}
 __device__ void tile_rows(const TileCountArgs& a, uint32_t rb, uint32_t* lds, uint32_t lds_words) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool staged = a.ntiles + 1 <= lds_words;
@@ -290,11 +301,23 @@ __device__ void tile_rows(const TileCountArgs& a, uint32_t rb, uint32_t* lds, ui
   for (int k = 0; k < 2; ++k) {
     const int64_t j = (int64_t)rb * kRowGaussians + wave * 128 + k * 64 + lane;
     const uint4 r = j < a.n ? a.rec[j] : make_uint4(0u, 0u, 1u, 0u);
-    const uint32_t h = r.x / r.z;
+    const uint32_t h = r.w;
     if (h <= kOwnRows) {
-      for (uint32_t y = 0; y < h; ++y) {
-        atomicAdd(&diff[r.y + y * tx], 1u);
-        atomicSub(&diff[r.y + y * tx + r.z], 1u);
+      if (a.tight && h > 0) {
+        const TightShape ts = tight_of(a, (uint32_t)j);
+        const int x0 = (int)(r.y % tx), y0 = (int)(r.y / tx);
+        for (uint32_t y = 0; y < h; ++y) {
+          const int2 sp = tight_row(ts, y0 + (int)y, x0, x0 + (int)r.z);
+          if (sp.y > sp.x) {
+            atomicAdd(&diff[(uint32_t)(y0 + (int)y) * tx + (uint32_t)sp.x], 1u);
+            atomicSub(&diff[(uint32_t)(y0 + (int)y) * tx + (uint32_t)sp.y], 1u);
+          }
+        }
+      } else {
+        for (uint32_t y = 0; y < h; ++y) {
+          atomicAdd(&diff[r.y + y * tx], 1u);
+          atomicSub(&diff[r.y + y * tx + r.z], 1u);
+        }
       }
     }
     uint64_t tall = __ballot(h > kOwnRows);
@@ -303,9 +326,22 @@ __device__ void tile_rows(const TileCountArgs& a, uint32_t rb, uint32_t* lds, ui
       tall &= tall - 1;
       const uint32_t hh = __builtin_amdgcn_readlane(h, src);
       const uint32_t tb = __builtin_amdgcn_readlane(r.y, src), w = __builtin_amdgcn_readlane(r.z, src);
-      for (uint32_t y = lane; y < hh; y += 64) {
-        atomicAdd(&diff[tb + y * tx], 1u);
-        atomicSub(&diff[tb + y * tx + w], 1u);
+      if (a.tight) {
+        const uint32_t js = (uint32_t)__builtin_amdgcn_readlane((int)j, src);
+        const TightShape ts = tight_of(a, js);
+        const int x0 = (int)(tb % tx), y0 = (int)(tb / tx);
+        for (uint32_t y = lane; y < hh; y += 64) {
+          const int2 sp = tight_row(ts, y0 + (int)y, x0, x0 + (int)w);
+          if (sp.y > sp.x) {
+            atomicAdd(&diff[(uint32_t)(y0 + (int)y) * tx + (uint32_t)sp.x], 1u);
+            atomicSub(&diff[(uint32_t)(y0 + (int)y) * tx + (uint32_t)sp.y], 1u);
+          }
+        }
+      } else {
+        for (uint32_t y = lane; y < hh; y += 64) {
+          atomicAdd(&diff[tb + y * tx], 1u);
+          atomicSub(&diff[tb + y * tx + w], 1u);
+        }
       }
     }
   }
@@ -867,7 +903,7 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(8)
     const uint32_t* __restrict__ chunk_first, int32_t tiles_x, int shift, int bits,
     const uint32_t* __restrict__ hist, uint32_t* __restrict__ status, uint32_t* __restrict__ ticket,
     uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint64_t* __restrict__ out_keys64,
-    const uint32_t* __restrict__ depth_bits) {
+    const uint32_t* __restrict__ depth_bits, TileCountArgs targs) {
   constexpr int ITEMS = 4, TILE = kSortThreads * ITEMS;
   static_assert(TILE == kEmitChunk && kEmitThreads == kSortThreads, "one emission chunk per sort tile");
   static_assert(kFuseWindow == kSortThreads, "one staged Gaussian per thread");
@@ -907,7 +943,31 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(8)
       s_tb[tid] = d.y;
       s_w[tid] = d.z;
       s_g[tid] = d.w;
-      if (d.x >= lo && d.x < hi) atomicMax(&s_owner[d.x - lo], (uint32_t)tid);
+      if (!targs.tight) {
+        if (d.x >= lo && d.x < hi) atomicMax(&s_owner[d.x - lo], (uint32_t)tid);
+      } else if (d.x < hi) {
+        // tight rows: the Gaussian's positions run row by row, each row a run of tile ids. The
+        // run holding position a >= lo leaves at chunk position a - cs its tile id (s_pk), its
+        // Gaussian (s_pv) and the marker a - cs + 1, which the max-scan hands to the run.
+        const uint4 r = targs.rec[d.w];  // (count, first tile, width, height)
+        if ((uint64_t)d.x + r.x > lo) {
+          const TightShape ts = tight_of(targs, d.w);
+          const int x0 = (int)(d.y % (uint32_t)tiles_x), y0 = (int)(d.y / (uint32_t)tiles_x);
+          uint64_t pos = d.x;
+          for (uint32_t y = 0; y < r.w && pos < hi; ++y) {
+            const int2 sp = tight_row(ts, y0 + (int)y, x0, x0 + (int)r.z);
+            const uint32_t len = (uint32_t)(sp.y - sp.x);
+            if (len > 0 && pos + len > lo) {
+              const uint64_t a = pos > lo ? pos : lo;
+              const uint32_t pc = (uint32_t)(a - cs);
+              s_pk[pc] = (uint32_t)(y0 + (int)y) * (uint32_t)tiles_x + (uint32_t)sp.x + (uint32_t)(a - pos);
+              s_pv[pc] = d.w;
+              s_owner[pc - done] = pc + 1u;
+            }
+            pos += len;
+          }
+        }
+      }
     }
     __syncthreads();
     // positions below the last window Gaussian's start are covered by this window
@@ -929,16 +989,41 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(8)
 #pragma unroll
     for (int q = 0; q < kEmitPer; ++q) s_owner[tid * kEmitPer + q] = max(before, o[q]);
     __syncthreads();
+    if (!targs.tight) {
 #pragma unroll
-    for (int q = 0; q < kEmitPer; ++q) {
-      const uint32_t p = done + (uint32_t)(q * kSortThreads + tid);
-      if (p < lim) {
-        const uint32_t li = s_owner[p - done];
-        const uint32_t local = (uint32_t)(cs + p - s_off[li]);
-        const uint32_t ww = s_w[li];
-        const uint32_t row = local / ww, col = local - row * ww;
-        s_pk[p] = s_tb[li] + row * (uint32_t)tiles_x + col;
-        s_pv[p] = s_g[li];
+      for (int q = 0; q < kEmitPer; ++q) {
+        const uint32_t p = done + (uint32_t)(q * kSortThreads + tid);
+        if (p < lim) {
+          const uint32_t li = s_owner[p - done];
+          const uint32_t local = (uint32_t)(cs + p - s_off[li]);
+          const uint32_t ww = s_w[li];
+          const uint32_t row = local / ww, col = local - row * ww;
+          s_pk[p] = s_tb[li] + row * (uint32_t)tiles_x + col;
+          s_pv[p] = s_g[li];
+        }
+      }
+    } else {
+      // every position of [lo, cover) has a run start at or below it (the run holding lo starts
+      // there); read all first, the run starts are overwritten with their own values after
+      uint32_t tk[kEmitPer], tv[kEmitPer];
+#pragma unroll
+      for (int q = 0; q < kEmitPer; ++q) {
+        const uint32_t p = done + (uint32_t)(q * kSortThreads + tid);
+        tk[q] = tv[q] = 0u;
+        if (p < lim) {
+          const uint32_t st = s_owner[p - done] - 1u;
+          tk[q] = s_pk[st] + (p - st);
+          tv[q] = s_pv[st];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < kEmitPer; ++q) {
+        const uint32_t p = done + (uint32_t)(q * kSortThreads + tid);
+        if (p < lim) {
+          s_pk[p] = tk[q];
+          s_pv[p] = tv[q];
+        }
       }
     }
     __syncthreads();
@@ -1071,6 +1156,8 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
     return set_error(GS_ERR_INVALID_ARG, "gs_bin_and_sort: NULL d_keys/d_ids with capacity > 0");
   if (n > 0 && (!proj || !proj->d_depths || !proj->d_tiles_touched || !proj->d_means2d || !proj->d_radii))
     return set_error(GS_ERR_INVALID_ARG, "gs_bin_and_sort: NULL projected record with n > 0");
+  if (n > 0 && cam->tight_tiles && (!proj->d_conics || !proj->d_opacities))
+    return set_error(GS_ERR_INVALID_ARG, "gs_bin_and_sort: tight_tiles needs the conics and opacities");
   const BinLayout L = bin_layout(n, pair_capacity, cam);
   if (n > 0 && (!d_workspace || workspace_bytes < L.total))
     return set_error(GS_ERR_INVALID_ARG, "gs_bin_and_sort: workspace smaller than gs_bin_workspace_bytes()");
@@ -1120,6 +1207,10 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
   // pass 0 carries the tile-row workgroups, pass 1 the tile-count finalizer
   TileCountArgs targs;
   targs.rec = (const uint4*)(ws + L.rec);
+  targs.means2d = proj->d_means2d;
+  targs.conics = proj->d_conics;
+  targs.opac = proj->d_opacities;
+  targs.tight = cam->tight_tiles;
   targs.n = n;
   targs.tiles_x = tiles_x;
   targs.ntiles = (uint32_t)ntiles;
@@ -1170,7 +1261,7 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
                          L.pbits[0], ctrl->hist_pair[0], pstatus, &ctrl->tickets[4],
                          last ? (uint32_t*)nullptr : (oa ? kA : kB), last ? d_ids : (oa ? vA : vB),
                          last ? d_keys : (uint64_t*)nullptr,
-                         last ? (const uint32_t*)proj->d_depths : (const uint32_t*)nullptr);
+                         last ? (const uint32_t*)proj->d_depths : (const uint32_t*)nullptr, targs);
     }
     // 8 keys per lane (8192 per workgroup) for large pair buffers
     const bool wide = pair_capacity > ((int64_t)1 << 19);

@@ -27,6 +27,7 @@ struct DevCamera {
   float bg[3];
   int32_t tiles_x, tiles_y;
   int32_t radius_mode, antialiased;  // the section-4 variants (0, 0: the default)
+  int32_t tight_tiles;               // list only the tiles of the rectangle the ellipse reaches
 };
 
 inline DevCamera to_dev(const gs_camera& c) {
@@ -40,6 +41,7 @@ inline DevCamera to_dev(const gs_camera& c) {
   d.tiles_y = (c.height + GS_TILE_SIZE - 1) / GS_TILE_SIZE;
   d.radius_mode = c.radius_mode;
   d.antialiased = c.antialiased;
+  d.tight_tiles = c.tight_tiles;
   return d;
 }
 
@@ -111,6 +113,68 @@ __device__ __forceinline__ TileRect tile_rect(float mx, float my, float rx, floa
   y0 = omin(omax(y0, 0.0f), (float)tiles_y);
   y1 = omin(omax(y1, 0.0f), (float)tiles_y);
   return {(int32_t)x0, (int32_t)y0, (int32_t)x1, (int32_t)y1};
+}
+
+// ---------------------------------------------------------------------------------------------
+// Tight tile rows (camera option tight_tiles): row ty of a splat's rectangle keeps the tiles
+// [xs, xe) whose pixel-centre box [16 tx + 0.5, 16 tx + 15.5] x [16 ty + 0.5, 16 ty + 15.5]
+// meets the ellipse sigma <= s2. No pixel centre beyond sigma = k^2 / 2 sees alpha >= 1/255
+// (k = min(3.33, sqrt(2 ln(255 o))), section 4's extent), and s2 widens that level by
+// 0.002 + s (0.002 + q / 65536), q = A C / (A C - B^2) >= 1 bounding the size of sigma's terms
+// on the ellipse (4 s q), so that fp32 rounding in the blend's sigma or in these bounds cannot
+// drop a reached pixel. With v = y - my over the row's centre rows (clipped to |v| <=
+// sqrt(2 s2 A / D), D = A C - B^2) the ellipse spans u = x - mx in [L, R]: R is largest at
+// v = -B t and L smallest at v = B t, t = sqrt(2 s2 / (C D)) (clamped into the row), with
+// u = (-B v +- sqrt(2 s2 A - D v^2)) / A. Degenerate or extreme shapes (D <= 0, q >= 1e6,
+// 2 s2 / D >= 1e30) keep the whole row. The projection counts with these functions, the binning
+// lists with them and the deterministic backward indexes pairs with them: the same fp32 ops,
+// contraction off, give the same tiles everywhere.
+// ---------------------------------------------------------------------------------------------
+struct TightShape {
+  float mx, my, A, B, C, D, s2, E;
+  bool full;  // keep every tile of the rectangle
+};
+__device__ __forceinline__ TightShape tight_shape(float mx, float my, float A, float B, float C, float o) {
+  TightShape t;
+  t.mx = mx;
+  t.my = my;
+  t.A = A;
+  t.B = B;
+  t.C = C;
+  float kk = 2.0f * act_log(255.0f * o);
+  if (!(kk > 0.0f)) kk = 0.0f;
+  float k = sqrtf(kk);
+  if (k > 3.33f) k = 3.33f;
+  const float s = 0.5f * k * k;
+  t.D = A * C - B * B;
+  const float q = (A * C) / t.D;
+  t.full = !(A > 0.0f) || !(C > 0.0f) || !(t.D > 0.0f) || !(q < 1e6f);
+  t.s2 = 0.0f;
+  t.E = 0.0f;
+  if (!t.full) {
+    t.s2 = s + (0.002f + s * (0.002f + q * 0x1p-16f));
+    t.E = 2.0f * t.s2 / t.D;
+    t.full = !(t.E < 1e30f);
+  }
+  return t;
+}
+// (xs, xe) of tile row ty inside the rectangle columns [x0, x1); xe == xs when the row is empty
+__device__ __forceinline__ int2 tight_row(const TightShape& t, int ty, int x0, int x1) {
+  if (t.full) return make_int2(x0, x1);
+  const float ry = sqrtf(t.E * t.A), tt = sqrtf(t.E / t.C);
+  const float ylo = ((float)(16 * ty) + 0.5f) - t.my, yhi = ((float)(16 * ty) + 15.5f) - t.my;
+  const float lo = omax(ylo, -ry), hi = omin(yhi, ry);
+  if (lo > hi) return make_int2(x0, x0);
+  const float vr = omin(omax(-(t.B * tt), lo), hi);
+  const float vl = omin(omax(t.B * tt, lo), hi);
+  const float R = (-(t.B * vr) + sqrtf(omax(2.0f * t.s2 * t.A - t.D * vr * vr, 0.0f))) / t.A;
+  const float L = (-(t.B * vl) - sqrtf(omax(2.0f * t.s2 * t.A - t.D * vl * vl, 0.0f))) / t.A;
+  float xs = ceilf((t.mx + L - 15.5f) / 16.0f);
+  float xe = floorf((t.mx + R - 0.5f) / 16.0f) + 1.0f;
+  xs = omin(omax(xs, (float)x0), (float)x1);
+  xe = omin(omax(xe, (float)x0), (float)x1);
+  if (xe < xs) xe = xs;
+  return make_int2((int)xs, (int)xe);
 }
 
 // ---------------------------------------------------------------------------------------------

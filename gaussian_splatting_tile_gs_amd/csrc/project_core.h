@@ -204,9 +204,19 @@ __device__ __forceinline__ ProjF32 project_f32(float m0, float m1, float m2, flo
   }
   const TileRect rc = tile_rect(mx, my, rx, ry, cam.tiles_x, cam.tiles_y);
   if (!(rc.x1 > rc.x0 && rc.y1 > rc.y0)) return P;
+  uint32_t tiles = (uint32_t)((rc.x1 - rc.x0) * (rc.y1 - rc.y0));
+  if (cam.tight_tiles) {  // only the tiles of the rectangle the ellipse reaches
+    const TightShape ts = tight_shape(mx, my, con0, con1, con2, o_eff);
+    tiles = 0;
+    for (int ty = rc.y0; ty < rc.y1; ++ty) {
+      const int2 sp = tight_row(ts, ty, rc.x0, rc.x1);
+      tiles += (uint32_t)(sp.y - sp.x);
+    }
+    if (tiles == 0) return P;
+  }
   P.rad[0] = (int32_t)rx;
   P.rad[1] = (int32_t)ry;
-  P.tiles = (uint32_t)((rc.x1 - rc.x0) * (rc.y1 - rc.y0));
+  P.tiles = tiles;
   P.drawn = true;
   return P;
 }

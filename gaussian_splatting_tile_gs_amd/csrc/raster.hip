@@ -342,14 +342,25 @@ __device__ __forceinline__ void reduce9_to_lds(const float* v, float* acc, int l
 
 // Slot of the pair (Gaussian g, tile (tx, ty)) in the per-pair gradient records: the pairs of a
 // Gaussian are contiguous from base[g] (the exclusive prefix sum of tiles_touched in id order),
-// in row-major order over its tile rectangle (the rectangle of the projection and the emitter).
+// in row-major order over its tile rectangle (the rectangle of the projection and the emitter; with
+// tight tiles only the tiles of each row's tight run).
 __device__ __forceinline__ uint32_t pair_slot(uint32_t g, const float* __restrict__ means2d,
                                               const int32_t* __restrict__ radii, const uint32_t* __restrict__ base,
-                                              int tx, int ty, int32_t tiles_x, int32_t tiles_y) {
+                                              int tx, int ty, const DevCamera& cam, float A, float B, float C,
+                                              float o) {
   const float2 m = *reinterpret_cast<const float2*>(means2d + 2 * g);
   const int2 r = *reinterpret_cast<const int2*>(radii + 2 * g);
-  const TileRect rc = tile_rect(m.x, m.y, (float)r.x, (float)r.y, tiles_x, tiles_y);
-  return base[g] + (uint32_t)((ty - rc.y0) * (rc.x1 - rc.x0) + (tx - rc.x0));
+  const TileRect rc = tile_rect(m.x, m.y, (float)r.x, (float)r.y, cam.tiles_x, cam.tiles_y);
+  if (!cam.tight_tiles) return base[g] + (uint32_t)((ty - rc.y0) * (rc.x1 - rc.x0) + (tx - rc.x0));
+  // tight tiles: the runs of the rows above, then the place in this row's run
+  const TightShape ts = tight_shape(m.x, m.y, A, B, C, o);
+  uint32_t local = 0;
+  for (int y = rc.y0; y < ty; ++y) {
+    const int2 sp = tight_row(ts, y, rc.x0, rc.x1);
+    local += (uint32_t)(sp.y - sp.x);
+  }
+  const int2 sp = tight_row(ts, ty, rc.x0, rc.x1);
+  return base[g] + local + (uint32_t)(tx - sp.x);
 }
 
 // Per-lane gradient terms of one splat for one pixel, back to front: consumes T (the
@@ -412,7 +423,7 @@ __device__ __forceinline__ void reduce_terms(const float* v, float* acc, int lan
 // front, like the sums of the whole-tile walk: a sum of the terms, never a difference).
 // Where the 2D gradient of a (tile, splat) pair goes (MODE):
 //   kBwdAtomic  added to g2d [9, n] with global fp32 atomics;
-//   kBwdRecords written to its own slot of rec [rec_cap, 9] (pair_slot), summed per Gaussian later;
+//   kBwdRecords written to its own slot of rec [rec_cap, 10] (pair_slot), summed per Gaussian later;
 //   kBwdDeterministic  as kBwdRecords, and the four waves' sums of a splat are kept apart in LDS
 //               (per 64-splat group, with a barrier after each group) and added in wave order,
 //               so every floating-point sum has a fixed order: bitwise-reproducible gradients.
@@ -500,7 +511,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
         rB = conics[3 * g + 1];
         rC = conics[3 * g + 2];
         ro = opac[g];
-        if (REC) rslot = pair_slot(g, means2d, radii, pair_base, tx, ty, cam.tiles_x, cam.tiles_y);
+        if (REC) rslot = pair_slot(g, means2d, radii, pair_base, tx, ty, cam, rA, rB, rC, ro);
       }
     }
     if (!DET)

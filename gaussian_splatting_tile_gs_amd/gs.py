@@ -33,7 +33,8 @@ class GsCamera(ctypes.Structure):
     _fields_ = [("viewmat", ctypes.c_float * 16), ("fx", ctypes.c_float), ("fy", ctypes.c_float),
                 ("cx", ctypes.c_float), ("cy", ctypes.c_float), ("width", ctypes.c_int32),
                 ("height", ctypes.c_int32), ("near_plane", ctypes.c_float), ("background", ctypes.c_float * 3),
-                ("radius_mode", ctypes.c_int32), ("antialiased", ctypes.c_int32)]
+                ("radius_mode", ctypes.c_int32), ("antialiased", ctypes.c_int32),
+                ("tight_tiles", ctypes.c_int32)]
 
 
 RADIUS_MODES = {"gsplat": 0, "3dgs": 1}
@@ -122,7 +123,8 @@ def _stream(stream):
 
 def make_camera(cam: dict) -> GsCamera:
     """GsCamera from a camera dict (viewmat [4,4], fx, fy, cx, cy, width, height, near, background;
-    optional radius_mode "gsplat" (default) or "3dgs", antialiased (default False))."""
+    optional radius_mode "gsplat" (default) or "3dgs", antialiased (default False), tight_tiles
+    (default False: the whole tile rectangle; True: only the tiles the splat's ellipse reaches))."""
     c = GsCamera()
     v = np.asarray(cam["viewmat"], np.float32).reshape(16)
     for i in range(16):
@@ -135,6 +137,7 @@ def make_camera(cam: dict) -> GsCamera:
         c.background[i] = float(bg[i])
     c.radius_mode = RADIUS_MODES[cam.get("radius_mode", "gsplat")]
     c.antialiased = 1 if cam.get("antialiased", False) else 0
+    c.tight_tiles = 1 if cam.get("tight_tiles", False) else 0
     return c
 
 

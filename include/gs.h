@@ -60,9 +60,16 @@ typedef struct gs_camera {
    * antialiased 1: the blend's opacity is o sqrt(det Sigma2d / det(Sigma2d + 0.3 I)), Sigma2d
    *   the projected covariance before the dilation (gsplat's "antialiased" mode, Mip-Splatting's
    *   2D filter); the cull and the extent use that opacity, and the backward differentiates it.
+   * tight_tiles 1: a splat is listed only in the tiles of its rectangle whose pixel-centre box
+   *   its ellipse sigma <= s2 reaches, s2 = k^2 / 2 (k the opacity-aware extent, at most 3.33)
+   *   widened by 0.002 + s (0.002 + q / 65536), q = A C / (A C - B^2) of the conic: section 4's
+   *   tighter bound, fewer pairs for the sort and the blend, the same image (every pixel with
+   *   alpha >= 1/255 stays listed). Decided row by row of the rectangle in fp32; tiles_touched
+   *   is then the tight count (0: not drawn).
    * The same options must be given to every call of one iteration. */
   int32_t radius_mode;
   int32_t antialiased;
+  int32_t tight_tiles;
 } gs_camera;
 
 /* Projected records, structure of arrays of length n, written by gs_project. A Gaussian is

@@ -257,11 +257,25 @@ def test_depth_channel(env, case, bwd):
 @pytest.mark.parametrize("case,opts,bwd", [
     ("tiny", {"antialiased": True}, "atomic"), ("tiny", {"radius_mode": "3dgs"}, "atomic"),
     ("ragged", {"antialiased": True, "radius_mode": "3dgs"}, "atomic"), ("tiny", {"antialiased": True}, "det"),
-    ("distill_30k", {"antialiased": True}, "atomic"), ("mid_150k_sh3", {"radius_mode": "3dgs"}, "atomic")])
+    ("distill_30k", {"antialiased": True}, "atomic"), ("mid_150k_sh3", {"radius_mode": "3dgs"}, "atomic"),
+    ("tiny", {"tight_tiles": True}, "atomic"), ("ragged", {"tight_tiles": True, "antialiased": True}, "det"),
+    ("needles", {"tight_tiles": True}, "det"), ("needles", {"tight_tiles": True, "radius_mode": "3dgs"}, "atomic"),
+    ("giant", {"tight_tiles": True}, "det"), ("distill_30k", {"tight_tiles": True}, "det"),
+    ("mid_150k_sh3", {"tight_tiles": True, "antialiased": True}, "atomic")])
 def test_variants(env, case, opts, bwd):
     if case == "tiny":
         wl = synth.WORKLOADS["tiny_1k"]
         scene, cam, pix = synth.make_scene(wl), dict(synth.make_cameras(wl)[0]), None
+    elif case in ("needles", "giant"):
+        # needles: elongated rotated splats of up to ~20 tile rows (the per-lane and per-wave row
+        # walks); giant: a few splats of thousands of tiles each on a 1600 x 1600 image, whose
+        # row runs cross several 4096-pair emission chunks
+        n, W, f, ls = (3000, 300, 200.0, (-4.0, -2.0)) if case == "needles" else (40, 1600, 900.0, (-2.5, -0.5))
+        scene = synth.random_scene(n, seed=31, width=W, height=W, focal=f, log_scales=ls, logit_std=2.0)
+        rng = np.random.default_rng(32)
+        scene["log_scales"][:, 0] += rng.uniform(0.0, 2.5, n)
+        cam = synth.make_camera(np.eye(4), W, W, f, background=(0.2, 0.3, 0.1))
+        pix = synth.sample_pixels(W, W, 4096, seed=2)
     elif case == "ragged":
         scene = synth.random_scene(300, seed=21, width=37, height=23, focal=30.0, sh_degree=3, logit_std=2.0)
         cam, pix = synth.make_camera(np.eye(4), 37, 23, 30.0, background=(0.2, 0.4, 0.6)), None
