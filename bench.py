@@ -62,6 +62,9 @@ def parse():
                          "bitwise reproducible); auto: the deterministic one up to 4M pairs per camera, where "
                          "concurrent iterations run it faster (no contended global atomics), else the atomic one")
     ap.add_argument("--deterministic", action="store_true", help="same as --backward deterministic")
+    ap.add_argument("--tile-lists", choices=("rect", "tight"), default="rect",
+                    help="rect: every tile of a splat's rectangle; tight: only the tiles its ellipse reaches "
+                         "(camera option tight_tiles: fewer pairs, the same image)")
     ap.add_argument("--optimizer", action="store_true",
                     help="a training step: each step also takes an Adam step on the raw parameters")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -195,7 +198,7 @@ def main():
     torch.cuda.set_device(0)
     wl = synth.WORKLOADS[args.workload]
     scene = synth.make_scene(wl)
-    cams_d = synth.make_cameras(wl)
+    cams_d = [dict(c, tight_tiles=args.tile_lists == "tight") for c in synth.make_cameras(wl)]
     cams = [gs.make_camera(c) for c in cams_d]
     W, H = wl.width, wl.height
     params = gs.scene_to_device(scene)
@@ -309,7 +312,7 @@ def main():
         "mpix_per_s": its * W * H / 1e6, "sorted_pairs_per_s": steps_pairs / elapsed,
         "config": {"workload": wl.name, "gaussians": wl.n, "width": W, "height": H, "cameras": ncam,
                    "loss": "0.8 L1 + 0.2 (1 - SSIM)" if pipe.ssim_lambda > 0 else "L1",
-                   "concurrent_cameras": nstreams, "backward": backward,
+                   "concurrent_cameras": nstreams, "backward": backward, "tile_lists": args.tile_lists,
                    "sh_degree": wl.sh_degree, "teacher_gaussians": int(teacher["means"].shape[0]),
                    "mean_pairs_per_camera": float(np.mean(pairs)), "parallelism": "single GPU"},
     }

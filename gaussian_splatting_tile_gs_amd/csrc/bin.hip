@@ -302,9 +302,13 @@ __device__ void tile_rows(const TileCountArgs& a, uint32_t rb, uint32_t* lds, ui
     const int64_t j = (int64_t)rb * kRowGaussians + wave * 128 + k * 64 + lane;
     const uint4 r = j < a.n ? a.rec[j] : make_uint4(0u, 0u, 1u, 0u);
     const uint32_t h = r.w;
+    // with tight tiles each lane prepares its own Gaussian's ellipse once; the wave walk of a
+    // tall one takes it from the owning lane
+    TightShape own{};
+    if (a.tight && h > 0) own = tight_of(a, (uint32_t)j);
     if (h <= kOwnRows) {
       if (a.tight && h > 0) {
-        const TightShape ts = tight_of(a, (uint32_t)j);
+        const TightShape& ts = own;
         const int x0 = (int)(r.y % tx), y0 = (int)(r.y / tx);
         for (uint32_t y = 0; y < h; ++y) {
           const int2 sp = tight_row(ts, y0 + (int)y, x0, x0 + (int)r.z);
@@ -327,8 +331,16 @@ __device__ void tile_rows(const TileCountArgs& a, uint32_t rb, uint32_t* lds, ui
       const uint32_t hh = __builtin_amdgcn_readlane(h, src);
       const uint32_t tb = __builtin_amdgcn_readlane(r.y, src), w = __builtin_amdgcn_readlane(r.z, src);
       if (a.tight) {
-        const uint32_t js = (uint32_t)__builtin_amdgcn_readlane((int)j, src);
-        const TightShape ts = tight_of(a, js);
+        TightShape ts;
+        ts.mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.mx), src));
+        ts.my = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.my), src));
+        ts.A = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.A), src));
+        ts.B = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.B), src));
+        ts.C = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.C), src));
+        ts.D = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.D), src));
+        ts.s2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.s2), src));
+        ts.E = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.E), src));
+        ts.full = __builtin_amdgcn_readlane((int)own.full, src) != 0;
         const int x0 = (int)(tb % tx), y0 = (int)(tb / tx);
         for (uint32_t y = lane; y < hh; y += 64) {
           const int2 sp = tight_row(ts, y0 + (int)y, x0, x0 + (int)w);
@@ -950,8 +962,8 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(8)
         // run holding position a >= lo leaves at chunk position a - cs its tile id (s_pk), its
         // Gaussian (s_pv) and the marker a - cs + 1, which the max-scan hands to the run.
         const uint4 r = targs.rec[d.w];  // (count, first tile, width, height)
+        const TightShape ts = tight_of(targs, d.w);  // its loads in flight with rec's
         if ((uint64_t)d.x + r.x > lo) {
-          const TightShape ts = tight_of(targs, d.w);
           const int x0 = (int)(d.y % (uint32_t)tiles_x), y0 = (int)(d.y / (uint32_t)tiles_x);
           uint64_t pos = d.x;
           for (uint32_t y = 0; y < r.w && pos < hi; ++y) {
