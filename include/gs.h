@@ -113,13 +113,15 @@ gs_status gs_project(int32_t n, int32_t sh_degree, const float* d_means, const f
 /*
  * gs_bin_and_sort -- count, emit, sort and range ("project, count, emit, sort, range" of the
  * SplatRs tile rasterizer). For every drawn Gaussian i and every tile (tx, ty) of its rectangle
- * it forms the key (ty * tiles_x + tx) << 32 | float_bits(depth_i) and the value i, sorts the
+ * (with cam->tight_tiles, every tile of the rectangle its ellipse reaches, row by row) it forms
+ * the key (ty * tiles_x + tx) << 32 | float_bits(depth_i) and the value i, sorts the
  * pairs by key, keeping equal keys in ascending i (stable), and writes per tile the range
  * [start, end) of its pairs in the sorted list ((0, 0) for an empty tile).
  * Implementation: a stable LSD radix sort of the Gaussians by depth, a prefix scan of the tile
  * counts in depth order, emission of (tile, i) pairs in that order, and a stable LSD radix sort
  * of the pairs by tile id (Onesweep-style single-pass passes with decoupled look-back).
- * Inputs: n and proj (from gs_project with the same camera); d_workspace of at least
+ * Inputs: n and proj (from gs_project with the same camera; it reads depths, tiles_touched,
+ *   means2d and radii, and with tight_tiles also conics and opacities); d_workspace of at least
  *   gs_bin_workspace_bytes(n, pair_capacity, cam) bytes (device, 256-byte aligned, contents
  *   arbitrary on entry and need not persist between calls); pair_capacity = length of d_keys
  *   and d_ids.

@@ -8,6 +8,7 @@ Small cases are compared whole; the full workload sizes compare projection and b
 pixels/gradients on a seeded pixel sample (a loss that is non-zero only on the sample, so the
 oracle's gradients are exact).
 """
+import math
 import time
 
 import numpy as np
@@ -261,11 +262,32 @@ def test_depth_channel(env, case, bwd):
     ("tiny", {"tight_tiles": True}, "atomic"), ("ragged", {"tight_tiles": True, "antialiased": True}, "det"),
     ("needles", {"tight_tiles": True}, "det"), ("needles", {"tight_tiles": True, "radius_mode": "3dgs"}, "atomic"),
     ("giant", {"tight_tiles": True}, "det"), ("distill_30k", {"tight_tiles": True}, "det"),
-    ("mid_150k_sh3", {"tight_tiles": True, "antialiased": True}, "atomic")])
+    ("mid_150k_sh3", {"tight_tiles": True, "antialiased": True}, "atomic"),
+    ("dim_corners", {"tight_tiles": True}, "det")])
 def test_variants(env, case, opts, bwd):
     if case == "tiny":
         wl = synth.WORKLOADS["tiny_1k"]
         scene, cam, pix = synth.make_scene(wl), dict(synth.make_cameras(wl)[0]), None
+    elif case == "dim_corners":
+        # ordinary splats plus 24 dim (o = 1.02/255), sub-pixel ones on tile corners: rectangles
+        # of four tiles, no pixel centre reached, so tight lists leave them undrawn
+        W, f, z = 96, 80.0, 3.0
+        scene = synth.random_scene(200, seed=41, width=W, height=W, focal=f)
+        cam = synth.make_camera(np.eye(4), W, W, f, background=(0.1, 0.1, 0.2))
+        o = 1.02 / 255.0
+        corners = [(16.0 * i, 16.0 * j) for i in range(1, 6) for j in range(1, 6)][:24]
+        m = np.array([[(x - cam["cx"]) * z / f, (y - cam["cy"]) * z / f, z] for x, y in corners])
+        k = len(corners)
+        scene["means"] = np.concatenate([scene["means"], m]).astype(scene["means"].dtype)
+        scene["log_scales"] = np.concatenate([scene["log_scales"], np.full((k, 3), -7.0)]).astype(
+            scene["log_scales"].dtype)
+        scene["quats"] = np.concatenate([scene["quats"], np.tile([1.0, 0, 0, 0], (k, 1))]).astype(
+            scene["quats"].dtype)
+        scene["opacity_logits"] = np.concatenate([scene["opacity_logits"], np.full(k, math.log(o / (1 - o)))]).astype(
+            scene["opacity_logits"].dtype)
+        scene["sh"] = np.concatenate([scene["sh"], np.full((k,) + scene["sh"].shape[1:], 0.5)]).astype(
+            scene["sh"].dtype)
+        pix = None
     elif case in ("needles", "giant"):
         # needles: elongated rotated splats of up to ~20 tile rows (the per-lane and per-wave row
         # walks); giant: a few splats of thousands of tiles each on a 1600 x 1600 image, whose

@@ -301,3 +301,20 @@ def test_tight_tiles_closed_form():
     x0, y0, x1, y1 = pr["rects"][0]
     assert len(exp) < (x1 - x0) * (y1 - y0)  # the rectangle's corners are dropped
     assert got == exp
+
+
+def test_tight_tiles_drop_a_splat_that_reaches_no_pixel_centre():
+    """A dim splat (o = 1.02 / 255) of sub-pixel extent on a tile corner: its rectangle holds four
+    tiles, but its ellipse reaches no pixel centre, so with tight lists it is not drawn (count 0,
+    radii 0); the image is the same either way (alpha < 1/255 at every centre)."""
+    f, z, W = 100.0, 4.0, 64
+    o = 1.02 / 255.0
+    sc = _one([0.0, 0.0, z], 0.001, math.log(o / (1.0 - o)))
+    cam_r = _cam(W, W, f)
+    cam_t = _cam(W, W, f, tight_tiles=True)
+    sc["means"][0, :2] = (32.0 - cam_r["cx"]) * z / f  # pixel position (32, 32): a tile corner
+    pr = oracle.project(sc, cam_r)
+    pt = oracle.project(sc, cam_t)
+    assert pr["tiles_touched"][0] == 4 and pr["rects"][0].tolist() == [1, 1, 3, 3]
+    assert pt["tiles_touched"][0] == 0 and pt["radii"][0].tolist() == [0, 0]
+    assert np.array_equal(oracle.render(pr, cam_r)["image"], oracle.render(pt, cam_t)["image"])
