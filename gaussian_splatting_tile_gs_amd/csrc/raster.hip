@@ -997,30 +997,71 @@ __global__ __launch_bounds__(kBaseThreads) void k_base_scan(int32_t n, const uin
   if (blockIdx.x == gridDim.x - 1 && threadIdx.x == kBaseThreads - 1) *total = run;
 }
 
-// dL/d(2D parameters) of every Gaussian from its records, one wave per Gaussian: lane l adds the
-// records l, l + 64, ... in order, then a fixed DPP tree adds the lanes (a fixed order). When
-// the pairs did not fit the records (total > rec_cap; the pair sort then left every tile range
-// empty) every gradient is zero.
+// dL/d(2D parameters) of every Gaussian from its records, in an order fixed by its pair count.
+// A wave takes 64 consecutive Gaussians, one per lane: a lane whose Gaussian has at most
+// kSegLane pairs adds its records in slot order (a record is 40 B, read as five float2). The
+// Gaussians of more pairs are then taken one at a time by the whole wave: lane l adds records
+// l, l + 64, ... in order and a fixed DPP tree adds the lanes. When the pairs did not fit the
+// records (total > rec_cap; the pair sort then left every tile range empty) every gradient is
+// zero.
+constexpr uint32_t kSegLane = 16;
 __global__ __launch_bounds__(256) void k_seg_reduce(int32_t n, const uint32_t* __restrict__ tiles_touched,
                                                     const uint32_t* __restrict__ base,
                                                     const unsigned long long* __restrict__ total,
                                                     const float* __restrict__ rec, uint32_t rec_cap,
                                                     float* __restrict__ g2d) {
-  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (g >= n) return;  // wave-uniform
-  const uint32_t cnt = *total <= (unsigned long long)rec_cap ? tiles_touched[g] : 0u;
-  const uint32_t b = base[g];
+  const int64_t g0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;
+  if (g0 >= n) return;  // wave-uniform
+  const int64_t g = g0 + lane;
+  const bool fits = *total <= (unsigned long long)rec_cap;
+  const uint32_t cnt = (g < n && fits) ? tiles_touched[g] : 0u;
+  const uint32_t b = g < n ? base[g] : 0u;
   float acc[kG2d];
 #pragma unroll
   for (int c = 0; c < kG2d; ++c) acc[c] = 0.0f;
-  for (uint32_t j = lane; j < cnt; j += 64) {
+  if (cnt <= kSegLane) {
+    // four records in flight at a time, added in slot order (a missing one adds nothing)
+    for (uint32_t j = 0; j < cnt; j += 4) {
+      float2 v[4][kG2d / 2];
 #pragma unroll
-    for (int c = 0; c < kG2d; ++c) acc[c] += rec[((size_t)b + j) * kG2d + c];
+      for (int i = 0; i < 4; ++i) {
+        const float2* r = reinterpret_cast<const float2*>(rec + ((size_t)b + j + (uint32_t)i) * kG2d);
+#pragma unroll
+        for (int c = 0; c < kG2d / 2; ++c) v[i][c] = j + (uint32_t)i < cnt ? r[c] : make_float2(0.0f, 0.0f);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (j + (uint32_t)i < cnt) {
+#pragma unroll
+          for (int c = 0; c < kG2d / 2; ++c) {
+            acc[2 * c] += v[i][c].x;
+            acc[2 * c + 1] += v[i][c].y;
+          }
+        }
+      }
+    }
   }
+  uint64_t big = __ballot(cnt > kSegLane);
+  while (big) {
+    const int src = __builtin_ctzll(big);
+    big &= big - 1;
+    const uint32_t cb = __builtin_amdgcn_readlane(cnt, src), bb = __builtin_amdgcn_readlane(b, src);
+    float w[kG2d];
 #pragma unroll
-  for (int c = 0; c < kG2d; ++c) acc[c] = wave_sum_lane63(acc[c]);
-  if (lane == 63) {
+    for (int c = 0; c < kG2d; ++c) w[c] = 0.0f;
+    for (uint32_t j = lane; j < cb; j += 64) {
+#pragma unroll
+      for (int c = 0; c < kG2d; ++c) w[c] += rec[((size_t)bb + j) * kG2d + c];
+    }
+#pragma unroll
+    for (int c = 0; c < kG2d; ++c) {
+      const float t = wave_sum_lane63(w[c]);
+      const float tb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 63));
+      if (lane == src) acc[c] = tb;
+    }
+  }
+  if (g < n) {
 #pragma unroll
     for (int c = 0; c < kG2d; ++c) g2d[(size_t)c * n + g] = acc[c];
   }
@@ -1181,7 +1222,7 @@ gs_status rasterize_bwd(const char* name, int mode, int32_t n, int32_t sh_degree
   }
   if (mode != kBwdAtomic) {
     TimedScope ts("bwd_reduce", s);
-    hipLaunchKernelGGL(k_seg_reduce, dim3((unsigned)(((size_t)n + 3) / 4)), dim3(256), 0, s, n,
+    hipLaunchKernelGGL(k_seg_reduce, dim3((unsigned)(((size_t)n + 255) / 256)), dim3(256), 0, s, n,
                        proj->d_tiles_touched, base, total, rec, (uint32_t)pair_capacity, g2d);
   }
   {
