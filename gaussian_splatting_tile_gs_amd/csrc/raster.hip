@@ -184,6 +184,8 @@ __device__ __forceinline__ void blend_step(const SplatEval& e, bool act, float c
 // DEPTH: also the depth channel, D = sum z_i alpha_i T_i (background depth 0; the chunks' depth
 // contributions go to ckpt_d, one float per pixel and slot).
 // ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float l1_sign(float d) { return d > 0.0f ? 1.0f : (d < 0.0f ? -1.0f : 0.0f); }
+
 template <bool COUNT, bool CKPT, bool DEPTH>
 __global__ __launch_bounds__(kRasterThreads) void k_blend(
     uint32_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ plan, uint32_t ntiles,
@@ -191,7 +193,8 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
     const float* __restrict__ means2d, const float* __restrict__ conics, const float* __restrict__ opac,
     const float* __restrict__ colors, const float* __restrict__ depths, const int32_t* __restrict__ radii,
     DevCamera cam, float* __restrict__ image, float* __restrict__ depth_out, float* __restrict__ final_T,
-    uint32_t* __restrict__ n_contrib, unsigned long long* __restrict__ eval_count) {
+    uint32_t* __restrict__ n_contrib, unsigned long long* __restrict__ eval_count,
+    const float* __restrict__ l1_target, float* __restrict__ l1_grad, float l1_scale) {
   __shared__ float4 s_a[kBatch];
   __shared__ float4 s_b[kBatch];
   __shared__ float s_c[kBatch];
@@ -282,9 +285,15 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
   }
   if (inside) {
     const int p = py_i * cam.W + px_i;
-    image[3 * p + 0] = fmaf(T, cam.bg[0], cr);
-    image[3 * p + 1] = fmaf(T, cam.bg[1], cg);
-    image[3 * p + 2] = fmaf(T, cam.bg[2], cb);
+    const float ir = fmaf(T, cam.bg[0], cr), ig = fmaf(T, cam.bg[1], cg), ib = fmaf(T, cam.bg[2], cb);
+    image[3 * p + 0] = ir;
+    image[3 * p + 1] = ig;
+    image[3 * p + 2] = ib;
+    if (l1_target) {  // uniform: the L1 gradient sign(image - target) / (3 h w), as gs_loss_l1 forms it
+      l1_grad[3 * p + 0] = l1_sign(ir - l1_target[3 * p + 0]) * l1_scale;
+      l1_grad[3 * p + 1] = l1_sign(ig - l1_target[3 * p + 1]) * l1_scale;
+      l1_grad[3 * p + 2] = l1_sign(ib - l1_target[3 * p + 2]) * l1_scale;
+    }
     final_T[p] = T;
     n_contrib[p] = last;
     if (DEPTH) depth_out[p] = cd;  // background depth 0
@@ -1084,19 +1093,21 @@ extern "C" size_t gs_raster_workspace_bytes(void) {
   return (size_t)kPlanMaxSlots * kRasterThreads * (sizeof(float4) + sizeof(float));
 }
 
-extern "C" gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const gs_camera* cam,
-                                      const uint32_t* d_ids, const uint32_t* d_tile_ranges,
-                                      const uint32_t* d_raster_plan, void* d_raster_ws, float* d_image,
-                                      float* d_depth, float* d_final_T, uint32_t* d_n_contrib,
-                                      uint64_t* d_eval_count, void* stream) {
+namespace {
+gs_status rasterize_fwd(const char* name, int32_t n, const gs_projected* proj, const gs_camera* cam,
+                        const uint32_t* d_ids, const uint32_t* d_tile_ranges, const uint32_t* d_raster_plan,
+                        void* d_raster_ws, float* d_image, float* d_depth, float* d_final_T, uint32_t* d_n_contrib,
+                        const float* d_target, float* d_dL_dimage, uint64_t* d_eval_count, void* stream) {
   std::string why;
-  if (n < 0) return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: n < 0");
-  if (!valid_camera(cam, &why)) return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: " + why);
+  const std::string nm = name;
+  if (n < 0) return set_error(GS_ERR_INVALID_ARG, nm + ": n < 0");
+  if (!valid_camera(cam, &why)) return set_error(GS_ERR_INVALID_ARG, nm + ": " + why);
   if (!d_tile_ranges || !d_image || !d_final_T || !d_n_contrib)
-    return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: NULL output or ranges");
-  if (n > 0 && (!proj_ok(proj) || !d_ids)) return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_fwd: NULL input");
+    return set_error(GS_ERR_INVALID_ARG, nm + ": NULL output or ranges");
+  if (n > 0 && (!proj_ok(proj) || !d_ids)) return set_error(GS_ERR_INVALID_ARG, nm + ": NULL input");
   const int64_t ntiles = (int64_t)((cam->width + 15) / 16) * ((cam->height + 15) / 16);
-  if (ntiles > ((int64_t)1 << 24)) return set_error(GS_ERR_LIMIT, "gs_rasterize_fwd: more than 2^24 tiles");
+  if (ntiles > ((int64_t)1 << 24)) return set_error(GS_ERR_LIMIT, nm + ": more than 2^24 tiles");
+  const float l1_scale = 1.0f / (float)((size_t)cam->width * cam->height * 3);
   const DevCamera dc = to_dev(*cam);
   hipStream_t s = (hipStream_t)stream;
   {
@@ -1119,9 +1130,30 @@ extern "C" gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const
                        n > 0 ? proj->d_conics : nullptr, n > 0 ? proj->d_opacities : nullptr,
                        n > 0 ? proj->d_colors : nullptr, n > 0 ? proj->d_depths : nullptr,
                        n > 0 ? proj->d_radii : nullptr, dc, d_image, d_depth, d_final_T, d_n_contrib,
-                       (unsigned long long*)d_eval_count);
+                       (unsigned long long*)d_eval_count, d_target, d_dL_dimage, l1_scale);
   }
-  return check_launch("gs_rasterize_fwd");
+  return check_launch(name);
+}
+}  // namespace
+
+extern "C" gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const gs_camera* cam,
+                                      const uint32_t* d_ids, const uint32_t* d_tile_ranges,
+                                      const uint32_t* d_raster_plan, void* d_raster_ws, float* d_image,
+                                      float* d_depth, float* d_final_T, uint32_t* d_n_contrib,
+                                      uint64_t* d_eval_count, void* stream) {
+  return rasterize_fwd("gs_rasterize_fwd", n, proj, cam, d_ids, d_tile_ranges, d_raster_plan, d_raster_ws, d_image,
+                       d_depth, d_final_T, d_n_contrib, nullptr, nullptr, d_eval_count, stream);
+}
+
+extern "C" gs_status gs_rasterize_fwd_l1(int32_t n, const gs_projected* proj, const gs_camera* cam,
+                                         const uint32_t* d_ids, const uint32_t* d_tile_ranges,
+                                         const uint32_t* d_raster_plan, void* d_raster_ws, float* d_image,
+                                         float* d_depth, float* d_final_T, uint32_t* d_n_contrib,
+                                         const float* d_target, float* d_dL_dimage, uint64_t* d_eval_count,
+                                         void* stream) {
+  if (!d_target || !d_dL_dimage) return set_error(GS_ERR_INVALID_ARG, "gs_rasterize_fwd_l1: NULL target or gradient");
+  return rasterize_fwd("gs_rasterize_fwd_l1", n, proj, cam, d_ids, d_tile_ranges, d_raster_plan, d_raster_ws,
+                       d_image, d_depth, d_final_T, d_n_contrib, d_target, d_dL_dimage, d_eval_count, stream);
 }
 
 namespace {

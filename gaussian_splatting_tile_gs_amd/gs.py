@@ -71,6 +71,7 @@ def load():
         "gs_raster_workspace_bytes": (sz, []),
         "gs_bin_and_sort": (i32, [i32, proj_p, cam_p, P, sz, i64, P, P, P, P, P, ctypes.POINTER(ctypes.c_int64), P]),
         "gs_rasterize_fwd": (i32, [i32, proj_p, cam_p, P, P, P, P, P, P, P, P, P, P]),
+        "gs_rasterize_fwd_l1": (i32, [i32, proj_p, cam_p, P, P, P, P, P, P, P, P, P, P, P, P]),
         "gs_bwd_workspace_bytes": (sz, [i32]),
         "gs_bwd_det_workspace_bytes": (sz, [i32, i64]),
         "gs_rasterize_bwd_deterministic": (i32, [i32, i32, P, P, P, P, P, cam_p, proj_p, P, P, P, P, P, P, P, P,
@@ -180,6 +181,15 @@ def gs_rasterize_fwd(n, proj: "Projected", cam: GsCamera, ids, tile_ranges, imag
     return _check(load().gs_rasterize_fwd(n, ctypes.byref(proj.struct()), ctypes.byref(cam), _ptr(ids),
                                           _ptr(tile_ranges), _ptr(plan), _ptr(raster_ws), _ptr(image), _ptr(depth),
                                           _ptr(final_T), _ptr(n_contrib), _ptr(eval_count), _stream(stream)))
+
+
+def gs_rasterize_fwd_l1(n, proj: "Projected", cam: GsCamera, ids, tile_ranges, image, final_T, n_contrib, target,
+                        dL_dimage, eval_count=None, stream=None, plan=None, raster_ws=None, depth=None):
+    """gs_rasterize_fwd with the L1 gradient sign(image - target) / (3 h w) written into dL_dimage."""
+    return _check(load().gs_rasterize_fwd_l1(n, ctypes.byref(proj.struct()), ctypes.byref(cam), _ptr(ids),
+                                             _ptr(tile_ranges), _ptr(plan), _ptr(raster_ws), _ptr(image),
+                                             _ptr(depth), _ptr(final_T), _ptr(n_contrib), _ptr(target),
+                                             _ptr(dL_dimage), _ptr(eval_count), _stream(stream)))
 
 
 def gs_bwd_workspace_bytes(n) -> int:
@@ -363,14 +373,21 @@ class Pipeline:
         if cap > self.capacity:
             self._alloc_pairs(int(cap))
 
-    def forward(self, cam: GsCamera, eval_count=None, stream=None, checkpoints=None, depth=None):
+    def forward(self, cam: GsCamera, eval_count=None, stream=None, checkpoints=None, depth=None, l1_target=None):
         """Blend. checkpoints (default: the "chunks" schedule) stores the per-chunk state that lets
-        the backward split long tiles; a render that no backward follows can leave it out."""
+        the backward split long tiles; a render that no backward follows can leave it out.
+        l1_target: also write the L1 gradient against it into self.dL_dimage (gs_rasterize_fwd_l1)."""
         ck = self.schedule == "chunks" if checkpoints is None else bool(checkpoints)
         self._ckpt_written = ck
-        gs_rasterize_fwd(self.n, self.proj, cam, self.ids, self.ranges, self.image, self.final_T, self.n_contrib,
-                         eval_count, stream, plan=self.plan if self.schedule != "tiles" else None,
-                         raster_ws=self.raster_ws if ck else None, depth=depth)
+        plan = self.plan if self.schedule != "tiles" else None
+        ws = self.raster_ws if ck else None
+        if l1_target is not None:
+            gs_rasterize_fwd_l1(self.n, self.proj, cam, self.ids, self.ranges, self.image, self.final_T,
+                                self.n_contrib, l1_target, self.dL_dimage, eval_count, stream, plan=plan,
+                                raster_ws=ws, depth=depth)
+        else:
+            gs_rasterize_fwd(self.n, self.proj, cam, self.ids, self.ranges, self.image, self.final_T, self.n_contrib,
+                             eval_count, stream, plan=plan, raster_ws=ws, depth=depth)
 
     def loss_l1(self, target, loss=None, stream=None):
         """The training loss's gradient into self.dL_dimage: L1, or with self.ssim_lambda > 0
@@ -405,12 +422,16 @@ class Pipeline:
                          pair_capacity=self.capacity if det else None, dL_ddepth=dL_ddepth)
 
     def iteration(self, cam: GsCamera, target, stream=None, wait=True):
-        """One fwd+bwd iteration: project, bin+sort, blend, L1 gradient, backward. wait=False runs
+        """One fwd+bwd iteration: project, bin+sort, blend, loss gradient (L1 inside the blend, or the
+        separate L1 + SSIM kernels), backward. wait=False runs
         it without any host wait (the pair buffers must already be large enough)."""
         self.project(cam, stream)
         self.bin(cam, stream, wait=wait)
-        self.forward(cam, stream=stream)
-        self.loss_l1(target, stream=stream)
+        if getattr(self, "ssim_lambda", 0.0) > 0.0:
+            self.forward(cam, stream=stream)
+            self.loss_l1(target, stream=stream)
+        else:  # the L1 gradient formed in the blend
+            self.forward(cam, stream=stream, l1_target=target)
         self.backward(cam, stream=stream)
 
     def adam_step(self, cfg: GsAdamConfig, stream=None):

@@ -182,6 +182,21 @@ gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const gs_camera*
                            uint64_t* d_eval_count, void* stream);
 
 /*
+ * gs_rasterize_fwd_l1 -- gs_rasterize_fwd with the L1 term of the training loss (section 7 of
+ * the PyTorch lesson) fused into the blend: as each pixel's colour is finished, its gradient
+ * dL/dimage = sign(image - target) / (3 h w) (sign(0) = 0) is written beside it, bit for bit what
+ * gs_loss_l1 writes from the same image, without reading the image back.
+ * Inputs and outputs: those of gs_rasterize_fwd, plus d_target [h,w,3] (device) and
+ * d_dL_dimage [h,w,3] (device, written for every pixel). The loss value itself is not formed
+ * (gs_loss_l1 gives it). Errors: those of gs_rasterize_fwd; GS_ERR_INVALID_ARG for a NULL
+ * d_target or d_dL_dimage.
+ */
+gs_status gs_rasterize_fwd_l1(int32_t n, const gs_projected* proj, const gs_camera* cam, const uint32_t* d_ids,
+                              const uint32_t* d_tile_ranges, const uint32_t* d_raster_plan, void* d_raster_ws,
+                              float* d_image, float* d_depth, float* d_final_T, uint32_t* d_n_contrib,
+                              const float* d_target, float* d_dL_dimage, uint64_t* d_eval_count, void* stream);
+
+/*
  * gs_rasterize_bwd -- gradients of a loss L with respect to the raw parameters, given
  * dL/dimage (section 6 of the PyTorch lesson). Each tile is walked back to front from each
  * pixel's last contributor; T_i = T_{i+1} / (1 - alpha_i) is recovered by division (the 0.99

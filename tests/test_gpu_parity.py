@@ -566,3 +566,44 @@ def test_concurrent_streams_match_sequential(env):
             assert torch.equal(pipes[k].image, img), f"camera {first + k}: image differs"
             for name, v in grads.items():
                 assert torch.equal(pipes[k].grads[name], v), f"camera {first + k}: {name} differs"
+
+
+@pytest.mark.parametrize("case", ["distill_30k", "ragged"])
+def test_fused_l1_forward(env, case):
+    """gs_rasterize_fwd_l1: the image, final T and counts are those of gs_rasterize_fwd, and the
+    gradient it writes is gs_loss_l1's on that image, bit for bit; the L1 value it implies
+    matches the oracle loss on the same image."""
+    from oracle import loss as oloss
+    gs, torch = env
+    if case == "ragged":
+        scene = synth.random_scene(300, seed=51, width=37, height=23, focal=30.0)
+        cam_d = synth.make_camera(np.eye(4), 37, 23, 30.0, background=(0.2, 0.4, 0.6))
+    else:
+        wl = synth.WORKLOADS[case]
+        scene, cam_d = synth.make_scene(wl), synth.make_cameras(wl)[3]
+    W, H = cam_d["width"], cam_d["height"]
+    cam = gs.make_camera(cam_d)
+    params = gs.scene_to_device(scene)
+    pipe = gs.Pipeline(params, W, H, pair_capacity=1 << 10)
+    pipe.project(cam)
+    pipe.bin(cam)
+    rng = np.random.default_rng(52)
+    target = torch.from_numpy(rng.uniform(0, 1, (H, W, 3)).astype(np.float32)).cuda()
+    pipe.forward(cam)
+    ref_img, ref_T, ref_nc = pipe.image.clone(), pipe.final_T.clone(), pipe.n_contrib.clone()
+    ref_grad = torch.empty_like(ref_img)
+    gs.gs_loss_l1(W, H, ref_img, target, ref_grad)
+    pipe.dL_dimage.fill_(float("nan"))
+    pipe.image.zero_()
+    pipe.forward(cam, l1_target=target)
+    torch.cuda.synchronize()
+    assert torch.equal(pipe.image, ref_img) and torch.equal(pipe.final_T, ref_T)
+    assert torch.equal(pipe.n_contrib, ref_nc)
+    assert torch.equal(pipe.dL_dimage, ref_grad), "fused L1 gradient differs from gs_loss_l1"
+    _, g_ref = oloss.loss_l1_ssim(ref_img.cpu().numpy().astype(np.float64), target.cpu().numpy().astype(np.float64),
+                                  0.0)
+    assert np.array_equal(pipe.dL_dimage.cpu().numpy().astype(np.float64), g_ref.astype(np.float32))
+    # a NULL target is an argument error
+    with pytest.raises(gs.GsError):
+        gs.gs_rasterize_fwd_l1(pipe.n, pipe.proj, cam, pipe.ids, pipe.ranges, pipe.image, pipe.final_T,
+                               pipe.n_contrib, None, pipe.dL_dimage)
