@@ -278,11 +278,13 @@ struct TileCountArgs {
 constexpr int kRowGaussians = 2048;  // Gaussians per row workgroup (two per lane)
 
 // Row workgroup rb: Gaussians [2048 rb, 2048 (rb + 1)) of the id order, two per lane. A lane
-// walks the rows of its own Gaussian when there are at most kOwnRows of them; the taller ones
+// walks the rows of its own Gaussian when there are at most kOwnRows (tight rows: kOwnRowsTight)
+// of them; the taller ones
 // are walked by the whole wave, one Gaussian at a time (its rectangle read with readlane), so a
 // screen-filling splat does not hold up its wave. The difference array is staged in LDS (`lds`,
 // `lds_words` long) when it fits.
 constexpr uint32_t kOwnRows = 8;
+constexpr uint32_t kOwnRowsTight = 32;  // tight rows cost more each, the wave walk wastes more lanes
 __device__ __forceinline__ TightShape tight_of(const TileCountArgs& a, uint32_t g) {
   const float2 m = *reinterpret_cast<const float2*>(a.means2d + 2 * (size_t)g);
   const float* c = a.conics + 3 * (size_t)g;
@@ -306,7 +308,8 @@ __device__ void tile_rows(const TileCountArgs& a, uint32_t rb, uint32_t* lds, ui
     // tall one takes it from the owning lane
     TightShape own{};
     if (a.tight && h > 0) own = tight_of(a, (uint32_t)j);
-    if (h <= kOwnRows) {
+    const uint32_t own_max = a.tight ? kOwnRowsTight : kOwnRows;
+    if (h <= own_max) {
       if (a.tight && h > 0) {
         const TightShape& ts = own;
         const int x0 = (int)(r.y % tx), y0 = (int)(r.y / tx);
@@ -324,7 +327,7 @@ __device__ void tile_rows(const TileCountArgs& a, uint32_t rb, uint32_t* lds, ui
         }
       }
     }
-    uint64_t tall = __ballot(h > kOwnRows);
+    uint64_t tall = __ballot(h > own_max);
     while (tall) {
       const int src = __builtin_ctzll(tall);
       tall &= tall - 1;

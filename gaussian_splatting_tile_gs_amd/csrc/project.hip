@@ -27,13 +27,46 @@ __global__ __launch_bounds__(kProjectThreads) void k_project(
     uint32_t* __restrict__ tiles_touched) {
   constexpr int K = (DEG + 1) * (DEG + 1);
   const int g = blockIdx.x * kProjectThreads + threadIdx.x;
-  if (g >= n) return;
+  const int lane = threadIdx.x & 63;
+  if (blockIdx.x * kProjectThreads + (threadIdx.x & ~63) >= n) return;  // whole waves past n only
+  const bool valid = g < n;
+  const int gg = valid ? g : n - 1;  // lanes past n compute a copy of the last Gaussian, store nothing
   float shc[K * 3];
 #pragma unroll
-  for (int i = 0; i < K * 3; ++i) shc[i] = sh[(size_t)g * (K * 3) + i];
-  const ProjF32 P = project_f32<DEG, true>(means[3 * g], means[3 * g + 1], means[3 * g + 2], log_scales[3 * g],
-                                            log_scales[3 * g + 1], log_scales[3 * g + 2],
-                                            *reinterpret_cast<const float4*>(quats + 4 * g), logits[g], shc, cam);
+  for (int i = 0; i < K * 3; ++i) shc[i] = sh[(size_t)gg * (K * 3) + i];
+  ProjF32 P = project_f32<DEG, true>(means[3 * gg], means[3 * gg + 1], means[3 * gg + 2], log_scales[3 * gg],
+                                      log_scales[3 * gg + 1], log_scales[3 * gg + 2],
+                                      *reinterpret_cast<const float4*>(quats + 4 * gg), logits[gg], shc, cam);
+  if (cam.tight_tiles) {
+    // tight counts of tall rectangles: the wave takes them one at a time, one lane per row, and
+    // adds the rows' tiles (integers: the order does not matter)
+    uint64_t pend = __ballot(valid && P.drawn && P.tiles == kTightPending);
+    while (pend) {
+      const int src = __builtin_ctzll(pend);
+      pend &= pend - 1;
+      auto bf = [&](float v) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src)); };
+      const float mx = bf(P.m2d[0]), my = bf(P.m2d[1]);
+      const float rx = (float)__builtin_amdgcn_readlane(P.rad[0], src);
+      const float ry = (float)__builtin_amdgcn_readlane(P.rad[1], src);
+      const TileRect rc = tile_rect(mx, my, rx, ry, cam.tiles_x, cam.tiles_y);
+      const TightShape ts = tight_shape(mx, my, bf(P.con[0]), bf(P.con[1]), bf(P.con[2]), bf(P.o));
+      uint32_t cnt = 0;
+      for (int ty = rc.y0 + lane; ty < rc.y1; ty += 64) {
+        const int2 sp = tight_row(ts, ty, rc.x0, rc.x1);
+        cnt += (uint32_t)(sp.y - sp.x);
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) cnt += (uint32_t)__shfl_xor((int)cnt, off, 64);
+      if (lane == src) {
+        P.tiles = cnt;
+        if (cnt == 0) {  // the ellipse reaches no pixel centre: not drawn
+          P.drawn = false;
+          P.rad[0] = P.rad[1] = 0;
+        }
+      }
+    }
+  }
+  if (!valid) return;
   means2d[2 * g] = P.m2d[0];
   means2d[2 * g + 1] = P.m2d[1];
   conics[3 * g] = P.con[0];

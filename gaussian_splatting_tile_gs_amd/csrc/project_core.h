@@ -56,6 +56,11 @@ struct ProjF32 {
 };
 
 // shc: the Gaussian's (DEG+1)^2 x 3 SH coefficients (only read when WITH_COLOR)
+// Tight counts of rectangles taller than this many rows are left to the projection kernel's
+// wave (one lane per row) so that one tall splat does not hold up the lanes of its wave.
+constexpr uint32_t kTightLaneRows = 16;
+constexpr uint32_t kTightPending = 0xFFFFFFFFu;
+
 template <int DEG, bool WITH_COLOR>
 __device__ __forceinline__ ProjF32 project_f32(float m0, float m1, float m2, float l0, float l1, float l2, float4 q4,
                                                float logit, const float* shc, const DevCamera& cam) {
@@ -206,13 +211,17 @@ __device__ __forceinline__ ProjF32 project_f32(float m0, float m1, float m2, flo
   if (!(rc.x1 > rc.x0 && rc.y1 > rc.y0)) return P;
   uint32_t tiles = (uint32_t)((rc.x1 - rc.x0) * (rc.y1 - rc.y0));
   if (cam.tight_tiles) {  // only the tiles of the rectangle the ellipse reaches
-    const TightShape ts = tight_shape(mx, my, con0, con1, con2, o_eff);
-    tiles = 0;
-    for (int ty = rc.y0; ty < rc.y1; ++ty) {
-      const int2 sp = tight_row(ts, ty, rc.x0, rc.x1);
-      tiles += (uint32_t)(sp.y - sp.x);
+    if (WITH_COLOR && rc.y1 - rc.y0 > (int)kTightLaneRows) {
+      tiles = kTightPending;  // counted by the whole wave (k_project), which also undraws a 0
+    } else {
+      const TightShape ts = tight_shape(mx, my, con0, con1, con2, o_eff);
+      tiles = 0;
+      for (int ty = rc.y0; ty < rc.y1; ++ty) {
+        const int2 sp = tight_row(ts, ty, rc.x0, rc.x1);
+        tiles += (uint32_t)(sp.y - sp.x);
+      }
+      if (tiles == 0) return P;
     }
-    if (tiles == 0) return P;
   }
   P.rad[0] = (int32_t)rx;
   P.rad[1] = (int32_t)ry;
