@@ -263,7 +263,7 @@ def test_depth_channel(env, case, bwd):
     ("needles", {"tight_tiles": True}, "det"), ("needles", {"tight_tiles": True, "radius_mode": "3dgs"}, "atomic"),
     ("giant", {"tight_tiles": True}, "det"), ("distill_30k", {"tight_tiles": True}, "det"),
     ("mid_150k_sh3", {"tight_tiles": True, "antialiased": True}, "atomic"),
-    ("dim_corners", {"tight_tiles": True}, "det")])
+    ("dim_corners", {"tight_tiles": True}, "det"), ("stress_400k_sh3", {"tight_tiles": True}, "det")])
 def test_variants(env, case, opts, bwd):
     if case == "tiny":
         wl = synth.WORKLOADS["tiny_1k"]
