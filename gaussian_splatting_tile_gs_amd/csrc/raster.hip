@@ -606,6 +606,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
     }
     __syncthreads();
     for (int w = 3; w >= 0; --w) {
+      if (w * 64 >= cnt) continue;  // workgroup-uniform: no splat staged in this group
       // DET: this wave's sums of group w's 64 splats, zeroed first (row `lane` per lane)
       float* part = s_acc + (size_t)wave * 64 * NT;
       if (DET) {
