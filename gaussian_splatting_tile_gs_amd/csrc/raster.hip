@@ -1227,10 +1227,10 @@ gs_status rasterize_bwd(const char* name, int mode, int32_t n, int32_t sh_degree
     hipLaunchKernelGGL(k_base_sums, dim3(nb), dim3(kBaseThreads), 0, s, n, proj->d_tiles_touched, bsum);
     hipLaunchKernelGGL(k_base_scan, dim3(nb), dim3(kBaseThreads), 0, s, n, proj->d_tiles_touched, bsum, base, total);
     // every record starts at zero: the pairs no pixel reaches are never staged. Each thread
-    // clears about 16 float4s (at most 4096 workgroups): small frames leave most of the GPU to
+    // clears about 4 float4s (at most 4096 workgroups): small frames leave most of the GPU to
     // concurrent iterations, large ones still fill it
     const size_t count4 = ((size_t)pair_capacity * kG2d + 3) / 4;
-    const size_t want = (count4 + 4095) / 4096;
+    const size_t want = (count4 + 1023) / 1024;
     const unsigned blocks = (unsigned)(want < 1 ? 1 : (want > 4096 ? 4096 : want));
     if (count4)
       hipLaunchKernelGGL(k_clear_records, dim3(blocks), dim3(256), 0, s, (float4*)rec, total, (uint32_t)pair_capacity);
