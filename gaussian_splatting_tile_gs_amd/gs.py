@@ -421,6 +421,59 @@ class Pipeline:
                          raster_ws=self.raster_ws if getattr(self, "_ckpt_written", False) else None,
                          pair_capacity=self.capacity if det else None, dL_ddepth=dL_ddepth)
 
+    # ---- feature channels: any per-Gaussian quantity blended with the colour's weights ----------
+    def _feature_args(self, cam: GsCamera, features):
+        """The camera with background 0 and the features laid out as three channels ([n, 3], the
+        unused ones 0): the blend and its backward treat them as colours."""
+        if features.dim() != 2 or features.shape[0] != self.n or not 1 <= features.shape[1] <= 3:
+            raise ValueError("features must be [n, C] with 1 <= C <= 3 (render more in groups of three)")
+        fcam = GsCamera()
+        ctypes.memmove(ctypes.byref(fcam), ctypes.byref(cam), ctypes.sizeof(GsCamera))
+        for i in range(3):
+            fcam.background[i] = 0.0
+        f3 = torch.zeros(self.n, 3, device=self.device, dtype=torch.float32)
+        f3[:, : features.shape[1]] = features
+        pr = self.proj
+        proj = Projected(pr.means2d, pr.conics, pr.depths, pr.opacities, f3, pr.radii, pr.tiles_touched)
+        return fcam, f3, proj
+
+    def render_features(self, cam: GsCamera, features, stream=None):
+        """F = sum_i f_i alpha_i T_i per pixel (background 0) for features [n, C], C <= 3, with this
+        iteration's projection and pair lists (section 5 of the PyTorch lesson: any channel goes
+        through the blend's weights). Returns [h, w, C]."""
+        fcam, _, proj = self._feature_args(cam, features)
+        img = torch.empty(self.height, self.width, 3, device=self.device, dtype=torch.float32)
+        ft = torch.empty_like(self.final_T)
+        nc = torch.empty_like(self.n_contrib)
+        gs_rasterize_fwd(self.n, proj, fcam, self.ids, self.ranges, img, ft, nc, None, stream)
+        return img[..., : features.shape[1]]
+
+    def features_backward(self, cam: GsCamera, features, dL_dF, stream=None):
+        """Gradients of a loss on render_features' output: dL/dfeatures [n, C] and the
+        geometry's share (means, log_scales, quats, opacity_logits), from the forward's final T
+        and counts. The colour loss's gradients come from backward(); the two add."""
+        fcam, f3, proj = self._feature_args(cam, features)
+        C = features.shape[1]
+        g3 = torch.zeros(self.height, self.width, 3, device=self.device, dtype=torch.float32)
+        g3[..., :C] = dL_dF
+        f = dict(device=self.device, dtype=torch.float32)
+        out = {"means": torch.empty(self.n, 3, **f), "log_scales": torch.empty(self.n, 3, **f),
+               "quats": torch.empty(self.n, 4, **f), "opacity_logits": torch.empty(self.n, **f),
+               "features": torch.empty(self.n, 1, 3, **f)}
+        det = getattr(self, "deterministic", False)
+        if det:
+            need = gs_bwd_det_workspace_bytes(self.n, self.capacity)
+            if getattr(self, "_det_ws", None) is None or self._det_ws.numel() < need:
+                self._det_ws = torch.empty(need, device=self.device, dtype=torch.uint8)
+        p = self.p
+        gs_rasterize_bwd(self.n, 0, p["means"], p["log_scales"], p["quats"], p["opacity_logits"], f3.view(self.n, 1, 3),
+                         fcam, proj, self.ids, self.ranges, self.final_T, self.n_contrib, g3,
+                         self._det_ws if det else self.bwd_ws, out["means"], out["log_scales"], out["quats"],
+                         out["opacity_logits"], out["features"], None, None, stream,
+                         pair_capacity=self.capacity if det else None)
+        out["features"] = out["features"].view(self.n, 3)[:, :C]
+        return out
+
     def iteration(self, cam: GsCamera, target, stream=None, wait=True):
         """One fwd+bwd iteration: project, bin+sort, blend, loss gradient (L1 inside the blend, or the
         separate L1 + SSIM kernels), backward. wait=False runs

@@ -174,6 +174,9 @@ gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const gs_camera* 
  *   splat (0 if none). d_eval_count: NULL, or a device uint64 to which the number of
  *   (pixel, entry) evaluations is added (a work counter for measurement).
  * Deterministic: no atomics on the outputs; each pixel is written once.
+ * Any per-Gaussian three-channel quantity blends with the same weights (section 5: any channel
+ * goes through the blend): pass it as proj->d_colors with a camera background of 0; given to
+ * gs_rasterize_bwd as degree-0 coefficients (basis 1) it comes back as their gradient.
  */
 size_t gs_raster_workspace_bytes(void);
 gs_status gs_rasterize_fwd(int32_t n, const gs_projected* proj, const gs_camera* cam, const uint32_t* d_ids,

@@ -607,3 +607,54 @@ def test_fused_l1_forward(env, case):
     with pytest.raises(gs.GsError):
         gs.gs_rasterize_fwd_l1(pipe.n, pipe.proj, cam, pipe.ids, pipe.ranges, pipe.image, pipe.final_T,
                                pipe.n_contrib, None, pipe.dL_dimage)
+
+
+@pytest.mark.parametrize("case,C,det", [("ragged", 2, False), ("tiny", 3, True), ("tiny", 1, False)])
+def test_feature_channels(env, case, C, det):
+    """Per-Gaussian features [n, C] blended with the colour's weights (background 0) and their
+    backward, against the oracle run on the same geometry with the features as degree-0 colours:
+    the rendered channels (1e-4 off the fragile pixels), dL/dfeatures and the geometry's share of
+    the gradients (the stated gradient tolerance)."""
+    gs, torch = env
+    if case == "ragged":
+        scene = synth.random_scene(300, seed=61, width=37, height=23, focal=30.0, sh_degree=3, logit_std=2.0)
+        cam_d = synth.make_camera(np.eye(4), 37, 23, 30.0, background=(0.2, 0.4, 0.6))
+    else:
+        wl = synth.WORKLOADS["tiny_1k"]
+        scene, cam_d = synth.make_scene(wl), synth.make_cameras(wl)[0]
+    W, H = cam_d["width"], cam_d["height"]
+    n = scene["means"].shape[0]
+    rng = np.random.default_rng(62)
+    feats = rng.normal(0, 1, (n, C)).astype(np.float32)
+    cam = gs.make_camera(cam_d)
+    params = gs.scene_to_device(scene)
+    pipe = gs.Pipeline(params, W, H, pair_capacity=1 << 12)
+    pipe.deterministic = det
+    pipe.project(cam)
+    pipe.bin(cam)
+    pipe.forward(cam)
+    fd = torch.from_numpy(feats).cuda()
+    F = pipe.render_features(cam, fd).cpu().numpy()
+    # the oracle: the same Gaussians with the features as view-independent colours, background 0
+    f3 = np.zeros((n, 1, 3), np.float32)
+    f3[:, 0, :C] = feats
+    scene_f = dict(scene, sh=f3, sh_degree=0)
+    cam_f = dict(cam_d, background=(0.0, 0.0, 0.0))
+    o_proj = oracle.project(scene_f, cam_f, np.float32)
+    o_fwd = oracle.render(o_proj, cam_f)
+    ok = ~o_fwd["fragile"]
+    d = np.abs(F.astype(np.float64) - o_fwd["image"][..., :C])
+    assert d[ok].max() <= 1e-4, f"feature channels differ by {d[ok].max():.3e}"
+    gF = rng.normal(0, 1, (H, W, C)).astype(np.float32)
+    gF[~ok] = 0.0  # no gradient where a decision sits on its threshold
+    out = pipe.features_backward(cam, fd, torch.from_numpy(gF).cuda())
+    torch.cuda.synchronize()
+    g3 = np.zeros((H, W, 3))
+    g3[..., :C] = gF
+    g2d, aref2d = oracle.render_backward(o_proj, cam_f, g3)
+    raw = oracle.project_backward(scene_f, cam_f, g2d, aref2d)
+    gsh = np.zeros((n, 1, 3), np.float32)
+    gsh[:, 0, :C] = out["features"].cpu().numpy()
+    gpu = {k: out[k].cpu().numpy() for k in ("means", "log_scales", "quats", "opacity_logits")}
+    gpu["sh"] = gsh
+    compare_grads(gpu, raw, 0, f"features {case} C={C}")
