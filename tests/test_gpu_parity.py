@@ -239,8 +239,10 @@ def test_deterministic_backward_capacity_and_arguments(env):
 
 # ---- depth channel --------------------------------------------------------------------------------
 @pytest.mark.parametrize("case,bwd", [("tiny", "atomic"), ("ragged", "det"), ("distill_30k", "atomic"),
-                                      ("mid_150k_sh3", "det"), ("tiny", "det_tiles")])
+                                      ("mid_150k_sh3", "det"), ("tiny", "det_tiles"), ("distill_30k+tight", "det"),
+                                      ("ragged+tight", "atomic")])
 def test_depth_channel(env, case, bwd):
+    case, _, opt = case.partition("+")
     if case == "tiny":
         wl = synth.WORKLOADS["tiny_1k"]
         scene, cam, pix = synth.make_scene(wl), synth.make_cameras(wl)[0], None
@@ -251,7 +253,9 @@ def test_depth_channel(env, case, bwd):
         wl = synth.WORKLOADS[case]
         scene, cam = synth.make_scene(wl), synth.make_cameras(wl)[0]
         pix = synth.sample_pixels(cam["width"], cam["height"], 4096, seed=1)
-    _pipeline_case(env, scene, cam, pixels=pix, label=f"{case} depth", bwd=bwd, depth=True)
+    if opt == "tight":
+        cam = dict(cam, tight_tiles=True)
+    _pipeline_case(env, scene, cam, pixels=pix, label=f"{case} {opt} depth", bwd=bwd, depth=True)
 
 
 # ---- tile-count variants (camera options) ---------------------------------------------------------
