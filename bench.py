@@ -75,7 +75,7 @@ def parse():
 
 
 def kernel_bytes(name, stats):
-    """Algorithmic HBM bytes of one launch of a binning kernel (see DESIGN.md)."""
+    """Algorithmic HBM bytes of one launch of a binning kernel."""
     P, N = stats["pairs"], stats["n"]
     return {
         "bin_prep": 48.0 * N,
@@ -190,7 +190,7 @@ def log(msg):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU: bench.py --gpus N with N > 1 is not supported"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU: bench.py --gpus N with N > 1 is not supported"}))
         sys.exit(2)
     import torch
 

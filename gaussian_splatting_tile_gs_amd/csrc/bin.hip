@@ -869,7 +869,7 @@ __global__ __launch_bounds__(kEmitThreads) void k_scan(int32_t n, const uint32_t
       const uint64_t notready = __ballot(fl == 0), pre = __ballot(fl == kFlagPre64);
       const int first_nr = notready ? __builtin_ctzll(notready) : 64;
       const int first_pre = pre ? __builtin_ctzll(pre) : 64;
-      const int take = first_pre < first_nr ? first_pre + 1 : first_nr;  // words consumed this round
+      const int take = first_pre < first_nr ? first_pre + 1 : first_nr;  // words consumed by this pass
       uint64_t v = lane < take ? (st & kValMask64) : 0ull;
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);

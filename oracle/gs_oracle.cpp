@@ -28,7 +28,7 @@
 // gradients) are accumulated in double from those fp32 decisions. T = double is used for the
 // closed-form pins and the finite-difference gradient checks.
 //
-// Readings where the pages leave a step open (each also listed in the design doc):
+// Readings where the pages leave a step open:
 //   - radius rule: gsplat's per-axis extent with the opacity-aware k = min(3.33, sqrt(2 ln(255 o)))
 //     (section 4 of the PyTorch lesson); Gaussians with o < 1/255 are culled;
 //   - tile rectangle [floor((mu - r)/16), ceil((mu + r)/16)) clamped to the grid;
