@@ -42,8 +42,9 @@ VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 
 # VALU instructions per (pixel, splat) evaluation on the kernels' main path, counted in the
 # gfx950 ISA of the built library: the blend loop body issues 54 VALU ops per two splats, the
-# backward loop body 143 per two splats (evaluation, gradient terms and wave reduction).
-VALU_PER_EVAL = {"blend": 27.0, "rbwd": 71.5}
+# backward loop body 133 per two splats (evaluation, gradient terms and the joint wave
+# reduction of both splats' terms).
+VALU_PER_EVAL = {"blend": 27.0, "rbwd": 66.5}
 
 
 def parse():

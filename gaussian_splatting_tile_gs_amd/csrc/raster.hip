@@ -408,6 +408,48 @@ __device__ __forceinline__ void splat_grad(bool contrib, const SplatEval& ev, fl
 }
 
 // The per-splat sums of reduce9_to_lds, plus (DEPTH) the tenth term summed into acc[9].
+// Two splats at once (a, b: nine terms each, summed over the wave into accA[0..8], accB[0..8]).
+// A permlane32 swap + add first puts splat a's term j in the low half and b's in the high half;
+// a permlane16 swap + add then leaves (a_k, a_k+4, b_k, b_k+4) in rows 0-3; a row_ror:8 exchange
+// and a row_half_mirror exchange split each row into four 4-lane groups (k = 2 bit2 + bit3 of
+// the lane), and two quad_perm adds finish each group: one register, 16 terms, fewer operations
+// and independent chains for the scheduler. Term 8 of both: one swap, then row shifts and a
+// row_bcast:15 leave a's sum in lane 31 and b's in lane 63.
+template <bool STORE>
+__device__ __forceinline__ void reduce18_to_lds(const float* a, const float* b, float* accA, float* accB, int lane) {
+  float u[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) u[j] = swap32_sum(a[j], b[j]);
+  float w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = swap16_sum(u[k], u[k + 4]);  // rows: a_k, a_k+4, b_k, b_k+4
+  const bool h8 = (lane & 8) != 0, h4 = (lane & 4) != 0;
+  const float x01 = (h8 ? w[1] : w[0]) + dppx<0x128>(h8 ? w[0] : w[1]);  // row_ror:8: l <-> l ^ 8
+  const float x23 = (h8 ? w[3] : w[2]) + dppx<0x128>(h8 ? w[2] : w[3]);
+  float x = (h4 ? x23 : x01) + dppx<0x141>(h4 ? x01 : x23);  // row_half_mirror: l <-> 7 - l
+  x = x + dppx<0x4E>(x);                                     // quad_perm [2,3,0,1]: l <-> l ^ 2
+  x = x + dppx<0xB1>(x);                                     // quad_perm [1,0,3,2]: l <-> l ^ 1
+  const int row = lane >> 4;
+  const int term = (h4 ? 2 : 0) + (h8 ? 1 : 0) + ((row & 1) ? 4 : 0);
+  float* acc = (row >> 1) ? accB : accA;
+  const float y0 = swap32_sum(a[8], b[8]);  // a in lanes 0-31, b in lanes 32-63
+  float y = y0 + dpp_f<0x111>(y0);          // row_shr:1
+  y = y + dpp_f<0x112>(y0);                 // row_shr:2
+  y = y + dpp_f<0x113>(y0);                 // row_shr:3
+  y = y + dpp_f<0x114>(y);                  // row_shr:4
+  y = y + dpp_f<0x118>(y);                  // row_shr:8: lane 15 of each row holds the row
+  y = y + dpp_f<0x142>(y);                  // row_bcast:15: lane 31 rows 0 + 1, lane 63 rows 2 + 3
+  if (STORE) {
+    if ((lane & 3) == 0) acc[term] = x;
+    if (lane == 31) accA[8] = y;
+    if (lane == 63) accB[8] = y;
+  } else {
+    if ((lane & 3) == 0) unsafeAtomicAdd(acc + term, x);
+    if (lane == 31) unsafeAtomicAdd(accA + 8, y);
+    if (lane == 63) unsafeAtomicAdd(accB + 8, y);
+  }
+}
+
 template <bool STORE, bool DEPTH>
 __device__ __forceinline__ void reduce_terms(const float* v, float* acc, int lane) {
   reduce9_to_lds<STORE>(v, acc, lane);
@@ -443,7 +485,7 @@ constexpr int kBwdAtomic = 0, kBwdRecords = 1, kBwdDeterministic = 2;
 constexpr int kG2d = 10;  // components of a 2D gradient: mean2d (2), conic (3), opacity, rgb (3), depth
 // DEPTH: the backward of the depth channel too (dL/ddepth given; tenth component dL/dz).
 template <bool COUNT, int MODE, bool DEPTH>
-__global__ __launch_bounds__(kRasterThreads) void k_rbwd(
+__global__ __launch_bounds__(kRasterThreads) __attribute__((amdgpu_waves_per_eu(7))) void k_rbwd(
     uint32_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ plan, uint32_t ntiles,
     const float4* __restrict__ ckpt, const float* __restrict__ ckpt_d, const uint32_t* __restrict__ ids,
     const float* __restrict__ means2d, const float* __restrict__ conics, const float* __restrict__ opac,
@@ -637,12 +679,14 @@ __global__ __launch_bounds__(kRasterThreads) void k_rbwd(
         float v0[NT], v1[NT];
         splat_grad<DEPTH>(c0, e0, dx0, dy0, b0.z, b0.w, cb0, z0, gr, gg, gb, gd, T, gS, v0);
         splat_grad<DEPTH>(c1, e1, dx1, dy1, b1.z, b1.w, cb1, z1, gr, gg, gb, gd, T, gS, v1);
-        if (DET) {
-          if (__any(c0)) reduce_terms<true, DEPTH>(v0, part + (k0 - w * 64) * NT, lane);
-          if (__any(c1)) reduce_terms<true, DEPTH>(v1, part + (k1 - w * 64) * NT, lane);
+        float* acc0 = DET ? part + (k0 - w * 64) * NT : s_acc + k0 * NT;
+        float* acc1 = DET ? part + (k1 - w * 64) * NT : s_acc + k1 * NT;
+        if (!DEPTH && has1) {
+          // both splats in one reduction (a splat no lane reaches adds zeros to its own slot)
+          if (__any(c0 || c1)) reduce18_to_lds<DET>(v0, v1, acc0, acc1, lane);
         } else {
-          if (__any(c0)) reduce_terms<false, DEPTH>(v0, s_acc + k0 * NT, lane);
-          if (__any(c1)) reduce_terms<false, DEPTH>(v1, s_acc + k1 * NT, lane);
+          if (__any(c0)) reduce_terms<DET, DEPTH>(v0, acc0, lane);
+          if (__any(c1)) reduce_terms<DET, DEPTH>(v1, acc1, lane);
         }
       }
       if (DET) {
