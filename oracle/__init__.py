@@ -29,7 +29,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# GS_ORACLE_LIB may name another build of gs_oracle.cpp (the sanitizer build of build.py --debug)
+LIB_PATH = os.environ.get("GS_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 # Unit roundoff of the fp32 implementation compared against (sets the fragility bands).
@@ -64,13 +65,15 @@ def load():
         getattr(lib, name).argtypes = [i32] + [P] * 7 + [i32, i32, i32, P, i64, P, f64] + [P] * 7
         getattr(lib, name).restype = ctypes.c_int
     for name in ("orc_render_bwd_f32", "orc_render_bwd_f64"):
-        getattr(lib, name).argtypes = [i32] + [P] * 7 + [i32, i32, i32, P, i64, P, f64, P, P, P]
+        getattr(lib, name).argtypes = [i32] + [P] * 7 + [i32, i32, i32, P, i64, P, f64, P, P, P, P]
         getattr(lib, name).restype = ctypes.c_int
     for name in ("orc_project_bwd_f32", "orc_project_bwd_f64"):
         getattr(lib, name).argtypes = [i32, i32] + [P] * 6 + [i32, i32] + [P] * 8
         getattr(lib, name).restype = ctypes.c_int
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = ctypes.c_int
+    lib.orc_set_num_threads.argtypes = [ctypes.c_int]
+    lib.orc_set_num_threads.restype = None
     _lib = lib
     return lib
 
@@ -114,6 +117,11 @@ def tiles_of(cam):
 
 def num_threads():
     return int(load().orc_num_threads())
+
+
+def set_num_threads(k):
+    """Threads of the oracle's later parallel loops."""
+    load().orc_set_num_threads(int(k))
 
 
 # ---------------------------------------------------------------------------------------------
@@ -261,14 +269,17 @@ def render(proj, cam, pixels=None, dtype=np.float32, band_eps=None):
 GRAD2D_NAMES = ("mean2d_x", "mean2d_y", "conic_A", "conic_B", "conic_C", "opacity", "r", "g", "b", "depth")
 
 
-def render_backward(proj, cam, dL_dimage, pixels=None, dtype=np.float32, band_eps=None, dL_ddepth=None):
+def render_backward(proj, cam, dL_dimage, pixels=None, dtype=np.float32, band_eps=None, dL_ddepth=None,
+                    plain_floor=False):
     """Analytic backward of the per-pixel render.
 
     dL_dimage: [H,W,3] (pixels=None) or [M,3] matching ``pixels``; dL_ddepth (optional): [H,W] or
     [M], the gradient on the depth channel.
     Returns (g2d [N,10] float64, aref [N,10] float64): per Gaussian d/d(mu'x, mu'y, A, B, C,
     opacity, r, g, b, depth) and the rounding scale of each (sum over pixels of the magnitudes of
-    the terms each contribution is computed from).
+    the terms each contribution is computed from, widened where the transmittance recovery loses
+    digits). With plain_floor=True a third array [N,10] follows: the sum over pixels of the
+    absolute per-pixel contribution, with no widening.
     """
     lib = load()
     if band_eps is None:
@@ -287,10 +298,11 @@ def render_backward(proj, cam, dL_dimage, pixels=None, dtype=np.float32, band_ep
     gd = _c(dL_ddepth, np.float64).reshape(M) if dL_ddepth is not None else None
     g2d = np.empty((n, 10))
     aref = np.empty((n, 10))
+    aplain = np.empty((n, 10)) if plain_floor else None
     fn = getattr(lib, "orc_render_bwd_" + _suffix(dtype))
     fn(n, *[_p(a) for a in ins], _tight(cam), W, H, _p(bg), M, _p(pix), float(band_eps), _p(g), _p(gd), _p(g2d),
-       _p(aref))
-    return g2d, aref
+       _p(aref), _p(aplain))
+    return (g2d, aref, aplain) if plain_floor else (g2d, aref)
 
 
 def _pad10(a, n):

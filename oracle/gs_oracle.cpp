@@ -678,28 +678,33 @@ int render_impl(int n, const T* means2d, const T* conics, const T* opac, const T
 // With a depth channel (dL_ddepth, may be NULL) its value z_i joins the colours: D = sum_i z_i a_i T_i
 // (background depth 0), so dD/dz_i = a_i T_i and dD/da_i = z_i T_i - S^D_i / (1 - a_i).
 // Output per Gaussian (10): d mu'_x, d mu'_y, dA, dB, dC, d opacity, d colour (3), d depth,
-// accumulated in double. aref is the rounding scale of each sum, for tolerance floors: per pixel, the absolute
-// values of the terms each contribution is computed from (|c| T + |S| / (1 - a) for dC/da, which
-// cancels when a splat's colour matches what lies behind it), times max(1, e_T / 1e-5) with e_T
-// the pixel's bound on the relative rounding of its transmittance, summed over pixels.
+// accumulated in double. Two rounding scales of each sum, for tolerance floors:
+//   aref_plain: the sum over pixels of the absolute per-pixel contribution |dC_p/d.| (may be NULL);
+//   aref: per pixel, the absolute values of the terms each contribution is computed from (|c| T +
+//     |S| / (1 - a) for dC/da, which cancels when a splat's colour matches what lies behind it),
+//     times max(1, e_T / 1e-5) with e_T the pixel's bound on the relative rounding of its
+//     transmittance, summed over pixels (may be NULL).
 template <class T>
 int render_bwd_impl(int n, const T* means2d, const T* conics, const T* opac, const T* colors,
                     const T* depths, const uint32_t* tiles, const int32_t* rects, int tight, int W, int H,
                     const T* bg, int64_t npix, const int32_t* pix, double band_eps,
-                    const double* dL_dimg, const double* dL_ddepth, double* g2d, double* aref) {
+                    const double* dL_dimg, const double* dL_ddepth, double* g2d, double* aref,
+                    double* aref_plain) {
   std::vector<Splat2D<T>> S;
   std::vector<int> order;
   build_splats<T>(n, means2d, conics, opac, colors, depths, tiles, rects, tight, S, order);
   if (!pix) npix = (int64_t)W * H;
   const int nt = nthreads();
-  std::vector<std::vector<double>> accg(nt), acca(nt);
+  std::vector<std::vector<double>> accg(nt), acca(nt), accp(nt);
 #pragma omp parallel
   {
     const int tid = thread_id();
     accg[tid].assign((size_t)n * 10, 0.0);
     acca[tid].assign((size_t)n * 10, 0.0);
+    accp[tid].assign((size_t)n * 10, 0.0);
     double* G = accg[tid].data();
     double* Aa = acca[tid].data();
+    double* Ap = accp[tid].data();
     Trace tr;
     std::vector<double> al, Ti, Gi;
 #pragma omp for schedule(dynamic, 16)
@@ -755,6 +760,7 @@ int render_bwd_impl(int n, const T* means2d, const T* conics, const T* opac, con
         for (int k = 0; k < 10; ++k) {
           G[(size_t)g * 10 + k] += contrib[k];
           Aa[(size_t)g * 10 + k] += mag[k] * tscale;
+          Ap[(size_t)g * 10 + k] += std::fabs(contrib[k]);
         }
         for (int ch = 0; ch < 3; ++ch) {
           Sacc[ch] += c[ch] * al[i] * Ti[i];
@@ -766,13 +772,15 @@ int render_bwd_impl(int n, const T* means2d, const T* conics, const T* opac, con
     }
   }
   for (size_t i = 0; i < (size_t)n * 10; ++i) {
-    double sg = 0, sa = 0;
+    double sg = 0, sa = 0, sp = 0;
     for (int t = 0; t < nt; ++t) {
       sg += accg[t][i];
       sa += acca[t][i];
+      sp += accp[t][i];
     }
     g2d[i] = sg;
     if (aref) aref[i] = sa;
+    if (aref_plain) aref_plain[i] = sp;
   }
   return 0;
 }
@@ -1035,7 +1043,8 @@ void orc_log_f32(const float* x, float* y, int64_t n) {
 // -- single steps, exposed for pins ---------------------------------------------------------------
 // quaternion (w,x,y,z) and log-scales -> normalised R [9] and Sigma [9]
 void orc_covariance_f64(const double* quat, const double* log_scale, double* R, double* Sigma) {
-  double cam[24] = {1, 0, 0, 0, 0, 1, 0, 0, 0, 0, 1, 0, 0, 0, 0, 1, 1, 1, 0, 0, 0.01, 0, 0, 0};
+  // identity view, unit focal lengths, near 0.01, black background, default options
+  double cam[kNumCam] = {1, 0, 0, 0, 0, 1, 0, 0, 0, 0, 1, 0, 0, 0, 0, 1, 1, 1, 0, 0, 0.01, 0, 0, 0, 0, 0, 0};
   double mean[3] = {0, 0, 1}, sh[3] = {0, 0, 0};
   Proj<double> P;
   Cam<double> c = make_cam<double>(cam, 1, 1);
@@ -1135,16 +1144,18 @@ int orc_render_f64(int n, const double* means2d, const double* conics, const dou
 int orc_render_bwd_f32(int n, const float* means2d, const float* conics, const float* opac, const float* colors,
                        const float* depths, const uint32_t* tiles, const int32_t* rects, int tight, int W,
                        int H, const float* bg, int64_t npix, const int32_t* pix, double band_eps,
-                       const double* dL_dimg, const double* dL_ddepth, double* g2d, double* aref) {
+                       const double* dL_dimg, const double* dL_ddepth, double* g2d, double* aref,
+                       double* aref_plain) {
   return render_bwd_impl<float>(n, means2d, conics, opac, colors, depths, tiles, rects, tight, W, H, bg, npix, pix,
-                                band_eps, dL_dimg, dL_ddepth, g2d, aref);
+                                band_eps, dL_dimg, dL_ddepth, g2d, aref, aref_plain);
 }
 int orc_render_bwd_f64(int n, const double* means2d, const double* conics, const double* opac,
                        const double* colors, const double* depths, const uint32_t* tiles, const int32_t* rects,
                        int tight, int W, int H, const double* bg, int64_t npix, const int32_t* pix, double band_eps,
-                       const double* dL_dimg, const double* dL_ddepth, double* g2d, double* aref) {
+                       const double* dL_dimg, const double* dL_ddepth, double* g2d, double* aref,
+                       double* aref_plain) {
   return render_bwd_impl<double>(n, means2d, conics, opac, colors, depths, tiles, rects, tight, W, H, bg, npix, pix,
-                                 band_eps, dL_dimg, dL_ddepth, g2d, aref);
+                                 band_eps, dL_dimg, dL_ddepth, g2d, aref, aref_plain);
 }
 
 int orc_project_bwd_f32(int n, int sh_degree, const float* means, const float* log_scales, const float* quats,
@@ -1163,5 +1174,14 @@ int orc_project_bwd_f64(int n, int sh_degree, const double* means, const double*
 }
 
 int orc_num_threads(void) { return nthreads(); }
+
+// Thread count of the later parallel regions (timing the oracle on one core or all of them).
+void orc_set_num_threads(int k) {
+#ifdef _OPENMP
+  if (k > 0) omp_set_num_threads(k);
+#else
+  (void)k;
+#endif
+}
 
 }  // extern "C"
