@@ -277,6 +277,43 @@ def test_sh_basis_orthonormal_and_degree0():
     assert oracle.project(sc, cam, np.float32)["colors"][0].tolist() == np.float32([0.3, 0.6, 0.9]).tolist()
 
 
+def _real_sh_scipy(l, m, dirs):
+    """sqrt(4 pi) times the real spherical harmonic of degree l, order m, from scipy's complex
+    harmonics (which carry the Condon-Shortley phase (-1)^m): m < 0 takes sqrt(2) (-1)^m Im Y_l^|m|,
+    m > 0 sqrt(2) (-1)^m Re Y_l^m, so the phase cancels and the order runs m = -l..l."""
+    from scipy.special import sph_harm_y
+
+    theta = np.arccos(np.clip(dirs[:, 2], -1.0, 1.0))  # polar angle from +z
+    phi = np.arctan2(dirs[:, 1], dirs[:, 0])           # azimuth from +x towards +y
+    y = sph_harm_y(l, abs(m), theta, phi)
+    if m < 0:
+        v = np.sqrt(2.0) * (-1.0) ** m * y.imag
+    elif m == 0:
+        v = y.real
+    else:
+        v = np.sqrt(2.0) * (-1.0) ** m * y.real
+    return np.sqrt(4.0 * np.pi) * v
+
+
+def test_sh_basis_order_and_signs_against_scipy():
+    # the basis reading: real SH scaled so that B_00 = 1, entry l^2 + (m + l) for m = -l..l, no
+    # Condon-Shortley phase; checked at the axes, the diagonal and random directions against an
+    # independent definition (associated Legendre functions in scipy), so a swapped pair or a
+    # flipped sign in any band fails even though the Gram matrix would not notice
+    rng = np.random.default_rng(5)
+    special = np.array([[1, 0, 0], [-1, 0, 0], [0, 1, 0], [0, -1, 0], [0, 0, 1], [0, 0, -1],
+                        [1, 1, 1], [-1, 2, -3]], np.float64)
+    dirs = np.concatenate([special, rng.normal(size=(64, 3))])
+    dirs /= np.linalg.norm(dirs, axis=1, keepdims=True)
+    B = oracle.sh_basis(3, dirs)
+    for l in range(4):
+        for m in range(-l, l + 1):
+            want = _real_sh_scipy(l, m, dirs)
+            assert np.allclose(B[:, l * l + m + l], want, atol=1e-12), (l, m)
+    # lower degrees leave the higher entries at zero
+    assert np.all(oracle.sh_basis(1, dirs)[:, 4:] == 0.0) and np.all(oracle.sh_basis(2, dirs)[:, 9:] == 0.0)
+
+
 # ---- invariants -----------------------------------------------------------------------------
 def test_weights_and_final_transmittance_sum_to_one():
     sc = synth.random_scene(40, seed=3, width=48, height=48, focal=50.0)
