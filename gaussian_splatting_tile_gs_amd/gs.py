@@ -379,6 +379,7 @@ class Pipeline:
         l1_target: also write the L1 gradient against it into self.dL_dimage (gs_rasterize_fwd_l1)."""
         ck = self.schedule == "chunks" if checkpoints is None else bool(checkpoints)
         self._ckpt_written = ck
+        self._ckpt_depth = ck and depth is not None  # the checkpoints hold the depth channel's parts
         plan = self.plan if self.schedule != "tiles" else None
         ws = self.raster_ws if ck else None
         if l1_target is not None:
@@ -404,8 +405,11 @@ class Pipeline:
 
     def backward(self, cam: GsCamera, dL_dimage=None, eval_count=None, stream=None, dL_ddepth=None):
         """self.deterministic selects gs_rasterize_bwd_deterministic (records sized by the pair
-        capacity) over gs_rasterize_bwd (fp32 atomics)."""
+        capacity) over gs_rasterize_bwd (fp32 atomics). The backward splits long tiles at the last
+        forward's checkpoints only when they hold what it reads: with dL_ddepth, the depth
+        channel's parts too; otherwise it walks whole tiles."""
         p, g = self.p, self.grads
+        use_ckpt = getattr(self, "_ckpt_written", False) and (dL_ddepth is None or getattr(self, "_ckpt_depth", False))
         det = getattr(self, "deterministic", False)
         ws = self.bwd_ws
         if det:
@@ -418,7 +422,7 @@ class Pipeline:
                          self.dL_dimage if dL_dimage is None else dL_dimage, ws, g["means"], g["log_scales"],
                          g["quats"], g["opacity_logits"], g["sh"], g["means2d"], eval_count, stream,
                          plan=self.plan if self.schedule != "tiles" else None,
-                         raster_ws=self.raster_ws if getattr(self, "_ckpt_written", False) else None,
+                         raster_ws=self.raster_ws if use_ckpt else None,
                          pair_capacity=self.capacity if det else None, dL_ddepth=dL_ddepth)
 
     # ---- feature channels: any per-Gaussian quantity blended with the colour's weights ----------
