@@ -555,7 +555,8 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
         }
         if (!a.plan) continue;
         const uint32_t slot = wave_class_slot(valid, count_class(c), s_cur, lane);
-        if (valid) a.plan[kPlanOrder + slot] = t;
+        // the class cursors partition [0, ntiles): every valid slot is below ntiles
+        if (valid && slot < a.ntiles) a.plan[kPlanOrder + slot] = t;
         // a tile of two or more chunks: its checkpoint slots and extra work items
         const uint32_t nch = (c + L - 1u) / L;
         const bool multi = valid && nch >= 2u;
@@ -741,6 +742,9 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(8)
   // workgroups of the depth passes get 48 KB
   constexpr uint32_t kLdsWords = (EXTRA != 0 && 2 * TILE < 12288) ? 12288u : 2u * TILE;
   static_assert(kSortWaves * kRadix <= 2 * TILE, "digit counts must fit in the key staging");
+  // the finalizer's step of tiles and its auxiliary words (histograms, classes, scan partials)
+  // are disjoint parts of s_mem
+  static_assert(EXTRA != 2 || kFinStep + kFinAuxWords <= kLdsWords, "finalizer LDS layout overlaps");
   __shared__ uint32_t s_mem[kLdsWords];
   uint32_t (*s_wcnt)[kRadix] = reinterpret_cast<uint32_t (*)[kRadix]>(s_mem);  // count, then offset
   __shared__ uint32_t s_dpre[kRadix];
