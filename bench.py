@@ -40,11 +40,17 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 
-# VALU instructions per (pixel, splat) evaluation on the kernels' main path, counted in the
-# gfx950 ISA of the built library: the blend loop body issues 54 VALU ops per two splats, the
-# backward loop body 133 per two splats (evaluation, gradient terms and the joint wave
-# reduction of both splats' terms).
-VALU_PER_EVAL = {"blend": 27.0, "rbwd": 66.5}
+# VALU lane-operations per (pixel, splat) evaluation that the roofline counts: the blend's is
+# its loop body in the gfx950 ISA of the built library (54 VALU ops per two splats); the
+# backward's is the algorithmic count of a (pixel, entry) walked back (evaluation, T recovery,
+# dL/dalpha and the nine gradient pieces: 60), with the loop body's ISA count beside it
+# (133 per two splats, the wave reduction included).
+VALU_PER_EVAL = {"blend": 27.0, "rbwd": 60.0}
+VALU_PER_EVAL_ISA = {"blend": 27.0, "rbwd": 66.5}
+# the binning kernels, and among them those that move keys (the radix passes and the emission
+# fused with the first pair pass)
+BIN_KERNELS = ("bin_prep", "hist_reduce", "depth_sort_pass", "scan", "emit_sort", "pair_sort_pass")
+SORT_KERNELS = ("depth_sort_pass", "emit_sort", "pair_sort_pass")
 
 
 def parse():
@@ -123,6 +129,8 @@ def cpu_baseline(wl, scene, cams_d, target_of, seconds):
 
     W, H = wl.width, wl.height
 
+    fragile = {}
+
     def one(ci, npix):
         cam = cams_d[ci]
         pix = synth.sample_pixels(W, H, npix, seed=1)
@@ -136,7 +144,19 @@ def cpu_baseline(wl, scene, cams_d, target_of, seconds):
         t3 = time.perf_counter()
         oracle.project_backward(scene, cam, g2d)
         t4 = time.perf_counter()
+        fragile[ci] = (int(npix), int(np.count_nonzero(fwd["fragile"])))
         return t4 - t0, (t1 - t0) + (t4 - t3) + (t3 - t1) / npix * W * H
+
+    # one core: a pixel sample of camera 0 grown to about a sixth of the budget
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    npix1 = 256
+    while True:
+        total1, frame1 = one(0, npix1)
+        if total1 >= seconds / 6.0 or npix1 >= W * H:
+            break
+        npix1 = min(W * H, int(npix1 * max(2.0, 0.8 * seconds / 6.0 / max(total1, 1e-3))))
+    oracle.set_num_threads(threads)
 
     npix = 1024
     while True:
@@ -158,8 +178,13 @@ def cpu_baseline(wl, scene, cams_d, target_of, seconds):
                   f"render + backward on {npix} seeded pixels of {W * H} (sparse L1 loss), chain rule; "
                   f"per-pixel time scaled to the full frame (measured {measured:.1f} s)")
     frame_s = sum(frames) / len(frames)
-    return {"value": 1.0 / frame_s, "unit": "iterations/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": sample, "measured_seconds": round(measured, 3), "frame_seconds": round(frame_s, 3)}
+    npx0, nfrag0 = fragile[0]
+    return {"value": 1.0 / frame_s, "unit": "iterations/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "measured_seconds": round(measured, 3), "frame_seconds": round(frame_s, 3),
+            "one_core": {"value": 1.0 / frame1, "unit": "iterations/s", "cores": 1,
+                         "sample": f"camera 0 of {wl.name}: {npix1} seeded pixels of {W * H}, per-pixel time scaled "
+                                   f"to the full frame (measured {total1:.1f} s)"},
+            "fragile_pixels": {"camera": 0, "pixels": npx0, "fragile": nfrag0}}
 
 
 def adam_roofline(gs, torch, params, grads, wl, launches=50):
@@ -311,7 +336,9 @@ def main():
         "value": its, "unit": "iterations/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": 1e3 * elapsed / args.steps, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
-        "mpix_per_s": its * W * H / 1e6, "sorted_pairs_per_s": steps_pairs / elapsed,
+        "mpix_per_s": its * W * H / 1e6, "sorted_pairs_per_s": None,
+        # pairs of the timed steps per second of the whole timed region (not of the sort alone)
+        "pairs_per_s_end_to_end": steps_pairs / elapsed,
         "config": {"workload": wl.name, "gaussians": wl.n, "width": W, "height": H, "cameras": ncam,
                    "loss": "0.8 L1 + 0.2 (1 - SSIM)" if pipe.ssim_lambda > 0 else "L1 (gradient formed in the blend)",
                    "concurrent_cameras": nstreams, "backward": backward, "tile_lists": args.tile_lists,
@@ -365,9 +392,12 @@ def main():
             evals = (evals_f if dom == "blend" else evals_b).item() / cnt
             ops = evals * VALU_PER_EVAL[dom]
             achieved = ops / avg_s / 1e12
+            isa = evals * VALU_PER_EVAL_ISA[dom] / avg_s / 1e12
             roof = {"bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TOPS, "unit": "TOP/s",
                     "frac": achieved / VALU_PEAK_TOPS, "traffic": traffic_for(dom, wl.name), "kernel": dom,
-                    "evals_per_launch": evals, "valu_per_eval": VALU_PER_EVAL[dom], "avg_us": avg_s * 1e6}
+                    "evals_per_launch": evals, "valu_per_eval": VALU_PER_EVAL[dom],
+                    "valu_per_eval_isa": VALU_PER_EVAL_ISA[dom], "frac_isa": isa / VALU_PEAK_TOPS,
+                    "avg_us": avg_s * 1e6}
         else:
             b = kernel_bytes(dom, stats) or 0.0
             achieved = b / avg_s / 1e9
@@ -375,9 +405,13 @@ def main():
                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(dom, wl.name), "kernel": dom,
                     "bytes_per_launch": b, "avg_us": avg_s * 1e6}
         result["roofline"] = roof
-        bin_names = ("bin_prep", "hist_reduce", "depth_sort_pass", "scan", "emit_sort", "pair_sort_pass")
-        bin_s = sum(per[k][0] for k in bin_names if k in per) / 1e3 / nprof
-        bin_b = sum((kernel_bytes(k, stats) or 0.0) * per[k][1] for k in bin_names if k in per) / nprof
+        bin_s = sum(per[k][0] for k in BIN_KERNELS if k in per) / 1e3 / nprof
+        bin_b = sum((kernel_bytes(k, stats) or 0.0) * per[k][1] for k in BIN_KERNELS if k in per) / nprof
+        sort_s = sum(per[k][0] for k in SORT_KERNELS if k in per) / 1e3 / nprof
+        # sorted pairs per second of the sort kernels' time and of the whole binning's
+        result["sorted_pairs_per_s"] = stats["pairs"] / sort_s if sort_s > 0 else None
+        result["sorted_pairs_per_s_bin_sort"] = stats["pairs"] / bin_s if bin_s > 0 else None
+        result["sort_kernels"] = [k for k in SORT_KERNELS if k in per]
         # the same time against the bytes a stable 64-bit (tile | depth) key sort with a separate
         # count/emit/range would move (172 B per pair + 32 B per Gaussian): what a design that
         # sorts the full keys would have to stream to finish in this time
@@ -392,9 +426,12 @@ def main():
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a pixel sample")
-        result["cpu_baseline"] = cpu_baseline(wl, scene, cams_d,
-                                              lambda i: targets[i].cpu().numpy().astype(np.float64),
-                                              args.cpu_seconds)
+        cb = cpu_baseline(wl, scene, cams_d, lambda i: targets[i].cpu().numpy().astype(np.float64),
+                          args.cpu_seconds)
+        # the oracle's fragile pixels (a skip/stop decision within fp32 rounding of its threshold)
+        # on the sample of camera 0 it rendered
+        result["fragile_pixels"] = cb.pop("fragile_pixels")
+        result["cpu_baseline"] = cb
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

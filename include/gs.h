@@ -241,9 +241,11 @@ gs_status gs_rasterize_bwd(int32_t n, int32_t sh_degree, const float* d_means, c
  * gs_rasterize_bwd_deterministic -- gs_rasterize_bwd with bitwise-reproducible gradients: the
  * same inputs give the same bits on every run. No floating-point atomics: the 2D gradient of
  * each (tile, Gaussian) pair is written to its own slot -- a Gaussian's pairs are contiguous
- * from the prefix sum of tiles_touched in id order, row-major over its tile rectangle -- and the
- * slots of a Gaussian are added in a fixed order (one wave per Gaussian, strided lanes, then a
- * fixed lane tree); inside a tile the four waves' sums of a splat are added in wave order.
+ * from the prefix sum of tiles_touched in id order, row-major over its tile rectangle (with
+ * tight_tiles, over each row's tight run) -- and the slots of a Gaussian are added in an order
+ * fixed by its pair count alone: a Gaussian of at most 16 pairs by one lane in slot order, a
+ * larger one by a whole wave (lane l adds slots l, l + 64, ... in order, then a fixed lane
+ * tree); inside a tile the four waves' sums of a splat are added in wave order.
  * Arguments as gs_rasterize_bwd, plus pair_capacity: at least the P of gs_bin_and_sort (the
  *   capacity given to it will do); d_dL_ddepth as in gs_rasterize_bwd; d_workspace (256-byte aligned) of at least
  *   gs_bwd_det_workspace_bytes(n, pair_capacity) bytes. If P > pair_capacity every gradient is 0
