@@ -49,8 +49,9 @@ VALU_PER_EVAL = {"blend": 27.0, "rbwd": 60.0}
 VALU_PER_EVAL_ISA = {"blend": 27.0, "rbwd": 66.5}
 # the binning kernels, and among them those that move keys (the radix passes and the emission
 # fused with the first pair pass)
-BIN_KERNELS = ("bin_prep", "hist_reduce", "depth_sort_pass", "scan", "emit_sort", "pair_sort_pass")
-SORT_KERNELS = ("depth_sort_pass", "emit_sort", "pair_sort_pass")
+BIN_KERNELS = ("small_local", "small_merge", "bin_prep", "hist_reduce", "depth_sort_pass", "scan", "emit_sort",
+               "pair_sort_pass")
+SORT_KERNELS = ("small_local", "small_merge", "depth_sort_pass", "emit_sort", "pair_sort_pass")
 
 
 def parse():
@@ -85,6 +86,12 @@ def kernel_bytes(name, stats):
     """Algorithmic HBM bytes of one launch of a binning kernel."""
     P, N = stats["pairs"], stats["n"]
     return {
+        # small frames: depth, tile count, mean and radii in (24 B), the rectangle record and the
+        # block-sorted key, id and count prefix out (28 B) per Gaussian
+        "small_local": 52.0 * N,
+        # the sorted keys, ids, count prefixes and rectangle records in (28 B), the depth-ordered
+        # record out (16 B) per Gaussian
+        "small_merge": 44.0 * N,
         "bin_prep": 48.0 * N,
         "depth_sort_pass": 16.0 * N,
         "scan": 40.0 * N,
@@ -379,7 +386,7 @@ def main():
         visible = int((pipe.proj.tiles_touched > 0).sum().item())
         K = (wl.sh_degree + 1) ** 2
         stats = {"pairs": float(np.mean(pairs)), "n": wl.n, "visible": visible, "pixels": W * H,
-                 "pair_passes": per.get("pair_sort_pass", [0, 0])[1] // max(1, per.get("scan", [0, 1])[1]),
+                 "pair_passes": per.get("pair_sort_pass", [0, 0])[1] // max(1, per.get("emit_sort", [0, 1])[1]),
                  "project_bytes": wl.n * (4 * (3 + 3 + 4 + 1 + 3 * K) + 52)}
         kernels = {}
         for name, (tot, cnt) in sorted(per.items(), key=lambda kv: -kv[1][0]):

@@ -47,6 +47,7 @@
 // writes 12 and gathers 4). With 2 pair passes that is 8 + 16 + 24 = 48 B/pair, plus about
 // 150 B per Gaussian for the depth sort, the rectangles and the scan.
 #include <algorithm>
+#include <mutex>
 
 #include "gs_internal.h"
 
@@ -274,7 +275,19 @@ struct TileCountArgs {
   int pshift[3];        // the pair passes' digit shifts and widths (tile id bits split evenly)
   int pbits[3];
   uint32_t* hist_pair;  // [npass][256]
+  // small frames: the difference array is the sum of tmat_rows per-block rows, tmat_stride apart
+  // (tdiff is then unused)
+  const uint32_t* tmat;
+  uint32_t tmat_rows;
+  uint32_t tmat_stride;
 };
+
+__device__ __forceinline__ uint32_t tdiff_at(const TileCountArgs& a, uint32_t t) {
+  if (!a.tmat) return a.tdiff[t];
+  uint32_t v = 0;
+  for (uint32_t r = 0; r < a.tmat_rows; ++r) v += a.tmat[(size_t)r * a.tmat_stride + t];
+  return v;
+}
 constexpr int kRowGaussians = 2048;  // Gaussians per row workgroup (two per lane)
 
 // Row workgroup rb: Gaussians [2048 rb, 2048 (rb + 1)) of the id order, two per lane. A lane
@@ -290,6 +303,70 @@ __device__ __forceinline__ TightShape tight_of(const TileCountArgs& a, uint32_t 
   const float* c = a.conics + 3 * (size_t)g;
   return tight_shape(m.x, m.y, c[0], c[1], c[2], a.opac[g]);
 }
+// One Gaussian per lane (rectangle r = (count, first tile, width, height), id j; valid lanes
+// only add): a lane walks its own rows when there are at most kOwnRows (tight: kOwnRowsTight);
+// taller rectangles are walked by the whole wave, one at a time. Every lane of the wave calls it.
+__device__ void tile_rows_item(const TileCountArgs& a, uint4 r, uint32_t j, bool valid, uint32_t* diff) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t tx = (uint32_t)a.tiles_x;
+  const uint32_t h = valid ? r.w : 0u;
+  // with tight tiles each lane prepares its own Gaussian's ellipse once; the wave walk of a
+  // tall one takes it from the owning lane
+  TightShape own{};
+  if (a.tight && h > 0) own = tight_of(a, j);
+  const uint32_t own_max = a.tight ? kOwnRowsTight : kOwnRows;
+  if (h <= own_max) {
+    if (a.tight && h > 0) {
+      const TightShape& ts = own;
+      const int x0 = (int)(r.y % tx), y0 = (int)(r.y / tx);
+      for (uint32_t y = 0; y < h; ++y) {
+        const int2 sp = tight_row(ts, y0 + (int)y, x0, x0 + (int)r.z);
+        if (sp.y > sp.x) {
+          atomicAdd(&diff[(uint32_t)(y0 + (int)y) * tx + (uint32_t)sp.x], 1u);
+          atomicSub(&diff[(uint32_t)(y0 + (int)y) * tx + (uint32_t)sp.y], 1u);
+        }
+      }
+    } else {
+      for (uint32_t y = 0; y < h; ++y) {
+        atomicAdd(&diff[r.y + y * tx], 1u);
+        atomicSub(&diff[r.y + y * tx + r.z], 1u);
+      }
+    }
+  }
+  uint64_t tall = __ballot(h > own_max);
+  while (tall) {
+    const int src = __builtin_ctzll(tall);
+    tall &= tall - 1;
+    const uint32_t hh = __builtin_amdgcn_readlane(h, src);
+    const uint32_t tb = __builtin_amdgcn_readlane(r.y, src), w = __builtin_amdgcn_readlane(r.z, src);
+    if (a.tight) {
+      TightShape ts;
+      ts.mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.mx), src));
+      ts.my = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.my), src));
+      ts.A = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.A), src));
+      ts.B = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.B), src));
+      ts.C = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.C), src));
+      ts.D = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.D), src));
+      ts.s2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.s2), src));
+      ts.E = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.E), src));
+      ts.full = __builtin_amdgcn_readlane((int)own.full, src) != 0;
+      const int x0 = (int)(tb % tx), y0 = (int)(tb / tx);
+      for (uint32_t y = lane; y < hh; y += 64) {
+        const int2 sp = tight_row(ts, y0 + (int)y, x0, x0 + (int)w);
+        if (sp.y > sp.x) {
+          atomicAdd(&diff[(uint32_t)(y0 + (int)y) * tx + (uint32_t)sp.x], 1u);
+          atomicSub(&diff[(uint32_t)(y0 + (int)y) * tx + (uint32_t)sp.y], 1u);
+        }
+      }
+    } else {
+      for (uint32_t y = lane; y < hh; y += 64) {
+        atomicAdd(&diff[tb + y * tx], 1u);
+        atomicSub(&diff[tb + y * tx + w], 1u);
+      }
+    }
+  }
+}
+
 __device__ void tile_rows(const TileCountArgs& a, uint32_t rb, uint32_t* lds, uint32_t lds_words) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool staged = a.ntiles + 1 <= lds_words;
@@ -298,67 +375,12 @@ __device__ void tile_rows(const TileCountArgs& a, uint32_t rb, uint32_t* lds, ui
     __syncthreads();
   }
   uint32_t* diff = staged ? lds : a.tdiff;
-  const uint32_t tx = (uint32_t)a.tiles_x;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int64_t j = (int64_t)rb * kRowGaussians + wave * 128 + k * 64 + lane;
-    const uint4 r = j < a.n ? a.rec[j] : make_uint4(0u, 0u, 1u, 0u);
-    const uint32_t h = r.w;
-    // with tight tiles each lane prepares its own Gaussian's ellipse once; the wave walk of a
-    // tall one takes it from the owning lane
-    TightShape own{};
-    if (a.tight && h > 0) own = tight_of(a, (uint32_t)j);
-    const uint32_t own_max = a.tight ? kOwnRowsTight : kOwnRows;
-    if (h <= own_max) {
-      if (a.tight && h > 0) {
-        const TightShape& ts = own;
-        const int x0 = (int)(r.y % tx), y0 = (int)(r.y / tx);
-        for (uint32_t y = 0; y < h; ++y) {
-          const int2 sp = tight_row(ts, y0 + (int)y, x0, x0 + (int)r.z);
-          if (sp.y > sp.x) {
-            atomicAdd(&diff[(uint32_t)(y0 + (int)y) * tx + (uint32_t)sp.x], 1u);
-            atomicSub(&diff[(uint32_t)(y0 + (int)y) * tx + (uint32_t)sp.y], 1u);
-          }
-        }
-      } else {
-        for (uint32_t y = 0; y < h; ++y) {
-          atomicAdd(&diff[r.y + y * tx], 1u);
-          atomicSub(&diff[r.y + y * tx + r.z], 1u);
-        }
-      }
-    }
-    uint64_t tall = __ballot(h > own_max);
-    while (tall) {
-      const int src = __builtin_ctzll(tall);
-      tall &= tall - 1;
-      const uint32_t hh = __builtin_amdgcn_readlane(h, src);
-      const uint32_t tb = __builtin_amdgcn_readlane(r.y, src), w = __builtin_amdgcn_readlane(r.z, src);
-      if (a.tight) {
-        TightShape ts;
-        ts.mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.mx), src));
-        ts.my = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.my), src));
-        ts.A = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.A), src));
-        ts.B = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.B), src));
-        ts.C = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.C), src));
-        ts.D = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.D), src));
-        ts.s2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.s2), src));
-        ts.E = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own.E), src));
-        ts.full = __builtin_amdgcn_readlane((int)own.full, src) != 0;
-        const int x0 = (int)(tb % tx), y0 = (int)(tb / tx);
-        for (uint32_t y = lane; y < hh; y += 64) {
-          const int2 sp = tight_row(ts, y0 + (int)y, x0, x0 + (int)w);
-          if (sp.y > sp.x) {
-            atomicAdd(&diff[(uint32_t)(y0 + (int)y) * tx + (uint32_t)sp.x], 1u);
-            atomicSub(&diff[(uint32_t)(y0 + (int)y) * tx + (uint32_t)sp.y], 1u);
-          }
-        }
-      } else {
-        for (uint32_t y = lane; y < hh; y += 64) {
-          atomicAdd(&diff[tb + y * tx], 1u);
-          atomicSub(&diff[tb + y * tx + w], 1u);
-        }
-      }
-    }
+    const bool valid = j < a.n;
+    const uint4 r = valid ? a.rec[j] : make_uint4(0u, 0u, 1u, 0u);
+    tile_rows_item(a, r, (uint32_t)j, valid, diff);
   }
   if (staged) {
     __syncthreads();
@@ -498,7 +520,7 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
 #pragma unroll
         for (int q = 0; q < kFinRows; ++q) {
           const uint32_t i = (uint32_t)(q * kSortThreads + tid);
-          if (q < rows) s[i] = i < m ? a.tdiff[cb + i] : 0u;
+          if (q < rows) s[i] = i < m ? tdiff_at(a, cb + i) : 0u;
         }
         // counts: the inclusive prefix of the differences = the next tile's exclusive one
         const uint32_t dtot = lds_rows_scan(s, rows, carry_d, s_wt, s_rt);
@@ -1067,6 +1089,307 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(8)
                            status, keys_out, vals_out, out_keys64, depth_bits);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Small frames (N <= kSmallMaxN): the depth order from sorted blocks and merge ranks, two launches
+// instead of the key-computing pass, four radix passes and the scan.
+//   k_small_local  one workgroup per block of 4096 Gaussians (ids [4096 b, 4096 b + 4096)):
+//                  depth keys and rectangles; the block's tile-count difference array (a row of
+//                  tmat); the block sorted stably by key in LDS (radix passes of up to 9 bits over
+//                  the bits the block's keys span); the sorted keys, ids and the exclusive prefix
+//                  of their tile counts written out
+//   k_small_merge  one workgroup per block: all N sorted keys held in LDS, each key's place in the
+//                  depth order is its place in its block plus, for every other block, the number
+//                  of its keys that come first (binary search; an earlier block's equal keys have
+//                  smaller ids and come first), and its first pair position is the sum of the
+//                  matching tile-count prefixes. It writes the depth-ordered records and the
+//                  emission chunks' first Gaussians as the scan does; one more workgroup is the
+//                  tile-count finalizer (the difference array is the sum of the blocks' rows)
+// The order is the stable (depth bits, id) order of the radix path, bit for bit.
+// ---------------------------------------------------------------------------------------------
+constexpr int kSmallBlock = kSortTile;  // 4096 Gaussians per block, four per thread
+constexpr int kSmallMaxBlocks = 9;
+constexpr int32_t kSmallMaxN = kSmallBlock * kSmallMaxBlocks;  // every key in 144 KB of LDS
+constexpr uint32_t kSmallMaxTiles = 16383;                      // a block's difference array in LDS
+constexpr int kLocalBits = 9;
+constexpr int kLocalRadix = 1 << kLocalBits;
+// k_small_local's dynamic LDS (words): per-wave digit counts, keys, values, tile counts by local
+// index, the difference array
+constexpr uint32_t kLocalCnt = kSortWaves * kLocalRadix;
+constexpr uint32_t kLocalFixedWords = kLocalCnt + 3 * kSmallBlock;
+
+struct SmallArgs {
+  int32_t n;
+  uint32_t nb;          // blocks
+  const float* depths;
+  const uint32_t* tiles;
+  const float* means2d;
+  const int32_t* radii;
+  int32_t tiles_x, tiles_y;
+  uint4* rec;           // [n] (count, first tile, width, height) in id order
+  uint32_t* skey;       // [nb, 4096] block-sorted depth keys (0xFFFFFFFF: not drawn)
+  uint32_t* sid;        // [nb, 4096] their ids
+  uint32_t* cpre;       // [nb, 4096] exclusive prefix of their tile counts in block-sorted order
+  uint32_t* btot;       // [nb] block totals of the tile counts
+  uint32_t* tmat;       // [nb, tmat_stride] per-block difference arrays of the per-tile counts
+  uint32_t tmat_stride;
+  uint32_t* zero;       // zeroed: control block, pair look-back words
+  size_t zero_words;
+  uint32_t* ranges;     // zeroed: [ntiles, 2]
+  size_t range_words;
+};
+
+// Exclusive sum over the values of the first 512 threads (the others pass 0); two barriers.
+__device__ __forceinline__ uint32_t block_excl_scan512(uint32_t v, uint32_t* s_wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t inc = wave_incl_scan<uint32_t>(v, lane);
+  if (wave < 8 && lane == 63) s_wsum[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) before += (w < wave) ? s_wsum[w] : 0u;
+  __syncthreads();
+  return before + inc - v;
+}
+
+// One stable radix pass over `bits` (<= 9) bits at `shift` of the workgroup's 4096 items, in LDS:
+// item i of lane l of wave w is element 256 w + 64 i + l on entry; the pass leaves the sequence
+// in s_k / s_v in its new order and, unless `last`, reloads the items from there.
+__device__ __forceinline__ void local_radix_pass(uint32_t (&k)[kSortItems], uint32_t (&v)[kSortItems], int shift,
+                                                 int bits, bool last, uint32_t* s_cnt, uint32_t* s_k,
+                                                 uint32_t* s_v, uint32_t* s_dig, uint32_t* s_wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t radix = 1u << bits, mask = radix - 1u;
+  for (uint32_t i = tid; i < (uint32_t)kSortWaves * kLocalRadix; i += kSortThreads) s_cnt[i] = 0u;
+  __syncthreads();
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t rank[kSortItems];
+#pragma unroll
+  for (int i = 0; i < kSortItems; ++i) {
+    const uint32_t d = (k[i] >> shift) & mask;
+    uint64_t m = ~0ull;
+    for (int b = 0; b < bits; ++b) {
+      const bool bit = (d >> b) & 1u;
+      const uint64_t bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    const uint32_t r = (uint32_t)__popcll(m & lt_mask);
+    const uint32_t pre = s_cnt[wave * kLocalRadix + d];
+    rank[i] = pre + r;
+    asm volatile("" : "+v"(rank[i]));
+    if (r == 0) s_cnt[wave * kLocalRadix + d] = pre + (uint32_t)__popcll(m);
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  uint32_t tot = 0;
+  if ((uint32_t)tid < radix) {
+    for (int w = 0; w < kSortWaves; ++w) {
+      const uint32_t c = s_cnt[w * kLocalRadix + tid];
+      s_cnt[w * kLocalRadix + tid] = tot;
+      tot += c;
+    }
+  }
+  const uint32_t dex = block_excl_scan512((uint32_t)tid < radix ? tot : 0u, s_wsum);
+  if ((uint32_t)tid < radix) s_dig[tid] = dex;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kSortItems; ++i) {
+    const uint32_t d = (k[i] >> shift) & mask;
+    const uint32_t pos = s_dig[d] + s_cnt[wave * kLocalRadix + d] + rank[i];
+    s_k[pos] = k[i];
+    s_v[pos] = v[i];
+  }
+  __syncthreads();
+  if (!last) {
+#pragma unroll
+    for (int i = 0; i < kSortItems; ++i) {
+      const uint32_t e = (uint32_t)(wave * 64 * kSortItems + i * 64 + lane);
+      k[i] = s_k[e];
+      v[i] = s_v[e];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kSortThreads) void k_small_local(SmallArgs sa, TileCountArgs ta) {
+  extern __shared__ uint32_t s_dyn[];
+  __shared__ uint32_t s_dig[kLocalRadix];
+  __shared__ uint32_t s_wsum[kSortWaves];
+  __shared__ uint32_t s_mm[2];
+  uint32_t* s_cnt = s_dyn;
+  uint32_t* s_k = s_cnt + kLocalCnt;
+  uint32_t* s_v = s_k + kSmallBlock;
+  uint32_t* s_tc = s_v + kSmallBlock;
+  uint32_t* s_diff = s_tc + kSmallBlock;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  {
+    const size_t gsz = (size_t)gridDim.x * kSortThreads;
+    for (size_t i = blockIdx.x * (size_t)kSortThreads + tid; i < sa.zero_words; i += gsz) sa.zero[i] = 0u;
+    for (size_t i = blockIdx.x * (size_t)kSortThreads + tid; i < sa.range_words; i += gsz) sa.ranges[i] = 0u;
+  }
+  if (blockIdx.x >= sa.nb) return;  // workgroup-uniform: zeroing only
+  const uint32_t b = blockIdx.x;
+  const uint32_t base = b * (uint32_t)kSmallBlock;
+  const uint32_t len = (uint32_t)sa.n - base < (uint32_t)kSmallBlock ? (uint32_t)sa.n - base : (uint32_t)kSmallBlock;
+  for (uint32_t t = tid; t <= ta.ntiles; t += kSortThreads) s_diff[t] = 0u;
+  if (tid == 0) {
+    s_mm[0] = 0xFFFFFFFFu;
+    s_mm[1] = 0u;
+  }
+  // element e = 256 w + 64 i + l of the block (id base + e)
+  uint32_t key[kSortItems], tc[kSortItems];
+  uint4 rc[kSortItems];
+  float2 m[kSortItems];
+  int2 r[kSortItems];
+  float z[kSortItems];
+#pragma unroll
+  for (int i = 0; i < kSortItems; ++i) {  // all loads in flight before any is used
+    const uint32_t e = (uint32_t)(wave * 64 * kSortItems + i * 64 + lane);
+    const bool valid = e < len;
+    const uint32_t g = base + e;
+    tc[i] = valid ? sa.tiles[g] : 0u;
+    z[i] = valid ? sa.depths[g] : 0.0f;
+    m[i] = valid ? *reinterpret_cast<const float2*>(sa.means2d + 2 * (size_t)g) : make_float2(0.0f, 0.0f);
+    r[i] = valid ? *reinterpret_cast<const int2*>(sa.radii + 2 * (size_t)g) : make_int2(0, 0);
+  }
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < kSortItems; ++i) {
+    const uint32_t e = (uint32_t)(wave * 64 * kSortItems + i * 64 + lane);
+    const bool valid = e < len;
+    key[i] = tc[i] > 0 ? __float_as_uint(z[i]) : 0xFFFFFFFFu;
+    uint32_t tb = 0, w = 1, h = 0;
+    if (tc[i] > 0) {
+      const TileRect rt = tile_rect(m[i].x, m[i].y, (float)r[i].x, (float)r[i].y, sa.tiles_x, sa.tiles_y);
+      tb = (uint32_t)(rt.y0 * sa.tiles_x + rt.x0);
+      w = (uint32_t)(rt.x1 - rt.x0);
+      h = (uint32_t)(rt.y1 - rt.y0);
+      kmin = min(kmin, key[i]);
+      kmax = max(kmax, key[i]);
+    }
+    rc[i] = make_uint4(tc[i], tb, w, h);
+    if (valid) sa.rec[base + e] = rc[i];
+    s_tc[e] = tc[i];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, 64));
+  }
+  __syncthreads();  // s_diff and s_mm initialised
+  if (lane == 0) {
+    atomicMin(&s_mm[0], kmin);
+    atomicMax(&s_mm[1], kmax);
+  }
+  // the block's pairs per tile (rows of rectangles into the difference array)
+#pragma unroll
+  for (int i = 0; i < kSortItems; ++i) {
+    const uint32_t e = (uint32_t)(wave * 64 * kSortItems + i * 64 + lane);
+    tile_rows_item(ta, rc[i], base + e, e < len, s_diff);
+  }
+  __syncthreads();
+  // codes: drawn keys minus the block's smallest, every other element one past the largest, so
+  // that they sort last in element order; only the bits the codes span are sorted
+  uint32_t lo = s_mm[0], hi = s_mm[1];
+  if (lo > hi) lo = hi = 0u;  // nothing drawn in this block
+  const uint32_t vmax = hi - lo + 1u;
+  const int tbits = 32 - __clz((int)vmax);
+  uint32_t code[kSortItems], val[kSortItems];
+#pragma unroll
+  for (int i = 0; i < kSortItems; ++i) {
+    code[i] = key[i] != 0xFFFFFFFFu ? key[i] - lo : vmax;
+    val[i] = (uint32_t)(wave * 64 * kSortItems + i * 64 + lane);
+  }
+  for (int sh = 0; sh < tbits; sh += kLocalBits) {  // workgroup-uniform
+    const int bits = tbits - sh < kLocalBits ? tbits - sh : kLocalBits;
+    local_radix_pass(code, val, sh, bits, sh + kLocalBits >= tbits, s_cnt, s_k, s_v, s_dig, s_wsum);
+  }
+  // the block's row of the difference array
+  for (uint32_t t = tid; t <= ta.ntiles; t += kSortThreads) sa.tmat[(size_t)b * sa.tmat_stride + t] = s_diff[t];
+  // sorted order, four consecutive elements per thread: raw keys, ids, tile-count prefix
+  uint32_t ok[kSortItems], oid[kSortItems], oc[kSortItems];
+  uint32_t own = 0;
+#pragma unroll
+  for (int i = 0; i < kSortItems; ++i) {
+    const uint32_t e = (uint32_t)(tid * kSortItems + i);
+    const uint32_t c = s_k[e], lv = s_v[e];
+    ok[i] = c == vmax ? 0xFFFFFFFFu : c + lo;
+    oid[i] = base + lv;
+    oc[i] = s_tc[lv];
+    own += oc[i];
+  }
+  uint32_t total;
+  uint32_t run = block_excl_scan1024<uint32_t>(own, s_wsum, &total);
+  uint4 pre;
+  pre.x = run;
+  pre.y = pre.x + oc[0];
+  pre.z = pre.y + oc[1];
+  pre.w = pre.z + oc[2];
+  const size_t o4 = (size_t)b * (kSmallBlock / 4) + tid;
+  reinterpret_cast<uint4*>(sa.skey)[o4] = make_uint4(ok[0], ok[1], ok[2], ok[3]);
+  reinterpret_cast<uint4*>(sa.sid)[o4] = make_uint4(oid[0], oid[1], oid[2], oid[3]);
+  reinterpret_cast<uint4*>(sa.cpre)[o4] = pre;
+  if (tid == 0) sa.btot[b] = total;
+}
+
+// Merge ranks. Workgroup b < nb takes block b's elements, four consecutive per thread; workgroup
+// nb is the tile-count finalizer. Dynamic LDS: max(nb 4096, the finalizer's) words.
+__global__ __launch_bounds__(kSortThreads) void k_small_merge(SmallArgs sa, uint4* __restrict__ drec,
+                                                              uint32_t* __restrict__ chunk_first, uint64_t capacity,
+                                                              Ctrl* ctrl, int64_t* __restrict__ user_num_pairs,
+                                                              uint32_t lds_words, TileCountArgs ta) {
+  extern __shared__ uint32_t s_dyn[];
+  const int tid = threadIdx.x;
+  const uint32_t nb = sa.nb;
+  if (blockIdx.x == nb) {  // workgroup-uniform
+    tile_finalize(ta, s_dyn, lds_words);
+    return;
+  }
+  const uint32_t b = blockIdx.x;
+  for (uint32_t q = tid; q < nb * (kSmallBlock / 4); q += kSortThreads)
+    reinterpret_cast<uint4*>(s_dyn)[q] = reinterpret_cast<const uint4*>(sa.skey)[q];
+  if (b == 0 && tid == 0) {  // P: the sum of the block totals
+    uint64_t P = 0;
+    for (uint32_t j = 0; j < nb; ++j) P += sa.btot[j];
+    ctrl->num_pairs = P;
+    ctrl->eff_pairs = P <= capacity ? P : 0u;
+    if (user_num_pairs) *user_num_pairs = (int64_t)P;
+  }
+  __syncthreads();
+  const uint32_t len_b = (uint32_t)sa.n - b * kSmallBlock < (uint32_t)kSmallBlock ? (uint32_t)sa.n - b * kSmallBlock
+                                                                                   : (uint32_t)kSmallBlock;
+#pragma unroll 1
+  for (int i = 0; i < kSortItems; ++i) {
+    const uint32_t e = (uint32_t)(tid * kSortItems + i);
+    if (e >= len_b) break;
+    const uint32_t key = s_dyn[b * kSmallBlock + e];
+    uint32_t rank = e;
+    uint64_t off = sa.cpre[(size_t)b * kSmallBlock + e];
+    for (uint32_t b2 = 0; b2 < nb; ++b2) {
+      if (b2 == b) continue;
+      const uint32_t len2 =
+          (uint32_t)sa.n - b2 * kSmallBlock < (uint32_t)kSmallBlock ? (uint32_t)sa.n - b2 * kSmallBlock : kSmallBlock;
+      const uint32_t* kk = s_dyn + b2 * kSmallBlock;
+      // the number of block b2's keys that come before this one: <= key for an earlier block
+      // (equal keys there have smaller ids), < key for a later one
+      uint32_t pos = 0;
+#pragma unroll
+      for (uint32_t step = kSmallBlock; step > 0; step >>= 1) {
+        if (pos + step <= len2) {
+          const uint32_t x = kk[pos + step - 1];
+          if (b2 < b ? x <= key : x < key) pos += step;
+        }
+      }
+      rank += pos;
+      off += pos < len2 ? sa.cpre[(size_t)b2 * kSmallBlock + pos] : sa.btot[b2];
+    }
+    const uint32_t g = sa.sid[(size_t)b * kSmallBlock + e];
+    const uint4 r = sa.rec[g];
+    drec[rank] = make_uint4(off < 0xFFFFFFFFull ? (uint32_t)off : 0xFFFFFFFFu, r.y, r.z, g);
+    const uint64_t end = off + r.x;
+    for (uint64_t c = (off + kEmitChunk - 1) / kEmitChunk * kEmitChunk; c < end && c < capacity; c += kEmitChunk)
+      chunk_first[c / kEmitChunk] = rank;
+  }
+}
+
 // The raster plan of a frame without pairs: natural tile order, no extra work items or checkpoints.
 __global__ void k_empty_plan(uint32_t* __restrict__ plan, uint32_t ntiles) {
   const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -1090,10 +1413,14 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, size_t count, uint32_t v) {
 // workspace layout: [ctrl | scan look-back | depth look-back | pair look-back] are zeroed by
 // k_bin_prep; the rest is written before it is read
 // ---------------------------------------------------------------------------------------------
+// [ctrl | pair look-back] is what the small-frame path zeroes, [ctrl .. zero_end) what the radix
+// path zeroes
 struct BinLayout {
-  size_t ctrl, scan_status, dstatus, pstatus, tdiff, zero_end;
-  size_t dhist, dkA, dvA, dkB, dvB, rec, drec, chunk_first, pkB, pvB, total;
-  uint32_t nbN, nbS, nbCap, nbEmit;
+  size_t ctrl, pstatus, small_zero_end, scan_status, dstatus, tdiff, zero_end;
+  size_t dhist, dkA, dvA, dkB, dvB, rec, drec, chunk_first, pkB, pvB;
+  size_t skey, sid, cpre, btot, tmat, total;
+  uint32_t nbN, nbS, nbCap, nbEmit, nbSmall, tmat_stride;
+  bool small;
   int tile_bits, npass, pshift[3], pbits[3];
 };
 
@@ -1122,10 +1449,15 @@ BinLayout bin_layout(int32_t n, int64_t cap, const gs_camera* cam) {
     off = align_up(off + bytes, A);
     return at;
   };
+  // small frames: every key in one workgroup's LDS, a block's difference array in LDS
+  L.small = n <= kSmallMaxN && ntiles <= (int64_t)kSmallMaxTiles;
+  L.nbSmall = L.small ? (uint32_t)((n + kSmallBlock - 1) / kSmallBlock) : 0u;
+  L.tmat_stride = (uint32_t)align_up((size_t)ntiles + 1, 64);
   L.ctrl = take(sizeof(Ctrl));
+  L.pstatus = take((size_t)L.npass * L.nbCap * kRadix * 4);
+  L.small_zero_end = off;
   L.scan_status = take((size_t)L.nbS * 8);
   L.dstatus = take((size_t)4 * L.nbN * kRadix * 4);
-  L.pstatus = take((size_t)L.npass * L.nbCap * kRadix * 4);
   L.tdiff = take(((size_t)ntiles + 1) * 4);
   L.zero_end = off;
   L.dhist = take((size_t)L.nbN * 4 * kRadix * 4);
@@ -1138,6 +1470,11 @@ BinLayout bin_layout(int32_t n, int64_t cap, const gs_camera* cam) {
   L.chunk_first = take((size_t)L.nbEmit * 4);
   L.pkB = take((size_t)cap * 4);
   L.pvB = take((size_t)cap * 4);
+  L.skey = take((size_t)L.nbSmall * kSmallBlock * 4);
+  L.sid = take((size_t)L.nbSmall * kSmallBlock * 4);
+  L.cpre = take((size_t)L.nbSmall * kSmallBlock * 4);
+  L.btot = take((size_t)L.nbSmall * 4);
+  L.tmat = take((size_t)L.nbSmall * L.tmat_stride * 4);
   L.total = off;
   return L;
 }
@@ -1158,10 +1495,33 @@ extern "C" size_t gs_bin_workspace_bytes(int32_t n, int64_t pair_capacity, const
   return bin_layout(n, pair_capacity, cam).total;
 }
 
-extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const gs_camera* cam, void* d_workspace,
-                                     size_t workspace_bytes, int64_t pair_capacity, uint64_t* d_keys,
-                                     uint32_t* d_ids, uint32_t* d_tile_ranges, uint32_t* d_raster_plan,
-                                     int64_t* d_num_pairs, int64_t* h_num_pairs, void* stream) {
+namespace {
+// The small-frame kernels take up to 144 KB of dynamic LDS: raise their limit (64 KB by default)
+// once per device.
+constexpr size_t kSmallLdsBytes = (size_t)(kLocalFixedWords + kSmallMaxTiles + 1) * 4;
+static_assert((size_t)kSmallMaxBlocks * kSmallBlock * 4 <= kSmallLdsBytes, "merge keys exceed the LDS limit set");
+static_assert(kSmallLdsBytes + 4 * (kLocalRadix + kSortWaves + 2) <= 160 * 1024, "LDS of a compute unit");
+std::mutex g_lds_mu;
+bool g_lds_set[64] = {};
+gs_status raise_small_lds_limits() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return set_error(GS_ERR_DEVICE, "gs_bin_and_sort: no current device");
+  std::lock_guard<std::mutex> lock(g_lds_mu);
+  if (g_lds_set[dev]) return GS_OK;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(k_small_local), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)kSmallLdsBytes) != hipSuccess ||
+      hipFuncSetAttribute(reinterpret_cast<const void*>(k_small_merge), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)kSmallLdsBytes) != hipSuccess)
+    return check_launch("gs_bin_and_sort: raising the LDS limit");
+  g_lds_set[dev] = true;
+  return GS_OK;
+}
+
+gs_status bin_and_sort(int32_t n, const gs_projected* proj, const gs_camera* cam, void* d_workspace,
+                       size_t workspace_bytes, int64_t pair_capacity, uint64_t* d_keys, uint32_t* d_ids,
+                       uint32_t* d_tile_ranges, uint32_t* d_raster_plan, int64_t* d_num_pairs, int64_t* h_num_pairs,
+                       void* stream) {
   std::string why;
   if (n < 0) return set_error(GS_ERR_INVALID_ARG, "gs_bin_and_sort: n < 0");
   if (!valid_camera(cam, &why)) return set_error(GS_ERR_INVALID_ARG, "gs_bin_and_sort: " + why);
@@ -1202,8 +1562,79 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
   uint64_t* scan_status = (uint64_t*)(ws + L.scan_status);
   uint32_t* dstatus = (uint32_t*)(ws + L.dstatus);
   uint32_t* pstatus = (uint32_t*)(ws + L.pstatus);
-  const size_t zero_words = (L.zero_end - L.ctrl) / 4;
   const int32_t tiles_x = (cam->width + 15) / 16, tiles_y = (cam->height + 15) / 16;
+  // the tile-count arguments: extra workgroups count the pairs of every tile and finalize them
+  TileCountArgs targs;
+  targs.rec = (const uint4*)(ws + L.rec);
+  targs.means2d = proj->d_means2d;
+  targs.conics = proj->d_conics;
+  targs.opac = proj->d_opacities;
+  targs.tight = cam->tight_tiles;
+  targs.n = n;
+  targs.tiles_x = tiles_x;
+  targs.ntiles = (uint32_t)ntiles;
+  targs.tdiff = (uint32_t*)(ws + L.tdiff);
+  targs.ranges = d_tile_ranges;
+  targs.plan = d_raster_plan;
+  targs.capacity = (uint64_t)pair_capacity;
+  targs.npass = L.npass;
+  for (int p = 0; p < 3; ++p) {
+    targs.pshift[p] = p < L.npass ? L.pshift[p] : 0;
+    targs.pbits[p] = p < L.npass ? L.pbits[p] : 0;
+  }
+  targs.hist_pair = &ctrl->hist_pair[0][0];
+  targs.tmat = nullptr;
+  targs.tmat_rows = 0;
+  targs.tmat_stride = 0;
+  // ping-pong of the pair sort: A = d_keys viewed as two u32 arrays of pair_capacity, B = workspace.
+  // The last pass writes the 64-bit keys over A, so it reads B: pass p writes B when
+  // npass - 2 - p is even, A otherwise.
+  uint32_t* kA = (uint32_t*)d_keys;
+  uint32_t* vA = kA ? kA + pair_capacity : nullptr;
+  uint32_t *kB = (uint32_t*)(ws + L.pkB), *vB = (uint32_t*)(ws + L.pvB);
+  if (L.small) {
+    SmallArgs sa;
+    sa.n = n;
+    sa.nb = L.nbSmall;
+    sa.depths = proj->d_depths;
+    sa.tiles = proj->d_tiles_touched;
+    sa.means2d = proj->d_means2d;
+    sa.radii = proj->d_radii;
+    sa.tiles_x = tiles_x;
+    sa.tiles_y = tiles_y;
+    sa.rec = (uint4*)(ws + L.rec);
+    sa.skey = (uint32_t*)(ws + L.skey);
+    sa.sid = (uint32_t*)(ws + L.sid);
+    sa.cpre = (uint32_t*)(ws + L.cpre);
+    sa.btot = (uint32_t*)(ws + L.btot);
+    sa.tmat = (uint32_t*)(ws + L.tmat);
+    sa.tmat_stride = L.tmat_stride;
+    sa.zero = (uint32_t*)(ws + L.ctrl);
+    sa.zero_words = (L.small_zero_end - L.ctrl) / 4;
+    sa.ranges = d_tile_ranges;
+    sa.range_words = (size_t)(2 * ntiles);
+    const size_t zwords = sa.zero_words + sa.range_words;
+    const size_t zblocks = (zwords + 16 * kSortThreads - 1) / (16 * kSortThreads);
+    const unsigned blocks = (unsigned)std::max<size_t>(L.nbSmall, std::min<size_t>(zblocks, 1024));
+    const size_t lds_local = ((size_t)kLocalFixedWords + (size_t)ntiles + 1) * 4;
+    const uint32_t merge_words = std::max<uint32_t>(L.nbSmall * kSmallBlock, kFinStep + kFinAuxWords);
+    const gs_status lst = raise_small_lds_limits();
+    if (lst != GS_OK) return lst;
+    {
+      TimedScope ts("small_local", s);
+      hipLaunchKernelGGL(k_small_local, dim3(blocks), dim3(kSortThreads), lds_local, s, sa, targs);
+    }
+    targs.tmat = sa.tmat;
+    targs.tmat_rows = L.nbSmall;
+    targs.tmat_stride = L.tmat_stride;
+    {
+      TimedScope ts("small_merge", s);
+      hipLaunchKernelGGL(k_small_merge, dim3(L.nbSmall + 1), dim3(kSortThreads), (size_t)merge_words * 4, s, sa,
+                         (uint4*)(ws + L.drec), (uint32_t*)(ws + L.chunk_first), (uint64_t)pair_capacity, ctrl,
+                         d_num_pairs, merge_words, targs);
+    }
+  } else {
+  const size_t zero_words = (L.zero_end - L.ctrl) / 4;
   {
     // enough workgroups for the depth keys, and for zeroing about 32 words per thread
     const size_t zwords = zero_words + (size_t)(2 * ntiles);
@@ -1224,25 +1655,6 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
                        L.nbN, ctrl);
   }
   // pass 0 carries the tile-row workgroups, pass 1 the tile-count finalizer
-  TileCountArgs targs;
-  targs.rec = (const uint4*)(ws + L.rec);
-  targs.means2d = proj->d_means2d;
-  targs.conics = proj->d_conics;
-  targs.opac = proj->d_opacities;
-  targs.tight = cam->tight_tiles;
-  targs.n = n;
-  targs.tiles_x = tiles_x;
-  targs.ntiles = (uint32_t)ntiles;
-  targs.tdiff = (uint32_t*)(ws + L.tdiff);
-  targs.ranges = d_tile_ranges;
-  targs.plan = d_raster_plan;
-  targs.capacity = (uint64_t)pair_capacity;
-  targs.npass = L.npass;
-  for (int p = 0; p < 3; ++p) {
-    targs.pshift[p] = p < L.npass ? L.pshift[p] : 0;
-    targs.pbits[p] = p < L.npass ? L.pbits[p] : 0;
-  }
-  targs.hist_pair = &ctrl->hist_pair[0][0];
   const uint32_t n_rows = (uint32_t)((n + kRowGaussians - 1) / kRowGaussians);
   for (int p = 0; p < 4; ++p) {
     const bool even = (p % 2) == 0;
@@ -1255,17 +1667,12 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
                        (uint32_t)n, (const uint64_t*)nullptr, 8 * p, 8, hist, direct_hist ? (int)L.nbN : 1,
                        4 * kRadix, dstatus + (size_t)p * L.nbN * kRadix, &ctrl->tickets[p], n_extra, targs);
   }
-  // ping-pong of the pair sort: A = d_keys viewed as two u32 arrays of pair_capacity, B = workspace.
-  // The last pass writes the 64-bit keys over A, so it reads B: pass p writes B when
-  // npass - 2 - p is even, A otherwise.
-  uint32_t* kA = (uint32_t*)d_keys;
-  uint32_t* vA = kA ? kA + pair_capacity : nullptr;
-  uint32_t *kB = (uint32_t*)(ws + L.pkB), *vB = (uint32_t*)(ws + L.pvB);
   {
     TimedScope ts("scan", s);
     hipLaunchKernelGGL(k_scan, dim3(L.nbS), dim3(kEmitThreads), 0, s, n, dvA, (const uint4*)(ws + L.rec),
                        (uint4*)(ws + L.drec), (uint32_t*)(ws + L.chunk_first), (uint64_t)pair_capacity, scan_status,
                        ctrl, d_num_pairs);
+  }
   }
   if (L.nbCap > 0) {
     auto out_A = [&](int p) { return ((L.npass - 2 - p) % 2) != 0; };
@@ -1312,4 +1719,13 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
     return set_error(GS_ERR_CAPACITY, "gs_bin_and_sort: " + std::to_string(P) + " pairs exceed the capacity " +
                                           std::to_string(pair_capacity));
   return GS_OK;
+}
+}  // namespace
+
+extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const gs_camera* cam, void* d_workspace,
+                                     size_t workspace_bytes, int64_t pair_capacity, uint64_t* d_keys,
+                                     uint32_t* d_ids, uint32_t* d_tile_ranges, uint32_t* d_raster_plan,
+                                     int64_t* d_num_pairs, int64_t* h_num_pairs, void* stream) {
+  return bin_and_sort(n, proj, cam, d_workspace, workspace_bytes, pair_capacity, d_keys, d_ids, d_tile_ranges,
+                      d_raster_plan, d_num_pairs, h_num_pairs, stream);
 }

@@ -467,6 +467,25 @@ def test_many_tiles(env, width, height):
     _pipeline_case(env, sc, cam, pixels=pix, label=f"tiles {width}x{height}")
 
 
+@pytest.mark.parametrize("n,tight", [(4096, False), (4097, True), (20000, False), (36864, False), (36864, True),
+                                     (36865, False)])
+def test_depth_order_block_sizes_ties_and_culled(env, n, tight):
+    """Frames of at most 36,864 Gaussians take their depth order from sorted blocks of 4096 and
+    merge ranks, larger ones from the radix passes: sizes at and across the block and path
+    boundaries, a third of the Gaussians at one exactly equal depth (stable: ascending id), a tenth
+    behind the camera and some fully transparent (not drawn, no pairs)."""
+    sc = synth.random_scene(n, seed=n, width=640, height=360, focal=400.0, log_scales=(-4.5, -2.5))
+    rng = np.random.default_rng(n + 1)
+    sc["means"][rng.random(n) < 0.33, 2] = 3.25
+    sc["means"][rng.random(n) < 0.1, 2] = -1.0
+    sc["opacity_logits"][rng.random(n) < 0.05] = -30.0
+    cam = synth.make_camera(np.eye(4), 640, 360, 400.0)
+    if tight:
+        cam["tight_tiles"] = True
+    pix = synth.sample_pixels(640, 360, 4096, seed=3)
+    _pipeline_case(env, sc, cam, pixels=pix, label=f"blocks n={n} tight={tight}")
+
+
 def test_opacity_extremes(env):
     sc = synth.random_scene(200, seed=8, width=48, height=48, focal=50.0)
     sc["opacity_logits"][:40] = 30.0
