@@ -37,35 +37,58 @@ constexpr int kBatch = kRasterThreads;         // splats staged per batch
 static_assert(kPlanMinChunk % kBatch == 0, "chunk boundaries must fall on batch starts");
 
 // Staged splat record: (mx, my, hA, hC), (B2, o, r, g), b. hA = A/2 log2e, B2 = B log2e,
-// hC = C/2 log2e, so that log2(e) sigma = hA dx^2 + hC dy^2 + B2 dx dy. Also returns the 4-bit
-// set of 8x8 quadrants of the tile where the splat can reach alpha >= 1/255 at some pixel
+// hC = C/2 log2e, so that log2(e) sigma = hA dx^2 + hC dy^2 + B2 dx dy. Staging also returns the
+// 4-bit set of 8x8 quadrants of the tile where the splat can reach alpha >= 1/255 at some pixel
 // centre (its ellipse at that level meets the quadrant); elsewhere it skips at every pixel.
 // The test uses the splat alone, not its radii, so it holds for every radius rule.
-// An id >= n (impossible for a well-formed sorted list) loads a record that never contributes.
-__device__ __forceinline__ uint32_t load_record(uint32_t g, uint32_t n, const float* __restrict__ means2d,
-                                                const float* __restrict__ conics, const float* __restrict__ opac,
-                                                const float* __restrict__ colors, const int32_t* __restrict__ radii,
-                                                float tx0, float ty0, float4& a, float4& b, float& c) {
-  if (g >= n) {
-    a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    b = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    c = 0.0f;
-    return 0u;
+// An id >= n (impossible for a well-formed sorted list) stages a record that never contributes.
+//
+// The raw record of one splat is loaded into registers first (in the blend a batch ahead of its
+// staging, so that its loads are in flight while the previous batch is walked).
+struct RawSplat {
+  float2 m;
+  float A, B, C, o, r, g, b, z;
+};
+template <bool DEPTH>
+__device__ __forceinline__ RawSplat load_raw(uint32_t g, uint32_t n, const float* __restrict__ means2d,
+                                             const float* __restrict__ conics, const float* __restrict__ opac,
+                                             const float* __restrict__ colors, const float* __restrict__ depths) {
+  RawSplat s;
+  if (g >= n) {  // past the list, or an id that cannot be: zero opacity, never contributes
+    s.m = make_float2(0.0f, 0.0f);
+    s.B = s.o = s.r = s.g = s.b = s.z = 0.0f;
+    s.A = s.C = 1.0f;
+    return s;
   }
-  const float2 m = *reinterpret_cast<const float2*>(means2d + 2 * g);
-  const float A = conics[3 * g], B = conics[3 * g + 1], C = conics[3 * g + 2];
-  a = make_float4(m.x, m.y, (0.5f * kLog2e) * A, (0.5f * kLog2e) * C);
-  b = make_float4(kLog2e * B, opac[g], colors[3 * g], colors[3 * g + 1]);
-  c = colors[3 * g + 2];
-  // Exact test of the splat's ellipse against each quadrant: the minimum over the quadrant's box
-  // of pixel centres of s2 = log2(e) sigma (a positive definite quadratic in the offset, so the
-  // minimum is 0 inside the box and otherwise lies on an edge, where it is a 1D quadratic) must
-  // not exceed log2(255 o), else alpha < 1/255 at every pixel centre of the quadrant. The slack
-  // (0.02 + 4e-6 times the size of the quadratic's terms over the tile) is far above the fp32
-  // rounding of both this bound and the evaluation's s2, so no contributing splat is dropped.
+  s.m = *reinterpret_cast<const float2*>(means2d + 2 * g);
+  s.A = conics[3 * g];
+  s.B = conics[3 * g + 1];
+  s.C = conics[3 * g + 2];
+  s.o = opac[g];
+  s.r = colors[3 * g];
+  s.g = colors[3 * g + 1];
+  s.b = colors[3 * g + 2];
+  s.z = DEPTH ? depths[g] : 0.0f;
+  return s;
+}
+
+// Stages a raw record: the pre-scaled LDS record (a, b, c) and the quadrant mask (0 when not
+// valid). Exact test of the splat's ellipse against each quadrant: the minimum over the
+// quadrant's box of pixel centres of s2 = log2(e) sigma (a positive definite quadratic in the
+// offset, so the minimum is 0 inside the box and otherwise lies on an edge, where it is a 1D
+// quadratic) must not exceed log2(255 o), else alpha < 1/255 at every pixel centre of the
+// quadrant. The slack (0.02 + 4e-6 times the size of the quadratic's terms over the tile) is far
+// above the fp32 rounding of both this bound and the evaluation's s2, so no contributing splat is
+// dropped.
+__device__ __forceinline__ uint32_t stage_raw(const RawSplat& rs, bool valid, float tx0, float ty0, float4& a,
+                                              float4& b, float& c) {
+  a = make_float4(rs.m.x, rs.m.y, (0.5f * kLog2e) * rs.A, (0.5f * kLog2e) * rs.C);
+  b = make_float4(kLog2e * rs.B, rs.o, rs.r, rs.g);
+  c = rs.b;
+  if (!valid) return 0u;
   const float qa = a.z, qb = b.x, qc = a.w;  // hA, B2, hC
   const float ia = 0.5f / qa, ic = 0.5f / qc;
-  const float ex0 = tx0 + 0.5f - m.x, ey0 = ty0 + 0.5f - m.y;  // offsets of the tile's first centre
+  const float ex0 = tx0 + 0.5f - rs.m.x, ey0 = ty0 + 0.5f - rs.m.y;  // offsets of the tile's first centre
   const float X = fmaxf(fabsf(ex0), fabsf(ex0 + 15.0f)), Y = fmaxf(fabsf(ey0), fabsf(ey0 + 15.0f));
   const float terms = fmaf(qa * X, X, fmaf(fabsf(qb) * X, Y, (qc * Y) * Y));
   const float lim = __log2f(255.0f * b.y) + fmaf(4e-6f, terms, 0.02f);
@@ -74,7 +97,7 @@ __device__ __forceinline__ uint32_t load_record(uint32_t g, uint32_t n, const fl
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const float x_lo = tx0 + (float)((q & 1) * 8) + 0.5f, y_lo = ty0 + (float)((q >> 1) * 8) + 0.5f;
-    const float x0 = x_lo - m.x, x1 = x0 + 7.0f, y0 = y_lo - m.y, y1 = y0 + 7.0f;
+    const float x0 = x_lo - rs.m.x, x1 = x0 + 7.0f, y0 = y_lo - rs.m.y, y1 = y0 + 7.0f;
     // on the edge x = e the minimiser is y = -B2 e / (2 hC), clamped; likewise on y = e
     const float s_l = q2(x0, fminf(fmaxf(-qb * x0 * ic, y0), y1));
     const float s_r = q2(x1, fminf(fmaxf(-qb * x1 * ic, y0), y1));
@@ -85,6 +108,15 @@ __device__ __forceinline__ uint32_t load_record(uint32_t g, uint32_t n, const fl
     qm |= hit ? (1u << q) : 0u;
   }
   return qm;
+}
+
+// Loads and stages one splat at once (the backward's staging).
+__device__ __forceinline__ uint32_t load_record(uint32_t g, uint32_t n, const float* __restrict__ means2d,
+                                                const float* __restrict__ conics, const float* __restrict__ opac,
+                                                const float* __restrict__ colors, float tx0, float ty0, float4& a,
+                                                float4& b, float& c) {
+  const RawSplat rs = load_raw<false>(g, n, means2d, conics, opac, colors, nullptr);
+  return stage_raw(rs, g < n, tx0, ty0, a, b, c);
 }
 
 // Sum over the 64 lanes of a wave with DPP; the total lands in lane 63 (other lanes hold partial
@@ -239,17 +271,23 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
     next_b += L;
     if (next_b >= len) next_b = 0xFFFFFFFFu;
   };
+  // Software pipeline over the batches: while batch k is walked, this thread's record of batch
+  // k + 1 is being loaded into registers and its id of batch k + 2 too, so neither the id load
+  // nor the record gather waits at a batch start.
+  uint32_t id_next2 = start + kBatch + tid < end ? ids[start + kBatch + tid] : n;
+  RawSplat raw = load_raw<DEPTH>(start + tid < end ? ids[start + tid] : n, n, means2d, conics, opac, colors, depths);
   for (uint32_t bs = start; bs < end; bs += kBatch) {
     if (__syncthreads_count(done) == kRasterThreads) break;
     if (CKPT && bs - start >= next_b) store_ckpt();  // workgroup-uniform
-    const uint32_t j = bs + tid;
-    uint32_t qm = 0;
-    if (j < end) {
-      const uint32_t g = ids[j];
-      qm = load_record(g, n, means2d, conics, opac, colors, radii, tx0, ty0, s_a[tid], s_b[tid], s_c[tid]);
-      if (DEPTH) s_z[tid] = g < n ? depths[g] : 0.0f;
+    const bool valid = bs + tid < end;
+    const uint32_t qm = stage_raw(raw, valid, tx0, ty0, s_a[tid], s_b[tid], s_c[tid]);
+    if (DEPTH) s_z[tid] = raw.z;
+    publish_quadrant_masks(qm, valid, s_qm);
+    {
+      const uint32_t j2 = bs + 2 * kBatch + tid;
+      raw = load_raw<DEPTH>(id_next2, n, means2d, conics, opac, colors, depths);
+      id_next2 = j2 < end ? ids[j2] : n;
     }
-    publish_quadrant_masks(qm, j < end, s_qm);
     __syncthreads();
     const uint32_t list1 = bs - start + 1u;  // 1-based list index of staged splat 0
     for (int w = 0; w < 4; ++w) {
@@ -555,7 +593,7 @@ __global__ __launch_bounds__(kRasterThreads) __attribute__((amdgpu_waves_per_eu(
     if (tid < cnt) {
       const uint32_t g = ids[start + bstart + (uint32_t)tid];
       s_id[tid] = g;
-      qm = load_record(g, n, means2d, conics, opac, colors, radii, tx0, ty0, s_a[tid], s_b[tid], s_c[tid]);
+      qm = load_record(g, n, means2d, conics, opac, colors, tx0, ty0, s_a[tid], s_b[tid], s_c[tid]);
       if (DEPTH) s_z[tid] = g < n ? depths[g] : 0.0f;
       if (g < n) {
         rA = conics[3 * g];
