@@ -65,7 +65,7 @@ def load():
         getattr(lib, name).argtypes = [i32] + [P] * 7 + [i32, i32, i32, P, i64, P, f64] + [P] * 7
         getattr(lib, name).restype = ctypes.c_int
     for name in ("orc_render_bwd_f32", "orc_render_bwd_f64"):
-        getattr(lib, name).argtypes = [i32] + [P] * 7 + [i32, i32, i32, P, i64, P, f64, P, P, P, P]
+        getattr(lib, name).argtypes = [i32] + [P] * 7 + [i32, i32, i32, P, i64, P, f64, P, P, P, P, P]
         getattr(lib, name).restype = ctypes.c_int
     for name in ("orc_project_bwd_f32", "orc_project_bwd_f64"):
         getattr(lib, name).argtypes = [i32, i32] + [P] * 6 + [i32, i32] + [P] * 8
@@ -278,8 +278,8 @@ def render_backward(proj, cam, dL_dimage, pixels=None, dtype=np.float32, band_ep
     Returns (g2d [N,10] float64, aref [N,10] float64): per Gaussian d/d(mu'x, mu'y, A, B, C,
     opacity, r, g, b, depth) and the rounding scale of each (sum over pixels of the magnitudes of
     the terms each contribution is computed from, widened where the transmittance recovery loses
-    digits). With plain_floor=True a third array [N,10] follows: the sum over pixels of the
-    absolute per-pixel contribution, with no widening.
+    digits). With plain_floor=True two more arrays [N,10] follow: the sum over pixels of the
+    absolute per-pixel contribution, and the term magnitudes without the widening.
     """
     lib = load()
     if band_eps is None:
@@ -299,10 +299,11 @@ def render_backward(proj, cam, dL_dimage, pixels=None, dtype=np.float32, band_ep
     g2d = np.empty((n, 10))
     aref = np.empty((n, 10))
     aplain = np.empty((n, 10)) if plain_floor else None
+    aterms = np.empty((n, 10)) if plain_floor else None
     fn = getattr(lib, "orc_render_bwd_" + _suffix(dtype))
     fn(n, *[_p(a) for a in ins], _tight(cam), W, H, _p(bg), M, _p(pix), float(band_eps), _p(g), _p(gd), _p(g2d),
-       _p(aref), _p(aplain))
-    return (g2d, aref, aplain) if plain_floor else (g2d, aref)
+       _p(aref), _p(aplain), _p(aterms))
+    return (g2d, aref, aplain, aterms) if plain_floor else (g2d, aref)
 
 
 def _pad10(a, n):

@@ -680,6 +680,7 @@ int render_impl(int n, const T* means2d, const T* conics, const T* opac, const T
 // Output per Gaussian (10): d mu'_x, d mu'_y, dA, dB, dC, d opacity, d colour (3), d depth,
 // accumulated in double. Two rounding scales of each sum, for tolerance floors:
 //   aref_plain: the sum over pixels of the absolute per-pixel contribution |dC_p/d.| (may be NULL);
+//   aref_terms: aref without the widening by the transmittance's rounding bound (may be NULL);
 //   aref: per pixel, the absolute values of the terms each contribution is computed from (|c| T +
 //     |S| / (1 - a) for dC/da, which cancels when a splat's colour matches what lies behind it),
 //     times max(1, e_T / 1e-5) with e_T the pixel's bound on the relative rounding of its
@@ -689,22 +690,24 @@ int render_bwd_impl(int n, const T* means2d, const T* conics, const T* opac, con
                     const T* depths, const uint32_t* tiles, const int32_t* rects, int tight, int W, int H,
                     const T* bg, int64_t npix, const int32_t* pix, double band_eps,
                     const double* dL_dimg, const double* dL_ddepth, double* g2d, double* aref,
-                    double* aref_plain) {
+                    double* aref_plain, double* aref_terms) {
   std::vector<Splat2D<T>> S;
   std::vector<int> order;
   build_splats<T>(n, means2d, conics, opac, colors, depths, tiles, rects, tight, S, order);
   if (!pix) npix = (int64_t)W * H;
   const int nt = nthreads();
-  std::vector<std::vector<double>> accg(nt), acca(nt), accp(nt);
+  std::vector<std::vector<double>> accg(nt), acca(nt), accp(nt), acct(nt);
 #pragma omp parallel
   {
     const int tid = thread_id();
     accg[tid].assign((size_t)n * 10, 0.0);
     acca[tid].assign((size_t)n * 10, 0.0);
     accp[tid].assign((size_t)n * 10, 0.0);
+    acct[tid].assign((size_t)n * 10, 0.0);
     double* G = accg[tid].data();
     double* Aa = acca[tid].data();
     double* Ap = accp[tid].data();
+    double* At = acct[tid].data();
     Trace tr;
     std::vector<double> al, Ti, Gi;
 #pragma omp for schedule(dynamic, 16)
@@ -761,6 +764,7 @@ int render_bwd_impl(int n, const T* means2d, const T* conics, const T* opac, con
           G[(size_t)g * 10 + k] += contrib[k];
           Aa[(size_t)g * 10 + k] += mag[k] * tscale;
           Ap[(size_t)g * 10 + k] += std::fabs(contrib[k]);
+          At[(size_t)g * 10 + k] += mag[k];
         }
         for (int ch = 0; ch < 3; ++ch) {
           Sacc[ch] += c[ch] * al[i] * Ti[i];
@@ -772,15 +776,17 @@ int render_bwd_impl(int n, const T* means2d, const T* conics, const T* opac, con
     }
   }
   for (size_t i = 0; i < (size_t)n * 10; ++i) {
-    double sg = 0, sa = 0, sp = 0;
+    double sg = 0, sa = 0, sp = 0, st = 0;
     for (int t = 0; t < nt; ++t) {
       sg += accg[t][i];
       sa += acca[t][i];
       sp += accp[t][i];
+      st += acct[t][i];
     }
     g2d[i] = sg;
     if (aref) aref[i] = sa;
     if (aref_plain) aref_plain[i] = sp;
+    if (aref_terms) aref_terms[i] = st;
   }
   return 0;
 }
@@ -1145,17 +1151,17 @@ int orc_render_bwd_f32(int n, const float* means2d, const float* conics, const f
                        const float* depths, const uint32_t* tiles, const int32_t* rects, int tight, int W,
                        int H, const float* bg, int64_t npix, const int32_t* pix, double band_eps,
                        const double* dL_dimg, const double* dL_ddepth, double* g2d, double* aref,
-                       double* aref_plain) {
+                       double* aref_plain, double* aref_terms) {
   return render_bwd_impl<float>(n, means2d, conics, opac, colors, depths, tiles, rects, tight, W, H, bg, npix, pix,
-                                band_eps, dL_dimg, dL_ddepth, g2d, aref, aref_plain);
+                                band_eps, dL_dimg, dL_ddepth, g2d, aref, aref_plain, aref_terms);
 }
 int orc_render_bwd_f64(int n, const double* means2d, const double* conics, const double* opac,
                        const double* colors, const double* depths, const uint32_t* tiles, const int32_t* rects,
                        int tight, int W, int H, const double* bg, int64_t npix, const int32_t* pix, double band_eps,
                        const double* dL_dimg, const double* dL_ddepth, double* g2d, double* aref,
-                       double* aref_plain) {
+                       double* aref_plain, double* aref_terms) {
   return render_bwd_impl<double>(n, means2d, conics, opac, colors, depths, tiles, rects, tight, W, H, bg, npix, pix,
-                                 band_eps, dL_dimg, dL_ddepth, g2d, aref, aref_plain);
+                                 band_eps, dL_dimg, dL_ddepth, g2d, aref, aref_plain, aref_terms);
 }
 
 int orc_project_bwd_f32(int n, int sh_degree, const float* means, const float* log_scales, const float* quats,

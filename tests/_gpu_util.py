@@ -146,10 +146,11 @@ def oracle_grads(scene, cam, o_proj, dL_dimage, pixels=None, dL_ddepth=None):
     floor, raw["aref_plain"] the sum over pixels of the absolute per-pixel contributions, each
     carried to the raw parameters through the absolute Jacobian. Returns (g2d, aref2d,
     aplain2d, raw)."""
-    g2d, aref2d, aplain2d = oracle.render_backward(o_proj, cam, dL_dimage, pixels=pixels, dL_ddepth=dL_ddepth,
-                                                   plain_floor=True)
+    g2d, aref2d, aplain2d, aterms2d = oracle.render_backward(o_proj, cam, dL_dimage, pixels=pixels,
+                                                             dL_ddepth=dL_ddepth, plain_floor=True)
     raw = oracle.project_backward(scene, cam, g2d, aref2d)
     raw["aref_plain"] = oracle.project_backward(scene, cam, g2d, aplain2d)["aref"]
+    raw["aref_terms"] = oracle.project_backward(scene, cam, g2d, aterms2d)["aref"]
     return g2d, aref2d, aplain2d, raw
 
 
@@ -168,6 +169,8 @@ def compare_grads(gpu_grads: dict, orc_raw: dict, sh_degree: int, label=""):
     floors = {"terms": oracle.split_raw(orc_raw["aref"], sh_degree)}
     if "aref_plain" in orc_raw:
         floors["plain"] = oracle.split_raw(orc_raw["aref_plain"], sh_degree)
+    if "aref_terms" in orc_raw:
+        floors["terms_unwidened"] = oracle.split_raw(orc_raw["aref_terms"], sh_degree)
     use = "plain" if ("plain" in floors and FLOOR == "plain") else "terms"
     stats = {f: [0, 0, 0.0] for f in floors}
     total = 0
