@@ -117,9 +117,11 @@ gs_status gs_project(int32_t n, int32_t sh_degree, const float* d_means, const f
  * the key (ty * tiles_x + tx) << 32 | float_bits(depth_i) and the value i, sorts the
  * pairs by key, keeping equal keys in ascending i (stable), and writes per tile the range
  * [start, end) of its pairs in the sorted list ((0, 0) for an empty tile).
- * Implementation: a stable LSD radix sort of the Gaussians by depth, a prefix scan of the tile
- * counts in depth order, emission of (tile, i) pairs in that order, and a stable LSD radix sort
- * of the pairs by tile id (Onesweep-style single-pass passes with decoupled look-back).
+ * Implementation: the Gaussians put in stable depth order (up to 36,864 of them and 16,383 tiles:
+ * blocks of 4096 sorted in LDS and merge-ranked against each other; beyond: a stable LSD radix
+ * sort), the first pair position of each from a prefix of the tile counts in depth order,
+ * emission of (tile, i) pairs in that order, and a stable LSD radix sort of the pairs by tile
+ * id (Onesweep-style single-pass passes with decoupled look-back).
  * Inputs: n and proj (from gs_project with the same camera; it reads depths, tiles_touched,
  *   means2d and radii, and with tight_tiles also conics and opacities); d_workspace of at least
  *   gs_bin_workspace_bytes(n, pair_capacity, cam) bytes (device, 256-byte aligned, contents
