@@ -1729,3 +1729,54 @@ extern "C" gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const 
   return bin_and_sort(n, proj, cam, d_workspace, workspace_bytes, pair_capacity, d_keys, d_ids, d_tile_ranges,
                       d_raster_plan, d_num_pairs, h_num_pairs, stream);
 }
+
+// ---------------------------------------------------------------------------------------------
+// The binning without allocation: its workspace is this file-scope device array, one copy per
+// GPU, held until the process ends. Host code never passes the array's name to a kernel (on the
+// host it only names a shadow); it passes the device address hipGetSymbolAddress returns, taken
+// once per device with that device current.
+// ---------------------------------------------------------------------------------------------
+namespace {
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+gs_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return set_error(GS_ERR_DEVICE, "gs_bin_and_sort_noalloc: no current device");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(GS_ERR_DEVICE, std::string("gs_bin_and_sort_noalloc: hipGetSymbolAddress: ") +
+                                          hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GS_OK;
+}
+}  // namespace
+
+extern "C" size_t gs_bin_noalloc_max_workspace_bytes(void) { return kStaticScratchBytes; }
+
+extern "C" gs_status gs_bin_and_sort_noalloc(int32_t n, const gs_projected* proj, const gs_camera* cam,
+                                             int64_t pair_capacity, uint64_t* d_keys, uint32_t* d_ids,
+                                             uint32_t* d_tile_ranges, uint32_t* d_raster_plan,
+                                             int64_t* d_num_pairs, void* stream) {
+  if (n < 0 || pair_capacity < 0 || !cam || cam->width <= 0 || cam->height <= 0)
+    return set_error(GS_ERR_INVALID_ARG, "gs_bin_and_sort_noalloc: n < 0, capacity < 0 or an invalid camera");
+  const size_t need = bin_layout(n, pair_capacity, cam).total;
+  if (need > kStaticScratchBytes)
+    return set_error(GS_ERR_LIMIT, "gs_bin_and_sort_noalloc: this frame needs " + std::to_string(need) +
+                                       " bytes of workspace, above the static maximum of " +
+                                       std::to_string(kStaticScratchBytes) + " (use gs_bin_and_sort)");
+  void* ws = nullptr;
+  const gs_status st = scratch_of_current_device(&ws);
+  if (st != GS_OK) return st;
+  return bin_and_sort(n, proj, cam, ws, kStaticScratchBytes, pair_capacity, d_keys, d_ids, d_tile_ranges,
+                      d_raster_plan, d_num_pairs, nullptr, stream);
+}

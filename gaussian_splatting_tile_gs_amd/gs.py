@@ -70,6 +70,8 @@ def load():
         "gs_raster_plan_words": (sz, [cam_p]),
         "gs_raster_workspace_bytes": (sz, []),
         "gs_bin_and_sort": (i32, [i32, proj_p, cam_p, P, sz, i64, P, P, P, P, P, ctypes.POINTER(ctypes.c_int64), P]),
+        "gs_bin_noalloc_max_workspace_bytes": (sz, []),
+        "gs_bin_and_sort_noalloc": (i32, [i32, proj_p, cam_p, i64, P, P, P, P, P, P]),
         "gs_rasterize_fwd": (i32, [i32, proj_p, cam_p, P, P, P, P, P, P, P, P, P, P]),
         "gs_rasterize_fwd_l1": (i32, [i32, proj_p, cam_p, P, P, P, P, P, P, P, P, P, P, P, P]),
         "gs_bwd_workspace_bytes": (sz, [i32]),
@@ -173,6 +175,19 @@ def gs_bin_and_sort(n, proj: "Projected", cam: GsCamera, workspace, pair_capacit
                                        ctypes.byref(P) if wait else None, _stream(stream)),
                 allow=(GS_ERR_CAPACITY,))
     return st, (int(P.value) if wait else None)
+
+
+def gs_bin_noalloc_max_workspace_bytes() -> int:
+    return int(load().gs_bin_noalloc_max_workspace_bytes())
+
+
+def gs_bin_and_sort_noalloc(n, proj: "Projected", cam: GsCamera, pair_capacity, keys, ids, tile_ranges,
+                            num_pairs_dev, stream=None, plan=None):
+    """gs_bin_and_sort with the library's static workspace: no allocation and no host wait; P
+    goes to num_pairs_dev (a one-element int64 CUDA tensor)."""
+    return _check(load().gs_bin_and_sort_noalloc(n, ctypes.byref(proj.struct()), ctypes.byref(cam), pair_capacity,
+                                                 _ptr(keys), _ptr(ids), _ptr(tile_ranges), _ptr(plan),
+                                                 _ptr(num_pairs_dev), _stream(stream)))
 
 
 def gs_rasterize_fwd(n, proj: "Projected", cam: GsCamera, ids, tile_ranges, image, final_T, n_contrib,

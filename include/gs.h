@@ -154,6 +154,27 @@ gs_status gs_bin_and_sort(int32_t n, const gs_projected* proj, const gs_camera* 
                           int64_t* h_num_pairs, void* stream);
 
 /*
+ * gs_bin_and_sort_noalloc -- gs_bin_and_sort for callers that cannot allocate (code under graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and results,
+ * with no workspace argument and no host wait. Its workspace is a static device array of
+ * gs_bin_noalloc_max_workspace_bytes() bytes (64 MiB), one per GPU, allocated with the library's
+ * code and held until the process ends; the call allocates nothing and calls no allocating
+ * routine. Every call on one GPU shares that array, so calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and must be serialized by the caller; the
+ * kernels clear what must start at zero, so one call's leftovers do not reach the next.
+ * Arguments: as gs_bin_and_sort without d_workspace, workspace_bytes and h_num_pairs; P goes to
+ *   *d_num_pairs (device int64, optional). Results are those of gs_bin_and_sort (overflow
+ *   included: every range (0, 0) and P reported in full).
+ * Errors: those of gs_bin_and_sort, and GS_ERR_LIMIT when gs_bin_workspace_bytes(n,
+ *   pair_capacity, cam) exceeds the static maximum (nothing is enqueued; use gs_bin_and_sort),
+ *   GS_ERR_DEVICE when the array's device address cannot be taken.
+ */
+size_t gs_bin_noalloc_max_workspace_bytes(void);
+gs_status gs_bin_and_sort_noalloc(int32_t n, const gs_projected* proj, const gs_camera* cam, int64_t pair_capacity,
+                                  uint64_t* d_keys, uint32_t* d_ids, uint32_t* d_tile_ranges,
+                                  uint32_t* d_raster_plan, int64_t* d_num_pairs, void* stream);
+
+/*
  * gs_rasterize_fwd -- per-pixel front-to-back alpha blending over the pixel's tile list (section
  * 5 of the PyTorch lesson): for each pair in the tile's range, in order,
  *   sigma = 0.5 (A dx^2 + C dy^2) + B dx dy with (dx, dy) = mean2d - pixel centre;
