@@ -275,18 +275,27 @@ struct TileCountArgs {
   int pshift[3];        // the pair passes' digit shifts and widths (tile id bits split evenly)
   int pbits[3];
   uint32_t* hist_pair;  // [npass][256]
-  // small frames: the difference array is the sum of tmat_rows per-block rows, tmat_stride apart
-  // (tdiff is then unused)
+  // small frames: the difference array is the sum of tmat_rows rows, tmat_stride apart (one per
+  // sorted block), and the finalizer writes every tile's range, (0, 0) included, since nothing
+  // zeroed them
   const uint32_t* tmat;
   uint32_t tmat_rows;
   uint32_t tmat_stride;
+  int32_t all_ranges;
 };
 
+constexpr uint32_t kMaxTmatRows = 9;  // the small-frame path's blocks
+// Entry t of the difference array: the sum of the rows' entries, their loads all in flight.
 __device__ __forceinline__ uint32_t tdiff_at(const TileCountArgs& a, uint32_t t) {
   if (!a.tmat) return a.tdiff[t];
-  uint32_t v = 0;
-  for (uint32_t r = 0; r < a.tmat_rows; ++r) v += a.tmat[(size_t)r * a.tmat_stride + t];
-  return v;
+  uint32_t v[kMaxTmatRows];
+#pragma unroll
+  for (uint32_t r = 0; r < kMaxTmatRows; ++r)
+    v[r] = a.tmat[(size_t)(r < a.tmat_rows ? r : 0u) * a.tmat_stride + t];
+  uint32_t sum = 0;
+#pragma unroll
+  for (uint32_t r = 0; r < kMaxTmatRows; ++r) sum += r < a.tmat_rows ? v[r] : 0u;
+  return sum;
 }
 constexpr int kRowGaussians = 2048;  // Gaussians per row workgroup (two per lane)
 
@@ -508,7 +517,7 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
   bool fits = false;
 #pragma unroll 1
   for (int sweep = 0; sweep < 2; ++sweep) {
-    if (sweep == 1 && !fits && !a.plan) break;
+    if (sweep == 1 && !fits && !a.plan && !a.all_ranges) break;
     uint32_t carry_d = 0, carry_c = 0;
 #pragma unroll 1
     for (uint32_t cb = 0; cb < a.ntiles; cb += kFinStep) {
@@ -563,6 +572,9 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
           a.ranges[2 * t] = st;
           a.ranges[2 * t + 1] = st + c;
           atomicAdd(&s_hist[0][t & ((1u << a.pbits[0]) - 1u)], c);
+        } else if (valid && a.all_ranges) {
+          a.ranges[2 * t] = 0u;
+          a.ranges[2 * t + 1] = 0u;
         }
         if (valid && fits) {
           // a run of 2^shift_k tiles starting at t: its digit-k count starts at -start(t) and
@@ -1092,30 +1104,34 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(8)
 // ---------------------------------------------------------------------------------------------
 // Small frames (N <= kSmallMaxN): the depth order from sorted blocks and merge ranks, two launches
 // instead of the key-computing pass, four radix passes and the scan.
-//   k_small_local  one workgroup per block of 4096 Gaussians (ids [4096 b, 4096 b + 4096)):
-//                  depth keys and rectangles; the block's tile-count difference array (a row of
-//                  tmat); the block sorted stably by key in LDS (radix passes of up to 9 bits over
-//                  the bits the block's keys span); the sorted keys, ids and the exclusive prefix
-//                  of their tile counts written out
-//   k_small_merge  one workgroup per block: all N sorted keys held in LDS, each key's place in the
-//                  depth order is its place in its block plus, for every other block, the number
-//                  of its keys that come first (binary search; an earlier block's equal keys have
-//                  smaller ids and come first), and its first pair position is the sum of the
-//                  matching tile-count prefixes. It writes the depth-ordered records and the
-//                  emission chunks' first Gaussians as the scan does; one more workgroup is the
-//                  tile-count finalizer (the difference array is the sum of the blocks' rows)
+//   k_small_local  workgroup b < nb sorts block b (ids [4096 b, 4096 b + 4096)) by depth key in
+//                  LDS (radix passes of up to 9 bits over the bits the block's keys span) and
+//                  writes the sorted keys, ids and the exclusive prefix of their tile counts;
+//                  workgroup nb counts the pairs of every tile from all N rectangles into a
+//                  difference array in its own LDS and finalizes it (ranges, pair-sort histograms,
+//                  raster plan); the others only clear the control block and look-back words
+//   k_small_merge  kSmallSplit workgroups per block, 512 keys each: every key's place in the depth
+//                  order is its place in its block plus, for every other block, how many of that
+//                  block's keys come first (binary search over all N keys held in LDS; an earlier
+//                  block's equal keys have smaller ids and come first); its first pair position is
+//                  the sum of the matching tile-count prefixes. It writes the depth-ordered
+//                  records and the emission chunks' first Gaussians as the scan does.
 // The order is the stable (depth bits, id) order of the radix path, bit for bit.
 // ---------------------------------------------------------------------------------------------
 constexpr int kSmallBlock = kSortTile;  // 4096 Gaussians per block, four per thread
 constexpr int kSmallMaxBlocks = 9;
 constexpr int32_t kSmallMaxN = kSmallBlock * kSmallMaxBlocks;  // every key in 144 KB of LDS
-constexpr uint32_t kSmallMaxTiles = 16383;                      // a block's difference array in LDS
+constexpr uint32_t kSmallMaxTiles = 16383;                      // the difference array in LDS
 constexpr int kLocalBits = 9;
 constexpr int kLocalRadix = 1 << kLocalBits;
+constexpr int kMergeThreads = kSortThreads;                     // the finalizer's workgroup size
+constexpr int kMergeItems = 1;
+constexpr int kSmallSplit = kSmallBlock / (kMergeThreads * kMergeItems);  // merge workgroups per block
 // k_small_local's dynamic LDS (words): per-wave digit counts, keys, values, tile counts by local
-// index, the difference array
+// index, then the block's difference array
 constexpr uint32_t kLocalCnt = kSortWaves * kLocalRadix;
-constexpr uint32_t kLocalFixedWords = kLocalCnt + 3 * kSmallBlock;
+constexpr uint32_t kLocalSortWords = kLocalCnt + 3 * kSmallBlock;
+constexpr uint32_t kCountFixedWords = kFinStep + kFinAuxWords;  // the finalizer's LDS
 
 struct SmallArgs {
   int32_t n;
@@ -1132,21 +1148,21 @@ struct SmallArgs {
   uint32_t* btot;       // [nb] block totals of the tile counts
   uint32_t* tmat;       // [nb, tmat_stride] per-block difference arrays of the per-tile counts
   uint32_t tmat_stride;
-  uint32_t* zero;       // zeroed: control block, pair look-back words
-  size_t zero_words;
-  uint32_t* ranges;     // zeroed: [ntiles, 2]
-  size_t range_words;
+  uint32_t* zero_a;     // cleared: the control block up to its pair-sort histograms
+  size_t zero_a_words;
+  uint32_t* zero_b;     // cleared: the pair look-back words
+  size_t zero_b_words;
 };
 
-// Exclusive sum over the values of the first 512 threads (the others pass 0); two barriers.
-__device__ __forceinline__ uint32_t block_excl_scan512(uint32_t v, uint32_t* s_wsum) {
+// Exclusive sum over the values of the first `nwaves` waves (the others pass 0), with DPP wave
+// scans; two barriers. s_wsum holds at least nwaves words.
+__device__ __forceinline__ uint32_t block_excl_scan_dpp(uint32_t v, int nwaves, uint32_t* s_wsum) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint32_t inc = wave_incl_scan<uint32_t>(v, lane);
-  if (wave < 8 && lane == 63) s_wsum[wave] = inc;
+  const uint32_t inc = wave_incl_scan_dpp(v);
+  if (wave < nwaves && lane == 63) s_wsum[wave] = inc;
   __syncthreads();
   uint32_t before = 0;
-#pragma unroll
-  for (int w = 0; w < 8; ++w) before += (w < wave) ? s_wsum[w] : 0u;
+  for (int w = 0; w < wave && w < nwaves; ++w) before += s_wsum[w];
   __syncthreads();
   return before + inc - v;
 }
@@ -1159,15 +1175,19 @@ __device__ __forceinline__ void local_radix_pass(uint32_t (&k)[kSortItems], uint
                                                  uint32_t* s_v, uint32_t* s_dig, uint32_t* s_wsum) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t radix = 1u << bits, mask = radix - 1u;
-  for (uint32_t i = tid; i < (uint32_t)kSortWaves * kLocalRadix; i += kSortThreads) s_cnt[i] = 0u;
-  __syncthreads();
+  // the first 2^bits counters of every wave (each wave clears its own)
+  for (uint32_t i = lane; i < radix; i += 64) s_cnt[wave * kLocalRadix + i] = 0u;
+  __builtin_amdgcn_wave_barrier();
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   uint32_t rank[kSortItems];
 #pragma unroll
   for (int i = 0; i < kSortItems; ++i) {
     const uint32_t d = (k[i] >> shift) & mask;
+    // all kLocalBits ballots, unconditionally: the digit's bits above `bits` are 0 in every lane
+    // and leave the match mask unchanged
     uint64_t m = ~0ull;
-    for (int b = 0; b < bits; ++b) {
+#pragma unroll
+    for (int b = 0; b < kLocalBits; ++b) {
       const bool bit = (d >> b) & 1u;
       const uint64_t bb = __ballot(bit);
       m &= bit ? bb : ~bb;
@@ -1180,15 +1200,20 @@ __device__ __forceinline__ void local_radix_pass(uint32_t (&k)[kSortItems], uint
     __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
+  // per digit (threads below 2^bits): the waves' exclusive offsets and the digit total, the 16
+  // counters loaded together; then the digit totals' exclusive scan
   uint32_t tot = 0;
   if ((uint32_t)tid < radix) {
+    uint32_t c[kSortWaves];
+#pragma unroll
+    for (int w = 0; w < kSortWaves; ++w) c[w] = s_cnt[w * kLocalRadix + tid];
+#pragma unroll
     for (int w = 0; w < kSortWaves; ++w) {
-      const uint32_t c = s_cnt[w * kLocalRadix + tid];
       s_cnt[w * kLocalRadix + tid] = tot;
-      tot += c;
+      tot += c[w];
     }
   }
-  const uint32_t dex = block_excl_scan512((uint32_t)tid < radix ? tot : 0u, s_wsum);
+  const uint32_t dex = block_excl_scan_dpp((uint32_t)tid < radix ? tot : 0u, kLocalRadix / 64, s_wsum);
   if ((uint32_t)tid < radix) s_dig[tid] = dex;
   __syncthreads();
 #pragma unroll
@@ -1214,18 +1239,19 @@ __global__ __launch_bounds__(kSortThreads) void k_small_local(SmallArgs sa, Tile
   __shared__ uint32_t s_dig[kLocalRadix];
   __shared__ uint32_t s_wsum[kSortWaves];
   __shared__ uint32_t s_mm[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (blockIdx.x >= sa.nb) {  // workgroup-uniform: clearing only
+    const size_t base_w = (size_t)(blockIdx.x - sa.nb) * kSortThreads + tid;
+    const size_t gsz = (size_t)(gridDim.x - sa.nb) * kSortThreads;
+    for (size_t i = base_w; i < sa.zero_a_words; i += gsz) sa.zero_a[i] = 0u;
+    for (size_t i = base_w; i < sa.zero_b_words; i += gsz) sa.zero_b[i] = 0u;
+    return;
+  }
   uint32_t* s_cnt = s_dyn;
   uint32_t* s_k = s_cnt + kLocalCnt;
   uint32_t* s_v = s_k + kSmallBlock;
   uint32_t* s_tc = s_v + kSmallBlock;
   uint32_t* s_diff = s_tc + kSmallBlock;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  {
-    const size_t gsz = (size_t)gridDim.x * kSortThreads;
-    for (size_t i = blockIdx.x * (size_t)kSortThreads + tid; i < sa.zero_words; i += gsz) sa.zero[i] = 0u;
-    for (size_t i = blockIdx.x * (size_t)kSortThreads + tid; i < sa.range_words; i += gsz) sa.ranges[i] = 0u;
-  }
-  if (blockIdx.x >= sa.nb) return;  // workgroup-uniform: zeroing only
   const uint32_t b = blockIdx.x;
   const uint32_t base = b * (uint32_t)kSmallBlock;
   const uint32_t len = (uint32_t)sa.n - base < (uint32_t)kSmallBlock ? (uint32_t)sa.n - base : (uint32_t)kSmallBlock;
@@ -1254,7 +1280,6 @@ __global__ __launch_bounds__(kSortThreads) void k_small_local(SmallArgs sa, Tile
 #pragma unroll
   for (int i = 0; i < kSortItems; ++i) {
     const uint32_t e = (uint32_t)(wave * 64 * kSortItems + i * 64 + lane);
-    const bool valid = e < len;
     key[i] = tc[i] > 0 ? __float_as_uint(z[i]) : 0xFFFFFFFFu;
     uint32_t tb = 0, w = 1, h = 0;
     if (tc[i] > 0) {
@@ -1266,7 +1291,7 @@ __global__ __launch_bounds__(kSortThreads) void k_small_local(SmallArgs sa, Tile
       kmax = max(kmax, key[i]);
     }
     rc[i] = make_uint4(tc[i], tb, w, h);
-    if (valid) sa.rec[base + e] = rc[i];
+    if (e < len) sa.rec[base + e] = rc[i];
     s_tc[e] = tc[i];
   }
 #pragma unroll
@@ -1274,12 +1299,12 @@ __global__ __launch_bounds__(kSortThreads) void k_small_local(SmallArgs sa, Tile
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
     kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, 64));
   }
-  __syncthreads();  // s_diff and s_mm initialised
+  __syncthreads();  // s_mm and s_diff initialised
   if (lane == 0) {
     atomicMin(&s_mm[0], kmin);
     atomicMax(&s_mm[1], kmax);
   }
-  // the block's pairs per tile (rows of rectangles into the difference array)
+  // the block's pairs per tile: rows of its rectangles into its difference array
 #pragma unroll
   for (int i = 0; i < kSortItems; ++i) {
     const uint32_t e = (uint32_t)(wave * 64 * kSortItems + i * 64 + lane);
@@ -1316,8 +1341,7 @@ __global__ __launch_bounds__(kSortThreads) void k_small_local(SmallArgs sa, Tile
     oc[i] = s_tc[lv];
     own += oc[i];
   }
-  uint32_t total;
-  uint32_t run = block_excl_scan1024<uint32_t>(own, s_wsum, &total);
+  const uint32_t run = block_excl_scan_dpp(own, kSortWaves, s_wsum);
   uint4 pre;
   pre.x = run;
   pre.y = pre.x + oc[0];
@@ -1327,26 +1351,43 @@ __global__ __launch_bounds__(kSortThreads) void k_small_local(SmallArgs sa, Tile
   reinterpret_cast<uint4*>(sa.skey)[o4] = make_uint4(ok[0], ok[1], ok[2], ok[3]);
   reinterpret_cast<uint4*>(sa.sid)[o4] = make_uint4(oid[0], oid[1], oid[2], oid[3]);
   reinterpret_cast<uint4*>(sa.cpre)[o4] = pre;
-  if (tid == 0) sa.btot[b] = total;
+  if (tid == kSortThreads - 1) sa.btot[b] = pre.w + oc[3];
 }
 
-// Merge ranks. Workgroup b < nb takes block b's elements, four consecutive per thread; workgroup
-// nb is the tile-count finalizer. Dynamic LDS: max(nb 4096, the finalizer's) words.
-__global__ __launch_bounds__(kSortThreads) void k_small_merge(SmallArgs sa, uint4* __restrict__ drec,
-                                                              uint32_t* __restrict__ chunk_first, uint64_t capacity,
-                                                              Ctrl* ctrl, int64_t* __restrict__ user_num_pairs,
-                                                              uint32_t lds_words, TileCountArgs ta) {
+// Merge ranks: workgroup kSmallSplit b + s takes block b's sorted elements [1024 s, 1024 s + 1024),
+// one per thread; workgroup kSmallSplit nb is the tile-count finalizer. Dynamic LDS: max(nb 4096,
+// the finalizer's) words (every block's sorted keys).
+__global__ __launch_bounds__(kMergeThreads) void k_small_merge(SmallArgs sa, uint4* __restrict__ drec,
+                                                               uint32_t* __restrict__ chunk_first, uint64_t capacity,
+                                                               Ctrl* ctrl, int64_t* __restrict__ user_num_pairs,
+                                                               uint32_t lds_words, TileCountArgs ta) {
   extern __shared__ uint32_t s_dyn[];
   const int tid = threadIdx.x;
   const uint32_t nb = sa.nb;
-  if (blockIdx.x == nb) {  // workgroup-uniform
+  if (blockIdx.x == nb * kSmallSplit) {  // workgroup-uniform: the tile-count finalizer
     tile_finalize(ta, s_dyn, lds_words);
     return;
   }
-  const uint32_t b = blockIdx.x;
-  for (uint32_t q = tid; q < nb * (kSmallBlock / 4); q += kSortThreads)
-    reinterpret_cast<uint4*>(s_dyn)[q] = reinterpret_cast<const uint4*>(sa.skey)[q];
-  if (b == 0 && tid == 0) {  // P: the sum of the block totals
+  const uint32_t b = blockIdx.x / kSmallSplit, sub = blockIdx.x % kSmallSplit;
+  {  // every block's sorted keys into LDS, eight 16-byte loads in flight per thread
+    const uint32_t nq = nb * (kSmallBlock / 4);
+    const uint4* src = reinterpret_cast<const uint4*>(sa.skey);
+    uint4* dst = reinterpret_cast<uint4*>(s_dyn);
+    for (uint32_t q0 = 0; q0 < nq; q0 += 8 * kMergeThreads) {
+      uint4 t[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t q = q0 + (uint32_t)(j * kMergeThreads + tid);
+        t[j] = q < nq ? src[q] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t q = q0 + (uint32_t)(j * kMergeThreads + tid);
+        if (q < nq) dst[q] = t[j];
+      }
+    }
+  }
+  if (blockIdx.x == 0 && tid == 0) {  // P: the sum of the block totals
     uint64_t P = 0;
     for (uint32_t j = 0; j < nb; ++j) P += sa.btot[j];
     ctrl->num_pairs = P;
@@ -1354,39 +1395,79 @@ __global__ __launch_bounds__(kSortThreads) void k_small_merge(SmallArgs sa, uint
     if (user_num_pairs) *user_num_pairs = (int64_t)P;
   }
   __syncthreads();
-  const uint32_t len_b = (uint32_t)sa.n - b * kSmallBlock < (uint32_t)kSmallBlock ? (uint32_t)sa.n - b * kSmallBlock
-                                                                                   : (uint32_t)kSmallBlock;
-#pragma unroll 1
-  for (int i = 0; i < kSortItems; ++i) {
-    const uint32_t e = (uint32_t)(tid * kSortItems + i);
-    if (e >= len_b) break;
-    const uint32_t key = s_dyn[b * kSmallBlock + e];
-    uint32_t rank = e;
-    uint64_t off = sa.cpre[(size_t)b * kSmallBlock + e];
-    for (uint32_t b2 = 0; b2 < nb; ++b2) {
-      if (b2 == b) continue;
-      const uint32_t len2 =
-          (uint32_t)sa.n - b2 * kSmallBlock < (uint32_t)kSmallBlock ? (uint32_t)sa.n - b2 * kSmallBlock : kSmallBlock;
-      const uint32_t* kk = s_dyn + b2 * kSmallBlock;
-      // the number of block b2's keys that come before this one: <= key for an earlier block
-      // (equal keys there have smaller ids), < key for a later one
-      uint32_t pos = 0;
+  auto block_len = [&](uint32_t bb) {
+    const uint32_t rest = (uint32_t)sa.n - bb * (uint32_t)kSmallBlock;
+    return rest < (uint32_t)kSmallBlock ? rest : (uint32_t)kSmallBlock;
+  };
+  const uint32_t len_b = block_len(b);
+  const uint32_t e0 = sub * (uint32_t)(kMergeThreads * kMergeItems) + (uint32_t)tid * kMergeItems;
+  // for each other block, how many of its keys come first: <= key for an earlier block (its equal
+  // keys have smaller ids), < key for a later one. All searches advance together.
+  uint32_t key[kMergeItems];
 #pragma unroll
-      for (uint32_t step = kSmallBlock; step > 0; step >>= 1) {
-        if (pos + step <= len2) {
-          const uint32_t x = kk[pos + step - 1];
-          if (b2 < b ? x <= key : x < key) pos += step;
-        }
+  for (int i = 0; i < kMergeItems; ++i) key[i] = s_dyn[b * kSmallBlock + e0 + (uint32_t)i];
+  uint32_t pos[kSmallMaxBlocks][kMergeItems];
+#pragma unroll
+  for (int b2 = 0; b2 < kSmallMaxBlocks; ++b2)
+#pragma unroll
+    for (int i = 0; i < kMergeItems; ++i) pos[b2][i] = 0u;
+  // branch-free: every step reads one key per (block, item), the index clamped into the block (a
+  // block that is this one or does not exist has length 0 and reads block 0's first key), so all
+  // reads of a step are in flight together
+  uint32_t len2[kSmallMaxBlocks], kbase[kSmallMaxBlocks];
+  bool before[kSmallMaxBlocks];
+#pragma unroll
+  for (int b2 = 0; b2 < kSmallMaxBlocks; ++b2) {
+    const bool use = (uint32_t)b2 < nb && (uint32_t)b2 != b;
+    len2[b2] = use ? block_len((uint32_t)b2) : 0u;
+    kbase[b2] = use ? (uint32_t)b2 * kSmallBlock : 0u;
+    before[b2] = (uint32_t)b2 < b;
+  }
+#pragma unroll
+  for (uint32_t step = kSmallBlock; step > 0; step >>= 1) {
+#pragma unroll
+    for (int b2 = 0; b2 < kSmallMaxBlocks; ++b2) {
+#pragma unroll
+      for (int i = 0; i < kMergeItems; ++i) {
+        const uint32_t p = pos[b2][i] + step;
+        const uint32_t idx = kbase[b2] + (p <= len2[b2] ? p - 1u : 0u);
+        const uint32_t x = s_dyn[idx];
+        const bool first = before[b2] ? x <= key[i] : x < key[i];
+        pos[b2][i] = (p <= len2[b2] && first) ? p : pos[b2][i];
       }
-      rank += pos;
-      off += pos < len2 ? sa.cpre[(size_t)b2 * kSmallBlock + pos] : sa.btot[b2];
     }
-    const uint32_t g = sa.sid[(size_t)b * kSmallBlock + e];
-    const uint4 r = sa.rec[g];
-    drec[rank] = make_uint4(off < 0xFFFFFFFFull ? (uint32_t)off : 0xFFFFFFFFu, r.y, r.z, g);
-    const uint64_t end = off + r.x;
-    for (uint64_t c = (off + kEmitChunk - 1) / kEmitChunk * kEmitChunk; c < end && c < capacity; c += kEmitChunk)
-      chunk_first[c / kEmitChunk] = rank;
+  }
+  // ranks and first pair positions: every block's prefix loads issued together
+  uint32_t rank[kMergeItems], g[kMergeItems];
+  uint64_t off[kMergeItems];
+#pragma unroll
+  for (int i = 0; i < kMergeItems; ++i) {
+    const uint32_t e = e0 + (uint32_t)i;
+    rank[i] = e;
+    off[i] = e < len_b ? sa.cpre[(size_t)b * kSmallBlock + e] : 0u;
+    g[i] = e < len_b ? sa.sid[(size_t)b * kSmallBlock + e] : 0u;
+  }
+#pragma unroll
+  for (int b2 = 0; b2 < kSmallMaxBlocks; ++b2) {
+    if (len2[b2] == 0u) continue;  // uniform
+#pragma unroll
+    for (int i = 0; i < kMergeItems; ++i) {
+      const uint32_t p = pos[b2][i];
+      rank[i] += p;
+      off[i] += p < len2[b2] ? sa.cpre[(size_t)b2 * kSmallBlock + p] : sa.btot[b2];
+    }
+  }
+  uint4 r[kMergeItems];
+#pragma unroll
+  for (int i = 0; i < kMergeItems; ++i) r[i] = sa.rec[g[i]];  // g = 0 past the block: a valid index, unused
+#pragma unroll
+  for (int i = 0; i < kMergeItems; ++i) {
+    const uint32_t e = e0 + (uint32_t)i;
+    if (e >= len_b) break;
+    drec[rank[i]] = make_uint4(off[i] < 0xFFFFFFFFull ? (uint32_t)off[i] : 0xFFFFFFFFu, r[i].y, r[i].z, g[i]);
+    const uint64_t end = off[i] + r[i].x;
+    for (uint64_t c = (off[i] + kEmitChunk - 1) / kEmitChunk * kEmitChunk; c < end && c < capacity; c += kEmitChunk)
+      chunk_first[c / kEmitChunk] = rank[i];
   }
 }
 
@@ -1496,11 +1577,13 @@ extern "C" size_t gs_bin_workspace_bytes(int32_t n, int64_t pair_capacity, const
 }
 
 namespace {
-// The small-frame kernels take up to 144 KB of dynamic LDS: raise their limit (64 KB by default)
+// The small-frame kernels take up to 112 and 144 KB of dynamic LDS: raise their limits (64 KB by default)
 // once per device.
-constexpr size_t kSmallLdsBytes = (size_t)(kLocalFixedWords + kSmallMaxTiles + 1) * 4;
-static_assert((size_t)kSmallMaxBlocks * kSmallBlock * 4 <= kSmallLdsBytes, "merge keys exceed the LDS limit set");
-static_assert(kSmallLdsBytes + 4 * (kLocalRadix + kSortWaves + 2) <= 160 * 1024, "LDS of a compute unit");
+constexpr size_t kSmallLocalLds = (size_t)(kLocalSortWords + kSmallMaxTiles + 1) * 4;
+constexpr size_t kSmallMergeLds = (size_t)kSmallMaxBlocks * kSmallBlock * 4;
+static_assert(kSmallLocalLds + 4 * (kLocalRadix + kSortWaves + 2) <= 160 * 1024, "LDS of a compute unit");
+static_assert((size_t)kCountFixedWords * 4 <= kSmallMergeLds && kSmallMergeLds + 8 <= 160 * 1024,
+              "LDS of a compute unit");
 std::mutex g_lds_mu;
 bool g_lds_set[64] = {};
 gs_status raise_small_lds_limits() {
@@ -1510,9 +1593,9 @@ gs_status raise_small_lds_limits() {
   std::lock_guard<std::mutex> lock(g_lds_mu);
   if (g_lds_set[dev]) return GS_OK;
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(k_small_local), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)kSmallLdsBytes) != hipSuccess ||
+                          (int)kSmallLocalLds) != hipSuccess ||
       hipFuncSetAttribute(reinterpret_cast<const void*>(k_small_merge), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)kSmallLdsBytes) != hipSuccess)
+                          (int)kSmallMergeLds) != hipSuccess)
     return check_launch("gs_bin_and_sort: raising the LDS limit");
   g_lds_set[dev] = true;
   return GS_OK;
@@ -1586,6 +1669,7 @@ gs_status bin_and_sort(int32_t n, const gs_projected* proj, const gs_camera* cam
   targs.tmat = nullptr;
   targs.tmat_rows = 0;
   targs.tmat_stride = 0;
+  targs.all_ranges = 0;
   // ping-pong of the pair sort: A = d_keys viewed as two u32 arrays of pair_capacity, B = workspace.
   // The last pass writes the 64-bit keys over A, so it reads B: pass p writes B when
   // npass - 2 - p is even, A otherwise.
@@ -1609,27 +1693,30 @@ gs_status bin_and_sort(int32_t n, const gs_projected* proj, const gs_camera* cam
     sa.btot = (uint32_t*)(ws + L.btot);
     sa.tmat = (uint32_t*)(ws + L.tmat);
     sa.tmat_stride = L.tmat_stride;
-    sa.zero = (uint32_t*)(ws + L.ctrl);
-    sa.zero_words = (L.small_zero_end - L.ctrl) / 4;
-    sa.ranges = d_tile_ranges;
-    sa.range_words = (size_t)(2 * ntiles);
-    const size_t zwords = sa.zero_words + sa.range_words;
-    const size_t zblocks = (zwords + 16 * kSortThreads - 1) / (16 * kSortThreads);
-    const unsigned blocks = (unsigned)std::max<size_t>(L.nbSmall, std::min<size_t>(zblocks, 1024));
-    const size_t lds_local = ((size_t)kLocalFixedWords + (size_t)ntiles + 1) * 4;
-    const uint32_t merge_words = std::max<uint32_t>(L.nbSmall * kSmallBlock, kFinStep + kFinAuxWords);
+    // cleared by the extra workgroups: the control block up to its pair-sort histograms (the
+    // finalizer writes those in the same launch) and the pair look-back words
+    sa.zero_a = (uint32_t*)(ws + L.ctrl);
+    sa.zero_a_words = offsetof(Ctrl, hist_pair) / 4;
+    sa.zero_b = pstatus;
+    sa.zero_b_words = (L.small_zero_end - L.pstatus) / 4;
+    const size_t zwords = sa.zero_a_words + sa.zero_b_words;
+    const unsigned zblocks = (unsigned)std::min<size_t>((zwords + 16 * kSortThreads - 1) / (16 * kSortThreads), 256);
+    const size_t lds_local = ((size_t)kLocalSortWords + ntiles + 1) * 4;
+    const uint32_t merge_words = std::max<uint32_t>(L.nbSmall * kSmallBlock, kCountFixedWords);
+    const size_t lds_merge = (size_t)merge_words * 4;
     const gs_status lst = raise_small_lds_limits();
     if (lst != GS_OK) return lst;
     {
       TimedScope ts("small_local", s);
-      hipLaunchKernelGGL(k_small_local, dim3(blocks), dim3(kSortThreads), lds_local, s, sa, targs);
+      hipLaunchKernelGGL(k_small_local, dim3(L.nbSmall + zblocks), dim3(kSortThreads), lds_local, s, sa, targs);
     }
     targs.tmat = sa.tmat;
     targs.tmat_rows = L.nbSmall;
     targs.tmat_stride = L.tmat_stride;
+    targs.all_ranges = 1;
     {
       TimedScope ts("small_merge", s);
-      hipLaunchKernelGGL(k_small_merge, dim3(L.nbSmall + 1), dim3(kSortThreads), (size_t)merge_words * 4, s, sa,
+      hipLaunchKernelGGL(k_small_merge, dim3(L.nbSmall * kSmallSplit + 1), dim3(kMergeThreads), lds_merge, s, sa,
                          (uint4*)(ws + L.drec), (uint32_t*)(ws + L.chunk_first), (uint64_t)pair_capacity, ctrl,
                          d_num_pairs, merge_words, targs);
     }
