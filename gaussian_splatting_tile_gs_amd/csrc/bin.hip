@@ -92,6 +92,25 @@ __device__ __forceinline__ void st_dev(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The lanes of the wave whose `bits`-bit digit equals this lane's (a 64-bit lane mask), from one
+// ballot per bit: a lane whose bit is 1 keeps the ballot's lanes, one whose bit is 0 its
+// complement. The flip mask makes that one xor-and per half of the mask.
+template <int MAXBITS>
+__device__ __forceinline__ uint64_t match_digit(uint32_t d, int bits, uint64_t m) {
+  uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
+#pragma unroll
+  for (int b = 0; b < MAXBITS; ++b) {
+    if (b < bits) {  // uniform
+      const uint32_t bit = (d >> b) & 1u;
+      const uint64_t bb = __ballot(bit);
+      const uint32_t flip = bit - 1u;  // 0 keeps the ballot, all ones complements it
+      lo &= (uint32_t)bb ^ flip;
+      hi &= (uint32_t)(bb >> 32) ^ flip;
+    }
+  }
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // Inclusive scan across a wave64 (Kogge-Stone over lane shuffles).
 template <typename T>
 __device__ __forceinline__ T wave_incl_scan(T v, int lane) {
@@ -417,13 +436,7 @@ __device__ __forceinline__ uint32_t count_class(uint32_t c) { return c ? 32u - (
 // Lanes with the same class share one LDS atomic on ctr[cls]; returns a valid lane's slot.
 // Every lane of the wave calls it.
 __device__ __forceinline__ uint32_t wave_class_slot(bool valid, uint32_t cls, uint32_t* ctr, int lane) {
-  uint64_t m = __ballot(valid);
-#pragma unroll
-  for (int b = 0; b < 6; ++b) {
-    const bool bit = (cls >> b) & 1u;
-    const uint64_t bb = __ballot(bit);
-    m &= bit ? bb : ~bb;
-  }
+  const uint64_t m = match_digit<6>(cls, 6, __ballot(valid));
   const int leader = __builtin_ctzll(m | (1ull << 63));
   uint32_t base = 0;
   if (valid && lane == leader) base = atomicAdd(&ctr[cls], (uint32_t)__popcll(m));
@@ -527,9 +540,12 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
       if (sweep == 0 || !one_step) {
         __syncthreads();  // the previous step's reads of s (neighbours included) are done
 #pragma unroll
-        for (int q = 0; q < kFinRows; ++q) {
-          const uint32_t i = (uint32_t)(q * kSortThreads + tid);
-          if (q < rows) s[i] = i < m ? tdiff_at(a, cb + i) : 0u;
+        for (int q = 0; q < kFinRows; q += 2) {  // two rows' loads in flight together
+          const uint32_t i0 = (uint32_t)(q * kSortThreads + tid), i1 = i0 + kSortThreads;
+          const uint32_t v0 = (q < rows && i0 < m) ? tdiff_at(a, cb + i0) : 0u;
+          const uint32_t v1 = (q + 1 < rows && i1 < m) ? tdiff_at(a, cb + i1) : 0u;
+          if (q < rows) s[i0] = v0;
+          if (q + 1 < rows) s[i1] = v1;
         }
         // counts: the inclusive prefix of the differences = the next tile's exclusive one
         const uint32_t dtot = lds_rows_scan(s, rows, carry_d, s_wt, s_rt);
@@ -682,12 +698,7 @@ __device__ __forceinline__ void radix_tile(uint32_t (&k)[ITEMS], uint32_t (&v)[I
     const uint32_t idx = base + (uint32_t)(wave * 64 * ITEMS + i * 64 + lane);
     const bool valid = idx < n;
     const uint32_t d = (k[i] >> shift) & mask;
-    uint64_t m = __ballot(valid);
-    for (int b = 0; b < bits; ++b) {
-      const bool bit = (d >> b) & 1u;
-      const uint64_t bb = __ballot(bit);
-      m &= bit ? bb : ~bb;
-    }
+    const uint64_t m = match_digit<8>(d, bits, __ballot(valid));
     const uint32_t r = (uint32_t)__popcll(m & lt_mask);
     uint32_t pre = 0;
     if (valid) pre = s_wcnt[wave][d];
@@ -1185,13 +1196,7 @@ __device__ __forceinline__ void local_radix_pass(uint32_t (&k)[kSortItems], uint
     const uint32_t d = (k[i] >> shift) & mask;
     // all kLocalBits ballots, unconditionally: the digit's bits above `bits` are 0 in every lane
     // and leave the match mask unchanged
-    uint64_t m = ~0ull;
-#pragma unroll
-    for (int b = 0; b < kLocalBits; ++b) {
-      const bool bit = (d >> b) & 1u;
-      const uint64_t bb = __ballot(bit);
-      m &= bit ? bb : ~bb;
-    }
+    const uint64_t m = match_digit<kLocalBits>(d, kLocalBits, ~0ull);
     const uint32_t r = (uint32_t)__popcll(m & lt_mask);
     const uint32_t pre = s_cnt[wave * kLocalRadix + d];
     rank[i] = pre + r;

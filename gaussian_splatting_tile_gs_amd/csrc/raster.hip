@@ -585,32 +585,29 @@ __global__ __launch_bounds__(kRasterThreads) __attribute__((amdgpu_waves_per_eu(
   const uint32_t chunk_end = hi < len ? hi : len;
 
   // Stage splats [bstart, bstart + cnt) of the list: ids, evaluation records and quadrant masks in
-  // LDS, the sums zeroed; the staging thread keeps its splat's raw conic and opacity for the finish.
-  float rA = 0.0f, rB = 0.0f, rC = 0.0f, ro = 1.0f;
+  // LDS, the sums zeroed; with records, the staging thread keeps its splat's record slot.
   uint32_t rslot = 0;
   auto stage = [&](uint32_t bstart, int cnt) {
     uint32_t qm = 0;
     if (tid < cnt) {
       const uint32_t g = ids[start + bstart + (uint32_t)tid];
       s_id[tid] = g;
-      qm = load_record(g, n, means2d, conics, opac, colors, tx0, ty0, s_a[tid], s_b[tid], s_c[tid]);
-      if (DEPTH) s_z[tid] = g < n ? depths[g] : 0.0f;
-      if (g < n) {
-        rA = conics[3 * g];
-        rB = conics[3 * g + 1];
-        rC = conics[3 * g + 2];
-        ro = opac[g];
-        if (REC) rslot = pair_slot(g, means2d, radii, pair_base, tx, ty, cam, rA, rB, rC, ro);
-      }
+      const RawSplat rs = load_raw<DEPTH>(g, n, means2d, conics, opac, colors, depths);
+      qm = stage_raw(rs, g < n, tx0, ty0, s_a[tid], s_b[tid], s_c[tid]);
+      if (DEPTH) s_z[tid] = rs.z;
+      if (REC && g < n) rslot = pair_slot(g, means2d, radii, pair_base, tx, ty, cam, rs.A, rs.B, rs.C, rs.o);
     }
     if (!DET)
       for (int i = tid; i < cnt * NT; i += kRasterThreads) s_acc[i] = 0.0f;
     publish_quadrant_masks(qm, tid < cnt, s_qm);
   };
   // the 2D gradient of staged splat tid from its sums P, to g2d or its record slot
+  // The conic is taken back from the staged record (its log2(e) scaling undone: within an ulp of
+  // the raw conic), the opacity as staged; so nothing of the splat stays in registers through the walk.
   auto finish = [&](const float* P) {
     const uint32_t g = s_id[tid];
-    const float A = rA, B = rB, C = rC, o = ro;
+    const float4 ra = s_a[tid], rb = s_b[tid];
+    const float A = ra.z / (0.5f * kLog2e), B = rb.x / kLog2e, C = ra.w / (0.5f * kLog2e), o = rb.y;
     float gv[kG2d];
     gv[0] = fmaf(A, P[0], B * P[1]);
     gv[1] = fmaf(B, P[0], C * P[1]);
