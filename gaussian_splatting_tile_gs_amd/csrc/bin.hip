@@ -83,15 +83,6 @@ struct Ctrl {
   uint32_t hist_pair[3][kRadix];
 };
 
-template <typename T>
-__device__ __forceinline__ T ld_dev(const T* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ void st_dev(T* p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // The lanes of the wave whose `bits`-bit digit equals this lane's (a 64-bit lane mask), from one
 // ballot per bit: a lane whose bit is 1 keeps the ballot's lanes, one whose bit is 0 its
 // complement. The flip mask makes that one xor-and per half of the mask.

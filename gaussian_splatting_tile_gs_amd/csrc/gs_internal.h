@@ -49,6 +49,24 @@ inline DevCamera to_dev(const gs_camera& c) {
 __host__ __device__ __forceinline__ float omax(float a, float b) { return (a < b) ? b : a; }
 __host__ __device__ __forceinline__ float omin(float a, float b) { return (b < a) ? b : a; }
 
+// Device-coherent accesses for data that other workgroups of the same launch read: relaxed
+// atomic loads and stores at device scope go past the per-XCD L2 to the point where every XCD
+// sees them, so no L2-wide write-back fence is needed. Once the issuing wave's memory counter has
+// drained (wait_mem) such a store is visible to every workgroup, so a word read after a flag that
+// was set behind it sees it.
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until this wave's memory operations have completed (a workgroup barrier does not: within
+// a workgroup, memory is coherent without it). Before a device-scope flag store, it makes the
+// device-coherent stores ahead of it visible to whoever sees the flag.
+__device__ __forceinline__ void wait_mem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ---------------------------------------------------------------------------------------------
 // Reproducible fp32 exp and log for the activations.
 // exp: Cody & Waite (1980) additive range reduction x = k ln2 + r, with ln2 split into a short

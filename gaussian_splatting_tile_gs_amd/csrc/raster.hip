@@ -208,85 +208,85 @@ __device__ __forceinline__ void blend_step(const SplatEval& e, bool act, float c
 
 // ---------------------------------------------------------------------------------------------
 // k-blend: one 256-thread workgroup per 16x16 tile; wave q owns the 8x8 quadrant q and walks its
-// splats two per iteration (their alphas are independent; the T updates are sequential).
-// With a raster plan, workgroup b takes tile order[b]; with a checkpoint buffer too, a tile
-// longer than the plan's chunk length L accumulates its colour per chunk of L list entries and
-// stores, for every chunk j, each pixel's transmittance after the chunk and the colour the chunk
-// added (slot j). The backward then splits the tile into chunks that run in parallel.
-// DEPTH: also the depth channel, D = sum z_i alpha_i T_i (background depth 0; the chunks' depth
-// contributions go to ckpt_d, one float per pixel and slot).
+// splats two per iteration (their alphas are independent; the T updates are sequential). With a
+// raster plan, workgroup b takes tile order[b].
+// CHUNKED (a plan and the raster workspace: a training forward): the backward splits a tile longer
+// than the plan's chunk length L into chunks of L list entries, so the forward stores for every
+// chunk j, per pixel, the transmittance after the chunk and the colour (and depth) it added
+// (checkpoint slot j of the tile). A tile of two chunks is walked by one workgroup that stores
+// the slots as it passes the chunk boundaries. A tile of three or more chunks is split: its
+// chunks are blended at once, one workgroup each (the plan's extra work items (tile, j >= 1) and
+// the tile's own workgroup for chunk 0). The workgroup of chunk j >= 1 first forms the
+// transmittance factor of chunk j - 1 (the product of 1 - alpha over its contributing splats, no
+// stop rule; a factor that falls to 1e-4 or below stays there) and publishes it, then waits for
+// the factors of chunks 0 .. j - 2 published by the workgroups of chunks 1 .. j - 1, starts from
+// their product and blends its chunk. A pixel that stopped in an earlier chunk starts at or below
+// 1e-4 and so adds nothing. The last of a split tile's workgroups to finish forms its pixels: the
+// transmittance of the first chunk that stopped (else of the last chunk), the colours summed over
+// the chunks in order, the last added entry of the last chunk that added one.
+// The chunk workgroups take tickets in launch order, so a workgroup only waits for workgroups that
+// have started; every wait is also bounded.
+// DEPTH: also the depth channel, D = sum z_i alpha_i T_i (background depth 0).
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ float l1_sign(float d) { return d > 0.0f ? 1.0f : (d < 0.0f ? -1.0f : 0.0f); }
 
-template <bool COUNT, bool CKPT, bool DEPTH>
-__global__ __launch_bounds__(kRasterThreads) void k_blend(
-    uint32_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ plan, uint32_t ntiles,
-    float4* __restrict__ ckpt, float* __restrict__ ckpt_d, const uint32_t* __restrict__ ids,
-    const float* __restrict__ means2d, const float* __restrict__ conics, const float* __restrict__ opac,
-    const float* __restrict__ colors, const float* __restrict__ depths, const int32_t* __restrict__ radii,
-    DevCamera cam, float* __restrict__ image, float* __restrict__ depth_out, float* __restrict__ final_T,
-    uint32_t* __restrict__ n_contrib, unsigned long long* __restrict__ eval_count,
-    const float* __restrict__ l1_target, float* __restrict__ l1_grad, float l1_scale) {
-  __shared__ float4 s_a[kBatch];
-  __shared__ float4 s_b[kBatch];
-  __shared__ float s_c[kBatch];
-  __shared__ float s_z[DEPTH ? kBatch : 1];
-  __shared__ uint64_t s_qm[4][4];
+constexpr uint32_t kSplitMinChunks = 3;      // tiles of this many chunks or more are split
+constexpr uint32_t kWaitPolls = 1u << 22;    // a bound on each wait for a published factor
 
-  const int tile = plan ? (int)plan[kPlanOrder + blockIdx.x] : (int)blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int tx = tile % cam.tiles_x, ty = tile / cam.tiles_x;
-  const float tx0 = (float)(tx * kTile), ty0 = (float)(ty * kTile);
-  const int px_i = tx * kTile + (wave & 1) * 8 + (lane & 7);
-  const int py_i = ty * kTile + (wave >> 1) * 8 + (lane >> 3);
-  const bool inside = px_i < cam.W && py_i < cam.H;
-  const float px = (float)px_i + 0.5f, py = (float)py_i + 0.5f;
-  const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
+// The raster workspace, per checkpoint slot and pixel: (T after the chunk, colour the chunk added),
+// the depth the chunk added, the transmittance factor of the chunk, the chunk's last added entry
+// with bit 31 set when the pixel stopped in it. Then the chunked forward's synchronisation words:
+// [0] ticket counter, [1] finished ticketed workgroups, per slot an arrival counter (used at a
+// split tile's first slot) and a published-factor flag. They are zero between calls (the last
+// ticketed workgroup resets the two counters, a split tile's last workgroup its own words), so
+// the workspace is zeroed once before its first use.
+struct RasterWs {
+  float4* ckpt;
+  float* ckpt_d;
+  float* tprod;
+  uint32_t* lastc;
+  uint32_t* sync;
+};
+constexpr size_t kRasterSyncWords = 2 + 2 * (size_t)kPlanMaxSlots;
+__host__ __device__ inline RasterWs raster_ws_parts(void* base) {
+  RasterWs w{};
+  if (!base) return w;
+  const size_t px = (size_t)kPlanMaxSlots * 256;
+  w.ckpt = (float4*)base;
+  w.ckpt_d = (float*)(w.ckpt + px);
+  w.tprod = w.ckpt_d + px;
+  w.lastc = (uint32_t*)(w.tprod + px);
+  w.sync = w.lastc + px;
+  return w;
+}
 
-  // (cr, cg, cb): the colour added so far; with checkpoints, by the current chunk only, and
-  // (pr, pg, pb) by the chunks before it
-  float T = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f, pr = 0.0f, pg = 0.0f, pb = 0.0f, cd = 0.0f, pd = 0.0f;
-  uint32_t last = 0, n_eval = 0;
-  bool done = !inside;
-  // chunk boundaries are multiples of L >= kBatch, so they fall on batch starts
-  const uint32_t len = end - start;
-  const uint32_t L = CKPT ? plan[kPlanChunk] : 0u;
-  uint32_t next_b = (CKPT && len > L) ? L : 0xFFFFFFFFu;
-  const size_t slot_px = (CKPT && len > L) ? (size_t)plan[kPlanOrder + ntiles + tile] * kRasterThreads + tid : 0;
-  float4* ck = (CKPT && len > L) ? ckpt + slot_px : nullptr;
-  float* ckd = (DEPTH && CKPT && len > L) ? ckpt_d + slot_px : nullptr;
-  auto store_ckpt = [&]() {
-    *ck = make_float4(T, cr, cg, cb);
-    ck += kRasterThreads;
-    pr += cr;
-    pg += cg;
-    pb += cb;
-    cr = cg = cb = 0.0f;
-    if (DEPTH) {
-      *ckd = cd;
-      ckd += kRasterThreads;
-      pd += cd;
-      cd = 0.0f;
-    }
-    next_b += L;
-    if (next_b >= len) next_b = 0xFFFFFFFFu;
-  };
-  // Software pipeline over the batches: while batch k is walked, this thread's record of batch
-  // k + 1 is being loaded into registers and its id of batch k + 2 too, so neither the id load
-  // nor the record gather waits at a batch start.
-  uint32_t id_next2 = start + kBatch + tid < end ? ids[start + kBatch + tid] : n;
-  RawSplat raw = load_raw<DEPTH>(start + tid < end ? ids[start + tid] : n, n, means2d, conics, opac, colors, depths);
-  for (uint32_t bs = start; bs < end; bs += kBatch) {
+// Walks list entries [rs, re) of a tile (staged 256 at a time, the next batch's records loading
+// while a batch is walked) and calls visit(k0, k1, has1, list1) for the staged splats reaching the
+// wave's quadrant, two per call; stops when every pixel of the workgroup is done. at_batch(e) is
+// called at each batch start (workgroup-uniform) with the batch's first list entry.
+template <bool DEPTH, typename VISIT, typename AT_BATCH>
+__device__ __forceinline__ void walk_entries(uint32_t n, const uint32_t* __restrict__ ids, uint32_t start, uint32_t rs,
+                                             uint32_t re, const float* __restrict__ means2d,
+                                             const float* __restrict__ conics, const float* __restrict__ opac,
+                                             const float* __restrict__ colors, const float* __restrict__ depths,
+                                             float tx0, float ty0, const bool& done, float4* s_a, float4* s_b,
+                                             float* s_c, float* s_z, uint64_t (*s_qm)[4], VISIT visit,
+                                             AT_BATCH at_batch) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const uint32_t b0 = start + rs, e0 = start + re;
+  uint32_t id_next2 = b0 + kBatch + tid < e0 ? ids[b0 + kBatch + tid] : n;
+  RawSplat raw = load_raw<DEPTH>(b0 + tid < e0 ? ids[b0 + tid] : n, n, means2d, conics, opac, colors, depths);
+  for (uint32_t bs = b0; bs < e0; bs += kBatch) {
     if (__syncthreads_count(done) == kRasterThreads) break;
-    if (CKPT && bs - start >= next_b) store_ckpt();  // workgroup-uniform
-    const bool valid = bs + tid < end;
+    at_batch(bs - start);
+    const bool valid = bs + tid < e0;
     const uint32_t qm = stage_raw(raw, valid, tx0, ty0, s_a[tid], s_b[tid], s_c[tid]);
     if (DEPTH) s_z[tid] = raw.z;
     publish_quadrant_masks(qm, valid, s_qm);
     {
       const uint32_t j2 = bs + 2 * kBatch + tid;
       raw = load_raw<DEPTH>(id_next2, n, means2d, conics, opac, colors, depths);
-      id_next2 = j2 < end ? ids[j2] : n;
+      id_next2 = j2 < e0 ? ids[j2] : n;
     }
     __syncthreads();
     const uint32_t list1 = bs - start + 1u;  // 1-based list index of staged splat 0
@@ -299,7 +299,128 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
         const bool has1 = m != 0;
         const int bit1 = has1 ? __builtin_ctzll(m) : bit0;
         if (has1) m &= m - 1;
-        const int k0 = w * 64 + bit0, k1 = w * 64 + bit1;
+        visit(w * 64 + bit0, w * 64 + bit1, has1, list1);
+      }
+    }
+  }
+}
+
+template <bool COUNT, bool CHUNKED, bool DEPTH>
+__global__ __launch_bounds__(kRasterThreads) void k_blend(
+    uint32_t n, const uint32_t* __restrict__ ranges, const uint32_t* __restrict__ plan, uint32_t ntiles, RasterWs ws,
+    const uint32_t* __restrict__ ids, const float* __restrict__ means2d, const float* __restrict__ conics,
+    const float* __restrict__ opac, const float* __restrict__ colors, const float* __restrict__ depths,
+    DevCamera cam, float* __restrict__ image, float* __restrict__ depth_out, float* __restrict__ final_T,
+    uint32_t* __restrict__ n_contrib, unsigned long long* __restrict__ eval_count,
+    const float* __restrict__ l1_target, float* __restrict__ l1_grad, float l1_scale) {
+  __shared__ float4 s_a[kBatch];
+  __shared__ float4 s_b[kBatch];
+  __shared__ float s_c[kBatch];
+  __shared__ float s_z[DEPTH ? kBatch : 1];
+  __shared__ uint64_t s_qm[4][4];
+  __shared__ uint32_t s_word;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int tile = -1;
+  uint32_t chunk = 0, nx = 0;
+  bool ticketed = false;
+  if (CHUNKED) {
+    nx = plan[kPlanExtra];
+    if (blockIdx.x < nx) {
+      // a chunk item: its ticket picks the item, so items are taken in the order they start
+      if (tid == 0) s_word = atomicAdd(&ws.sync[0], 1u);
+      __syncthreads();
+      const uint32_t b = s_word;
+      ticketed = true;
+      if (b < nx) {  // always, with the counters zero at the launch
+        const uint32_t* item = plan + kPlanOrder + 2 * ntiles + 2 * b;
+        tile = (int)item[0];
+        chunk = item[1];
+      }
+    } else {
+      if (blockIdx.x - nx >= ntiles) return;  // workgroup-uniform
+      tile = (int)plan[kPlanOrder + blockIdx.x - nx];
+    }
+  } else {
+    tile = plan ? (int)plan[kPlanOrder + blockIdx.x] : (int)blockIdx.x;
+  }
+  uint32_t n_eval = 0;
+  if (tile >= 0) {
+    const int tx = tile % cam.tiles_x, ty = tile / cam.tiles_x;
+    const float tx0 = (float)(tx * kTile), ty0 = (float)(ty * kTile);
+    const int px_i = tx * kTile + (wave & 1) * 8 + (lane & 7);
+    const int py_i = ty * kTile + (wave >> 1) * 8 + (lane >> 3);
+    const bool inside = px_i < cam.W && py_i < cam.H;
+    const float px = (float)px_i + 0.5f, py = (float)py_i + 0.5f;
+    const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
+    const uint32_t len = end - start;
+    const uint32_t L = CHUNKED ? plan[kPlanChunk] : 1u;
+    const uint32_t nch = (CHUNKED && len > L) ? (len + L - 1u) / L : 1u;
+    const bool split = CHUNKED && nch >= kSplitMinChunks;
+    const uint32_t sbase = nch > 1 ? plan[kPlanOrder + ntiles + tile] : 0u;  // the tile's first slot
+    // a chunk item of an unsplit tile has nothing to do: the tile's workgroup walks all of it
+    if (chunk == 0 || split) {
+      const uint32_t rs = split ? chunk * L : 0u;
+      const uint32_t re = split ? (rs + L < len ? rs + L : len) : len;
+      float T = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f, cd = 0.0f;
+      if (split && chunk > 0) {
+        // the factor of chunk - 1, published for the later chunks
+        float F = 1.0f;
+        bool fdone = !inside;
+        walk_entries<false>(n, ids, start, rs - L, rs, means2d, conics, opac, colors, depths, tx0, ty0, fdone, s_a,
+                            s_b, s_c, s_z, s_qm, [&](int k0, int k1, bool has1, uint32_t) {
+          const float4 a0 = s_a[k0], b0 = s_b[k0];
+          const float4 a1 = s_a[k1], b1 = s_b[k1];
+          const SplatEval e0 = eval_splat(a0.x - px, a0.y - py, a0.z, b0.x, a0.w, b0.y);
+          const SplatEval e1 = eval_splat(a1.x - px, a1.y - py, a1.z, b1.x, a1.w, b1.y);
+          F = (!fdone && !e0.skip) ? F * (1.0f - e0.alpha) : F;
+          F = (has1 && !fdone && !e1.skip) ? F * (1.0f - e1.alpha) : F;
+          fdone = fdone || __float_as_uint(F) <= __float_as_uint(kTransmittanceMin);
+        }, [](uint32_t) {});
+        // published with device-coherent stores, complete before the barrier and so before the flag
+        if (inside) st_dev(ws.tprod + (size_t)(sbase + chunk - 1u) * kRasterThreads + tid, F);
+        wait_mem();
+        __syncthreads();
+        if (tid == 0) {
+          uint32_t* flag = ws.sync + 2 + kPlanMaxSlots + sbase;
+          st_dev(flag + chunk - 1u, 1u);
+          for (uint32_t i = 0; i + 1u < chunk; ++i) {
+            uint32_t polls = 0;
+            while (ld_dev(flag + i) == 0u && ++polls < kWaitPolls) __builtin_amdgcn_s_sleep(2);
+          }
+        }
+        __syncthreads();
+        if (inside) {
+          for (uint32_t i = 0; i + 1u < chunk; ++i) T *= ld_dev(ws.tprod + (size_t)(sbase + i) * kRasterThreads + tid);
+          T *= F;
+        }
+      }
+      uint32_t last = 0;
+      // a chunk that starts at or below 1e-4 would stop at its first contributing splat: done already
+      bool done = !inside || __float_as_uint(T) <= __float_as_uint(kTransmittanceMin);
+      // an unsplit tile of two chunks stores slot j as it passes the start of chunk j + 1; (pr, pg,
+      // pb, pd) hold the colour of the chunks before the current one
+      float pr = 0.0f, pg = 0.0f, pb = 0.0f, pd = 0.0f;
+      const bool seq_ckpt = CHUNKED && !split && nch > 1;
+      uint32_t next_b = seq_ckpt ? L : 0xFFFFFFFFu;
+      const size_t slot0 = (size_t)sbase * kRasterThreads + tid;
+      size_t cur = slot0;  // the slot of the chunk being walked (sequential checkpoints)
+      auto store_ckpt = [&]() {
+        if (inside) {
+          ws.ckpt[cur] = make_float4(T, cr, cg, cb);
+          if (DEPTH) ws.ckpt_d[cur] = cd;
+        }
+        cur += kRasterThreads;
+        pr += cr;
+        pg += cg;
+        pb += cb;
+        pd += cd;
+        cr = cg = cb = cd = 0.0f;
+        next_b += L;
+        if (next_b >= len) next_b = 0xFFFFFFFFu;
+      };
+      walk_entries<DEPTH>(n, ids, start, rs, re, means2d, conics, opac, colors, depths, tx0, ty0, done, s_a, s_b,
+                          s_c, s_z, s_qm, [&](int k0, int k1, bool has1, uint32_t list1) {
         const float4 a0 = s_a[k0], b0 = s_b[k0];
         const float4 a1 = s_a[k1], b1 = s_b[k1];
         const float c0 = s_c[k0], c1 = s_c[k1];
@@ -309,34 +430,86 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
         if (COUNT) n_eval += (done ? 0u : 1u) + ((done || !has1) ? 0u : 1u);
         blend_step<DEPTH>(e0, true, b0.z, b0.w, c0, z0, list1 + (uint32_t)k0, T, cr, cg, cb, cd, last, done);
         blend_step<DEPTH>(e1, has1, b1.z, b1.w, c1, z1, list1 + (uint32_t)k1, T, cr, cg, cb, cd, last, done);
+      }, [&](uint32_t e) {
+        if (seq_ckpt && e >= next_b) store_ckpt();  // workgroup-uniform
+      });
+      if (seq_ckpt) {
+        while (next_b != 0xFFFFFFFFu) store_ckpt();  // boundaries past the last walked batch
+        if (inside) {  // the last chunk's slot
+          ws.ckpt[cur] = make_float4(T, cr, cg, cb);
+          if (DEPTH) ws.ckpt_d[cur] = cd;
+        }
+        cr += pr;
+        cg += pg;
+        cb += pb;
+        cd += pd;
+      }
+      bool finish = !split;
+      if (split) {
+        // this chunk's slot; the tile's last workgroup to get here forms its pixels
+        const size_t o = slot0 + (size_t)chunk * kRasterThreads;
+        if (inside) {  // device-coherent stores, complete before the barrier and so before the arrival
+          float* ck = (float*)(ws.ckpt + o);
+          st_dev(ck + 0, T);
+          st_dev(ck + 1, cr);
+          st_dev(ck + 2, cg);
+          st_dev(ck + 3, cb);
+          if (DEPTH) st_dev(ws.ckpt_d + o, cd);
+          st_dev(ws.lastc + o, last | (done ? 0x80000000u : 0u));
+        }
+        wait_mem();
+        __syncthreads();
+        if (tid == 0) s_word = atomicAdd(ws.sync + 2 + sbase, 1u);
+        __syncthreads();
+        finish = s_word == nch - 1u;
+        if (finish) {
+          T = 1.0f;
+          cr = cg = cb = cd = 0.0f;
+          last = 0;
+          bool stopped = false;
+          for (uint32_t c = 0; c < nch && inside; ++c) {
+            const size_t oc = slot0 + (size_t)c * kRasterThreads;
+            const float* ck = (const float*)(ws.ckpt + oc);
+            const float sT = ld_dev(ck + 0);
+            cr += ld_dev(ck + 1);
+            cg += ld_dev(ck + 2);
+            cb += ld_dev(ck + 3);
+            const uint32_t lc = ld_dev(ws.lastc + oc);
+            if (DEPTH) cd += ld_dev(ws.ckpt_d + oc);
+            last = max(last, lc & 0x7FFFFFFFu);
+            if (!stopped) T = sT;  // the first chunk that stopped holds the final transmittance
+            stopped = stopped || (lc >> 31) != 0u;
+          }
+          // every workgroup of the tile has arrived, so no one reads its words any more
+          if (tid == 0) st_dev(ws.sync + 2 + sbase, 0u);
+          for (uint32_t i = tid; i + 1u < nch; i += kRasterThreads) st_dev(ws.sync + 2 + kPlanMaxSlots + sbase + i, 0u);
+        }
+      }
+      if (finish && inside) {
+        const int p = py_i * cam.W + px_i;
+        const float ir = fmaf(T, cam.bg[0], cr), ig = fmaf(T, cam.bg[1], cg), ib = fmaf(T, cam.bg[2], cb);
+        image[3 * p + 0] = ir;
+        image[3 * p + 1] = ig;
+        image[3 * p + 2] = ib;
+        if (l1_target) {  // uniform: the L1 gradient sign(image - target) / (3 h w), as gs_loss_l1 forms it
+          l1_grad[3 * p + 0] = l1_sign(ir - l1_target[3 * p + 0]) * l1_scale;
+          l1_grad[3 * p + 1] = l1_sign(ig - l1_target[3 * p + 1]) * l1_scale;
+          l1_grad[3 * p + 2] = l1_sign(ib - l1_target[3 * p + 2]) * l1_scale;
+        }
+        final_T[p] = T;
+        n_contrib[p] = last;
+        if (DEPTH) depth_out[p] = cd;  // background depth 0
       }
     }
   }
-  if (CKPT) {
-    while (next_b != 0xFFFFFFFFu) store_ckpt();  // boundaries past the last walked batch
-    if (ck) *ck = make_float4(T, cr, cg, cb);    // the last chunk's slot
-    if (DEPTH && ckd) *ckd = cd;
-    cr += pr;
-    cg += pg;
-    cb += pb;
-    cd += pd;
-  }
-  if (inside) {
-    const int p = py_i * cam.W + px_i;
-    const float ir = fmaf(T, cam.bg[0], cr), ig = fmaf(T, cam.bg[1], cg), ib = fmaf(T, cam.bg[2], cb);
-    image[3 * p + 0] = ir;
-    image[3 * p + 1] = ig;
-    image[3 * p + 2] = ib;
-    if (l1_target) {  // uniform: the L1 gradient sign(image - target) / (3 h w), as gs_loss_l1 forms it
-      l1_grad[3 * p + 0] = l1_sign(ir - l1_target[3 * p + 0]) * l1_scale;
-      l1_grad[3 * p + 1] = l1_sign(ig - l1_target[3 * p + 1]) * l1_scale;
-      l1_grad[3 * p + 2] = l1_sign(ib - l1_target[3 * p + 2]) * l1_scale;
-    }
-    final_T[p] = T;
-    n_contrib[p] = last;
-    if (DEPTH) depth_out[p] = cd;  // background depth 0
-  }
   if (COUNT) count_evals(n_eval, eval_count);
+  if (CHUNKED && ticketed && tid == 0) {
+    // the last ticketed workgroup to finish: every ticket has been taken, so the counters reset
+    if (atomicAdd(ws.sync + 1, 1u) == nx - 1u) {
+      st_dev(ws.sync + 0, 0u);
+      st_dev(ws.sync + 1, 0u);
+    }
+  }
 }
 
 // gfx950 lane exchanges: v_permlane32_swap trades lanes 32-63 of its first operand for lanes 0-31
@@ -1169,8 +1342,10 @@ bool proj_ok(const gs_projected* p) {
 }  // namespace
 
 extern "C" size_t gs_raster_workspace_bytes(void) {
-  // per slot and pixel: (T, r, g, b) and the depth channel's contribution
-  return (size_t)kPlanMaxSlots * kRasterThreads * (sizeof(float4) + sizeof(float));
+  // per slot and pixel: (T, r, g, b), the depth channel's contribution, the chunk's transmittance
+  // factor, its last added entry and stop flag; then the chunked forward's synchronisation words
+  return (size_t)kPlanMaxSlots * kRasterThreads * (sizeof(float4) + 2 * sizeof(float) + sizeof(uint32_t)) +
+         kRasterSyncWords * sizeof(uint32_t);
 }
 
 namespace {
@@ -1191,7 +1366,8 @@ gs_status rasterize_fwd(const char* name, int32_t n, const gs_projected* proj, c
   const DevCamera dc = to_dev(*cam);
   hipStream_t s = (hipStream_t)stream;
   {
-    TimedScope ts("blend", s);
+    // with a plan and the raster workspace (a training forward) the checkpoints are stored and
+    // tiles of three or more chunks are blended chunk by chunk in parallel
     const bool ck = d_raster_plan && d_raster_ws;
     const bool dep = d_depth != nullptr;
     auto pick = [&](auto c_, auto k_, auto d_) {
@@ -1203,14 +1379,20 @@ gs_status rasterize_fwd(const char* name, int32_t n, const gs_projected* proj, c
                                    : (dep ? pick(T1{}, F0{}, T1{}) : pick(T1{}, F0{}, F0{})))
                              : (ck ? (dep ? pick(F0{}, T1{}, T1{}) : pick(F0{}, T1{}, F0{}))
                                    : (dep ? pick(F0{}, F0{}, T1{}) : pick(F0{}, F0{}, F0{})));
-    float4* ws4 = d_raster_plan ? (float4*)d_raster_ws : nullptr;
-    float* wsd = ws4 ? (float*)(ws4 + (size_t)kPlanMaxSlots * kRasterThreads) : nullptr;
-    hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges,
-                       d_raster_plan, (uint32_t)ntiles, ws4, wsd, d_ids, n > 0 ? proj->d_means2d : nullptr,
-                       n > 0 ? proj->d_conics : nullptr, n > 0 ? proj->d_opacities : nullptr,
-                       n > 0 ? proj->d_colors : nullptr, n > 0 ? proj->d_depths : nullptr,
-                       n > 0 ? proj->d_radii : nullptr, dc, d_image, d_depth, d_final_T, d_n_contrib,
-                       (unsigned long long*)d_eval_count, d_target, d_dL_dimage, l1_scale);
+    const RasterWs wsp = raster_ws_parts(ck ? d_raster_ws : nullptr);
+    const float* m2 = n > 0 ? proj->d_means2d : nullptr;
+    const float* co = n > 0 ? proj->d_conics : nullptr;
+    const float* op = n > 0 ? proj->d_opacities : nullptr;
+    const float* cl = n > 0 ? proj->d_colors : nullptr;
+    const float* dp = n > 0 ? proj->d_depths : nullptr;
+    {
+      TimedScope ts("blend", s);
+      // a training forward adds the chunk items (at most kPlanMaxChunks; the plan says how many)
+      const unsigned grid = (unsigned)(ck ? ntiles + kPlanMaxChunks : ntiles);
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges, d_raster_plan,
+                         (uint32_t)ntiles, wsp, d_ids, m2, co, op, cl, dp, dc, d_image, d_depth, d_final_T,
+                         d_n_contrib, (unsigned long long*)d_eval_count, d_target, d_dL_dimage, l1_scale);
+    }
   }
   return check_launch(name);
 }

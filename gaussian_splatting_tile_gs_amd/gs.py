@@ -21,6 +21,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgs_hip.so")
 
 GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_LIMIT, GS_ERR_DEVICE = 0, 1, 2, 3, 4
+# the raster workspace ends with the chunked forward's synchronisation words (two counters, then an
+# arrival counter and a flag per checkpoint slot, 4096 slots), zero between calls
+RASTER_SYNC_BYTES = 4 * (2 + 2 * 4096)
 
 
 class GsError(RuntimeError):
@@ -337,7 +340,7 @@ class Pipeline:
         cam0 = GsCamera()
         cam0.width, cam0.height = width, height
         self.plan = torch.empty(gs_raster_plan_words(cam0), device=device, dtype=torch.int32)
-        self.raster_ws = torch.empty(gs_raster_workspace_bytes(), device=device, dtype=torch.uint8)
+        self.raster_ws = torch.zeros(gs_raster_workspace_bytes(), device=device, dtype=torch.uint8)
         self.bwd_ws = torch.empty(gs_bwd_workspace_bytes(self.n), device=device, dtype=torch.uint8)
         K = (params["sh_degree"] + 1) ** 2
         f = dict(device=device, dtype=torch.float32)

@@ -184,10 +184,15 @@ gs_status gs_bin_and_sort_noalloc(int32_t n, const gs_projected* proj, const gs_
  * Inputs: proj, d_ids and d_tile_ranges from gs_bin_and_sort for the same camera;
  *   d_raster_plan (optional, NULL = tiles in id order) from that gs_bin_and_sort call: the tiles
  *   are taken in its order (scheduling only, the results do not change); d_raster_ws (optional,
- *   gs_raster_workspace_bytes() bytes, device, used only with a plan): the forward stores there,
- *   for tiles longer than the plan's chunk length L, per chunk of L list entries and per pixel
- *   the transmittance after the chunk and the colour the chunk added, which lets
- *   gs_rasterize_bwd split such tiles (the image is then summed chunk by chunk).
+ *   gs_raster_workspace_bytes() bytes, device, zero-filled by the caller before its first use,
+ *   used only with a plan; every call leaves its synchronisation words zero again): the forward
+ *   stores there, for tiles longer than the plan's chunk length L, per chunk of L list entries
+ *   and per pixel the transmittance after the chunk and the colour the chunk added, which lets
+ *   gs_rasterize_bwd split such tiles. With it, a tile of three or more chunks is blended chunk
+ *   by chunk in parallel: chunk j starts from the product of the earlier chunks' transmittance
+ *   factors (1 - alpha multiplied over their contributing splats), and the image is summed chunk
+ *   by chunk, so results equal those without a workspace up to rounding. Calls that share a
+ *   workspace must not overlap (one stream, or ordered streams).
  * Outputs: d_image [h,w,3]; d_depth [h,w] (optional, NULL = not rendered): the depth channel,
  *   the splats' camera z through the same weights, D = sum z_i alpha_i T_i with background depth
  *   0 (section 5: any channel, depth included, blends with the same weights; with a workspace

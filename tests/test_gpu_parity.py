@@ -77,7 +77,7 @@ def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7
     fT = torch.empty(H, W, device="cuda")
     nc = torch.empty(H, W, device="cuda", dtype=torch.int32)
     evals = torch.zeros(1, device="cuda", dtype=torch.int64)
-    rws = torch.empty(gs.gs_raster_workspace_bytes(), device="cuda", dtype=torch.uint8)
+    rws = torch.zeros(gs.gs_raster_workspace_bytes(), device="cuda", dtype=torch.uint8)
     dep = torch.empty(H, W, device="cuda") if depth else None
     gs.gs_rasterize_fwd(params["n"], proj, cam, ids, ranges, img, fT, nc, evals, plan=plan, raster_ws=rws, depth=dep)
     torch.cuda.synchronize()
@@ -609,6 +609,56 @@ def test_concurrent_streams_match_sequential(env):
             assert torch.equal(pipes[k].image, img), f"camera {first + k}: image differs"
             for name, v in grads.items():
                 assert torch.equal(pipes[k].grads[name], v), f"camera {first + k}: {name} differs"
+
+
+@pytest.mark.parametrize("name,depth", [("mid_150k_sh3", False), ("mid_150k_sh3", True), ("deep", False)])
+def test_chunked_forward_matches_whole_tiles(env, name, depth):
+    """A training forward (plan and raster workspace) blends the chunks of each tile of three or
+    more chunks at once, every chunk starting from the product of the earlier chunks'
+    transmittance factors. Its pixels match one workgroup per tile within rounding (the last
+    added entry too, off the pixels whose stop decision sits within rounding of 1e-4), a second
+    call gives the same bits, and the call leaves the workspace's synchronisation words zero."""
+    gs, torch = env
+    if name == "deep":
+        # 40,000 splats over a ragged 150 x 90 image: tiles of thousands of entries (many chunks)
+        W, H = 150, 90
+        scene = synth.random_scene(40000, seed=51, width=W, height=H, focal=110.0, logit_std=1.5)
+        cam = gs.make_camera(synth.make_camera(np.eye(4), W, H, 110.0, background=(0.3, 0.2, 0.1)))
+    else:
+        wl = synth.WORKLOADS[name]
+        W, H, scene = wl.width, wl.height, synth.make_scene(wl)
+        cam = gs.make_camera(synth.make_cameras(wl)[0])
+    params = gs.scene_to_device(scene)
+    p = gs.Pipeline(params, W, H, pair_capacity=1 << 20)
+    p.project(cam)
+    p.bin(cam)
+    plan = p.plan.cpu().numpy().view(np.uint32)
+    lens = np.diff(p.ranges.cpu().numpy().view(np.uint32).astype(np.int64), axis=1)[:, 0]
+    nch = -(-lens // int(plan[0]))
+    log(f"[{name}] L={plan[0]} tiles of >= 3 chunks: {(nch >= 3).sum()}, longest {nch.max()} chunks")
+    assert (nch >= 3).sum() >= 10
+    outs = []
+    for ck in (False, True, True):
+        dep = torch.empty(H, W, device="cuda") if depth else None
+        p.forward(cam, checkpoints=ck, depth=dep)
+        torch.cuda.synchronize()
+        outs.append((p.image.clone(), p.final_T.clone(), p.n_contrib.clone(), dep))
+        if ck:
+            sync = p.raster_ws[-gs.RASTER_SYNC_BYTES:]
+            assert int(torch.count_nonzero(sync)) == 0, "synchronisation words left set"
+    for a, b in zip(outs[1], outs[2]):
+        assert a is None or torch.equal(a, b), "two chunked forwards differ"
+    img0, T0, nc0, d0 = (x.cpu().numpy() if x is not None else None for x in outs[0])
+    img1, T1, nc1, d1 = (x.cpu().numpy() if x is not None else None for x in outs[1])
+    same = nc0 == nc1
+    assert same.mean() >= 0.999, f"{(~same).sum()} pixels end at another entry"
+    assert np.abs(img1 - img0)[same].max() <= 1e-5
+    assert np.abs(T1 - T0)[same].max() <= 1e-6
+    assert np.abs(img1 - img0).max() <= 1e-4 + 1e-6
+    if depth:
+        assert np.abs(d1 - d0)[same].max() <= 1e-5 * max(1.0, float(np.abs(d0).max()))
+    log(f"[{name}] chunked forward: {(~same).sum()} pixels end at another entry, max |diff| "
+        f"{np.abs(img1 - img0).max():.2e}")
 
 
 @pytest.mark.parametrize("case", ["distill_30k", "ragged"])
