@@ -93,8 +93,10 @@ def kernel_bytes(name, stats):
         # record out (16 B) per Gaussian
         "small_merge": 44.0 * N,
         "bin_prep": 48.0 * N,
-        "depth_sort_pass": 16.0 * N,
-        "scan": 40.0 * N,
+        # the first depth pass sorts all N keys and drops the culled ones, the other three sort the
+        # visible ones (per launch: the mean of the four passes)
+        "depth_sort_pass": (16.0 * N + 3 * 16.0 * stats["visible"]) / 4.0,
+        "scan": 40.0 * stats["visible"],
         # the emission fused with the first pair pass: depth-ordered records in, pairs out
         # (the final pass when it is the only one: 64-bit keys, ids and the depth gather)
         "emit_sort": 16.0 * stats["visible"] + (16.0 if stats["pair_passes"] == 0 else 8.0) * P,

@@ -13,7 +13,10 @@
 //                     tile range the later kernels rely on (no memset nodes, no host wait)
 //   2. k_hist_reduce  the per-workgroup depth histograms summed (beyond 32 workgroups; below
 //                     that each depth pass sums them itself)
-//   3. 4 x k_onesweep stable LSD radix sort of the N Gaussians by depth bits; extra workgroups of
+//   3. 4 x k_onesweep stable LSD radix sort of the N Gaussians by depth bits; the first pass drops
+//                     the culled ones (their key is 0xFFFFFFFF and the histograms leave them out),
+//                     so the later passes, the scan and the emission see only the V drawn ones
+//                     (a camera inside a large scene draws a tenth of it); extra workgroups of
 //                     the first two passes count the pairs of every tile (they do not depend on
 //                     the depth order) and turn the counts into the tile ranges and the
 //                     tile-digit histograms of the pair sort
@@ -44,8 +47,9 @@
 // index order (four keys per lane keep each wave's ranking chain short).
 //
 // Bytes per pair (algorithmic): emit writes 8; each pair pass reads 8 and writes 8 (the last
-// writes 12 and gathers 4). With 2 pair passes that is 8 + 16 + 24 = 48 B/pair, plus about
-// 150 B per Gaussian for the depth sort, the rectangles and the scan.
+// writes 12 and gathers 4). With 2 pair passes that is 8 + 16 + 24 = 48 B/pair, plus 64 B per
+// Gaussian (prep and the first depth pass) and about 90 B per drawn Gaussian (three depth
+// passes, the scan, the emission's records).
 #include <algorithm>
 #include <mutex>
 
@@ -78,6 +82,7 @@ constexpr uint64_t kValMask64 = (1ull << 62) - 1;
 struct Ctrl {
   uint64_t num_pairs;    // P
   uint64_t eff_pairs;    // P if it fits the capacity, else 0: what the pair kernels process
+  uint64_t n_visible;    // drawn Gaussians (large frames: the depth sort's length after its first pass)
   uint32_t tickets[16];  // [0..3] depth passes, [4..6] pair passes, [7] scan, [8] scan workgroups done
   uint32_t hist_depth[4][kRadix];
   uint32_t hist_pair[3][kRadix];
@@ -231,8 +236,10 @@ __global__ __launch_bounds__(kSortThreads) void k_bin_prep(int32_t n, const floa
         h = (uint32_t)(rc.y1 - rc.y0);
       }
       rec[idx] = make_uint4(t[i], tb, w, h);
+      if (t[i] > 0) {  // culled keys leave the depth sort in its first pass
 #pragma unroll
-      for (int p = 0; p < 4; ++p) atomicAdd(&s_hist[p][(k[i] >> (8 * p)) & 0xFF], 1u);
+        for (int p = 0; p < 4; ++p) atomicAdd(&s_hist[p][(k[i] >> (8 * p)) & 0xFF], 1u);
+      }
     }
   }
   __syncthreads();
@@ -669,13 +676,18 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
 // writes the keys out with consecutive threads. s_mem (2 TILE words) must hold zeroed per-wave
 // digit counts in its first 16 x 256 words; h is this thread's digit count of the pass (threads
 // below 256). Every thread calls it.
-template <bool FINAL, int ITEMS>
+// DROP: keys equal to kCulledKey (culled Gaussians) are left out: the pass writes the other keys,
+// densely, and its workgroup with ticket 0 stores their number (the sum of the pass's histogram,
+// which does not count them) to *n_kept.
+constexpr uint32_t kCulledKey = 0xFFFFFFFFu;
+template <bool FINAL, int ITEMS, bool DROP = false>
 __device__ __forceinline__ void radix_tile(uint32_t (&k)[ITEMS], uint32_t (&v)[ITEMS], uint32_t n, uint32_t base,
                                            uint32_t vb, int shift, int bits, uint32_t h, uint32_t* s_mem,
                                            uint32_t* s_dpre, uint32_t* s_goff, uint32_t* s_wsum,
                                            uint32_t* __restrict__ status, uint32_t* __restrict__ keys_out,
                                            uint32_t* __restrict__ vals_out, uint64_t* __restrict__ out_keys64,
-                                           const uint32_t* __restrict__ depth_bits) {
+                                           const uint32_t* __restrict__ depth_bits,
+                                           uint64_t* __restrict__ n_kept = nullptr) {
   constexpr int TILE = kSortThreads * ITEMS;
   uint32_t* s_keys = s_mem;
   uint32_t* s_vals = s_mem + TILE;
@@ -687,7 +699,7 @@ __device__ __forceinline__ void radix_tile(uint32_t (&k)[ITEMS], uint32_t (&v)[I
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     const uint32_t idx = base + (uint32_t)(wave * 64 * ITEMS + i * 64 + lane);
-    const bool valid = idx < n;
+    const bool valid = idx < n && (!DROP || k[i] != kCulledKey);
     const uint32_t d = (k[i] >> shift) & mask;
     const uint64_t m = match_digit<8>(d, bits, __ballot(valid));
     const uint32_t r = (uint32_t)__popcll(m & lt_mask);
@@ -715,10 +727,11 @@ __device__ __forceinline__ void radix_tile(uint32_t (&k)[ITEMS], uint32_t (&v)[I
     }
     st_dev(status + (size_t)vb * kRadix + tid, (vb == 0 ? kFlagPre : kFlagAgg) | tot);
   }
-  uint32_t dummy;
-  const uint32_t bucket_excl = block_excl_scan256<uint32_t>(h, s_wsum, &dummy);
-  const uint32_t dpre = block_excl_scan256<uint32_t>(tot, s_wsum, &dummy);
+  uint32_t htot, ttot;
+  const uint32_t bucket_excl = block_excl_scan256<uint32_t>(h, s_wsum, &htot);
+  const uint32_t dpre = block_excl_scan256<uint32_t>(tot, s_wsum, &ttot);
   if (tid < kRadix) s_dpre[tid] = dpre;  // 0 past the pass's digits
+  if (DROP && vb == 0 && tid == 0) st_dev(n_kept, (uint64_t)htot);
   __syncthreads();
 
   // ---- scatter to LDS in local sorted order (it needs no look-back, and frees the registers
@@ -732,7 +745,7 @@ __device__ __forceinline__ void radix_tile(uint32_t (&k)[ITEMS], uint32_t (&v)[I
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     const uint32_t idx = base + (uint32_t)(wave * 64 * ITEMS + i * 64 + lane);
-    if (idx < n) {
+    if (idx < n && (!DROP || k[i] != kCulledKey)) {
       s_keys[rank[i]] = k[i];
       s_vals[rank[i]] = v[i];
     }
@@ -747,7 +760,8 @@ __device__ __forceinline__ void radix_tile(uint32_t (&k)[ITEMS], uint32_t (&v)[I
     s_goff[tid] = bucket_excl + excl - dpre;
   }
   __syncthreads();
-  const uint32_t count = (n - base < (uint32_t)TILE) ? (n - base) : (uint32_t)TILE;
+  // the tile's keys in LDS: all of its range, or with DROP the kept ones (the digit totals' sum)
+  const uint32_t count = DROP ? ttot : ((n - base < (uint32_t)TILE) ? (n - base) : (uint32_t)TILE);
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     const uint32_t j = (uint32_t)(i * kSortThreads + tid);
@@ -771,7 +785,7 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(8)
     uint32_t* __restrict__ vals_out, uint64_t* __restrict__ out_keys64, const uint32_t* __restrict__ depth_bits,
     uint32_t n_host, const uint64_t* __restrict__ n_dev, int shift, int bits, const uint32_t* __restrict__ hist,
     int hist_parts, int hist_stride, uint32_t* __restrict__ status, uint32_t* __restrict__ ticket,
-    uint32_t n_extra, TileCountArgs targs) {
+    uint32_t n_extra, TileCountArgs targs, uint64_t* __restrict__ n_kept) {
   constexpr int TILE = kSortThreads * ITEMS;
   // the per-wave digit counts share LDS with the staged keys (they are dead by then), so a
   // workgroup of 8 keys per lane takes 64 KB and two fit on a compute unit; the extra
@@ -828,8 +842,9 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(8)
       for (int q = 0; q < kSortThreads / kRadix; ++q) h += s_part[q * kRadix + tid];
     }
   }
-  radix_tile<FINAL, ITEMS>(k, v, n, base, vb, shift, bits, h, s_mem, s_dpre, s_goff, s_wsum, status, keys_out,
-                           vals_out, out_keys64, depth_bits);
+  // the first depth pass (the one with the tile-row workgroups) drops the culled Gaussians
+  radix_tile<FINAL, ITEMS, EXTRA == 1>(k, v, n, base, vb, shift, bits, h, s_mem, s_dpre, s_goff, s_wsum, status,
+                                       keys_out, vals_out, out_keys64, depth_bits, n_kept);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -866,7 +881,8 @@ __device__ __forceinline__ T block_scan1024(T v, T identity, T* s_wsum, T* total
 // Gaussian id) of each, and for every pair chunk (kEmitChunk positions) that starts inside one of
 // its Gaussians' runs, that Gaussian's depth index into chunk_first. The last workgroup
 // publishes P.
-__global__ __launch_bounds__(kEmitThreads) void k_scan(int32_t n, const uint32_t* __restrict__ sorted_ids,
+__global__ __launch_bounds__(kEmitThreads) void k_scan(int32_t n_all, const uint64_t* __restrict__ n_drawn,
+                                                       const uint32_t* __restrict__ sorted_ids,
                                                        const uint4* __restrict__ rec, uint4* __restrict__ drec,
                                                        uint32_t* __restrict__ chunk_first, uint64_t capacity,
                                                        uint64_t* __restrict__ status, Ctrl* ctrl,
@@ -874,6 +890,10 @@ __global__ __launch_bounds__(kEmitThreads) void k_scan(int32_t n, const uint32_t
   __shared__ uint64_t s_wsum[kEmitWaves];
   __shared__ uint32_t s_vb;
   __shared__ uint64_t s_excl;
+  // the depth order holds the drawn Gaussians only; workgroup 0 always runs, so P is published
+  // also when none is drawn, and the idle ones take no ticket
+  const int n = (int)min((uint64_t)n_all, *n_drawn);
+  if (blockIdx.x > 0 && (int64_t)blockIdx.x * kScanTile >= n) return;  // workgroup-uniform
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) s_vb = atomicAdd(&ctrl->tickets[7], 1u);
   __syncthreads();
@@ -954,13 +974,16 @@ __global__ __launch_bounds__(kEmitThreads) void k_scan(int32_t n, const uint32_t
 constexpr int kFuseWindow = 1024;  // Gaussians staged per emission round (one per thread)
 template <bool FINAL>
 __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_emit_sort(
-    const uint64_t* __restrict__ n_dev, int32_t n, const uint4* __restrict__ drec,
+    const uint64_t* __restrict__ n_dev, int32_t n_all, const uint64_t* __restrict__ n_drawn,
+    const uint4* __restrict__ drec,
     const uint32_t* __restrict__ chunk_first, int32_t tiles_x, int shift, int bits,
     const uint32_t* __restrict__ hist, uint32_t* __restrict__ status, uint32_t* __restrict__ ticket,
     uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint64_t* __restrict__ out_keys64,
     const uint32_t* __restrict__ depth_bits, TileCountArgs targs) {
   constexpr int ITEMS = 4, TILE = kSortThreads * ITEMS;
   static_assert(TILE == kEmitChunk && kEmitThreads == kSortThreads, "one emission chunk per sort tile");
+  // the depth-ordered records: n_all, or (large frames) the drawn Gaussians only
+  const int32_t n = n_drawn ? (int32_t)min((uint64_t)n_all, *n_drawn) : n_all;
   static_assert(kFuseWindow == kSortThreads, "one staged Gaussian per thread");
   __shared__ uint32_t s_mem[2 * TILE];  // the emitted pairs (keys, values), then the sort's staging
   __shared__ uint32_t s_owner[TILE];
@@ -1745,16 +1768,18 @@ gs_status bin_and_sort(int32_t n, const gs_projected* proj, const gs_camera* cam
     const uint32_t n_extra = p == 0 ? n_rows : (p == 1 ? 1u : 0u);
     auto kern = p == 0 ? k_onesweep<false, 1, 4> : (p == 1 ? k_onesweep<false, 2, 4> : k_onesweep<false, 0, 4>);
     TimedScope ts("depth_sort_pass", s);
+    // pass 0 sorts all n keys and drops the culled ones; the later passes sort the drawn ones
     hipLaunchKernelGGL(kern, dim3(L.nbN + n_extra), dim3(kSortThreads), 0, s, even ? dkA : dkB, even ? dvA : dvB,
                        even ? dkB : dkA, even ? dvB : dvA, (uint64_t*)nullptr, (const uint32_t*)nullptr,
-                       (uint32_t)n, (const uint64_t*)nullptr, 8 * p, 8, hist, direct_hist ? (int)L.nbN : 1,
-                       4 * kRadix, dstatus + (size_t)p * L.nbN * kRadix, &ctrl->tickets[p], n_extra, targs);
+                       (uint32_t)n, p == 0 ? (const uint64_t*)nullptr : &ctrl->n_visible, 8 * p, 8, hist,
+                       direct_hist ? (int)L.nbN : 1, 4 * kRadix, dstatus + (size_t)p * L.nbN * kRadix,
+                       &ctrl->tickets[p], n_extra, targs, p == 0 ? &ctrl->n_visible : (uint64_t*)nullptr);
   }
   {
     TimedScope ts("scan", s);
-    hipLaunchKernelGGL(k_scan, dim3(L.nbS), dim3(kEmitThreads), 0, s, n, dvA, (const uint4*)(ws + L.rec),
-                       (uint4*)(ws + L.drec), (uint32_t*)(ws + L.chunk_first), (uint64_t)pair_capacity, scan_status,
-                       ctrl, d_num_pairs);
+    hipLaunchKernelGGL(k_scan, dim3(L.nbS), dim3(kEmitThreads), 0, s, n, &ctrl->n_visible, dvA,
+                       (const uint4*)(ws + L.rec), (uint4*)(ws + L.drec), (uint32_t*)(ws + L.chunk_first),
+                       (uint64_t)pair_capacity, scan_status, ctrl, d_num_pairs);
   }
   }
   if (L.nbCap > 0) {
@@ -1765,8 +1790,9 @@ gs_status bin_and_sort(int32_t n, const gs_projected* proj, const gs_camera* cam
       const bool last = L.npass == 1;
       auto kern = last ? k_emit_sort<true> : k_emit_sort<false>;
       const bool oa = out_A(0);
+      // large frames: the depth-ordered records of the drawn Gaussians only
       hipLaunchKernelGGL(kern, dim3(L.nbCap), dim3(kSortThreads), 0, s, &ctrl->eff_pairs, n,
-                         (const uint4*)(ws + L.drec), (const uint32_t*)(ws + L.chunk_first), tiles_x, L.pshift[0],
+                         L.small ? (const uint64_t*)nullptr : &ctrl->n_visible, (const uint4*)(ws + L.drec), (const uint32_t*)(ws + L.chunk_first), tiles_x, L.pshift[0],
                          L.pbits[0], ctrl->hist_pair[0], pstatus, &ctrl->tickets[4],
                          last ? (uint32_t*)nullptr : (oa ? kA : kB), last ? d_ids : (oa ? vA : vB),
                          last ? d_keys : (uint64_t*)nullptr,
@@ -1788,7 +1814,7 @@ gs_status bin_and_sort(int32_t n, const gs_projected* proj, const gs_camera* cam
                          last ? d_ids : vo, last ? d_keys : (uint64_t*)nullptr,
                          last ? (const uint32_t*)proj->d_depths : (const uint32_t*)nullptr, 0u, &ctrl->eff_pairs,
                          shift, bits, ctrl->hist_pair[p], 1, 0, pstatus + (size_t)p * L.nbCap * kRadix,
-                         &ctrl->tickets[4 + p], 0u, targs);
+                         &ctrl->tickets[4 + p], 0u, targs, (uint64_t*)nullptr);
     }
   }
   const gs_status st = check_launch("gs_bin_and_sort");

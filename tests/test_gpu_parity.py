@@ -338,7 +338,7 @@ def test_empty_and_all_culled(env):
     gs, torch = env
     cam_d = synth.make_camera(np.eye(4), 40, 24, 30.0, background=(0.3, 0.2, 0.1))
     cam = gs.make_camera(cam_d)
-    for n in (0, 5):
+    for n in (0, 5, 40000):  # 40,000: the large-frame path, whose depth sort drops culled keys
         sc = synth.random_scene(max(n, 1), seed=3, width=40, height=24, focal=30.0)
         if n == 0:
             sc = {k: (v[:0] if isinstance(v, np.ndarray) else v) for k, v in sc.items()}
@@ -358,6 +358,20 @@ def test_empty_and_all_culled(env):
             pipe.backward(cam)
             torch.cuda.synchronize()
             assert all(np.all(v.cpu().numpy() == 0) for v in pipe.grads.values())
+
+
+@pytest.mark.parametrize("visible_every", [10, 997])
+def test_large_frame_mostly_culled(env, visible_every):
+    """Above 36,864 Gaussians the depth sort's first pass drops the culled ones and the later
+    passes, the scan and the emission run on the drawn ones only: a scene where one Gaussian in
+    10 (or in 997) is in front of the camera bins, blends and back-propagates like the oracle."""
+    n, W, f = 60000, 200, 160.0
+    scene = synth.random_scene(n, seed=61, width=W, height=W, focal=f)
+    behind = np.arange(n) % visible_every != 0
+    scene["means"][behind, 2] *= -1.0
+    cam = synth.make_camera(np.eye(4), W, W, f, background=(0.2, 0.1, 0.3))
+    _pipeline_case(env, scene, cam, pixels=synth.sample_pixels(W, W, 4096, seed=3),
+                   label=f"mostly culled 1/{visible_every}", bwd="det")
 
 
 def test_capacity_overflow_contract(env):
