@@ -1131,16 +1131,18 @@ __global__ __launch_bounds__(kSortThreads) __attribute__((amdgpu_waves_per_eu(8)
 // instead of the key-computing pass, four radix passes and the scan.
 //   k_small_local  workgroup b < nb sorts block b (ids [4096 b, 4096 b + 4096)) by depth key in
 //                  LDS (radix passes of up to 9 bits over the bits the block's keys span) and
-//                  writes the sorted keys, ids and the exclusive prefix of their tile counts;
-//                  workgroup nb counts the pairs of every tile from all N rectangles into a
-//                  difference array in its own LDS and finalizes it (ranges, pair-sort histograms,
-//                  raster plan); the others only clear the control block and look-back words
-//   k_small_merge  kSmallSplit workgroups per block, 512 keys each: every key's place in the depth
+//                  writes the sorted keys, ids and the exclusive prefix of their tile counts; it
+//                  also adds its Gaussians' rectangle rows into its own row of per-tile count
+//                  differences (tmat); the other workgroups only clear the control block and
+//                  look-back words
+//   k_small_merge  kSmallSplit workgroups per block, 1024 keys each: every key's place in the depth
 //                  order is its place in its block plus, for every other block, how many of that
 //                  block's keys come first (binary search over all N keys held in LDS; an earlier
 //                  block's equal keys have smaller ids and come first); its first pair position is
 //                  the sum of the matching tile-count prefixes. It writes the depth-ordered
-//                  records and the emission chunks' first Gaussians as the scan does.
+//                  records and the emission chunks' first Gaussians as the scan does. Its last
+//                  workgroup is the tile finalizer: it sums the blocks' count rows and writes the
+//                  ranges, the pair-sort histograms, P and the raster plan.
 // The order is the stable (depth bits, id) order of the radix path, bit for bit.
 // ---------------------------------------------------------------------------------------------
 constexpr int kSmallBlock = kSortTile;  // 4096 Gaussians per block, four per thread
