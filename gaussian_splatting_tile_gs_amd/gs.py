@@ -287,6 +287,9 @@ def gs_adam_step(n, sh_degree, step, cfg: GsAdamConfig, params: dict, grads: dic
                                _ptr(m), _ptr(v), _stream(stream)))
 
 
+_PROJ_FIELDS = ("means2d", "conics", "depths", "opacities", "colors", "radii", "tiles_touched")
+
+
 @dataclass
 class Projected:
     means2d: torch.Tensor
@@ -305,11 +308,14 @@ class Projected:
                          torch.empty(n, device=device, dtype=torch.int32))
 
     def struct(self) -> GsProjected:
-        s = GsProjected()
-        for f in ("means2d", "conics", "depths", "opacities", "colors", "radii", "tiles_touched"):
-            setattr(s, "d_" + f, getattr(self, f).data_ptr())
-        self._keep = s
-        return s
+        """The C struct of the seven pointers, rebuilt only when one of them changed."""
+        ptrs = tuple(getattr(self, f).data_ptr() for f in _PROJ_FIELDS)
+        if getattr(self, "_keep_ptrs", None) != ptrs:
+            s = GsProjected()
+            for f, q in zip(_PROJ_FIELDS, ptrs):
+                setattr(s, "d_" + f, q)
+            self._keep, self._keep_ptrs = s, ptrs
+        return self._keep
 
 
 def scene_to_device(scene: dict, device="cuda"):
@@ -431,10 +437,7 @@ class Pipeline:
         det = getattr(self, "deterministic", False)
         ws = self.bwd_ws
         if det:
-            need = gs_bwd_det_workspace_bytes(self.n, self.capacity)
-            if getattr(self, "_det_ws", None) is None or self._det_ws.numel() < need:
-                self._det_ws = torch.empty(need, device=self.device, dtype=torch.uint8)
-            ws = self._det_ws
+            ws = self._det_workspace()
         gs_rasterize_bwd(self.n, p["sh_degree"], p["means"], p["log_scales"], p["quats"], p["opacity_logits"],
                          p["sh"], cam, self.proj, self.ids, self.ranges, self.final_T, self.n_contrib,
                          self.dL_dimage if dL_dimage is None else dL_dimage, ws, g["means"], g["log_scales"],
@@ -496,10 +499,60 @@ class Pipeline:
         out["features"] = out["features"].view(self.n, 3)[:, :C]
         return out
 
+    def _det_workspace(self):
+        need = gs_bwd_det_workspace_bytes(self.n, self.capacity)
+        if getattr(self, "_det_ws", None) is None or self._det_ws.numel() < need:
+            self._det_ws = torch.empty(need, device=self.device, dtype=torch.uint8)
+        return self._det_ws
+
+    def _iteration_args(self):
+        """The arguments of a no-wait L1 iteration's four entry points except the camera, the target
+        and the stream, built once per set of buffers (their pointers do not change between
+        iterations, and rebuilding them was half of the host's time per iteration)."""
+        det = getattr(self, "deterministic", False)
+        key = (self.capacity, det, self.keys.data_ptr(), self.bin_ws.data_ptr(), id(self.p))
+        if getattr(self, "_iter_key", None) == key:
+            return self._iter_args
+        p, g = self.p, self.grads
+        P = _ptr
+        proj = ctypes.byref(self.proj.struct())
+        raw = (P(p["means"]), P(p["log_scales"]), P(p["quats"]), P(p["opacity_logits"]), P(p["sh"]))
+        ws = self._det_workspace() if det else self.bwd_ws
+        a = {
+            "proj": proj,
+            "project": (self.n, p["sh_degree"]) + raw,
+            "bin": (ctypes.c_void_p(self.bin_ws.data_ptr()), self.bin_ws.numel() * self.bin_ws.element_size(),
+                    self.capacity, P(self.keys), P(self.ids), P(self.ranges), P(self.plan), P(self.num_pairs_dev),
+                    None),
+            "fwd_pre": (P(self.ids), P(self.ranges), P(self.plan), P(self.raster_ws), P(self.image), None,
+                        P(self.final_T), P(self.n_contrib)),
+            "fwd_post": (P(self.dL_dimage), None),
+            "bwd_pre": (self.n, p["sh_degree"]) + raw,
+            "bwd_post": (P(self.ids), P(self.ranges), P(self.plan), P(self.raster_ws), P(self.final_T),
+                         P(self.n_contrib), P(self.dL_dimage), None)
+                        + ((int(self.capacity),) if det else ())
+                        + (P(ws), ws.numel() * ws.element_size(), P(g["means"]), P(g["log_scales"]), P(g["quats"]),
+                           P(g["opacity_logits"]), P(g["sh"]), P(g["means2d"]), None),
+            "bwd": load().gs_rasterize_bwd_deterministic if det else load().gs_rasterize_bwd,
+        }
+        self._iter_key, self._iter_args = key, a
+        return a
+
     def iteration(self, cam: GsCamera, target, stream=None, wait=True):
         """One fwd+bwd iteration: project, bin+sort, blend, loss gradient (L1 inside the blend, or the
         separate L1 + SSIM kernels), backward. wait=False runs
         it without any host wait (the pair buffers must already be large enough)."""
+        if not wait and getattr(self, "ssim_lambda", 0.0) <= 0.0 and self.schedule == "chunks":
+            # the same four calls as below, with the unchanging arguments taken from a cache
+            lib, a = load(), self._iteration_args()
+            cp, s, tp = ctypes.byref(cam), _stream(stream), _ptr(target)
+            _check(lib.gs_project(*a["project"], cp, a["proj"], s))
+            _check(lib.gs_bin_and_sort(self.n, a["proj"], cp, *a["bin"], s), allow=(GS_ERR_CAPACITY,))
+            self.num_pairs = None
+            _check(lib.gs_rasterize_fwd_l1(self.n, a["proj"], cp, *a["fwd_pre"], tp, *a["fwd_post"], s))
+            self._ckpt_written, self._ckpt_depth = True, False
+            _check(a["bwd"](*a["bwd_pre"], cp, a["proj"], *a["bwd_post"], s))
+            return
         self.project(cam, stream)
         self.bin(cam, stream, wait=wait)
         if getattr(self, "ssim_lambda", 0.0) > 0.0:
