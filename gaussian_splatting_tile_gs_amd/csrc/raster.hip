@@ -352,6 +352,14 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
     const int py_i = ty * kTile + (wave >> 1) * 8 + (lane >> 3);
     const bool inside = px_i < cam.W && py_i < cam.H;
     const float px = (float)px_i + 0.5f, py = (float)py_i + 0.5f;
+    // the fused L1's target, loaded now so that the finished pixel does not wait for it
+    float tr = 0.0f, tg = 0.0f, tb = 0.0f;
+    if (l1_target && inside) {
+      const int p = py_i * cam.W + px_i;
+      tr = l1_target[3 * p + 0];
+      tg = l1_target[3 * p + 1];
+      tb = l1_target[3 * p + 2];
+    }
     const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
     const uint32_t len = end - start;
     const uint32_t L = CHUNKED ? plan[kPlanChunk] : 1u;
@@ -492,9 +500,9 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
         image[3 * p + 1] = ig;
         image[3 * p + 2] = ib;
         if (l1_target) {  // uniform: the L1 gradient sign(image - target) / (3 h w), as gs_loss_l1 forms it
-          l1_grad[3 * p + 0] = l1_sign(ir - l1_target[3 * p + 0]) * l1_scale;
-          l1_grad[3 * p + 1] = l1_sign(ig - l1_target[3 * p + 1]) * l1_scale;
-          l1_grad[3 * p + 2] = l1_sign(ib - l1_target[3 * p + 2]) * l1_scale;
+          l1_grad[3 * p + 0] = l1_sign(ir - tr) * l1_scale;
+          l1_grad[3 * p + 1] = l1_sign(ig - tg) * l1_scale;
+          l1_grad[3 * p + 2] = l1_sign(ib - tb) * l1_scale;
         }
         final_T[p] = T;
         n_contrib[p] = last;
@@ -804,9 +812,7 @@ __global__ __launch_bounds__(kRasterThreads) __attribute__((amdgpu_waves_per_eu(
         if (gv[c] != 0.0f) unsafeAtomicAdd(g2d + (size_t)c * n + g, gv[c]);
     }
   };
-  // a chunk of at most one batch is staged at once: its loads overlap the pixels' loads below
   const bool single = chunk_end <= lo + (uint32_t)kBatch;
-  if (single && chunk_end > lo) stage(lo, (int)(chunk_end - lo));
 
   float T = 1.0f, gr = 0.0f, gg = 0.0f, gb = 0.0f, gd = 0.0f, gS = 0.0f;
   uint32_t nc = 0;
@@ -838,6 +844,9 @@ __global__ __launch_bounds__(kRasterThreads) __attribute__((amdgpu_waves_per_eu(
       gS = T * ((gr * cam.bg[0] + gg * cam.bg[1]) + gb * cam.bg[2]);
     }
   }
+  // a chunk of at most one batch is staged at once, after the pixels' loads above are issued,
+  // so that its own chain of loads (ids, then records) overlaps them
+  if (single && chunk_end > lo) stage(lo, (int)(chunk_end - lo));
   if (tid == 0) s_max = 0;
   __syncthreads();
   const uint32_t wmax = wave_max_lane63(nc);
