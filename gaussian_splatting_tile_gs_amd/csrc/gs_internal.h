@@ -236,7 +236,7 @@ __device__ __forceinline__ SplatEval eval_splat(float dx, float dy, float hA, fl
 // L >= P / kPlanMaxChunks keeps X below kPlanMaxChunks and the slots below 2 kPlanMaxChunks.
 // ---------------------------------------------------------------------------------------------
 constexpr uint32_t kPlanChunk = 0, kPlanExtra = 1, kPlanCheckpoints = 2, kPlanOrder = 4;
-constexpr uint32_t kPlanMinChunk = 256;  // one raster batch: chunk boundaries are batch starts
+constexpr uint32_t kPlanMinChunk = 128;  // half a raster batch: boundaries fall where a mask word starts
 constexpr uint32_t kPlanMaxChunks = 2048;
 constexpr uint32_t kPlanMaxSlots = 2 * kPlanMaxChunks;
 inline size_t plan_words(size_t ntiles) { return kPlanOrder + 2 * ntiles + 2 * kPlanMaxChunks; }

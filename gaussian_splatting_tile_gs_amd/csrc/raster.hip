@@ -34,7 +34,9 @@ namespace {
 constexpr int kTile = 16;
 constexpr int kRasterThreads = kTile * kTile;  // 256: one pixel per thread
 constexpr int kBatch = kRasterThreads;         // splats staged per batch
-static_assert(kPlanMinChunk % kBatch == 0, "chunk boundaries must fall on batch starts");
+// chunk lengths are powers of two >= kPlanMinChunk: a boundary falls on a batch start or on the
+// start of a 64-splat word of the quadrant masks, where each wave can store its pixels' state
+static_assert(kBatch % kPlanMinChunk == 0 && kPlanMinChunk % 64 == 0, "chunk boundaries must fall on mask words");
 
 // Staged splat record: (mx, my, hA, hC), (B2, o, r, g), b. hA = A/2 log2e, B2 = B log2e,
 // hC = C/2 log2e, so that log2(e) sigma = hA dx^2 + hC dy^2 + B2 dx dy. Staging also returns the
@@ -213,9 +215,10 @@ __device__ __forceinline__ void blend_step(const SplatEval& e, bool act, float c
 // CHUNKED (a plan and the raster workspace: a training forward): the backward splits a tile longer
 // than the plan's chunk length L into chunks of L list entries, so the forward stores for every
 // chunk j, per pixel, the transmittance after the chunk and the colour (and depth) it added
-// (checkpoint slot j of the tile). A tile of two chunks is walked by one workgroup that stores
-// the slots as it passes the chunk boundaries. A tile of three or more chunks is split: its
-// chunks are blended at once, one workgroup each (the plan's extra work items (tile, j >= 1) and
+// (checkpoint slot j of the tile). A tile that is not split is walked by one workgroup that stores
+// the slots as it passes the chunk boundaries (each wave for its own pixels, where the boundary's
+// 64-splat mask word starts). A tile of three or more chunks and more than 512 entries is split:
+// its chunks are blended at once, one workgroup each (the plan's extra work items (tile, j >= 1) and
 // the tile's own workgroup for chunk 0). The workgroup of chunk j >= 1 first forms the
 // transmittance factor of chunk j - 1 (the product of 1 - alpha over its contributing splats, no
 // stop rule; a factor that falls to 1e-4 or below stays there) and publishes it, then waits for
@@ -230,7 +233,11 @@ __device__ __forceinline__ void blend_step(const SplatEval& e, bool act, float c
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ float l1_sign(float d) { return d > 0.0f ? 1.0f : (d < 0.0f ? -1.0f : 0.0f); }
 
-constexpr uint32_t kSplitMinChunks = 3;      // tiles of this many chunks or more are split
+// a tile is split when it has three or more chunks and more than this many entries: the split's
+// chain (a factor pass and a blend of one chunk each) must be well below the whole tile's walk to
+// pay for the factor passes' extra work
+constexpr uint32_t kSplitMinChunks = 3;
+constexpr uint32_t kSplitMinEntries = 513;
 constexpr uint32_t kWaitPolls = 1u << 22;    // a bound on each wait for a published factor
 
 // The raster workspace, per checkpoint slot and pixel: (T after the chunk, colour the chunk added),
@@ -262,23 +269,23 @@ __host__ __device__ inline RasterWs raster_ws_parts(void* base) {
 
 // Walks list entries [rs, re) of a tile (staged 256 at a time, the next batch's records loading
 // while a batch is walked) and calls visit(k0, k1, has1, list1) for the staged splats reaching the
-// wave's quadrant, two per call; stops when every pixel of the workgroup is done. at_batch(e) is
-// called at each batch start (workgroup-uniform) with the batch's first list entry.
-template <bool DEPTH, typename VISIT, typename AT_BATCH>
+// wave's quadrant, two per call; stops when every pixel of the workgroup is done. at_word(e) is
+// called by each wave before it walks a 64-splat word of its mask (wave-uniform), with the word's
+// first list entry.
+template <bool DEPTH, typename VISIT, typename AT_WORD>
 __device__ __forceinline__ void walk_entries(uint32_t n, const uint32_t* __restrict__ ids, uint32_t start, uint32_t rs,
                                              uint32_t re, const float* __restrict__ means2d,
                                              const float* __restrict__ conics, const float* __restrict__ opac,
                                              const float* __restrict__ colors, const float* __restrict__ depths,
                                              float tx0, float ty0, const bool& done, float4* s_a, float4* s_b,
                                              float* s_c, float* s_z, uint64_t (*s_qm)[4], VISIT visit,
-                                             AT_BATCH at_batch) {
+                                             AT_WORD at_word) {
   const int tid = threadIdx.x, wave = tid >> 6;
   const uint32_t b0 = start + rs, e0 = start + re;
   uint32_t id_next2 = b0 + kBatch + tid < e0 ? ids[b0 + kBatch + tid] : n;
   RawSplat raw = load_raw<DEPTH>(b0 + tid < e0 ? ids[b0 + tid] : n, n, means2d, conics, opac, colors, depths);
   for (uint32_t bs = b0; bs < e0; bs += kBatch) {
     if (__syncthreads_count(done) == kRasterThreads) break;
-    at_batch(bs - start);
     const bool valid = bs + tid < e0;
     const uint32_t qm = stage_raw(raw, valid, tx0, ty0, s_a[tid], s_b[tid], s_c[tid]);
     if (DEPTH) s_z[tid] = raw.z;
@@ -291,6 +298,7 @@ __device__ __forceinline__ void walk_entries(uint32_t n, const uint32_t* __restr
     __syncthreads();
     const uint32_t list1 = bs - start + 1u;  // 1-based list index of staged splat 0
     for (int w = 0; w < 4; ++w) {
+      at_word(bs - start + (uint32_t)(w * 64));
       uint64_t m = uniform64(s_qm[wave][w]);
       while (m) {
         if (!__any(!done)) break;
@@ -364,7 +372,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
     const uint32_t len = end - start;
     const uint32_t L = CHUNKED ? plan[kPlanChunk] : 1u;
     const uint32_t nch = (CHUNKED && len > L) ? (len + L - 1u) / L : 1u;
-    const bool split = CHUNKED && nch >= kSplitMinChunks;
+    const bool split = CHUNKED && nch >= kSplitMinChunks && len >= kSplitMinEntries;
     const uint32_t sbase = nch > 1 ? plan[kPlanOrder + ntiles + tile] : 0u;  // the tile's first slot
     // a chunk item of an unsplit tile has nothing to do: the tile's workgroup walks all of it
     if (chunk == 0 || split) {
@@ -406,8 +414,9 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
       uint32_t last = 0;
       // a chunk that starts at or below 1e-4 would stop at its first contributing splat: done already
       bool done = !inside || __float_as_uint(T) <= __float_as_uint(kTransmittanceMin);
-      // an unsplit tile of two chunks stores slot j as it passes the start of chunk j + 1; (pr, pg,
-      // pb, pd) hold the colour of the chunks before the current one
+      // an unsplit tile of two chunks stores slot j as it passes the start of chunk j + 1 (each wave
+      // its own pixels, where the boundary's mask word starts); (pr, pg, pb, pd) hold the colour of
+      // the chunks before the current one
       float pr = 0.0f, pg = 0.0f, pb = 0.0f, pd = 0.0f;
       const bool seq_ckpt = CHUNKED && !split && nch > 1;
       uint32_t next_b = seq_ckpt ? L : 0xFFFFFFFFu;
@@ -439,7 +448,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
         blend_step<DEPTH>(e0, true, b0.z, b0.w, c0, z0, list1 + (uint32_t)k0, T, cr, cg, cb, cd, last, done);
         blend_step<DEPTH>(e1, has1, b1.z, b1.w, c1, z1, list1 + (uint32_t)k1, T, cr, cg, cb, cd, last, done);
       }, [&](uint32_t e) {
-        if (seq_ckpt && e >= next_b) store_ckpt();  // workgroup-uniform
+        if (seq_ckpt && e >= next_b) store_ckpt();  // wave-uniform
       });
       if (seq_ckpt) {
         while (next_b != 0xFFFFFFFFu) store_ckpt();  // boundaries past the last walked batch
@@ -1376,7 +1385,7 @@ gs_status rasterize_fwd(const char* name, int32_t n, const gs_projected* proj, c
   hipStream_t s = (hipStream_t)stream;
   {
     // with a plan and the raster workspace (a training forward) the checkpoints are stored and
-    // tiles of three or more chunks are blended chunk by chunk in parallel
+    // tiles of three or more chunks and more than 512 entries are blended chunk by chunk in parallel
     const bool ck = d_raster_plan && d_raster_ws;
     const bool dep = d_depth != nullptr;
     auto pick = [&](auto c_, auto k_, auto d_) {

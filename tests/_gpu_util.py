@@ -84,7 +84,7 @@ def run_gpu_bin(gs, torch, params_n, proj, cam, capacity):
 
 def assert_raster_plan(plan_np, ranges_np, P):
     """The raster plan: tiles ordered by non-increasing bit length of their pair count (empty
-    ones last), a chunk length L = the smallest power of two >= 256 with P <= 2048 L, and for
+    ones last), a chunk length L = the smallest power of two >= 128 with P <= 2048 L, and for
     every tile of k = ceil(count / L) >= 2 chunks k checkpoint slots (disjoint intervals that
     tile [0, slots)) and the extra work items (tile, 1 .. k - 1), in any order."""
     plan = plan_np.view(np.uint32).astype(np.int64)
@@ -95,7 +95,7 @@ def assert_raster_plan(plan_np, ranges_np, P):
     cnt = ranges_np[:, 1].astype(np.int64) - ranges_np[:, 0]
     cls = np.where(cnt[order] > 0, np.floor(np.log2(np.maximum(cnt[order], 1))).astype(np.int64) + 1, 0)
     assert np.all(np.diff(cls) <= 0), "tile order is not heaviest class first"
-    want_L = 256
+    want_L = 128
     while want_L * 2048 < P:
         want_L *= 2
     assert L == want_L, (L, want_L)
