@@ -21,9 +21,6 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgs_hip.so")
 
 GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_LIMIT, GS_ERR_DEVICE = 0, 1, 2, 3, 4
-# the raster workspace ends with the chunked forward's synchronisation words (two counters, then an
-# arrival counter and a flag per checkpoint slot, 4096 slots), zero between calls
-RASTER_SYNC_BYTES = 4 * (2 + 2 * 4096)
 
 
 class GsError(RuntimeError):
@@ -160,6 +157,20 @@ def gs_bin_workspace_bytes(n, pair_capacity, cam: GsCamera) -> int:
 
 def gs_raster_plan_words(cam: GsCamera) -> int:
     return int(load().gs_raster_plan_words(ctypes.byref(cam)))
+
+
+def plan_max_chunks() -> int:
+    """The most extra work items a raster plan holds (the plan is 4 + 2 tiles + 2 of these words)."""
+    cam = GsCamera()
+    cam.width, cam.height = 16, 16
+    return (gs_raster_plan_words(cam) - 4 - 2) // 2
+
+
+def raster_sync_bytes() -> int:
+    """The end of the raster workspace: the chunked forward's synchronisation words (two counters,
+    then an arrival counter and a flag per checkpoint slot, two slots per plan chunk), zero
+    between calls."""
+    return 4 * (2 + 2 * 2 * plan_max_chunks())
 
 
 def gs_raster_workspace_bytes() -> int:

@@ -84,9 +84,11 @@ def run_gpu_bin(gs, torch, params_n, proj, cam, capacity):
 
 def assert_raster_plan(plan_np, ranges_np, P):
     """The raster plan: tiles ordered by non-increasing bit length of their pair count (empty
-    ones last), a chunk length L = the smallest power of two >= 128 with P <= 2048 L, and for
-    every tile of k = ceil(count / L) >= 2 chunks k checkpoint slots (disjoint intervals that
-    tile [0, slots)) and the extra work items (tile, 1 .. k - 1), in any order."""
+    ones last), a chunk length L = the smallest power of two >= 128 with P <= C L (C = the plan's
+    chunk limit), and for every tile of k = ceil(count / L) >= 2 chunks k checkpoint slots
+    (disjoint intervals that tile [0, slots)) and the extra work items (tile, 1 .. k - 1), in any
+    order."""
+    from gaussian_splatting_tile_gs_amd import gs as gs_mod
     plan = plan_np.view(np.uint32).astype(np.int64)
     n = ranges_np.shape[0]
     L, n_extra, n_ck = plan[0], plan[1], plan[2]
@@ -96,13 +98,14 @@ def assert_raster_plan(plan_np, ranges_np, P):
     cls = np.where(cnt[order] > 0, np.floor(np.log2(np.maximum(cnt[order], 1))).astype(np.int64) + 1, 0)
     assert np.all(np.diff(cls) <= 0), "tile order is not heaviest class first"
     want_L = 128
-    while want_L * 2048 < P:
+    C = gs_mod.plan_max_chunks()
+    while want_L * C < P:
         want_L *= 2
     assert L == want_L, (L, want_L)
     nch = (cnt + L - 1) // L
     multi = np.nonzero(nch >= 2)[0]
     assert n_extra == (nch[multi] - 1).sum() and n_ck == nch[multi].sum()
-    assert n_extra < 2048
+    assert n_extra < C
     base = plan[4 + n + multi]
     span = np.zeros(n_ck, np.int64)
     for t, b0 in zip(multi, base):

@@ -73,6 +73,8 @@ def test_host_only_helpers(lib):
     assert lib.gs_loss_ssim_workspace_bytes(980, 545) >= 980 * 545 * 36 + 62 * 35 * 8
     assert lib.gs_loss_ssim_workspace_bytes(0, 10) == 0
     lib.gs_raster_workspace_bytes.restype = ctypes.c_size_t
-    # per checkpoint slot (4096) and pixel (256): (T, r, g, b), depth part, factor, last entry;
-    # then the synchronisation words the binding finds at the end
-    assert lib.gs_raster_workspace_bytes() == 4096 * 256 * 28 + gs.RASTER_SYNC_BYTES
+    # per checkpoint slot (two per plan chunk) and pixel (256): (T, r, g, b), depth part, factor,
+    # last entry; then the synchronisation words the binding finds at the end
+    slots = 2 * gs.plan_max_chunks()
+    assert slots >= 4096
+    assert lib.gs_raster_workspace_bytes() == slots * 256 * 28 + gs.raster_sync_bytes()

@@ -658,7 +658,7 @@ def test_chunked_forward_matches_whole_tiles(env, name, depth):
         torch.cuda.synchronize()
         outs.append((p.image.clone(), p.final_T.clone(), p.n_contrib.clone(), dep))
         if ck:
-            sync = p.raster_ws[-gs.RASTER_SYNC_BYTES:]
+            sync = p.raster_ws[-gs.raster_sync_bytes():]
             assert int(torch.count_nonzero(sync)) == 0, "synchronisation words left set"
     for a, b in zip(outs[1], outs[2]):
         assert a is None or torch.equal(a, b), "two chunked forwards differ"
