@@ -513,14 +513,14 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
   uint32_t(*s_hist)[kRadix] = reinterpret_cast<uint32_t(*)[kRadix]>(aux);  // rows 0-2: histograms
   uint32_t* s_cls = aux + 3 * kRadix;  // tiles per count class (33)
   uint32_t* s_cur = s_cls + 64;        // next order slot per class
-  uint32_t* s_misc = s_cls + 128;      // [0] extra work items, [1] checkpoint slots
+  uint32_t* s_misc = s_cls + 128;      // [0] extra work items, [1] checkpoint slots, [2] split chunks
   uint32_t* s_wt = aux + 4 * kRadix;   // kFinRows x 16 scan partials
   uint32_t* s_rt = aux + 5 * kRadix;   // kFinRows row sums
   uint32_t* s = lds;                   // the step's tiles
   const bool one_step = a.ntiles <= kFinStep;
   if (tid < kRadix)
     for (int k = 0; k < a.npass; ++k) s_hist[k][tid] = 0;
-  if (tid < 130) s_cls[tid] = 0;  // classes, cursors, misc
+  if (tid < 131) s_cls[tid] = 0;  // classes, cursors, misc
   if (tid == 0) s_p64 = 0;
   __syncthreads();
   uint64_t P = 0;
@@ -625,6 +625,26 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
             extra[2 * (x0 + j) + 1] = j + 1u;
           }
         }
+        // a tile the training forward splits: its blended chunks after the first, in order
+        const bool spl = valid && fits && plan_split(c, L);
+        uint32_t fb = 0, nb = 0;
+        if (spl) {
+          nb = plan_blended_chunks(c, L);
+          fb = atomicAdd(&s_misc[2], nb - 1u);
+        }
+        uint32_t* fitems = a.plan + kPlanOrder + 2 * a.ntiles + 2 * kPlanMaxChunks;
+        mm = __ballot(spl);
+        while (mm) {
+          const int src = __builtin_ctzll(mm);
+          mm &= mm - 1;
+          const uint32_t n1 = (uint32_t)__builtin_amdgcn_readlane((int)nb, src) - 1u;
+          const uint32_t x0 = (uint32_t)__builtin_amdgcn_readlane((int)fb, src);
+          const uint32_t tt = (uint32_t)__builtin_amdgcn_readlane((int)t, src);
+          for (uint32_t j = (uint32_t)lane; j < n1; j += 64) {
+            fitems[2 * (x0 + j)] = tt;
+            fitems[2 * (x0 + j) + 1] = j + 1u;
+          }
+        }
       }
     }
     if (sweep == 0) {
@@ -655,6 +675,7 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
     a.plan[kPlanChunk] = L;
     a.plan[kPlanExtra] = s_misc[0];
     a.plan[kPlanCheckpoints] = s_misc[1];
+    a.plan[kPlanSplit] = s_misc[2];
   }
 }
 
@@ -1499,6 +1520,7 @@ __global__ void k_empty_plan(uint32_t* __restrict__ plan, uint32_t ntiles) {
     plan[kPlanChunk] = kPlanMinChunk;
     plan[kPlanExtra] = 0;
     plan[kPlanCheckpoints] = 0;
+    plan[kPlanSplit] = 0;
   }
   if (i < ntiles) {
     plan[kPlanOrder + i] = i;

@@ -226,20 +226,33 @@ __device__ __forceinline__ SplatEval eval_splat(float dx, float dy, float hA, fl
 
 // ---------------------------------------------------------------------------------------------
 // Raster plan (written by gs_bin_and_sort, read by the raster calls), u32 words:
-//   [0] chunk length L, [1] X = extra work items, [2] checkpoint slots, [3] unused,
+//   [0] chunk length L, [1] X = extra work items, [2] checkpoint slots, [3] XF = split chunks,
 //   [4, 4 + T)          tile processing order (T = number of tiles),
 //   [4 + T, 4 + 2T)     per tile with two or more chunks, the index of its first checkpoint slot,
-//   [4 + 2T, 4 + 2T + 2X)  the extra work items (tile, chunk >= 1).
+//   [4 + 2T, 4 + 2T + 2X)  the extra work items (tile, chunk >= 1),
+//   [4 + 2T + 2M, 4 + 2T + 2M + 2XF)  (M = kPlanMaxChunks) the training forward's extra work
+//                       items (tile, blended chunk >= 1) of the tiles it splits.
 // A tile with c pairs has k = ceil(c / L) chunks of L list entries; when k >= 2 it has k slots,
 // slot j holding, per pixel, the transmittance after chunk j and the colour that chunk j added.
 // The backward's work items are the X extra ones, then (order[i], chunk 0) for every tile.
 // L >= P / kPlanMaxChunks keeps X below kPlanMaxChunks and the slots below 2 kPlanMaxChunks.
+// The training forward blends a tile of more than 512 entries and at least three chunks of 2 L
+// entries chunk by chunk in parallel (plan_split): its work items are the XF split chunks, then
+// (order[i], first chunk) for every tile; XF < X / 2.
 // ---------------------------------------------------------------------------------------------
-constexpr uint32_t kPlanChunk = 0, kPlanExtra = 1, kPlanCheckpoints = 2, kPlanOrder = 4;
+constexpr uint32_t kPlanChunk = 0, kPlanExtra = 1, kPlanCheckpoints = 2, kPlanSplit = 3, kPlanOrder = 4;
 constexpr uint32_t kPlanMinChunk = 128;  // half a raster batch: boundaries fall where a mask word starts
-constexpr uint32_t kPlanMaxChunks = 2048;
+constexpr uint32_t kPlanMaxChunks = 4096;
 constexpr uint32_t kPlanMaxSlots = 2 * kPlanMaxChunks;
-inline size_t plan_words(size_t ntiles) { return kPlanOrder + 2 * ntiles + 2 * kPlanMaxChunks; }
+constexpr uint32_t kPlanMaxSplit = kPlanMaxChunks / 2;
+inline size_t plan_words(size_t ntiles) { return kPlanOrder + 2 * ntiles + 2 * kPlanMaxChunks + 2 * kPlanMaxSplit; }
+// The training forward's split rule: the split's chain (a factor pass and a blend of one blended
+// chunk of 2 L entries) must be well below the whole tile's walk to pay for the factor passes.
+constexpr uint32_t kSplitMinChunks = 3, kSplitMinEntries = 513;
+__host__ __device__ inline uint32_t plan_blended_chunks(uint32_t c, uint32_t L) { return (c + 2u * L - 1u) / (2u * L); }
+__host__ __device__ inline bool plan_split(uint32_t c, uint32_t L) {
+  return c >= kSplitMinEntries && plan_blended_chunks(c, L) >= kSplitMinChunks;
+}
 
 // ---------------------------------------------------------------------------------------------
 // Host side: status, last error, kernel timing.

@@ -215,29 +215,25 @@ __device__ __forceinline__ void blend_step(const SplatEval& e, bool act, float c
 // CHUNKED (a plan and the raster workspace: a training forward): the backward splits a tile longer
 // than the plan's chunk length L into chunks of L list entries, so the forward stores for every
 // chunk j, per pixel, the transmittance after the chunk and the colour (and depth) it added
-// (checkpoint slot j of the tile). A tile that is not split is walked by one workgroup that stores
-// the slots as it passes the chunk boundaries (each wave for its own pixels, where the boundary's
-// 64-splat mask word starts). A tile of three or more chunks and more than 512 entries is split:
-// its chunks are blended at once, one workgroup each (the plan's extra work items (tile, j >= 1) and
-// the tile's own workgroup for chunk 0). The workgroup of chunk j >= 1 first forms the
-// transmittance factor of chunk j - 1 (the product of 1 - alpha over its contributing splats, no
-// stop rule; a factor that falls to 1e-4 or below stays there) and publishes it, then waits for
-// the factors of chunks 0 .. j - 2 published by the workgroups of chunks 1 .. j - 1, starts from
-// their product and blends its chunk. A pixel that stopped in an earlier chunk starts at or below
-// 1e-4 and so adds nothing. The last of a split tile's workgroups to finish forms its pixels: the
-// transmittance of the first chunk that stopped (else of the last chunk), the colours summed over
-// the chunks in order, the last added entry of the last chunk that added one.
+// (checkpoint slot j of the tile); each wave stores its own pixels' slot as it passes a boundary,
+// where the boundary's 64-splat mask word starts. A tile that is not split is walked by one
+// workgroup. A tile of three or more blended chunks of 2 L entries and more than 512 entries is
+// split: its blended chunks run at once, one workgroup each (the plan's extra work items
+// (tile, j) of even j >= 2, and the tile's own workgroup for the first). The workgroup of blended
+// chunk c >= 1 first forms the transmittance factor of blended chunk c - 1 (the product of
+// 1 - alpha over its contributing splats, no stop rule; a factor that falls to 1e-4 or below stays
+// there) and publishes it, then waits for the factors of blended chunks 0 .. c - 2 published by
+// the workgroups of blended chunks 1 .. c - 1, starts from their product and blends its chunk,
+// storing the slots of its two plan chunks. A pixel that stopped in an earlier chunk starts at or
+// below 1e-4 and so adds nothing. The last of a split tile's workgroups to finish forms its
+// pixels: the transmittance of the first plan chunk that stopped (else of the last chunk), the
+// colours summed over the chunks in order, the last added entry of the last chunk that added one.
 // The chunk workgroups take tickets in launch order, so a workgroup only waits for workgroups that
 // have started; every wait is also bounded.
 // DEPTH: also the depth channel, D = sum z_i alpha_i T_i (background depth 0).
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ float l1_sign(float d) { return d > 0.0f ? 1.0f : (d < 0.0f ? -1.0f : 0.0f); }
 
-// a tile is split when it has three or more chunks and more than this many entries: the split's
-// chain (a factor pass and a blend of one chunk each) must be well below the whole tile's walk to
-// pay for the factor passes' extra work
-constexpr uint32_t kSplitMinChunks = 3;
-constexpr uint32_t kSplitMinEntries = 513;
 constexpr uint32_t kWaitPolls = 1u << 22;    // a bound on each wait for a published factor
 
 // The raster workspace, per checkpoint slot and pixel: (T after the chunk, colour the chunk added),
@@ -333,17 +329,17 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
   uint32_t chunk = 0, nx = 0;
   bool ticketed = false;
   if (CHUNKED) {
-    nx = plan[kPlanExtra];
+    nx = plan[kPlanSplit];
     if (blockIdx.x < nx) {
-      // a chunk item: its ticket picks the item, so items are taken in the order they start
+      // a split chunk: its ticket picks the item, so items are taken in the order they start
       if (tid == 0) s_word = atomicAdd(&ws.sync[0], 1u);
       __syncthreads();
       const uint32_t b = s_word;
       ticketed = true;
       if (b < nx) {  // always, with the counters zero at the launch
-        const uint32_t* item = plan + kPlanOrder + 2 * ntiles + 2 * b;
+        const uint32_t* item = plan + kPlanOrder + 2 * ntiles + 2 * kPlanMaxChunks + 2 * b;
         tile = (int)item[0];
-        chunk = item[1];
+        chunk = 2u * item[1];  // the plan chunk that starts the blended chunk
       }
     } else {
       if (blockIdx.x - nx >= ntiles) return;  // workgroup-uniform
@@ -371,19 +367,25 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
     const uint32_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
     const uint32_t len = end - start;
     const uint32_t L = CHUNKED ? plan[kPlanChunk] : 1u;
-    const uint32_t nch = (CHUNKED && len > L) ? (len + L - 1u) / L : 1u;
-    const bool split = CHUNKED && nch >= kSplitMinChunks && len >= kSplitMinEntries;
+    const uint32_t nch = (CHUNKED && len > L) ? (len + L - 1u) / L : 1u;  // the plan's chunks
+    // a split tile is blended in chunks of two plan chunks (the split pays only for long chains;
+    // the backward's chunks stay short), fc of them
+    const uint32_t Lf = 2u * L;
+    const uint32_t nf = plan_blended_chunks(len, L);
+    const bool split = CHUNKED && plan_split(len, L);
+    const uint32_t fc = chunk >> 1;  // the blended chunk that plan chunk `chunk` belongs to
     const uint32_t sbase = nch > 1 ? plan[kPlanOrder + ntiles + tile] : 0u;  // the tile's first slot
-    // a chunk item of an unsplit tile has nothing to do: the tile's workgroup walks all of it
-    if (chunk == 0 || split) {
-      const uint32_t rs = split ? chunk * L : 0u;
-      const uint32_t re = split ? (rs + L < len ? rs + L : len) : len;
+    // the items are the split tiles' blended chunks; a tile's own workgroup takes its first one
+    // (all of it when it is not split)
+    {
+      const uint32_t rs = split ? fc * Lf : 0u;
+      const uint32_t re = split ? (rs + Lf < len ? rs + Lf : len) : len;
       float T = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f, cd = 0.0f;
-      if (split && chunk > 0) {
-        // the factor of chunk - 1, published for the later chunks
+      if (split && fc > 0) {
+        // the factor of blended chunk fc - 1, published for the later ones
         float F = 1.0f;
         bool fdone = !inside;
-        walk_entries<false>(n, ids, start, rs - L, rs, means2d, conics, opac, colors, depths, tx0, ty0, fdone, s_a,
+        walk_entries<false>(n, ids, start, rs - Lf, rs, means2d, conics, opac, colors, depths, tx0, ty0, fdone, s_a,
                             s_b, s_c, s_z, s_qm, [&](int k0, int k1, bool has1, uint32_t) {
           const float4 a0 = s_a[k0], b0 = s_b[k0];
           const float4 a1 = s_a[k1], b1 = s_b[k1];
@@ -394,39 +396,53 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
           fdone = fdone || __float_as_uint(F) <= __float_as_uint(kTransmittanceMin);
         }, [](uint32_t) {});
         // published with device-coherent stores, complete before the barrier and so before the flag
-        if (inside) st_dev(ws.tprod + (size_t)(sbase + chunk - 1u) * kRasterThreads + tid, F);
+        if (inside) st_dev(ws.tprod + (size_t)(sbase + fc - 1u) * kRasterThreads + tid, F);
         wait_mem();
         __syncthreads();
         if (tid == 0) {
           uint32_t* flag = ws.sync + 2 + kPlanMaxSlots + sbase;
-          st_dev(flag + chunk - 1u, 1u);
-          for (uint32_t i = 0; i + 1u < chunk; ++i) {
+          st_dev(flag + fc - 1u, 1u);
+          for (uint32_t i = 0; i + 1u < fc; ++i) {
             uint32_t polls = 0;
             while (ld_dev(flag + i) == 0u && ++polls < kWaitPolls) __builtin_amdgcn_s_sleep(2);
           }
         }
         __syncthreads();
         if (inside) {
-          for (uint32_t i = 0; i + 1u < chunk; ++i) T *= ld_dev(ws.tprod + (size_t)(sbase + i) * kRasterThreads + tid);
+          for (uint32_t i = 0; i + 1u < fc; ++i) T *= ld_dev(ws.tprod + (size_t)(sbase + i) * kRasterThreads + tid);
           T *= F;
         }
       }
       uint32_t last = 0;
       // a chunk that starts at or below 1e-4 would stop at its first contributing splat: done already
       bool done = !inside || __float_as_uint(T) <= __float_as_uint(kTransmittanceMin);
-      // an unsplit tile of two chunks stores slot j as it passes the start of chunk j + 1 (each wave
-      // its own pixels, where the boundary's mask word starts); (pr, pg, pb, pd) hold the colour of
-      // the chunks before the current one
+      // the walk stores the slot of plan chunk j as it passes the start of chunk j + 1 (each wave
+      // its own pixels, where the boundary's mask word starts); a blended chunk of a split tile
+      // stores its plan chunks' slots device-coherently (another workgroup sums them), with the
+      // last added entry and the stop bit; (pr, pg, pb, pd) hold the colour of the chunks before
+      // the current one
       float pr = 0.0f, pg = 0.0f, pb = 0.0f, pd = 0.0f;
-      const bool seq_ckpt = CHUNKED && !split && nch > 1;
-      uint32_t next_b = seq_ckpt ? L : 0xFFFFFFFFu;
+      const bool ckpts = CHUNKED && nch > 1;
+      uint32_t next_b = (ckpts && rs + L < re) ? rs + L : 0xFFFFFFFFu;
       const size_t slot0 = (size_t)sbase * kRasterThreads + tid;
-      size_t cur = slot0;  // the slot of the chunk being walked (sequential checkpoints)
-      auto store_ckpt = [&]() {
-        if (inside) {
+      size_t cur = slot0 + (split ? (size_t)(2u * fc) * kRasterThreads : 0u);  // the slot being filled
+      auto put_slot = [&]() {
+        if (!inside) return;
+        if (split) {
+          float* ck = (float*)(ws.ckpt + cur);
+          st_dev(ck + 0, T);
+          st_dev(ck + 1, cr);
+          st_dev(ck + 2, cg);
+          st_dev(ck + 3, cb);
+          if (DEPTH) st_dev(ws.ckpt_d + cur, cd);
+          st_dev(ws.lastc + cur, last | (done ? 0x80000000u : 0u));
+        } else {
           ws.ckpt[cur] = make_float4(T, cr, cg, cb);
           if (DEPTH) ws.ckpt_d[cur] = cd;
         }
+      };
+      auto store_ckpt = [&]() {
+        put_slot();
         cur += kRasterThreads;
         pr += cr;
         pg += cg;
@@ -434,7 +450,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
         pd += cd;
         cr = cg = cb = cd = 0.0f;
         next_b += L;
-        if (next_b >= len) next_b = 0xFFFFFFFFu;
+        if (next_b >= re) next_b = 0xFFFFFFFFu;
       };
       walk_entries<DEPTH>(n, ids, start, rs, re, means2d, conics, opac, colors, depths, tx0, ty0, done, s_a, s_b,
                           s_c, s_z, s_qm, [&](int k0, int k1, bool has1, uint32_t list1) {
@@ -448,14 +464,11 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
         blend_step<DEPTH>(e0, true, b0.z, b0.w, c0, z0, list1 + (uint32_t)k0, T, cr, cg, cb, cd, last, done);
         blend_step<DEPTH>(e1, has1, b1.z, b1.w, c1, z1, list1 + (uint32_t)k1, T, cr, cg, cb, cd, last, done);
       }, [&](uint32_t e) {
-        if (seq_ckpt && e >= next_b) store_ckpt();  // wave-uniform
+        if (ckpts && e >= next_b) store_ckpt();  // wave-uniform
       });
-      if (seq_ckpt) {
+      if (ckpts) {
         while (next_b != 0xFFFFFFFFu) store_ckpt();  // boundaries past the last walked batch
-        if (inside) {  // the last chunk's slot
-          ws.ckpt[cur] = make_float4(T, cr, cg, cb);
-          if (DEPTH) ws.ckpt_d[cur] = cd;
-        }
+        put_slot();                                  // the last plan chunk's slot
         cr += pr;
         cg += pg;
         cb += pb;
@@ -463,22 +476,13 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
       }
       bool finish = !split;
       if (split) {
-        // this chunk's slot; the tile's last workgroup to get here forms its pixels
-        const size_t o = slot0 + (size_t)chunk * kRasterThreads;
-        if (inside) {  // device-coherent stores, complete before the barrier and so before the arrival
-          float* ck = (float*)(ws.ckpt + o);
-          st_dev(ck + 0, T);
-          st_dev(ck + 1, cr);
-          st_dev(ck + 2, cg);
-          st_dev(ck + 3, cb);
-          if (DEPTH) st_dev(ws.ckpt_d + o, cd);
-          st_dev(ws.lastc + o, last | (done ? 0x80000000u : 0u));
-        }
+        // the slots are out (device-coherent, complete before the barrier and so before the
+        // arrival); the tile's last blended chunk to get here forms its pixels
         wait_mem();
         __syncthreads();
         if (tid == 0) s_word = atomicAdd(ws.sync + 2 + sbase, 1u);
         __syncthreads();
-        finish = s_word == nch - 1u;
+        finish = s_word == nf - 1u;
         if (finish) {
           T = 1.0f;
           cr = cg = cb = cd = 0.0f;
@@ -499,7 +503,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
           }
           // every workgroup of the tile has arrived, so no one reads its words any more
           if (tid == 0) st_dev(ws.sync + 2 + sbase, 0u);
-          for (uint32_t i = tid; i + 1u < nch; i += kRasterThreads) st_dev(ws.sync + 2 + kPlanMaxSlots + sbase + i, 0u);
+          for (uint32_t i = tid; i + 1u < nf; i += kRasterThreads) st_dev(ws.sync + 2 + kPlanMaxSlots + sbase + i, 0u);
         }
       }
       if (finish && inside) {
@@ -1385,7 +1389,8 @@ gs_status rasterize_fwd(const char* name, int32_t n, const gs_projected* proj, c
   hipStream_t s = (hipStream_t)stream;
   {
     // with a plan and the raster workspace (a training forward) the checkpoints are stored and
-    // tiles of three or more chunks and more than 512 entries are blended chunk by chunk in parallel
+    // tiles of three or more blended chunks (2 L entries) and more than 512 entries are blended
+    // chunk by chunk in parallel
     const bool ck = d_raster_plan && d_raster_ws;
     const bool dep = d_depth != nullptr;
     auto pick = [&](auto c_, auto k_, auto d_) {
@@ -1405,8 +1410,8 @@ gs_status rasterize_fwd(const char* name, int32_t n, const gs_projected* proj, c
     const float* dp = n > 0 ? proj->d_depths : nullptr;
     {
       TimedScope ts("blend", s);
-      // a training forward adds the chunk items (at most kPlanMaxChunks; the plan says how many)
-      const unsigned grid = (unsigned)(ck ? ntiles + kPlanMaxChunks : ntiles);
+      // a training forward adds the split chunks (at most kPlanMaxSplit; the plan says how many)
+      const unsigned grid = (unsigned)(ck ? ntiles + kPlanMaxSplit : ntiles);
       hipLaunchKernelGGL(kern, dim3(grid), dim3(kRasterThreads), 0, s, (uint32_t)n, d_tile_ranges, d_raster_plan,
                          (uint32_t)ntiles, wsp, d_ids, m2, co, op, cl, dp, dc, d_image, d_depth, d_final_T,
                          d_n_contrib, (unsigned long long*)d_eval_count, d_target, d_dL_dimage, l1_scale);

@@ -160,10 +160,11 @@ def gs_raster_plan_words(cam: GsCamera) -> int:
 
 
 def plan_max_chunks() -> int:
-    """The most extra work items a raster plan holds (the plan is 4 + 2 tiles + 2 of these words)."""
+    """The most extra work items a raster plan holds, M (the plan is 4 + 2 tiles + 2 M + 2 (M / 2)
+    words: the items, then the training forward's split chunks)."""
     cam = GsCamera()
     cam.width, cam.height = 16, 16
-    return (gs_raster_plan_words(cam) - 4 - 2) // 2
+    return (gs_raster_plan_words(cam) - 4 - 2) // 3
 
 
 def raster_sync_bytes() -> int:

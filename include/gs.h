@@ -130,7 +130,7 @@ gs_status gs_project(int32_t n, int32_t sh_degree, const float* d_means, const f
  * Outputs: d_keys [P] uint64, d_ids [P] uint32, d_tile_ranges [tiles, 2] uint32;
  *   d_raster_plan (optional, gs_raster_plan_words(cam) uint32): how the raster calls schedule the
  *   frame -- the tiles in an order with the ones holding more pairs first (by the bit length of
- *   the count, empty tiles last), a chunk length L (a power of two >= 128 with P <= 2048 L),
+ *   the count, empty tiles last), a chunk length L (a power of two >= 128 with P <= 4096 L),
  *   and for every tile of two or more chunks of L list entries its checkpoint slots and the
  *   backward's extra work items (its chunks after the first); P itself goes to
  *   *d_num_pairs (device int64, optional, written on `stream`) and to *h_num_pairs (host,
@@ -188,10 +188,11 @@ gs_status gs_bin_and_sort_noalloc(int32_t n, const gs_projected* proj, const gs_
  *   used only with a plan; every call leaves its synchronisation words zero again): the forward
  *   stores there, for tiles longer than the plan's chunk length L, per chunk of L list entries
  *   and per pixel the transmittance after the chunk and the colour the chunk added, which lets
- *   gs_rasterize_bwd split such tiles. With it, a tile of three or more chunks and more than 512
- *   entries is blended chunk by chunk in parallel: chunk j starts from the product of the earlier
- *   chunks' transmittance factors (1 - alpha multiplied over their contributing splats), and the
- *   image is summed chunk by chunk, so results equal those without a workspace up to rounding.
+ *   gs_rasterize_bwd split such tiles. With it, a tile of more than 512 entries and three or more
+ *   chunks of 2 L entries is blended chunk by chunk in parallel: a chunk starts from the product
+ *   of the earlier chunks' transmittance factors (1 - alpha multiplied over their contributing
+ *   splats), and the image is summed chunk by chunk, so results equal those without a workspace
+ *   up to rounding.
  *   Calls that share a workspace must not overlap (one stream, or ordered streams).
  * Outputs: d_image [h,w,3]; d_depth [h,w] (optional, NULL = not rendered): the depth channel,
  *   the splats' camera z through the same weights, D = sum z_i alpha_i T_i with background depth

@@ -115,6 +115,18 @@ def assert_raster_plan(plan_np, ranges_np, P):
     items = plan[4 + 2 * n:4 + 2 * n + 2 * n_extra].reshape(-1, 2)
     want = sorted((t, c) for t in multi for c in range(1, nch[t]))
     assert sorted(map(tuple, items.tolist())) == want, "extra work items differ"
+    # the training forward's split chunks: tiles of more than 512 entries and at least three
+    # chunks of 2 L entries, their chunks after the first, each tile's together in order
+    nb = (cnt + 2 * L - 1) // (2 * L)
+    spl = np.nonzero((cnt > 512) & (nb >= 3))[0]
+    n_split = plan[3]
+    assert n_split == (nb[spl] - 1).sum() and n_split <= C // 2
+    fitems = plan[4 + 2 * n + 2 * C:4 + 2 * n + 2 * C + 2 * n_split].reshape(-1, 2)
+    assert sorted(map(tuple, fitems.tolist())) == sorted((t, c) for t in spl for c in range(1, nb[t])), \
+        "split chunks differ"
+    for t in spl:  # a tile's chunks in ascending order (a chunk waits only on earlier items)
+        pos = np.nonzero(fitems[:, 0] == t)[0]
+        assert np.array_equal(fitems[pos, 1], np.arange(1, nb[t])) and np.all(np.diff(pos) == 1)
 
 
 def pixel_last_ids(nc, ids_np, ranges_np, pixels, width):

@@ -37,10 +37,12 @@ def test_finalizer_lds_layout_fits():
     lds = 12288                           # the finalizer pass's s_mem words (2 x 4096 keys < 12288)
     assert "kFinAuxWords = 8 * kRadix" in open(SRC).read()
     assert step + aux <= lds, "steps of tiles overlap the auxiliary words"
-    # the auxiliary words: three histogram rows, then classes (33), cursors (33) and two counters
-    # in the fourth row, scan partials (rows x 16) in the fifth, row sums (rows) in the sixth
+    # the auxiliary words: three histogram rows, then classes (33), cursors (33) and three
+    # counters in the fourth row, scan partials (rows x 16) in the fifth, row sums (rows) in the
+    # sixth; the zeroing covers the classes, cursors and counters
     cls, cur, misc = 3 * radix, 3 * radix + 64, 3 * radix + 128
-    assert cls + 33 <= cur and cur + 33 <= misc and misc + 2 <= 4 * radix
+    assert cls + 33 <= cur and cur + 33 <= misc and misc + 3 <= 4 * radix
+    assert "if (tid < 131) s_cls[tid] = 0;" in open(SRC).read()
     assert 4 * radix + rows * 16 <= 5 * radix and 5 * radix + rows <= aux
 
 
