@@ -443,6 +443,34 @@ __device__ __forceinline__ uint32_t wave_class_slot(bool valid, uint32_t cls, ui
   return base + (uint32_t)__popcll(m & lt);
 }
 
+// The wave's lanes take v consecutive units each of the LDS counter *ctr, in lane order, with one
+// atomic for the wave (none when the wave takes nothing); returns the lane's first unit. Every
+// lane of the wave calls it.
+__device__ __forceinline__ uint32_t wave_take(uint32_t v, uint32_t* ctr, int lane);
+// Work items (t, 1 .. n) of a tile from position x0 on (two words each): a lane writes its own
+// tile's when they are few, the wave together (one tile at a time) for longer lists. Every lane of
+// the wave calls it.
+__device__ __forceinline__ void write_items(uint32_t n, uint32_t x0, uint32_t t, uint32_t* items, int lane) {
+  constexpr uint32_t kOwnItems = 8;
+  if (n <= kOwnItems)
+    for (uint32_t j = 0; j < n; ++j) {
+      items[2 * (x0 + j)] = t;
+      items[2 * (x0 + j) + 1] = j + 1u;
+    }
+  uint64_t mm = __ballot(n > kOwnItems);
+  while (mm) {
+    const int src = __builtin_ctzll(mm);
+    mm &= mm - 1;
+    const uint32_t n1 = (uint32_t)__builtin_amdgcn_readlane((int)n, src);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)x0, src);
+    const uint32_t tt = (uint32_t)__builtin_amdgcn_readlane((int)t, src);
+    for (uint32_t j = (uint32_t)lane; j < n1; j += 64) {
+      items[2 * (b + j)] = tt;
+      items[2 * (b + j) + 1] = j + 1u;
+    }
+  }
+}
+
 // DPP lane shifts within rows of 16 lanes (row_shr) and row broadcasts (row_bcast); lanes whose
 // source lies outside the row read 0, lanes of rows outside ROWMASK are left as they are.
 template <int CTRL, int ROWMASK>
@@ -463,6 +491,17 @@ __device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
   v += dpp_u32<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
   v += dpp_u32<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
   return v;
+}
+
+__device__ __forceinline__ uint32_t wave_take(uint32_t v, uint32_t* ctr, int lane) {
+  const uint32_t inc = wave_incl_scan_dpp(v);
+  const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+  uint32_t base = 0;
+  if (tot != 0u) {  // wave-uniform
+    if (lane == 0) base = atomicAdd(ctr, tot);
+    base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
+  }
+  return base + inc - v;
 }
 
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
@@ -524,7 +563,8 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
   if (tid == 0) s_p64 = 0;
   __syncthreads();
   uint64_t P = 0;
-  uint32_t P32 = 0, L = kPlanMinChunk;
+  uint32_t P32 = 0, L = kPlanMinChunk, lbits = 7;  // L = 2^lbits
+  static_assert(kPlanMinChunk == 128u, "lbits starts at log2 of the minimum chunk");
   bool fits = false;
 #pragma unroll 1
   for (int sweep = 0; sweep < 2; ++sweep) {
@@ -537,13 +577,25 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
       uint32_t step_end = P32;  // the start after the step's last tile
       if (sweep == 0 || !one_step) {
         __syncthreads();  // the previous step's reads of s (neighbours included) are done
+        if (a.tmat) {  // a tile's difference sums the blocks' rows: two rows' loads in flight together
 #pragma unroll
-        for (int q = 0; q < kFinRows; q += 2) {  // two rows' loads in flight together
-          const uint32_t i0 = (uint32_t)(q * kSortThreads + tid), i1 = i0 + kSortThreads;
-          const uint32_t v0 = (q < rows && i0 < m) ? tdiff_at(a, cb + i0) : 0u;
-          const uint32_t v1 = (q + 1 < rows && i1 < m) ? tdiff_at(a, cb + i1) : 0u;
-          if (q < rows) s[i0] = v0;
-          if (q + 1 < rows) s[i1] = v1;
+          for (int q = 0; q < kFinRows; q += 2) {
+            const uint32_t i0 = (uint32_t)(q * kSortThreads + tid), i1 = i0 + kSortThreads;
+            const uint32_t v0 = (q < rows && i0 < m) ? tdiff_at(a, cb + i0) : 0u;
+            const uint32_t v1 = (q + 1 < rows && i1 < m) ? tdiff_at(a, cb + i1) : 0u;
+            if (q < rows) s[i0] = v0;
+            if (q + 1 < rows) s[i1] = v1;
+          }
+        } else {  // every row's load in flight together
+          uint32_t v[kFinRows];
+#pragma unroll
+          for (int q = 0; q < kFinRows; ++q) {
+            const uint32_t i = (uint32_t)(q * kSortThreads + tid);
+            v[q] = (q < rows && i < m) ? a.tdiff[cb + i] : 0u;
+          }
+#pragma unroll
+          for (int q = 0; q < kFinRows; ++q)
+            if (q < rows) s[q * kSortThreads + tid] = v[q];
         }
         // counts: the inclusive prefix of the differences = the next tile's exclusive one
         const uint32_t dtot = lds_rows_scan(s, rows, carry_d, s_wt, s_rt);
@@ -575,7 +627,6 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
         step_end = carry_c;
       }
       if (sweep == 0) continue;
-      uint32_t* extra = a.plan + kPlanOrder + 2 * a.ntiles;
 #pragma unroll 1
       for (int q = 0; q < rows; ++q) {
         const uint32_t i = (uint32_t)(q * kSortThreads + tid), t = cb + i;
@@ -605,46 +656,18 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
         const uint32_t slot = wave_class_slot(valid, count_class(c), s_cur, lane);
         // the class cursors partition [0, ntiles): every valid slot is below ntiles
         if (valid && slot < a.ntiles) a.plan[kPlanOrder + slot] = t;
-        // a tile of two or more chunks: its checkpoint slots and extra work items
-        const uint32_t nch = (c + L - 1u) / L;
-        const bool multi = valid && nch >= 2u;
-        uint32_t xb = 0;
-        if (multi) {
-          a.plan[kPlanOrder + a.ntiles + t] = atomicAdd(&s_misc[1], nch);
-          xb = atomicAdd(&s_misc[0], nch - 1u);
-        }
-        uint64_t mm = __ballot(multi);
-        while (mm) {  // the wave writes each such tile's items together
-          const int src = __builtin_ctzll(mm);
-          mm &= mm - 1;
-          const uint32_t n1 = (uint32_t)__builtin_amdgcn_readlane((int)nch, src) - 1u;
-          const uint32_t x0 = (uint32_t)__builtin_amdgcn_readlane((int)xb, src);
-          const uint32_t tt = (uint32_t)__builtin_amdgcn_readlane((int)t, src);
-          for (uint32_t j = (uint32_t)lane; j < n1; j += 64) {
-            extra[2 * (x0 + j)] = tt;
-            extra[2 * (x0 + j) + 1] = j + 1u;
-          }
-        }
-        // a tile the training forward splits: its blended chunks after the first, in order
-        const bool spl = valid && fits && plan_split(c, L);
-        uint32_t fb = 0, nb = 0;
-        if (spl) {
-          nb = plan_blended_chunks(c, L);
-          fb = atomicAdd(&s_misc[2], nb - 1u);
-        }
-        uint32_t* fitems = a.plan + kPlanOrder + 2 * a.ntiles + 2 * kPlanMaxChunks;
-        mm = __ballot(spl);
-        while (mm) {
-          const int src = __builtin_ctzll(mm);
-          mm &= mm - 1;
-          const uint32_t n1 = (uint32_t)__builtin_amdgcn_readlane((int)nb, src) - 1u;
-          const uint32_t x0 = (uint32_t)__builtin_amdgcn_readlane((int)fb, src);
-          const uint32_t tt = (uint32_t)__builtin_amdgcn_readlane((int)t, src);
-          for (uint32_t j = (uint32_t)lane; j < n1; j += 64) {
-            fitems[2 * (x0 + j)] = tt;
-            fitems[2 * (x0 + j) + 1] = j + 1u;
-          }
-        }
+        // a tile of two or more chunks: its checkpoint slots and extra work items (chunks 1 ..); a
+        // tile the training forward splits: its blended chunks after the first, in order (c is 0
+        // for lanes past the step and on overflow)
+        const uint32_t nch = (c + L - 1u) >> lbits;
+        const bool multi = nch >= 2u;
+        const uint32_t nb = plan_split_pow2(c, lbits) ? plan_blended_chunks_pow2(c, lbits) : 1u;
+        const uint32_t sb = wave_take(multi ? nch : 0u, &s_misc[1], lane);
+        const uint32_t xb = wave_take(multi ? nch - 1u : 0u, &s_misc[0], lane);
+        const uint32_t fb = wave_take(nb - 1u, &s_misc[2], lane);
+        if (multi) a.plan[kPlanOrder + a.ntiles + t] = sb;
+        write_items(multi ? nch - 1u : 0u, xb, t, a.plan + kPlanOrder + 2 * a.ntiles, lane);
+        write_items(nb - 1u, fb, t, a.plan + kPlanOrder + 2 * a.ntiles + 2 * kPlanMaxChunks, lane);
       }
     }
     if (sweep == 0) {
@@ -653,7 +676,10 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
       P32 = carry_c;
       fits = P <= a.capacity;
       if (fits)
-        while ((uint64_t)L * kPlanMaxChunks < P) L <<= 1;
+        while ((uint64_t)L * kPlanMaxChunks < P) {
+          L <<= 1;
+          ++lbits;
+        }
       if (tid == 0) {
         // on overflow every tile is empty for the raster calls: all in class 0
         uint32_t slot = 0;

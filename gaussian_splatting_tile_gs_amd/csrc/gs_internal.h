@@ -249,10 +249,21 @@ inline size_t plan_words(size_t ntiles) { return kPlanOrder + 2 * ntiles + 2 * k
 // The training forward's split rule: the split's chain (a factor pass and a blend of one blended
 // chunk of 2 L entries) must be well below the whole tile's walk to pay for the factor passes.
 constexpr uint32_t kSplitMinChunks = 3, kSplitMinEntries = 513;
-__host__ __device__ inline uint32_t plan_blended_chunks(uint32_t c, uint32_t L) { return (c + 2u * L - 1u) / (2u * L); }
-__host__ __device__ inline bool plan_split(uint32_t c, uint32_t L) {
+__host__ __device__ constexpr uint32_t plan_blended_chunks(uint32_t c, uint32_t L) { return (c + 2u * L - 1u) / (2u * L); }
+__host__ __device__ constexpr bool plan_split(uint32_t c, uint32_t L) {
   return c >= kSplitMinEntries && plan_blended_chunks(c, L) >= kSplitMinChunks;
 }
+// The same for L = 2^lb (the binning's finalizer, where L is a power of two): shifts for divisions.
+__host__ __device__ constexpr uint32_t plan_blended_chunks_pow2(uint32_t c, uint32_t lb) {
+  return (c + (2u << lb) - 1u) >> (lb + 1u);
+}
+__host__ __device__ constexpr bool plan_split_pow2(uint32_t c, uint32_t lb) {
+  return c >= kSplitMinEntries && plan_blended_chunks_pow2(c, lb) >= kSplitMinChunks;
+}
+static_assert(plan_split_pow2(512, 7) == plan_split(512, 128) && plan_split_pow2(513, 7) == plan_split(513, 128) &&
+                  plan_split_pow2(768, 8) == plan_split(768, 256) && plan_split_pow2(1025, 8) == plan_split(1025, 256) &&
+                  plan_blended_chunks_pow2(100000, 9) == plan_blended_chunks(100000, 512),
+              "the power-of-two forms must agree with the general ones");
 
 // ---------------------------------------------------------------------------------------------
 // Host side: status, last error, kernel timing.
