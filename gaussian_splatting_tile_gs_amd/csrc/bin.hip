@@ -421,9 +421,10 @@ __device__ void tile_rows(const TileCountArgs& a, uint32_t rb, uint32_t* lds, ui
 // takes tiles 1024 q + tid, so each row of 1024 tiles is loaded and stored contiguously. The
 // difference array is scanned into per-tile counts and the counts into range starts, in place.
 // A first sweep finds P (64 bits) and how many tiles fall in each count class (bit length of the
-// count). A second writes the ranges and the pair-sort histograms (when P fits), the processing
-// order (heaviest class first, empty tiles last, so that the long raster workgroups start
-// first), and for each tile of two or more chunks of L its checkpoint slots and extra work items
+// count), per XCD list (plan_xcd). A second writes the ranges and the pair-sort histograms (when P
+// fits), the processing order (each XCD's list heaviest class first, empty tiles last, so that
+// the long raster workgroups start first; the lists interleaved so that a tile's slot runs on its
+// XCD), and for each tile of two or more chunks of L its checkpoint slots and extra work items
 // (chunks 1 ..). With one step the second sweep finds the starts still in LDS.
 // The code is loops over rows rather than unrolled: it runs once per frame, on one compute unit,
 // where straight-line code would wait on instruction fetch.
@@ -431,13 +432,14 @@ __device__ void tile_rows(const TileCountArgs& a, uint32_t rb, uint32_t* lds, ui
 // run's count is the difference of the range starts at its ends, added with two LDS atomics.
 __device__ __forceinline__ uint32_t count_class(uint32_t c) { return c ? 32u - (uint32_t)__clz(c) : 0u; }
 
-// Lanes with the same class share one LDS atomic on ctr[cls]; returns a valid lane's slot.
-// Every lane of the wave calls it.
-__device__ __forceinline__ uint32_t wave_class_slot(bool valid, uint32_t cls, uint32_t* ctr, int lane) {
-  const uint64_t m = match_digit<6>(cls, 6, __ballot(valid));
+// Lanes with the same key (BITS bits) share one LDS atomic on ctr[key]; returns a valid lane's
+// place. Every lane of the wave calls it.
+template <int BITS>
+__device__ __forceinline__ uint32_t wave_key_slot(bool valid, uint32_t key, uint32_t* ctr, int lane) {
+  const uint64_t m = match_digit<BITS>(key, BITS, __ballot(valid));
   const int leader = __builtin_ctzll(m | (1ull << 63));
   uint32_t base = 0;
-  if (valid && lane == leader) base = atomicAdd(&ctr[cls], (uint32_t)__popcll(m));
+  if (valid && lane == leader) base = atomicAdd(&ctr[key], (uint32_t)__popcll(m));
   base = __shfl(base, leader, 64);
   const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
   return base + (uint32_t)__popcll(m & lt);
@@ -513,6 +515,11 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
 constexpr int kFinRows = 10;
 constexpr uint32_t kFinStep = kSortThreads * kFinRows;
 constexpr uint32_t kFinAuxWords = 8 * kRadix;  // histograms, classes, scan partials
+constexpr uint32_t kFinClasses = 33;           // count classes 0 (empty) .. 32
+constexpr uint32_t kFinKeys = kXcds * kFinClasses;  // (XCD, class): key x * 33 + class, 9 bits
+constexpr uint32_t kFinMisc = 16;
+static_assert(kFinKeys <= 512, "the (XCD, class) key takes 9 bits");
+static_assert(3 * kRadix + 2 * kFinKeys + kFinMisc + 17 * kFinRows <= kFinAuxWords, "finalizer auxiliary words overflow");
 
 // Exclusive scan, in place, of `rows` rows of 1024 values in LDS (s[1024 q + tid] in thread
 // tid), offset by carry; returns the sum (mod 2^32). Every thread calls it; it ends with a
@@ -550,20 +557,24 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
   const int tid = threadIdx.x, lane = tid & 63;
   uint32_t* aux = lds + (lds_words - kFinAuxWords);
   uint32_t(*s_hist)[kRadix] = reinterpret_cast<uint32_t(*)[kRadix]>(aux);  // rows 0-2: histograms
-  uint32_t* s_cls = aux + 3 * kRadix;  // tiles per count class (33)
-  uint32_t* s_cur = s_cls + 64;        // next order slot per class
-  uint32_t* s_misc = s_cls + 128;      // [0] extra work items, [1] checkpoint slots, [2] split chunks
-  uint32_t* s_wt = aux + 4 * kRadix;   // kFinRows x 16 scan partials
-  uint32_t* s_rt = aux + 5 * kRadix;   // kFinRows row sums
+  uint32_t* s_cls = aux + 3 * kRadix;  // tiles per (XCD, count class)
+  uint32_t* s_cur = s_cls + kFinKeys;  // next place in the XCD's list per (XCD, class)
+  // [0] extra work items, [1] checkpoint slots, [2] split chunks, [3] tail slots, [8 + x] the
+  // length of XCD x's list
+  uint32_t* s_misc = s_cur + kFinKeys;
+  uint32_t* s_wt = s_misc + kFinMisc;  // kFinRows x 16 scan partials
+  uint32_t* s_rt = s_wt + 16 * kFinRows;  // kFinRows row sums
   uint32_t* s = lds;                   // the step's tiles
   const bool one_step = a.ntiles <= kFinStep;
   if (tid < kRadix)
     for (int k = 0; k < a.npass; ++k) s_hist[k][tid] = 0;
-  if (tid < 131) s_cls[tid] = 0;  // classes, cursors, misc
+  if (tid < (int)(2 * kFinKeys + kFinMisc)) s_cls[tid] = 0;  // classes, cursors, misc
   if (tid == 0) s_p64 = 0;
   __syncthreads();
   uint64_t P = 0;
   uint32_t P32 = 0, L = kPlanMinChunk, lbits = 7;  // L = 2^lbits
+  uint32_t mlist = 0;                                // the shortest XCD list
+  const uint32_t tiles_x = (uint32_t)a.tiles_x;
   static_assert(kPlanMinChunk == 128u, "lbits starts at log2 of the minimum chunk");
   bool fits = false;
 #pragma unroll 1
@@ -617,7 +628,7 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
             const uint32_t i = (uint32_t)(q * kSortThreads + tid);
             const uint32_t cq = s[i];  // this thread's own entry (0 past the step)
             c64 += cq;
-            wave_class_slot(i < m, count_class(cq), s_cls, lane);
+            wave_key_slot<9>(i < m, plan_xcd(cb + i, tiles_x) * kFinClasses + count_class(cq), s_cls, lane);
           }
           c64 = wave_sum_u64(c64);
           if (lane == 0) atomicAdd(&s_p64, (unsigned long long)c64);
@@ -653,8 +664,14 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
           }
         }
         if (!a.plan) continue;
-        const uint32_t slot = wave_class_slot(valid, count_class(c), s_cur, lane);
-        // the class cursors partition [0, ntiles): every valid slot is below ntiles
+        // the tile's place in its XCD's list; the lists interleave (slot 8 place + x) up to the
+        // shortest one's length, the longer lists' rest take the slots after that. The places of a
+        // list cover [0, its length) and the rest [8 mlist, ntiles): every valid slot is below ntiles
+        const uint32_t x = plan_xcd(t, tiles_x);
+        const uint32_t place = wave_key_slot<9>(valid, x * kFinClasses + count_class(c), s_cur, lane);
+        const bool rest = valid && place >= mlist;
+        const uint32_t rslot = wave_take(rest ? 1u : 0u, &s_misc[3], lane);
+        const uint32_t slot = rest ? kXcds * mlist + rslot : kXcds * place + x;
         if (valid && slot < a.ntiles) a.plan[kPlanOrder + slot] = t;
         // a tile of two or more chunks: its checkpoint slots and extra work items (chunks 1 ..); a
         // tile the training forward splits: its blended chunks after the first, in order (c is 0
@@ -680,15 +697,20 @@ __device__ void tile_finalize(const TileCountArgs& a, uint32_t* lds, uint32_t ld
           L <<= 1;
           ++lbits;
         }
-      if (tid == 0) {
-        // on overflow every tile is empty for the raster calls: all in class 0
-        uint32_t slot = 0;
-        for (int c = 32; c >= 0; --c) {
-          s_cur[c] = slot;
-          slot += fits ? s_cls[c] : (c == 0 ? a.ntiles : 0u);
+      if (tid < (int)kXcds) {
+        // XCD tid's list, heaviest class first; on overflow every tile is empty for the raster
+        // calls: all in class 0
+        uint32_t place = 0;
+        for (int c = (int)kFinClasses - 1; c >= 0; --c) {
+          const uint32_t k = (uint32_t)tid * kFinClasses + (uint32_t)c;
+          s_cur[k] = fits ? place : 0u;
+          place += s_cls[k];
         }
+        s_misc[8 + tid] = place;
       }
       __syncthreads();
+      mlist = s_misc[8];
+      for (uint32_t x = 1; x < kXcds; ++x) mlist = min(mlist, s_misc[8 + x]);
     }
   }
   if (tid == 0 && fits)  // the last run ends at P

@@ -227,24 +227,40 @@ __device__ __forceinline__ SplatEval eval_splat(float dx, float dy, float hA, fl
 // ---------------------------------------------------------------------------------------------
 // Raster plan (written by gs_bin_and_sort, read by the raster calls), u32 words:
 //   [0] chunk length L, [1] X = extra work items, [2] checkpoint slots, [3] XF = split chunks,
-//   [4, 4 + T)          tile processing order (T = number of tiles),
+//   [4, 4 + T)          tile processing order (T = number of tiles): slot 8 p + x holds place p of
+//                       XCD x's list of tiles (plan_xcd), heaviest count class first, up to the
+//                       shortest list's length m; the slots from 8 m on hold the longer lists' rest,
 //   [4 + T, 4 + 2T)     per tile with two or more chunks, the index of its first checkpoint slot,
 //   [4 + 2T, 4 + 2T + 2X)  the extra work items (tile, chunk >= 1),
 //   [4 + 2T + 2M, 4 + 2T + 2M + 2XF)  (M = kPlanMaxChunks) the training forward's extra work
 //                       items (tile, blended chunk >= 1) of the tiles it splits.
 // A tile with c pairs has k = ceil(c / L) chunks of L list entries; when k >= 2 it has k slots,
 // slot j holding, per pixel, the transmittance after chunk j and the colour that chunk j added.
-// The backward's work items are the X extra ones, then (order[i], chunk 0) for every tile.
+// The backward's work items are the X extra ones, then, from the next multiple of 8 on (so that
+// slot i runs on XCD i mod 8), (order[i], chunk 0) for every tile.
 // L >= P / kPlanMaxChunks keeps X below kPlanMaxChunks and the slots below 2 kPlanMaxChunks.
 // The training forward blends a tile of more than 512 entries and at least three chunks of 2 L
 // entries chunk by chunk in parallel (plan_split): its work items are the XF split chunks, then
-// (order[i], first chunk) for every tile; XF < X / 2.
+// (order[i], first chunk) for every tile, again from the next multiple of 8 on; XF < X / 2.
 // ---------------------------------------------------------------------------------------------
 constexpr uint32_t kPlanChunk = 0, kPlanExtra = 1, kPlanCheckpoints = 2, kPlanSplit = 3, kPlanOrder = 4;
+// Workgroup b of a launch runs on XCD b mod 8, and each XCD has its own L2. A 128-B line of a 4-B
+// per-pixel array holds 32 pixels of a row: the two tiles of a 2x1 block of tiles, which the order
+// puts on one XCD. The blocks go round the XCDs along a row of blocks, each row of tiles shifted
+// by three, so that every XCD gets a share of every part of the frame.
+constexpr uint32_t kXcds = 8;
+__host__ __device__ constexpr uint32_t plan_xcd(uint32_t t, uint32_t tiles_x) {
+  return ((t % tiles_x) / 2u + 3u * (t / tiles_x)) % kXcds;
+}
+// The first work item of the tiles after n items before them: the next multiple of kXcds.
+__host__ __device__ constexpr uint32_t plan_xcd_align(uint32_t n) { return (n + kXcds - 1u) / kXcds * kXcds; }
 constexpr uint32_t kPlanMinChunk = 128;  // half a raster batch: boundaries fall where a mask word starts
 constexpr uint32_t kPlanMaxChunks = 4096;
 constexpr uint32_t kPlanMaxSlots = 2 * kPlanMaxChunks;
 constexpr uint32_t kPlanMaxSplit = kPlanMaxChunks / 2;
+// X < kPlanMaxChunks and XF < kPlanMaxSplit, so the aligned start of the tiles stays within the
+// launches' extra workgroups (kPlanMaxChunks, kPlanMaxSplit)
+static_assert(kPlanMaxChunks % kXcds == 0 && kPlanMaxSplit % kXcds == 0, "extra workgroups must align to the XCDs");
 inline size_t plan_words(size_t ntiles) { return kPlanOrder + 2 * ntiles + 2 * kPlanMaxChunks + 2 * kPlanMaxSplit; }
 // The training forward's split rule: the split's chain (a factor pass and a blend of one blended
 // chunk of 2 L entries) must be well below the whole tile's walk to pay for the factor passes.

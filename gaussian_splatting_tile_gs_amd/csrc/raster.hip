@@ -342,8 +342,10 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
         chunk = 2u * item[1];  // the plan chunk that starts the blended chunk
       }
     } else {
-      if (blockIdx.x - nx >= ntiles) return;  // workgroup-uniform
-      tile = (int)plan[kPlanOrder + blockIdx.x - nx];
+      // the tiles from a multiple of 8 on: order slot i runs on XCD i mod 8
+      const uint32_t b0 = plan_xcd_align(nx);
+      if (blockIdx.x < b0 || blockIdx.x - b0 >= ntiles) return;  // workgroup-uniform
+      tile = (int)plan[kPlanOrder + blockIdx.x - b0];
     }
   } else {
     tile = plan ? (int)plan[kPlanOrder + blockIdx.x] : (int)blockIdx.x;
@@ -752,8 +754,10 @@ __global__ __launch_bounds__(kRasterThreads) __attribute__((amdgpu_waves_per_eu(
       tile = (int)item[0];
       chunk = item[1];
     } else {
-      if (blockIdx.x - nx >= ntiles) return;  // workgroup-uniform
-      tile = (int)plan[kPlanOrder + blockIdx.x - nx];
+      // the tiles from a multiple of 8 on: order slot i runs on XCD i mod 8
+      const uint32_t b0 = plan_xcd_align(nx);
+      if (blockIdx.x < b0 || blockIdx.x - b0 >= ntiles) return;  // workgroup-uniform
+      tile = (int)plan[kPlanOrder + blockIdx.x - b0];
     }
     const uint32_t L = plan[kPlanChunk];
     const uint32_t len = ranges[2 * tile + 1] - ranges[2 * tile];

@@ -82,12 +82,20 @@ def run_gpu_bin(gs, torch, params_n, proj, cam, capacity):
     return st, P, keys, ids, ranges, plan
 
 
-def assert_raster_plan(plan_np, ranges_np, P):
-    """The raster plan: tiles ordered by non-increasing bit length of their pair count (empty
-    ones last), a chunk length L = the smallest power of two >= 128 with P <= C L (C = the plan's
-    chunk limit), and for every tile of k = ceil(count / L) >= 2 chunks k checkpoint slots
-    (disjoint intervals that tile [0, slots)) and the extra work items (tile, 1 .. k - 1), in any
-    order."""
+def tile_xcd(t, tiles_x):
+    """The XCD the plan's order gives tile t: 2x1 blocks of tiles round the 8 XCDs along a row of
+    blocks, each row of tiles shifted by three."""
+    t = np.asarray(t, np.int64)
+    return ((t % tiles_x) // 2 + 3 * (t // tiles_x)) % 8
+
+
+def assert_raster_plan(plan_np, ranges_np, P, tiles_x):
+    """The raster plan: per XCD (tile_xcd) a list of its tiles by non-increasing bit length of
+    their pair count (empty ones last); slot 8 p + x holds place p of XCD x's list up to the
+    shortest list's length m, the slots from 8 m on the longer lists' rest; a chunk length L = the
+    smallest power of two >= 128 with P <= C L (C = the plan's chunk limit); for every tile of
+    k = ceil(count / L) >= 2 chunks k checkpoint slots (disjoint intervals that tile [0, slots))
+    and the extra work items (tile, 1 .. k - 1), in any order."""
     from gaussian_splatting_tile_gs_amd import gs as gs_mod
     plan = plan_np.view(np.uint32).astype(np.int64)
     n = ranges_np.shape[0]
@@ -95,8 +103,17 @@ def assert_raster_plan(plan_np, ranges_np, P):
     order = plan[4:4 + n]
     assert np.array_equal(np.sort(order), np.arange(n)), "tile order is not a permutation"
     cnt = ranges_np[:, 1].astype(np.int64) - ranges_np[:, 0]
-    cls = np.where(cnt[order] > 0, np.floor(np.log2(np.maximum(cnt[order], 1))).astype(np.int64) + 1, 0)
-    assert np.all(np.diff(cls) <= 0), "tile order is not heaviest class first"
+    cls_t = np.where(cnt > 0, np.floor(np.log2(np.maximum(cnt, 1))).astype(np.int64) + 1, 0)
+    xcd = tile_xcd(np.arange(n), tiles_x)
+    m = int(np.bincount(xcd, minlength=8).min())
+    head = order[:8 * m].reshape(m, 8)
+    assert np.all(xcd[head] == np.arange(8)[None, :]), "a slot below 8 m is not on its tile's XCD"
+    for x in range(8):
+        lc = cls_t[head[:, x]]
+        assert np.all(np.diff(lc) <= 0), f"XCD {x}'s list is not heaviest class first"
+        rest = order[8 * m:][xcd[order[8 * m:]] == x]
+        if m and rest.size:
+            assert cls_t[rest].max() <= lc[-1], f"XCD {x}'s rest is heavier than its list"
     want_L = 128
     C = gs_mod.plan_max_chunks()
     while want_L * C < P:

@@ -63,7 +63,7 @@ def _pipeline_case(env, scene, cam_dict, pixels=None, backward=True, grad_seed=7
     assert np.array_equal(keys_np, o_keys), "sorted keys differ"
     assert np.array_equal(ids_np, o_ids), "sorted ids differ"
     assert np.array_equal(ranges_np, o_ranges), "tile ranges differ"
-    assert_raster_plan(plan.cpu().numpy(), ranges_np, P)
+    assert_raster_plan(plan.cpu().numpy(), ranges_np, P, (cam_dict["width"] + 15) // 16)
     iso = proj_from_numpy(gs, torch, o_proj)
     st2, P2, keys2, ids2, ranges2, _ = run_gpu_bin(gs, torch, params["n"], iso, cam, P_exp)
     assert st2 == gs.GS_OK and P2 == P_exp

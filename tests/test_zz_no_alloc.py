@@ -36,7 +36,8 @@ def _bin_both(gs, torch, scene, cam_d, capacity):
             gs.gs_bin_and_sort(n, proj, cam, ws, capacity, keys, ids, ranges, P, wait=False, plan=plan)
         torch.cuda.synchronize()
         Pn = int(P.item())
-        out.append((Pn, keys[:Pn].cpu().numpy(), ids[:Pn].cpu().numpy(), ranges.cpu().numpy(), plan.cpu().numpy()))
+        out.append((Pn, keys[:Pn].cpu().numpy(), ids[:Pn].cpu().numpy(), ranges.cpu().numpy(), plan.cpu().numpy(),
+                    (cam_d["width"] + 15) // 16))
     return out
 
 
@@ -46,7 +47,7 @@ def _check_equal(a, b):
         assert np.array_equal(x, y), what
     assert np.array_equal(a[4][:4], b[4][:4]), "plan header"
     for r in (a, b):
-        assert_raster_plan(r[4], r[3].view(np.uint32), r[0])
+        assert_raster_plan(r[4], r[3].view(np.uint32), r[0], r[5])
 
 
 def test_noalloc_matches_workspace_binning_twice(env_gpu):
