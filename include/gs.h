@@ -129,8 +129,10 @@ gs_status gs_project(int32_t n, int32_t sh_degree, const float* d_means, const f
  *   and d_ids.
  * Outputs: d_keys [P] uint64, d_ids [P] uint32, d_tile_ranges [tiles, 2] uint32;
  *   d_raster_plan (optional, gs_raster_plan_words(cam) uint32): how the raster calls schedule the
- *   frame -- the tiles in an order with the ones holding more pairs first (by the bit length of
- *   the count, empty tiles last), a chunk length L (a power of two >= 128 with P <= 4096 L),
+ *   frame -- the tiles in an order that gives each of the GPU's 8 XCDs (workgroup b runs on XCD
+ *   b mod 8) its own list of tiles, 2x1 blocks of neighbouring tiles together, each list with the
+ *   tiles holding more pairs first (by the bit length of the count, empty tiles last), the lists
+ *   interleaved; a chunk length L (a power of two >= 128 with P <= 4096 L),
  *   and for every tile of two or more chunks of L list entries its checkpoint slots and the
  *   backward's extra work items (its chunks after the first); P itself goes to
  *   *d_num_pairs (device int64, optional, written on `stream`) and to *h_num_pairs (host,
