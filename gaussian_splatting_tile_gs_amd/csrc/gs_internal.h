@@ -208,6 +208,7 @@ constexpr float kTransmittanceMin = 1e-4f;
 struct SplatEval {
   float alpha;  // min(0.99, o G), meaningful when !skip
   float G;      // exp(-sigma)
+  float s2;     // log2(e) sigma
   bool skip;    // sigma < 0 or alpha < 1/255
   bool capped;  // o G >= 0.99 (alpha is the constant cap: no gradient to o or sigma)
 };
@@ -216,6 +217,7 @@ __device__ __forceinline__ SplatEval eval_splat(float dx, float dy, float hA, fl
   // s2 = log2(e) * sigma = dx (hA dx + B2 dy) + hC dy^2: five VALU operations
   const float s2 = fmaf(fmaf(hA, dx, B2 * dy), dx, (hC * dy) * dy);
   SplatEval e;
+  e.s2 = s2;
   e.G = __builtin_amdgcn_exp2f(-s2);  // v_exp_f32; results below 2^-126 flush to 0 (alpha < 1/255)
   const float raw = o * e.G;          // never NaN: o in [0, 1], G in [0, inf)
   e.capped = raw >= kAlphaMax;

@@ -38,7 +38,7 @@ constexpr int kBatch = kRasterThreads;         // splats staged per batch
 // start of a 64-splat word of the quadrant masks, where each wave can store its pixels' state
 static_assert(kBatch % kPlanMinChunk == 0 && kPlanMinChunk % 64 == 0, "chunk boundaries must fall on mask words");
 
-// Staged splat record: (mx, my, hA, hC), (B2, o, r, g), b. hA = A/2 log2e, B2 = B log2e,
+// Staged splat record: (mx, my, hA, hC), (B2, o, r, g), (b, z, 0, 0). hA = A/2 log2e, B2 = B log2e,
 // hC = C/2 log2e, so that log2(e) sigma = hA dx^2 + hC dy^2 + B2 dx dy. Staging also returns the
 // 4-bit set of 8x8 quadrants of the tile where the splat can reach alpha >= 1/255 at some pixel
 // centre (its ellipse at that level meets the quadrant); elsewhere it skips at every pixel.
@@ -46,7 +46,10 @@ static_assert(kBatch % kPlanMinChunk == 0 && kPlanMinChunk % 64 == 0, "chunk bou
 // An id >= n (impossible for a well-formed sorted list) stages a record that never contributes.
 //
 // The raw record of one splat is loaded into registers first (in the blend a batch ahead of its
-// staging, so that its loads are in flight while the previous batch is walked).
+// staging, so that its loads are in flight while the previous batch is walked). The three parts
+// sit in three arrays of 16-B entries, so that a walk reads all of splat k's record from one
+// address register (k times 16) with three offsets; the backward with a depth channel keeps the
+// third part in 8-B entries, (b, z), for its LDS budget. z is 0 without a depth channel.
 struct RawSplat {
   float2 m;
   float A, B, C, o, r, g, b, z;
@@ -82,11 +85,14 @@ __device__ __forceinline__ RawSplat load_raw(uint32_t g, uint32_t n, const float
 // quadrant. The slack (0.02 + 4e-6 times the size of the quadratic's terms over the tile) is far
 // above the fp32 rounding of both this bound and the evaluation's s2, so no contributing splat is
 // dropped.
+__device__ __forceinline__ void put_bz(float4& c, float b, float z) { c = make_float4(b, z, 0.0f, 0.0f); }
+__device__ __forceinline__ void put_bz(float2& c, float b, float z) { c = make_float2(b, z); }
+template <typename BZ>
 __device__ __forceinline__ uint32_t stage_raw(const RawSplat& rs, bool valid, float tx0, float ty0, float4& a,
-                                              float4& b, float& c) {
+                                              float4& b, BZ& c) {
   a = make_float4(rs.m.x, rs.m.y, (0.5f * kLog2e) * rs.A, (0.5f * kLog2e) * rs.C);
   b = make_float4(kLog2e * rs.B, rs.o, rs.r, rs.g);
-  c = rs.b;
+  put_bz(c, rs.b, rs.z);
   if (!valid) return 0u;
   const float qa = a.z, qb = b.x, qc = a.w;  // hA, B2, hC
   const float ia = 0.5f / qa, ic = 0.5f / qc;
@@ -110,15 +116,6 @@ __device__ __forceinline__ uint32_t stage_raw(const RawSplat& rs, bool valid, fl
     qm |= hit ? (1u << q) : 0u;
   }
   return qm;
-}
-
-// Loads and stages one splat at once (the backward's staging).
-__device__ __forceinline__ uint32_t load_record(uint32_t g, uint32_t n, const float* __restrict__ means2d,
-                                                const float* __restrict__ conics, const float* __restrict__ opac,
-                                                const float* __restrict__ colors, float tx0, float ty0, float4& a,
-                                                float4& b, float& c) {
-  const RawSplat rs = load_raw<false>(g, n, means2d, conics, opac, colors, nullptr);
-  return stage_raw(rs, g < n, tx0, ty0, a, b, c);
 }
 
 // Sum over the 64 lanes of a wave with DPP; the total lands in lane 63 (other lanes hold partial
@@ -182,6 +179,17 @@ __device__ __forceinline__ void publish_quadrant_masks(uint32_t qm, bool valid, 
     const uint64_t b = __ballot(valid && ((qm >> q) & 1u));
     if (lane == 0) s_qm[q][wave] = b;
   }
+}
+
+// Per-lane flags as wave-uniform lane masks (bit l: lane l), kept in scalar registers, so that
+// testing, combining and setting them costs no vector instruction: lane_in(m) is this lane's bit,
+// lanes_where(c) the mask of the lanes where c holds (of a single compare, it is that compare's
+// own result).
+__device__ __forceinline__ bool lane_in(uint64_t m) { return __builtin_amdgcn_inverse_ballot_w64(m); }
+__device__ __forceinline__ uint64_t lanes_where(bool c) { return __builtin_amdgcn_ballot_w64(c); }
+// The lanes where a splat is skipped (sigma < 0 or alpha < 1/255), one mask per compare.
+__device__ __forceinline__ uint64_t lanes_skipped(const SplatEval& e) {
+  return lanes_where(e.s2 < 0.0f) | lanes_where(e.alpha < kAlphaMin);
 }
 
 // One front-to-back blend step of a pixel (section 5's loop body, predicated). DEPTH: the depth
@@ -274,7 +282,7 @@ __device__ __forceinline__ void walk_entries(uint32_t n, const uint32_t* __restr
                                              const float* __restrict__ conics, const float* __restrict__ opac,
                                              const float* __restrict__ colors, const float* __restrict__ depths,
                                              float tx0, float ty0, const bool& done, float4* s_a, float4* s_b,
-                                             float* s_c, float* s_z, uint64_t (*s_qm)[4], VISIT visit,
+                                             float4* s_c, uint64_t (*s_qm)[4], VISIT visit,
                                              AT_WORD at_word) {
   const int tid = threadIdx.x, wave = tid >> 6;
   const uint32_t b0 = start + rs, e0 = start + re;
@@ -284,7 +292,6 @@ __device__ __forceinline__ void walk_entries(uint32_t n, const uint32_t* __restr
     if (__syncthreads_count(done) == kRasterThreads) break;
     const bool valid = bs + tid < e0;
     const uint32_t qm = stage_raw(raw, valid, tx0, ty0, s_a[tid], s_b[tid], s_c[tid]);
-    if (DEPTH) s_z[tid] = raw.z;
     publish_quadrant_masks(qm, valid, s_qm);
     {
       const uint32_t j2 = bs + 2 * kBatch + tid;
@@ -319,8 +326,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
     const float* __restrict__ l1_target, float* __restrict__ l1_grad, float l1_scale) {
   __shared__ float4 s_a[kBatch];
   __shared__ float4 s_b[kBatch];
-  __shared__ float s_c[kBatch];
-  __shared__ float s_z[DEPTH ? kBatch : 1];
+  __shared__ float4 s_c[kBatch];
   __shared__ uint64_t s_qm[4][4];
   __shared__ uint32_t s_word;
 
@@ -388,7 +394,7 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
         float F = 1.0f;
         bool fdone = !inside;
         walk_entries<false>(n, ids, start, rs - Lf, rs, means2d, conics, opac, colors, depths, tx0, ty0, fdone, s_a,
-                            s_b, s_c, s_z, s_qm, [&](int k0, int k1, bool has1, uint32_t) {
+                            s_b, s_c, s_qm, [&](int k0, int k1, bool has1, uint32_t) {
           const float4 a0 = s_a[k0], b0 = s_b[k0];
           const float4 a1 = s_a[k1], b1 = s_b[k1];
           const SplatEval e0 = eval_splat(a0.x - px, a0.y - py, a0.z, b0.x, a0.w, b0.y);
@@ -455,11 +461,13 @@ __global__ __launch_bounds__(kRasterThreads) void k_blend(
         if (next_b >= re) next_b = 0xFFFFFFFFu;
       };
       walk_entries<DEPTH>(n, ids, start, rs, re, means2d, conics, opac, colors, depths, tx0, ty0, done, s_a, s_b,
-                          s_c, s_z, s_qm, [&](int k0, int k1, bool has1, uint32_t list1) {
+                          s_c, s_qm, [&](int k0, int k1, bool has1, uint32_t list1) {
         const float4 a0 = s_a[k0], b0 = s_b[k0];
         const float4 a1 = s_a[k1], b1 = s_b[k1];
-        const float c0 = s_c[k0], c1 = s_c[k1];
-        const float z0 = DEPTH ? s_z[k0] : 0.0f, z1 = DEPTH ? s_z[k1] : 0.0f;
+        const float2 cz0 = *reinterpret_cast<const float2*>(&s_c[k0]);
+        const float2 cz1 = *reinterpret_cast<const float2*>(&s_c[k1]);
+        const float c0 = cz0.x, c1 = cz1.x;
+        const float z0 = DEPTH ? cz0.y : 0.0f, z1 = DEPTH ? cz1.y : 0.0f;
         const SplatEval e0 = eval_splat(a0.x - px, a0.y - py, a0.z, b0.x, a0.w, b0.y);
         const SplatEval e1 = eval_splat(a1.x - px, a1.y - py, a1.z, b1.x, a1.w, b1.y);
         if (COUNT) n_eval += (done ? 0u : 1u) + ((done || !has1) ? 0u : 1u);
@@ -673,14 +681,13 @@ __device__ __forceinline__ void reduce18_to_lds(const float* a, const float* b, 
   y = y + dpp_f<0x114>(y);                  // row_shr:4
   y = y + dpp_f<0x118>(y);                  // row_shr:8: lane 15 of each row holds the row
   y = y + dpp_f<0x142>(y);                  // row_bcast:15: lane 31 rows 0 + 1, lane 63 rows 2 + 3
+  float* acc8 = ((lane & 32) ? accB : accA) + 8;  // lanes 31 and 63 store, one instruction for both
   if (STORE) {
     if ((lane & 3) == 0) acc[term] = x;
-    if (lane == 31) accA[8] = y;
-    if (lane == 63) accB[8] = y;
+    if ((lane & 31) == 31) *acc8 = y;
   } else {
     if ((lane & 3) == 0) unsafeAtomicAdd(acc + term, x);
-    if (lane == 31) unsafeAtomicAdd(accA + 8, y);
-    if (lane == 63) unsafeAtomicAdd(accB + 8, y);
+    if ((lane & 31) == 31) unsafeAtomicAdd(acc8, y);
   }
 }
 
@@ -732,12 +739,12 @@ __global__ __launch_bounds__(kRasterThreads) __attribute__((amdgpu_waves_per_eu(
   // together); without DEPTH the tenth component is not written (it stays 0)
   constexpr bool REC = MODE != kBwdAtomic, DET = MODE == kBwdDeterministic;
   constexpr int NT = DEPTH ? 10 : 9;  // terms summed per splat
+  using BZ = typename std::conditional<DEPTH, float2, float4>::type;
   __shared__ float4 s_a[kBatch];
   __shared__ float4 s_b[kBatch];
-  __shared__ float s_c[kBatch];
-  __shared__ float s_z[DEPTH ? kBatch : 1];
+  __shared__ BZ s_c[kBatch];
   __shared__ uint32_t s_id[kBatch];
-  __shared__ float s_acc[kBatch * NT];
+  __shared__ float s_acc[(kBatch + (DEPTH ? 0 : 4)) * NT];  // the splats' sums (then a spare slot per wave)
   __shared__ uint64_t s_qm[4][4];
   __shared__ uint32_t s_max;
 
@@ -792,7 +799,6 @@ __global__ __launch_bounds__(kRasterThreads) __attribute__((amdgpu_waves_per_eu(
       s_id[tid] = g;
       const RawSplat rs = load_raw<DEPTH>(g, n, means2d, conics, opac, colors, depths);
       qm = stage_raw(rs, g < n, tx0, ty0, s_a[tid], s_b[tid], s_c[tid]);
-      if (DEPTH) s_z[tid] = rs.z;
       if (REC && g < n) rslot = pair_slot(g, means2d, radii, pair_base, tx, ty, cam, rs.A, rs.B, rs.C, rs.o);
     }
     if (!DET)
@@ -898,29 +904,37 @@ __global__ __launch_bounds__(kRasterThreads) __attribute__((amdgpu_waves_per_eu(
         m &= ~(1ull << bit1);  // no-op when !has1 (m is already 0)
         const int k0 = __builtin_amdgcn_readfirstlane(w * 64 + bit0);
         const int k1 = __builtin_amdgcn_readfirstlane(w * 64 + bit1);
-        const bool act0 = bstart + (uint32_t)k0 < nc;
-        const bool act1 = has1 && (bstart + (uint32_t)k1 < nc);
-        if (!__any(act0 || act1)) continue;
+        // the lanes that have reached each splat (from their last contributor back)
+        const uint64_t act0_m = lanes_where(bstart + (uint32_t)k0 < nc);
+        const uint64_t act1_m = has1 ? lanes_where(bstart + (uint32_t)k1 < nc) : 0ull;
+        if ((act0_m | act1_m) == 0ull) continue;
+        const bool act0 = lane_in(act0_m), act1 = lane_in(act1_m);
         const float4 a0 = s_a[k0], b0 = s_b[k0];
         const float4 a1 = s_a[k1], b1 = s_b[k1];
-        const float cb0 = s_c[k0], cb1 = s_c[k1];
-        const float z0 = DEPTH ? s_z[k0] : 0.0f, z1 = DEPTH ? s_z[k1] : 0.0f;
+        const float2 cz0 = *reinterpret_cast<const float2*>(&s_c[k0]);
+        const float2 cz1 = *reinterpret_cast<const float2*>(&s_c[k1]);
+        const float cb0 = cz0.x, cb1 = cz1.x;
+        const float z0 = DEPTH ? cz0.y : 0.0f, z1 = DEPTH ? cz1.y : 0.0f;
         const float dx0 = a0.x - px, dy0 = a0.y - py, dx1 = a1.x - px, dy1 = a1.y - py;
         const SplatEval e0 = eval_splat(dx0, dy0, a0.z, b0.x, a0.w, b0.y);
         const SplatEval e1 = eval_splat(dx1, dy1, a1.z, b1.x, a1.w, b1.y);
         if (COUNT) n_eval += (act0 ? 1u : 0u) + (act1 ? 1u : 0u);
-        const bool c0 = act0 && !e0.skip, c1 = act1 && !e1.skip;
+        const uint64_t c0_m = act0_m & ~lanes_skipped(e0), c1_m = act1_m & ~lanes_skipped(e1);
+        const bool c0 = lane_in(c0_m), c1 = lane_in(c1_m);
         float v0[NT], v1[NT];
         splat_grad<DEPTH>(c0, e0, dx0, dy0, b0.z, b0.w, cb0, z0, gr, gg, gb, gd, T, gS, v0);
         splat_grad<DEPTH>(c1, e1, dx1, dy1, b1.z, b1.w, cb1, z1, gr, gg, gb, gd, T, gS, v1);
         float* acc0 = DET ? part + (k0 - w * 64) * NT : s_acc + k0 * NT;
-        float* acc1 = DET ? part + (k1 - w * 64) * NT : s_acc + k1 * NT;
-        if (!DEPTH && has1) {
-          // both splats in one reduction (a splat no lane reaches adds zeros to its own slot)
-          if (__any(c0 || c1)) reduce18_to_lds<DET>(v0, v1, acc0, acc1, lane);
+        float* acc1 = !has1 ? (DEPTH ? acc0 : s_acc + (kBatch + wave) * NT)  // (DEPTH: never used)
+                            : DET ? part + (k1 - w * 64) * NT : s_acc + k1 * NT;
+        if (!DEPTH) {
+          // both splats in one reduction: a splat no lane reaches adds zeros to its own slot, and
+          // the missing partner of a lone splat (its terms all zero) goes to the wave's spare slot,
+          // which is never read; one path, so the compiler keeps no copies of the terms
+          if ((c0_m | c1_m) != 0ull) reduce18_to_lds<DET>(v0, v1, acc0, acc1, lane);
         } else {
-          if (__any(c0)) reduce_terms<DET, DEPTH>(v0, acc0, lane);
-          if (__any(c1)) reduce_terms<DET, DEPTH>(v1, acc1, lane);
+          if (c0_m != 0ull) reduce_terms<DET, DEPTH>(v0, acc0, lane);
+          if (c1_m != 0ull) reduce_terms<DET, DEPTH>(v1, acc1, lane);
         }
       }
       if (DET) {
