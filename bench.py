@@ -41,12 +41,13 @@ HBM_PEAK_GBS = 8000.0
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 
 # VALU lane-operations per (pixel, splat) evaluation that the roofline counts: the blend's is
-# its loop body in the gfx950 ISA of the built library (54 VALU ops per two splats); the
-# backward's is the algorithmic count of a (pixel, entry) walked back (evaluation, T recovery,
-# dL/dalpha and the nine gradient pieces: 60), with the loop body's ISA count beside it
-# (133 per two splats, the wave reduction included).
+# the algorithmic count of a front-to-back step (evaluation, alpha, transmittance test and
+# update, three colour sums: 27); the backward's that of a (pixel, entry) walked back
+# (evaluation, T recovery, dL/dalpha and the nine gradient pieces: 60). Beside them, the loop
+# bodies' counts in the gfx950 ISA of the built library (52 VALU ops per two splats in the
+# blend; 126 in the backward, the wave reduction included).
 VALU_PER_EVAL = {"blend": 27.0, "rbwd": 60.0}
-VALU_PER_EVAL_ISA = {"blend": 27.0, "rbwd": 66.5}
+VALU_PER_EVAL_ISA = {"blend": 26.0, "rbwd": 63.0}
 # the binning kernels, and among them those that move keys (the radix passes and the emission
 # fused with the first pair pass)
 BIN_KERNELS = ("small_local", "small_merge", "bin_prep", "hist_reduce", "depth_sort_pass", "scan", "emit_sort",
