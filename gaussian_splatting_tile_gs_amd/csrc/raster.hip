@@ -715,14 +715,15 @@ __device__ __forceinline__ void reduce_terms(const float* v, float* acc, int lan
 // front, like the sums of the whole-tile walk: a sum of the terms, never a difference).
 // Where the 2D gradient of a (tile, splat) pair goes (MODE):
 //   kBwdAtomic  added to g2d [9, n] with global fp32 atomics;
-//   kBwdRecords written to its own slot of rec [rec_cap, 10] (pair_slot), summed per Gaussian later;
-//   kBwdDeterministic  as kBwdRecords, and the four waves' sums of a splat are kept apart in LDS
-//               (per 64-splat group, with a barrier after each group) and added in wave order,
-//               so every floating-point sum has a fixed order: bitwise-reproducible gradients.
+//   kBwdDeterministic  written to its own slot of rec [rec_cap, 10] (pair_slot), summed per
+//               Gaussian later in a fixed order; the four waves' sums of a splat are kept apart in
+//               LDS (per 64-splat group, with a barrier after each group) and added in wave order,
+//               so every floating-point sum has a fixed order: bitwise-reproducible gradients
+//               (LDS atomics across the waves instead of the barriers measured slower).
 // With records, the slots of the pairs a chunk does not stage (behind every pixel's last
 // contributor) keep the zeros the records were cleared to before the launch.
 // ---------------------------------------------------------------------------------------------
-constexpr int kBwdAtomic = 0, kBwdRecords = 1, kBwdDeterministic = 2;
+constexpr int kBwdAtomic = 0, kBwdDeterministic = 2;
 constexpr int kG2d = 10;  // components of a 2D gradient: mean2d (2), conic (3), opacity, rgb (3), depth
 // DEPTH: the backward of the depth channel too (dL/ddepth given; tenth component dL/dz).
 template <bool COUNT, int MODE, bool DEPTH>
@@ -1541,8 +1542,7 @@ gs_status rasterize_bwd(const char* name, int mode, int32_t n, int32_t sh_degree
     TimedScope ts("rbwd", s);
     auto pick = [&](auto count_tag, auto depth_tag) {
       constexpr bool C = decltype(count_tag)::value, D = decltype(depth_tag)::value;
-      return mode == kBwdAtomic ? k_rbwd<C, kBwdAtomic, D>
-                                : mode == kBwdRecords ? k_rbwd<C, kBwdRecords, D> : k_rbwd<C, kBwdDeterministic, D>;
+      return mode == kBwdAtomic ? k_rbwd<C, kBwdAtomic, D> : k_rbwd<C, kBwdDeterministic, D>;
     };
     const bool dep = d_dL_ddepth != nullptr;
     auto kern = d_eval_count ? (dep ? pick(std::true_type{}, std::true_type{}) : pick(std::true_type{}, std::false_type{}))
