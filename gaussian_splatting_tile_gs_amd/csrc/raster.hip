@@ -1222,19 +1222,13 @@ __global__ void k_fill_zero(float* __restrict__ p, size_t count) {
 
 // Clears the records of the P = *total pairs (none when P exceeds the capacity: nothing is then
 // read), four floats per store.
-__global__ void k_clear_records(float4* __restrict__ rec, const unsigned long long* __restrict__ total,
-                                uint32_t rec_cap) {
-  const unsigned long long P = *total;
-  if (P > rec_cap) return;
-  const size_t count = ((size_t)P * kG2d + 3) / 4;  // the record array is 256-byte aligned and padded
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < count; i += (size_t)gridDim.x * blockDim.x)
-    rec[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-}
 
 // ---------------------------------------------------------------------------------------------
 // Per-pair records: base[g] = sum of tiles_touched over ids < g (exclusive prefix in id order),
 // total = the sum over all ids (= P). Two launches, reduce then scan, over blocks of 4096 ids;
-// integer sums, so the result does not depend on the order of the additions.
+// integer sums, so the result does not depend on the order of the additions. The reduce launch's
+// workgroups past the blocks clear the whole record array meanwhile (every record starts at zero:
+// the pairs no pixel reaches are never staged), which needs no P and so no launch of its own.
 // ---------------------------------------------------------------------------------------------
 constexpr int kBaseThreads = 1024, kBaseItems = 4, kBaseTile = kBaseThreads * kBaseItems;
 
@@ -1250,8 +1244,15 @@ __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v
 }
 
 __global__ __launch_bounds__(kBaseThreads) void k_base_sums(int32_t n, const uint32_t* __restrict__ tiles_touched,
-                                                            unsigned long long* __restrict__ bsum) {
+                                                            unsigned long long* __restrict__ bsum, uint32_t nb,
+                                                            float4* __restrict__ rec, size_t rec4) {
   __shared__ unsigned long long s_w[kBaseThreads / 64];
+  if (blockIdx.x >= nb) {  // a clearing workgroup (workgroup-uniform)
+    const size_t stride = (size_t)(gridDim.x - nb) * kBaseThreads;
+    for (size_t i = (size_t)(blockIdx.x - nb) * kBaseThreads + threadIdx.x; i < rec4; i += stride)
+      rec[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    return;
+  }
   unsigned long long v = 0;
 #pragma unroll
   for (int i = 0; i < kBaseItems; ++i) {
@@ -1527,16 +1528,15 @@ gs_status rasterize_bwd(const char* name, int mode, int32_t n, int32_t sh_degree
     rec = (float*)(ws + RL.rec);
     unsigned long long* bsum = (unsigned long long*)(ws + RL.bsum);
     const unsigned nb = (unsigned)(((size_t)n + kBaseTile - 1) / kBaseTile);
-    hipLaunchKernelGGL(k_base_sums, dim3(nb), dim3(kBaseThreads), 0, s, n, proj->d_tiles_touched, bsum);
+    // the whole record array is cleared by extra workgroups of the reduce launch, about 4 float4s
+    // per thread (at most 1024 workgroups): small frames leave most of the GPU to concurrent
+    // iterations, large ones still fill it
+    const size_t rec4 = ((size_t)pair_capacity * kG2d + 3) / 4;
+    const size_t want = (rec4 + 4 * kBaseThreads - 1) / (4 * kBaseThreads);
+    const unsigned nclear = (unsigned)(want > 1024 ? 1024 : want);
+    hipLaunchKernelGGL(k_base_sums, dim3(nb + nclear), dim3(kBaseThreads), 0, s, n, proj->d_tiles_touched, bsum, nb,
+                       (float4*)rec, rec4);
     hipLaunchKernelGGL(k_base_scan, dim3(nb), dim3(kBaseThreads), 0, s, n, proj->d_tiles_touched, bsum, base, total);
-    // every record starts at zero: the pairs no pixel reaches are never staged. Each thread
-    // clears about 4 float4s (at most 4096 workgroups): small frames leave most of the GPU to
-    // concurrent iterations, large ones still fill it
-    const size_t count4 = ((size_t)pair_capacity * kG2d + 3) / 4;
-    const size_t want = (count4 + 1023) / 1024;
-    const unsigned blocks = (unsigned)(want < 1 ? 1 : (want > 4096 ? 4096 : want));
-    if (count4)
-      hipLaunchKernelGGL(k_clear_records, dim3(blocks), dim3(256), 0, s, (float4*)rec, total, (uint32_t)pair_capacity);
   }
   {
     TimedScope ts("rbwd", s);
