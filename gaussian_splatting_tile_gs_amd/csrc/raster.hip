@@ -964,6 +964,64 @@ __global__ __launch_bounds__(kRasterThreads) __attribute__((amdgpu_waves_per_eu(
   if (COUNT) count_evals(n_eval, eval_count);
 }
 
+// dL/d(2D parameters) of Gaussian g from its records, in an order fixed by its pair count. A
+// wave takes 64 consecutive Gaussians, one per lane (every lane of the wave calls this; g may be
+// past n): a lane whose Gaussian has at most kSegLane pairs adds its records in slot order (a
+// record is 40 B, read as five float2). The Gaussians of more pairs are then taken one at a time
+// by the whole wave: lane l adds records l, l + 64, ... in order and a fixed DPP tree adds the
+// lanes. When the pairs did not fit the records (fits false: the pair sort then left every tile
+// range empty) every gradient is zero.
+constexpr uint32_t kSegLane = 16;
+__device__ __forceinline__ void seg_sum(int32_t n, int64_t g, int lane, const uint32_t* __restrict__ tiles_touched,
+                                        const uint32_t* __restrict__ base, bool fits, const float* __restrict__ rec,
+                                        float* acc) {
+  const uint32_t cnt = (g < n && fits) ? tiles_touched[g] : 0u;
+  const uint32_t b = g < n ? base[g] : 0u;
+#pragma unroll
+  for (int c = 0; c < kG2d; ++c) acc[c] = 0.0f;
+  if (cnt <= kSegLane) {
+    // four records in flight at a time, added in slot order (a missing one adds nothing)
+    for (uint32_t j = 0; j < cnt; j += 4) {
+      float2 v[4][kG2d / 2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float2* r = reinterpret_cast<const float2*>(rec + ((size_t)b + j + (uint32_t)i) * kG2d);
+#pragma unroll
+        for (int c = 0; c < kG2d / 2; ++c) v[i][c] = j + (uint32_t)i < cnt ? r[c] : make_float2(0.0f, 0.0f);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (j + (uint32_t)i < cnt) {
+#pragma unroll
+          for (int c = 0; c < kG2d / 2; ++c) {
+            acc[2 * c] += v[i][c].x;
+            acc[2 * c + 1] += v[i][c].y;
+          }
+        }
+      }
+    }
+  }
+  uint64_t big = __ballot(cnt > kSegLane);
+  while (big) {
+    const int src = __builtin_ctzll(big);
+    big &= big - 1;
+    const uint32_t cb = __builtin_amdgcn_readlane(cnt, src), bb = __builtin_amdgcn_readlane(b, src);
+    float w[kG2d];
+#pragma unroll
+    for (int c = 0; c < kG2d; ++c) w[c] = 0.0f;
+    for (uint32_t j = lane; j < cb; j += 64) {
+#pragma unroll
+      for (int c = 0; c < kG2d; ++c) w[c] += rec[((size_t)bb + j) * kG2d + c];
+    }
+#pragma unroll
+    for (int c = 0; c < kG2d; ++c) {
+      const float t = wave_sum_lane63(w[c]);
+      const float tb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 63));
+      if (lane == src) acc[c] = tb;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // k-pbwd: chain rule from the 2D gradients (mean2d, conic, opacity, colour) to the raw
 // parameters (sections 1-4 of the PyTorch lesson, differentiated). One thread per Gaussian.
@@ -1008,23 +1066,36 @@ __device__ __forceinline__ void sh_basis_grad_f64(int degree, double x, double y
   dB[15][0] = 3.0 * s358 * (x * x - y * y); dB[15][1] = -6.0 * s358 * x * y;
 }
 
-template <int DEG>
+// SEG (the deterministic backward): the 2D gradient is summed from the per-pair records here
+// (seg_sum: a wave per 64 consecutive Gaussians, the same lanes as the chain rule's), else read
+// from g2d [10, n].
+template <int DEG, bool SEG>
 __global__ __launch_bounds__(256) void k_pbwd(
     int32_t n, const float* __restrict__ means, const float* __restrict__ log_scales, const float* __restrict__ quats,
     const float* __restrict__ logits, const float* __restrict__ sh, DevCamera cam,
-    const uint32_t* __restrict__ tiles_touched, const float* __restrict__ g2d, float* __restrict__ d_means,
-    float* __restrict__ d_log_scales, float* __restrict__ d_quats, float* __restrict__ d_logits,
-    float* __restrict__ d_sh, float* __restrict__ d_means2d) {
+    const uint32_t* __restrict__ tiles_touched, const float* __restrict__ g2d, const uint32_t* __restrict__ base,
+    const unsigned long long* __restrict__ total, const float* __restrict__ rec, uint32_t rec_cap,
+    float* __restrict__ d_means, float* __restrict__ d_log_scales, float* __restrict__ d_quats,
+    float* __restrict__ d_logits, float* __restrict__ d_sh, float* __restrict__ d_means2d) {
   constexpr int K = (DEG + 1) * (DEG + 1);
   const int g = blockIdx.x * 256 + threadIdx.x;
-  if (g >= n) return;
+  double G9[kG2d];  // the 2D gradient; G9[9] is dL/d(camera z) of the depth channel
+  if (SEG) {
+    if (blockIdx.x * 256 + (threadIdx.x & ~63) >= n) return;  // wave-uniform: the wave's first Gaussian
+    float acc[kG2d];
+    seg_sum(n, g, threadIdx.x & 63, tiles_touched, base, *total <= (unsigned long long)rec_cap, rec, acc);
+    if (g >= n) return;
+#pragma unroll
+    for (int c = 0; c < kG2d; ++c) G9[c] = (double)acc[c];
+  } else {
+    if (g >= n) return;
+#pragma unroll
+    for (int c = 0; c < kG2d; ++c) G9[c] = (double)g2d[(size_t)c * n + g];  // [10, n]
+  }
   double gm[3] = {0, 0, 0}, gl[3] = {0, 0, 0}, gq4[4] = {0, 0, 0, 0}, glogit = 0.0;
   double gsh[K * 3];
 #pragma unroll
   for (int i = 0; i < K * 3; ++i) gsh[i] = 0.0;
-  double G9[kG2d];  // the 2D gradient; G9[9] is dL/d(camera z) of the depth channel
-#pragma unroll
-  for (int c = 0; c < kG2d; ++c) G9[c] = (double)g2d[(size_t)c * n + g];  // [10, n]
 
   const bool drawn = tiles_touched[g] > 0;
   if (drawn) {
@@ -1301,75 +1372,6 @@ __global__ __launch_bounds__(kBaseThreads) void k_base_scan(int32_t n, const uin
   if (blockIdx.x == gridDim.x - 1 && threadIdx.x == kBaseThreads - 1) *total = run;
 }
 
-// dL/d(2D parameters) of every Gaussian from its records, in an order fixed by its pair count.
-// A wave takes 64 consecutive Gaussians, one per lane: a lane whose Gaussian has at most
-// kSegLane pairs adds its records in slot order (a record is 40 B, read as five float2). The
-// Gaussians of more pairs are then taken one at a time by the whole wave: lane l adds records
-// l, l + 64, ... in order and a fixed DPP tree adds the lanes. When the pairs did not fit the
-// records (total > rec_cap; the pair sort then left every tile range empty) every gradient is
-// zero.
-constexpr uint32_t kSegLane = 16;
-__global__ __launch_bounds__(256) void k_seg_reduce(int32_t n, const uint32_t* __restrict__ tiles_touched,
-                                                    const uint32_t* __restrict__ base,
-                                                    const unsigned long long* __restrict__ total,
-                                                    const float* __restrict__ rec, uint32_t rec_cap,
-                                                    float* __restrict__ g2d) {
-  const int lane = threadIdx.x & 63;
-  const int64_t g0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;
-  if (g0 >= n) return;  // wave-uniform
-  const int64_t g = g0 + lane;
-  const bool fits = *total <= (unsigned long long)rec_cap;
-  const uint32_t cnt = (g < n && fits) ? tiles_touched[g] : 0u;
-  const uint32_t b = g < n ? base[g] : 0u;
-  float acc[kG2d];
-#pragma unroll
-  for (int c = 0; c < kG2d; ++c) acc[c] = 0.0f;
-  if (cnt <= kSegLane) {
-    // four records in flight at a time, added in slot order (a missing one adds nothing)
-    for (uint32_t j = 0; j < cnt; j += 4) {
-      float2 v[4][kG2d / 2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float2* r = reinterpret_cast<const float2*>(rec + ((size_t)b + j + (uint32_t)i) * kG2d);
-#pragma unroll
-        for (int c = 0; c < kG2d / 2; ++c) v[i][c] = j + (uint32_t)i < cnt ? r[c] : make_float2(0.0f, 0.0f);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (j + (uint32_t)i < cnt) {
-#pragma unroll
-          for (int c = 0; c < kG2d / 2; ++c) {
-            acc[2 * c] += v[i][c].x;
-            acc[2 * c + 1] += v[i][c].y;
-          }
-        }
-      }
-    }
-  }
-  uint64_t big = __ballot(cnt > kSegLane);
-  while (big) {
-    const int src = __builtin_ctzll(big);
-    big &= big - 1;
-    const uint32_t cb = __builtin_amdgcn_readlane(cnt, src), bb = __builtin_amdgcn_readlane(b, src);
-    float w[kG2d];
-#pragma unroll
-    for (int c = 0; c < kG2d; ++c) w[c] = 0.0f;
-    for (uint32_t j = lane; j < cb; j += 64) {
-#pragma unroll
-      for (int c = 0; c < kG2d; ++c) w[c] += rec[((size_t)bb + j) * kG2d + c];
-    }
-#pragma unroll
-    for (int c = 0; c < kG2d; ++c) {
-      const float t = wave_sum_lane63(w[c]);
-      const float tb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 63));
-      if (lane == src) acc[c] = tb;
-    }
-  }
-  if (g < n) {
-#pragma unroll
-    for (int c = 0; c < kG2d; ++c) g2d[(size_t)c * n + g] = acc[c];
-  }
-}
 
 }  // namespace
 }  // namespace gs
@@ -1558,17 +1560,15 @@ gs_status rasterize_bwd(const char* name, int mode, int32_t n, int32_t sh_degree
                        proj->d_colors, proj->d_depths, proj->d_radii, dc, d_final_T, d_n_contrib, d_dL_dimage,
                        d_dL_ddepth, g2d, base, rec, (uint32_t)pair_capacity, (unsigned long long*)d_eval_count);
   }
-  if (mode != kBwdAtomic) {
-    TimedScope ts("bwd_reduce", s);
-    hipLaunchKernelGGL(k_seg_reduce, dim3((unsigned)(((size_t)n + 255) / 256)), dim3(256), 0, s, n,
-                       proj->d_tiles_touched, base, total, rec, (uint32_t)pair_capacity, g2d);
-  }
   {
+    // with records (the deterministic backward) the chain rule's launch sums them first
     TimedScope ts("pbwd", s);
     const dim3 grid((n + 255) / 256), block(256);
-#define GS_LAUNCH_PBWD(D)                                                                                       \
-  hipLaunchKernelGGL(k_pbwd<D>, grid, block, 0, s, n, d_means, d_log_scales, d_quats, d_opacity_logits, d_sh, dc, \
-                     proj->d_tiles_touched, g2d, d_grad_means, d_grad_log_scales, d_grad_quats,                 \
+    const bool seg = mode != kBwdAtomic;
+#define GS_LAUNCH_PBWD(D)                                                                                        \
+  hipLaunchKernelGGL((seg ? k_pbwd<D, true> : k_pbwd<D, false>), grid, block, 0, s, n, d_means, d_log_scales,     \
+                     d_quats, d_opacity_logits, d_sh, dc, proj->d_tiles_touched, g2d, base, total, rec,          \
+                     (uint32_t)pair_capacity, d_grad_means, d_grad_log_scales, d_grad_quats,                     \
                      d_grad_opacity_logits, d_grad_sh, d_grad_means2d)
     switch (sh_degree) {
       case 0: GS_LAUNCH_PBWD(0); break;
