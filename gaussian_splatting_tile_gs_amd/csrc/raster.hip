@@ -721,7 +721,7 @@ __device__ __forceinline__ void reduce_terms(const float* v, float* acc, int lan
 //               so every floating-point sum has a fixed order: bitwise-reproducible gradients
 //               (LDS atomics across the waves instead of the barriers measured slower).
 // With records, the slots of the pairs a chunk does not stage (behind every pixel's last
-// contributor) keep the zeros the records were cleared to before the launch.
+// contributor) get zeros, so that all P records are written by the launch.
 // ---------------------------------------------------------------------------------------------
 constexpr int kBwdAtomic = 0, kBwdDeterministic = 2;
 constexpr int kG2d = 10;  // components of a 2D gradient: mean2d (2), conic (3), opacity, rgb (3), depth
@@ -825,9 +825,9 @@ __global__ __launch_bounds__(kRasterThreads) __attribute__((amdgpu_waves_per_eu(
     gv[8] = P[8];
     gv[9] = DEPTH ? P[9] : 0.0f;
     if (REC) {
-      if (rslot < rec_cap) {
+      if (rslot < rec_cap) {  // every component (without DEPTH the tenth is 0)
 #pragma unroll
-        for (int c = 0; c < NT; ++c) rec[(size_t)rslot * kG2d + c] = gv[c];
+        for (int c = 0; c < kG2d; ++c) rec[(size_t)rslot * kG2d + c] = gv[c];
       }
     } else {
       // one plane per component: the atomics of a lane go to different cache lines
@@ -878,6 +878,22 @@ __global__ __launch_bounds__(kRasterThreads) __attribute__((amdgpu_waves_per_eu(
   __syncthreads();
   const uint32_t max_nc = s_max < hi ? s_max : hi;
   uint32_t n_eval = 0;
+  if (REC && !single) {
+    // the pairs behind every pixel's last contributor are never staged: their records get
+    // zeros here, so that every record of the P pairs is written once (a single batch stages
+    // its whole chunk, and the walk's batches cover [lo, max_nc))
+    for (uint32_t e = (max_nc > lo ? max_nc : lo) + (uint32_t)tid; e < chunk_end; e += kRasterThreads) {
+      const uint32_t g = ids[start + e];
+      if (g >= n) continue;
+      const bool tt = cam.tight_tiles != 0;
+      const uint32_t zs = pair_slot(g, means2d, radii, pair_base, tx, ty, cam, tt ? conics[3 * g] : 1.0f,
+                                    tt ? conics[3 * g + 1] : 0.0f, tt ? conics[3 * g + 2] : 1.0f, tt ? opac[g] : 0.0f);
+      if (zs < rec_cap) {
+#pragma unroll
+        for (int c = 0; c < kG2d; ++c) rec[(size_t)zs * kG2d + c] = 0.0f;
+      }
+    }
+  }
 
   // a staged single batch covers [lo, chunk_end), which holds [lo, max_nc)
   for (uint32_t bend = single ? chunk_end : max_nc; bend > lo;) {
@@ -1297,9 +1313,8 @@ __global__ void k_fill_zero(float* __restrict__ p, size_t count) {
 // ---------------------------------------------------------------------------------------------
 // Per-pair records: base[g] = sum of tiles_touched over ids < g (exclusive prefix in id order),
 // total = the sum over all ids (= P). Two launches, reduce then scan, over blocks of 4096 ids;
-// integer sums, so the result does not depend on the order of the additions. The reduce launch's
-// workgroups past the blocks clear the whole record array meanwhile (every record starts at zero:
-// the pairs no pixel reaches are never staged), which needs no P and so no launch of its own.
+// integer sums, so the result does not depend on the order of the additions. The records need
+// no clearing: the backward writes every pair's record, zeros for the pairs it does not stage.
 // ---------------------------------------------------------------------------------------------
 constexpr int kBaseThreads = 1024, kBaseItems = 4, kBaseTile = kBaseThreads * kBaseItems;
 
@@ -1315,15 +1330,8 @@ __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v
 }
 
 __global__ __launch_bounds__(kBaseThreads) void k_base_sums(int32_t n, const uint32_t* __restrict__ tiles_touched,
-                                                            unsigned long long* __restrict__ bsum, uint32_t nb,
-                                                            float4* __restrict__ rec, size_t rec4) {
+                                                            unsigned long long* __restrict__ bsum) {
   __shared__ unsigned long long s_w[kBaseThreads / 64];
-  if (blockIdx.x >= nb) {  // a clearing workgroup (workgroup-uniform)
-    const size_t stride = (size_t)(gridDim.x - nb) * kBaseThreads;
-    for (size_t i = (size_t)(blockIdx.x - nb) * kBaseThreads + threadIdx.x; i < rec4; i += stride)
-      rec[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    return;
-  }
   unsigned long long v = 0;
 #pragma unroll
   for (int i = 0; i < kBaseItems; ++i) {
@@ -1476,7 +1484,7 @@ BwdRecLayout bwd_rec_layout(int32_t n, int64_t cap) {
   L.total = align_up(L.base + (size_t)n * 4, 256);
   L.bsum = align_up(L.total + 8, 256);
   L.rec = align_up(L.bsum + nb * 8, 256);
-  L.bytes = align_up(L.rec + (size_t)cap * kG2d * 4 + 16, 256);  // + one float4 of clearing slack
+  L.bytes = align_up(L.rec + (size_t)cap * kG2d * 4 + 16, 256);
   return L;
 }
 
@@ -1530,14 +1538,7 @@ gs_status rasterize_bwd(const char* name, int mode, int32_t n, int32_t sh_degree
     rec = (float*)(ws + RL.rec);
     unsigned long long* bsum = (unsigned long long*)(ws + RL.bsum);
     const unsigned nb = (unsigned)(((size_t)n + kBaseTile - 1) / kBaseTile);
-    // the whole record array is cleared by extra workgroups of the reduce launch, about 4 float4s
-    // per thread (at most 1024 workgroups): small frames leave most of the GPU to concurrent
-    // iterations, large ones still fill it
-    const size_t rec4 = ((size_t)pair_capacity * kG2d + 3) / 4;
-    const size_t want = (rec4 + 4 * kBaseThreads - 1) / (4 * kBaseThreads);
-    const unsigned nclear = (unsigned)(want > 1024 ? 1024 : want);
-    hipLaunchKernelGGL(k_base_sums, dim3(nb + nclear), dim3(kBaseThreads), 0, s, n, proj->d_tiles_touched, bsum, nb,
-                       (float4*)rec, rec4);
+    hipLaunchKernelGGL(k_base_sums, dim3(nb), dim3(kBaseThreads), 0, s, n, proj->d_tiles_touched, bsum);
     hipLaunchKernelGGL(k_base_scan, dim3(nb), dim3(kBaseThreads), 0, s, n, proj->d_tiles_touched, bsum, base, total);
   }
   {
