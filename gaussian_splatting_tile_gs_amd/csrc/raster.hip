@@ -1313,10 +1313,13 @@ __global__ void k_fill_zero(float* __restrict__ p, size_t count) {
 // ---------------------------------------------------------------------------------------------
 // Per-pair records: base[g] = sum of tiles_touched over ids < g (exclusive prefix in id order),
 // total = the sum over all ids (= P). Two launches, reduce then scan, over blocks of 4096 ids;
-// integer sums, so the result does not depend on the order of the additions. The records need
-// no clearing: the backward writes every pair's record, zeros for the pairs it does not stage.
+// integer sums, so the result does not depend on the order of the additions. Up to kBaseOne
+// blocks the scan launch alone does it, each block summing the counts of all ids before it (at
+// most 15 x 4096, eight loads in flight per thread). The records need no clearing: the backward
+// writes every pair's record, zeros for the pairs it does not stage.
 // ---------------------------------------------------------------------------------------------
 constexpr int kBaseThreads = 1024, kBaseItems = 4, kBaseTile = kBaseThreads * kBaseItems;
+constexpr unsigned kBaseOne = 16;
 
 __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v, unsigned long long* s_w) {
   for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
@@ -1342,15 +1345,27 @@ __global__ __launch_bounds__(kBaseThreads) void k_base_sums(int32_t n, const uin
   if (threadIdx.x == 0) bsum[blockIdx.x] = t;
 }
 
+template <bool FROM_COUNTS>
 __global__ __launch_bounds__(kBaseThreads) void k_base_scan(int32_t n, const uint32_t* __restrict__ tiles_touched,
                                                             const unsigned long long* __restrict__ bsum,
                                                             uint32_t* __restrict__ base,
                                                             unsigned long long* __restrict__ total) {
   __shared__ unsigned long long s_w[kBaseThreads / 64];
   __shared__ unsigned long long s_x[kBaseThreads / 64];
-  // the totals of the blocks before this one
+  // the totals of the blocks before this one: from k_base_sums, or (FROM_COUNTS) from the counts
   unsigned long long pre = 0;
-  for (uint32_t b = threadIdx.x; b < blockIdx.x; b += kBaseThreads) pre += bsum[b];
+  if (FROM_COUNTS) {
+    const int64_t lim = (int64_t)blockIdx.x * kBaseTile;  // every id before the block (all < n)
+    for (int64_t i = threadIdx.x; i < lim; i += 8 * kBaseThreads) {
+      uint32_t v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = i + k * kBaseThreads < lim ? tiles_touched[i + k * kBaseThreads] : 0u;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) pre += v[k];
+    }
+  } else {
+    for (uint32_t b = threadIdx.x; b < blockIdx.x; b += kBaseThreads) pre += bsum[b];
+  }
   pre = block_sum_u64(pre, s_w);
   // exclusive scan of this block's 4096 counts, four consecutive ids per thread
   const int64_t i0 = (int64_t)blockIdx.x * kBaseTile + (int64_t)threadIdx.x * kBaseItems;
@@ -1538,8 +1553,14 @@ gs_status rasterize_bwd(const char* name, int mode, int32_t n, int32_t sh_degree
     rec = (float*)(ws + RL.rec);
     unsigned long long* bsum = (unsigned long long*)(ws + RL.bsum);
     const unsigned nb = (unsigned)(((size_t)n + kBaseTile - 1) / kBaseTile);
-    hipLaunchKernelGGL(k_base_sums, dim3(nb), dim3(kBaseThreads), 0, s, n, proj->d_tiles_touched, bsum);
-    hipLaunchKernelGGL(k_base_scan, dim3(nb), dim3(kBaseThreads), 0, s, n, proj->d_tiles_touched, bsum, base, total);
+    if (nb <= kBaseOne) {
+      hipLaunchKernelGGL(k_base_scan<true>, dim3(nb), dim3(kBaseThreads), 0, s, n, proj->d_tiles_touched, bsum, base,
+                         total);
+    } else {
+      hipLaunchKernelGGL(k_base_sums, dim3(nb), dim3(kBaseThreads), 0, s, n, proj->d_tiles_touched, bsum);
+      hipLaunchKernelGGL(k_base_scan<false>, dim3(nb), dim3(kBaseThreads), 0, s, n, proj->d_tiles_touched, bsum, base,
+                         total);
+    }
   }
   {
     TimedScope ts("rbwd", s);
